@@ -1,0 +1,152 @@
+"""Plain fp64 CPU oracle for the fast-weight matrix-memory scan.
+
+TEST INFRASTRUCTURE. Only tests/, the smoke check and the benchmark's CPU
+baseline leg may import or run this module. The library never calls it, and it
+shares no code with the HIP path (it imports nothing from that package).
+
+It is the sequential recurrence written out, one token at a time, in float64,
+vectorised only over independent heads (b, h). Sources (page titles as printed):
+
+  [FWA]  "Fast Weight Attention for Continual Learning" reading notes
+         (inkeast.github.io MessageDaily): section 3.2 (instantaneous ridge loss and
+         its normalised gradient step), section 4.1 (read-after-write pairing
+         x_t = phi(k_{t-1}), y_t = v_t and the boundary x_1 = 0, eta_1 = 0),
+         section 4.2 (Falcon-1 rule, beta in (0,2), per-step descent lemma,
+         NLMS limit).
+  [AFFN] hncyxsy.com blog post "attention is also an FFN" (news/211194):
+         section 2.1 (S_i = sum_{j<=i} phi(k_j) v_j^T, y_i = phi(q_i)^T S_i),
+         section 3.2 (decayed write S_t = lambda S_{t-1} + phi(k_t) v_t^T),
+         section 4.1 (phi = elu + 1, state of shape d_k x d_v kept in fp32).
+
+Readings where the pages leave a step open (listed in the design doc as D1..D14):
+  D1  per-key-channel lambda: the decay is diag(1 - eta*lambda_t) on the rows of S
+      and eta's denominator uses max_i lambda_{t,i}.
+  D2  step 1 of a sequence (no previous key) neither decays nor writes.
+  D3  the shifted key crosses call boundaries through (xprev, has_prev).
+  D4  beta_t, lambda_t are indexed by the target's step t.
+  D7  additive rule: the `lam` slot carries the retention gamma_t (None = 1) and
+      `beta` an optional write scale (None = 1); pairing is same-index.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+RULE_DELTA = 0
+RULE_ADDITIVE = 1
+
+
+def phi(x: np.ndarray, kind: str) -> np.ndarray:
+    """Feature map. 'elu1' is elu(x) + 1, i.e. x + 1 for x > 0 and exp(x) otherwise
+    ([AFFN] section 4.1); 'identity' returns x."""
+    x = np.asarray(x, dtype=np.float64)
+    if kind == "identity":
+        return x.copy()
+    if kind == "elu1":
+        return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    raise ValueError(kind)
+
+
+def _heads(a, tail_ndim):
+    """Flatten leading (B, H) into one head axis."""
+    a = np.asarray(a, dtype=np.float64)
+    return a.reshape((-1,) + a.shape[a.ndim - tail_ndim:])
+
+
+def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
+         S0=None, xprev0=None, has0=None):
+    """Run the recurrence over a whole sequence.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] or None; lam: [B,H,T] (or
+    [B,H,T,dk] when per_channel) or None. S0: [B,H,dk,dv] or None (zeros);
+    xprev0: [B,H,dk] or None; has0: [B,H] or None (no previous key).
+
+    Returns (o [B,H,T,dv], S [B,H,dk,dv], xprev [B,H,dk], has [B,H]) in float64.
+    """
+    q = np.asarray(q)
+    B, H, T, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    N = B * H
+    Q = _heads(q, 2)
+    K = _heads(k, 2)
+    V = _heads(v, 2)
+    Bt = None if beta is None else _heads(beta, 1)
+    if lam is None:
+        Lm = None
+    else:
+        Lm = _heads(lam, 2 if per_channel else 1)
+
+    S = np.zeros((N, dk, dv)) if S0 is None else _heads(S0, 2).copy()
+    xprev = np.zeros((N, dk)) if xprev0 is None else _heads(xprev0, 1).copy()
+    has = np.zeros(N, dtype=bool) if has0 is None else (np.asarray(has0).reshape(N) != 0)
+    O = np.zeros((N, T, dv))
+
+    for t in range(T):
+        qt = phi(Q[:, t], phi_kind)
+        kt = phi(K[:, t], phi_kind)
+        vt = V[:, t]
+        if rule == RULE_DELTA:
+            # [FWA] 4.1: the pair written at step t is (phi(k_{t-1}), v_t); with no
+            # previous key the pair is (0, v_t) with eta = 0, so nothing happens.
+            x = np.where(has[:, None], xprev, 0.0)
+            if Lm is None:
+                lam_t = np.zeros(N)
+                lam_hat = lam_t
+            elif per_channel:
+                lam_t = Lm[:, t, :]                  # [N, dk]
+                lam_hat = lam_t.max(axis=1)          # reading D1
+            else:
+                lam_t = Lm[:, t]
+                lam_hat = lam_t
+            # [FWA] 3.2 / 4.2: eta_t = beta_t / (||x_t||^2 + lambda_t + eps).
+            den = np.sum(x * x, axis=1) + lam_hat + eps
+            eta = np.where(has, Bt[:, t] / np.where(has, den, 1.0), 0.0)
+            # residual against the state before this step's write
+            r = vt - np.einsum("nij,ni->nj", S, x)
+            decay = 1.0 - (eta[:, None] * lam_t if per_channel else (eta * lam_t)[:, None])
+            S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]
+        elif rule == RULE_ADDITIVE:
+            # [AFFN] 3.2: S_t = gamma_t S_{t-1} + phi(k_t) v_t^T (times an optional
+            # write scale beta_t, reading D7).
+            if Lm is None:
+                gam = np.ones((N, 1, 1))
+            elif per_channel:
+                gam = Lm[:, t, :, None]
+            else:
+                gam = Lm[:, t][:, None, None]
+            b = np.ones(N) if Bt is None else Bt[:, t]
+            S = gam * S + b[:, None, None] * kt[:, :, None] * vt[:, None, :]
+        else:
+            raise ValueError(rule)
+        xprev = kt
+        has = np.ones(N, dtype=bool)
+        # read after write: o_t = S_t^T phi(q_t) ([AFFN] 2.1; [FWA] 4.1)
+        O[:, t] = np.einsum("nij,ni->nj", S, qt)
+
+    return (O.reshape(B, H, T, dv), S.reshape(B, H, dk, dv), xprev.reshape(B, H, dk),
+            has.reshape(B, H).astype(np.int32))
+
+
+def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
+         S0=None, xprev0=None, has0=None):
+    """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
+    (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
+    q = np.asarray(q)[:, :, None]
+    k = np.asarray(k)[:, :, None]
+    v = np.asarray(v)[:, :, None]
+    beta = None if beta is None else np.asarray(beta)[:, :, None]
+    if lam is not None:
+        lam = np.asarray(lam)
+        lam = lam[:, :, None, :] if per_channel else lam[:, :, None]
+    o, S, xp, h = scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind, eps=eps,
+                       per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0)
+    return o[:, :, 0], S, xp, h
+
+
+def relerr(x, ref) -> float:
+    """max|x - ref| / rms(ref), both over the whole tensor, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    if rms == 0.0:
+        return float(np.max(np.abs(x - ref))) if x.size else 0.0
+    return float(np.max(np.abs(x - ref)) / rms) if x.size else 0.0

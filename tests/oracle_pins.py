@@ -1,0 +1,373 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each pin takes the oracle module as an argument (so the mutation test can run the
+same pins on copies of the oracle with a planted mistake) and raises
+AssertionError when the oracle disagrees with the pinned fact. None of them
+re-types the oracle's recurrence: each compares it with a different statement of
+the result (a closed form, a brute-force sum, an invariant, a hand calculation).
+
+Page titles as printed:
+  [FWA]  "Fast Weight Attention for Continual Learning" reading notes
+  [AFFN] hncyxsy.com blog post "attention is also an FFN"
+  [MEM]  "You could have invented transformers from memory" (Alex Wang)
+  [FPKM] "Fast-weight Product Key Memory" notes
+"""
+from __future__ import annotations
+
+from fractions import Fraction as Fr
+
+import numpy as np
+
+DELTA, ADD = 0, 1
+
+
+def _unit_rows(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=1, keepdims=True)
+
+
+def _bh(a):
+    """Add the (B=1, H=1) leading axes."""
+    return np.asarray(a, dtype=np.float64)[None, None]
+
+
+def pin_p1_outer_product_store(orc):
+    """[MEM] outer-product memory store: the additive write with no decay and a
+    zero start leaves S = sum_i phi(k_i) v_i^T, the stacked product K^T V (the page's
+    W = V^T K, transposed to the d_k x d_v orientation of [AFFN] 4.1)."""
+    rng = np.random.default_rng(11)
+    for phi_kind in ("identity", "elu1"):
+        T, dk, dv = 23, 6, 5
+        q = rng.standard_normal((T, dk))
+        k = rng.standard_normal((T, dk))
+        v = rng.standard_normal((T, dv))
+        _, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), None, None, rule=ADD, phi_kind=phi_kind)
+        if phi_kind == "identity":
+            Kf = k
+        else:
+            Kf = np.where(k > 0, k + 1.0, np.exp(np.minimum(k, 0.0)))
+        np.testing.assert_allclose(S[0, 0], Kf.T @ v, rtol=0, atol=1e-12)
+
+
+def pin_p2_quadratic_form(orc):
+    """[AFFN] 2.1: with gamma = 1 the read equals causal linear attention in its
+    quadratic form o_t = sum_{j<=t} (phi(q_t) . phi(k_j)) v_j, brute-forced."""
+    rng = np.random.default_rng(12)
+    T, dk, dv = 13, 5, 4
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    o, _, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), None, None, rule=ADD, phi_kind="elu1")
+
+    def f(x):
+        return [xi + 1.0 if xi > 0 else float(np.exp(xi)) for xi in x]
+
+    for t in range(T):
+        qt = f(q[t])
+        want = [0.0] * dv
+        for j in range(t + 1):
+            kj = f(k[j])
+            w = sum(qt[i] * kj[i] for i in range(dk))
+            for c in range(dv):
+                want[c] += w * v[j][c]
+        np.testing.assert_allclose(o[0, 0, t], want, rtol=0, atol=1e-12)
+
+
+def pin_p2_decayed_quadratic_form(orc):
+    """[AFFN] 3.2, unrolled: with S_t = gamma_t S_{t-1} + phi(k_t) v_t^T,
+    o_t = sum_{j<=t} (prod_{j<s<=t} gamma_s) (phi(q_t).phi(k_j)) v_j and
+    S_T = sum_j (prod_{s>j} gamma_s) phi(k_j) v_j^T. Scalar and per-channel gamma."""
+    rng = np.random.default_rng(13)
+    T, dk, dv = 11, 4, 3
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    S0 = rng.standard_normal((dk, dv))
+    for per_channel in (False, True):
+        gam = rng.uniform(0.3, 1.0, size=(T, dk) if per_channel else (T,))
+        beta = rng.uniform(0.5, 1.5, size=T)
+        o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(gam), rule=ADD,
+                              phi_kind="identity", per_channel=per_channel, S0=_bh(S0))
+        g = gam if per_channel else np.repeat(gam[:, None], dk, axis=1)
+        for t in range(T + 1):
+            # state after t tokens, channel by channel
+            want_S = np.zeros((dk, dv))
+            for i in range(dk):
+                p0 = 1.0
+                for s in range(t):
+                    p0 *= g[s, i]
+                for c in range(dv):
+                    acc = p0 * S0[i, c]
+                    for j in range(t):
+                        p = 1.0
+                        for s in range(j + 1, t):
+                            p *= g[s, i]
+                        acc += p * beta[j] * k[j, i] * v[j, c]
+                    want_S[i, c] = acc
+            if t == T:
+                np.testing.assert_allclose(S[0, 0], want_S, rtol=0, atol=1e-12)
+            if t >= 1:
+                np.testing.assert_allclose(o[0, 0, t - 1], want_S.T @ q[t - 1], rtol=0, atol=1e-12)
+
+
+def pin_p3_first_step_noop(orc):
+    """[FWA] 4.1: the first token of a sequence has no causal pair (x_1 = 0,
+    eta_1 = 0), so its write leaves S_0 untouched, bit for bit, even with a large
+    lambda_1; its read is S_0^T q_1."""
+    rng = np.random.default_rng(14)
+    dk, dv = 7, 5
+    for per_channel in (False, True):
+        S0 = rng.standard_normal((2, 3, dk, dv))
+        q = rng.standard_normal((2, 3, 1, dk))
+        k = rng.standard_normal((2, 3, 1, dk))
+        v = rng.standard_normal((2, 3, 1, dv))
+        beta = rng.uniform(0.1, 1.9, size=(2, 3, 1))
+        lam = rng.uniform(0.5, 5.0, size=(2, 3, 1, dk) if per_channel else (2, 3, 1))
+        o, S, xp, has = orc.scan(q, k, v, beta, lam, rule=DELTA, per_channel=per_channel, S0=S0)
+        assert np.array_equal(S, S0), "step 1 must not change S"
+        np.testing.assert_allclose(o[:, :, 0], np.einsum("bhij,bhi->bhj", S0, q[:, :, 0]),
+                                   rtol=0, atol=1e-12)
+        assert np.array_equal(xp, k[:, :, 0]) and np.all(has == 1)
+
+
+def pin_p4_nlms_rewrite(orc):
+    """[FWA] 4.2: with lambda = eps = 0 the rule is NLMS; with beta = 1 the step
+    rewrites the memory so that it recalls the newest target exactly
+    (S_t^T x_t = y_t, the one-step rewrite of [FPKM] 3.2.1). Read with q_t = k_{t-1}."""
+    rng = np.random.default_rng(15)
+    T, dk, dv = 40, 6, 4
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    q = np.concatenate([rng.standard_normal((1, dk)), k[:-1]], axis=0)
+    S0 = rng.standard_normal((dk, dv))
+    o, _, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.ones(T)), _bh(np.zeros(T)),
+                          rule=DELTA, eps=0.0, S0=_bh(S0))
+    np.testing.assert_allclose(o[0, 0, 1:], v[1:], rtol=0, atol=1e-10)
+
+
+def pin_p5_orthonormal_recall(orc):
+    """[MEM] recall with orthonormal keys has no interference, so recall is exact.
+    Delta rule, beta = 1, lambda = eps = 0, S_0 = 0, shifted pairing: the memory
+    maps k_j to v_{j+1} for every written key."""
+    rng = np.random.default_rng(16)
+    dk, dv = 8, 5
+    T = dk + 1
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = np.concatenate([Qm.T, rng.standard_normal((1, dk))], axis=0)   # k_0..k_{T-2} orthonormal
+    v = rng.standard_normal((T, dv))
+    q = rng.standard_normal((T, dk))
+    _, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.ones(T)), None, rule=DELTA, eps=0.0)
+    for j in range(T - 1):
+        np.testing.assert_allclose(S[0, 0].T @ k[j], v[j + 1], rtol=0, atol=1e-12)
+
+
+def _ridge_loss(S, x, y, lam_vec):
+    r = S.T @ x - y
+    return 0.5 * float(r @ r) + 0.5 * float(np.sum(lam_vec[:, None] * S * S))
+
+
+def pin_p6_descent_lemma(orc, trials=400):
+    """[FWA] 3.2 and 4.2 (Lemma 3.1): each step does not increase the instantaneous
+    ridge loss l_t(S) = 1/2 ||S^T x_t - y_t||^2 + 1/2 sum_i lambda_{t,i} ||S_{i,:}||^2
+    for beta in (0, 2). Per-channel lambda uses the max-channel denominator
+    (reading D1), which bounds the loss's curvature; trials include large lambda and
+    small keys so that a weaker denominator would fail."""
+    rng = np.random.default_rng(17)
+    for trial in range(trials):
+        per_channel = trial % 2 == 1
+        dk, dv = 5, 3
+        S = rng.standard_normal((dk, dv)) * rng.uniform(0.1, 3.0)
+        xp = rng.standard_normal(dk) * rng.uniform(0.05, 2.0)
+        for _ in range(3):
+            k = rng.standard_normal(dk) * rng.uniform(0.05, 2.0)
+            v = rng.standard_normal(dv) * rng.uniform(0.1, 3.0)
+            beta = rng.uniform(0.01, 1.99)
+            lam = rng.uniform(0.0, 4.0, size=dk) if per_channel else rng.uniform(0.0, 4.0)
+            lam_arr = lam[None, None, :] if per_channel else np.array([[lam]])
+            _, S_new, xp_new, _ = orc.step(
+                rng.standard_normal((1, 1, dk)), k[None, None], v[None, None],
+                np.array([[beta]]), lam_arr, rule=DELTA, eps=1e-6, per_channel=per_channel,
+                S0=S[None, None], xprev0=xp[None, None], has0=np.array([[1]]))
+            lam_vec = lam if per_channel else np.full(dk, lam)
+            before = _ridge_loss(S, xp, v, lam_vec)
+            after = _ridge_loss(S_new[0, 0], xp, v, lam_vec)
+            assert after <= before * (1 + 1e-12) + 1e-14, (trial, before, after)
+            S, xp = S_new[0, 0], xp_new[0, 0]
+
+
+def pin_p7_zero_beta(orc):
+    """[FWA] 3.2: beta = 0 makes eta = 0: no decay and no write, so S_t = S_0 and
+    o_t = S_0^T q_t at every step."""
+    rng = np.random.default_rng(18)
+    T, dk, dv = 9, 6, 4
+    S0 = rng.standard_normal((dk, dv))
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    lam = rng.uniform(0.1, 2.0, size=T)
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.zeros(T)), _bh(lam), rule=DELTA,
+                          S0=_bh(S0))
+    assert np.array_equal(S[0, 0], S0)
+    np.testing.assert_allclose(o[0, 0], q @ S0, rtol=0, atol=1e-12)
+
+
+def pin_p8_per_channel_equal(orc):
+    """Reading D1 reduces to the scalar rule when every channel has the same lambda."""
+    rng = np.random.default_rng(19)
+    T, dk, dv = 17, 6, 5
+    q = rng.standard_normal((2, 2, T, dk))
+    k = rng.standard_normal((2, 2, T, dk))
+    v = rng.standard_normal((2, 2, T, dv))
+    beta = rng.uniform(0.1, 1.9, size=(2, 2, T))
+    lam = rng.uniform(0.0, 0.5, size=(2, 2, T))
+    a = orc.scan(q, k, v, beta, lam, rule=DELTA)
+    b = orc.scan(q, k, v, beta, np.repeat(lam[..., None], dk, axis=-1), rule=DELTA,
+                 per_channel=True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-13)
+
+
+def pin_p9_hand_delta(orc):
+    """[AFFN] 5.2 advises checking a length-2, d = 4 case by hand. Delta rule,
+    phi = id, eps = 0, S_0 = 0; token 1 has no pair. Worked by hand:
+      t=2: x = k_1 = e_1, eta = 1/(1+1) = 1/2, r = v_2, S_2 = 1/2 e_1 v_2^T
+           -> row 0 = (1/2, 1, 3/2, 2)
+      t=3: x = k_2 = (1,1,0,0), ||x||^2 = 2, eta = 1/(2+1) = 1/3,
+           S_2^T x = (1/2, 1, 3/2, 2), r = (7/2, 2, 1/2, -1), decay 2/3
+           row 0 = 2/3 (1/2,1,3/2,2) + 1/3 r = (3/2, 4/3, 7/6, 1)
+           row 1 = 1/3 r = (7/6, 2/3, 1/6, -1/3)
+      reads: o_1 = 0, o_2 = S_2^T (1,0,0,1) = row 0 of S_2,
+             o_3 = S_3^T (0,1,1,0) = row 1 of S_3."""
+    k = np.array([[1, 0, 0, 0], [1, 1, 0, 0], [0, 0, 1, 0]], dtype=np.float64)
+    v = np.array([[9, 9, 9, 9], [1, 2, 3, 4], [4, 3, 2, 1]], dtype=np.float64)
+    q = np.array([[1, 1, 1, 1], [1, 0, 0, 1], [0, 1, 1, 0]], dtype=np.float64)
+    beta = np.array([1.0, 1.0, 1.0])
+    lam = np.array([5.0, 1.0, 1.0])          # lambda_1 is irrelevant: step 1 is a no-op
+    o, S, xp, has = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(lam), rule=DELTA, eps=0.0)
+    S3 = [[Fr(3, 2), Fr(4, 3), Fr(7, 6), Fr(1)],
+          [Fr(7, 6), Fr(2, 3), Fr(1, 6), Fr(-1, 3)],
+          [0, 0, 0, 0], [0, 0, 0, 0]]
+    o_want = [[0, 0, 0, 0],
+              [Fr(1, 2), Fr(1), Fr(3, 2), Fr(2)],
+              [Fr(7, 6), Fr(2, 3), Fr(1, 6), Fr(-1, 3)]]
+    np.testing.assert_allclose(S[0, 0], np.array(S3, dtype=np.float64), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[0, 0], np.array(o_want, dtype=np.float64), rtol=0, atol=1e-14)
+    assert np.array_equal(xp[0, 0], k[2]) and has[0, 0] == 1
+
+
+def pin_p9_hand_additive(orc):
+    """Additive rule with phi = elu+1 ([AFFN] 4.1) and gamma = 1/2, worked by hand:
+      phi(k_1) = phi(0,1) = (1,2), phi(k_2) = phi(1,0) = (2,1), v_1 = (1,0), v_2 = (0,1)
+      S_1 = phi(k_1) v_1^T = [[1,0],[2,0]]
+      S_2 = 1/2 S_1 + phi(k_2) v_2^T = [[1/2,2],[1,1]]
+      o_1 = S_1^T phi(0,0) = S_1^T (1,1) = (3,0)
+      o_2 = S_2^T phi(1,1) = S_2^T (2,2) = (3,6)"""
+    k = np.array([[0.0, 1.0], [1.0, 0.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    q = np.array([[0.0, 0.0], [1.0, 1.0]])
+    gam = np.array([0.5, 0.5])
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), None, _bh(gam), rule=ADD, phi_kind="elu1")
+    np.testing.assert_allclose(S[0, 0], [[0.5, 2.0], [1.0, 1.0]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0], [[3.0, 0.0], [3.0, 6.0]], rtol=0, atol=1e-15)
+
+
+def pin_p10_state_carry(orc):
+    """Reading D3: a scan split in two with the state (S, xprev, has_prev) carried,
+    and T single-token steps, both equal one scan over the whole sequence."""
+    rng = np.random.default_rng(20)
+    B, H, T, dk, dv = 2, 2, 12, 5, 4
+    for rule in (DELTA, ADD):
+        q = rng.standard_normal((B, H, T, dk))
+        k = rng.standard_normal((B, H, T, dk))
+        v = rng.standard_normal((B, H, T, dv))
+        beta = rng.uniform(0.1, 1.9, size=(B, H, T))
+        lam = rng.uniform(0.0, 0.9, size=(B, H, T)) if rule == DELTA else rng.uniform(0.5, 1.0, size=(B, H, T))
+        phi_kind = "identity" if rule == DELTA else "elu1"
+        full = orc.scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind)
+        T1 = 5
+        a = orc.scan(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], beta[:, :, :T1], lam[:, :, :T1],
+                     rule=rule, phi_kind=phi_kind)
+        b = orc.scan(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], beta[:, :, T1:], lam[:, :, T1:],
+                     rule=rule, phi_kind=phi_kind, S0=a[1], xprev0=a[2], has0=a[3])
+        np.testing.assert_allclose(np.concatenate([a[0], b[0]], axis=2), full[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(b[1], full[1], rtol=0, atol=1e-12)
+        S, xp, has = None, None, None
+        outs = []
+        for t in range(T):
+            o, S, xp, has = orc.step(q[:, :, t], k[:, :, t], v[:, :, t], beta[:, :, t],
+                                     lam[:, :, t], rule=rule, phi_kind=phi_kind,
+                                     S0=S, xprev0=xp, has0=has)
+            outs.append(o)
+        np.testing.assert_allclose(np.stack(outs, axis=2), full[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(S, full[1], rtol=0, atol=1e-12)
+
+
+def pin_p11_interference_ratio(orc):
+    """[MEM] recall produces interference: storing M random unit keys additively in
+    d_k dimensions and recalling with a stored key gives
+    E ||interference||^2 / ||signal||^2 = (M - 1)/d_k. Checked statistically (+-10%)."""
+    rng = np.random.default_rng(21)
+    dk, dv = 64, 64
+    for M in (16, 64, 128):
+        ratios = []
+        for _ in range(6):
+            keys = _unit_rows(rng, M, dk)
+            vals = _unit_rows(rng, M, dv)
+            # M writes, then M read-only tokens (k = 0, v = 0) that query each stored key
+            k = np.concatenate([keys, np.zeros((M, dk))])
+            v = np.concatenate([vals, np.zeros((M, dv))])
+            q = np.concatenate([np.zeros((M, dk)), keys])
+            o, _, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), None, None, rule=ADD)
+            rec = o[0, 0, M:]
+            ratios.extend(np.sum((rec - vals) ** 2, axis=1) / np.sum(vals ** 2, axis=1))
+        want = (M - 1) / dk
+        got = float(np.mean(ratios))
+        assert abs(got - want) <= 0.1 * want, (M, got, want)
+
+
+def pin_p12_min_norm_store(orc):
+    """[MEM] optimal linear memory store: for M <= d_k independent keys the
+    least-squares store of minimum norm recalls exactly, W = V^T (K K^T)^{-1} K.
+    Sweeping the M pairs repeatedly through the NLMS limit of the delta rule from
+    S_0 = 0 (Kaczmarz's projections) converges to it; in the d_k x d_v orientation
+    S* = K^T (K K^T)^{-1} V."""
+    rng = np.random.default_rng(22)
+    M, dk, dv = 5, 8, 3
+    keys = rng.standard_normal((M, dk))
+    vals = rng.standard_normal((M, dv))
+    sweeps = 300
+    T = M * sweeps + 1
+    idx_k = np.arange(T) % M
+    idx_v = (np.arange(T) - 1) % M          # token t carries v = vals[(t-1) mod M]: pair (k_{t-1}, v_t)
+    k = keys[idx_k]
+    v = vals[idx_v]
+    q = np.zeros((T, dk))
+    _, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.ones(T)), None, rule=DELTA, eps=0.0)
+    S_star = keys.T @ np.linalg.solve(keys @ keys.T, vals)
+    np.testing.assert_allclose(S[0, 0], S_star, rtol=0, atol=1e-9)
+
+
+def pin_relerr_metric(orc):
+    """The parity metric max|x - ref| / rms(ref) on a case worked by hand."""
+    ref = np.array([3.0, -4.0])          # rms = sqrt((9 + 16)/2) = 5/sqrt(2)
+    x = np.array([3.5, -4.0])
+    assert abs(orc.relerr(x, ref) - 0.5 / (5.0 / np.sqrt(2.0))) < 1e-15
+
+
+ALL_PINS = [
+    pin_p1_outer_product_store,
+    pin_p2_quadratic_form,
+    pin_p2_decayed_quadratic_form,
+    pin_p3_first_step_noop,
+    pin_p4_nlms_rewrite,
+    pin_p5_orthonormal_recall,
+    pin_p6_descent_lemma,
+    pin_p7_zero_beta,
+    pin_p8_per_channel_equal,
+    pin_p9_hand_delta,
+    pin_p9_hand_additive,
+    pin_p10_state_carry,
+    pin_p11_interference_ratio,
+    pin_p12_min_norm_store,
+    pin_relerr_metric,
+]

@@ -1,0 +1,59 @@
+"""Planted mistakes in copies of the oracle must each make some pin fail.
+
+Each mutant is the oracle's source with one plausible slip (a dropped term, a
+wrong sign or index, a swapped operand, a different reading); it is executed as a
+throwaway module on the CPU and the pins are run against it.
+"""
+import inspect
+import types
+
+import pytest
+
+from oracle import fwmem_oracle
+from tests import oracle_pins
+
+MUTANTS = {
+    "residual_sign": ('r = vt - np.einsum("nij,ni->nj", S, x)',
+                      'r = vt + np.einsum("nij,ni->nj", S, x)'),
+    "same_index_pairing": ("x = np.where(has[:, None], xprev, 0.0)",
+                           "x = np.where(has[:, None], kt, 0.0)"),
+    "no_ridge_decay": ("decay = 1.0 - (", "decay = 1.0 + 0.0 * ("),
+    "no_key_energy": ("den = np.sum(x * x, axis=1) + lam_hat + eps",
+                      "den = 1.0 + lam_hat + eps"),
+    "no_lambda_in_eta": ("den = np.sum(x * x, axis=1) + lam_hat + eps",
+                         "den = np.sum(x * x, axis=1) + eps"),
+    "first_step_writes": ("eta = np.where(has, Bt[:, t] / np.where(has, den, 1.0), 0.0)",
+                          "eta = Bt[:, t] / den"),
+    "mean_channel_reading": ("lam_hat = lam_t.max(axis=1)", "lam_hat = lam_t.mean(axis=1)"),
+    "transposed_read": ('O[:, t] = np.einsum("nij,ni->nj", S, qt)',
+                        'O[:, t] = np.einsum("nji,ni->nj", S, qt)'),
+    "additive_no_decay": ("S = gam * S + b", "S = S + b"),
+    "additive_no_beta": ("S = gam * S + b[:, None, None] *", "S = gam * S + 1.0 *"),
+    "elu_no_shift": ("np.where(x > 0, x + 1.0,", "np.where(x > 0, x,"),
+    "residual_uses_query": ('r = vt - np.einsum("nij,ni->nj", S, x)',
+                            'r = vt - np.einsum("nij,ni->nj", S, qt)'),
+    "write_uses_value_not_residual": ("eta[:, None, None] * x[:, :, None] * r[:, None, :]",
+                                      "eta[:, None, None] * x[:, :, None] * vt[:, None, :]"),
+    "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
+                          "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(fwmem_oracle)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches_mutant(name):
+    mod = _mutant(*MUTANTS[name])
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or a crash caused by the slip
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutant {name}"
