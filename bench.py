@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of libfwmem on one MI355X.
+
+A step is one pass of the whole scan (the chunk-prep kernel, then the propagate
+kernel: exactly fwmem_scan_fwd) over one batch of synthetic input already resident
+in HBM. The default workload is the delta rule at B=4, H=16, T=4096, d_k=d_v=128
+with bf16 q/k/v (beta = 2 sigmoid(N(0,1)), lambda = softplus(N(-4,1)), seed 0).
+
+Prints ONE JSON line. `roofline` is for the longer of the two kernels, from HIP
+events recorded around every launch on the stream the kernels run on. The decode
+kernel (fwmem_step at B=256, H=32, d=128) is measured in the same run and reported
+under `decode`. `cpu_baseline` is the fp64 oracle timed on the host (a bounded
+sample of the same workload, one batch element).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fast-weight scan tokens/s per GPU (H=16,d=128,T=4096) + % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def scan_bytes_per_token_head(w, out_bytes=4):
+    """Algorithmic HBM bytes of the scan per (token, head): q, k, v read once, beta and
+    lambda read once, out written once (the state adds d_k*d_v*8 per head per call)."""
+    es = 2 if w.dtype == "bf16" else 4
+    lam = 0 if w.lam is None else 4 * (w.dk if w.per_channel else 1)
+    beta = 0 if w.beta is None else 4
+    return (2 * w.dk + w.dv) * es + beta + lam + w.dv * out_bytes
+
+
+def kernel_bytes(w, which):
+    """Algorithmic bytes of one launch of each kernel (its own inputs and outputs)."""
+    es = 2 if w.dtype == "bf16" else 4
+    N = w.B * w.H * w.T
+    lam = 0 if w.lam is None else 4 * (w.dk if w.per_channel else 1)
+    beta = 0 if w.beta is None else 4
+    state = w.B * w.H * w.dk * w.dv * 4
+    if which == "prep":   # reads q, k, beta, lambda
+        return N * (2 * w.dk * es + beta + lam)
+    # propagate: reads q, k, v (and lambda when per channel), writes out; state in and out
+    return N * ((2 * w.dk + w.dv) * es + (lam if w.per_channel else 0) + 4 * w.dv) + 2 * state
+
+
+def scan_mfma_flops(w, C=64):
+    """MFMA flops executed per launch of each kernel (lower-triangular K blocks skipped).
+
+    prep, per (head, chunk): 10 lower 16x16 tiles over K = d_k for each Gram product
+    (X X^T for the delta rule, and Q X^T): 2*16*16*d_k flops per tile.
+    propagate, per (head, chunk): X S, Q S and X^T U are 2*C*d_k*d_v each; T R and M U
+    take 6 MFMA blocks of 16x16x32 per 16 value columns. The additive rule has no X S
+    and no T R."""
+    nch = (w.T + C - 1) // C
+    units = w.B * w.H * nch
+    delta = w.rule == 0
+    tile = 2 * 16 * 16 * w.dk
+    prep = units * (2 if delta else 1) * 10 * tile
+    dense = 2 * C * w.dk * w.dv
+    tri = 6 * (2 * 16 * 16 * 32) * (w.dv // 16)
+    prop = units * ((3 * dense + 2 * tri) if delta else (2 * dense + tri))
+    return prep, prop
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="delta_bf16_h16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan shards over heads with no "
+              "communication, and this build has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_scan_amd import fwmem as F
+    from linear_attention_scan_amd import workloads as wl
+
+    F.load()  # fails loudly when the library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    w = wl.SCAN_WORKLOADS[args.workload](seed=0)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev_t(x, dt=None):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return t.to(dt).to(dev) if dt is not None else t.to(dev)
+
+    q, k, v = dev_t(w.q, tdt), dev_t(w.k, tdt), dev_t(w.v, tdt)
+    beta = None if w.beta is None else dev_t(w.beta)
+    lam = None if w.lam is None else dev_t(w.lam)
+    flags = (F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
+    shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
+    md = F.mode(w.rule, flags, w.eps, 0)
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.float32, device=dev)
+    S_out = F.State(w.B, w.H, w.dk, w.dv, device=dev)
+    ws_n = F.workspace_bytes(shp, md)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+
+    def launch(entry):
+        st = F.scan_fwd_raw(shp, q, k, v, beta, lam, md, None, out, S_out.buf, ws, ws_n,
+                            stream, entry=entry)
+        if st != F.OK:
+            raise F.FwmemError(st, entry)
+
+    for _ in range(args.warmup):
+        launch(F.PHASE_PREP)
+        launch(F.PHASE_PROPAGATE)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(F.PHASE_PREP)
+        ev[i][1].record(stream)
+        launch(F.PHASE_PROPAGATE)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    ms_prep = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    ms_prop = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+
+    tokens = w.B * w.T
+    value = tokens / (ms_step * 1e-3)
+    kern = {
+        "prep": {"ms": ms_prep, "bytes": kernel_bytes(w, "prep")},
+        "propagate": {"ms": ms_prop, "bytes": kernel_bytes(w, "propagate")},
+    }
+    fl_prep, fl_prop = scan_mfma_flops(w)
+    kern["prep"]["mfma_flops"] = fl_prep
+    kern["propagate"]["mfma_flops"] = fl_prop
+    for name, kk in kern.items():
+        kk["GBs"] = kk["bytes"] / (kk["ms"] * 1e-3) / 1e9
+        kk["mfma_TFLOPs"] = kk["mfma_flops"] / (kk["ms"] * 1e-3) / 1e12
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"{dom}_kernel",
+        "achieved": round(kern[dom]["GBs"], 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(kern[dom]["GBs"] / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "mfma_TFLOPs": round(kern[dom]["mfma_TFLOPs"], 2),
+        "mfma_frac": round(kern[dom]["mfma_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
+    }
+    whole_bytes = w.B * w.H * w.T * scan_bytes_per_token_head(w) + 2 * w.B * w.H * w.dk * w.dv * 4
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "rule": "delta" if w.rule == 0 else "additive", "inputs": w.dtype,
+                   "chunk": 64, "seed": 0},
+        "roofline": roofline,
+        "kernels": {n: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),
+                        "mfma_TFLOPs": round(kk["mfma_TFLOPs"], 2)} for n, kk in kern.items()},
+        "whole_step_GBs": round(whole_bytes / (ms_step * 1e-3) / 1e9, 1),
+    }
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(args.decode_steps, dev, stream)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_per_copy": 2 * n,
+                                      "GBs": round(2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(steps, dev, stream):
+    """fwmem_step at B=256, H=32, d=128 (delta rule, lambda = 0.01): HBM stream of the
+    512 MiB fp32 state per step. Inputs come from a pool of 16 pre-generated steps."""
+    import numpy as np
+    import torch
+
+    from linear_attention_scan_amd import fwmem as F
+    from linear_attention_scan_amd import workloads as wl
+    B, H, d = 256, 32, 128
+    pool = []
+    for s in range(16):
+        inp = wl.decode_step(0, s, B, H, d)
+        pool.append(tuple(torch.from_numpy(x).to(dt).to(dev) for x, dt in (
+            (inp.q, torch.bfloat16), (inp.k, torch.bfloat16), (inp.v, torch.bfloat16),
+            (inp.beta, torch.float32), (inp.lam, torch.float32))))
+    sa, sb = F.State(B, H, d, d, device=dev), F.State(B, H, d, d, device=dev)
+    sa.S.copy_(torch.from_numpy(wl.decode_state0(0, B, H, d)))
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    shp = F.shape(B, H, 1, d, d, F.BF16)
+    md = F.mode(0, 0, 1e-6, 0)
+
+    def one(i):
+        q, k, v, be, la = pool[i % len(pool)]
+        src, dst = (sa, sb) if i % 2 == 0 else (sb, sa)
+        st = F.step_raw(shp, q, k, v, be, la, md, src.buf, out, dst.buf, stream)
+        if st != F.OK:
+            raise F.FwmemError(st, "fwmem_step")
+
+    for i in range(5):
+        one(i)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        one(5 + i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per_head = 2 * d * d * 4 + 3 * d * 2 + 8 + d * 4 + 2 * d * 4 + 8
+    nbytes = B * H * per_head
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "decode B=256 H=32 d=128", "kernel": "step_kernel", "steps": steps,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": nbytes}}
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, untuned, on a bounded sample: batch element 0 (all H heads)
+    over the first T_s tokens, T_s chosen to take roughly 10-20 s."""
+    import numpy as np
+
+    from oracle import fwmem_oracle as orc
+    # calibrate on 256 tokens, then run a sample sized for ~12 s
+    def run(Ts):
+        sl = (slice(0, 1), slice(None), slice(0, Ts))
+        t0 = time.perf_counter()
+        orc.scan(w.q[sl], w.k[sl], w.v[sl], None if w.beta is None else w.beta[sl],
+                 None if w.lam is None else w.lam[sl], rule=w.rule, phi_kind=w.phi, eps=w.eps,
+                 per_channel=w.per_channel)
+        return time.perf_counter() - t0
+    t_cal = run(256)
+    Ts = int(min(w.T, max(256, 256 * 12.0 / max(t_cal, 1e-3))))
+    t = run(Ts)
+    return {"value": round(Ts / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch element 0 of {w.B} (all {w.H} heads), first {Ts} of {w.T} tokens, "
+                      f"fp64 NumPy recurrence, single thread, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * libfwmem — the fast-weight matrix-memory scan on AMD Instinct MI355X (gfx950).
+ *
+ * Each head (b, h) carries an associative memory S (d_k x d_v, fp32; row i is key
+ * channel i). Token t writes S with one of two rules and then reads it:
+ *
+ *   DELTA (online ridge / normalised delta rule; "Fast Weight Attention for
+ *   Continual Learning" reading notes, sections 3.2, 4.1 and 4.2):
+ *       x_t = phi(k_{t-1}) (read-after-write pairing), y_t = v_t,
+ *       eta_t = beta_t / (||x_t||^2 + lambda_t + eps),
+ *       r_t = y_t - S_{t-1}^T x_t,
+ *       S_t = (1 - eta_t lambda_t) S_{t-1} + eta_t x_t r_t^T,
+ *       and for the first token of a sequence x_1 = 0, eta_1 = 0 (no decay, no write).
+ *   ADDITIVE (linear attention with decay; hncyxsy.com blog post "attention is also
+ *   an FFN", sections 2.1 and 3.2):
+ *       S_t = gamma_t S_{t-1} + beta_t phi(k_t) v_t^T   (same-index pairing).
+ *
+ *   Read (both rules, after the write): o_t = S_t^T phi(q_t).
+ *
+ * phi is the identity, or elu(x)+1 (the blog post above, section 4.1) with
+ * FWMEM_PHI_ELU1. With FWMEM_LAMBDA_PER_CHANNEL, lambda (delta) or gamma
+ * (additive) is a d_k-vector per token: the decay diag(1 - eta_t lambda_t) (resp.
+ * diag(gamma_t)) scales the rows of S, and eta's denominator uses max_i lambda_{t,i}.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are caller-owned DEVICE pointers, dense, row-major, in
+ *     the layouts given below. The library never allocates, frees or synchronises.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream).
+ *     Argument errors are reported before anything is enqueued; device faults appear
+ *     at the caller's next synchronisation. No exception crosses this interface.
+ *   - Functions are stateless and thread-safe. Kernels use no atomics: repeated calls
+ *     on the same inputs give bit-identical results.
+ *   - Supported sizes: d_k and d_v in {64, 128}; chunk (scan) 0 (= 64) or 64.
+ *
+ * State buffer (one per call side; S_in and S_out may be the same buffer):
+ *   bytes [0, 4*BH*dk*dv)                 S       [B][H][dk][dv] float32
+ *   bytes [4*BH*dk*dv, +4*BH*dk)          x_prev  [B][H][dk]     float32 (= phi(k) of the
+ *                                                                 last token seen)
+ *   bytes [.., +4*BH)                     has_prev[B][H]         int32 (0: the next token
+ *                                                                 starts a sequence)
+ *   padded to fwmem_state_bytes(). S_in == NULL means S = 0, has_prev = 0.
+ */
+#ifndef FWMEM_H
+#define FWMEM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* fwmem_stream; /* the same handle type as hipStream_t */
+
+typedef enum {
+  FWMEM_OK = 0,
+  FWMEM_EINVAL = -1,       /* NULL required pointer, negative size, unknown rule/flag/dtype, bad eps */
+  FWMEM_EUNSUPPORTED = -2, /* a size or chunk length this build has no kernel for */
+  FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda) */
+  FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
+  FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
+  FWMEM_EWORKSPACE = -6    /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
+} fwmem_status;
+
+typedef enum { FWMEM_RULE_DELTA = 0, FWMEM_RULE_ADDITIVE = 1 } fwmem_rule;
+
+/* Storage type of q, k, v. bf16 inputs run on fp16 MFMA operands (power-of-two
+ * scaled, fp32 accumulation); f32 inputs run on fp32 MFMA. */
+typedef enum { FWMEM_F32 = 0, FWMEM_BF16 = 1 } fwmem_dtype;
+
+enum {
+  FWMEM_PHI_ELU1 = 1u << 0,           /* phi = elu(x)+1 on q and k; default identity */
+  FWMEM_LAMBDA_PER_CHANNEL = 1u << 1, /* lambda/gamma is [B][H][T][dk] instead of [B][H][T] */
+  FWMEM_OUT_BF16 = 1u << 2            /* out is bf16 instead of float32 (adds rounding up to
+                                         2^-9 relative per element) */
+};
+
+typedef struct {
+  int32_t B, H, T, dk, dv; /* T is ignored by fwmem_step (one token) */
+  int32_t dtype;           /* fwmem_dtype */
+} fwmem_shape;
+
+typedef struct {
+  int32_t rule;   /* fwmem_rule */
+  uint32_t flags; /* FWMEM_* flags above */
+  float eps;      /* delta rule's eps (>= 0, finite); ignored by ADDITIVE */
+  int32_t chunk;  /* scan chunk length: 0 = library default (64) */
+} fwmem_mode;
+
+/* Bytes of one state buffer (layout above), a multiple of 256. */
+fwmem_status fwmem_state_bytes(const fwmem_shape* shape, size_t* bytes);
+
+/* Bytes of device workspace fwmem_scan_fwd needs for this shape and mode
+ * (0 when T == 0). Its contents need no initialisation and are scratch only. */
+fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
+                                        size_t* bytes);
+
+/*
+ * Whole-sequence scan (chunk-parallel; "Fast Weight Attention for Continual
+ * Learning" reading notes, section 4.4, describes the intra-chunk solve /
+ * inter-chunk recurrence structure this follows).
+ *
+ *   q, k   [B][H][T][dk]  dtype      (required)
+ *   v      [B][H][T][dv]  dtype      (required)
+ *   beta   [B][H][T]      float32    DELTA: required, beta in (0, 2) expected, never
+ *                                    clamped. ADDITIVE: optional write scale (NULL = 1).
+ *   lambda [B][H][T] or [B][H][T][dk] float32
+ *                                    DELTA: ridge lambda >= 0 (NULL = 0).
+ *                                    ADDITIVE: retention gamma in [0, 1] (NULL = 1).
+ *                                    The decay 1 - eta*lambda (resp. gamma) must lie in
+ *                                    [-1, 1]; exact zero is allowed.
+ *   S_in   state buffer or NULL (zero state, sequence start)
+ *   out    [B][H][T][dv]  float32 (bf16 with FWMEM_OUT_BF16)   (required when T > 0)
+ *   S_out  state buffer or NULL (final state not written); may equal S_in
+ *   workspace, ws_bytes: device scratch of at least fwmem_scan_workspace_bytes()
+ *
+ * After the call S_out holds S_T, x_prev = phi(k_T) and has_prev = 1 (T > 0), so a
+ * later scan or fwmem_step continues the same sequence.
+ */
+fwmem_status fwmem_scan_fwd(const fwmem_shape* shape, const void* q, const void* k,
+                            const void* v, const float* beta, const float* lambda,
+                            const fwmem_mode* mode, const void* S_in, void* out, void* S_out,
+                            void* workspace, size_t ws_bytes, fwmem_stream stream);
+
+/*
+ * The two phases of fwmem_scan_fwd, for callers that schedule them separately (and
+ * for per-kernel timing). Same arguments and checks as fwmem_scan_fwd; calling
+ * fwmem_scan_chunk_prep and then fwmem_scan_chunk_propagate with identical
+ * arguments on one stream is exactly fwmem_scan_fwd.
+ *   prep:      intra-chunk work, parallel over (head, chunk): reads q, k, beta,
+ *              lambda and the carried key of S_in; writes only the workspace.
+ *   propagate: the inter-chunk recurrence, serial along T: reads q, k, v, lambda,
+ *              S_in and the workspace that prep wrote; writes out and S_out.
+ */
+fwmem_status fwmem_scan_chunk_prep(const fwmem_shape* shape, const void* q, const void* k,
+                                   const void* v, const float* beta, const float* lambda,
+                                   const fwmem_mode* mode, const void* S_in, void* out,
+                                   void* S_out, void* workspace, size_t ws_bytes,
+                                   fwmem_stream stream);
+fwmem_status fwmem_scan_chunk_propagate(const fwmem_shape* shape, const void* q, const void* k,
+                                        const void* v, const float* beta, const float* lambda,
+                                        const fwmem_mode* mode, const void* S_in, void* out,
+                                        void* S_out, void* workspace, size_t ws_bytes,
+                                        fwmem_stream stream);
+
+/*
+ * One-token recurrent decode: the same recurrence for a single token per head
+ * ("Fast Weight Attention for Continual Learning" reading notes, section 3.2:
+ * fixed-size state at inference; the blog post's section 3.1: O(d^2) per step).
+ *
+ *   q, k [B][H][dk] dtype; v [B][H][dv] dtype; beta [B][H]; lambda [B][H] or
+ *   [B][H][dk]; out [B][H][dv] float32 (bf16 with FWMEM_OUT_BF16).
+ *   S_in: state buffer or NULL (zero state); S_out: state buffer (required);
+ *   S_in == S_out updates in place. shape->T is ignored.
+ */
+fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, const void* v,
+                        const float* beta, const float* lambda, const fwmem_mode* mode,
+                        const void* S_in, void* out, void* S_out, fwmem_stream stream);
+
+/* A static, human-readable name for a status code. */
+const char* fwmem_strerror(fwmem_status status);
+
+/* Library version, e.g. "0.1.0". */
+const char* fwmem_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FWMEM_H */

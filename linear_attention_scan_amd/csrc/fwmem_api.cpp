@@ -1,0 +1,297 @@
+// C ABI of libfwmem: argument checks, buffer layout and dispatch to the launchers.
+// Every check runs on the host before anything is enqueued; the functions keep no
+// state between calls.
+#include "fwmem.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fwmem_internal.h"
+
+namespace {
+
+using fwmem::kChunk;
+
+constexpr uint32_t kKnownFlags = FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect (empty ranges never do).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+struct Sizes {
+  size_t BH, nS, nX, nH;  // element counts of the state parts
+  size_t state_bytes;
+};
+
+Sizes sizes_of(const fwmem_shape* s) {
+  Sizes z;
+  z.BH = (size_t)s->B * (size_t)s->H;
+  z.nS = z.BH * (size_t)s->dk * (size_t)s->dv;
+  z.nX = z.BH * (size_t)s->dk;
+  z.nH = z.BH;
+  z.state_bytes = align256(4 * (z.nS + z.nX + z.nH));
+  return z;
+}
+
+fwmem_status check_shape(const fwmem_shape* s, bool need_T) {
+  if (s == nullptr) return FWMEM_EINVAL;
+  if (s->B < 0 || s->H < 0 || s->dk <= 0 || s->dv <= 0) return FWMEM_EINVAL;
+  if (need_T && s->T < 0) return FWMEM_EINVAL;
+  if (s->dtype != FWMEM_F32 && s->dtype != FWMEM_BF16) return FWMEM_EINVAL;
+  return FWMEM_OK;
+}
+
+fwmem_status check_mode(const fwmem_mode* m) {
+  if (m == nullptr) return FWMEM_EINVAL;
+  if (m->rule != FWMEM_RULE_DELTA && m->rule != FWMEM_RULE_ADDITIVE) return FWMEM_EINVAL;
+  if ((m->flags & ~kKnownFlags) != 0) return FWMEM_EINVAL;
+  if (!std::isfinite(m->eps) || m->eps < 0.f) return FWMEM_EINVAL;
+  if (m->chunk != 0 && m->chunk != kChunk) return FWMEM_EUNSUPPORTED;
+  return FWMEM_OK;
+}
+
+// Pointers into a state buffer.
+struct StatePtrs {
+  float* S;
+  float* x;
+  int32_t* h;
+};
+
+StatePtrs state_ptrs(const void* base, const Sizes& z) {
+  char* b = static_cast<char*>(const_cast<void*>(base));
+  if (b == nullptr) return {nullptr, nullptr, nullptr};
+  return {reinterpret_cast<float*>(b), reinterpret_cast<float*>(b + 4 * z.nS),
+          reinterpret_cast<int32_t*>(b + 4 * (z.nS + z.nX))};
+}
+
+size_t esize(int dtype) { return dtype == FWMEM_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fwmem_version(void) { return "0.1.0"; }
+
+const char* fwmem_strerror(fwmem_status st) {
+  switch (st) {
+    case FWMEM_OK: return "ok";
+    case FWMEM_EINVAL: return "invalid argument";
+    case FWMEM_EUNSUPPORTED: return "unsupported size or chunk length";
+    case FWMEM_EALIGN: return "misaligned pointer";
+    case FWMEM_EOVERLAP: return "overlapping buffers";
+    case FWMEM_ELAUNCH: return "kernel launch failed";
+    case FWMEM_EWORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+fwmem_status fwmem_state_bytes(const fwmem_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return FWMEM_EINVAL;
+  const fwmem_status st = check_shape(shape, false);
+  if (st != FWMEM_OK) return st;
+  *bytes = sizes_of(shape).state_bytes;
+  return FWMEM_OK;
+}
+
+fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
+                                        size_t* bytes) {
+  if (bytes == nullptr) return FWMEM_EINVAL;
+  fwmem_status st = check_shape(shape, true);
+  if (st != FWMEM_OK) return st;
+  st = check_mode(mode);
+  if (st != FWMEM_OK) return st;
+  if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
+  const size_t BH = (size_t)shape->B * (size_t)shape->H;
+  const size_t nchunks = ((size_t)shape->T + kChunk - 1) / kChunk;
+  *bytes = BH * nchunks * fwmem::scan_record_bytes(shape->dtype == FWMEM_BF16, shape->dk);
+  return FWMEM_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, const void* v,
+                       const float* beta, const float* lambda, const fwmem_mode* mode,
+                       const void* S_in, void* out, void* S_out, void* workspace, size_t ws_bytes,
+                       fwmem_stream stream, int phases) {
+  fwmem_status st = check_shape(shape, true);
+  if (st != FWMEM_OK) return st;
+  st = check_mode(mode);
+  if (st != FWMEM_OK) return st;
+  if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
+
+  const Sizes z = sizes_of(shape);
+  if (z.BH == 0) return FWMEM_OK;
+  const bool delta = mode->rule == FWMEM_RULE_DELTA;
+  const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
+  const size_t T = (size_t)shape->T;
+  const size_t es = esize(shape->dtype);
+
+  if (T > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return FWMEM_EINVAL;
+    if (delta && beta == nullptr) return FWMEM_EINVAL;
+  }
+  // alignment
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(workspace, 16) || !aligned(beta, 4) ||
+      !aligned(lambda, pc ? 16 : 4))
+    return FWMEM_EALIGN;
+
+  // overlap
+  const size_t nq = z.BH * T * shape->dk * es, nv = z.BH * T * shape->dv * es;
+  const size_t nb = z.BH * T * 4, nl = z.BH * T * 4 * (pc ? shape->dk : 1);
+  const size_t no = z.BH * T * shape->dv * ((mode->flags & FWMEM_OUT_BF16) ? 2 : 4);
+  size_t need = 0;
+  st = fwmem_scan_workspace_bytes(shape, mode, &need);
+  if (st != FWMEM_OK) return st;
+  if (S_in != nullptr && S_out != nullptr && S_in != S_out &&
+      overlap(S_in, z.state_bytes, S_out, z.state_bytes))
+    return FWMEM_EOVERLAP;
+  const void* ins[] = {q, k, v, beta, lambda, S_in, S_out, workspace};
+  const size_t nins[] = {nq, nq, nv, nb, nl, z.state_bytes, z.state_bytes, need};
+  for (int i = 0; i < 8; ++i)
+    if (overlap(out, no, ins[i], nins[i])) return FWMEM_EOVERLAP;
+  for (int i = 0; i < 7; ++i)
+    if (overlap(workspace, need, ins[i], nins[i])) return FWMEM_EOVERLAP;
+  if (S_out != nullptr)
+    for (int i = 0; i < 5; ++i)
+      if (overlap(S_out, z.state_bytes, ins[i], nins[i])) return FWMEM_EOVERLAP;
+
+  const StatePtrs si = state_ptrs(S_in, z), so = state_ptrs(S_out, z);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+
+  if (T == 0) {
+    if (S_out == nullptr || S_out == S_in || (phases & 2) == 0) return FWMEM_OK;
+    const hipError_t e = fwmem::launch_state_copy(si.S, si.x, si.h, so.S, so.x, so.h, z.nS, z.nX,
+                                                  z.nH, hs);
+    return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+  }
+  if (workspace == nullptr || ws_bytes < need) return FWMEM_EWORKSPACE;
+
+  fwmem::ScanParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.lam = lambda;
+  p.S_in = si.S;
+  p.xprev_in = si.x;
+  p.has_in = si.h;
+  p.out = out;
+  p.S_out = so.S;
+  p.xprev_out = so.x;
+  p.has_out = so.h;
+  p.ws = static_cast<char*>(workspace);
+  p.BH = (int)z.BH;
+  p.T = (int)T;
+  p.dk = shape->dk;
+  p.dv = shape->dv;
+  p.nchunks = (int)((T + kChunk - 1) / kChunk);
+  p.delta = delta ? 1 : 0;
+  p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
+  p.flags = mode->flags;
+  p.eps = mode->eps;
+  if (z.BH > 0x7fffffff / 8 || (size_t)p.nchunks * z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
+  const hipError_t e = fwmem::launch_scan(p, hs, phases);
+  return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fwmem_status fwmem_scan_fwd(const fwmem_shape* shape, const void* q, const void* k, const void* v,
+                            const float* beta, const float* lambda, const fwmem_mode* mode,
+                            const void* S_in, void* out, void* S_out, void* workspace,
+                            size_t ws_bytes, fwmem_stream stream) {
+  return scan_impl(shape, q, k, v, beta, lambda, mode, S_in, out, S_out, workspace, ws_bytes,
+                   stream, 3);
+}
+
+fwmem_status fwmem_scan_chunk_prep(const fwmem_shape* shape, const void* q, const void* k,
+                                   const void* v, const float* beta, const float* lambda,
+                                   const fwmem_mode* mode, const void* S_in, void* out,
+                                   void* S_out, void* workspace, size_t ws_bytes,
+                                   fwmem_stream stream) {
+  return scan_impl(shape, q, k, v, beta, lambda, mode, S_in, out, S_out, workspace, ws_bytes,
+                   stream, 1);
+}
+
+fwmem_status fwmem_scan_chunk_propagate(const fwmem_shape* shape, const void* q, const void* k,
+                                        const void* v, const float* beta, const float* lambda,
+                                        const fwmem_mode* mode, const void* S_in, void* out,
+                                        void* S_out, void* workspace, size_t ws_bytes,
+                                        fwmem_stream stream) {
+  return scan_impl(shape, q, k, v, beta, lambda, mode, S_in, out, S_out, workspace, ws_bytes,
+                   stream, 2);
+}
+
+fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, const void* v,
+                        const float* beta, const float* lambda, const fwmem_mode* mode,
+                        const void* S_in, void* out, void* S_out, fwmem_stream stream) {
+  fwmem_status st = check_shape(shape, false);
+  if (st != FWMEM_OK) return st;
+  st = check_mode(mode);
+  if (st != FWMEM_OK) return st;
+  if (!fwmem::step_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
+  const Sizes z = sizes_of(shape);
+  if (z.BH == 0) return FWMEM_OK;
+  const bool delta = mode->rule == FWMEM_RULE_DELTA;
+  const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || S_out == nullptr)
+    return FWMEM_EINVAL;
+  if (delta && beta == nullptr) return FWMEM_EINVAL;
+  const size_t es = esize(shape->dtype);
+  if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(out, 16) ||
+      !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(beta, 4) || !aligned(lambda, 4))
+    return FWMEM_EALIGN;
+  const size_t nq = z.BH * shape->dk * es, nv = z.BH * shape->dv * es;
+  const size_t nb = z.BH * 4, nl = z.BH * 4 * (pc ? shape->dk : 1);
+  const size_t no = z.BH * shape->dv * ((mode->flags & FWMEM_OUT_BF16) ? 2 : 4);
+  if (S_in != nullptr && S_in != S_out && overlap(S_in, z.state_bytes, S_out, z.state_bytes))
+    return FWMEM_EOVERLAP;
+  const void* ins[] = {q, k, v, beta, lambda, S_in, S_out};
+  const size_t nins[] = {nq, nq, nv, nb, nl, z.state_bytes, z.state_bytes};
+  for (int i = 0; i < 7; ++i)
+    if (overlap(out, no, ins[i], nins[i])) return FWMEM_EOVERLAP;
+  for (int i = 0; i < 5; ++i)
+    if (overlap(S_out, z.state_bytes, ins[i], nins[i])) return FWMEM_EOVERLAP;
+
+  const StatePtrs si = state_ptrs(S_in, z), so = state_ptrs(S_out, z);
+  fwmem::StepParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.lam = lambda;
+  p.S_in = si.S;
+  p.xprev_in = si.x;
+  p.has_in = si.h;
+  p.out = out;
+  p.S_out = so.S;
+  p.xprev_out = so.x;
+  p.has_out = so.h;
+  p.BH = (int)z.BH;
+  p.dk = shape->dk;
+  p.dv = shape->dv;
+  p.delta = delta ? 1 : 0;
+  p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
+  p.flags = mode->flags;
+  p.eps = mode->eps;
+  if (z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
+  const hipError_t e = fwmem::launch_step(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Device building blocks shared by the libfwmem kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA operand conventions. A 16x16 fp32 accumulator tile ("C layout") is held by
+// one wave: lane l owns rows 4*(l/16)+i, i = 0..3, of column l%16. The kernels keep
+// every intermediate matrix that feeds a later product in this layout and turn it
+// straight into the next product's B operand, with no LDS round trip, by choosing
+// which K index each operand slot carries:
+//   * fp16 policy (PolF16, v_mfma_f32_16x16x32_f16): within a K block of 32, lane
+//     group g = l/16 carries K = 4g+i (slots 0..3) and 16+4g+i (slots 4..7), i.e.
+//     exactly the rows lane l owns in the two 16-row C tiles of that block.
+//   * fp32 policy (PolF32, v_mfma_f32_16x16x4_f32): a K block of 16 is four
+//     instructions; instruction i takes K = 4g+i, again the lane's own rows.
+// A operands are read from LDS with the same K mapping. Since the A and B slots of
+// one lane refer to the same K, the contraction is exact whatever order the
+// hardware sums the slots in.
+//
+// fp16 operands carry a power-of-two scale so that any finite fp32 value range
+// maps into fp16 without overflow: a block of values with max |x| = m is stored
+// as x * 2^s with m * 2^s in [2^14, 2^15), and products are unscaled in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwmem {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// elu(x) + 1: x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Reduction over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Power-of-two factor 2^s with m * 2^s in [2^14, 2^15) for finite m > 0; 1 otherwise.
+__device__ __forceinline__ float pow2_scale(float m) {
+  if (!(m > 0.f) || !(m <= 3.4028234e38f)) return 1.f;
+  int e;
+  (void)frexpf(m, &e);  // m in [2^(e-1), 2^e)
+  int s = 15 - e;
+  s = s < -126 ? -126 : (s > 126 ? 126 : s);
+  return ldexpf(1.f, s);
+}
+
+// ---------------------------------------------------------------------------
+// Precision policies.
+
+struct PolF16 {
+  using op_t = _Float16;
+  using frag_t = h8;
+  static constexpr int KB = 32;          // K extent of one operand block
+  static constexpr bool kScaled = true;  // operands carry power-of-two scales
+  static constexpr int kPad = 8;         // LDS row padding, elements
+
+  __device__ static __forceinline__ op_t cvt(float x) { return (op_t)x; }
+
+  // Operand fragment from a row-major LDS row (K contiguous) for K block kb.
+  __device__ static __forceinline__ frag_t lds_row(const op_t* row, int kb, int g) {
+    const h4 lo = *reinterpret_cast<const h4*>(row + kb * 32 + 4 * g);
+    const h4 hi = *reinterpret_cast<const h4*>(row + kb * 32 + 16 + 4 * g);
+    frag_t r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+  // Operand fragment from C-layout tiles c[2kb], c[2kb+1], each value times s.
+  __device__ static __forceinline__ frag_t from_c(const f4* c, int kb, float s) {
+    frag_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = (op_t)(c[2 * kb][i] * s);
+      r[4 + i] = (op_t)(c[2 * kb + 1][i] * s);
+    }
+    return r;
+  }
+  __device__ static __forceinline__ void mma(f4& acc, const frag_t& a, const frag_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+  }
+};
+
+struct PolF32 {
+  using op_t = float;
+  using frag_t = f4;
+  static constexpr int KB = 16;
+  static constexpr bool kScaled = false;
+  static constexpr int kPad = 4;
+
+  __device__ static __forceinline__ op_t cvt(float x) { return x; }
+
+  __device__ static __forceinline__ frag_t lds_row(const op_t* row, int kb, int g) {
+    return *reinterpret_cast<const f4*>(row + kb * 16 + 4 * g);
+  }
+  // Fragment whose K runs down a column: element (k, m) at base[k * ld + m].
+  __device__ static __forceinline__ frag_t lds_col(const op_t* base, int ld, int m, int kb, int g) {
+    frag_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = base[(kb * 16 + 4 * g + i) * ld + m];
+    return r;
+  }
+  __device__ static __forceinline__ frag_t from_c(const f4* c, int kb, float s) {
+    return c[kb] * s;
+  }
+  __device__ static __forceinline__ void mma(f4& acc, const frag_t& a, const frag_t& b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+  }
+};
+
+// Input element access: bf16 (stored as uint16_t) or float.
+template <typename InT>
+struct In;
+
+template <>
+struct In<uint16_t> {
+  static constexpr int VW = 8;  // elements per 16-byte load
+  using Pol = PolF16;
+  __device__ static __forceinline__ void load(const uint16_t* p, float (&x)[VW]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(a[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+    }
+  }
+  __device__ static __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+};
+
+template <>
+struct In<float> {
+  static constexpr int VW = 4;
+  using Pol = PolF32;
+  __device__ static __forceinline__ void load(const float* p, float (&x)[VW]) {
+    const float4 w = *reinterpret_cast<const float4*>(p);
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  }
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+};
+
+// log|a| (floored so that an exact zero gives a large negative finite value) and
+// whether a < 0; decay products are carried as (sum of logs, sign parity).
+__device__ __forceinline__ float log_abs_floor(float a) { return __logf(fmaxf(fabsf(a), 1e-30f)); }
+
+}  // namespace fwmem

@@ -1,0 +1,76 @@
+// Internal interface between the C-ABI layer (fwmem_api.cpp) and the kernel
+// launchers (fwmem_scan.hip, fwmem_step.hip). Host code only sees plain structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fwmem {
+
+enum : uint32_t {
+  kFlagPhiElu1 = 1u << 0,
+  kFlagPerChannel = 1u << 1,
+  kFlagOutBf16 = 1u << 2,
+};
+
+constexpr int kChunk = 64;  // scan chunk length (tokens)
+
+// Pointers are device pointers; optional ones may be null.
+struct ScanParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;     // [BH][T] (optional for the additive rule)
+  const float* lam;      // [BH][T] or [BH][T][dk], optional
+  const float* S_in;     // [BH][dk][dv] or null (zeros)
+  const float* xprev_in; // [BH][dk] or null
+  const int32_t* has_in; // [BH] or null
+  void* out;             // [BH][T][dv] fp32 or bf16
+  float* S_out;          // [BH][dk][dv] or null (state not written)
+  float* xprev_out;      // [BH][dk] (with S_out)
+  int32_t* has_out;      // [BH]     (with S_out)
+  char* ws;              // workspace records
+  int BH, T, dk, dv, nchunks;
+  int delta;             // 1: delta rule, 0: additive
+  int bf16;              // 1: bf16 inputs, 0: fp32
+  uint32_t flags;
+  float eps;
+};
+
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;      // [BH] (optional for the additive rule)
+  const float* lam;       // [BH] or [BH][dk], optional
+  const float* S_in;      // [BH][dk][dv] or null
+  const float* xprev_in;  // [BH][dk] or null
+  const int32_t* has_in;  // [BH] or null
+  void* out;              // [BH][dv]
+  float* S_out;           // [BH][dk][dv] (required)
+  float* xprev_out;
+  int32_t* has_out;
+  int BH, dk, dv;
+  int delta, bf16;
+  uint32_t flags;
+  float eps;
+};
+
+// Bytes of one (head, chunk) workspace record.
+size_t scan_record_bytes(int bf16, int dk);
+// Whether kernels exist for this size.
+bool scan_supported(int dk, int dv);
+bool step_supported(int dk, int dv);
+
+// Enqueue the scan (T >= 1): phases bit 0 = prep kernel, bit 1 = propagate kernel.
+// Returns hipSuccess or the launch error.
+hipError_t launch_scan(const ScanParams& p, hipStream_t stream, int phases);
+// Enqueue one decode step.
+hipError_t launch_step(const StepParams& p, hipStream_t stream);
+// S_out := S_in (or the zero state), for T == 0 scans. Bytes is the state size.
+hipError_t launch_state_copy(const float* S_in, const float* xprev_in, const int32_t* has_in,
+                             float* S_out, float* xprev_out, int32_t* has_out, size_t nS,
+                             size_t nX, size_t nH, hipStream_t stream);
+
+}  // namespace fwmem

@@ -1,0 +1,206 @@
+// One-token recurrent decode for gfx950: a pure stream of the fp32 state.
+//
+// Per head (delta rule, "Fast Weight Attention for Continual Learning" reading
+// notes, sections 3.2 and 4.1):
+//   x = x_prev (if a previous key exists, else 0)
+//   eta = beta / (||x||^2 + lambda_hat + eps)  (0 without a previous key)
+//   r = v - S^T x
+//   S' = diag(a) S + eta x r^T,  a = 1 - eta lambda   (scalar or per key channel)
+//   o = S'^T q~ = S^T (a o q~) + eta (x . q~) r
+// so one read of S yields both column reductions (S^T x and S^T (a o q~)) and the
+// state is written back from registers: exactly one read and one write of S.
+// Additive rule ("attention is also an FFN", section 3.2):
+//   S' = diag(gamma) S + b phi(k) v^T,  o = S^T (gamma o q~) + b (phi(k) . q~) v.
+//
+// Layout: one 256-thread workgroup per head. Thread (rg, cq) owns float4 column
+// group cq (4 value columns) of rows rg, rg + RG, ...; a wave's 16-byte loads cover
+// whole rows of S, so every access is a coalesced 128-bit load or store.
+#include "fwmem_device.h"
+#include "fwmem_internal.h"
+
+namespace fwmem {
+
+namespace {
+
+constexpr int NT = 256;
+
+template <typename InT, int DK, int DV, bool DELTA, bool PC>
+__global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
+  constexpr int TPRd = DV / 4;       // threads per row (float4 each)
+  constexpr int RG = NT / TPRd;      // row groups
+  constexpr int RPT = DK / RG;       // rows per thread
+  constexpr int RGW = 64 / TPRd;     // row groups per wave
+  constexpr int NWV = NT / 64;
+  static_assert(DK % RG == 0 && RGW >= 1, "shape");
+
+  __shared__ float s_x[DK], s_q[DK], s_a[DK], s_k[DK];
+  __shared__ float s_red[2][NWV][DV];
+  __shared__ float s_sc[4];
+
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cq = tid % TPRd, rg = tid / TPRd;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const InT* qp = static_cast<const InT*>(p.q) + (size_t)bh * DK;
+  const InT* kp = static_cast<const InT*>(p.k) + (size_t)bh * DK;
+  const InT* vp = static_cast<const InT*>(p.v) + (size_t)bh * DV;
+  const bool has = p.has_in != nullptr && p.has_in[bh] != 0;
+
+  // Issue the state loads first: they are the whole cost of the step.
+  f4 S[RPT];
+  const float* Sin = p.S_in != nullptr ? p.S_in + (size_t)bh * DK * DV : nullptr;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int row = rg + RG * j;
+    S[j] = Sin != nullptr
+               ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(Sin + (size_t)row * DV) + cq)
+               : f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Per-head vectors into LDS.
+  for (int i = tid; i < DK; i += NT) {
+    float q = In<InT>::load1(qp + i);
+    float k = In<InT>::load1(kp + i);
+    if (elu) { q = phi_elu1(q); k = phi_elu1(k); }
+    s_q[i] = q;
+    s_k[i] = k;
+    s_x[i] = (DELTA && has && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
+  }
+  __syncthreads();
+
+  // Scalars: ||x||^2, max lambda (per channel), x.q or k.q; wave 0 reduces.
+  if (wave == 0) {
+    float nx = 0.f, dq = 0.f, lm = 0.f;
+    for (int i = lane; i < DK; i += 64) {
+      const float xi = DELTA ? s_x[i] : s_k[i];
+      nx += xi * xi;
+      dq += xi * s_q[i];
+      if (PC && p.lam != nullptr) lm = fmaxf(lm, p.lam[(size_t)bh * DK + i]);
+    }
+    nx = wave_sum(nx);
+    dq = wave_sum(dq);
+    lm = wave_max(lm);
+    if (lane == 0) {
+      float eta = 0.f, a = 1.f;
+      if (DELTA) {
+        const float lam = PC ? lm : (p.lam != nullptr ? p.lam[bh] : 0.f);
+        if (has) eta = p.beta[bh] / (nx + lam + p.eps);
+        a = 1.f - eta * lam;
+      } else {
+        eta = p.beta != nullptr ? p.beta[bh] : 1.f;  // write scale
+        a = (!PC && p.lam != nullptr) ? p.lam[bh] : 1.f;
+      }
+      s_sc[0] = eta;
+      s_sc[1] = a;
+      s_sc[2] = dq;
+    }
+  }
+  __syncthreads();
+  const float eta = s_sc[0], a_sc = s_sc[1], dq = s_sc[2];
+  for (int i = tid; i < DK; i += NT) {
+    float a = a_sc;
+    if (PC) {
+      const float lam = p.lam != nullptr ? p.lam[(size_t)bh * DK + i] : (DELTA ? 0.f : 1.f);
+      a = DELTA ? 1.f - eta * lam : lam;
+    }
+    s_a[i] = a;
+  }
+  __syncthreads();
+
+  // Column partial sums over this thread's rows: p = S^T x, w = S^T (a o q).
+  f4 pp = {0.f, 0.f, 0.f, 0.f}, ww = pp;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int row = rg + RG * j;
+    const float xi = s_x[row], aq = s_a[row] * s_q[row];
+    pp += S[j] * xi;
+    ww += S[j] * aq;
+  }
+  // reduce over the row groups inside the wave (lanes cq, cq + TPRd, ...)
+#pragma unroll
+  for (int o = TPRd; o < 64; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pp[e] += __shfl_xor(pp[e], o);
+      ww[e] += __shfl_xor(ww[e], o);
+    }
+  }
+  if (lane < TPRd) {
+    *reinterpret_cast<f4*>(&s_red[0][wave][4 * cq]) = pp;
+    *reinterpret_cast<f4*>(&s_red[1][wave][4 * cq]) = ww;
+  }
+  __syncthreads();
+  f4 P = {0.f, 0.f, 0.f, 0.f}, W = P;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    P += *reinterpret_cast<const f4*>(&s_red[0][w][4 * cq]);
+    W += *reinterpret_cast<const f4*>(&s_red[1][w][4 * cq]);
+  }
+
+  float v4[4];
+  {
+    const int c = 4 * cq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v4[e] = In<InT>::load1(vp + c + e);
+  }
+  // r (delta) or the written value b*v (additive), and the output.
+  const f4 vv = {v4[0], v4[1], v4[2], v4[3]};
+  const f4 r = DELTA ? (vv - P) * eta : vv * eta;  // the written value u
+  const f4 o = W + r * dq;
+
+  // New state from registers.
+  float* Sout = p.S_out + (size_t)bh * DK * DV;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int row = rg + RG * j;
+    const float a = s_a[row];
+    const float xi = DELTA ? s_x[row] : s_k[row];
+    const f4 n4 = S[j] * a + r * xi;
+    __builtin_nontemporal_store(n4, reinterpret_cast<f4*>(Sout + (size_t)row * DV) + cq);
+  }
+  if (rg == 0) {
+    const size_t ob = (size_t)bh * DV + 4 * cq;
+    if (p.flags & kFlagOutBf16) {
+      uint16_t* op = static_cast<uint16_t*>(p.out) + ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) op[e] = f32_to_bf16_bits(o[e]);
+    } else {
+      *reinterpret_cast<f4*>(static_cast<float*>(p.out) + ob) = o;
+    }
+  }
+  for (int i = tid; i < DK; i += NT) p.xprev_out[(size_t)bh * DK + i] = s_k[i];
+  if (tid == 0) p.has_out[bh] = 1;
+}
+
+template <typename InT, int DK, int DV>
+hipError_t launch_t(const StepParams& p, hipStream_t st) {
+  const bool pc = (p.flags & kFlagPerChannel) != 0;
+  const dim3 grid(p.BH), block(NT);
+  if (p.delta) {
+    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, true, false>), grid, block, 0, st, p);
+  } else {
+    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, false, false>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename InT>
+hipError_t launch_in(const StepParams& p, hipStream_t st) {
+  if (p.dk == 64 && p.dv == 64) return launch_t<InT, 64, 64>(p, st);
+  if (p.dk == 64 && p.dv == 128) return launch_t<InT, 64, 128>(p, st);
+  if (p.dk == 128 && p.dv == 64) return launch_t<InT, 128, 64>(p, st);
+  return launch_t<InT, 128, 128>(p, st);
+}
+
+}  // namespace
+
+bool step_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
+
+hipError_t launch_step(const StepParams& p, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  return p.bf16 ? launch_in<uint16_t>(p, st) : launch_in<float>(p, st);
+}
+
+}  // namespace fwmem
