@@ -28,6 +28,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+// 16-byte raw words as a native vector (HIP's uint4 is a struct that SROA keeps in memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -155,12 +157,13 @@ struct In<uint16_t> {
   static constexpr int VW = 8;  // elements per 16-byte load
   using Pol = PolF16;
   __device__ static __forceinline__ void load(const uint16_t* p, float (&x)[VW]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+    decode(*reinterpret_cast<const u32x4*>(p), x);
+  }
+  __device__ static __forceinline__ void decode(const u32x4& w, float (&x)[VW]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_bits_to_f32(a[i] & 0xffffu);
-      x[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
     }
   }
   __device__ static __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
@@ -171,8 +174,11 @@ struct In<float> {
   static constexpr int VW = 4;
   using Pol = PolF32;
   __device__ static __forceinline__ void load(const float* p, float (&x)[VW]) {
-    const float4 w = *reinterpret_cast<const float4*>(p);
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+    decode(*reinterpret_cast<const u32x4*>(p), x);
+  }
+  __device__ static __forceinline__ void decode(const u32x4& w, float (&x)[VW]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
   }
   __device__ static __forceinline__ float load1(const float* p) { return *p; }
 };

@@ -46,12 +46,12 @@ struct Rec {
   using op_t = typename PolOf<InT>::op_t;
   static constexpr size_t kT = 0;                                   // op_t [CH][CH]
   static constexpr size_t kM = kT + sizeof(op_t) * CH * CH;         // op_t [CH][CH]
-  static constexpr size_t kEta = kM + sizeof(op_t) * CH * CH;       // float [CH]
-  static constexpr size_t kG = kEta + 4 * CH;                       // float [CH] log|Gamma_t|
-  static constexpr size_t kSg = kG + 4 * CH;                        // float [CH] sign(Gamma_t)
-  static constexpr size_t kX0 = kSg + 4 * CH;                       // float [DK] key before token 0
-  static constexpr size_t kSc = kX0 + 4 * DK;                       // float [4] 1/sT, 1/sM, has_prev
-  static constexpr size_t kBytes = (kSc + 16 + 255) / 256 * 256;
+  // per token t: (fP, fV, fO, fU), the row factors the propagate kernel applies
+  static constexpr size_t kFac = kM + sizeof(op_t) * CH * CH;       // float4 [CH]
+  static constexpr size_t kX0 = kFac + 16 * CH;                     // float [DK] key before token 0
+  // 1/sT, 1/sM, has_prev, Gamma_C (scalar decay), sX, sQ
+  static constexpr size_t kSc = kX0 + 4 * DK;                       // float [8]
+  static constexpr size_t kBytes = (kSc + 32 + 255) / 256 * 256;
 };
 
 // ---------------------------------------------------------------- row staging
@@ -153,21 +153,20 @@ __device__ StageScales stage_rows(const ScanParams& p, int bh, int t0, const flo
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int t = ps * RPP + tid / TPR;
-    typename Pol::op_t xo[VW], qo[VW];
+    typename Pol::frag_t xo, qo;  // VW operands = 16 bytes
 #pragma unroll
     for (int j = 0; j < VW; ++j) {
       xo[j] = Pol::cvt(xr[ps][j] * sc.sX);
       qo[j] = Pol::cvt(qr[ps][j] * sc.sQ);
     }
-    // 16-byte stores of VW operands (8 halves or 4 floats)
-    *reinterpret_cast<uint4*>(Xs + t * ldX + col) = *reinterpret_cast<const uint4*>(xo);
-    *reinterpret_cast<uint4*>(Qs + t * ldX + col) = *reinterpret_cast<const uint4*>(qo);
+    *reinterpret_cast<typename Pol::frag_t*>(Xs + t * ldX + col) = xo;
+    *reinterpret_cast<typename Pol::frag_t*>(Qs + t * ldX + col) = qo;
     if (WRITE_XU) {
       if constexpr (Pol::kScaled) {
 #pragma unroll
         for (int j = 0; j < VW; ++j) XU[(col + j) * ldT + t] = xo[j];
       } else {
-        *reinterpret_cast<uint4*>(XU + t * ldX + col) = *reinterpret_cast<const uint4*>(xo);
+        *reinterpret_cast<typename Pol::frag_t*>(XU + t * ldX + col) = xo;
       }
     }
   }
@@ -505,28 +504,52 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       sT = pow2_scale(block_max(mt_, s_red));
       sM = pow2_scale(block_max(mm_, s_red + NW));
     }
-    op_t to[16], mo[16];
+    using frag_t = typename Pol::frag_t;
+    constexpr int EV = 16 / sizeof(op_t);  // elements per 16-byte vector
+    frag_t* Tg = reinterpret_cast<frag_t*>(reinterpret_cast<op_t*>(rec + RC::kT) + t * CH + c0);
+    frag_t* Mg = reinterpret_cast<frag_t*>(reinterpret_cast<op_t*>(rec + RC::kM) + t * CH + c0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { to[j] = Pol::cvt(tv[j] * sT); mo[j] = Pol::cvt(mv[j] * sM); }
-    op_t* Tg = reinterpret_cast<op_t*>(rec + RC::kT) + t * CH + c0;
-    op_t* Mg = reinterpret_cast<op_t*>(rec + RC::kM) + t * CH + c0;
-    constexpr int NV = 16 * sizeof(op_t) / 16;
+    for (int j = 0; j < 16 / EV; ++j) {
+      frag_t tw, mw;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      if (DELTA) reinterpret_cast<uint4*>(Tg)[j] = reinterpret_cast<const uint4*>(to)[j];
-      reinterpret_cast<uint4*>(Mg)[j] = reinterpret_cast<const uint4*>(mo)[j];
+      for (int e = 0; e < EV; ++e) {
+        tw[e] = Pol::cvt(tv[j * EV + e] * sT);
+        mw[e] = Pol::cvt(mv[j * EV + e] * sM);
+      }
+      if (DELTA) Tg[j] = tw;
+      Mg[j] = mw;
     }
     if (tid < CH) {
-      reinterpret_cast<float*>(rec + RC::kEta)[tid] = s_eta[tid];
-      reinterpret_cast<float*>(rec + RC::kG)[tid] = s_g[tid];
-      reinterpret_cast<float*>(rec + RC::kSg)[tid] = s_sg[tid];
+      // Row factors of the propagate step (see the header comment): with X, Q stored
+      // scaled by sX, sQ,
+      //   R = fV V - fP (X S),  O = fO (Q S) + M U,  S' = Gamma_C S + X^T (fU U).
+      // Per-channel decay is folded into the operands instead, so only eta and the
+      // scales remain.
+      const int t = tid;
+      const float e = s_eta[t];
+      f4 fac;
+      if (PC) {
+        fac = f4{e / sc.sX, e, 1.f / sc.sQ, 1.f / sc.sX};
+      } else {
+        const float gprev = t ? s_g[t - 1] : 0.f;
+        const float sprev = t ? s_sg[t - 1] : 1.f;
+        const float gammaPrev = sprev * __expf(gprev);
+        const float gammaT = s_sg[t] * __expf(s_g[t]);
+        const float ratioC = s_sg[CH - 1] * s_sg[t] * __expf(s_g[CH - 1] - s_g[t]);
+        fac = f4{e * gammaPrev / sc.sX, e, gammaT / sc.sQ, ratioC / sc.sX};
+      }
+      reinterpret_cast<f4*>(rec + RC::kFac)[t] = fac;
     }
     if (tid == 0) {
       float* scv = reinterpret_cast<float*>(rec + RC::kSc);
       scv[0] = 1.f / sT;
       scv[1] = 1.f / sM;
       scv[2] = has_in ? 1.f : 0.f;
-      scv[3] = 0.f;
+      scv[3] = PC ? 1.f : s_sg[CH - 1] * __expf(s_g[CH - 1]);
+      scv[4] = sc.sX;
+      scv[5] = sc.sQ;
+      scv[6] = 0.f;
+      scv[7] = 0.f;
     }
     if (c == 0 && tid < DK) {
       reinterpret_cast<float*>(rec + RC::kX0)[tid] = x0 != nullptr ? x0[tid] : 0.f;
@@ -553,8 +576,8 @@ struct PropLds {
   static constexpr size_t oT = oQ + kX;
   static constexpr size_t oM = oT + kC;
   static constexpr size_t oV = oM + kC;
-  static constexpr size_t oS = oV + kV;  // small: 6*CH + DK + 4*NW + 16 floats
-  static constexpr size_t kBytes = oS + 4 * (6 * CH + DK + 4 * NW + 16);
+  static constexpr size_t oS = oV + kV;  // small: 5*CH + DK + 4*NW + 16 floats
+  static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 4 * NW + 16);
 };
 
 template <typename InT, int DK, bool DELTA, bool PC>
@@ -582,8 +605,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   float* s_fV = s_fP + CH;
   float* s_fO = s_fV + CH;
   float* s_fU = s_fO + CH;
-  float* s_eta = s_fU + CH;
-  float* s_misc = s_eta + CH;  // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
+  float* s_misc = s_fU + CH;   // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
   float* s_gC = s_misc + CH;   // [DK] per-channel Gamma_C
   float* s_red = s_gC + DK;
 
@@ -620,76 +642,130 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   const bool has_in = reinterpret_cast<const float*>(rec0 + RC::kSc)[2] != 0.f;
   const float* x0 = (DELTA && has_in) ? reinterpret_cast<const float*>(rec0 + RC::kX0) : nullptr;
 
-  for (int c = 0; c < p.nchunks; ++c) {
-    const int t0 = c * CH;
-    const char* rec = rec0 + (size_t)c * RC::kBytes;
+  // ---- software pipeline: the next chunk's global data is loaded into registers
+  // while the current chunk computes; staging then only writes LDS.
+  using Rw = Rows<InT, DK>;
+  constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
+  constexpr int TPRv = 64 / VW, RPPv = NT / TPRv, NPV = CH / RPPv;  // value tile
+  constexpr int EPT = CH * CH / NT, NVT = EPT * (int)sizeof(op_t) / 16;  // T and M
+  const InT* kp = static_cast<const InT*>(p.k);
+  const InT* qp = static_cast<const InT*>(p.q);
+  const InT* vp = static_cast<const InT*>(p.v);
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const int col = (tid % TPR) * VW;           // row staging: this thread's columns
+  const int vcol = (tid % TPRv) * VW;         // value tile: this thread's columns
+  const int e0 = tid * EPT;                   // T / M: this thread's elements
+  u32x4 px[NPASS], pq[NPASS], pv[NPV], pt[NVT], pm[NVT];
+  f4 pf = {0.f, 0.f, 0.f, 0.f};
+  uint32_t valid = 0;
 
-    // ---- stage the chunk into LDS
-    const StageScales sc = stage_rows<InT, DK, DELTA, !PC>(p, bh, t0, c == 0 ? x0 : nullptr, Xs, Qs,
-                                                           XU, LDX, LDT, nullptr, s_red);
-    {
-      // value tile [CH][64] -> fp32
-      constexpr int VWv = In<InT>::VW;
-      constexpr int TPRv = 64 / VWv;
-      constexpr int RPPv = NT / TPRv;
-      const InT* vp = static_cast<const InT*>(p.v);
-      const int cc = (tid % TPRv) * VWv;
-#pragma unroll
-      for (int ps = 0; ps < CH / RPPv; ++ps) {
-        const int t = ps * RPPv + tid / TPRv;
-        const int tau = t0 + t;
-        float x[VWv];
-#pragma unroll
-        for (int j = 0; j < VWv; ++j) x[j] = 0.f;
-        if (tau < p.T && grp * 64 + cc < dv) In<InT>::load(vp + (rowbase + tau) * dv + grp * 64 + cc, x);
-#pragma unroll
-        for (int j = 0; j < VWv; ++j) Vs[t * LDV + cc + j] = x[j];
-      }
-      // T and M from the record
-      constexpr int EPT = CH * CH / NT;  // elements per thread
-      constexpr int NV = EPT * sizeof(op_t) / 16;
-      const int e0 = tid * EPT;
-      const int rr = e0 / CH, cc2 = e0 % CH;
-      const uint4* Tg = reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(rec + RC::kT) + e0);
-      const uint4* Mg = reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(rec + RC::kM) + e0);
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (DELTA) reinterpret_cast<uint4*>(Ts + rr * LDC + cc2)[j] = Tg[j];
-        reinterpret_cast<uint4*>(Ms + rr * LDC + cc2)[j] = Mg[j];
-      }
-      // token factors
-      if (tid < CH) {
-        const int t = tid;
-        const float* eta = reinterpret_cast<const float*>(rec + RC::kEta);
-        const float* gg = reinterpret_cast<const float*>(rec + RC::kG);
-        const float* sg = reinterpret_cast<const float*>(rec + RC::kSg);
-        const float e = eta[t];
-        s_eta[t] = e;
-        if (PC) {
-          s_fP[t] = e / sc.sX;
-          s_fV[t] = e;
-          s_fO[t] = 1.f / sc.sQ;
-          s_fU[t] = 1.f / sc.sX;
-        } else {
-          const float gprev = t ? gg[t - 1] : 0.f;
-          const float sprev = t ? sg[t - 1] : 1.f;
-          const float gammaPrev = sprev * __expf(gprev);
-          const float gammaT = sg[t] * __expf(gg[t]);
-          const float ratioC = sg[CH - 1] * sg[t] * __expf(gg[CH - 1] - gg[t]);
-          s_fP[t] = e * gammaPrev / sc.sX;
-          s_fV[t] = e;
-          s_fO[t] = gammaT / sc.sQ;
-          s_fU[t] = ratioC / sc.sX;
-          if (t == 0) s_misc[0] = sg[CH - 1] * __expf(gg[CH - 1]);
+  // Iteration c stages chunk c from registers, then issues the loads of chunk c+1
+  // and computes chunk c while they are in flight (c = -1 only loads chunk 0).
+  for (int c = -1; c < p.nchunks; ++c) {
+    const int t0 = c * CH;
+    if (c >= 0) {
+      // ---- registers -> LDS (chunk c)
+        const float* scv = reinterpret_cast<const float*>(rec0 + (size_t)c * RC::kBytes + RC::kSc);
+        const float sX = scv[4], sQ = scv[5];
+    #pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const int t = ps * RPP + tid / TPR;
+          float x[VW], qv[VW];
+          In<InT>::decode(px[ps], x);
+          In<InT>::decode(pq[ps], qv);
+          if (DELTA && t0 + t == 0) {
+    #pragma unroll
+            for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[col + j] : 0.f;
+          } else if (elu && (valid >> ps & 1u)) {
+    #pragma unroll
+            for (int j = 0; j < VW; ++j) x[j] = phi_elu1(x[j]);
+          }
+          if (elu && (valid >> (16 + ps) & 1u)) {
+    #pragma unroll
+            for (int j = 0; j < VW; ++j) qv[j] = phi_elu1(qv[j]);
+          }
+          frag_t xo, qo;  // VW operands = 16 bytes
+    #pragma unroll
+          for (int j = 0; j < VW; ++j) {
+            xo[j] = Pol::cvt(x[j] * sX);
+            qo[j] = Pol::cvt(qv[j] * sQ);
+          }
+          *reinterpret_cast<frag_t*>(Xs + t * LDX + col) = xo;
+          *reinterpret_cast<frag_t*>(Qs + t * LDX + col) = qo;
+          if (!PC) {
+            if constexpr (Pol::kScaled) {
+    #pragma unroll
+              for (int j = 0; j < VW; ++j) XU[(col + j) * LDT + t] = xo[j];
+            } else {
+              *reinterpret_cast<frag_t*>(XU + t * LDX + col) = xo;
+            }
+          }
         }
-        if (t == 0) {
-          const float* scv = reinterpret_cast<const float*>(rec + RC::kSc);
+    #pragma unroll
+        for (int ps = 0; ps < NPV; ++ps) {
+          const int t = ps * RPPv + tid / TPRv;
+          float x[VW];
+          In<InT>::decode(pv[ps], x);
+    #pragma unroll
+          for (int j = 0; j < VW; ++j) Vs[t * LDV + vcol + j] = x[j];
+        }
+        const int rr = e0 / CH, cc2 = e0 % CH;
+    #pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+          if (DELTA) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
+          reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
+        }
+        if (tid < CH) {
+          s_fP[tid] = pf[0];
+          s_fV[tid] = pf[1];
+          s_fO[tid] = pf[2];
+          s_fU[tid] = pf[3];
+        }
+        if (tid == 0) {
+          s_misc[0] = scv[3];
           s_misc[1] = scv[0];
           s_misc[2] = scv[1];
         }
-      }
+      __syncthreads();
     }
-    __syncthreads();
+    if (c + 1 < p.nchunks) {
+      // ---- global -> registers (chunk c+1)
+      const int cn = c + 1;
+        const int t0 = cn * CH;
+        const char* rec = rec0 + (size_t)cn * RC::kBytes;
+        valid = 0;
+    #pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const int tau = t0 + ps * RPP + tid / TPR;
+          px[ps] = u32x4{0u, 0u, 0u, 0u};
+          pq[ps] = u32x4{0u, 0u, 0u, 0u};
+          if (tau < p.T) {
+            const int src = DELTA ? tau - 1 : tau;
+            if (src >= 0) {
+              px[ps] = *reinterpret_cast<const u32x4*>(kp + (rowbase + src) * DK + col);
+              valid |= 1u << ps;
+            }
+            pq[ps] = *reinterpret_cast<const u32x4*>(qp + (rowbase + tau) * DK + col);
+            valid |= 1u << (16 + ps);
+          }
+        }
+    #pragma unroll
+        for (int ps = 0; ps < NPV; ++ps) {
+          const int tau = t0 + ps * RPPv + tid / TPRv;
+          pv[ps] = u32x4{0u, 0u, 0u, 0u};
+          if (tau < p.T && grp * 64 + vcol < dv)
+            pv[ps] = *reinterpret_cast<const u32x4*>(vp + (rowbase + tau) * dv + grp * 64 + vcol);
+        }
+        const u32x4* Tg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kT) + e0);
+        const u32x4* Mg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kM) + e0);
+    #pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+          if (DELTA) pt[j] = Tg[j];
+          pm[j] = Mg[j];
+        }
+        if (tid < CH) pf = reinterpret_cast<const f4*>(rec + RC::kFac)[tid];
+    }
+    if (c < 0) continue;
 
     if (PC) {
       // per-channel decay folded into the operands: X*Gamma_prev, Q*Gamma, X*Gamma_C/Gamma
@@ -704,7 +780,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           const int tau = t0 + t;
           float lam = DELTA ? 0.f : 1.f;
           if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
-          const float a = DELTA ? 1.f - s_eta[t] * lam : lam;
+          const float a = DELTA ? 1.f - s_fV[t] * lam : lam;
           gsum += log_abs_floor(a);
           pr ^= (a < 0.f) ? 1u : 0u;
           gcol[t] = gsum;
