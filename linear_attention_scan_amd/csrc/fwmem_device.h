@@ -12,7 +12,10 @@
 //     instructions; instruction i takes K = 4g+i, again the lane's own rows.
 // A operands are read from LDS with the same K mapping. Since the A and B slots of
 // one lane refer to the same K, the contraction is exact whatever order the
-// hardware sums the slots in.
+// hardware sums the slots in. For the fp16 policy, LDS rows store each K block of
+// 32 in the permuted order p(16h + 4g + i) = 8g + 4h + i, so that the eight
+// operands of lane group g are one contiguous 16-byte read (kpos() maps logical K
+// to the stored position).
 //
 // fp16 operands carry a power-of-two scale so that any finite fp32 value range
 // maps into fp16 without overflow: a block of values with max |x| = m is stored
@@ -26,6 +29,7 @@ namespace fwmem {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 // 16-byte raw words as a native vector (HIP's uint4 is a struct that SROA keeps in memory)
@@ -60,6 +64,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Max over the four lanes that hold one column of an MFMA C tile (lanes l, l^16,
+// l^32, l^48): per-column operand scales need only this two-step exchange.
+__device__ __forceinline__ float col_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
 // Reduction over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
@@ -83,6 +95,18 @@ __device__ __forceinline__ float pow2_scale(float m) {
   s = s < -126 ? -126 : (s > 126 ? 126 : s);
   return ldexpf(1.f, s);
 }
+// The same factor and its exact inverse (both powers of two, no division).
+__device__ __forceinline__ void pow2_scale2(float m, float& sc, float& inv) {
+  int s = 0;
+  if (m > 0.f && m <= 3.4028234e38f) {
+    int e;
+    (void)frexpf(m, &e);
+    s = 15 - e;
+    s = s < -126 ? -126 : (s > 126 ? 126 : s);
+  }
+  sc = ldexpf(1.f, s);
+  inv = ldexpf(1.f, -s);
+}
 
 // ---------------------------------------------------------------------------
 // Precision policies.
@@ -96,14 +120,24 @@ struct PolF16 {
 
   __device__ static __forceinline__ op_t cvt(float x) { return (op_t)x; }
 
-  // Operand fragment from a row-major LDS row (K contiguous) for K block kb.
+  // Stored position of logical K index k within an LDS row (see the header comment).
+  __device__ static __forceinline__ int kpos(int k) {
+    const int o = k & 31;
+    return (k & ~31) + 8 * ((o >> 2) & 3) + 4 * (o >> 4) + (o & 3);
+  }
+  // Operand fragment of lane group g for K block kb: one 16-byte read.
   __device__ static __forceinline__ frag_t lds_row(const op_t* row, int kb, int g) {
-    const h4 lo = *reinterpret_cast<const h4*>(row + kb * 32 + 4 * g);
-    const h4 hi = *reinterpret_cast<const h4*>(row + kb * 32 + 16 + 4 * g);
-    frag_t r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-    return r;
+    return *reinterpret_cast<const frag_t*>(row + kb * 32 + 8 * g);
+  }
+  // Store 8 operands of logical K k0..k0+7 (k0 a multiple of 8) into a row.
+  __device__ static __forceinline__ void store_run(op_t* row, int k0, const frag_t& v) {
+    const int p = kpos(k0);  // k0+4..k0+7 sit 8 positions further
+    *reinterpret_cast<h4*>(row + p) = h4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<h4*>(row + p + 8) = h4{v[4], v[5], v[6], v[7]};
+  }
+  // Store 4 operands of logical K k0..k0+3 (k0 a multiple of 4).
+  __device__ static __forceinline__ void store4(op_t* row, int k0, float a, float b, float c, float d) {
+    *reinterpret_cast<h4*>(row + kpos(k0)) = h4{(op_t)a, (op_t)b, (op_t)c, (op_t)d};
   }
   // Operand fragment from C-layout tiles c[2kb], c[2kb+1], each value times s.
   __device__ static __forceinline__ frag_t from_c(const f4* c, int kb, float s) {
@@ -129,8 +163,15 @@ struct PolF32 {
 
   __device__ static __forceinline__ op_t cvt(float x) { return x; }
 
+  __device__ static __forceinline__ int kpos(int k) { return k; }
   __device__ static __forceinline__ frag_t lds_row(const op_t* row, int kb, int g) {
     return *reinterpret_cast<const f4*>(row + kb * 16 + 4 * g);
+  }
+  __device__ static __forceinline__ void store_run(op_t* row, int k0, const frag_t& v) {
+    *reinterpret_cast<f4*>(row + k0) = v;
+  }
+  __device__ static __forceinline__ void store4(op_t* row, int k0, float a, float b, float c, float d) {
+    *reinterpret_cast<f4*>(row + k0) = f4{a, b, c, d};
   }
   // Fragment whose K runs down a column: element (k, m) at base[k * ld + m].
   __device__ static __forceinline__ frag_t lds_col(const op_t* base, int ld, int m, int kb, int g) {

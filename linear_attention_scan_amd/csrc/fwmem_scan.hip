@@ -23,11 +23,12 @@
 // Two kernels:
 //   prep_kernel: one workgroup per (head, chunk), fully parallel. Builds the chunk's
 //     Gram X X^T and Q X^T on MFMA, the decay masks, T = (I + L)^-1 in fp32 (blocked
-//     forward substitution in LDS) and writes T, M and the token scalars to the
-//     workspace.
+//     forward substitution in LDS) and writes T, M, the per-token row factors and
+//     the operand scales to the workspace.
 //   prop_kernel: one workgroup per (head, group of 64 value columns); each of its
 //     4 waves owns a 16-column tile of S in registers (fp32, MFMA C layout) and walks
-//     the chunks in order; the only serial dependency is along T.
+//     the chunks in order; the only serial dependency is along T. The next chunk's
+//     global data is loaded into registers while the current chunk computes.
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
 
@@ -44,24 +45,21 @@ using PolOf = typename In<InT>::Pol;
 template <typename InT, int DK>
 struct Rec {
   using op_t = typename PolOf<InT>::op_t;
+  // T and M rows in the policy's LDS operand order (copied verbatim into LDS)
   static constexpr size_t kT = 0;                                   // op_t [CH][CH]
   static constexpr size_t kM = kT + sizeof(op_t) * CH * CH;         // op_t [CH][CH]
-  // per token t: (fP, fV, fO, fU), the row factors the propagate kernel applies
-  static constexpr size_t kFac = kM + sizeof(op_t) * CH * CH;       // float4 [CH]
+  // per token t: fP, fV, fO, fU (four arrays of CH), the row factors of the step
+  //   R = fV V - fP (X S),  O = fO (Q S) + M U,  S' = Gamma_C S + X^T (fU U)
+  static constexpr size_t kFac = kM + sizeof(op_t) * CH * CH;       // float [4][CH]
   static constexpr size_t kX0 = kFac + 16 * CH;                     // float [DK] key before token 0
   // 1/sT, 1/sM, has_prev, Gamma_C (scalar decay), sX, sQ
   static constexpr size_t kSc = kX0 + 4 * DK;                       // float [8]
   static constexpr size_t kBytes = (kSc + 32 + 255) / 256 * 256;
 };
 
-// ---------------------------------------------------------------- row staging
-// Loads the chunk's x rows (shifted keys for the delta rule) and q rows, applies
-// phi, and stores them scaled into LDS as MFMA operands. Also returns the row
-// norms ||x_t||^2 (fp32) into s_norm when requested.
+// Thread layout of a [CH][DK] row staging: 16-byte loads of VW elements.
 template <typename InT, int DK>
 struct Rows {
-  using Pol = PolOf<InT>;
-  using op_t = typename Pol::op_t;
   static constexpr int VW = In<InT>::VW;
   static constexpr int TPR = DK / VW;   // threads per row
   static constexpr int RPP = NT / TPR;  // rows per pass
@@ -69,108 +67,11 @@ struct Rows {
   static_assert(CH % RPP == 0, "rows");
 };
 
-struct StageScales {
-  float sX, sQ;
-};
-
-// x0: the key carried into token 0 of the sequence (fp32, phi already applied) or
-// null; used by the delta rule when the chunk starts at token 0.
-// XU (optional): second copy of X for the state update, transposed [DK][ldT] for
-// the fp16 policy.
-template <typename InT, int DK, bool DELTA, bool WRITE_XU>
-__device__ StageScales stage_rows(const ScanParams& p, int bh, int t0, const float* x0,
-                                  typename PolOf<InT>::op_t* Xs, typename PolOf<InT>::op_t* Qs,
-                                  typename PolOf<InT>::op_t* XU, int ldX, int ldT,
-                                  float* s_norm, float* s_red) {
-  using R = Rows<InT, DK>;
-  using Pol = typename R::Pol;
-  constexpr int VW = R::VW, TPR = R::TPR, RPP = R::RPP, NPASS = R::NPASS;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const InT* kp = static_cast<const InT*>(p.k);
-  const InT* qp = static_cast<const InT*>(p.q);
-  const bool elu = (p.flags & kFlagPhiElu1) != 0;
-  const size_t rowbase = (size_t)bh * (size_t)p.T;
-  const int col = (tid % TPR) * VW;
-
-  float xr[NPASS][VW], qr[NPASS][VW];
-  float mx = 0.f, mq = 0.f;
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int t = ps * RPP + tid / TPR;
-    const int tau = t0 + t;
-#pragma unroll
-    for (int j = 0; j < VW; ++j) { xr[ps][j] = 0.f; qr[ps][j] = 0.f; }
-    if (tau < p.T) {
-      if (DELTA) {
-        if (tau >= 1) {
-          In<InT>::load(kp + (rowbase + tau - 1) * DK + col, xr[ps]);
-          if (elu) {
-#pragma unroll
-            for (int j = 0; j < VW; ++j) xr[ps][j] = phi_elu1(xr[ps][j]);
-          }
-        } else if (x0 != nullptr) {
-#pragma unroll
-          for (int j = 0; j < VW; ++j) xr[ps][j] = x0[col + j];
-        }
-      } else {
-        In<InT>::load(kp + (rowbase + tau) * DK + col, xr[ps]);
-        if (elu) {
-#pragma unroll
-          for (int j = 0; j < VW; ++j) xr[ps][j] = phi_elu1(xr[ps][j]);
-        }
-      }
-      In<InT>::load(qp + (rowbase + tau) * DK + col, qr[ps]);
-      if (elu) {
-#pragma unroll
-        for (int j = 0; j < VW; ++j) qr[ps][j] = phi_elu1(qr[ps][j]);
-      }
-    }
-    float ns = 0.f;
-#pragma unroll
-    for (int j = 0; j < VW; ++j) {
-      ns += xr[ps][j] * xr[ps][j];
-      mx = fmaxf(mx, fabsf(xr[ps][j]));
-      mq = fmaxf(mq, fabsf(qr[ps][j]));
-    }
-    if (s_norm != nullptr) {
-      ns = group_sum<TPR>(ns);
-      if (tid % TPR == 0) s_norm[t] = ns;
-    }
-  }
-  StageScales sc{1.f, 1.f};
-  if (Pol::kScaled) {
-    mx = wave_max(mx);
-    mq = wave_max(mq);
-    if (lane == 0) { s_red[wave] = mx; s_red[NW + wave] = mq; }
-    __syncthreads();
-    float a = s_red[0], b = s_red[NW];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) { a = fmaxf(a, s_red[w]); b = fmaxf(b, s_red[NW + w]); }
-    sc.sX = pow2_scale(a);
-    sc.sQ = pow2_scale(b);
-  }
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int t = ps * RPP + tid / TPR;
-    typename Pol::frag_t xo, qo;  // VW operands = 16 bytes
-#pragma unroll
-    for (int j = 0; j < VW; ++j) {
-      xo[j] = Pol::cvt(xr[ps][j] * sc.sX);
-      qo[j] = Pol::cvt(qr[ps][j] * sc.sQ);
-    }
-    *reinterpret_cast<typename Pol::frag_t*>(Xs + t * ldX + col) = xo;
-    *reinterpret_cast<typename Pol::frag_t*>(Qs + t * ldX + col) = qo;
-    if (WRITE_XU) {
-      if constexpr (Pol::kScaled) {
-#pragma unroll
-        for (int j = 0; j < VW; ++j) XU[(col + j) * ldT + t] = xo[j];
-      } else {
-        *reinterpret_cast<typename Pol::frag_t*>(XU + t * ldX + col) = xo;
-      }
-    }
-  }
-  return sc;
+// 16-byte load at a uniform base plus a 32-bit byte offset (lets the compiler use
+// the scalar-base + vector-offset addressing form).
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const T* base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
 // Block-wide max of a per-thread value (all threads must call it).
@@ -197,8 +98,8 @@ __device__ __forceinline__ void wave_prefix(float& la, int& ng) {
   }
 }
 
-// ---------------------------------------------------------------- prep kernel
-template <typename InT, int DK, bool DELTA, bool PC>
+// ================================================================ prep kernel
+template <typename InT, int DK>
 struct PrepLds {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
@@ -207,23 +108,25 @@ struct PrepLds {
   static constexpr size_t kOp = (size_t)CH * LDX * sizeof(op_t);
   static constexpr size_t kMat = (size_t)CH * LDF * 4;
   static constexpr size_t kReg = ((kOp > kMat ? kOp : kMat) + 15) / 16 * 16;
-  static constexpr int kRegions = 4;
   static constexpr size_t kSmall = 4 * (5 * CH + 4 * NW + 16);
-  static constexpr size_t kBytes = kRegions * kReg + kSmall;
+  static constexpr size_t kBytes = 4 * kReg + kSmall;
 };
 
-template <typename InT, int DK, bool DELTA, bool PC>
+template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
 __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
-  using L = PrepLds<InT, DK, DELTA, PC>;
+  using frag_t = typename Pol::frag_t;
+  using L = PrepLds<InT, DK>;
   using RC = Rec<InT, DK>;
+  using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDF = L::LDF;
+  constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
   __shared__ __align__(16) char smem[L::kBytes];
   char* reg[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) reg[r] = smem + r * L::kReg;
-  float* s_norm = reinterpret_cast<float*>(smem + L::kRegions * L::kReg);
+  float* s_norm = reinterpret_cast<float*>(smem + 4 * L::kReg);
   float* s_lam = s_norm + CH;
   float* s_eta = s_lam + CH;
   float* s_g = s_eta + CH;
@@ -237,11 +140,78 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   const size_t rowbase = (size_t)bh * p.T;
   const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
   const float* x0 = (DELTA && has_in) ? p.xprev_in + (size_t)bh * DK : nullptr;
+  const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
+  const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
 
+  // Token gates for wave 0 (lane = token), loaded first so their latency overlaps
+  // the row loads.
+  float g_beta = 0.f, g_lam = 0.f;
+  if (wave == 0 && t0 + lane < p.T) {
+    const size_t ti = rowbase + t0 + lane;
+    g_beta = p.beta != nullptr ? p.beta[ti] : 1.f;
+    if (!PC && p.lam != nullptr) g_lam = p.lam[ti];
+  }
+
+  // ---- row staging: x rows (shifted keys for the delta rule) and q rows, phi
+  // applied, scaled by one power of two per matrix, into LDS as MFMA operands.
   op_t* Xs = reinterpret_cast<op_t*>(reg[0]);
   op_t* Qs = reinterpret_cast<op_t*>(reg[1]);
-  const StageScales sc =
-      stage_rows<InT, DK, DELTA, false>(p, bh, t0, x0, Xs, Qs, nullptr, LDX, 0, s_norm, s_red);
+  float sX = 1.f, sQ = 1.f;
+  {
+    const int col = (tid % TPR) * VW;
+    float xr[NPASS][VW], qr[NPASS][VW];
+    float mx = 0.f, mq = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int t = ps * RPP + tid / TPR;
+      const int tau = t0 + t;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) { xr[ps][j] = 0.f; qr[ps][j] = 0.f; }
+      if (tau < p.T) {
+        const int src = DELTA ? tau - 1 : tau;
+        if (src >= 0) {
+          In<InT>::load(kbase + (uint32_t)(src * DK + col), xr[ps]);
+          if (ELU) {
+#pragma unroll
+            for (int j = 0; j < VW; ++j) xr[ps][j] = phi_elu1(xr[ps][j]);
+          }
+        } else if (x0 != nullptr) {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) xr[ps][j] = x0[col + j];
+        }
+        In<InT>::load(qbase + (uint32_t)(tau * DK + col), qr[ps]);
+        if (ELU) {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) qr[ps][j] = phi_elu1(qr[ps][j]);
+        }
+      }
+      float ns = 0.f;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        ns += xr[ps][j] * xr[ps][j];
+        mx = fmaxf(mx, fabsf(xr[ps][j]));
+        mq = fmaxf(mq, fabsf(qr[ps][j]));
+      }
+      ns = group_sum<TPR>(ns);
+      if (tid % TPR == 0) s_norm[t] = ns;
+    }
+    if (Pol::kScaled) {
+      sX = pow2_scale(block_max(mx, s_red));
+      sQ = pow2_scale(block_max(mq, s_red + NW));
+    }
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int t = ps * RPP + tid / TPR;
+      frag_t xo, qo;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        xo[j] = Pol::cvt(xr[ps][j] * sX);
+        qo[j] = Pol::cvt(qr[ps][j] * sQ);
+      }
+      Pol::store_run(Xs + t * LDX, col, xo);
+      Pol::store_run(Qs + t * LDX, col, qo);
+    }
+  }
 
   // Per-channel: eta's denominator uses the channel max of lambda.
   if (DELTA && PC) {
@@ -252,8 +222,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       const int tau = t0 + t;
       float m = 0.f;
       if (tau < p.T && p.lam != nullptr) {
-        const float4 w = *reinterpret_cast<const float4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
-        m = fmaxf(fmaxf(w.x, w.y), fmaxf(w.z, w.w));
+        const f4 w = *reinterpret_cast<const f4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
+        m = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
       }
       m = group_max<TPRL>(m);
       if (tid % TPRL == 0) s_lam[t] = m;
@@ -269,14 +239,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     float eta = 0.f, a = 1.f;
     if (DELTA) {
       const bool hasx = active && (tau >= 1 || has_in);
-      float lam_t = 0.f;
-      if (PC) lam_t = s_lam[t];
-      else if (active && p.lam != nullptr) lam_t = p.lam[rowbase + tau];
-      if (hasx) eta = p.beta[rowbase + tau] / (s_norm[t] + lam_t + p.eps);
+      const float lam_t = PC ? s_lam[t] : g_lam;
+      if (hasx) eta = g_beta / (s_norm[t] + lam_t + p.eps);
       a = 1.f - eta * lam_t;
     } else {
-      if (active) eta = p.beta != nullptr ? p.beta[rowbase + tau] : 1.f;
-      if (active && p.lam != nullptr && !PC) a = p.lam[rowbase + tau];
+      if (active) eta = g_beta;
+      if (active && p.lam != nullptr && !PC) a = g_lam;
     }
     s_eta[t] = eta;
     float la = log_abs_floor(a);
@@ -288,15 +256,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   __syncthreads();
 
   // Operand sources of the two Gram products.
-  const op_t* A_L = Xs;  // rows x_t (scaled), decay applied by mask
+  const op_t* A_L = Xs;  // rows x_t (scaled); scalar decay is applied by the mask
   const op_t* A_M = Qs;
   const op_t* B_X = Xs;
-  float invL = 1.f / (sc.sX * sc.sX);
-  float invM = 1.f / (sc.sQ * sc.sX);
+  float invL = 1.f / (sX * sX);
+  float invM = 1.f / (sQ * sX);
   float* Lf = reinterpret_cast<float*>(reg[2]);
   float* Mf = reinterpret_cast<float*>(reg[3]);
-  float* Tf = reinterpret_cast<float*>(reg[0]);  // after the Gram, X is dead
-  float* Ysc = reinterpret_cast<float*>(reg[1]); // after the Gram, Q is dead
+  float* Tf = reinterpret_cast<float*>(reg[0]);   // after the Gram, X is dead
+  float* Ysc = reinterpret_cast<float*>(reg[1]);  // after the Gram, Q is dead
 
   if (PC) {
     // Column pass, one thread per key channel: Gamma ratios per channel, anchored
@@ -310,6 +278,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     uint64_t par = 0;
     float mAL = 0.f, mBX = 0.f, mAM = 0.f;
     const int i = tid;
+    const int ip = Pol::kpos(i);
     if (i < DK) {
       float gs = 0.f;
       uint32_t pr = 0;
@@ -337,16 +306,16 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         sAM = pow2_scale(block_max(mAM, s_red + 2 * NW));
       }
       if (pass == 1) {
-        invL = 1.f / (sc.sX * sAL * sc.sX * sBX);
-        invM = 1.f / (sc.sQ * sAM * sc.sX * sBX);
+        invL = 1.f / (sX * sAL * sX * sBX);
+        invM = 1.f / (sQ * sAM * sX * sBX);
       }
       if (i < DK) {
         const float anc = gcol[TA];
         const uint32_t apr = (uint32_t)(par >> TA) & 1u;
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-          const float xh = (float)Xs[t * LDX + i];
-          const float qh = (float)Qs[t * LDX + i];
+          const float xh = (float)Xs[t * LDX + ip];
+          const float qh = (float)Qs[t * LDX + ip];
           const float gprev = t ? gcol[t - 1] : 0.f;
           const uint32_t pprev = t ? (uint32_t)(par >> (t - 1)) & 1u : 0u;
           const uint32_t pcur = (uint32_t)(par >> t) & 1u;
@@ -359,9 +328,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
             mBX = fmaxf(mBX, fabsf(vBX));
             mAM = fmaxf(mAM, fabsf(vAM));
           } else {
-            if (DELTA) AL[t * LDX + i] = Pol::cvt(vAL * sAL);
-            BX[t * LDX + i] = Pol::cvt(vBX * sBX);
-            AM[t * LDX + i] = Pol::cvt(vAM * sAM);
+            if (DELTA) AL[t * LDX + ip] = Pol::cvt(vAL * sAL);
+            BX[t * LDX + ip] = Pol::cvt(vBX * sBX);
+            AM[t * LDX + ip] = Pol::cvt(vAM * sAM);
           }
         }
       }
@@ -486,7 +455,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     }
   }
 
-  // Write T (delta) and M, scaled, plus the token scalars, to the record.
+  // Write T (delta) and M, scaled and in operand order, plus the token factors.
   char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
   {
     const int t = tid >> 2, c0 = (tid & 3) * 16;
@@ -504,41 +473,39 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       sT = pow2_scale(block_max(mt_, s_red));
       sM = pow2_scale(block_max(mm_, s_red + NW));
     }
-    using frag_t = typename Pol::frag_t;
-    constexpr int EV = 16 / sizeof(op_t);  // elements per 16-byte vector
-    frag_t* Tg = reinterpret_cast<frag_t*>(reinterpret_cast<op_t*>(rec + RC::kT) + t * CH + c0);
-    frag_t* Mg = reinterpret_cast<frag_t*>(reinterpret_cast<op_t*>(rec + RC::kM) + t * CH + c0);
+    op_t* Tg = reinterpret_cast<op_t*>(rec + RC::kT) + t * CH;
+    op_t* Mg = reinterpret_cast<op_t*>(rec + RC::kM) + t * CH;
 #pragma unroll
-    for (int j = 0; j < 16 / EV; ++j) {
-      frag_t tw, mw;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) {
-        tw[e] = Pol::cvt(tv[j * EV + e] * sT);
-        mw[e] = Pol::cvt(mv[j * EV + e] * sM);
-      }
-      if (DELTA) Tg[j] = tw;
-      Mg[j] = mw;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int k0 = c0 + 4 * r4;
+      if (DELTA)
+        Pol::store4(Tg, k0, tv[4 * r4] * sT, tv[4 * r4 + 1] * sT, tv[4 * r4 + 2] * sT, tv[4 * r4 + 3] * sT);
+      Pol::store4(Mg, k0, mv[4 * r4] * sM, mv[4 * r4 + 1] * sM, mv[4 * r4 + 2] * sM, mv[4 * r4 + 3] * sM);
     }
     if (tid < CH) {
-      // Row factors of the propagate step (see the header comment): with X, Q stored
-      // scaled by sX, sQ,
+      // The row factors of the propagate step: with X, Q stored scaled by sX, sQ,
       //   R = fV V - fP (X S),  O = fO (Q S) + M U,  S' = Gamma_C S + X^T (fU U).
       // Per-channel decay is folded into the operands instead, so only eta and the
       // scales remain.
-      const int t = tid;
-      const float e = s_eta[t];
-      f4 fac;
+      const int tt = tid;
+      const float e = s_eta[tt];
+      float fP, fO, fU;
       if (PC) {
-        fac = f4{e / sc.sX, e, 1.f / sc.sQ, 1.f / sc.sX};
+        fP = e / sX;
+        fO = 1.f / sQ;
+        fU = 1.f / sX;
       } else {
-        const float gprev = t ? s_g[t - 1] : 0.f;
-        const float sprev = t ? s_sg[t - 1] : 1.f;
-        const float gammaPrev = sprev * __expf(gprev);
-        const float gammaT = s_sg[t] * __expf(s_g[t]);
-        const float ratioC = s_sg[CH - 1] * s_sg[t] * __expf(s_g[CH - 1] - s_g[t]);
-        fac = f4{e * gammaPrev / sc.sX, e, gammaT / sc.sQ, ratioC / sc.sX};
+        const float gprev = tt ? s_g[tt - 1] : 0.f;
+        const float sprev = tt ? s_sg[tt - 1] : 1.f;
+        fP = e * (sprev * __expf(gprev)) / sX;
+        fO = (s_sg[tt] * __expf(s_g[tt])) / sQ;
+        fU = (s_sg[CH - 1] * s_sg[tt] * __expf(s_g[CH - 1] - s_g[tt])) / sX;
       }
-      reinterpret_cast<f4*>(rec + RC::kFac)[t] = fac;
+      float* fac = reinterpret_cast<float*>(rec + RC::kFac);
+      fac[tt] = fP;
+      fac[CH + tt] = e;
+      fac[2 * CH + tt] = fO;
+      fac[3 * CH + tt] = fU;
     }
     if (tid == 0) {
       float* scv = reinterpret_cast<float*>(rec + RC::kSc);
@@ -546,8 +513,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       scv[1] = 1.f / sM;
       scv[2] = has_in ? 1.f : 0.f;
       scv[3] = PC ? 1.f : s_sg[CH - 1] * __expf(s_g[CH - 1]);
-      scv[4] = sc.sX;
-      scv[5] = sc.sQ;
+      scv[4] = sX;
+      scv[5] = sQ;
       scv[6] = 0.f;
       scv[7] = 0.f;
     }
@@ -557,13 +524,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   }
 }
 
-// ---------------------------------------------------------------- propagate kernel
-template <typename InT, int DK, bool PC>
+// ================================================================ propagate kernel
+template <typename InT, int DK>
 struct PropLds {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   static constexpr int LDX = DK + Pol::kPad;  // [CH][DK] operands
-  static constexpr int LDT = CH + Pol::kPad;  // [DK][CH] transposed operand (fp16 policy)
+  // [DK][CH] transposed operand (fp16 policy). A stride of 34 dwords puts the
+  // 4-byte token-pair writes of 8-channel groups in distinct banks.
+  static constexpr int LDT = CH + 4;
   static constexpr int LDC = CH + Pol::kPad;  // [CH][CH] operands
   static constexpr int LDV = 64 + 4;          // [CH][64] fp32 value tile
   static constexpr size_t kX = (size_t)CH * LDX * sizeof(op_t);
@@ -580,19 +549,27 @@ struct PropLds {
   static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 4 * NW + 16);
 };
 
-template <typename InT, int DK, bool DELTA, bool PC>
+template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
 __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
-  using L = PropLds<InT, DK, PC>;
+  using L = PropLds<InT, DK>;
   using RC = Rec<InT, DK>;
+  using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDT = L::LDT, LDC = L::LDC, LDV = L::LDV;
   constexpr int KB = Pol::KB;
   constexpr int NKD = DK / KB;  // K blocks over d_k
   constexpr int NKC = CH / KB;  // K blocks over the chunk
   constexpr int NMT = CH / 16;  // row tiles of a chunk
   constexpr int NRT = DK / 16;  // row tiles of S
+  constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
+  constexpr int TPRv = 64 / VW, RPPv = NT / TPRv, NPV = CH / RPPv;      // value tile
+  constexpr int EPT = CH * CH / NT, NVT = EPT * (int)sizeof(op_t) / 16;  // T and M
+  // fp16 policy: x rows are staged by (token pair, 8-channel group) tasks so that the
+  // transposed copy XU is written as 4-byte token pairs.
+  constexpr int NXT = Pol::kScaled ? (CH / 2) * (DK / 8) / NT : 0;  // tasks per thread
+  constexpr int NPX = Pol::kScaled ? 2 * NXT : NPASS;
 
   __shared__ __align__(16) char smem[L::kBytes];
   op_t* Xs = reinterpret_cast<op_t*>(smem + L::oX);
@@ -601,13 +578,13 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   op_t* Ts = reinterpret_cast<op_t*>(smem + L::oT);
   op_t* Ms = reinterpret_cast<op_t*>(smem + L::oM);
   float* Vs = reinterpret_cast<float*>(smem + L::oV);
-  float* s_fP = reinterpret_cast<float*>(smem + L::oS);
-  float* s_fV = s_fP + CH;
-  float* s_fO = s_fV + CH;
-  float* s_fU = s_fO + CH;
-  float* s_misc = s_fU + CH;   // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
-  float* s_gC = s_misc + CH;   // [DK] per-channel Gamma_C
-  float* s_red = s_gC + DK;
+  float* s_fac = reinterpret_cast<float*>(smem + L::oS);  // [4][CH]: fP, fV, fO, fU
+  float* s_misc = s_fac + 4 * CH;  // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
+  float* s_gC = s_misc + CH;       // [DK] per-channel Gamma_C
+  const float* s_fP = s_fac;
+  const float* s_fV = s_fac + CH;
+  const float* s_fO = s_fac + 2 * CH;
+  const float* s_fU = s_fac + 3 * CH;
 
   // Workgroup -> (head, column group); the groups of one head share an XCD (and
   // its L2), since consecutive workgroups are dealt round-robin over the 8 XCDs.
@@ -625,6 +602,13 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   const int dv = p.dv;
   const size_t rowbase = (size_t)bh * p.T;
   const bool out_bf16 = (p.flags & kFlagOutBf16) != 0;
+  // per-head base pointers; every per-thread offset below fits in 32 bits
+  const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
+  const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
+  const InT* vbase = static_cast<const InT*>(p.v) + rowbase * dv + grp * 64;
+  float* obase32 = static_cast<float*>(p.out) + rowbase * dv + grp * 64;
+  uint16_t* obase16 = static_cast<uint16_t*>(p.out) + rowbase * dv + grp * 64;
+  const uint32_t olane = (uint32_t)(4 * g * dv + wave * 16 + n);  // lane's part of the offset
 
   f4 s[NRT];
 #pragma unroll
@@ -642,21 +626,12 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   const bool has_in = reinterpret_cast<const float*>(rec0 + RC::kSc)[2] != 0.f;
   const float* x0 = (DELTA && has_in) ? reinterpret_cast<const float*>(rec0 + RC::kX0) : nullptr;
 
-  // ---- software pipeline: the next chunk's global data is loaded into registers
-  // while the current chunk computes; staging then only writes LDS.
-  using Rw = Rows<InT, DK>;
-  constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
-  constexpr int TPRv = 64 / VW, RPPv = NT / TPRv, NPV = CH / RPPv;  // value tile
-  constexpr int EPT = CH * CH / NT, NVT = EPT * (int)sizeof(op_t) / 16;  // T and M
-  const InT* kp = static_cast<const InT*>(p.k);
-  const InT* qp = static_cast<const InT*>(p.q);
-  const InT* vp = static_cast<const InT*>(p.v);
-  const bool elu = (p.flags & kFlagPhiElu1) != 0;
-  const int col = (tid % TPR) * VW;           // row staging: this thread's columns
-  const int vcol = (tid % TPRv) * VW;         // value tile: this thread's columns
-  const int e0 = tid * EPT;                   // T / M: this thread's elements
-  u32x4 px[NPASS], pq[NPASS], pv[NPV], pt[NVT], pm[NVT];
+  const int col = (tid % TPR) * VW;    // row staging: this thread's columns
+  const int vcol = (tid % TPRv) * VW;  // value tile: this thread's columns
+  const int e0 = tid * EPT;            // T / M: this thread's elements
+  u32x4 px[NPX], pq[NPASS], pv[NPV], pt[NVT], pm[NVT];
   f4 pf = {0.f, 0.f, 0.f, 0.f};
+  float psX = 1.f, psQ = 1.f, pinvT = 1.f, pinvM = 1.f, pgC = 1.f;
   uint32_t valid = 0;
 
   // Iteration c stages chunk c from registers, then issues the loads of chunk c+1
@@ -665,105 +640,163 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
     const int t0 = c * CH;
     if (c >= 0) {
       // ---- registers -> LDS (chunk c)
-        const float* scv = reinterpret_cast<const float*>(rec0 + (size_t)c * RC::kBytes + RC::kSc);
-        const float sX = scv[4], sQ = scv[5];
-    #pragma unroll
+      if constexpr (Pol::kScaled) {
+#pragma unroll
+        for (int r = 0; r < NXT; ++r) {
+          const int task = tid + NT * r;
+          const int cg = (task & 3) + 4 * (task >> 7), tp = (task >> 2) & 31;
+          frag_t xo[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = 2 * tp + h;
+            float x[VW];
+            In<InT>::decode(px[2 * r + h], x);
+            if (DELTA && t0 + t == 0) {
+#pragma unroll
+              for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[8 * cg + j] : 0.f;
+            } else if (ELU && (valid >> (2 * r + h) & 1u)) {
+#pragma unroll
+              for (int j = 0; j < VW; ++j) x[j] = phi_elu1(x[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < VW; ++j) xo[h][j] = Pol::cvt(x[j] * psX);
+            Pol::store_run(Xs + t * LDX, 8 * cg, xo[h]);
+          }
+          if (!PC) {
+            const int tp2 = Pol::kpos(2 * tp);  // tokens 2tp, 2tp+1 are adjacent
+#pragma unroll
+            for (int j = 0; j < VW; ++j)
+              *reinterpret_cast<h2*>(XU + (8 * cg + j) * LDT + tp2) = h2{xo[0][j], xo[1][j]};
+          }
+        }
+      } else {
+#pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
           const int t = ps * RPP + tid / TPR;
-          float x[VW], qv[VW];
+          float x[VW];
           In<InT>::decode(px[ps], x);
-          In<InT>::decode(pq[ps], qv);
           if (DELTA && t0 + t == 0) {
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[col + j] : 0.f;
-          } else if (elu && (valid >> ps & 1u)) {
-    #pragma unroll
+          } else if (ELU && (valid >> ps & 1u)) {
+#pragma unroll
             for (int j = 0; j < VW; ++j) x[j] = phi_elu1(x[j]);
           }
-          if (elu && (valid >> (16 + ps) & 1u)) {
-    #pragma unroll
-            for (int j = 0; j < VW; ++j) qv[j] = phi_elu1(qv[j]);
-          }
-          frag_t xo, qo;  // VW operands = 16 bytes
-    #pragma unroll
-          for (int j = 0; j < VW; ++j) {
-            xo[j] = Pol::cvt(x[j] * sX);
-            qo[j] = Pol::cvt(qv[j] * sQ);
-          }
-          *reinterpret_cast<frag_t*>(Xs + t * LDX + col) = xo;
-          *reinterpret_cast<frag_t*>(Qs + t * LDX + col) = qo;
-          if (!PC) {
-            if constexpr (Pol::kScaled) {
-    #pragma unroll
-              for (int j = 0; j < VW; ++j) XU[(col + j) * LDT + t] = xo[j];
-            } else {
-              *reinterpret_cast<frag_t*>(XU + t * LDX + col) = xo;
-            }
-          }
+          frag_t xo;
+#pragma unroll
+          for (int j = 0; j < VW; ++j) xo[j] = Pol::cvt(x[j] * psX);
+          Pol::store_run(Xs + t * LDX, col, xo);
+          if (!PC) Pol::store_run(XU + t * LDX, col, xo);
         }
-    #pragma unroll
-        for (int ps = 0; ps < NPV; ++ps) {
-          const int t = ps * RPPv + tid / TPRv;
-          float x[VW];
-          In<InT>::decode(pv[ps], x);
-    #pragma unroll
-          for (int j = 0; j < VW; ++j) Vs[t * LDV + vcol + j] = x[j];
+      }
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        const int t = ps * RPP + tid / TPR;
+        float qv[VW];
+        In<InT>::decode(pq[ps], qv);
+        if (ELU && (valid >> (16 + ps) & 1u)) {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) qv[j] = phi_elu1(qv[j]);
         }
-        const int rr = e0 / CH, cc2 = e0 % CH;
-    #pragma unroll
-        for (int j = 0; j < NVT; ++j) {
-          if (DELTA) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
-          reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
-        }
-        if (tid < CH) {
-          s_fP[tid] = pf[0];
-          s_fV[tid] = pf[1];
-          s_fO[tid] = pf[2];
-          s_fU[tid] = pf[3];
-        }
-        if (tid == 0) {
-          s_misc[0] = scv[3];
-          s_misc[1] = scv[0];
-          s_misc[2] = scv[1];
-        }
+        frag_t qo;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) qo[j] = Pol::cvt(qv[j] * psQ);
+        Pol::store_run(Qs + t * LDX, col, qo);
+      }
+#pragma unroll
+      for (int ps = 0; ps < NPV; ++ps) {
+        const int t = ps * RPPv + tid / TPRv;
+        float x[VW];
+        In<InT>::decode(pv[ps], x);
+#pragma unroll
+        for (int j = 0; j < VW; j += 4)
+          *reinterpret_cast<f4*>(Vs + t * LDV + vcol + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+      }
+      const int rr = e0 / CH, cc2 = e0 % CH;
+#pragma unroll
+      for (int j = 0; j < NVT; ++j) {
+        if (DELTA) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
+        reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
+      }
+      if (tid < CH) {
+        s_fac[tid] = pf[0];
+        s_fac[CH + tid] = pf[1];
+        s_fac[2 * CH + tid] = pf[2];
+        s_fac[3 * CH + tid] = pf[3];
+      }
+      if (tid == 0) {
+        s_misc[0] = pgC;
+        s_misc[1] = pinvT;
+        s_misc[2] = pinvM;
+      }
       __syncthreads();
     }
     if (c + 1 < p.nchunks) {
       // ---- global -> registers (chunk c+1)
-      const int cn = c + 1;
-        const int t0 = cn * CH;
-        const char* rec = rec0 + (size_t)cn * RC::kBytes;
-        valid = 0;
-    #pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-          const int tau = t0 + ps * RPP + tid / TPR;
-          px[ps] = u32x4{0u, 0u, 0u, 0u};
-          pq[ps] = u32x4{0u, 0u, 0u, 0u};
-          if (tau < p.T) {
+      const int tn = t0 + CH;
+      const char* rec = rec0 + (size_t)(c + 1) * RC::kBytes;
+      valid = 0;
+      if constexpr (Pol::kScaled) {
+#pragma unroll
+        for (int r = 0; r < NXT; ++r) {
+          const int task = tid + NT * r;
+          const int cg = (task & 3) + 4 * (task >> 7), tp = (task >> 2) & 31;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int tau = tn + 2 * tp + h;
             const int src = DELTA ? tau - 1 : tau;
-            if (src >= 0) {
-              px[ps] = *reinterpret_cast<const u32x4*>(kp + (rowbase + src) * DK + col);
-              valid |= 1u << ps;
+            px[2 * r + h] = u32x4{0u, 0u, 0u, 0u};
+            if (tau < p.T && src >= 0) {
+              px[2 * r + h] = ld16(kbase, (uint32_t)(src * DK + 8 * cg) * (uint32_t)sizeof(InT));
+              valid |= 1u << (2 * r + h);
             }
-            pq[ps] = *reinterpret_cast<const u32x4*>(qp + (rowbase + tau) * DK + col);
-            valid |= 1u << (16 + ps);
           }
         }
-    #pragma unroll
-        for (int ps = 0; ps < NPV; ++ps) {
-          const int tau = t0 + ps * RPPv + tid / TPRv;
-          pv[ps] = u32x4{0u, 0u, 0u, 0u};
-          if (tau < p.T && grp * 64 + vcol < dv)
-            pv[ps] = *reinterpret_cast<const u32x4*>(vp + (rowbase + tau) * dv + grp * 64 + vcol);
+      } else {
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          const int tau = tn + ps * RPP + tid / TPR;
+          const int src = DELTA ? tau - 1 : tau;
+          px[ps] = u32x4{0u, 0u, 0u, 0u};
+          if (tau < p.T && src >= 0) {
+            px[ps] = ld16(kbase, (uint32_t)(src * DK + col) * (uint32_t)sizeof(InT));
+            valid |= 1u << ps;
+          }
         }
-        const u32x4* Tg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kT) + e0);
-        const u32x4* Mg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kM) + e0);
-    #pragma unroll
-        for (int j = 0; j < NVT; ++j) {
-          if (DELTA) pt[j] = Tg[j];
-          pm[j] = Mg[j];
+      }
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        const int tau = tn + ps * RPP + tid / TPR;
+        pq[ps] = u32x4{0u, 0u, 0u, 0u};
+        if (tau < p.T) {
+          pq[ps] = ld16(qbase, (uint32_t)(tau * DK + col) * (uint32_t)sizeof(InT));
+          valid |= 1u << (16 + ps);
         }
-        if (tid < CH) pf = reinterpret_cast<const f4*>(rec + RC::kFac)[tid];
+      }
+#pragma unroll
+      for (int ps = 0; ps < NPV; ++ps) {
+        const int tau = tn + ps * RPPv + tid / TPRv;
+        pv[ps] = u32x4{0u, 0u, 0u, 0u};
+        if (tau < p.T && grp * 64 + vcol < dv)
+          pv[ps] = ld16(vbase, (uint32_t)(tau * dv + vcol) * (uint32_t)sizeof(InT));
+      }
+      const u32x4* Tg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kT) + e0);
+      const u32x4* Mg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kM) + e0);
+#pragma unroll
+      for (int j = 0; j < NVT; ++j) {
+        if (DELTA) pt[j] = Tg[j];
+        pm[j] = Mg[j];
+      }
+      if (tid < CH) {
+        const float* fac = reinterpret_cast<const float*>(rec + RC::kFac);
+        pf = f4{fac[tid], fac[CH + tid], fac[2 * CH + tid], fac[3 * CH + tid]};
+      }
+      const float* scv = reinterpret_cast<const float*>(rec + RC::kSc);
+      pinvT = scv[0];
+      pinvM = scv[1];
+      pgC = scv[3];
+      psX = scv[4];
+      psQ = scv[5];
     }
     if (c < 0) continue;
 
@@ -771,6 +804,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       // per-channel decay folded into the operands: X*Gamma_prev, Q*Gamma, X*Gamma_C/Gamma
       const int i = tid;
       if (i < DK) {
+        const int ip = Pol::kpos(i);
         float gcol[CH];
         uint64_t par = 0;
         float gsum = 0.f;
@@ -796,11 +830,11 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           const float fprev = (pprev ? -1.f : 1.f) * __expf(t ? gcol[t - 1] : 0.f);
           const float fcur = (pcur ? -1.f : 1.f) * __expf(gcol[t]);
           const float fend = ((pC ^ pcur) ? -1.f : 1.f) * __expf(gC - gcol[t]);
-          const float xh = (float)Xs[t * LDX + i];
-          if constexpr (Pol::kScaled) XU[i * LDT + t] = Pol::cvt(xh * fend);
+          const float xh = (float)Xs[t * LDX + ip];
+          if constexpr (Pol::kScaled) XU[i * LDT + Pol::kpos(t)] = Pol::cvt(xh * fend);
           else XU[t * LDX + i] = Pol::cvt(xh * fend);
-          Xs[t * LDX + i] = Pol::cvt(xh * fprev);
-          Qs[t * LDX + i] = Pol::cvt((float)Qs[t * LDX + i] * fcur);
+          Xs[t * LDX + ip] = Pol::cvt(xh * fprev);
+          Qs[t * LDX + ip] = Pol::cvt((float)Qs[t * LDX + ip] * fcur);
         }
       }
       __syncthreads();
@@ -808,14 +842,16 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 
     if (wave_on) {
       const float invT = s_misc[1], invM = s_misc[2];
-      // S as the B operand of X S and Q S
+      // row factors of the lane's rows: 4 consecutive rows per tile
+      auto fac4 = [&](const float* f, int mt) { return *reinterpret_cast<const f4*>(f + 16 * mt + 4 * g); };
+      // S as the B operand of X S and Q S (one power-of-two scale per column)
       float ms = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) ms = fmaxf(ms, fabsf(s[rt][ii]));
-      const float sS = Pol::kScaled ? pow2_scale(wave_max(ms)) : 1.f;
-      const float isS = 1.f / sS;
+      float sS = 1.f, isS = 1.f;
+      if (Pol::kScaled) pow2_scale2(col_max(ms), sS, isS);
       frag_t Sf[NKD];
 #pragma unroll
       for (int kb = 0; kb < NKD; ++kb) Sf[kb] = Pol::from_c(s, kb, sS);
@@ -836,15 +872,17 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * mt + 4 * g + ii;
-            const float r = s_fV[t] * Vs[t * LDV + wave * 16 + n] - s_fP[t] * isS * P[mt][ii];
+            const float r = fac4(s_fV, mt)[ii] * Vs[t * LDV + wave * 16 + n] -
+                            fac4(s_fP, mt)[ii] * isS * P[mt][ii];
             P[mt][ii] = r;
             mr = fmaxf(mr, fabsf(r));
           }
-        const float sR = Pol::kScaled ? pow2_scale(wave_max(mr)) : 1.f;
+        float sR = 1.f, isR = 1.f;
+        if (Pol::kScaled) pow2_scale2(col_max(mr), sR, isR);
         frag_t Rf[NKC];
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb) Rf[kb] = Pol::from_c(P, kb, sR);
-        const float fu = invT / sR;
+        const float fu = invT * isR;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
           f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -860,7 +898,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * mt + 4 * g + ii;
-            U[mt][ii] = s_fV[t] * Vs[t * LDV + wave * 16 + n];
+            U[mt][ii] = fac4(s_fV, mt)[ii] * Vs[t * LDV + wave * 16 + n];
           }
       }
 
@@ -872,20 +910,20 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
         const op_t* arow = Qs + (16 * mt + n) * LDX;
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) Pol::mma(O[mt], Pol::lds_row(arow, kb, g), Sf[kb]);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) O[mt][ii] *= s_fO[16 * mt + 4 * g + ii] * isS;
+        O[mt] *= fac4(s_fO, mt) * isS;
       }
       float mu = 0.f;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) mu = fmaxf(mu, fabsf(U[mt][ii]));
-      const float sU = Pol::kScaled ? pow2_scale(wave_max(mu)) : 1.f;
+      float sU = 1.f, isU = 1.f;
+      if (Pol::kScaled) pow2_scale2(col_max(mu), sU, isU);
       {
         frag_t Uf[NKC];
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb) Uf[kb] = Pol::from_c(U, kb, sU);
-        const float fm = invM / sU;
+        const float fm = invM * isU;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
           f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -901,25 +939,24 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int tau = t0 + 16 * mt + 4 * g + ii;
-          if (tau < p.T) {
-            const size_t o = (rowbase + tau) * dv + c0 + n;
-            if (out_bf16) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(O[mt][ii]);
-            else static_cast<float*>(p.out)[o] = O[mt][ii];
+          const int trow = t0 + 16 * mt + ii;  // uniform part of the row
+          if (trow + 4 * g < p.T) {
+            const uint32_t o = (uint32_t)(trow * dv) + olane;
+            if (out_bf16) obase16[o] = f32_to_bf16_bits(O[mt][ii]);
+            else obase32[o] = O[mt][ii];
           }
         }
 
       // S' = Gamma_C S + X^T (diag(Gamma_C/Gamma) U)
       float mut = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt) {
+        U[mt] *= fac4(s_fU, mt);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          U[mt][ii] *= s_fU[16 * mt + 4 * g + ii];
-          mut = fmaxf(mut, fabsf(U[mt][ii]));
-        }
-      const float sUt = Pol::kScaled ? pow2_scale(wave_max(mut)) : 1.f;
-      const float iUt = 1.f / sUt;
+        for (int ii = 0; ii < 4; ++ii) mut = fmaxf(mut, fabsf(U[mt][ii]));
+      }
+      float sUt = 1.f, iUt = 1.f;
+      if (Pol::kScaled) pow2_scale2(col_max(mut), sUt, iUt);
       frag_t Utf[NKC];
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb) Utf[kb] = Pol::from_c(U, kb, sUt);
@@ -934,10 +971,11 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           else a = PolF32::lds_col(XU, LDX, 16 * rt + n, kb, g);
           Pol::mma(acc, a, Utf[kb]);
         }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float gc = PC ? s_gC[16 * rt + 4 * g + ii] : gCs;
-          s[rt][ii] = gc * s[rt][ii] + acc[ii] * iUt;
+        if (PC) {
+          const f4 gc = *reinterpret_cast<const f4*>(s_gC + 16 * rt + 4 * g);
+          s[rt] = gc * s[rt] + acc * iUt;
+        } else {
+          s[rt] = s[rt] * gCs + acc * iUt;
         }
       }
     }
@@ -954,11 +992,9 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           p.S_out[((size_t)bh * DK + 16 * rt + 4 * g + ii) * dv + c0 + n] = s[rt][ii];
     }
     if (grp == 0) {
-      const InT* kp = static_cast<const InT*>(p.k);
-      const bool elu = (p.flags & kFlagPhiElu1) != 0;
       for (int i = tid; i < DK; i += NT) {
-        float x = In<InT>::load1(kp + (rowbase + p.T - 1) * DK + i);
-        if (elu) x = phi_elu1(x);
+        float x = In<InT>::load1(kbase + (uint32_t)((p.T - 1) * DK + i));
+        if (ELU) x = phi_elu1(x);
         p.xprev_out[(size_t)bh * DK + i] = x;
       }
       if (tid == 0) p.has_out[bh] = 1;
@@ -988,29 +1024,35 @@ bool scan_supported(int dk, int dv) {
   return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
-template <typename InT, int DK, bool DELTA, bool PC>
+template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
 static hipError_t launch_scan_t(const ScanParams& p, hipStream_t st, int phases) {
   if (phases & 1) {
     const unsigned nprep = (unsigned)((size_t)p.BH * p.nchunks);
-    hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC>), dim3(nprep), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC, ELU>), dim3(nprep), dim3(NT), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
     const int NG = (p.dv + 63) / 64;
     const unsigned nprop = (unsigned)(8 * NG * ((p.BH + 7) / 8));
-    hipLaunchKernelGGL((prop_kernel<InT, DK, DELTA, PC>), dim3(nprop), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((prop_kernel<InT, DK, DELTA, PC, ELU>), dim3(nprop), dim3(NT), 0, st, p);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <typename InT, int DK, bool DELTA, bool PC>
+static hipError_t launch_scan_e(const ScanParams& p, hipStream_t st, int ph) {
+  return (p.flags & kFlagPhiElu1) ? launch_scan_t<InT, DK, DELTA, PC, true>(p, st, ph)
+                                  : launch_scan_t<InT, DK, DELTA, PC, false>(p, st, ph);
 }
 
 template <typename InT, int DK>
 static hipError_t launch_scan_dk(const ScanParams& p, hipStream_t st, int ph) {
   const bool pc = (p.flags & kFlagPerChannel) != 0;
   if (p.delta)
-    return pc ? launch_scan_t<InT, DK, true, true>(p, st, ph) : launch_scan_t<InT, DK, true, false>(p, st, ph);
-  return pc ? launch_scan_t<InT, DK, false, true>(p, st, ph) : launch_scan_t<InT, DK, false, false>(p, st, ph);
+    return pc ? launch_scan_e<InT, DK, true, true>(p, st, ph) : launch_scan_e<InT, DK, true, false>(p, st, ph);
+  return pc ? launch_scan_e<InT, DK, false, true>(p, st, ph) : launch_scan_e<InT, DK, false, false>(p, st, ph);
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t st, int phases) {
