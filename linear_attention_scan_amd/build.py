@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfwmem.so")
-SOURCES = ["fwmem_api.cpp", "fwmem_scan.hip", "fwmem_step.hip"]
+SOURCES = ["fwmem_api.cpp", "fwmem_scan.hip", "fwmem_scan_split.hip", "fwmem_step.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,6 +24,8 @@ FLAGS = [
     # packed fp32 instructions stay disabled (the compiler would otherwise form
     # v_pk_* fp32 ops from plain float code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (no accumulator-register copies around VALU use)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]

@@ -111,7 +111,7 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
   if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   const size_t BH = (size_t)shape->B * (size_t)shape->H;
   const size_t nchunks = ((size_t)shape->T + kChunk - 1) / kChunk;
-  *bytes = BH * nchunks * fwmem::scan_record_bytes(shape->dtype == FWMEM_BF16, shape->dk);
+  *bytes = BH * nchunks * fwmem::scan_record_bytes(shape->dtype == FWMEM_BF16, shape->dk, mode->flags);
   return FWMEM_OK;
 }
 
@@ -202,6 +202,11 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   p.flags = mode->flags;
   p.eps = mode->eps;
   if (z.BH > 0x7fffffff / 8 || (size_t)p.nchunks * z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
+  // per-head byte offsets of every buffer (inputs, outputs, records) stay below 2^31
+  const size_t dmax = (size_t)(shape->dk > shape->dv ? shape->dk : shape->dv);
+  if (T * dmax * 4 > 0x7fffffffu ||
+      (size_t)p.nchunks * fwmem::scan_record_bytes(p.bf16, shape->dk, p.flags) > 0x7fffffffu)
+    return FWMEM_EUNSUPPORTED;
   const hipError_t e = fwmem::launch_scan(p, hs, phases);
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
 }

@@ -58,7 +58,11 @@ struct StepParams {
 };
 
 // Bytes of one (head, chunk) workspace record.
-size_t scan_record_bytes(int bf16, int dk);
+size_t scan_record_bytes(int bf16, int dk, uint32_t flags);
+// bf16 inputs with the identity feature map and scalar decay take the split-operand
+// propagate kernel (fwmem_scan_split.hip).
+bool scan_split_path(int bf16, uint32_t flags);
+hipError_t launch_prop_split(const ScanParams& p, hipStream_t stream);
 // Whether kernels exist for this size.
 bool scan_supported(int dk, int dv);
 bool step_supported(int dk, int dv);
