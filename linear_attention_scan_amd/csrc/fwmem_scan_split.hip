@@ -16,6 +16,8 @@
 #include "fwmem_internal.h"
 #include "fwmem_split.h"
 
+#include <type_traits>
+
 namespace fwmem {
 namespace {
 
@@ -97,14 +99,14 @@ __device__ __forceinline__ LoadOffs<DK> load_offsets(const Lane& L, int dv, int 
   return o;
 }
 
-// Enqueue the direct loads of chunk c into B (every thread of the workgroup). For the
+// Direct loads of chunk c into B, issued by every thread of the workgroup. For the
 // delta rule the X resource starts one row early (x_t is the key before token t); the
-// row before token 0 is forced out of range and patched from the record later.
+// row before token 0 is forced out of range and patched from the record later. A chunk
+// past the end (c == nchunks) lies wholly outside the ranges and loads zeros.
 template <int DK, bool DELTA>
-__device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c,
-                                            const Lane& L, const LoadOffs<DK>& o, const Srcs& src) {
+__device__ __forceinline__ void issue_xq(SplitBuf<DK, DELTA>& B, int c, const Lane& L, const LoadOffs<DK>& o,
+                                         const Srcs& src) {
   using LO = LoadOffs<DK>;
-  using RC = RecSplit<DK>;
   const uint32_t sx = (uint32_t)(c * CH * DK * 2);
 #pragma unroll
   for (int ii = 0; ii < LO::NXI; ++ii) {
@@ -114,6 +116,13 @@ __device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanPa
     dma16(src.x, xo, sx, &B.x[64 * i]);
     dma16(src.q, o.x[ii], sx, &B.q[64 * i]);
   }
+}
+
+template <int DK, bool DELTA>
+__device__ __forceinline__ void issue_rest(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, const Lane& L,
+                                           const LoadOffs<DK>& o, const Srcs& src) {
+  using LO = LoadOffs<DK>;
+  using RC = RecSplit<DK>;
   const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
   if constexpr (DELTA) {
 #pragma unroll
@@ -138,152 +147,20 @@ __device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanPa
   else if (L.lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
 }
 
-// One chunk for one wave: updates the state slice s and produces the outputs O.
-template <int DK, bool DELTA>
-__device__ __forceinline__ void compute_chunk(const SplitBuf<DK, DELTA>& B, const Lane& L,
-                                              f4 (&s)[DK / 16], f4 (&O)[4]) {
-  using Buf = SplitBuf<DK, DELTA>;
-  constexpr int NGR = Buf::NGR;
-  constexpr int NKD = DK / 32;
-  constexpr int NRT = DK / 16;
-  const int g = L.g, n = L.n;
-
-  auto fac4 = [&](int k, int m) -> f4 {
-    return *reinterpret_cast<const f4*>(&B.fac[k * CH + tok_of(m, 4 * g)]);
-  };
-  auto xfrag = [&](const u32x4* X, int m, int kb) -> bf8 {
-    const int row = tok_of(m, n);
-    return __builtin_bit_cast(bf8, X[row * NGR + ((4 * kb + g) ^ xswz<DK>(row))]);
-  };
-  // X^T fragment: rows d_k tok_of(rt, n), K = tokens 32kb + 8g + s, from the row-major X
-  // tile; each transpose read gives four consecutive K slots.
-  auto xtfrag = [&](int rt, int kb) -> bf8 {
-    s4 h[2];
-    const int dk0 = 32 * (rt >> 1) + 8 * (n & 3) + 4 * (rt & 1);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = 32 * kb + 8 * g + (n >> 2) + 4 * hh;
-      const char* a = reinterpret_cast<const char*>(&B.x[row * NGR + ((dk0 >> 3) ^ xswz<DK>(row))]) +
-                      (dk0 & 7) * 2;
-      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)a);
-    }
-    typedef short s8 __attribute__((ext_vector_type(8)));
-    const s8 r = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-    return __builtin_bit_cast(bf8, r);
-  };
-  auto vval = [&](int m, int i) -> float {
-    const int row = tok_of(m, 4 * g + i);
-    const int vc = L.wave * 16 + n;
-    const uint16_t* vp = reinterpret_cast<const uint16_t*>(&B.v[row * 4 + ((vc >> 3) ^ vswz(row))]);
-    return bf16_bits_to_f32(vp[vc & 7]);
-  };
-
-  bf8 Sh[NKD], Sl[NKD];
-#pragma unroll
-  for (int kb = 0; kb < NKD; ++kb) split_c(s, kb, Sh[kb], Sl[kb]);
-
-  f4 U[4];
-  if constexpr (DELTA) {
-    f4 P[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      P[m] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKD; ++kb) {
-        const bf8 a = xfrag(B.x, m, kb);
-        mma_bf16(P[m], a, Sh[kb]);
-        mma_bf16(P[m], a, Sl[kb]);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f4 fv = fac4(1, m), fp = fac4(0, m);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) P[m][i] = fv[i] * vval(m, i) - fp[i] * P[m][i];
-    }
-    bf8 Rh[2], Rl[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) split_c(P, kb, Rh[kb], Rl[kb]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) U[m] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int f = 0; f < kTriFrags; ++f) {
-      const int m = tri_m(f), kb = tri_kb(f);
-      const bf8 th = __builtin_bit_cast(bf8, B.t[(2 * f) * 64 + L.lane]);
-      const bf8 tl = __builtin_bit_cast(bf8, B.t[(2 * f + 1) * 64 + L.lane]);
-      mma_bf16(U[m], th, Rh[kb]);
-      mma_bf16(U[m], th, Rl[kb]);
-      mma_bf16(U[m], tl, Rh[kb]);
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f4 fv = fac4(1, m);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[m][i] = fv[i] * vval(m, i);
-    }
-  }
-
-  // O = diag(fO) Q S + M U
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKD; ++kb) {
-      const bf8 a = xfrag(B.q, m, kb);
-      mma_bf16(acc, a, Sh[kb]);
-      mma_bf16(acc, a, Sl[kb]);
-    }
-    O[m] = acc * fac4(2, m);
-  }
-  {
-    bf8 Uh[2], Ul[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) split_c(U, kb, Uh[kb], Ul[kb]);
-#pragma unroll
-    for (int f = 0; f < kTriFrags; ++f) {
-      const int m = tri_m(f), kb = tri_kb(f);
-      const bf8 mh = __builtin_bit_cast(bf8, B.m[(2 * f) * 64 + L.lane]);
-      const bf8 ml = __builtin_bit_cast(bf8, B.m[(2 * f + 1) * 64 + L.lane]);
-      mma_bf16(O[m], mh, Uh[kb]);
-      mma_bf16(O[m], mh, Ul[kb]);
-      mma_bf16(O[m], ml, Uh[kb]);
-    }
-  }
-
-  // S' = Gamma_C S + X^T diag(fU) U
-#pragma unroll
-  for (int m = 0; m < 4; ++m) U[m] *= fac4(3, m);
-  bf8 Wh[2], Wl[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) split_c(U, kb, Wh[kb], Wl[kb]);
-  const float gC = B.fac[4 * CH];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    f4 acc = s[rt] * gC;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf8 a = xtfrag(rt, kb);
-      mma_bf16(acc, a, Wh[kb]);
-      mma_bf16(acc, a, Wl[kb]);
-    }
-    s[rt] = acc;
-  }
-}
-
-// Outputs of chunk c: lane rows tok_of(m, 4g+i) of column col, through a buffer resource
-// over the head's output rows (stores past the sequence end fall outside its range).
-template <bool BF>
-__device__ __forceinline__ void store_rows(int dv, const f4 (&O)[4], int c, __amdgpu_buffer_rsrc_t ro,
-                                           uint32_t olofs) {
-  constexpr uint32_t es = BF ? 2u : 4u;
+// Outputs of chunk c (c may be -1: nothing is stored): lane rows tok_of(m, 4g+i) of its
+// column, through a buffer resource over the head's output rows, so rows past the
+// sequence end fall outside its range.
+template <bool OBF>
+__device__ __forceinline__ void store_out(int dv, const f4 (&O)[4], int c, __amdgpu_buffer_rsrc_t ro,
+                                          uint32_t olofs) {
+  constexpr uint32_t es = OBF ? 2u : 4u;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = c * CH + 32 * (m >> 1) + 4 * (m & 1) + i;  // uniform part of the row
-      const uint32_t so = (uint32_t)(r * dv) * es;
-      if constexpr (BF) {
+      const uint32_t so = c >= 0 ? (uint32_t)(r * dv) * es : 0x80000000u;
+      if constexpr (OBF) {
         const __bf16 h = (__bf16)O[m][i];
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ro, olofs * es, so, 0);
       } else {
@@ -292,36 +169,379 @@ __device__ __forceinline__ void store_rows(int dv, const f4 (&O)[4], int c, __am
     }
 }
 
-__device__ __forceinline__ void store_out(const ScanParams& p, const f4 (&O)[4], int c,
-                                          __amdgpu_buffer_rsrc_t ro, uint32_t olofs) {
-  if ((p.flags & kFlagOutBf16) != 0) store_rows<true>(p.dv, O, c, ro, olofs);
-  else store_rows<false>(p.dv, O, c, ro, olofs);
+// ---------------------------------------------------------------- chunk step
+// Scheduling. A single wave issues in order, so its matrix unit and its VALU only run
+// at the same time if the instruction stream alternates between them. The chunk is
+// therefore written as a sequence of micro-regions fenced by sched_barrier: each holds
+// one MFMA plus a fixed share of the independent work (operand splits, row factors,
+// LDS reads for later MFMAs, the next chunk's direct loads, the previous chunk's output
+// stores), in the order given here.
+#define FW_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// hi/lo split of two fp32 values into one packed bf16 word each
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf2 h = {(__bf16)x0, (__bf16)x1};
+  const uint32_t w = __builtin_bit_cast(uint32_t, h);
+  const bf2 l = {(__bf16)(x0 - __uint_as_float(w << 16)), (__bf16)(x1 - __uint_as_float(w & 0xffff0000u))};
+  hi = w;
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Word j (slots 2j, 2j+1) of the B fragment of K block kb from C tiles c[2kb], c[2kb+1],
+// each value times f (the row factor of its tile row).
+template <int KB, int J>
+__device__ __forceinline__ void split_word(const f4* c, u32x4& hi, u32x4& lo) {
+  constexpr int t = 2 * KB + (J >> 1), r = 2 * (J & 1);
+  uint32_t h, l;
+  split2(c[t][r], c[t][r + 1], h, l);
+  hi[J] = h;
+  lo[J] = l;
+}
+template <int KB, int J>
+__device__ __forceinline__ void split_word_scaled(const f4* c, const f4* f, u32x4& hi, u32x4& lo) {
+  constexpr int t = 2 * KB + (J >> 1), r = 2 * (J & 1);
+  uint32_t h, l;
+  split2(c[t][r] * f[t][r], c[t][r + 1] * f[t][r + 1], h, l);
+  hi[J] = h;
+  lo[J] = l;
+}
+
+__device__ __forceinline__ void mma_w(f4& acc, const bf8& a, const u32x4& b) {
+  mma_bf16(acc, a, __builtin_bit_cast(bf8, b));
+}
+
+// The K-th direct load of this wave for chunk c: X and Q rows alternately.
+template <int DK, bool DELTA, int K>
+__device__ __forceinline__ void dma_xq_op(SplitBuf<DK, DELTA>& B, int c, const Lane& L, const LoadOffs<DK>& o,
+                                          const Srcs& src) {
+  constexpr int ii = K >> 1;
+  const int i = ii * kSplitWaves + L.wave;
+  const uint32_t sx = (uint32_t)(c * CH * DK * 2);
+  if constexpr ((K & 1) == 0) {
+    uint32_t xo = o.x[ii];
+    if (DELTA && c == 0 && 64 * i + L.lane < LoadOffs<DK>::NGR) xo = 0x80000000u;  // row 0 of chunk 0
+    dma16(src.x, xo, sx, &B.x[64 * i]);
+  } else {
+    dma16(src.q, o.x[ii], sx, &B.q[64 * i]);
+  }
+}
+
+// The K-th of the other direct loads: T fragments (delta rule), M fragments, value
+// rows, row factors.
+template <int DK, bool DELTA, int K>
+__device__ __forceinline__ void dma_rest_op(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, const Lane& L,
+                                            const LoadOffs<DK>& o, const Srcs& src) {
+  using RC = RecSplit<DK>;
+  constexpr int NT = DELTA ? kTriFrags : 0;  // per wave: 2 * kTriFrags / kSplitWaves
+  constexpr int NMF = kTriFrags;
+  const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
+  if constexpr (K < NT) {
+    const int j = K * kSplitWaves + L.wave;
+    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kT + j * 1024), &B.t[64 * j]);
+  } else if constexpr (K < NT + NMF) {
+    const int j = (K - NT) * kSplitWaves + L.wave;
+    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kM + j * 1024), &B.m[64 * j]);
+  } else if constexpr (K < NT + NMF + LoadOffs<DK>::NVI) {
+    constexpr int ii = K - NT - NMF;
+    const int i = ii * kSplitWaves + L.wave;
+    dma16(src.v, o.v[ii], (uint32_t)(c * CH * p.dv * 2), &B.v[64 * i]);
+  } else if constexpr (K == NT + NMF + LoadOffs<DK>::NVI) {
+    if (L.wave == 0) dma16(src.w, o.lane16, sw + (uint32_t)RC::kFac, &B.fac[0]);
+    else if (L.lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
+  }
+}
 template <int DK, bool DELTA>
-__device__ __forceinline__ void run_chunk(SplitBuf<DK, DELTA>& cur, SplitBuf<DK, DELTA>& nxt,
-                                          const ScanParams& p, int c, const Lane& L, f4 (&s)[DK / 16],
-                                          f4 (&O)[4], const LoadOffs<DK>& lo, const Srcs& src,
-                                          const char* rec0, __amdgpu_buffer_rsrc_t ro, uint32_t olofs) {
-  // this chunk's loads (and the previous chunk's output stores) have completed in
-  // every wave once all waves pass the barrier; the other buffer is free again
+constexpr int kRestOps = (DELTA ? kTriFrags : 0) + kTriFrags + LoadOffs<DK>::NVI + 1;
+
+// The K-th output store of chunk c (K = 4m + i: row tok_of(m, 4g+i)); c = -1 stores nothing.
+template <bool OBF, int K>
+__device__ __forceinline__ void store_op(int dv, const f4 (&O)[4], int c, __amdgpu_buffer_rsrc_t ro,
+                                         uint32_t olofs) {
+  constexpr int m = K >> 2, i = K & 3;
+  constexpr uint32_t es = OBF ? 2u : 4u;
+  const int r = c * CH + 32 * (m >> 1) + 4 * (m & 1) + i;
+  const uint32_t so = c >= 0 ? (uint32_t)(r * dv) * es : 0x80000000u;
+  if constexpr (OBF) {
+    const __bf16 h = (__bf16)O[m][i];
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ro, olofs * es, so, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m][i]), ro, olofs * es, so, 0);
+  }
+}
+
+// Even share [lo, hi) of N items for slot I of S slots.
+template <int N, int S, int I>
+struct Share {
+  static constexpr int lo = N * I / S, hi = N * (I + 1) / S;
+};
+
+// One chunk for one wave: waits for chunk c in B, enqueues chunk c+1 into N, stores the
+// outputs of chunk c-1 (held in O), updates the state slice s and leaves chunk c's
+// outputs in O.
+template <int DK, bool DELTA, bool OBF>
+__device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N, const ScanParams& p,
+                                           int c, const Lane& L, f4 (&s)[DK / 16], f4 (&O)[4],
+                                           const LoadOffs<DK>& lo, const Srcs& src, const char* rec0,
+                                           __amdgpu_buffer_rsrc_t ro, uint32_t olofs) {
+  using Buf = SplitBuf<DK, DELTA>;
+  constexpr int NGR = Buf::NGR;
+  constexpr int NKD = DK / 32;       // K blocks over d_k
+  constexpr int NRT = DK / 16;       // row tiles of S
+  constexpr int NKH = NKD / 2;       // K blocks of the first half of Q S
+  constexpr int NRH = NRT / 2;
+  constexpr int NXQ = 2 * LoadOffs<DK>::NXI;  // X and Q direct loads of this wave
+  constexpr int NREST = kRestOps<DK, DELTA>;
+  const int g = L.g, n = L.n;
+
+  // this chunk's loads (and older output stores) are complete in every wave once all
+  // waves pass the barrier; the other buffer is free again
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (DELTA && c == 0) {
-    // x_0 is the carried key (zero without one): overwrite row 0 of the first X tile
-    constexpr int NGR = SplitBuf<DK, DELTA>::NGR;
+    // x_0 is the carried key (zero without one): row 0 of the first X tile
     if (threadIdx.x < NGR) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(rec0 + RecSplit<DK>::kX0 + 16 * threadIdx.x);
-      cur.x[threadIdx.x ^ xswz<DK>(0)] = w;
+      B.x[threadIdx.x ^ xswz<DK>(0)] = w;
     }
     __syncthreads();
   }
-  if (c + 1 < p.nchunks) issue_chunk<DK, DELTA>(nxt, p, c + 1, L, lo, src);
-  if (c > 0) store_out(p, O, c - 1, ro, olofs);
-  compute_chunk<DK, DELTA>(cur, L, s, O);
+
+  auto fac4 = [&](int k, int m) -> f4 {
+    return *reinterpret_cast<const f4*>(&B.fac[k * CH + tok_of(m, 4 * g)]);
+  };
+  auto xfrag = [&](const u32x4* X, int m, int kb) -> bf8 {
+    const int row = tok_of(m, n);
+    return __builtin_bit_cast(bf8, X[row * NGR + ((4 * kb + g) ^ xswz<DK>(row))]);
+  };
+  // Half hh of the X^T fragment (rt, kb): rows d_k tok_of(rt, n), K slots 4hh..4hh+3 =
+  // tokens 32kb + 8g + 4hh + j, by one transpose read of the row-major X tile.
+  auto xthalf = [&](int rt, int kb, int hh) -> s4 {
+    const int dk0 = 32 * (rt >> 1) + 8 * (n & 3) + 4 * (rt & 1);
+    const int row = 32 * kb + 8 * g + (n >> 2) + 4 * hh;
+    const char* a = reinterpret_cast<const char*>(&B.x[row * NGR + ((dk0 >> 3) ^ xswz<DK>(row))]) +
+                    (dk0 & 7) * 2;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)a);
+  };
+  auto xtjoin = [](const s4& a, const s4& b) -> bf8 {
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    const s8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf8, r);
+  };
+  // Values of the lane's four rows tok_of(m, 4g+i), i = 0..3 (consecutive tokens), in its
+  // column: one transpose read, in which lane 4i+q of the group supplies columns
+  // 4q..4q+3 of token row i.
+  auto vrows = [&](int m) -> s4 {
+    const int row = tok_of(m, 4 * g) + (n >> 2);
+    const int c0 = L.wave * 16 + 4 * (n & 3);
+    const char* a = reinterpret_cast<const char*>(&B.v[row * 4 + ((c0 >> 3) ^ vswz(row))]) + (c0 & 7) * 2;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)a);
+  };
+  auto vf = [](const s4& h, int i) { return bf16_bits_to_f32((uint32_t)(uint16_t)h[i]); };
+  auto tfrag = [&](const u32x4* T, int f, int part) -> bf8 {
+    return __builtin_bit_cast(bf8, T[(2 * f + part) * 64 + L.lane]);
+  };
+
+  // ---- A: X fragments, value rows and their factors; split of S's first K block
+  bf8 xf[4][NKD];
+#pragma unroll
+  for (int kb = 0; kb < NKD; ++kb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xf[m][kb] = xfrag(B.x, m, kb);
+  s4 vv[4];
+  f4 fvr[4], fpr[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    vv[m] = vrows(m);
+    fvr[m] = fac4(1, m);
+    if (DELTA) fpr[m] = fac4(0, m);
+  }
+  u32x4 Sh[NKD], Sl[NKD];
+  static_for<0, 4>([&](auto J) { split_word<0, J>(s, Sh[0], Sl[0]); });
+  FW_FENCE();
+
+  // ---- B: P = X S (8 NKD MFMAs; the additive rule has none and keeps only the side
+  // work). Alongside: the split of S's K blocks 1.., the next chunk's X and Q loads, the
+  // previous chunk's output stores, the first half of the Q fragments.
+  f4 P[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) P[m] = f4{0.f, 0.f, 0.f, 0.f};
+  bf8 qf[4][NKD];
+  constexpr int NB = 8 * NKD;
+  static_for<0, NB>([&](auto I) {
+    constexpr int i = I, kb = i / 8, m = (i % 8) / 2, part = i % 2;
+    if constexpr (DELTA) mma_w(P[m], xf[m][kb], part ? Sl[kb] : Sh[kb]);
+    FW_FENCE();
+    if constexpr (kb + 1 < NKD && part == 0) split_word<kb + 1, m>(s, Sh[kb + 1], Sl[kb + 1]);
+    static_for<Share<NXQ + 16, NB, i>::lo, Share<NXQ + 16, NB, i>::hi>([&](auto K) {
+      if constexpr (K < NXQ) dma_xq_op<DK, DELTA, K>(N, c + 1, L, lo, src);
+      else store_op<OBF, K - NXQ>(p.dv, O, c - 1, ro, olofs);
+    });
+    static_for<Share<4 * NKH, NB, i>::lo, Share<4 * NKH, NB, i>::hi>([&](auto K) {
+      qf[K % 4][K / 4] = xfrag(B.q, K % 4, K / 4);
+    });
+    FW_FENCE();
+  });
+
+  // ---- C: first half of Q S. Alongside: R = fV V - fP P and its split (delta rule) or
+  // U = fV V (additive); the second half of the Q fragments and the T fragments.
+  f4 Oq[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) Oq[m] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 U[4];
+  u32x4 Rh[2], Rl[2];
+  bf8 th[kTriFrags], tl[kTriFrags];
+  constexpr int NC = 8 * NKH;
+  // side work items: 16 row values (4 per tile) interleaved with the 8 split words, in
+  // dependency order (tiles 0,1 -> words of K block 0 -> tiles 2,3 -> words of block 1)
+  constexpr int NCV = DELTA ? 24 : 16;
+  constexpr int NCD = 4 * (NKD - NKH) + (DELTA ? 2 * kTriFrags : 0);
+  static_for<0, NC>([&](auto I) {
+    constexpr int i = I, kb = i / 8, m = (i % 8) / 2, part = i % 2;
+    mma_w(Oq[m], qf[m][kb], part ? Sl[kb] : Sh[kb]);
+    FW_FENCE();
+    static_for<Share<NCV, NC, i>::lo, Share<NCV, NC, i>::hi>([&](auto K) {
+      constexpr int k = K;
+      if constexpr (DELTA) {
+        constexpr int grp = k / 12, w = k % 12;  // 12 items per K block: 8 values, 4 words
+        if constexpr (w < 8) {
+          constexpr int t = 2 * grp + w / 4, r = w % 4;
+          P[t][r] = fvr[t][r] * vf(vv[t], r) - fpr[t][r] * P[t][r];
+        } else {
+          split_word<grp, w - 8>(P, Rh[grp], Rl[grp]);
+        }
+      } else {
+        constexpr int t = k / 4, r = k % 4;
+        U[t][r] = fvr[t][r] * vf(vv[t], r);
+      }
+    });
+    static_for<Share<NCD, NC, i>::lo, Share<NCD, NC, i>::hi>([&](auto K) {
+      constexpr int k = K;
+      if constexpr (k < 4 * (NKD - NKH)) {
+        qf[k % 4][NKH + k / 4] = xfrag(B.q, k % 4, NKH + k / 4);
+      } else {
+        constexpr int f = (k - 4 * (NKD - NKH)) / 2, part = (k - 4 * (NKD - NKH)) % 2;
+        if constexpr (part == 0) th[f] = tfrag(B.t, f, 0);
+        else tl[f] = tfrag(B.t, f, 1);
+      }
+    });
+    FW_FENCE();
+  });
+
+  // ---- D: U = T R (delta rule: 18 MFMAs). Alongside: the next chunk's other loads, the
+  // factors of O and W, the M fragments.
+  f4 for_[4], fur[4];
+  bf8 mh[kTriFrags], ml[kTriFrags];
+  float gC;
+  constexpr int ND = DELTA ? 3 * kTriFrags : 1;
+  constexpr int NDD = 9 + 2 * kTriFrags;
+  if constexpr (DELTA) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) U[m] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  static_for<0, ND>([&](auto I) {
+    constexpr int i = I, f = i / 3, part = i % 3;
+    if constexpr (DELTA) {
+      constexpr int m = tri_m(f), kb = tri_kb(f);
+      if constexpr (part == 0) mma_w(U[m], th[f], Rh[kb]);
+      else if constexpr (part == 1) mma_w(U[m], th[f], Rl[kb]);
+      else mma_w(U[m], tl[f], Rh[kb]);
+    }
+    FW_FENCE();
+    static_for<Share<NREST, ND, i>::lo, Share<NREST, ND, i>::hi>([&](auto K) {
+      dma_rest_op<DK, DELTA, K>(N, p, c + 1, L, lo, src);
+    });
+    static_for<Share<NDD, ND, i>::lo, Share<NDD, ND, i>::hi>([&](auto K) {
+      constexpr int k = K;
+      if constexpr (k < 4) for_[k] = fac4(2, k);
+      else if constexpr (k < 8) fur[k - 4] = fac4(3, k - 4);
+      else if constexpr (k == 8) gC = B.fac[4 * CH];
+      else {
+        constexpr int f = (k - 9) / 2, part = (k - 9) % 2;
+        if constexpr (part == 0) mh[f] = tfrag(B.m, f, 0);
+        else ml[f] = tfrag(B.m, f, 1);
+      }
+    });
+    FW_FENCE();
+  });
+
+  // ---- E: second half of Q S. Alongside: the split of U; O's Q S part scaled by fO as
+  // each tile completes; the first half of the X^T fragments.
+  u32x4 Uh[2], Ul[2];
+  f4 Om[4];
+  s4 xth[NRT][2][2];
+  constexpr int NE = 8 * (NKD - NKH);
+  constexpr int NED = 4 * NRH;  // transpose reads
+  static_for<0, NE>([&](auto I) {
+    constexpr int i = I, kb = NKH + i / 8, m = (i % 8) / 2, part = i % 2;
+    mma_w(Oq[m], qf[m][kb], part ? Sl[kb] : Sh[kb]);
+    FW_FENCE();
+    static_for<Share<8, NE, i>::lo, Share<8, NE, i>::hi>([&](auto K) {
+      split_word<K / 4, K % 4>(U, Uh[K / 4], Ul[K / 4]);
+    });
+    // the last K block's MFMAs for tile m are i = NE - 8 + 2m, +1; scale two slots later
+    if constexpr (i >= NE - 8 + 3 && ((i - (NE - 8 + 3)) % 2) == 0) {
+      constexpr int mm = (i - (NE - 8 + 3)) / 2;
+      Om[mm] = Oq[mm] * for_[mm];
+    }
+    static_for<Share<NED, NE, i>::lo, Share<NED, NE, i>::hi>([&](auto K) {
+      constexpr int k = K, rt = k / 4, kb = (k / 2) % 2, hh = k % 2;
+      xth[rt][kb][hh] = xthalf(rt, kb, hh);
+    });
+    FW_FENCE();
+  });
+  Om[3] = Oq[3] * for_[3];
+
+  // ---- F: O += M U (18 MFMAs). Alongside: W = fU U and its split; the second half of
+  // the X^T fragments.
+  u32x4 Wh[2], Wl[2];
+  constexpr int NF = 3 * kTriFrags;
+  constexpr int NFD = 4 * (NRT - NRH);
+  static_for<0, NF>([&](auto I) {
+    constexpr int i = I, f = i / 3, part = i % 3;
+    constexpr int m = tri_m(f), kb = tri_kb(f);
+    if constexpr (part == 0) mma_w(Om[m], mh[f], Uh[kb]);
+    else if constexpr (part == 1) mma_w(Om[m], mh[f], Ul[kb]);
+    else mma_w(Om[m], ml[f], Uh[kb]);
+    FW_FENCE();
+    static_for<Share<8, NF, i>::lo, Share<8, NF, i>::hi>([&](auto K) {
+      split_word_scaled<K / 4, K % 4>(U, fur, Wh[K / 4], Wl[K / 4]);
+    });
+    static_for<Share<NFD, NF, i>::lo, Share<NFD, NF, i>::hi>([&](auto K) {
+      constexpr int k = K, rt = NRH + k / 4, kb = (k / 2) % 2, hh = k % 2;
+      xth[rt][kb][hh] = xthalf(rt, kb, hh);
+    });
+    FW_FENCE();
+  });
+
+  // ---- G: S' = Gamma_C S + X^T W (4 NRT MFMAs); the decay of row tile rt+1 alongside
+  // the MFMAs of row tile rt
+  f4 acc[NRT];
+  acc[0] = s[0] * gC;
+  constexpr int NG = 4 * NRT;
+  static_for<0, NG>([&](auto I) {
+    constexpr int i = I, rt = i / 4, kb = (i % 4) / 2, part = i % 2;
+    mma_w(acc[rt], xtjoin(xth[rt][kb][0], xth[rt][kb][1]), part ? Wl[kb] : Wh[kb]);
+    FW_FENCE();
+    if constexpr (i % 4 == 0 && rt + 1 < NRT) acc[rt + 1] = s[rt + 1] * gC;
+    FW_FENCE();
+  });
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) s[rt] = acc[rt];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) O[m] = Om[m];
 }
 
-template <int DK, bool DELTA>
+template <int DK, bool DELTA, bool OBF>
 __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
   using Buf = SplitBuf<DK, DELTA>;
   constexpr int NRT = DK / 16;
@@ -345,7 +565,7 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
   const uint16_t* qb = static_cast<const uint16_t*>(p.q) + rowbase * DK;
   const uint16_t* vb = static_cast<const uint16_t*>(p.v) + rowbase * dv;
   const char* rec0 = p.ws + (size_t)bh * p.nchunks * RecSplit<DK>::kBytes;
-  const uint32_t oes = (p.flags & kFlagOutBf16) != 0 ? 2u : 4u;
+  constexpr uint32_t oes = OBF ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t ro =
       rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes);
   const int col = grp * kSplitCols + L.wave * 16 + L.n;  // this lane's value column
@@ -365,12 +585,13 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
       s[rt][i] = p.S_in != nullptr ? p.S_in[((size_t)bh * DK + tok_of(rt, 4 * L.g + i)) * dv + col] : 0.f;
 
   f4 O[4];
-  issue_chunk<DK, DELTA>(B0, p, 0, L, lo, src);
+  issue_xq<DK, DELTA>(B0, 0, L, lo, src);
+  issue_rest<DK, DELTA>(B0, p, 0, L, lo, src);
   for (int c = 0; c < p.nchunks; c += 2) {
-    run_chunk<DK, DELTA>(B0, B1, p, c, L, s, O, lo, src, rec0, ro, olofs);
-    if (c + 1 < p.nchunks) run_chunk<DK, DELTA>(B1, B0, p, c + 1, L, s, O, lo, src, rec0, ro, olofs);
+    chunk_step<DK, DELTA, OBF>(B0, B1, p, c, L, s, O, lo, src, rec0, ro, olofs);
+    if (c + 1 < p.nchunks) chunk_step<DK, DELTA, OBF>(B1, B0, p, c + 1, L, s, O, lo, src, rec0, ro, olofs);
   }
-  store_out(p, O, p.nchunks - 1, ro, olofs);
+  store_out<OBF>(dv, O, p.nchunks - 1, ro, olofs);
 
   if (p.S_out != nullptr) {
 #pragma unroll
@@ -390,7 +611,10 @@ template <int DK, bool DELTA>
 hipError_t launch_t(const ScanParams& p, hipStream_t st) {
   const int ngrp = p.dv / kSplitCols;
   const unsigned grid = (unsigned)(8 * ngrp * ((p.BH + 7) / 8));
-  hipLaunchKernelGGL((prop_split_kernel<DK, DELTA>), dim3(grid), dim3(NTS), 0, st, p);
+  if (p.flags & kFlagOutBf16)
+    hipLaunchKernelGGL((prop_split_kernel<DK, DELTA, true>), dim3(grid), dim3(NTS), 0, st, p);
+  else
+    hipLaunchKernelGGL((prop_split_kernel<DK, DELTA, false>), dim3(grid), dim3(NTS), 0, st, p);
   return hipGetLastError();
 }
 
