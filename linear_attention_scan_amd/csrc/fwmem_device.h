@@ -228,4 +228,15 @@ struct In<float> {
 // whether a < 0; decay products are carried as (sum of logs, sign parity).
 __device__ __forceinline__ float log_abs_floor(float a) { return __logf(fmaxf(fabsf(a), 1e-30f)); }
 
+// Inclusive prefix over the 64 lanes of a wave of (log|a|, count of negative a).
+__device__ __forceinline__ void wave_prefix(float& la, int& ng) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(la, o);
+    const int z = __shfl_up(ng, o);
+    if (lane >= o) { la += y; ng += z; }
+  }
+}
+
 }  // namespace fwmem

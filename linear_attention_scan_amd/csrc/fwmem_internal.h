@@ -62,6 +62,7 @@ size_t scan_record_bytes(int bf16, int dk, uint32_t flags);
 // bf16 inputs with the identity feature map and scalar decay take the split-operand
 // propagate kernel (fwmem_scan_split.hip).
 bool scan_split_path(int bf16, uint32_t flags);
+hipError_t launch_prep_split(const ScanParams& p, hipStream_t stream);
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t stream);
 // Whether kernels exist for this size.
 bool scan_supported(int dk, int dv);

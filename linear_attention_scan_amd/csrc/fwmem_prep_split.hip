@@ -1,0 +1,314 @@
+// Prep kernel of the split path (bf16 inputs, identity feature map, scalar decay): one
+// workgroup per (head, chunk) builds the chunk's record (RecSplit) from its keys,
+// queries and gates.
+//
+// With Gamma_t the decay since the chunk start ("Fast Weight Attention for Continual
+// Learning" reading notes, sections 4.1-4.4; the algebra is derived in fwmem_scan.hip):
+//   L_ts = eta_t (Gamma_{t-1}/Gamma_s) x_t . x_s  (s < t),   T = (I + L)^-1  (delta rule)
+//   M_ts = (Gamma_t / Gamma_s) q_t . x_s          (s <= t)
+// and the per-token row factors fP = eta Gamma_{t-1}, fV = eta, fO = Gamma_t,
+// fU = Gamma_C / Gamma_t with Gamma_C the decay over the whole chunk.
+//
+// Steps (4 waves):
+//   1. X and Q rows arrive in LDS by direct loads (rows past the sequence end read as
+//      zeros); wave 0 loads the gates.
+//   2. Gram products X X^T and Q X^T on bf16 MFMA: the products of bf16 values are exact
+//      and accumulate in fp32. The diagonal of X X^T gives |x_t|^2.
+//   3. Wave 0 forms eta_t, the decay prefix (log-sum and sign parity) and the row factors.
+//   4. The masked L and M are written to LDS in fp32.
+//   5. T = (I + L)^-1 by 16x16 blocks: wave b inverts diagonal block b by forward
+//      substitution, then wave j forms column block j of T,
+//        T_ij = -D_i sum_{k=j}^{i-1} L_ik T_kj,
+//      on fp32 MFMA from LDS and its own registers, with no further synchronisation.
+//   6. T and M are written to the record as bf16 hi/lo A fragments.
+#include "fwmem_internal.h"
+#include "fwmem_split.h"
+
+namespace fwmem {
+namespace {
+
+constexpr int CH = kChunk;
+constexpr int NTP = 256;
+
+// fp32 [64][64] matrix in LDS: element (r, c) at r * 64 + (c ^ 4 (r % 16)); groups of
+// four aligned columns stay contiguous.
+__device__ __forceinline__ int mat_idx(int r, int c) { return r * 64 + (c ^ ((r & 15) << 2)); }
+
+constexpr int kRegion = 16384;  // bytes of each of the three LDS regions
+
+// Lower 16x16 tiles of a 64x64 matrix, in row order: tile -> (row tile, column tile).
+__device__ constexpr int low_mt(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__device__ constexpr int low_nt(int t) { return t - (low_mt(t) * (low_mt(t) + 1)) / 2; }
+
+// C += A B for 16x16 blocks in fp32 MFMA: lane (g, n) supplies A[n][4g..4g+3] (a) and
+// B[4g+q][n] (b, the C layout of a previous product).
+__device__ __forceinline__ void mma_f32_block(f4& acc, const f4& a, const f4& b) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+}
+
+// Column block J of T: T_ij for i = J+1..3 (wave J), given D_J (= T_JJ, B layout) in Tc[J].
+template <int J>
+__device__ __forceinline__ void t_column_block(const float* Lf, float* Tf, f4 (&Tc)[4], int g, int n) {
+#pragma unroll
+  for (int i = J + 1; i < 4; ++i) {
+    f4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = J; k < i; ++k) {
+      const f4 a = *reinterpret_cast<const f4*>(&Lf[mat_idx(16 * i + n, 16 * k + 4 * g)]);
+      mma_f32_block(y, a, Tc[k]);
+    }
+    const f4 d = *reinterpret_cast<const f4*>(&Tf[mat_idx(16 * i + n, 16 * i + 4 * g)]);
+    f4 t = {0.f, 0.f, 0.f, 0.f};
+    mma_f32_block(t, d, y);
+    Tc[i] = -t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Tf[mat_idx(16 * i + 4 * g + q, 16 * J + n)] = -t[q];
+  }
+}
+
+template <int DK, bool DELTA>
+__global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
+  using RC = RecSplit<DK>;
+  constexpr int NGR = DK / 8;          // 16-byte granules per X / Q row
+  constexpr int NKD = DK / 32;         // K blocks over d_k
+  constexpr int NI = CH * NGR / 64;    // direct loads per tile
+  static_assert(CH * DK * 2 <= kRegion, "tile fits a region");
+  __shared__ __align__(16) char smem[3 * kRegion + 4 * CH * 4];
+  u32x4* Xs = reinterpret_cast<u32x4*>(smem);
+  u32x4* Qs = reinterpret_cast<u32x4*>(smem + kRegion);
+  float* Lf = reinterpret_cast<float*>(smem);            // after the Gram products
+  float* Mf = reinterpret_cast<float*>(smem + kRegion);  // after the Gram products
+  float* Tf = reinterpret_cast<float*>(smem + 2 * kRegion);
+  float* s_diag = reinterpret_cast<float*>(smem + 3 * kRegion);
+  float* s_eta = s_diag + CH;
+  float* s_g = s_eta + CH;
+  float* s_sg = s_g + CH;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int c = __builtin_amdgcn_readfirstlane(blockIdx.x % p.nchunks);
+  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x / p.nchunks);
+  const int t0 = c * CH, T = p.T;
+  const size_t rowbase = (size_t)bh * T;
+  const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
+  const uint16_t* kb = static_cast<const uint16_t*>(p.k) + rowbase * DK;
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q) + rowbase * DK;
+  char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
+
+  // ---- 1. rows into LDS (X starts one row early for the delta rule: x_t = k_{t-1})
+  {
+    const __amdgpu_buffer_rsrc_t rx = rsrc(DELTA ? kb - DK : kb, (uint32_t)(T * DK * 2));
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (uint32_t)(T * DK * 2));
+    const uint32_t so = (uint32_t)(t0 * DK * 2);
+#pragma unroll
+    for (int ii = 0; ii < NI / 4; ++ii) {
+      const int i = ii * 4 + wave;
+      const int pos = 64 * i + lane;
+      const int row = pos / NGR;
+      const uint32_t off = (uint32_t)(row * DK + 8 * ((pos % NGR) ^ xswz<DK>(row))) * 2u;
+      // the row before token 0 is the carried key, written below
+      dma16(rx, (DELTA && c == 0 && row == 0) ? 0x80000000u : off, so, &Xs[64 * i]);
+      dma16(rq, off, so, &Qs[64 * i]);
+    }
+  }
+  float g_beta = 0.f, g_lam = 0.f;
+  if (wave == 0 && t0 + lane < T) {
+    g_beta = p.beta != nullptr ? p.beta[rowbase + t0 + lane] : 1.f;
+    if (p.lam != nullptr) g_lam = p.lam[rowbase + t0 + lane];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (DELTA && c == 0 && tid < NGR) {
+    // threads tid < NGR issued the loads of row 0, so their own wait covers them
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (has_in) {
+      const float* x0 = p.xprev_in + (size_t)bh * DK + 8 * tid;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)f32_to_bf16_bits(x0[2 * j]) | ((uint32_t)f32_to_bf16_bits(x0[2 * j + 1]) << 16);
+    }
+    Xs[tid ^ xswz<DK>(0)] = w;
+  }
+  __syncthreads();
+
+  // ---- 2. Gram products: jobs over the 10 lower 16x16 tiles of X X^T (delta) and Q X^T
+  constexpr int NJ = DELTA ? 20 : 10;
+  constexpr int JPW = (NJ + 3) / 4;
+  auto rowfrag = [&](const u32x4* S, int row, int kq) -> bf8 {
+    return __builtin_bit_cast(bf8, S[row * NGR + ((4 * kq + g) ^ xswz<DK>(row))]);
+  };
+  f4 acc[JPW];
+#pragma unroll
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int job = jj * 4 + wave;
+    acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
+    if (job < NJ) {
+      const bool gram = DELTA && job < 10;
+      const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
+      const u32x4* A = gram ? Xs : Qs;
+#pragma unroll
+      for (int kq = 0; kq < NKD; ++kq)
+        mma_bf16(acc[jj], rowfrag(A, 16 * mt + n, kq), rowfrag(Xs, 16 * nt + n, kq));
+      if (gram && mt == nt && (n >> 2) == g) {
+        const int i = n & 3;
+        s_diag[16 * mt + n] = i == 0 ? acc[jj][0] : i == 1 ? acc[jj][1] : i == 2 ? acc[jj][2] : acc[jj][3];
+      }
+    }
+  }
+  __syncthreads();  // diagonal complete; X and Q no longer read
+
+  // ---- 3. token scalars and row factors (wave 0, lane = token)
+  if (wave == 0) {
+    const int t = lane, tau = t0 + t;
+    const bool active = tau < T;
+    float eta = 0.f, a = 1.f;
+    if (DELTA) {
+      const bool hasx = active && (tau >= 1 || has_in);
+      if (hasx) eta = g_beta / (s_diag[t] + g_lam + p.eps);
+      a = 1.f - eta * g_lam;
+    } else {
+      if (active) eta = g_beta;
+      if (active && p.lam != nullptr) a = g_lam;
+    }
+    float la = log_abs_floor(a);
+    int ng = a < 0.f ? 1 : 0;
+    wave_prefix(la, ng);
+    const float sg = (ng & 1) ? -1.f : 1.f;
+    s_eta[t] = eta;
+    s_g[t] = la;
+    s_sg[t] = sg;
+    float gprev = __shfl_up(la, 1), sprev = __shfl_up(sg, 1);
+    if (t == 0) {
+      gprev = 0.f;
+      sprev = 1.f;
+    }
+    const float gC = __shfl(la, CH - 1), sC = __shfl(sg, CH - 1);
+    float* fac = reinterpret_cast<float*>(rec + RC::kFac);
+    fac[t] = eta * sprev * __expf(gprev);
+    fac[CH + t] = eta;
+    fac[2 * CH + t] = sg * __expf(la);
+    fac[3 * CH + t] = sC * sg * __expf(gC - la);
+    fac[4 * CH + t] = t == 0 ? sC * __expf(gC) : (t == 1 ? (has_in ? 1.f : 0.f) : 0.f);
+  }
+  __syncthreads();
+
+  // ---- 4. masked L (delta) and M, fp32, into LDS; zero the two upper 16x16 tiles that
+  // the output fragments cover (row tiles 0 / 2, column tiles 1 / 3)
+#pragma unroll
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int job = jj * 4 + wave;
+    if (job < NJ) {
+      const bool gram = DELTA && job < 10;
+      const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
+      float* dst = gram ? Lf : Mf;
+      const int s = 16 * nt + n;
+      const float gs = s_g[s], ss = s_sg[s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * g + i;
+        float v = 0.f;
+        if (gram) {
+          if (s < t) {
+            const float gp = t ? s_g[t - 1] : 0.f, sp = t ? s_sg[t - 1] : 1.f;
+            v = s_eta[t] * sp * ss * __expf(gp - gs) * acc[jj][i];
+          }
+        } else if (s <= t) {
+          v = s_sg[t] * ss * __expf(s_g[t] - gs) * acc[jj][i];
+        }
+        dst[mat_idx(t, s)] = v;
+      }
+    }
+  }
+  {
+    // wave w zeroes tile w of: M(0,1), M(2,3), T(0,1), T(2,3)
+    float* dst = wave < 2 ? Mf : Tf;
+    const int r0 = (wave & 1) ? 32 : 0;
+    if (DELTA || wave < 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[mat_idx(r0 + 4 * g + q, r0 + 16 + n)] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. T = (I + L)^-1
+  if constexpr (DELTA) {
+    f4 Tc[4];
+    {
+      // diagonal block b = wave: lane (g, n) forms column n of D_b, keeps rows 4g..4g+3
+      const int b = wave;
+      float d[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* lrow = &Lf[(16 * b + r) * 64];
+        float s0 = (r == n) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < r; k4 += 4) {
+          const f4 l = *reinterpret_cast<const f4*>(lrow + ((16 * b + k4) ^ (r << 2)));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (k4 + q < r) {
+              if (q & 1) s1 -= l[q] * d[k4 + q];
+              else s0 -= l[q] * d[k4 + q];
+            }
+          }
+        }
+        d[r] = s0 + s1;
+      }
+      f4 db;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * g + q;
+        db[q] = g == 0 ? d[q] : g == 1 ? d[4 + q] : g == 2 ? d[8 + q] : d[12 + q];
+        Tf[mat_idx(16 * b + r, 16 * b + n)] = db[q];
+      }
+      Tc[0] = Tc[1] = Tc[2] = Tc[3] = db;
+    }
+    __syncthreads();  // every D_b in LDS
+    if (wave == 0) t_column_block<0>(Lf, Tf, Tc, g, n);
+    else if (wave == 1) t_column_block<1>(Lf, Tf, Tc, g, n);
+    else if (wave == 2) t_column_block<2>(Lf, Tf, Tc, g, n);
+    __syncthreads();
+  }
+
+  // ---- 6. T (delta) and M as split A fragments: row tok_of(m, lane % 16), K columns
+  // 32kb + 8 (lane / 16) .. +7
+#pragma unroll
+  for (int r = 0; r < 2 * kTriFrags * 64 / NTP; ++r) {
+    const int task = tid + NTP * r;
+    const int mat = task / (kTriFrags * 64);  // 0: T, 1: M
+    if (mat == 0 && !DELTA) continue;
+    const int f = (task >> 6) % kTriFrags, ln = task & 63;
+    const int row = tok_of(tri_m(f), ln & 15), k0 = 32 * tri_kb(f) + 8 * (ln >> 4);
+    const float* src = mat == 0 ? Tf : Mf;
+    const f4 x0 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0)]);
+    const f4 x1 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0 + 4)]);
+    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    bf8 hi, lo;
+    split8(x, hi, lo);
+    u32x4* dst = reinterpret_cast<u32x4*>(rec + (mat == 0 ? RC::kT : RC::kM)) + (2 * f) * 64 + ln;
+    dst[0] = __builtin_bit_cast(u32x4, hi);
+    dst[64] = __builtin_bit_cast(u32x4, lo);
+  }
+  if (c == 0 && tid < DK) {
+    uint16_t v = 0;
+    if (DELTA && has_in) v = f32_to_bf16_bits(p.xprev_in[(size_t)bh * DK + tid]);
+    reinterpret_cast<uint16_t*>(rec + RC::kX0)[tid] = v;
+  }
+}
+
+template <int DK, bool DELTA>
+hipError_t launch_t(const ScanParams& p, hipStream_t st) {
+  const unsigned grid = (unsigned)((size_t)p.BH * p.nchunks);
+  hipLaunchKernelGGL((prep_split_kernel<DK, DELTA>), dim3(grid), dim3(NTP), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prep_split(const ScanParams& p, hipStream_t st) {
+  if (p.dk == 64) return p.delta ? launch_t<64, true>(p, st) : launch_t<64, false>(p, st);
+  return p.delta ? launch_t<128, true>(p, st) : launch_t<128, false>(p, st);
+}
+
+}  // namespace fwmem

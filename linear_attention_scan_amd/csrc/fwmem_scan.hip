@@ -31,7 +31,7 @@
 //     global data is loaded into registers while the current chunk computes.
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
-#include "fwmem_split.h"
+#include "fwmem_split.h"  // record size of the split path
 
 namespace fwmem {
 
@@ -88,17 +88,6 @@ __device__ __forceinline__ float block_max(float v, float* s_red) {
   return m;
 }
 
-// Inclusive prefix over the 64 lanes of a wave of (log|a|, count of negative a).
-__device__ __forceinline__ void wave_prefix(float& la, int& ng) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(la, o);
-    const int z = __shfl_up(ng, o);
-    if (lane >= o) { la += y; ng += z; }
-  }
-}
-
 // ================================================================ prep kernel
 template <typename InT, int DK>
 struct PrepLds {
@@ -113,9 +102,7 @@ struct PrepLds {
   static constexpr size_t kBytes = 4 * kReg + kSmall;
 };
 
-// SPLIT selects the record of the split propagate kernel (RecSplit: unscaled T and M as
-// bf16 hi/lo A fragments in its token order); otherwise the fp16 / fp32 record (Rec).
-template <typename InT, int DK, bool DELTA, bool PC, bool ELU, bool SPLIT>
+template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
 __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
@@ -456,48 +443,6 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       }
       __syncthreads();
     }
-  }
-
-  if constexpr (SPLIT) {
-    // Split record: T and M as A fragments (row tok_of(m, lane % 16), K columns
-    // 32kb + 8 (lane / 16) .. +7), hi and lo; unscaled row factors.
-    static_assert(!PC && !ELU && sizeof(InT) == 2, "split record: bf16, identity map, scalar decay");
-    using RS = RecSplit<DK>;
-    char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RS::kBytes;
-#pragma unroll
-    for (int r = 0; r < 2 * kTriFrags * 64 / NT; ++r) {
-      const int task = tid + NT * r;
-      const int mat = task / (kTriFrags * 64);  // 0: T, 1: M
-      if (mat == 0 && !DELTA) continue;
-      const int f = (task >> 6) % kTriFrags, ln = task & 63;
-      const int row = tok_of(tri_m(f), ln & 15), k0 = 32 * tri_kb(f) + 8 * (ln >> 4);
-      const float* src = (mat == 0 ? Tf : Mf) + row * LDF + k0;
-      const f4 a = *reinterpret_cast<const f4*>(src), b = *reinterpret_cast<const f4*>(src + 4);
-      const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      bf8 hi, lo;
-      split8(x, hi, lo);
-      u32x4* dst = reinterpret_cast<u32x4*>(rec + (mat == 0 ? RS::kT : RS::kM)) + (2 * f) * 64 + ln;
-      dst[0] = __builtin_bit_cast(u32x4, hi);
-      dst[64] = __builtin_bit_cast(u32x4, lo);
-    }
-    float* fac = reinterpret_cast<float*>(rec + RS::kFac);
-    if (tid < CH) {
-      const int tt = tid;
-      const float e = s_eta[tt];
-      const float gprev = tt ? s_g[tt - 1] : 0.f;
-      const float sprev = tt ? s_sg[tt - 1] : 1.f;
-      fac[tt] = e * (sprev * __expf(gprev));
-      fac[CH + tt] = e;
-      fac[2 * CH + tt] = s_sg[tt] * __expf(s_g[tt]);
-      fac[3 * CH + tt] = s_sg[CH - 1] * s_sg[tt] * __expf(s_g[CH - 1] - s_g[tt]);
-    } else if (tid < 2 * CH) {
-      const int j = tid - CH;
-      fac[4 * CH + j] = j == 0 ? s_sg[CH - 1] * __expf(s_g[CH - 1]) : (j == 1 ? (has_in ? 1.f : 0.f) : 0.f);
-    }
-    if (c == 0 && tid < DK) {
-      reinterpret_cast<uint16_t*>(rec + RS::kX0)[tid] = x0 != nullptr ? f32_to_bf16_bits(x0[tid]) : (uint16_t)0;
-    }
-    return;
   }
 
   // Write T (delta) and M, scaled and in operand order, plus the token factors.
@@ -1080,15 +1025,14 @@ static hipError_t launch_scan_t(const ScanParams& p, hipStream_t st, int phases)
   if constexpr (sizeof(InT) == 2 && !PC && !ELU) {
     // bf16, identity map, scalar decay: split-operand propagate kernel
     if (phases & 1) {
-      hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC, ELU, true>), dim3(nprep), dim3(NT), 0, st, p);
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = launch_prep_split(p, st);
       if (e != hipSuccess) return e;
     }
     if (phases & 2) return launch_prop_split(p, st);
     return hipSuccess;
   } else {
     if (phases & 1) {
-      hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC, ELU, false>), dim3(nprep), dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC, ELU>), dim3(nprep), dim3(NT), 0, st, p);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -88,4 +88,28 @@ __device__ __forceinline__ void mma_bf16(f4& acc, const bf8& a, const bf8& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// ---- LDS tiles and direct loads
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(3))) s4* lds_s4ptr;
+
+// Granule slot of 16-byte granule cg in row `row` of a [CH][DK] bf16 tile is
+// cg ^ xswz(row): conflict-free for both the row-fragment and the transpose reads.
+template <int DK>
+__device__ __forceinline__ int xswz(int row) {
+  if constexpr (DK == 128) return ((row & 3) << 2) | ((row >> 3) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 3) & 3);
+}
+// Value tile [CH][32] bf16: four granules per row.
+__device__ __forceinline__ int vswz(int row) { return (row >> 3) & 3; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
+}
+
+
 }  // namespace fwmem
