@@ -22,7 +22,8 @@ namespace fwmem {
 namespace {
 
 constexpr int CH = kChunk;
-constexpr int NTS = 64 * kSplitWaves;
+constexpr int kLoader = kSplitWaves;          // index of the loader wave
+constexpr int NTS = 64 * (kSplitWaves + 1);    // compute waves + one loader wave
 
 template <int DK, bool DELTA>
 struct SplitBuf {
@@ -46,106 +47,142 @@ struct Srcs {
   __amdgpu_buffer_rsrc_t x, q, v, w;
 };
 
-// Loop-invariant lane offsets of the direct loads (bytes from the chunk's first row).
+// Loop-invariant lane offsets of the loader wave's direct loads (bytes from the chunk's
+// first row).
 template <int DK>
 struct LoadOffs {
   static constexpr int NGR = DK / 8;
-  static constexpr int NXI = CH * NGR / 64 / kSplitWaves;  // X (and Q) loads per wave
-  static constexpr int NVI = CH * kSplitCols / 8 / 64 / kSplitWaves;
+  static constexpr int NXI = CH * NGR / 64;             // X (and Q) loads per chunk
+  static constexpr int NVI = CH * kSplitCols / 8 / 64;  // value-tile loads per chunk
   uint32_t x[NXI];  // row * DK * 2 + 16 * granule
   uint32_t v[NVI];  // row * dv * 2 + 2 * (first column of the granule)
   uint32_t lane16;  // 16 * lane
 };
 
 template <int DK>
-__device__ __forceinline__ LoadOffs<DK> load_offsets(const Lane& L, int dv, int grp) {
+__device__ __forceinline__ LoadOffs<DK> load_offsets(int lane, int dv, int grp) {
   using LO = LoadOffs<DK>;
   constexpr int NGR = LO::NGR;
   LO o;
 #pragma unroll
   for (int ii = 0; ii < LO::NXI; ++ii) {
-    const int pos = 64 * (ii * kSplitWaves + L.wave) + L.lane;
+    const int pos = 64 * ii + lane;
     const int row = pos / NGR;
     o.x[ii] = (uint32_t)(row * DK + 8 * ((pos % NGR) ^ xswz<DK>(row))) * 2u;
   }
 #pragma unroll
   for (int ii = 0; ii < LO::NVI; ++ii) {
-    const int pos = 64 * (ii * kSplitWaves + L.wave) + L.lane;
+    const int pos = 64 * ii + lane;
     const int row = pos >> 2;
     o.v[ii] = (uint32_t)(row * dv + grp * kSplitCols + 8 * ((pos & 3) ^ vswz(row))) * 2u;
   }
-  o.lane16 = (uint32_t)L.lane * 16u;
+  o.lane16 = (uint32_t)lane * 16u;
   return o;
 }
 
-// Direct loads of chunk c into B, issued by every thread of the workgroup. For the
-// delta rule the X resource starts one row early (x_t is the key before token t); the
-// row before token 0 is forced out of range and patched from the record later. A chunk
-// past the end (c == nchunks) lies wholly outside the ranges and loads zeros.
-template <int DK, bool DELTA>
-__device__ __forceinline__ void issue_xq(SplitBuf<DK, DELTA>& B, int c, const Lane& L, const LoadOffs<DK>& o,
-                                         const Srcs& src) {
-  using LO = LoadOffs<DK>;
-  const uint32_t sx = (uint32_t)(c * CH * DK * 2);
-#pragma unroll
-  for (int ii = 0; ii < LO::NXI; ++ii) {
-    const int i = ii * kSplitWaves + L.wave;
-    uint32_t xo = o.x[ii];
-    if (DELTA && c == 0 && 64 * i + L.lane < LO::NGR) xo = 0x80000000u;  // row 0 of chunk 0
-    dma16(src.x, xo, sx, &B.x[64 * i]);
-    dma16(src.q, o.x[ii], sx, &B.q[64 * i]);
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
 
+// Output tiles of a chunk, staged in LDS by the compute waves for the loader wave:
+// [chunk parity][compute wave][tile m][lane], in the MFMA C layout.
+struct OutStage {
+  f4 o[2][kSplitWaves][4][64];
+};
+
+// The loader's stores of chunk c's outputs from the stage: lane (g, n) writes rows
+// tok_of(m, 4g+i) of column 16w + n of each compute wave w, through a buffer resource
+// over the head's output rows (rows past the sequence end fall outside its range).
+template <bool OBF>
+__device__ __forceinline__ void store_staged(const OutStage& st, int c, int lane, int dv, int grp,
+                                             __amdgpu_buffer_rsrc_t ro) {
+  constexpr uint32_t es = OBF ? 2u : 4u;
+  const int g = lane >> 4, n = lane & 15;
+  static_for<0, kSplitWaves>([&](auto W) {
+    const uint32_t vo = (uint32_t)(8 * g * dv + grp * kSplitCols + 16 * W + n) * es;
+    static_for<0, 4>([&](auto M) {
+      constexpr int m = M;
+      const f4 v = st.o[c & 1][W][m][lane];
+      static_for<0, 4>([&](auto I) {
+        constexpr int i = I;
+        const int r = c * CH + 32 * (m >> 1) + 4 * (m & 1) + i;
+        const uint32_t so = (uint32_t)(r * dv) * es;
+        if constexpr (OBF) {
+          const __bf16 h = (__bf16)v[i];
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ro, vo, so, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), ro, vo, so, 0);
+        }
+      });
+    });
+  });
+}
+
+// Direct loads of chunk c into B by the loader wave. For the delta rule the X resource
+// starts one row early (x_t is the key before token t); the row before token 0 is
+// forced out of range and patched from the record afterwards. Rows past the sequence
+// end read as zeros.
 template <int DK, bool DELTA>
-__device__ __forceinline__ void issue_rest(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, const Lane& L,
-                                           const LoadOffs<DK>& o, const Srcs& src) {
+__device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, int lane,
+                                            const LoadOffs<DK>& o, const Srcs& src) {
   using LO = LoadOffs<DK>;
   using RC = RecSplit<DK>;
+  const uint32_t sx = (uint32_t)(c * CH * DK * 2);
+  static_for<0, LO::NXI>([&](auto I) {
+    constexpr int i = I;
+    uint32_t xo = o.x[i];
+    if (DELTA && c == 0 && 64 * i + lane < LO::NGR) xo = 0x80000000u;  // row 0 of chunk 0
+    dma16(src.x, xo, sx, &B.x[64 * i]);
+    dma16(src.q, o.x[i], sx, &B.q[64 * i]);
+  });
   const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
   if constexpr (DELTA) {
-#pragma unroll
-    for (int jj = 0; jj < 2 * kTriFrags / kSplitWaves; ++jj) {
-      const int j = jj * kSplitWaves + L.wave;
-      dma16(src.w, o.lane16, sw + (uint32_t)(RC::kT + j * 1024), &B.t[64 * j]);
-    }
+    static_for<0, 2 * kTriFrags>([&](auto J) {
+      dma16(src.w, o.lane16, sw + (uint32_t)(RC::kT + J * 1024), &B.t[64 * J]);
+    });
   }
-#pragma unroll
-  for (int jj = 0; jj < 2 * kTriFrags / kSplitWaves; ++jj) {
-    const int j = jj * kSplitWaves + L.wave;
-    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kM + j * 1024), &B.m[64 * j]);
-  }
+  static_for<0, 2 * kTriFrags>([&](auto J) {
+    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kM + J * 1024), &B.m[64 * J]);
+  });
   const uint32_t sv = (uint32_t)(c * CH * p.dv * 2);
-#pragma unroll
-  for (int ii = 0; ii < LO::NVI; ++ii) {
-    const int i = ii * kSplitWaves + L.wave;
-    dma16(src.v, o.v[ii], sv, &B.v[64 * i]);
-  }
+  static_for<0, LO::NVI>([&](auto I) { dma16(src.v, o.v[I], sv, &B.v[64 * I]); });
   // row factors: 1280 bytes
-  if (L.wave == 0) dma16(src.w, o.lane16, sw + (uint32_t)RC::kFac, &B.fac[0]);
-  else if (L.lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
+  dma16(src.w, o.lane16, sw + (uint32_t)RC::kFac, &B.fac[0]);
+  if (lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
 }
 
-// Outputs of chunk c (c may be -1: nothing is stored): lane rows tok_of(m, 4g+i) of its
-// column, through a buffer resource over the head's output rows, so rows past the
-// sequence end fall outside its range.
-template <bool OBF>
-__device__ __forceinline__ void store_out(int dv, const f4 (&O)[4], int c, __amdgpu_buffer_rsrc_t ro,
-                                          uint32_t olofs) {
-  constexpr uint32_t es = OBF ? 2u : 4u;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = c * CH + 32 * (m >> 1) + 4 * (m & 1) + i;  // uniform part of the row
-      const uint32_t so = c >= 0 ? (uint32_t)(r * dv) * es : 0x80000000u;
-      if constexpr (OBF) {
-        const __bf16 h = (__bf16)O[m][i];
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ro, olofs * es, so, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m][i]), ro, olofs * es, so, 0);
-      }
-    }
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations are
+// complete before it arrives, and the compiler moves no memory access across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One chunk for the loader wave: once the loads of chunk c (in B) have landed, patch in
+// the carried key and release the chunk to the compute waves; then enqueue chunk c+1
+// into N (free again: the compute waves finished chunk c-1 before the barrier) and
+// store chunk c-1's outputs from the stage.
+template <int DK, bool DELTA, bool OBF>
+__device__ __forceinline__ void loader_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N, const OutStage& st,
+                                            const ScanParams& p, int c, int lane, const LoadOffs<DK>& o,
+                                            const Srcs& src, const char* rec0, int grp,
+                                            __amdgpu_buffer_rsrc_t ro) {
+  constexpr int NGR = SplitBuf<DK, DELTA>::NGR;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (DELTA && c == 0 && lane < NGR) {
+    // x_0 is the carried key (zero without one): row 0 of the first X tile
+    B.x[lane ^ xswz<DK>(0)] = *reinterpret_cast<const u32x4*>(rec0 + RecSplit<DK>::kX0 + 16 * lane);
+  }
+  lds_barrier();
+  if (c + 1 < p.nchunks) issue_chunk<DK, DELTA>(N, p, c + 1, lane, o, src);
+  // chunk c-1's outputs were staged before the barrier
+  if (c > 0) store_staged<OBF>(st, c - 1, lane, p.dv, grp, ro);
 }
 
 // ---------------------------------------------------------------- chunk step
@@ -157,13 +194,6 @@ __device__ __forceinline__ void store_out(int dv, const f4 (&O)[4], int c, __amd
 // stores), in the order given here.
 #define FW_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
@@ -199,101 +229,28 @@ __device__ __forceinline__ void mma_w(f4& acc, const bf8& a, const u32x4& b) {
   mma_bf16(acc, a, __builtin_bit_cast(bf8, b));
 }
 
-// The K-th direct load of this wave for chunk c: X and Q rows alternately.
-template <int DK, bool DELTA, int K>
-__device__ __forceinline__ void dma_xq_op(SplitBuf<DK, DELTA>& B, int c, const Lane& L, const LoadOffs<DK>& o,
-                                          const Srcs& src) {
-  constexpr int ii = K >> 1;
-  const int i = ii * kSplitWaves + L.wave;
-  const uint32_t sx = (uint32_t)(c * CH * DK * 2);
-  if constexpr ((K & 1) == 0) {
-    uint32_t xo = o.x[ii];
-    if (DELTA && c == 0 && 64 * i + L.lane < LoadOffs<DK>::NGR) xo = 0x80000000u;  // row 0 of chunk 0
-    dma16(src.x, xo, sx, &B.x[64 * i]);
-  } else {
-    dma16(src.q, o.x[ii], sx, &B.q[64 * i]);
-  }
-}
-
-// The K-th of the other direct loads: T fragments (delta rule), M fragments, value
-// rows, row factors.
-template <int DK, bool DELTA, int K>
-__device__ __forceinline__ void dma_rest_op(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, const Lane& L,
-                                            const LoadOffs<DK>& o, const Srcs& src) {
-  using RC = RecSplit<DK>;
-  constexpr int NT = DELTA ? kTriFrags : 0;  // per wave: 2 * kTriFrags / kSplitWaves
-  constexpr int NMF = kTriFrags;
-  const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
-  if constexpr (K < NT) {
-    const int j = K * kSplitWaves + L.wave;
-    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kT + j * 1024), &B.t[64 * j]);
-  } else if constexpr (K < NT + NMF) {
-    const int j = (K - NT) * kSplitWaves + L.wave;
-    dma16(src.w, o.lane16, sw + (uint32_t)(RC::kM + j * 1024), &B.m[64 * j]);
-  } else if constexpr (K < NT + NMF + LoadOffs<DK>::NVI) {
-    constexpr int ii = K - NT - NMF;
-    const int i = ii * kSplitWaves + L.wave;
-    dma16(src.v, o.v[ii], (uint32_t)(c * CH * p.dv * 2), &B.v[64 * i]);
-  } else if constexpr (K == NT + NMF + LoadOffs<DK>::NVI) {
-    if (L.wave == 0) dma16(src.w, o.lane16, sw + (uint32_t)RC::kFac, &B.fac[0]);
-    else if (L.lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
-  }
-}
-template <int DK, bool DELTA>
-constexpr int kRestOps = (DELTA ? kTriFrags : 0) + kTriFrags + LoadOffs<DK>::NVI + 1;
-
-// The K-th output store of chunk c (K = 4m + i: row tok_of(m, 4g+i)); c = -1 stores nothing.
-template <bool OBF, int K>
-__device__ __forceinline__ void store_op(int dv, const f4 (&O)[4], int c, __amdgpu_buffer_rsrc_t ro,
-                                         uint32_t olofs) {
-  constexpr int m = K >> 2, i = K & 3;
-  constexpr uint32_t es = OBF ? 2u : 4u;
-  const int r = c * CH + 32 * (m >> 1) + 4 * (m & 1) + i;
-  const uint32_t so = c >= 0 ? (uint32_t)(r * dv) * es : 0x80000000u;
-  if constexpr (OBF) {
-    const __bf16 h = (__bf16)O[m][i];
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ro, olofs * es, so, 0);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m][i]), ro, olofs * es, so, 0);
-  }
-}
-
 // Even share [lo, hi) of N items for slot I of S slots.
 template <int N, int S, int I>
 struct Share {
   static constexpr int lo = N * I / S, hi = N * (I + 1) / S;
 };
 
-// One chunk for one wave: waits for chunk c in B, enqueues chunk c+1 into N, stores the
-// outputs of chunk c-1 (held in O), updates the state slice s and leaves chunk c's
-// outputs in O.
-template <int DK, bool DELTA, bool OBF>
-__device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N, const ScanParams& p,
-                                           int c, const Lane& L, f4 (&s)[DK / 16], f4 (&O)[4],
-                                           const LoadOffs<DK>& lo, const Srcs& src, const char* rec0,
-                                           __amdgpu_buffer_rsrc_t ro, uint32_t olofs) {
+// One chunk for one compute wave: waits for chunk c in B, updates the state slice s and
+// stages chunk c's outputs in st for the loader wave.
+template <int DK, bool DELTA>
+__device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStage& st, int c, const Lane& L,
+                                           f4 (&s)[DK / 16]) {
   using Buf = SplitBuf<DK, DELTA>;
   constexpr int NGR = Buf::NGR;
   constexpr int NKD = DK / 32;       // K blocks over d_k
   constexpr int NRT = DK / 16;       // row tiles of S
   constexpr int NKH = NKD / 2;       // K blocks of the first half of Q S
   constexpr int NRH = NRT / 2;
-  constexpr int NXQ = 2 * LoadOffs<DK>::NXI;  // X and Q direct loads of this wave
-  constexpr int NREST = kRestOps<DK, DELTA>;
   const int g = L.g, n = L.n;
 
-  // this chunk's loads (and older output stores) are complete in every wave once all
-  // waves pass the barrier; the other buffer is free again
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  if (DELTA && c == 0) {
-    // x_0 is the carried key (zero without one): row 0 of the first X tile
-    if (threadIdx.x < NGR) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(rec0 + RecSplit<DK>::kX0 + 16 * threadIdx.x);
-      B.x[threadIdx.x ^ xswz<DK>(0)] = w;
-    }
-    __syncthreads();
-  }
+  // the loader wave releases chunk c once its loads have landed; the compute waves have
+  // finished with chunk c-1, so the loader may refill that buffer
+  lds_barrier();
 
   auto fac4 = [&](int k, int m) -> f4 {
     return *reinterpret_cast<const f4*>(&B.fac[k * CH + tok_of(m, 4 * g)]);
@@ -356,15 +313,13 @@ __device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, 
   for (int m = 0; m < 4; ++m) P[m] = f4{0.f, 0.f, 0.f, 0.f};
   bf8 qf[4][NKD];
   constexpr int NB = 8 * NKD;
+  constexpr int NC = 8 * NKH;
+  constexpr int ND = DELTA ? 3 * kTriFrags : 1;
   static_for<0, NB>([&](auto I) {
     constexpr int i = I, kb = i / 8, m = (i % 8) / 2, part = i % 2;
     if constexpr (DELTA) mma_w(P[m], xf[m][kb], part ? Sl[kb] : Sh[kb]);
     FW_FENCE();
     if constexpr (kb + 1 < NKD && part == 0) split_word<kb + 1, m>(s, Sh[kb + 1], Sl[kb + 1]);
-    static_for<Share<NXQ + 16, NB, i>::lo, Share<NXQ + 16, NB, i>::hi>([&](auto K) {
-      if constexpr (K < NXQ) dma_xq_op<DK, DELTA, K>(N, c + 1, L, lo, src);
-      else store_op<OBF, K - NXQ>(p.dv, O, c - 1, ro, olofs);
-    });
     static_for<Share<4 * NKH, NB, i>::lo, Share<4 * NKH, NB, i>::hi>([&](auto K) {
       qf[K % 4][K / 4] = xfrag(B.q, K % 4, K / 4);
     });
@@ -379,7 +334,6 @@ __device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, 
   f4 U[4];
   u32x4 Rh[2], Rl[2];
   bf8 th[kTriFrags], tl[kTriFrags];
-  constexpr int NC = 8 * NKH;
   // side work items: 16 row values (4 per tile) interleaved with the 8 split words, in
   // dependency order (tiles 0,1 -> words of K block 0 -> tiles 2,3 -> words of block 1)
   constexpr int NCV = DELTA ? 24 : 16;
@@ -421,7 +375,6 @@ __device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, 
   f4 for_[4], fur[4];
   bf8 mh[kTriFrags], ml[kTriFrags];
   float gC;
-  constexpr int ND = DELTA ? 3 * kTriFrags : 1;
   constexpr int NDD = 9 + 2 * kTriFrags;
   if constexpr (DELTA) {
 #pragma unroll
@@ -436,9 +389,6 @@ __device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, 
       else mma_w(U[m], tl[f], Rh[kb]);
     }
     FW_FENCE();
-    static_for<Share<NREST, ND, i>::lo, Share<NREST, ND, i>::hi>([&](auto K) {
-      dma_rest_op<DK, DELTA, K>(N, p, c + 1, L, lo, src);
-    });
     static_for<Share<NDD, ND, i>::lo, Share<NDD, ND, i>::hi>([&](auto K) {
       constexpr int k = K;
       if constexpr (k < 4) for_[k] = fac4(2, k);
@@ -517,7 +467,7 @@ __device__ __forceinline__ void chunk_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, 
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) s[rt] = acc[rt];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) O[m] = Om[m];
+  for (int m = 0; m < 4; ++m) st.o[c & 1][L.wave][m][L.lane] = Om[m];
 }
 
 template <int DK, bool DELTA, bool OBF>
@@ -525,6 +475,7 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
   using Buf = SplitBuf<DK, DELTA>;
   constexpr int NRT = DK / 16;
   __shared__ Buf B0, B1;
+  __shared__ OutStage st;
 
   // workgroup -> (head, column group); the groups of a head share an XCD and its L2
   const int ngrp = p.dv / kSplitCols;
@@ -548,13 +499,28 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
   const __amdgpu_buffer_rsrc_t ro =
       rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes);
   const int col = grp * kSplitCols + L.wave * 16 + L.n;  // this lane's value column
-  const uint32_t olofs = (uint32_t)(8 * L.g * dv + col);  // lane part of an output offset
-  const LoadOffs<DK> lo = load_offsets<DK>(L, dv, grp);
-  Srcs src;
-  src.x = rsrc(DELTA ? kb - DK : kb, (uint32_t)(p.T * DK * 2));
-  src.q = rsrc(qb, (uint32_t)(p.T * DK * 2));
-  src.v = rsrc(vb, (uint32_t)(p.T * dv * 2));
-  src.w = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecSplit<DK>::kBytes));
+  if (L.wave == kLoader) {
+    // loader wave: one barrier per chunk, like the compute waves
+    const LoadOffs<DK> lo = load_offsets<DK>(L.lane, dv, grp);
+    Srcs src;
+    src.x = rsrc(DELTA ? kb - DK : kb, (uint32_t)(p.T * DK * 2));
+    src.q = rsrc(qb, (uint32_t)(p.T * DK * 2));
+    src.v = rsrc(vb, (uint32_t)(p.T * dv * 2));
+    src.w = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecSplit<DK>::kBytes));
+    issue_chunk<DK, DELTA>(B0, p, 0, L.lane, lo, src);
+    for (int c = 0; c < p.nchunks; c += 2) {
+      loader_step<DK, DELTA, OBF>(B0, B1, st, p, c, L.lane, lo, src, rec0, grp, ro);
+      if (c + 1 < p.nchunks) loader_step<DK, DELTA, OBF>(B1, B0, st, p, c + 1, L.lane, lo, src, rec0, grp, ro);
+    }
+    lds_barrier();  // the last chunk's outputs are staged
+    store_staged<OBF>(st, p.nchunks - 1, L.lane, dv, grp, ro);
+    if (p.S_out != nullptr && grp == 0) {
+      for (int i = L.lane; i < DK; i += 64)
+        p.xprev_out[(size_t)bh * DK + i] = bf16_bits_to_f32(kb[(uint32_t)((p.T - 1) * DK + i)]);
+      if (L.lane == 0) p.has_out[bh] = 1;
+    }
+    return;
+  }
 
   f4 s[NRT];
 #pragma unroll
@@ -563,14 +529,11 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     for (int i = 0; i < 4; ++i)
       s[rt][i] = p.S_in != nullptr ? p.S_in[((size_t)bh * DK + tok_of(rt, 4 * L.g + i)) * dv + col] : 0.f;
 
-  f4 O[4];
-  issue_xq<DK, DELTA>(B0, 0, L, lo, src);
-  issue_rest<DK, DELTA>(B0, p, 0, L, lo, src);
   for (int c = 0; c < p.nchunks; c += 2) {
-    chunk_step<DK, DELTA, OBF>(B0, B1, p, c, L, s, O, lo, src, rec0, ro, olofs);
-    if (c + 1 < p.nchunks) chunk_step<DK, DELTA, OBF>(B1, B0, p, c + 1, L, s, O, lo, src, rec0, ro, olofs);
+    chunk_step<DK, DELTA>(B0, st, c, L, s);
+    if (c + 1 < p.nchunks) chunk_step<DK, DELTA>(B1, st, c + 1, L, s);
   }
-  store_out<OBF>(dv, O, p.nchunks - 1, ro, olofs);
+  lds_barrier();  // hand the last chunk's outputs to the loader
 
   if (p.S_out != nullptr) {
 #pragma unroll
@@ -578,11 +541,6 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         p.S_out[((size_t)bh * DK + tok_of(rt, 4 * L.g + i)) * dv + col] = s[rt][i];
-    if (grp == 0) {
-      for (int i = threadIdx.x; i < DK; i += NTS)
-        p.xprev_out[(size_t)bh * DK + i] = bf16_bits_to_f32(kb[(uint32_t)((p.T - 1) * DK + i)]);
-      if (threadIdx.x == 0) p.has_out[bh] = 1;
-    }
   }
 }
 

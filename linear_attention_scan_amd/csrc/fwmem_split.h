@@ -107,8 +107,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Direct 16-byte-per-lane load into LDS. The destination is passed to the instruction
+// as its 32-bit LDS offset (the low half of the generic address of an LDS object), which
+// avoids a generic-to-local conversion with a null check for the object at offset 0.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
+  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(uintptr_t)a, 16, voff, soff, 0, 0);
 }
 
 
