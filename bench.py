@@ -6,11 +6,12 @@ kernel: exactly fwmem_scan_fwd) over one batch of synthetic input already reside
 in HBM. The default workload is the delta rule at B=4, H=16, T=4096, d_k=d_v=128
 with bf16 q/k/v (beta = 2 sigmoid(N(0,1)), lambda = softplus(N(-4,1)), seed 0).
 
-Prints ONE JSON line. `roofline` is for the longer of the two kernels, from HIP
-events recorded around every launch on the stream the kernels run on. The decode
-kernel (fwmem_step at B=256, H=32, d=128) is measured in the same run and reported
-under `decode`. `cpu_baseline` is the fp64 oracle timed on the host (a bounded
-sample of the same workload, one batch element).
+Prints ONE JSON line. `value` comes from K steps timed back to back; `roofline` is for
+the longer of the two kernels, from HIP events recorded around every launch of a second
+run of K steps, on the stream the kernels run on. The decode kernel (fwmem_step at
+B=256, H=32, d=128) is measured in the same run and reported under `decode`.
+`cpu_baseline` is the fp64 oracle timed on the host (a bounded sample of the same
+workload: whole batch elements, about 10 s).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -27,7 +28,71 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fast-weight scan tokens/s per GPU (H=16,d=128,T=4096) + % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
-MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "linear_attention_scan_amd", "csrc")
+
+# HBM traffic per launch of the scan kernels on the default workload (B=4 H=16 T=4096
+# d=128, bf16, delta rule), from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in runs of
+# their own, each scaled by what the same counter reads for a plain 1 GiB device copy in
+# the same run (FETCH_SIZE x2.0, WRITE_SIZE x1.0). A record is reported only while the
+# kernel's sources still hash to the recorded digest; after any change it is null until
+# the counters are taken again.
+MEASURED_TRAFFIC = {
+    ("delta_bf16_h16", "prop_split_kernel"): {
+        "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h"),
+        "sha256": {
+            "fwmem_scan_split.hip": "fb3d107a968905fab1bf69176c016e11fe5766fb95da5c09ca66cb7c496f2fc0",
+            "fwmem_split.h": "79815937c6a25bd5b6f7f0f1c7538b567e6e2ad40fb47736385bf1d89bb51cd2",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+        },
+        "fetch_kib": 150219.1, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("delta_bf16_h16", "prep_split_kernel"): {
+        "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h"),
+        "sha256": {
+            "fwmem_prep_split.hip": "8128dcce33d9595377c92a18e69bb6dadeb4b281dea9c163de592cad6328f63d",
+            "fwmem_split.h": "79815937c6a25bd5b6f7f0f1c7538b567e6e2ad40fb47736385bf1d89bb51cd2",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+        },
+        "fetch_kib": 66675.2, "write_kib": 103440.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+}
+
+
+def measured_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch from the counter record, or None when there is no
+    record or the kernel's sources have changed since it was taken."""
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
+    if rec is None:
+        return None
+    for name in rec["sources"]:
+        try:
+            with open(os.path.join(CSRC, name), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != rec["sha256"][name]:
+                    return None
+        except OSError:
+            return None
+    return int(round(rec["fetch_kib"] * 1024 * rec["read_factor"]
+                     + rec["write_kib"] * 1024 * rec["write_factor"]))
+
+
+def kernel_names(w):
+    """Names of the prep and propagate kernels that the library launches for w: bf16
+    inputs with the identity feature map and a scalar decay take the split-operand
+    kernels, everything else the general ones."""
+    split = w.dtype == "bf16" and not w.per_channel and w.phi != "elu1"
+    return ({"prep": "prep_split_kernel", "propagate": "prop_split_kernel"} if split
+            else {"prep": "prep_kernel", "propagate": "prop_kernel"})
+
+
+def compute_dtype(w):
+    """Arithmetic type of the scan: the split kernels multiply bf16 operands (hi/lo pairs
+    for computed matrices), the general kernels fp16 operands for bf16 inputs and fp32
+    operands for fp32 inputs; all accumulate in fp32."""
+    if w.dtype != "bf16":
+        return "f32"
+    return "bf16" if kernel_names(w)["prep"] == "prep_split_kernel" else "f16"
 
 
 def scan_bytes_per_token_head(w, out_bytes=4):
@@ -59,7 +124,8 @@ def scan_mfma_flops(w, C=64):
     (X X^T for the delta rule, and Q X^T): 2*16*16*d_k flops per tile.
     propagate, per (head, chunk): X S, Q S and X^T U are 2*C*d_k*d_v each; T R and M U
     take 6 MFMA blocks of 16x16x32 per 16 value columns. The additive rule has no X S
-    and no T R."""
+    and no T R. Each product is counted once: the split kernels evaluate a product with a
+    hi/lo operand as two or three MFMAs, and those repeats are not counted."""
     nch = (w.T + C - 1) // C
     units = w.B * w.H * nch
     delta = w.rule == 0
@@ -74,19 +140,19 @@ def scan_mfma_flops(w, C=64):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="delta_bf16_h16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan shards over heads with no "
-              "communication, and this build has no multi-GPU path. Run with --gpus 1.",
+              "communication, and the library has no multi-GPU path. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -130,10 +196,22 @@ def main():
         launch(F.PHASE_PROPAGATE)
     torch.cuda.synchronize()
 
+    # Timed region 1, the step rate: K steps back to back, bracketed by synchronisations.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(K):
+        launch(F.PHASE_PREP)
+        launch(F.PHASE_PROPAGATE)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+
+    # Timed region 2, the kernels' launch durations: the same K steps with a HIP event
+    # before and after every launch, on the stream the kernels run on. The events add a
+    # few microseconds per launch, which is why the step rate is taken without them.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
     for i in range(K):
         ev[i][0].record(stream)
         launch(F.PHASE_PREP)
@@ -141,8 +219,6 @@ def main():
         launch(F.PHASE_PROPAGATE)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
     ms_prep = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     ms_prop = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     assert bool(torch.isfinite(out).all()), "non-finite output"
@@ -160,16 +236,19 @@ def main():
         kk["GBs"] = kk["bytes"] / (kk["ms"] * 1e-3) / 1e9
         kk["mfma_TFLOPs"] = kk["mfma_flops"] / (kk["ms"] * 1e-3) / 1e12
     dom = max(kern, key=lambda n: kern[n]["ms"])
+    names = kernel_names(w)
     roofline = {
         "bound": "hbm",
-        "kernel": f"{dom}_kernel",
+        "kernel": names[dom],
         "achieved": round(kern[dom]["GBs"], 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(kern[dom]["GBs"] / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(w.name, names[dom]),
+        "algorithmic_bytes": kern[dom]["bytes"],
+        "launch_ms": round(kern[dom]["ms"], 5),
         "mfma_TFLOPs": round(kern[dom]["mfma_TFLOPs"], 2),
-        "mfma_frac": round(kern[dom]["mfma_TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
+        "mfma_frac": round(kern[dom]["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
     }
     whole_bytes = w.B * w.H * w.T * scan_bytes_per_token_head(w) + 2 * w.B * w.H * w.dk * w.dv * 4
 
@@ -184,14 +263,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if w.dtype == "bf16" else "f32",
+        "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "rule": "delta" if w.rule == 0 else "additive", "inputs": w.dtype,
                    "chunk": 64, "seed": 0},
         "roofline": roofline,
-        "kernels": {n: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),
-                        "mfma_TFLOPs": round(kk["mfma_TFLOPs"], 2)} for n, kk in kern.items()},
+        "kernels": {names[n]: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),
+                               "mfma_TFLOPs": round(kk["mfma_TFLOPs"], 2),
+                               "traffic": measured_traffic(w.name, names[n])}
+                    for n, kk in kern.items()},
         "whole_step_GBs": round(whole_bytes / (ms_step * 1e-3) / 1e9, 1),
     }
 
@@ -248,14 +329,14 @@ def bench_decode(steps, dev, stream):
         if st != F.OK:
             raise F.FwmemError(st, "fwmem_step")
 
-    for i in range(5):
+    for i in range(20):
         one(i)
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     evs[0].record(stream)
     for i in range(steps):
-        one(5 + i)
-        evs[i + 1].record(stream)
+        one(20 + i)
+    evs[1].record(stream)
     torch.cuda.synchronize()
     ms = evs[0].elapsed_time(evs[-1]) / steps
     per_head = 2 * d * d * 4 + 3 * d * 2 + 8 + d * 4 + 2 * d * 4 + 8
@@ -268,26 +349,33 @@ def bench_decode(steps, dev, stream):
                          "bytes_per_launch": nbytes}}
 
 
-def cpu_baseline(w):
-    """The fp64 oracle, untuned, on a bounded sample: batch element 0 (all H heads)
-    over the first T_s tokens, T_s chosen to take roughly 10-20 s."""
-    import numpy as np
+def cpu_baseline(w, min_s=10.0):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload: whole batch
+    elements (all H heads, all T tokens) in order, repeating the batch if it is done in
+    under min_s seconds, until about min_s seconds of CPU work. BLAS is held to one thread,
+    so `cores` is exact."""
+    from threadpoolctl import threadpool_limits
 
     from oracle import fwmem_oracle as orc
-    # calibrate on 256 tokens, then run a sample sized for ~12 s
-    def run(Ts):
-        sl = (slice(0, 1), slice(None), slice(0, Ts))
-        t0 = time.perf_counter()
+
+    def run(b):
+        sl = (slice(b, b + 1), slice(None), slice(None))
         orc.scan(w.q[sl], w.k[sl], w.v[sl], None if w.beta is None else w.beta[sl],
                  None if w.lam is None else w.lam[sl], rule=w.rule, phi_kind=w.phi, eps=w.eps,
                  per_channel=w.per_channel)
-        return time.perf_counter() - t0
-    t_cal = run(256)
-    Ts = int(min(w.T, max(256, 256 * 12.0 / max(t_cal, 1e-3))))
-    t = run(Ts)
-    return {"value": round(Ts / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch element 0 of {w.B} (all {w.H} heads), first {Ts} of {w.T} tokens, "
-                      f"fp64 NumPy recurrence, single thread, {t:.1f} s"}
+
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            run(n % w.B)
+            n += 1
+            t = time.perf_counter() - t0
+            if t >= min_s:
+                break
+    return {"value": round(n * w.T / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} batch elements of {w.T} tokens x {w.H} heads (batch elements "
+                      f"0..{w.B - 1} in turn), fp64 NumPy recurrence, one thread, {t:.1f} s"}
 
 
 if __name__ == "__main__":

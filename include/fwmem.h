@@ -60,7 +60,7 @@ typedef struct ihipStream_t* fwmem_stream; /* the same handle type as hipStream_
 typedef enum {
   FWMEM_OK = 0,
   FWMEM_EINVAL = -1,       /* NULL required pointer, negative size, unknown rule/flag/dtype, bad eps */
-  FWMEM_EUNSUPPORTED = -2, /* a size or chunk length this build has no kernel for */
+  FWMEM_EUNSUPPORTED = -2, /* a size or chunk length the library has no kernel for */
   FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda) */
   FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
   FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */

@@ -6,13 +6,14 @@
 //   R = diag(fV) V - diag(fP) (X S),   U = T R            (delta rule)
 //   U = diag(fV) V                                        (additive rule)
 //   O = diag(fO) (Q S) + M U,   S' = Gamma_C S + X^T diag(fU) U.
-// One workgroup = 2 waves = one head and 32 value columns; each wave keeps a 16-column
-// slice of S (d_k x 16, fp32, MFMA C layout) in registers and walks the chunks in
-// order. X, Q, T, M, V and the row factors of a chunk are brought into LDS by direct
-// global-to-LDS loads, double-buffered: the loads of chunk c+1 are in flight while
-// chunk c computes, and one barrier per chunk separates the two. X is stored once,
-// row-major with an XOR swizzle; X^T operands are read from it with the LDS transpose
-// read. All products run on bf16 MFMA with the split operands of fwmem_split.h.
+// One workgroup = one head and 32 value columns, in three waves. Each of the two compute
+// waves keeps a 16-column slice of S (d_k x 16, fp32, MFMA C layout) in registers and
+// walks the chunks in order. The third wave moves data: it brings X, Q, T, M, V and the
+// row factors of chunk c+1 into LDS by direct global-to-LDS loads while chunk c computes
+// (double-buffered), and stores chunk c-1's outputs, which the compute waves stage in
+// LDS. One barrier per chunk separates the phases. X is stored once, row-major with an
+// XOR swizzle; X^T operands are read from it with the LDS transpose read. All products
+// run on bf16 MFMA with the split operands of fwmem_split.h.
 #include "fwmem_internal.h"
 #include "fwmem_split.h"
 

@@ -84,6 +84,19 @@ def test_mixed_head_dims(dk, dv, rule):
     check_scan(w)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("beta_kind", ["one", "sigmoid"])
+def test_additive_identity_bf16(dk, dv, beta_kind):
+    """The additive rule with phi = identity on bf16 inputs: the split-operand kernels
+    without the triangular solve. Ragged T spans several chunks and a tail; the decayed
+    retention and an optional write scale come from the same draws as the additive
+    workload."""
+    w = wl.make_scan(B=2, H=3, T=333, dk=dk, dv=dv, rule=wl.RULE_ADDITIVE,
+                     normalise_qk=False, beta_kind=beta_kind, lam_kind="gamma",
+                     seed=7 * dk + dv, name=f"additive identity {dk}x{dv} beta={beta_kind}")
+    check_scan(w)
+
+
 def test_nonzero_initial_state_and_carried_key():
     w = wl.delta_bf16(seed=3, B=2, H=2, T=150)
     rng = np.random.default_rng(9)
