@@ -39,6 +39,7 @@ struct SplitBuf {
 
 struct Lane {
   int lane, wave, g, n;  // wave is wave-uniform (an SGPR)
+  uint32_t neg0, neg1;   // the packed bf16 pairs (-1, 0) and (0, -1), in SGPRs (see split2)
 };
 
 // Buffer resources of one head's inputs and workspace records. Every direct load goes
@@ -198,34 +199,31 @@ __device__ __forceinline__ void loader_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK,
 
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
-// hi/lo split of two fp32 values into one packed bf16 word each
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+// hi/lo split of two fp32 values into one packed bf16 word each. hi is the packed
+// rounding of the pair; each residual x - hi is one v_dot2c_f32_bf16 of the packed hi with
+// the pair (-1, 0) or (0, -1), accumulated onto x: the products are exact and x - hi is
+// representable in fp32, so the residual is exact, as a subtraction would give it, in two
+// instructions instead of four. The two pairs must reach the instruction as registers:
+// gfx950 reads an inline constant in a packed bf16 operand as a 32-bit float pattern, so
+// -1.0 would arrive as the pair (0, -1), while the compiler assumes (-1, 0).
+__device__ __forceinline__ void split2(float x0, float x1, const Lane& L, uint32_t& hi, uint32_t& lo) {
   const bf2 h = {(__bf16)x0, (__bf16)x1};
-  const uint32_t w = __builtin_bit_cast(uint32_t, h);
-  const bf2 l = {(__bf16)(x0 - __uint_as_float(w << 16)), (__bf16)(x1 - __uint_as_float(w & 0xffff0000u))};
-  hi = w;
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2, L.neg0), x0, false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2, L.neg1), x1, false);
+  const bf2 l = {(__bf16)r0, (__bf16)r1};
+  hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// Word j (slots 2j, 2j+1) of the B fragment of K block kb from C tiles c[2kb], c[2kb+1],
-// each value times f (the row factor of its tile row).
+// Word j (slots 2j, 2j+1) of the B fragment of K block kb from C tiles c[2kb], c[2kb+1].
 template <int KB, int J>
-__device__ __forceinline__ void split_word(const f4* c, u32x4& hi, u32x4& lo) {
+__device__ __forceinline__ void split_word(const f4* c, const Lane& L, u32x4& hi, u32x4& lo) {
   constexpr int t = 2 * KB + (J >> 1), r = 2 * (J & 1);
   uint32_t h, l;
-  split2(c[t][r], c[t][r + 1], h, l);
+  split2(c[t][r], c[t][r + 1], L, h, l);
   hi[J] = h;
   lo[J] = l;
 }
-template <int KB, int J>
-__device__ __forceinline__ void split_word_scaled(const f4* c, const f4* f, u32x4& hi, u32x4& lo) {
-  constexpr int t = 2 * KB + (J >> 1), r = 2 * (J & 1);
-  uint32_t h, l;
-  split2(c[t][r] * f[t][r], c[t][r + 1] * f[t][r + 1], h, l);
-  hi[J] = h;
-  lo[J] = l;
-}
-
 __device__ __forceinline__ void mma_w(f4& acc, const bf8& a, const u32x4& b) {
   mma_bf16(acc, a, __builtin_bit_cast(bf8, b));
 }
@@ -302,8 +300,18 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     fvr[m] = fac4(1, m);
     if (DELTA) fpr[m] = fac4(0, m);
   }
+  // The split of S also forms acc = Gamma_C S, the accumulator of the state update, so
+  // that the split may overwrite S.
+  const float gC = B.fac[4 * CH];
+  f4 acc[NRT];
   u32x4 Sh[NKD], Sl[NKD];
-  static_for<0, 4>([&](auto J) { split_word<0, J>(s, Sh[0], Sl[0]); });
+  auto split_s = [&](auto KB, auto J) {
+    constexpr int kb = KB, j = J, t = 2 * kb + (j >> 1), r = 2 * (j & 1);
+    acc[t][r] = s[t][r] * gC;
+    acc[t][r + 1] = s[t][r + 1] * gC;
+    split_word<kb, j>(s, L, Sh[kb], Sl[kb]);
+  };
+  static_for<0, 4>([&](auto J) { split_s(std::integral_constant<int, 0>{}, J); });
   FW_FENCE();
 
   // ---- B: P = X S (8 NKD MFMAs; the additive rule has none and keeps only the side
@@ -320,7 +328,8 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     constexpr int i = I, kb = i / 8, m = (i % 8) / 2, part = i % 2;
     if constexpr (DELTA) mma_w(P[m], xf[m][kb], part ? Sl[kb] : Sh[kb]);
     FW_FENCE();
-    if constexpr (kb + 1 < NKD && part == 0) split_word<kb + 1, m>(s, Sh[kb + 1], Sl[kb + 1]);
+    if constexpr (kb + 1 < NKD && part == 0)
+      split_s(std::integral_constant<int, kb + 1>{}, std::integral_constant<int, m>{});
     static_for<Share<4 * NKH, NB, i>::lo, Share<4 * NKH, NB, i>::hi>([&](auto K) {
       qf[K % 4][K / 4] = xfrag(B.q, K % 4, K / 4);
     });
@@ -351,7 +360,7 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
           constexpr int t = 2 * grp + w / 4, r = w % 4;
           P[t][r] = fvr[t][r] * vf(vv[t], r) - fpr[t][r] * P[t][r];
         } else {
-          split_word<grp, w - 8>(P, Rh[grp], Rl[grp]);
+          split_word<grp, w - 8>(P, L, Rh[grp], Rl[grp]);
         }
       } else {
         constexpr int t = k / 4, r = k % 4;
@@ -375,8 +384,7 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
   // factors of O and W, the M fragments.
   f4 for_[4], fur[4];
   bf8 mh[kTriFrags], ml[kTriFrags];
-  float gC;
-  constexpr int NDD = 9 + 2 * kTriFrags;
+  constexpr int NDD = 8 + 2 * kTriFrags;
   if constexpr (DELTA) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) U[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -394,9 +402,8 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
       constexpr int k = K;
       if constexpr (k < 4) for_[k] = fac4(2, k);
       else if constexpr (k < 8) fur[k - 4] = fac4(3, k - 4);
-      else if constexpr (k == 8) gC = B.fac[4 * CH];
       else {
-        constexpr int f = (k - 9) / 2, part = (k - 9) % 2;
+        constexpr int f = (k - 8) / 2, part = (k - 8) % 2;
         if constexpr (part == 0) mh[f] = tfrag(B.m, f, 0);
         else ml[f] = tfrag(B.m, f, 1);
       }
@@ -404,9 +411,11 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     FW_FENCE();
   });
 
-  // ---- E: second half of Q S. Alongside: the split of U; O's Q S part scaled by fO as
-  // each tile completes; the first half of the X^T fragments.
+  // ---- E: second half of Q S. Alongside: W = fU U, then the split of U (which may then
+  // overwrite U); O's Q S part scaled by fO as each tile completes; the first half of the
+  // X^T fragments.
   u32x4 Uh[2], Ul[2];
+  f4 Wt[4];
   f4 Om[4];
   s4 xth[NRT][2][2];
   constexpr int NE = 8 * (NKD - NKH);
@@ -416,7 +425,10 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     mma_w(Oq[m], qf[m][kb], part ? Sl[kb] : Sh[kb]);
     FW_FENCE();
     static_for<Share<8, NE, i>::lo, Share<8, NE, i>::hi>([&](auto K) {
-      split_word<K / 4, K % 4>(U, Uh[K / 4], Ul[K / 4]);
+      constexpr int t = 2 * (K / 4) + ((K % 4) >> 1), r = 2 * ((K % 4) & 1);
+      Wt[t][r] = U[t][r] * fur[t][r];
+      Wt[t][r + 1] = U[t][r + 1] * fur[t][r + 1];
+      split_word<K / 4, K % 4>(U, L, Uh[K / 4], Ul[K / 4]);
     });
     // the last K block's MFMAs for tile m are i = NE - 8 + 2m, +1; scale two slots later
     if constexpr (i >= NE - 8 + 3 && ((i - (NE - 8 + 3)) % 2) == 0) {
@@ -431,8 +443,8 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
   });
   Om[3] = Oq[3] * for_[3];
 
-  // ---- F: O += M U (18 MFMAs). Alongside: W = fU U and its split; the second half of
-  // the X^T fragments.
+  // ---- F: O += M U (18 MFMAs). Alongside: the split of W; the second half of the X^T
+  // fragments.
   u32x4 Wh[2], Wl[2];
   constexpr int NF = 3 * kTriFrags;
   constexpr int NFD = 4 * (NRT - NRH);
@@ -444,7 +456,7 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     else mma_w(Om[m], ml[f], Uh[kb]);
     FW_FENCE();
     static_for<Share<8, NF, i>::lo, Share<8, NF, i>::hi>([&](auto K) {
-      split_word_scaled<K / 4, K % 4>(U, fur, Wh[K / 4], Wl[K / 4]);
+      split_word<K / 4, K % 4>(Wt, L, Wh[K / 4], Wl[K / 4]);
     });
     static_for<Share<NFD, NF, i>::lo, Share<NFD, NF, i>::hi>([&](auto K) {
       constexpr int k = K, rt = NRH + k / 4, kb = (k / 2) % 2, hh = k % 2;
@@ -453,16 +465,11 @@ __device__ __forceinline__ void chunk_step(const SplitBuf<DK, DELTA>& B, OutStag
     FW_FENCE();
   });
 
-  // ---- G: S' = Gamma_C S + X^T W (4 NRT MFMAs); the decay of row tile rt+1 alongside
-  // the MFMAs of row tile rt
-  f4 acc[NRT];
-  acc[0] = s[0] * gC;
+  // ---- G: S' = Gamma_C S + X^T W (4 NRT MFMAs onto acc)
   constexpr int NG = 4 * NRT;
   static_for<0, NG>([&](auto I) {
     constexpr int i = I, rt = i / 4, kb = (i % 4) / 2, part = i % 2;
     mma_w(acc[rt], xtjoin(xth[rt][kb][0], xth[rt][kb][1]), part ? Wl[kb] : Wh[kb]);
-    FW_FENCE();
-    if constexpr (i % 4 == 0 && rt + 1 < NRT) acc[rt + 1] = s[rt + 1] * gC;
     FW_FENCE();
   });
 #pragma unroll
@@ -490,6 +497,9 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
   L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   L.g = L.lane >> 4;
   L.n = L.lane & 15;
+  // opaque moves keep the two pairs out of inline-constant folding
+  asm volatile("s_mov_b32 %0, 0xbf80" : "=s"(L.neg0));
+  asm volatile("s_mov_b32 %0, 0xbf800000" : "=s"(L.neg1));
   const int dv = p.dv;
   const size_t rowbase = (size_t)bh * p.T;
   const uint16_t* kb = static_cast<const uint16_t*>(p.k) + rowbase * DK;
