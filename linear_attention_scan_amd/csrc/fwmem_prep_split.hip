@@ -189,7 +189,14 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     fac[CH + t] = eta;
     fac[2 * CH + t] = sg * __expf(la);
     fac[3 * CH + t] = sC * sg * __expf(gC - la);
-    fac[4 * CH + t] = t == 0 ? sC * __expf(gC) : (t == 1 ? (has_in ? 1.f : 0.f) : 0.f);
+    // row 4: [Gamma_C, has_prev, Gamma_C of the next chunk, 0...]. Slot 2 of a record is
+    // written by the next chunk's workgroup (1 for the last chunk), so that the propagate
+    // kernel knows the next decay one chunk early.
+    const float gamma_c = sC * __expf(gC);
+    const bool last = c + 1 == p.nchunks;
+    if (t != 2 || last)
+      fac[4 * CH + t] = t == 0 ? gamma_c : (t == 1 ? (has_in ? 1.f : 0.f) : (t == 2 ? 1.f : 0.f));
+    if (t == 2 && c > 0) reinterpret_cast<float*>(rec - RC::kBytes + RC::kFac)[4 * CH + 2] = gamma_c;
   }
   __syncthreads();
 

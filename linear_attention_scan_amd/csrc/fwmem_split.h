@@ -29,8 +29,8 @@ namespace fwmem {
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitWaves = 2;                  // waves of a propagate workgroup
-constexpr int kSplitCols = 16 * kSplitWaves;    // value columns of a propagate workgroup
+constexpr int kSplitTiles = 2;                  // 16-column value tiles of a propagate workgroup
+constexpr int kSplitCols = 16 * kSplitTiles;    // value columns of a propagate workgroup
 constexpr int kTriFrags = 6;                    // nonzero (m, kb) blocks of a 64x64 lower-triangular operand
 
 __host__ __device__ constexpr int tok_of(int m, int r) {
@@ -49,7 +49,7 @@ struct RecSplit {
   static constexpr size_t kM = kT + 2 * kTriFrags * 1024;
   // float [5][64]: per token fP, fV, fO, fU (the row factors of
   //   R = fV V - fP (X S),  O = fO (Q S) + M U,  S' = Gamma_C S + X^T (fU U)),
-  // then [Gamma_C, has_prev, 0...].
+  // then [Gamma_C, has_prev, Gamma_C of the next chunk (1 after the last), 0...].
   static constexpr size_t kFac = kM + 2 * kTriFrags * 1024;
   static constexpr size_t kFacBytes = 5 * 64 * 4;
   // bf16 [DK]: the key feature that precedes the chunk's first token (chunk 0 only).
