@@ -148,6 +148,71 @@ __device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanPa
   if (lane < 16) dma16(src.w, o.lane16, sw + (uint32_t)(RC::kFac + 1024), &B.fac[256]);
 }
 
+// Direct loads of the X, Q and V rows of chunk c >= 1 into B (the record arrives through
+// the loader's registers).
+template <int DK, bool DELTA>
+__device__ __forceinline__ void issue_rows(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c,
+                                           const LoadOffs<DK>& o, const Srcs& src) {
+  using LO = LoadOffs<DK>;
+  const uint32_t sx = (uint32_t)(c * CH * DK * 2);
+  static_for<0, LO::NXI>([&](auto I) {
+    dma16(src.x, o.x[I], sx, &B.x[64 * I]);
+    dma16(src.q, o.x[I], sx, &B.q[64 * I]);
+  });
+  const uint32_t sv = (uint32_t)(c * CH * p.dv * 2);
+  static_for<0, LO::NVI>([&](auto I) { dma16(src.v, o.v[I], sv, &B.v[64 * I]); });
+}
+
+// A chunk's record (T, M and the row factors), held in the loader wave's registers: it
+// is loaded two chunks ahead and written to LDS one chunk ahead, so that its loads have a
+// whole chunk period more to land than the row loads, which go straight to LDS one
+// chunk ahead. (Register loads of the rows as well proved slower than direct loads.)
+template <int DK, bool DELTA>
+struct ChunkRegs {
+  static constexpr int NT = DELTA ? 2 * kTriFrags : 0;
+  static constexpr int NLOADS = NT + 2 * kTriFrags + 2;
+  u32x4 t[DELTA ? 2 * kTriFrags : 1];
+  u32x4 m[2 * kTriFrags];
+  u32x4 f0, f1;
+};
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <int DK, bool DELTA>
+__device__ __forceinline__ void load_regs(ChunkRegs<DK, DELTA>& r, const Srcs& src, int c, const LoadOffs<DK>& o,
+                                          int lane) {
+  using RC = RecSplit<DK>;
+  const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
+  if constexpr (DELTA) {
+    static_for<0, 2 * kTriFrags>([&](auto J) { r.t[J] = ld16(src.w, o.lane16, sw + (uint32_t)(RC::kT + J * 1024)); });
+  }
+  static_for<0, 2 * kTriFrags>([&](auto J) { r.m[J] = ld16(src.w, o.lane16, sw + (uint32_t)(RC::kM + J * 1024)); });
+  r.f0 = ld16(src.w, o.lane16, sw + (uint32_t)RC::kFac);
+  // the last 256 bytes of the factors: lanes 16.. read out of range (zeros, no traffic)
+  r.f1 = ld16(src.w, lane < 16 ? o.lane16 : 0x80000000u, sw + (uint32_t)(RC::kFac + 1024));
+}
+
+template <int DK, bool DELTA>
+__device__ __forceinline__ void store_regs(SplitBuf<DK, DELTA>& B, const ChunkRegs<DK, DELTA>& r, int lane) {
+  if constexpr (DELTA) {
+#pragma unroll
+    for (int j = 0; j < 2 * kTriFrags; ++j) B.t[64 * j + lane] = r.t[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 2 * kTriFrags; ++j) B.m[64 * j + lane] = r.m[j];
+  reinterpret_cast<u32x4*>(B.fac)[lane] = r.f0;
+  if (lane < 16) reinterpret_cast<u32x4*>(B.fac)[64 + lane] = r.f1;
+}
+
+// s_waitcnt vmcnt(n) (n <= 63), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier that orders LDS accesses only: this wave's LDS operations are
 // complete before it arrives, and the compiler moves no memory access across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -184,21 +249,29 @@ __device__ __forceinline__ void set_flag(int* f, int v) {
   *flag_ptr(f) = v;
 }
 
-// One chunk for the loader wave: once the loads of chunk c (in B) have landed, patch in
-// the carried key and release the chunk to the compute waves; then enqueue chunk c+1
-// into N (free again: the compute waves finished chunk c-1 before the barrier).
+// One chunk for the loader wave. Outstanding on entry: the direct row loads of chunk c
+// (into B), then the register loads of chunk c+1's record (if there is a chunk c+1).
+// Once the rows have landed, patch in the carried key and release chunk c to the
+// compute waves; then, with B's partner N free again (the compute waves finished chunk
+// c-1 before the barrier), enqueue chunk c+1's rows into N, write its record from
+// registers into N, and start the register loads of chunk c+2's record.
 template <int DK, bool DELTA>
-__device__ __forceinline__ void loader_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N, const ScanParams& p,
-                                            int c, int lane, const LoadOffs<DK>& o, const Srcs& src,
-                                            const char* rec0) {
+__device__ __forceinline__ void loader_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N,
+                                            ChunkRegs<DK, DELTA>& R, const ScanParams& p, int c, int lane,
+                                            const LoadOffs<DK>& o, const Srcs& src, const char* rec0) {
   constexpr int NGR = SplitBuf<DK, DELTA>::NGR;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (c + 1 < p.nchunks) wait_vm<ChunkRegs<DK, DELTA>::NLOADS>();
+  else wait_vm<0>();
   if (DELTA && c == 0 && lane < NGR) {
     // x_0 is the carried key (zero without one): row 0 of the first X tile
     B.x[lane ^ xswz<DK>(0)] = *reinterpret_cast<const u32x4*>(rec0 + RecSplit<DK>::kX0 + 16 * lane);
   }
   lds_barrier();
-  if (c + 1 < p.nchunks) issue_chunk<DK, DELTA>(N, p, c + 1, lane, o, src);
+  if (c + 1 < p.nchunks) {
+    issue_rows<DK, DELTA>(N, p, c + 1, o, src);
+    store_regs<DK, DELTA>(N, R, lane);
+    if (c + 2 < p.nchunks) load_regs<DK, DELTA>(R, src, c + 2, o, lane);
+  }
 }
 
 // ---------------------------------------------------------------- compute waves
@@ -609,9 +682,11 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     src.v = rsrc(vb, (uint32_t)(p.T * dv * 2));
     src.w = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecSplit<DK>::kBytes));
     issue_chunk<DK, DELTA>(B0, p, 0, lane, lo, src);
+    ChunkRegs<DK, DELTA> R;
+    if (p.nchunks > 1) load_regs<DK, DELTA>(R, src, 1, lo, lane);
     for (int c = 0; c < p.nchunks; c += 2) {
-      loader_step<DK, DELTA>(B0, B1, p, c, lane, lo, src, rec0);
-      if (c + 1 < p.nchunks) loader_step<DK, DELTA>(B1, B0, p, c + 1, lane, lo, src, rec0);
+      loader_step<DK, DELTA>(B0, B1, R, p, c, lane, lo, src, rec0);
+      if (c + 1 < p.nchunks) loader_step<DK, DELTA>(B1, B0, R, p, c + 1, lane, lo, src, rec0);
     }
     if (p.S_out != nullptr && grp == 0) {
       for (int i = lane; i < DK; i += 64)
