@@ -34,7 +34,7 @@ constexpr int NTP = 256;
 // four aligned columns stay contiguous.
 __device__ __forceinline__ int mat_idx(int r, int c) { return r * 64 + (c ^ ((r & 15) << 2)); }
 
-constexpr int kRegion = 16384;  // bytes of each of the three LDS regions
+constexpr int kRegion = 16384;  // bytes of each of the two LDS regions
 
 // Lower 16x16 tiles of a 64x64 matrix, in row order: tile -> (row tile, column tile).
 __device__ constexpr int low_mt(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
@@ -67,6 +67,29 @@ __device__ __forceinline__ void t_column_block(const float* Lf, float* Tf, f4 (&
   }
 }
 
+// A lower-triangular fp32 [64][64] matrix in LDS (mat_idx layout) to the record as its
+// six split A fragments: fragment f, lane ln holds row tok_of(m_f, ln % 16), K columns
+// 32 kb_f + 8 (ln / 16) .. +7; hi at 2f, lo at 2f+1.
+template <size_t OFF>
+__device__ __forceinline__ void split_to_record(const float* src, char* rec, int tid) {
+#pragma unroll
+  for (int r = 0; r < (kTriFrags * 64 + NTP - 1) / NTP; ++r) {
+    const int task = tid + NTP * r;
+    if (task < kTriFrags * 64) {
+      const int f = task >> 6, ln = task & 63;
+      const int row = tok_of(tri_m(f), ln & 15), k0 = 32 * tri_kb(f) + 8 * (ln >> 4);
+      const f4 x0 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0)]);
+      const f4 x1 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0 + 4)]);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      bf8 hi, lo;
+      split8(x, hi, lo);
+      u32x4* dst = reinterpret_cast<u32x4*>(rec + OFF) + (2 * f) * 64 + ln;
+      dst[0] = __builtin_bit_cast(u32x4, hi);
+      dst[64] = __builtin_bit_cast(u32x4, lo);
+    }
+  }
+}
+
 template <int DK, bool DELTA>
 __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   using RC = RecSplit<DK>;
@@ -74,13 +97,15 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   constexpr int NKD = DK / 32;         // K blocks over d_k
   constexpr int NI = CH * NGR / 64;    // direct loads per tile
   static_assert(CH * DK * 2 <= kRegion, "tile fits a region");
-  __shared__ __align__(16) char smem[3 * kRegion + 4 * CH * 4];
+  // Two regions: X, then L; Q, then M, then T (once M is in the record). 33 KiB in all,
+  // so that four workgroups share a CU.
+  __shared__ __align__(16) char smem[2 * kRegion + 4 * CH * 4];
   u32x4* Xs = reinterpret_cast<u32x4*>(smem);
   u32x4* Qs = reinterpret_cast<u32x4*>(smem + kRegion);
   float* Lf = reinterpret_cast<float*>(smem);            // after the Gram products
   float* Mf = reinterpret_cast<float*>(smem + kRegion);  // after the Gram products
-  float* Tf = reinterpret_cast<float*>(smem + 2 * kRegion);
-  float* s_diag = reinterpret_cast<float*>(smem + 3 * kRegion);
+  float* Tf = Mf;                                        // after M's split
+  float* s_diag = reinterpret_cast<float*>(smem + 2 * kRegion);
   float* s_eta = s_diag + CH;
   float* s_g = s_eta + CH;
   float* s_sg = s_g + CH;
@@ -201,45 +226,69 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   __syncthreads();
 
   // ---- 4. masked L (delta) and M, fp32, into LDS; zero the two upper 16x16 tiles that
-  // the output fragments cover (row tiles 0 / 2, column tiles 1 / 3)
+  // the output fragments cover (row tiles 0 / 2, column tiles 1 / 3). The token scalars
+  // of every job are read before the first store (the stores could alias them).
+  float sc_g[JPW][4], sc_sg[JPW][4], sc_eta[JPW][4], sc_gp[JPW][4], sc_sp[JPW][4], sc_gs[JPW], sc_ss[JPW];
+#pragma unroll
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int job = jj * 4 + wave;
+    const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
+    const int s = 16 * nt + n;
+    sc_gs[jj] = s_g[s];
+    sc_ss[jj] = s_sg[s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g + i;
+      sc_g[jj][i] = s_g[t];
+      sc_sg[jj][i] = s_sg[t];
+      sc_eta[jj][i] = s_eta[t];
+      sc_gp[jj][i] = t ? s_g[t - 1] : 0.f;
+      sc_sp[jj][i] = t ? s_sg[t - 1] : 1.f;
+    }
+  }
+  // Branch-free per element: the decay ratio is formed for every element and the masked
+  // ones are replaced by zero (a ratio that overflows there is discarded by the select).
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int job = jj * 4 + wave;
     if (job < NJ) {
-      const bool gram = DELTA && job < 10;
+      const bool gram = DELTA && job < 10;  // wave-uniform
       const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
       float* dst = gram ? Lf : Mf;
       const int s = 16 * nt + n;
-      const float gs = s_g[s], ss = s_sg[s];
+      const float gs = sc_gs[jj], ss = sc_ss[jj];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g + i;
-        float v = 0.f;
-        if (gram) {
-          if (s < t) {
-            const float gp = t ? s_g[t - 1] : 0.f, sp = t ? s_sg[t - 1] : 1.f;
-            v = s_eta[t] * sp * ss * __expf(gp - gs) * acc[jj][i];
-          }
-        } else if (s <= t) {
-          v = s_sg[t] * ss * __expf(s_g[t] - gs) * acc[jj][i];
-        }
-        dst[mat_idx(t, s)] = v;
+        const float coef = gram ? sc_eta[jj][i] * sc_sp[jj][i] : sc_sg[jj][i];
+        const float ga = gram ? sc_gp[jj][i] : sc_g[jj][i];
+        const bool keep = gram ? (s < t) : (s <= t);
+        const float r = __builtin_amdgcn_exp2f((ga - gs) * 1.44269504088896341f);
+        const float v = coef * ss * r * acc[jj][i];
+        dst[mat_idx(t, s)] = keep ? v : 0.f;
       }
     }
   }
-  {
-    // wave w zeroes tile w of: M(0,1), M(2,3), T(0,1), T(2,3)
-    float* dst = wave < 2 ? Mf : Tf;
+  if (wave < 2) {
+    // wave w zeroes tile w of: M(0,1), M(2,3)
     const int r0 = (wave & 1) ? 32 : 0;
-    if (DELTA || wave < 2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[mat_idx(r0 + 4 * g + q, r0 + 16 + n)] = 0.f;
-    }
+    for (int q = 0; q < 4; ++q) Mf[mat_idx(r0 + 4 * g + q, r0 + 16 + n)] = 0.f;
   }
   __syncthreads();
 
-  // ---- 5. T = (I + L)^-1
+  // ---- 5. M as split A fragments into the record (its region then holds T)
+  split_to_record<RC::kM>(Mf, rec, tid);
+
+  // ---- 6. T = (I + L)^-1
   if constexpr (DELTA) {
+    __syncthreads();  // M has left its region
+    if (wave >= 2) {
+      // wave 2 / 3 zeroes T(0,1) / T(2,3)
+      const int r0 = (wave & 1) ? 32 : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Tf[mat_idx(r0 + 4 * g + q, r0 + 16 + n)] = 0.f;
+    }
     f4 Tc[4];
     {
       // diagonal block b = wave: lane (g, n) forms column n of D_b, keeps rows 4g..4g+3
@@ -276,26 +325,9 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     else if (wave == 1) t_column_block<1>(Lf, Tf, Tc, g, n);
     else if (wave == 2) t_column_block<2>(Lf, Tf, Tc, g, n);
     __syncthreads();
-  }
 
-  // ---- 6. T (delta) and M as split A fragments: row tok_of(m, lane % 16), K columns
-  // 32kb + 8 (lane / 16) .. +7
-#pragma unroll
-  for (int r = 0; r < 2 * kTriFrags * 64 / NTP; ++r) {
-    const int task = tid + NTP * r;
-    const int mat = task / (kTriFrags * 64);  // 0: T, 1: M
-    if (mat == 0 && !DELTA) continue;
-    const int f = (task >> 6) % kTriFrags, ln = task & 63;
-    const int row = tok_of(tri_m(f), ln & 15), k0 = 32 * tri_kb(f) + 8 * (ln >> 4);
-    const float* src = mat == 0 ? Tf : Mf;
-    const f4 x0 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0)]);
-    const f4 x1 = *reinterpret_cast<const f4*>(&src[mat_idx(row, k0 + 4)]);
-    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    bf8 hi, lo;
-    split8(x, hi, lo);
-    u32x4* dst = reinterpret_cast<u32x4*>(rec + (mat == 0 ? RC::kT : RC::kM)) + (2 * f) * 64 + ln;
-    dst[0] = __builtin_bit_cast(u32x4, hi);
-    dst[64] = __builtin_bit_cast(u32x4, lo);
+    // ---- 7. T as split A fragments into the record
+    split_to_record<RC::kT>(Tf, rec, tid);
   }
   if (c == 0 && tid < DK) {
     uint16_t v = 0;
