@@ -69,8 +69,10 @@ typedef enum {
 
 typedef enum { FWMEM_RULE_DELTA = 0, FWMEM_RULE_ADDITIVE = 1 } fwmem_rule;
 
-/* Storage type of q, k, v. bf16 inputs run on fp16 MFMA operands (power-of-two
- * scaled, fp32 accumulation); f32 inputs run on fp32 MFMA. */
+/* Storage type of q, k, v. All products accumulate in fp32. bf16 inputs with the
+ * identity feature map and a scalar decay run on bf16 MFMA, with every computed
+ * matrix carried as a bf16 hi + lo pair. Other bf16 inputs run on fp16 MFMA operands
+ * with power-of-two scales. f32 inputs run on fp32 MFMA. */
 typedef enum { FWMEM_F32 = 0, FWMEM_BF16 = 1 } fwmem_dtype;
 
 enum {
