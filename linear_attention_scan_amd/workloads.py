@@ -25,6 +25,10 @@ Recipes (the names match the workload table of the design document):
   delta_long_pc     B=1 H=8 T=131072 d=128, bf16, delta rule, per-key-channel
                     lambda = softplus(N(-5,1)) of shape [B,H,T,dk];
                     beta = sigmoid(N(0,1)); S0 = 0.
+  inner_bf16        B=4 H=8 T=4096 d=128, bf16, inner-product rule (shifted pair,
+                    normalised step, the target written in place of the residual);
+                    delta_bf16's distributions (no workload on the pages fixes them).
+  inner_f32_small   as delta_f32_small with the inner-product rule.
   decode            B=256 H=32 d=128, 1000 single-token steps (delta rule).
                     S0 ~ N(0, 0.02) fp32 with no previous key; per step
                     q,k,v ~ N(0,1) bf16 with q,k normalised; beta = sigmoid(N(0,1));
@@ -44,6 +48,7 @@ import numpy as np
 
 RULE_DELTA = 0
 RULE_ADDITIVE = 1
+RULE_INNER = 2
 PHI_IDENTITY = "identity"
 PHI_ELU1 = "elu1"
 
@@ -190,6 +195,18 @@ def delta_long_pc(seed=0, B=1, H=8, T=131072, d=128):
                      name="delta_long_pc")
 
 
+def inner_bf16(seed=0, B=4, H=8, T=4096, d=128):
+    return make_scan(B=B, H=H, T=T, dk=d, dv=d, dtype="bf16", rule=RULE_INNER,
+                     beta_kind="two_sigmoid", lam_kind="softplus", lam_mu=-4.0, seed=seed,
+                     name="inner_bf16")
+
+
+def inner_f32_small(seed=0, T=256):
+    return make_scan(B=1, H=1, T=T, dk=64, dv=64, dtype="f32", rule=RULE_INNER,
+                     beta_kind="sigmoid", lam_kind="const", lam_const=0.01, seed=seed,
+                     name="inner_f32_small")
+
+
 # ---------------------------------------------------------------- decode (one token per step)
 
 @dataclasses.dataclass
@@ -223,4 +240,6 @@ SCAN_WORKLOADS = {
     "delta_bf16_h16": delta_bf16_h16,
     "additive_bf16": additive_bf16,
     "delta_long_pc": delta_long_pc,
+    "inner_bf16": inner_bf16,
+    "inner_f32_small": inner_f32_small,
 }

@@ -12,7 +12,9 @@ vectorised only over independent heads (b, h). Sources (page titles as printed):
          its normalised gradient step), section 4.1 (read-after-write pairing
          x_t = phi(k_{t-1}), y_t = v_t and the boundary x_1 = 0, eta_1 = 0),
          section 4.2 (Falcon-1 rule, beta in (0,2), per-step descent lemma,
-         NLMS limit).
+         NLMS limit), section 4.3 (the inner-product family, Falcon-1A: the same
+         shifted pair, step size and decay, with the target written in place of the
+         residual).
   [AFFN] hncyxsy.com blog post "attention is also an FFN" (news/211194):
          section 2.1 (S_i = sum_{j<=i} phi(k_j) v_j^T, y_i = phi(q_i)^T S_i),
          section 3.2 (decayed write S_t = lambda S_{t-1} + phi(k_t) v_t^T),
@@ -26,6 +28,9 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
   D4  beta_t, lambda_t are indexed by the target's step t.
   D7  additive rule: the `lam` slot carries the retention gamma_t (None = 1) and
       `beta` an optional write scale (None = 1); pairing is same-index.
+  D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
+      per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
+      required as for the delta rule.
 """
 from __future__ import annotations
 
@@ -33,6 +38,7 @@ import numpy as np
 
 RULE_DELTA = 0
 RULE_ADDITIVE = 1
+RULE_INNER = 2
 
 
 def phi(x: np.ndarray, kind: str) -> np.ndarray:
@@ -84,7 +90,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         qt = phi(Q[:, t], phi_kind)
         kt = phi(K[:, t], phi_kind)
         vt = V[:, t]
-        if rule == RULE_DELTA:
+        if rule in (RULE_DELTA, RULE_INNER):
             # [FWA] 4.1: the pair written at step t is (phi(k_{t-1}), v_t); with no
             # previous key the pair is (0, v_t) with eta = 0, so nothing happens.
             x = np.where(has[:, None], xprev, 0.0)
@@ -100,10 +106,16 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
             # [FWA] 3.2 / 4.2: eta_t = beta_t / (||x_t||^2 + lambda_t + eps).
             den = np.sum(x * x, axis=1) + lam_hat + eps
             eta = np.where(has, Bt[:, t] / np.where(has, den, 1.0), 0.0)
-            # residual against the state before this step's write
-            r = vt - np.einsum("nij,ni->nj", S, x)
             decay = 1.0 - (eta[:, None] * lam_t if per_channel else (eta * lam_t)[:, None])
-            S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]
+            if rule == RULE_DELTA:
+                # residual against the state before this step's write
+                r = vt - np.einsum("nij,ni->nj", S, x)
+                S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]
+            else:
+                # [FWA] 4.3: the negative inner-product loss -<S^T x_t, y_t> +
+                # (lambda_t/2)|S|^2 has gradient lambda_t S - x_t y_t^T, so the step
+                # writes the target y_t = v_t itself, with no residual.
+                S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * vt[:, None, :]
         elif rule == RULE_ADDITIVE:
             # [AFFN] 3.2: S_t = gamma_t S_{t-1} + phi(k_t) v_t^T (times an optional
             # write scale beta_t, reading D7).

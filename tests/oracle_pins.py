@@ -18,7 +18,7 @@ from fractions import Fraction as Fr
 
 import numpy as np
 
-DELTA, ADD = 0, 1
+DELTA, ADD, INNER = 0, 1, 2
 
 
 def _unit_rows(rng, n, d):
@@ -347,6 +347,162 @@ def pin_p12_min_norm_store(orc):
     np.testing.assert_allclose(S[0, 0], S_star, rtol=0, atol=1e-9)
 
 
+def _shifted_eta(k, beta, lam, eps):
+    """eta_t of the shifted pair for one head, brute force: x_1 = 0 with eta_1 = 0,
+    then x_t = k_{t-1}, eta_t = beta_t / (|x_t|^2 + lambda_t + eps) ([FWA] 4.1, 4.2)."""
+    T = k.shape[0]
+    eta = np.zeros(T)
+    for t in range(1, T):
+        eta[t] = beta[t] / (float(k[t - 1] @ k[t - 1]) + lam[t] + eps)
+    return eta
+
+
+def pin_p13_inner_hebbian_sum(orc):
+    """[FWA] 4.3: with lambda = 0 the inner-product rule is a pure additive write of
+    the shifted pair, so S_T = sum_{t>=2} eta_t k_{t-1} v_t^T and
+    o_t = sum_{2<=j<=t} eta_j (q_t . k_{j-1}) v_j, both brute-forced."""
+    rng = np.random.default_rng(31)
+    T, dk, dv, eps = 12, 5, 3, 1e-3
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    beta = rng.uniform(0.1, 1.9, T)
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), None, rule=INNER, eps=eps)
+    eta = _shifted_eta(k, beta, np.zeros(T), eps)
+    S_ref = np.zeros((dk, dv))
+    for j in range(1, T):
+        S_ref += eta[j] * np.outer(k[j - 1], v[j])
+    np.testing.assert_allclose(S[0, 0], S_ref, rtol=0, atol=1e-12)
+    for t in range(T):
+        ref = np.zeros(dv)
+        for j in range(1, t + 1):
+            ref += eta[j] * float(q[t] @ k[j - 1]) * v[j]
+        np.testing.assert_allclose(o[0, 0, t], ref, rtol=0, atol=1e-12)
+
+
+def pin_p14_inner_decayed_sum(orc):
+    """[FWA] 4.3 with lambda > 0, unrolled: each write eta_j x_j v_j^T is scaled by the
+    decays of the later steps, S_T = sum_j diag(prod_{s>j} a_s) eta_j x_j v_j^T with
+    a_s = 1 - eta_s lambda_s (a d_k-vector for per-channel lambda, eta's denominator
+    taking the channel max, reading D1), starting from a nonzero S_0 that decays as a
+    whole. The read o_t = S_t^T q_t is checked against the same unrolled sum."""
+    rng = np.random.default_rng(32)
+    T, dk, dv, eps = 10, 4, 3, 1e-6
+    for per_channel in (False, True):
+        q = rng.standard_normal((T, dk))
+        k = rng.standard_normal((T, dk))
+        v = rng.standard_normal((T, dv))
+        beta = rng.uniform(0.1, 1.9, T)
+        lam = rng.uniform(0.05, 0.6, (T, dk) if per_channel else T)
+        S0 = rng.standard_normal((dk, dv))
+        o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(lam), rule=INNER, eps=eps,
+                              per_channel=per_channel, S0=_bh(S0))
+        lam_hat = lam.max(axis=1) if per_channel else lam
+        eta = _shifted_eta(k, beta, lam_hat, eps)
+        a = [1.0 - eta[s] * (lam[s] if per_channel else np.full(dk, lam[s])) for s in range(T)]
+
+        def state_at(t):  # S_t for t = 0..T-1 (after step t), brute force
+            acc = S0 * np.prod([a[s] for s in range(0, t + 1)], axis=0)[:, None]
+            for j in range(1, t + 1):
+                dec = np.prod([a[s] for s in range(j + 1, t + 1)], axis=0) if j < t else np.ones(dk)
+                acc = acc + (dec * eta[j] * k[j - 1])[:, None] * v[j][None, :]
+            return acc
+
+        np.testing.assert_allclose(S[0, 0], state_at(T - 1), rtol=0, atol=1e-12)
+        for t in range(T):
+            np.testing.assert_allclose(o[0, 0, t], state_at(t).T @ q[t], rtol=0, atol=1e-12)
+
+
+def _inner_loss(S, x, y, lam):
+    return -float(x @ S @ y) + 0.5 * lam * float(np.sum(S * S))
+
+
+def pin_p15_inner_gradient_step(orc, trials=300):
+    """[FWA] 4.3: each step is a gradient step of size eta_t on the instantaneous loss
+    l_t(S) = -<S^T x_t, y_t> + (lambda_t/2)|S|_F^2. That loss is quadratic with
+    Hessian lambda_t I, so the step changes it by exactly
+    -eta |g|^2 (1 - lambda eta / 2) with g = lambda S_{t-1} - x_t y_t^T, which is a
+    decrease whenever beta_t in (0, 2)."""
+    rng = np.random.default_rng(33)
+    dk, dv = 5, 4
+    for _ in range(trials):
+        S0 = rng.standard_normal((dk, dv))
+        x = rng.standard_normal(dk) * rng.uniform(0.1, 3.0)
+        y = rng.standard_normal(dv)
+        beta = rng.uniform(0.05, 1.95)
+        lam = rng.uniform(0.01, 2.0)
+        eps = 1e-6
+        k = np.stack([x, rng.standard_normal(dk)])
+        v = np.stack([rng.standard_normal(dv), y])
+        _, S, _, _ = orc.scan(_bh(np.zeros((2, dk))), _bh(k), _bh(v), _bh(np.array([1.0, beta])),
+                              _bh(np.array([0.3, lam])), rule=INNER, eps=eps, S0=_bh(S0))
+        # step 1 has no previous key, so S after step 1 is S0 and step 2 writes (x, y)
+        eta = beta / (float(x @ x) + lam + eps)
+        g = lam * S0 - np.outer(x, y)
+        before, after = _inner_loss(S0, x, y, lam), _inner_loss(S[0, 0], x, y, lam)
+        expect = -eta * float(np.sum(g * g)) * (1.0 - 0.5 * lam * eta)
+        assert after <= before + 1e-12
+        assert abs((after - before) - expect) <= 1e-10 * max(1.0, abs(expect))
+
+
+def pin_p16_inner_first_step_noop(orc):
+    """[FWA] 4.1: x_1 = 0 and eta_1 = 0 make the first write of a sequence a no-op for
+    the inner-product rule too: S_1 equals S_0 exactly and o_1 = S_0^T q_1."""
+    rng = np.random.default_rng(34)
+    dk, dv = 6, 5
+    S0 = rng.standard_normal((dk, dv))
+    q = rng.standard_normal((1, dk))
+    k = rng.standard_normal((1, dk))
+    v = rng.standard_normal((1, dv))
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.array([1.7])), _bh(np.array([0.9])),
+                          rule=INNER, S0=_bh(S0))
+    assert np.array_equal(S[0, 0], S0)
+    np.testing.assert_allclose(o[0, 0, 0], S0.T @ q[0], rtol=0, atol=1e-13)
+
+
+def pin_p17_inner_is_shifted_linear_attention(orc):
+    """[FWA] 4.3 calls the inner-product rule the shifted-pair version of linear
+    attention's accumulation: it equals the additive rule (pinned by P1, P2, P2')
+    run on the keys shifted by one token, with write scale eta_t and retention
+    1 - eta_t lambda_t computed here by brute force."""
+    rng = np.random.default_rng(35)
+    T, dk, dv, eps = 15, 6, 4, 1e-6
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    beta = rng.uniform(0.1, 1.9, T)
+    lam = rng.uniform(0.0, 0.5, T)
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(lam), rule=INNER, eps=eps)
+    eta = _shifted_eta(k, beta, lam, eps)
+    k_shift = np.vstack([np.zeros((1, dk)), k[:-1]])
+    o2, S2, _, _ = orc.scan(_bh(q), _bh(k_shift), _bh(v), _bh(eta), _bh(1.0 - eta * lam), rule=ADD)
+    np.testing.assert_allclose(S[0, 0], S2[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0, 0], o2[0, 0], rtol=0, atol=1e-12)
+
+
+def pin_p9_hand_inner(orc):
+    """A case worked by hand ([AFFN] 5.2's advice to check a tiny case), in exact
+    fractions. d_k = 2, d_v = 1, beta = 1, lambda = 1/2, eps = 0, q_t = (1, 1),
+    k_1 = (1, 0), k_2 = (0, 2), v = (5, 3, 7):
+      t = 1: no previous key, S_1 = 0, o_1 = 0;
+      t = 2: x = (1, 0), eta = 1/(1 + 1/2) = 2/3, a = 2/3, S_2 = (2/3)(1, 0)^T 3 = (2, 0)^T,
+             o_2 = 2;
+      t = 3: x = (0, 2), eta = 1/(4 + 1/2) = 2/9, a = 8/9,
+             S_3 = (8/9)(2, 0)^T + (2/9)(0, 2)^T 7 = (16/9, 28/9)^T, o_3 = 44/9."""
+    q = np.ones((3, 2))
+    k = np.array([[1.0, 0.0], [0.0, 2.0], [3.0, -1.0]])
+    v = np.array([[5.0], [3.0], [7.0]])
+    o, S, xp, h = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.ones(3)), _bh(np.full(3, 0.5)),
+                           rule=INNER, eps=0.0)
+    exp_o = [Fr(0), Fr(2), Fr(44, 9)]
+    exp_S = [Fr(16, 9), Fr(28, 9)]
+    for t in range(3):
+        assert abs(o[0, 0, t, 0] - float(exp_o[t])) < 1e-14
+    for i in range(2):
+        assert abs(S[0, 0, i, 0] - float(exp_S[i])) < 1e-14
+    assert np.array_equal(xp[0, 0], k[2]) and h[0, 0] == 1
+
+
 def pin_relerr_metric(orc):
     """The parity metric max|x - ref| / rms(ref) on a case worked by hand."""
     ref = np.array([3.0, -4.0])          # rms = sqrt((9 + 16)/2) = 5/sqrt(2)
@@ -369,5 +525,11 @@ ALL_PINS = [
     pin_p10_state_carry,
     pin_p11_interference_ratio,
     pin_p12_min_norm_store,
+    pin_p13_inner_hebbian_sum,
+    pin_p14_inner_decayed_sum,
+    pin_p15_inner_gradient_step,
+    pin_p16_inner_first_step_noop,
+    pin_p17_inner_is_shifted_linear_attention,
+    pin_p9_hand_inner,
     pin_relerr_metric,
 ]

@@ -34,6 +34,13 @@ MUTANTS = {
                             'r = vt - np.einsum("nij,ni->nj", S, qt)'),
     "write_uses_value_not_residual": ("eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                                       "eta[:, None, None] * x[:, :, None] * vt[:, None, :]"),
+    "inner_writes_residual": ("eta[:, None, None] * x[:, :, None] * vt[:, None, :]",
+                              "eta[:, None, None] * x[:, :, None] * (vt - np.einsum(\"nij,ni->nj\", S, x))[:, None, :]"),
+    "inner_same_index_pairing": ("* x[:, :, None] * vt[:, None, :]", "* kt[:, :, None] * vt[:, None, :]"),
+    "inner_no_decay": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * vt",
+                       "S = S + eta[:, None, None] * x[:, :, None] * vt"),
+    "inner_unnormalised_step": ("eta[:, None, None] * x[:, :, None] * vt[:, None, :]",
+                                "Bt[:, t][:, None, None] * x[:, :, None] * vt[:, None, :]"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }

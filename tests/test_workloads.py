@@ -40,3 +40,10 @@ def test_decode_steps_are_reproducible():
     assert np.array_equal(s0.q, s1.q) and not np.array_equal(s0.q, s2.q)
     S0 = wl.decode_state0(0, B=2, H=2, d=16)
     assert S0.shape == (2, 2, 16, 16) and abs(float(S0.std()) - 0.02) < 0.005
+
+
+def test_inner_recipe():
+    w = wl.inner_bf16(seed=2, B=1, H=2, T=30, d=16)
+    d = wl.delta_bf16(seed=2, B=1, H=2, T=30, d=16)
+    assert w.rule == wl.RULE_INNER and w.name == "inner_bf16"
+    assert np.array_equal(w.k, d.k) and np.array_equal(w.beta, d.beta) and np.array_equal(w.lam, d.lam)
