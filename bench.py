@@ -121,16 +121,18 @@ def scan_mfma_flops(w, C=64):
     """MFMA flops executed per launch of each kernel (lower-triangular K blocks skipped).
 
     prep, per (head, chunk): 10 lower 16x16 tiles over K = d_k for each Gram product
-    (X X^T for the delta rule, and Q X^T): 2*16*16*d_k flops per tile.
+    (X X^T for the shifted-pair rules, delta and inner-product, and Q X^T):
+    2*16*16*d_k flops per tile.
     propagate, per (head, chunk): X S, Q S and X^T U are 2*C*d_k*d_v each; T R and M U
-    take 6 MFMA blocks of 16x16x32 per 16 value columns. The additive rule has no X S
-    and no T R. Each product is counted once: the split kernels evaluate a product with a
+    take 6 MFMA blocks of 16x16x32 per 16 value columns. The additive and inner-product
+    rules have no X S and no T R. Each product is counted once: the split kernels evaluate a product with a
     hi/lo operand as two or three MFMAs, and those repeats are not counted."""
     nch = (w.T + C - 1) // C
     units = w.B * w.H * nch
     delta = w.rule == 0
+    shifted = w.rule != 1
     tile = 2 * 16 * 16 * w.dk
-    prep = units * (2 if delta else 1) * 10 * tile
+    prep = units * (2 if shifted else 1) * 10 * tile
     dense = 2 * C * w.dk * w.dv
     tri = 6 * (2 * 16 * 16 * 32) * (w.dv // 16)
     prop = units * ((3 * dense + 2 * tri) if delta else (2 * dense + tri))
@@ -266,7 +268,7 @@ def main():
         "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
-                   "rule": "delta" if w.rule == 0 else "additive", "inputs": w.dtype,
+                   "rule": ("delta", "additive", "inner")[w.rule], "inputs": w.dtype,
                    "chunk": 64, "seed": 0},
         "roofline": roofline,
         "kernels": {names[n]: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),

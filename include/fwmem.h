@@ -15,12 +15,18 @@
  *   an FFN", sections 2.1 and 3.2):
  *       S_t = gamma_t S_{t-1} + beta_t phi(k_t) v_t^T   (same-index pairing).
  *
- *   Read (both rules, after the write): o_t = S_t^T phi(q_t).
+ *   INNER (inner-product family, Falcon-1A; the reading notes above, section 4.3:
+ *   the gradient step on the negative inner-product loss writes the target itself):
+ *       x_t, eta_t and the first-token boundary as for DELTA,
+ *       S_t = (1 - eta_t lambda_t) S_{t-1} + eta_t x_t y_t^T   (no residual).
+ *
+ *   Read (every rule, after the write): o_t = S_t^T phi(q_t).
  *
  * phi is the identity, or elu(x)+1 (the blog post above, section 4.1) with
  * FWMEM_PHI_ELU1. With FWMEM_LAMBDA_PER_CHANNEL, lambda (delta) or gamma
  * (additive) is a d_k-vector per token: the decay diag(1 - eta_t lambda_t) (resp.
- * diag(gamma_t)) scales the rows of S, and eta's denominator uses max_i lambda_{t,i}.
+ * diag(gamma_t)) scales the rows of S, and eta's denominator (DELTA, INNER) uses
+ * max_i lambda_{t,i}.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are caller-owned DEVICE pointers, dense, row-major, in
@@ -67,7 +73,7 @@ typedef enum {
   FWMEM_EWORKSPACE = -6    /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
 } fwmem_status;
 
-typedef enum { FWMEM_RULE_DELTA = 0, FWMEM_RULE_ADDITIVE = 1 } fwmem_rule;
+typedef enum { FWMEM_RULE_DELTA = 0, FWMEM_RULE_ADDITIVE = 1, FWMEM_RULE_INNER = 2 } fwmem_rule;
 
 /* Storage type of q, k, v. All products accumulate in fp32. bf16 inputs with the
  * identity feature map and a scalar decay run on bf16 MFMA, with every computed
@@ -109,10 +115,11 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
  *
  *   q, k   [B][H][T][dk]  dtype      (required)
  *   v      [B][H][T][dv]  dtype      (required)
- *   beta   [B][H][T]      float32    DELTA: required, beta in (0, 2) expected, never
- *                                    clamped. ADDITIVE: optional write scale (NULL = 1).
+ *   beta   [B][H][T]      float32    DELTA, INNER: required, beta in (0, 2) expected,
+ *                                    never clamped. ADDITIVE: optional write scale
+ *                                    (NULL = 1).
  *   lambda [B][H][T] or [B][H][T][dk] float32
- *                                    DELTA: ridge lambda >= 0 (NULL = 0).
+ *                                    DELTA, INNER: ridge lambda >= 0 (NULL = 0).
  *                                    ADDITIVE: retention gamma in [0, 1] (NULL = 1).
  *                                    The decay 1 - eta*lambda (resp. gamma) must lie in
  *                                    [-1, 1]; exact zero is allowed.

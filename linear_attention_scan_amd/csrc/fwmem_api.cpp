@@ -51,7 +51,8 @@ fwmem_status check_shape(const fwmem_shape* s, bool need_T) {
 
 fwmem_status check_mode(const fwmem_mode* m) {
   if (m == nullptr) return FWMEM_EINVAL;
-  if (m->rule != FWMEM_RULE_DELTA && m->rule != FWMEM_RULE_ADDITIVE) return FWMEM_EINVAL;
+  if (m->rule != FWMEM_RULE_DELTA && m->rule != FWMEM_RULE_ADDITIVE && m->rule != FWMEM_RULE_INNER)
+    return FWMEM_EINVAL;
   if ((m->flags & ~kKnownFlags) != 0) return FWMEM_EINVAL;
   if (!std::isfinite(m->eps) || m->eps < 0.f) return FWMEM_EINVAL;
   if (m->chunk != 0 && m->chunk != kChunk) return FWMEM_EUNSUPPORTED;
@@ -131,14 +132,15 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
 
   const Sizes z = sizes_of(shape);
   if (z.BH == 0) return FWMEM_OK;
-  const bool delta = mode->rule == FWMEM_RULE_DELTA;
+  // the delta and inner-product rules take beta as their step size
+  const bool needs_beta = mode->rule != FWMEM_RULE_ADDITIVE;
   const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
   const size_t T = (size_t)shape->T;
   const size_t es = esize(shape->dtype);
 
   if (T > 0) {
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return FWMEM_EINVAL;
-    if (delta && beta == nullptr) return FWMEM_EINVAL;
+    if (needs_beta && beta == nullptr) return FWMEM_EINVAL;
   }
   // alignment
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -197,7 +199,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   p.dk = shape->dk;
   p.dv = shape->dv;
   p.nchunks = (int)((T + kChunk - 1) / kChunk);
-  p.delta = delta ? 1 : 0;
+  p.rule = mode->rule;
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
   p.flags = mode->flags;
   p.eps = mode->eps;
@@ -251,11 +253,12 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
   if (!fwmem::step_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   const Sizes z = sizes_of(shape);
   if (z.BH == 0) return FWMEM_OK;
-  const bool delta = mode->rule == FWMEM_RULE_DELTA;
+  // the delta and inner-product rules take beta as their step size
+  const bool needs_beta = mode->rule != FWMEM_RULE_ADDITIVE;
   const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || S_out == nullptr)
     return FWMEM_EINVAL;
-  if (delta && beta == nullptr) return FWMEM_EINVAL;
+  if (needs_beta && beta == nullptr) return FWMEM_EINVAL;
   const size_t es = esize(shape->dtype);
   if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(out, 16) ||
       !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(beta, 4) || !aligned(lambda, 4))
@@ -290,7 +293,7 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
   p.BH = (int)z.BH;
   p.dk = shape->dk;
   p.dv = shape->dv;
-  p.delta = delta ? 1 : 0;
+  p.rule = mode->rule;
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
   p.flags = mode->flags;
   p.eps = mode->eps;

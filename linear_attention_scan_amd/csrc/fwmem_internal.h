@@ -16,6 +16,23 @@ enum : uint32_t {
 
 constexpr int kChunk = 64;  // scan chunk length (tokens)
 
+// Write rules (the values of fwmem_rule).
+enum : int { kRuleDelta = 0, kRuleAdditive = 1, kRuleInner = 2 };
+
+// What each rule needs of the kernels:
+//   shift: the written key is the previous token's (x_t = phi(k_{t-1})), with the key
+//          carried across calls in the state and a no-op first step at a sequence start;
+//   solve: the write is the residual, which couples the chunk's tokens through the
+//          unit-lower-triangular solve (delta rule only);
+//   nlms:  the step size is eta_t = beta_t / (|x_t|^2 + lambda_t + eps) and the decay
+//          is 1 - eta_t lambda_t (otherwise beta is a write scale and lambda the decay).
+template <int RULE>
+struct Rule {
+  static constexpr bool shift = RULE != kRuleAdditive;
+  static constexpr bool solve = RULE == kRuleDelta;
+  static constexpr bool nlms = RULE != kRuleAdditive;
+};
+
 // Pointers are device pointers; optional ones may be null.
 struct ScanParams {
   const void* q;
@@ -32,7 +49,7 @@ struct ScanParams {
   int32_t* has_out;      // [BH]     (with S_out)
   char* ws;              // workspace records
   int BH, T, dk, dv, nchunks;
-  int delta;             // 1: delta rule, 0: additive
+  int rule;              // kRuleDelta, kRuleAdditive or kRuleInner
   int bf16;              // 1: bf16 inputs, 0: fp32
   uint32_t flags;
   float eps;
@@ -52,7 +69,8 @@ struct StepParams {
   float* xprev_out;
   int32_t* has_out;
   int BH, dk, dv;
-  int delta, bf16;
+  int rule;  // kRuleDelta, kRuleAdditive or kRuleInner
+  int bf16;
   uint32_t flags;
   float eps;
 };

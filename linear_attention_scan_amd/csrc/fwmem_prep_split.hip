@@ -4,7 +4,8 @@
 //
 // With Gamma_t the decay since the chunk start ("Fast Weight Attention for Continual
 // Learning" reading notes, sections 4.1-4.4; the algebra is derived in fwmem_scan.hip):
-//   L_ts = eta_t (Gamma_{t-1}/Gamma_s) x_t . x_s  (s < t),   T = (I + L)^-1  (delta rule)
+//   L_ts = eta_t (Gamma_{t-1}/Gamma_s) x_t . x_s  (s < t),   T = (I + L)^-1  (delta rule;
+//   the inner-product rule shares the shifted keys and eta_t but has no solve)
 //   M_ts = (Gamma_t / Gamma_s) q_t . x_s          (s <= t)
 // and the per-token row factors fP = eta Gamma_{t-1}, fV = eta, fO = Gamma_t,
 // fU = Gamma_C / Gamma_t with Gamma_C the decay over the whole chunk.
@@ -90,9 +91,10 @@ __device__ __forceinline__ void split_to_record(const float* src, char* rec, int
   }
 }
 
-template <int DK, bool DELTA>
+template <int DK, int RULE>
 __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   using RC = RecSplit<DK>;
+  using R = Rule<RULE>;
   constexpr int NGR = DK / 8;          // 16-byte granules per X / Q row
   constexpr int NKD = DK / 32;         // K blocks over d_k
   constexpr int NI = CH * NGR / 64;    // direct loads per tile
@@ -122,9 +124,9 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   const uint16_t* qb = static_cast<const uint16_t*>(p.q) + rowbase * DK;
   char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
 
-  // ---- 1. rows into LDS (X starts one row early for the delta rule: x_t = k_{t-1})
+  // ---- 1. rows into LDS (X starts one row early for the shifted pair: x_t = k_{t-1})
   {
-    const __amdgpu_buffer_rsrc_t rx = rsrc(DELTA ? kb - DK : kb, (uint32_t)(T * DK * 2));
+    const __amdgpu_buffer_rsrc_t rx = rsrc(R::shift ? kb - DK : kb, (uint32_t)(T * DK * 2));
     const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (uint32_t)(T * DK * 2));
     const uint32_t so = (uint32_t)(t0 * DK * 2);
 #pragma unroll
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
       const int row = pos / NGR;
       const uint32_t off = (uint32_t)(row * DK + 8 * ((pos % NGR) ^ xswz<DK>(row))) * 2u;
       // the row before token 0 is the carried key, written below
-      dma16(rx, (DELTA && c == 0 && row == 0) ? 0x80000000u : off, so, &Xs[64 * i]);
+      dma16(rx, (R::shift && c == 0 && row == 0) ? 0x80000000u : off, so, &Xs[64 * i]);
       dma16(rq, off, so, &Qs[64 * i]);
     }
   }
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     if (p.lam != nullptr) g_lam = p.lam[rowbase + t0 + lane];
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (DELTA && c == 0 && tid < NGR) {
+  if (R::shift && c == 0 && tid < NGR) {
     // threads tid < NGR issued the loads of row 0, so their own wait covers them
     u32x4 w = {0u, 0u, 0u, 0u};
     if (has_in) {
@@ -157,8 +159,9 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   }
   __syncthreads();
 
-  // ---- 2. Gram products: jobs over the 10 lower 16x16 tiles of X X^T (delta) and Q X^T
-  constexpr int NJ = DELTA ? 20 : 10;
+  // ---- 2. Gram products: jobs over the 10 lower 16x16 tiles of X X^T (shifted pair: its
+  // diagonal gives |x_t|^2, its lower part L for the delta rule) and Q X^T
+  constexpr int NJ = R::shift ? 20 : 10;
   constexpr int JPW = (NJ + 3) / 4;
   auto rowfrag = [&](const u32x4* S, int row, int kq) -> bf8 {
     return __builtin_bit_cast(bf8, S[row * NGR + ((4 * kq + g) ^ xswz<DK>(row))]);
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     const int job = jj * 4 + wave;
     acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
     if (job < NJ) {
-      const bool gram = DELTA && job < 10;
+      const bool gram = R::shift && job < 10;
       const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
       const u32x4* A = gram ? Xs : Qs;
 #pragma unroll
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     const int t = lane, tau = t0 + t;
     const bool active = tau < T;
     float eta = 0.f, a = 1.f;
-    if (DELTA) {
+    if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
       if (hasx) eta = g_beta / (s_diag[t] + g_lam + p.eps);
       a = 1.f - eta * g_lam;
@@ -251,8 +254,8 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int job = jj * 4 + wave;
-    if (job < NJ) {
-      const bool gram = DELTA && job < 10;  // wave-uniform
+    if (job < NJ && (R::solve || !(R::shift && job < 10))) {
+      const bool gram = R::shift && job < 10;  // wave-uniform
       const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
       float* dst = gram ? Lf : Mf;
       const int s = 16 * nt + n;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   split_to_record<RC::kM>(Mf, rec, tid);
 
   // ---- 6. T = (I + L)^-1
-  if constexpr (DELTA) {
+  if constexpr (R::solve) {
     __syncthreads();  // M has left its region
     if (wave >= 2) {
       // wave 2 / 3 zeroes T(0,1) / T(2,3)
@@ -331,23 +334,29 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   }
   if (c == 0 && tid < DK) {
     uint16_t v = 0;
-    if (DELTA && has_in) v = f32_to_bf16_bits(p.xprev_in[(size_t)bh * DK + tid]);
+    if (R::shift && has_in) v = f32_to_bf16_bits(p.xprev_in[(size_t)bh * DK + tid]);
     reinterpret_cast<uint16_t*>(rec + RC::kX0)[tid] = v;
   }
 }
 
-template <int DK, bool DELTA>
+template <int DK, int RULE>
 hipError_t launch_t(const ScanParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)p.BH * p.nchunks);
-  hipLaunchKernelGGL((prep_split_kernel<DK, DELTA>), dim3(grid), dim3(NTP), 0, st, p);
+  hipLaunchKernelGGL((prep_split_kernel<DK, RULE>), dim3(grid), dim3(NTP), 0, st, p);
   return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const ScanParams& p, hipStream_t st) {
+  if (p.rule == kRuleDelta) return launch_t<DK, kRuleDelta>(p, st);
+  if (p.rule == kRuleInner) return launch_t<DK, kRuleInner>(p, st);
+  return launch_t<DK, kRuleAdditive>(p, st);
 }
 
 }  // namespace
 
 hipError_t launch_prep_split(const ScanParams& p, hipStream_t st) {
-  if (p.dk == 64) return p.delta ? launch_t<64, true>(p, st) : launch_t<64, false>(p, st);
-  return p.delta ? launch_t<128, true>(p, st) : launch_t<128, false>(p, st);
+  return p.dk == 64 ? launch_dk<64>(p, st) : launch_dk<128>(p, st);
 }
 
 }  // namespace fwmem

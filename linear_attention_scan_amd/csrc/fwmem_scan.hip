@@ -17,8 +17,10 @@
 //   O   = diag(Gamma) Q S + M U,  M_ts = (Gamma_t/Gamma_s) q_t . x_s  (s <= t)
 //   S' = Gamma_C S + X^T diag(Gamma_C / Gamma) U.
 // The additive rule ("attention is also an FFN", sections 2.1 and 3.2) is the same
-// skeleton with U = diag(beta) V and no solve. Per-key-channel decay turns the
-// Gamma ratios into d_k-vectors that are folded into the X / Q operands.
+// skeleton with U = diag(beta) V and no solve. The inner-product rule (section 4.3 of
+// the notes) keeps the delta rule's shifted keys, eta_t and decay, and writes
+// U = diag(eta) V with no solve. Per-key-channel decay turns the Gamma ratios into
+// d_k-vectors that are folded into the X / Q operands.
 //
 // Two kernels:
 //   prep_kernel: one workgroup per (head, chunk), fully parallel. Builds the chunk's
@@ -102,8 +104,9 @@ struct PrepLds {
   static constexpr size_t kBytes = 4 * kReg + kSmall;
 };
 
-template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
+template <typename InT, int DK, int RULE, bool PC, bool ELU>
 __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
+  using R = Rule<RULE>;
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   const int t0 = c * CH;
   const size_t rowbase = (size_t)bh * p.T;
   const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
-  const float* x0 = (DELTA && has_in) ? p.xprev_in + (size_t)bh * DK : nullptr;
+  const float* x0 = (R::shift && has_in) ? p.xprev_in + (size_t)bh * DK : nullptr;
   const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
   const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
 
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     if (!PC && p.lam != nullptr) g_lam = p.lam[ti];
   }
 
-  // ---- row staging: x rows (shifted keys for the delta rule) and q rows, phi
+  // ---- row staging: x rows (shifted keys for the shifted pair) and q rows, phi
   // applied, scaled by one power of two per matrix, into LDS as MFMA operands.
   op_t* Xs = reinterpret_cast<op_t*>(reg[0]);
   op_t* Qs = reinterpret_cast<op_t*>(reg[1]);
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
 #pragma unroll
       for (int j = 0; j < VW; ++j) { xr[ps][j] = 0.f; qr[ps][j] = 0.f; }
       if (tau < p.T) {
-        const int src = DELTA ? tau - 1 : tau;
+        const int src = R::shift ? tau - 1 : tau;
         if (src >= 0) {
           In<InT>::load(kbase + (uint32_t)(src * DK + col), xr[ps]);
           if (ELU) {
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   }
 
   // Per-channel: eta's denominator uses the channel max of lambda.
-  if (DELTA && PC) {
+  if (R::nlms && PC) {
     constexpr int TPRL = DK / 4, RPPL = NT / TPRL, NPL = CH / RPPL;
 #pragma unroll
     for (int ps = 0; ps < NPL; ++ps) {
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     const int tau = t0 + t;
     const bool active = tau < p.T;
     float eta = 0.f, a = 1.f;
-    if (DELTA) {
+    if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
       const float lam_t = PC ? s_lam[t] : g_lam;
       if (hasx) eta = g_beta / (s_norm[t] + lam_t + p.eps);
@@ -275,9 +278,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
 #pragma unroll
       for (int t = 0; t < CH; ++t) {
         const int tau = t0 + t;
-        float lam = DELTA ? 0.f : 1.f;
+        float lam = R::nlms ? 0.f : 1.f;
         if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
-        const float a = DELTA ? 1.f - s_eta[t] * lam : lam;
+        const float a = R::nlms ? 1.f - s_eta[t] * lam : lam;
         gs += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;
         gcol[t] = gs;
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
             mBX = fmaxf(mBX, fabsf(vBX));
             mAM = fmaxf(mAM, fabsf(vAM));
           } else {
-            if (DELTA) AL[t * LDX + ip] = Pol::cvt(vAL * sAL);
+            if (R::solve) AL[t * LDX + ip] = Pol::cvt(vAL * sAL);
             BX[t * LDX + ip] = Pol::cvt(vBX * sBX);
             AM[t * LDX + ip] = Pol::cvt(vAM * sAM);
           }
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       const int mat = job >> 4;  // 0: L from X X^T, 1: M from Q X^T
       const int mt = (job >> 2) & 3, nt = job & 3;
       acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
-      if (mt >= nt && (mat == 1 || DELTA)) {
+      if (mt >= nt && (mat == 1 || R::solve)) {
         const op_t* arow = (mat == 0 ? A_L : A_M) + (16 * mt + n) * LDX;
         const op_t* brow = B_X + (16 * nt + n) * LDX;
 #pragma unroll
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       const int job = wave + NW * jj;
       const int mat = job >> 4;
       const int mt = (job >> 2) & 3, nt = job & 3;
-      if (mat == 0 && !DELTA) continue;
+      if (mat == 0 && !R::solve) continue;
       float* dst = mat == 0 ? Lf : Mf;
       const int s = 16 * nt + n;
 #pragma unroll
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   __syncthreads();
 
   // T = (I + L)^-1 by blocked forward substitution (16x16 blocks, fp32).
-  if (DELTA) {
+  if (R::solve) {
     constexpr int NB = CH / 16;
     if (wave == 0) {
       const int b = lane >> 4, j = lane & 15;
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     }
   }
 
-  // Write T (delta) and M, scaled and in operand order, plus the token factors.
+  // Write T (delta rule) and M, scaled and in operand order, plus the token factors.
   char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
   {
     const int t = tid >> 2, c0 = (tid & 3) * 16;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     float mt_ = 0.f, mm_ = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      tv[j] = DELTA ? Tf[t * LDF + c0 + j] : 0.f;
+      tv[j] = R::solve ? Tf[t * LDF + c0 + j] : 0.f;
       mv[j] = Mf[t * LDF + c0 + j];
       mt_ = fmaxf(mt_, fabsf(tv[j]));
       mm_ = fmaxf(mm_, fabsf(mv[j]));
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int k0 = c0 + 4 * r4;
-      if (DELTA)
+      if (R::solve)
         Pol::store4(Tg, k0, tv[4 * r4] * sT, tv[4 * r4 + 1] * sT, tv[4 * r4 + 2] * sT, tv[4 * r4 + 3] * sT);
       Pol::store4(Mg, k0, mv[4 * r4] * sM, mv[4 * r4 + 1] * sM, mv[4 * r4 + 2] * sM, mv[4 * r4 + 3] * sM);
     }
@@ -539,8 +542,9 @@ struct PropLds {
   static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 4 * NW + 16);
 };
 
-template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
+template <typename InT, int DK, int RULE, bool PC, bool ELU>
 __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
+  using R = Rule<RULE>;
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 
   const char* rec0 = p.ws + (size_t)bh * p.nchunks * RC::kBytes;
   const bool has_in = reinterpret_cast<const float*>(rec0 + RC::kSc)[2] != 0.f;
-  const float* x0 = (DELTA && has_in) ? reinterpret_cast<const float*>(rec0 + RC::kX0) : nullptr;
+  const float* x0 = (R::shift && has_in) ? reinterpret_cast<const float*>(rec0 + RC::kX0) : nullptr;
 
   const int col = (tid % TPR) * VW;    // row staging: this thread's columns
   const int vcol = (tid % TPRv) * VW;  // value tile: this thread's columns
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
             const int t = 2 * tp + h;
             float x[VW];
             In<InT>::decode(px[2 * r + h], x);
-            if (DELTA && t0 + t == 0) {
+            if (R::shift && t0 + t == 0) {
 #pragma unroll
               for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[8 * cg + j] : 0.f;
             } else if (ELU && (valid >> (2 * r + h) & 1u)) {
@@ -665,7 +669,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           const int t = ps * RPP + tid / TPR;
           float x[VW];
           In<InT>::decode(px[ps], x);
-          if (DELTA && t0 + t == 0) {
+          if (R::shift && t0 + t == 0) {
 #pragma unroll
             for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[col + j] : 0.f;
           } else if (ELU && (valid >> ps & 1u)) {
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       const int rr = e0 / CH, cc2 = e0 % CH;
 #pragma unroll
       for (int j = 0; j < NVT; ++j) {
-        if (DELTA) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
+        if (R::solve) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
         reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
       }
       if (tid < CH) {
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int tau = tn + 2 * tp + h;
-            const int src = DELTA ? tau - 1 : tau;
+            const int src = R::shift ? tau - 1 : tau;
             px[2 * r + h] = u32x4{0u, 0u, 0u, 0u};
             if (tau < p.T && src >= 0) {
               px[2 * r + h] = ld16(kbase, (uint32_t)(src * DK + 8 * cg) * (uint32_t)sizeof(InT));
@@ -746,7 +750,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
           const int tau = tn + ps * RPP + tid / TPR;
-          const int src = DELTA ? tau - 1 : tau;
+          const int src = R::shift ? tau - 1 : tau;
           px[ps] = u32x4{0u, 0u, 0u, 0u};
           if (tau < p.T && src >= 0) {
             px[ps] = ld16(kbase, (uint32_t)(src * DK + col) * (uint32_t)sizeof(InT));
@@ -774,7 +778,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       const u32x4* Mg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kM) + e0);
 #pragma unroll
       for (int j = 0; j < NVT; ++j) {
-        if (DELTA) pt[j] = Tg[j];
+        if (R::solve) pt[j] = Tg[j];
         pm[j] = Mg[j];
       }
       if (tid < CH) {
@@ -802,9 +806,9 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
           const int tau = t0 + t;
-          float lam = DELTA ? 0.f : 1.f;
+          float lam = R::nlms ? 0.f : 1.f;
           if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
-          const float a = DELTA ? 1.f - s_fV[t] * lam : lam;
+          const float a = R::nlms ? 1.f - s_fV[t] * lam : lam;
           gsum += log_abs_floor(a);
           pr ^= (a < 0.f) ? 1u : 0u;
           gcol[t] = gsum;
@@ -847,7 +851,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       for (int kb = 0; kb < NKD; ++kb) Sf[kb] = Pol::from_c(s, kb, sS);
 
       f4 U[NMT];
-      if (DELTA) {
+      if (R::solve) {
         f4 P[NMT];
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
@@ -1019,7 +1023,7 @@ bool scan_supported(int dk, int dv) {
   return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
-template <typename InT, int DK, bool DELTA, bool PC, bool ELU>
+template <typename InT, int DK, int RULE, bool PC, bool ELU>
 static hipError_t launch_scan_t(const ScanParams& p, hipStream_t st, int phases) {
   const unsigned nprep = (unsigned)((size_t)p.BH * p.nchunks);
   if constexpr (sizeof(InT) == 2 && !PC && !ELU) {
@@ -1032,32 +1036,37 @@ static hipError_t launch_scan_t(const ScanParams& p, hipStream_t st, int phases)
     return hipSuccess;
   } else {
     if (phases & 1) {
-      hipLaunchKernelGGL((prep_kernel<InT, DK, DELTA, PC, ELU>), dim3(nprep), dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((prep_kernel<InT, DK, RULE, PC, ELU>), dim3(nprep), dim3(NT), 0, st, p);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     if (phases & 2) {
       const int NG = (p.dv + 63) / 64;
       const unsigned nprop = (unsigned)(8 * NG * ((p.BH + 7) / 8));
-      hipLaunchKernelGGL((prop_kernel<InT, DK, DELTA, PC, ELU>), dim3(nprop), dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((prop_kernel<InT, DK, RULE, PC, ELU>), dim3(nprop), dim3(NT), 0, st, p);
       return hipGetLastError();
     }
     return hipSuccess;
   }
 }
 
-template <typename InT, int DK, bool DELTA, bool PC>
+template <typename InT, int DK, int RULE, bool PC>
 static hipError_t launch_scan_e(const ScanParams& p, hipStream_t st, int ph) {
-  return (p.flags & kFlagPhiElu1) ? launch_scan_t<InT, DK, DELTA, PC, true>(p, st, ph)
-                                  : launch_scan_t<InT, DK, DELTA, PC, false>(p, st, ph);
+  return (p.flags & kFlagPhiElu1) ? launch_scan_t<InT, DK, RULE, PC, true>(p, st, ph)
+                                  : launch_scan_t<InT, DK, RULE, PC, false>(p, st, ph);
+}
+
+template <typename InT, int DK, int RULE>
+static hipError_t launch_scan_r(const ScanParams& p, hipStream_t st, int ph) {
+  return (p.flags & kFlagPerChannel) ? launch_scan_e<InT, DK, RULE, true>(p, st, ph)
+                                     : launch_scan_e<InT, DK, RULE, false>(p, st, ph);
 }
 
 template <typename InT, int DK>
 static hipError_t launch_scan_dk(const ScanParams& p, hipStream_t st, int ph) {
-  const bool pc = (p.flags & kFlagPerChannel) != 0;
-  if (p.delta)
-    return pc ? launch_scan_e<InT, DK, true, true>(p, st, ph) : launch_scan_e<InT, DK, true, false>(p, st, ph);
-  return pc ? launch_scan_e<InT, DK, false, true>(p, st, ph) : launch_scan_e<InT, DK, false, false>(p, st, ph);
+  if (p.rule == kRuleDelta) return launch_scan_r<InT, DK, kRuleDelta>(p, st, ph);
+  if (p.rule == kRuleInner) return launch_scan_r<InT, DK, kRuleInner>(p, st, ph);
+  return launch_scan_r<InT, DK, kRuleAdditive>(p, st, ph);
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t st, int phases) {

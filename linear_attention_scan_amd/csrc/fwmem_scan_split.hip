@@ -1,10 +1,12 @@
 // Split-operand propagate kernel of the chunked scan: bf16 inputs, identity feature
-// map, scalar decay, delta or additive rule.
+// map, scalar decay; delta, additive or inner-product rule.
 //
 // Per chunk (the chunk algebra of fwmem_scan.hip, "Fast Weight Attention for
 // Continual Learning" reading notes, sections 3.2 and 4.1-4.4):
 //   R = diag(fV) V - diag(fP) (X S),   U = T R            (delta rule)
-//   U = diag(fV) V                                        (additive rule)
+//   U = diag(fV) V                     (additive and inner-product rules; fV = eta for
+//                                       the inner-product rule, the write scale beta
+//                                       for the additive one)
 //   O = diag(fO) (Q S) + M U,   S' = Gamma_C S + X^T diag(fU) U.
 //
 // One workgroup = one head and 32 value columns (two 16-column tiles), in five waves.
@@ -43,12 +45,12 @@ constexpr int CH = kChunk;
 constexpr int kLoader = 2 * kSplitTiles;       // index of the loader wave
 constexpr int NTS = 64 * (2 * kSplitTiles + 1);
 
-template <int DK, bool DELTA>
+template <int DK, bool SOLVE>
 struct SplitBuf {
   static constexpr int NGR = DK / 8;  // granules per X / Q row
   u32x4 x[CH * NGR];
   u32x4 q[CH * NGR];
-  u32x4 t[DELTA ? 2 * kTriFrags * 64 : 1];
+  u32x4 t[SOLVE ? 2 * kTriFrags * 64 : 1];
   u32x4 m[2 * kTriFrags * 64];
   u32x4 v[CH * kSplitCols / 8];
   float fac[5 * CH];
@@ -115,12 +117,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Direct loads of chunk c into B by the loader wave. For the delta rule the X resource
+// Direct loads of chunk c into B by the loader wave. For the shifted pair the X resource
 // starts one row early (x_t is the key before token t); the row before token 0 is
 // forced out of range and patched from the record afterwards. Rows past the sequence
 // end read as zeros.
-template <int DK, bool DELTA>
-__device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c, int lane,
+template <int DK, bool SOLVE, bool SHIFT>
+__device__ __forceinline__ void issue_chunk(SplitBuf<DK, SOLVE>& B, const ScanParams& p, int c, int lane,
                                             const LoadOffs<DK>& o, const Srcs& src) {
   using LO = LoadOffs<DK>;
   using RC = RecSplit<DK>;
@@ -128,12 +130,12 @@ __device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanPa
   static_for<0, LO::NXI>([&](auto I) {
     constexpr int i = I;
     uint32_t xo = o.x[i];
-    if (DELTA && c == 0 && 64 * i + lane < LO::NGR) xo = 0x80000000u;  // row 0 of chunk 0
+    if (SHIFT && c == 0 && 64 * i + lane < LO::NGR) xo = 0x80000000u;  // row 0 of chunk 0
     dma16(src.x, xo, sx, &B.x[64 * i]);
     dma16(src.q, o.x[i], sx, &B.q[64 * i]);
   });
   const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
-  if constexpr (DELTA) {
+  if constexpr (SOLVE) {
     static_for<0, 2 * kTriFrags>([&](auto J) {
       dma16(src.w, o.lane16, sw + (uint32_t)(RC::kT + J * 1024), &B.t[64 * J]);
     });
@@ -150,8 +152,8 @@ __device__ __forceinline__ void issue_chunk(SplitBuf<DK, DELTA>& B, const ScanPa
 
 // Direct loads of the X, Q and V rows of chunk c >= 1 into B (the record arrives through
 // the loader's registers).
-template <int DK, bool DELTA>
-__device__ __forceinline__ void issue_rows(SplitBuf<DK, DELTA>& B, const ScanParams& p, int c,
+template <int DK, bool SOLVE>
+__device__ __forceinline__ void issue_rows(SplitBuf<DK, SOLVE>& B, const ScanParams& p, int c,
                                            const LoadOffs<DK>& o, const Srcs& src) {
   using LO = LoadOffs<DK>;
   const uint32_t sx = (uint32_t)(c * CH * DK * 2);
@@ -167,11 +169,11 @@ __device__ __forceinline__ void issue_rows(SplitBuf<DK, DELTA>& B, const ScanPar
 // is loaded two chunks ahead and written to LDS one chunk ahead, so that its loads have a
 // whole chunk period more to land than the row loads, which go straight to LDS one
 // chunk ahead. (Register loads of the rows as well proved slower than direct loads.)
-template <int DK, bool DELTA>
+template <int DK, bool SOLVE>
 struct ChunkRegs {
-  static constexpr int NT = DELTA ? 2 * kTriFrags : 0;
+  static constexpr int NT = SOLVE ? 2 * kTriFrags : 0;
   static constexpr int NLOADS = NT + 2 * kTriFrags + 2;
-  u32x4 t[DELTA ? 2 * kTriFrags : 1];
+  u32x4 t[SOLVE ? 2 * kTriFrags : 1];
   u32x4 m[2 * kTriFrags];
   u32x4 f0, f1;
 };
@@ -180,12 +182,12 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-template <int DK, bool DELTA>
-__device__ __forceinline__ void load_regs(ChunkRegs<DK, DELTA>& r, const Srcs& src, int c, const LoadOffs<DK>& o,
+template <int DK, bool SOLVE>
+__device__ __forceinline__ void load_regs(ChunkRegs<DK, SOLVE>& r, const Srcs& src, int c, const LoadOffs<DK>& o,
                                           int lane) {
   using RC = RecSplit<DK>;
   const uint32_t sw = (uint32_t)((size_t)c * RC::kBytes);
-  if constexpr (DELTA) {
+  if constexpr (SOLVE) {
     static_for<0, 2 * kTriFrags>([&](auto J) { r.t[J] = ld16(src.w, o.lane16, sw + (uint32_t)(RC::kT + J * 1024)); });
   }
   static_for<0, 2 * kTriFrags>([&](auto J) { r.m[J] = ld16(src.w, o.lane16, sw + (uint32_t)(RC::kM + J * 1024)); });
@@ -194,9 +196,9 @@ __device__ __forceinline__ void load_regs(ChunkRegs<DK, DELTA>& r, const Srcs& s
   r.f1 = ld16(src.w, lane < 16 ? o.lane16 : 0x80000000u, sw + (uint32_t)(RC::kFac + 1024));
 }
 
-template <int DK, bool DELTA>
-__device__ __forceinline__ void store_regs(SplitBuf<DK, DELTA>& B, const ChunkRegs<DK, DELTA>& r, int lane) {
-  if constexpr (DELTA) {
+template <int DK, bool SOLVE>
+__device__ __forceinline__ void store_regs(SplitBuf<DK, SOLVE>& B, const ChunkRegs<DK, SOLVE>& r, int lane) {
+  if constexpr (SOLVE) {
 #pragma unroll
     for (int j = 0; j < 2 * kTriFrags; ++j) B.t[64 * j + lane] = r.t[j];
   }
@@ -255,22 +257,22 @@ __device__ __forceinline__ void set_flag(int* f, int v) {
 // compute waves; then, with B's partner N free again (the compute waves finished chunk
 // c-1 before the barrier), enqueue chunk c+1's rows into N, write its record from
 // registers into N, and start the register loads of chunk c+2's record.
-template <int DK, bool DELTA>
-__device__ __forceinline__ void loader_step(SplitBuf<DK, DELTA>& B, SplitBuf<DK, DELTA>& N,
-                                            ChunkRegs<DK, DELTA>& R, const ScanParams& p, int c, int lane,
+template <int DK, bool SOLVE, bool SHIFT>
+__device__ __forceinline__ void loader_step(SplitBuf<DK, SOLVE>& B, SplitBuf<DK, SOLVE>& N,
+                                            ChunkRegs<DK, SOLVE>& R, const ScanParams& p, int c, int lane,
                                             const LoadOffs<DK>& o, const Srcs& src, const char* rec0) {
-  constexpr int NGR = SplitBuf<DK, DELTA>::NGR;
-  if (c + 1 < p.nchunks) wait_vm<ChunkRegs<DK, DELTA>::NLOADS>();
+  constexpr int NGR = SplitBuf<DK, SOLVE>::NGR;
+  if (c + 1 < p.nchunks) wait_vm<ChunkRegs<DK, SOLVE>::NLOADS>();
   else wait_vm<0>();
-  if (DELTA && c == 0 && lane < NGR) {
+  if (SHIFT && c == 0 && lane < NGR) {
     // x_0 is the carried key (zero without one): row 0 of the first X tile
     B.x[lane ^ xswz<DK>(0)] = *reinterpret_cast<const u32x4*>(rec0 + RecSplit<DK>::kX0 + 16 * lane);
   }
   lds_barrier();
   if (c + 1 < p.nchunks) {
-    issue_rows<DK, DELTA>(N, p, c + 1, o, src);
-    store_regs<DK, DELTA>(N, R, lane);
-    if (c + 2 < p.nchunks) load_regs<DK, DELTA>(R, src, c + 2, o, lane);
+    issue_rows<DK, SOLVE>(N, p, c + 1, o, src);
+    store_regs<DK, SOLVE>(N, R, lane);
+    if (c + 2 < p.nchunks) load_regs<DK, SOLVE>(R, src, c + 2, o, lane);
   }
 }
 
@@ -316,9 +318,9 @@ struct Share {
 };
 
 // LDS operand reads shared by both roles.
-template <int DK, bool DELTA>
+template <int DK, bool SOLVE>
 struct Frags {
-  using Buf = SplitBuf<DK, DELTA>;
+  using Buf = SplitBuf<DK, SOLVE>;
   static constexpr int NGR = Buf::NGR;
   const Buf& B;
   const Lane& L;
@@ -370,13 +372,13 @@ __device__ __forceinline__ float vf(const s4& h, int i) {
 // Gamma_C S (for c > 0; S itself for c = 0) and Sh/Sl the split of S; on exit acc holds
 // Gamma_C' S' with Gamma_C' the next chunk's decay (1 after the last chunk) and Sh/Sl
 // the split of S'.
-template <int DK, bool DELTA>
-__device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff<DK>& H, int c, bool last,
+template <int DK, bool SOLVE>
+__device__ __forceinline__ void alpha_step(const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H, int c, bool last,
                                            const Lane& L, f4 (&acc)[DK / 16], u32x4 (&Sh)[DK / 32],
                                            u32x4 (&Sl)[DK / 32]) {
   constexpr int NKD = DK / 32;  // K blocks over d_k
   constexpr int NRT = DK / 16;  // row tiles of S
-  const Frags<DK, DELTA> F{B, L};
+  const Frags<DK, SOLVE> F{B, L};
 
   // the loader wave releases chunk c once its loads have landed; the compute waves have
   // finished with chunk c-1, so the loader may refill that buffer
@@ -384,7 +386,7 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
 
   // ---- A: operand reads; the first chunk scales S by its decay here
   bf8 xf[4][NKD];
-  if constexpr (DELTA) {
+  if constexpr (SOLVE) {
 #pragma unroll
     for (int kb = 0; kb < NKD; ++kb) xf[0][kb] = F.xfrag(B.x, 0, kb);
   }
@@ -394,7 +396,7 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
   for (int m = 0; m < 4; ++m) {
     vv[m] = F.vrows(m);
     fvr[m] = F.fac4(1, m);
-    if (DELTA) fpr[m] = F.fac4(0, m);
+    if (SOLVE) fpr[m] = F.fac4(0, m);
   }
   if (c == 0) {
     const float g0 = B.fac[4 * CH];
@@ -408,7 +410,7 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
   bf8 th[kTriFrags], tl[kTriFrags];
   s4 xth[NRT][2][2];
   float gCn;
-  if constexpr (DELTA) {
+  if constexpr (SOLVE) {
     // ---- B: P = X S by token tile (8 NKD MFMAs). Tile m completes before tile m+1
     // starts, so R = fV V - fP P and its split run one tile behind. Alongside: the X
     // fragments of the next tile, the T fragments, the remaining factors.
@@ -488,7 +490,7 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
       FW_FENCE();
     });
   } else {
-    // additive rule: U = fV V; the remaining reads
+    // no solve (additive and inner-product rules): U = fV V; the remaining reads
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -506,13 +508,13 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
 
   // ---- D: the rest of the U hand-off and of W = fU U; the flag follows once every LDS
   // access of this wave so far has completed (the X^T reads are needed next anyway)
-  constexpr int M0 = DELTA ? 2 : 0;  // tiles already handed over and scaled in C
+  constexpr int M0 = SOLVE ? 2 : 0;  // tiles already handed over and scaled in C
 #pragma unroll
   for (int m = M0; m < 4; ++m) {
     H.u[L.tile][m][L.lane] = U[m];
     Wt[m] = U[m] * fur[m];
   }
-  if constexpr (!DELTA) static_for<0, 4>([&](auto J) { split_word<0, J>(Wt, Wh[0], Wl[0]); });
+  if constexpr (!SOLVE) static_for<0, 4>([&](auto J) { split_word<0, J>(Wt, Wh[0], Wl[0]); });
   lds_wait();
   set_flag(&H.uflag[L.tile], c + 1);
   FW_FENCE();
@@ -569,11 +571,11 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, DELTA>& B, Handoff
 }
 
 // ---- beta: the outputs of one tile for chunk c
-template <int DK, bool DELTA, bool OBF>
-__device__ __forceinline__ void beta_step(const SplitBuf<DK, DELTA>& B, Handoff<DK>& H, int c, const Lane& L,
+template <int DK, bool SOLVE, bool OBF>
+__device__ __forceinline__ void beta_step(const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H, int c, const Lane& L,
                                           int dv, uint32_t vo, __amdgpu_buffer_rsrc_t ro) {
   constexpr int NKD = DK / 32;
-  const Frags<DK, DELTA> F{B, L};
+  const Frags<DK, SOLVE> F{B, L};
   lds_barrier();
 
   // ---- A: the split state of this chunk; tell alpha it may write the next one
@@ -650,9 +652,10 @@ __device__ __forceinline__ void beta_step(const SplitBuf<DK, DELTA>& B, Handoff<
   });
 }
 
-template <int DK, bool DELTA, bool OBF>
+template <int DK, int RULE, bool OBF>
 __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
-  using Buf = SplitBuf<DK, DELTA>;
+  constexpr bool SOLVE = Rule<RULE>::solve, SHIFT = Rule<RULE>::shift;
+  using Buf = SplitBuf<DK, SOLVE>;
   constexpr int NRT = DK / 16;
   constexpr int NKD = DK / 32;
   __shared__ Buf B0, B1;
@@ -677,16 +680,16 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     const uint16_t* vb = static_cast<const uint16_t*>(p.v) + rowbase * dv;
     const LoadOffs<DK> lo = load_offsets<DK>(lane, dv, grp);
     Srcs src;
-    src.x = rsrc(DELTA ? kb - DK : kb, (uint32_t)(p.T * DK * 2));
+    src.x = rsrc(SHIFT ? kb - DK : kb, (uint32_t)(p.T * DK * 2));
     src.q = rsrc(qb, (uint32_t)(p.T * DK * 2));
     src.v = rsrc(vb, (uint32_t)(p.T * dv * 2));
     src.w = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecSplit<DK>::kBytes));
-    issue_chunk<DK, DELTA>(B0, p, 0, lane, lo, src);
-    ChunkRegs<DK, DELTA> R;
-    if (p.nchunks > 1) load_regs<DK, DELTA>(R, src, 1, lo, lane);
+    issue_chunk<DK, SOLVE, SHIFT>(B0, p, 0, lane, lo, src);
+    ChunkRegs<DK, SOLVE> R;
+    if (p.nchunks > 1) load_regs<DK, SOLVE>(R, src, 1, lo, lane);
     for (int c = 0; c < p.nchunks; c += 2) {
-      loader_step<DK, DELTA>(B0, B1, R, p, c, lane, lo, src, rec0);
-      if (c + 1 < p.nchunks) loader_step<DK, DELTA>(B1, B0, R, p, c + 1, lane, lo, src, rec0);
+      loader_step<DK, SOLVE, SHIFT>(B0, B1, R, p, c, lane, lo, src, rec0);
+      if (c + 1 < p.nchunks) loader_step<DK, SOLVE, SHIFT>(B1, B0, R, p, c + 1, lane, lo, src, rec0);
     }
     if (p.S_out != nullptr && grp == 0) {
       for (int i = lane; i < DK; i += 64)
@@ -726,8 +729,8 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     set_flag(&H.uflag[L.tile], 0);
 
     for (int c = 0; c < p.nchunks; c += 2) {
-      alpha_step<DK, DELTA>(B0, H, c, c + 1 == p.nchunks, L, acc, Sh, Sl);
-      if (c + 1 < p.nchunks) alpha_step<DK, DELTA>(B1, H, c + 1, c + 2 == p.nchunks, L, acc, Sh, Sl);
+      alpha_step<DK, SOLVE>(B0, H, c, c + 1 == p.nchunks, L, acc, Sh, Sl);
+      if (c + 1 < p.nchunks) alpha_step<DK, SOLVE>(B1, H, c + 1, c + 2 == p.nchunks, L, acc, Sh, Sl);
     }
     // after the last chunk acc holds S' (its next-chunk decay is 1)
     if (p.S_out != nullptr) {
@@ -745,27 +748,33 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
       rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes);
   const uint32_t vo = (uint32_t)(8 * L.g * dv + col) * oes;
   for (int c = 0; c < p.nchunks; c += 2) {
-    beta_step<DK, DELTA, OBF>(B0, H, c, L, dv, vo, ro);
-    if (c + 1 < p.nchunks) beta_step<DK, DELTA, OBF>(B1, H, c + 1, L, dv, vo, ro);
+    beta_step<DK, SOLVE, OBF>(B0, H, c, L, dv, vo, ro);
+    if (c + 1 < p.nchunks) beta_step<DK, SOLVE, OBF>(B1, H, c + 1, L, dv, vo, ro);
   }
 }
 
-template <int DK, bool DELTA>
+template <int DK, int RULE>
 hipError_t launch_t(const ScanParams& p, hipStream_t st) {
   const int ngrp = p.dv / kSplitCols;
   const unsigned grid = (unsigned)(8 * ngrp * ((p.BH + 7) / 8));
   if (p.flags & kFlagOutBf16)
-    hipLaunchKernelGGL((prop_split_kernel<DK, DELTA, true>), dim3(grid), dim3(NTS), 0, st, p);
+    hipLaunchKernelGGL((prop_split_kernel<DK, RULE, true>), dim3(grid), dim3(NTS), 0, st, p);
   else
-    hipLaunchKernelGGL((prop_split_kernel<DK, DELTA, false>), dim3(grid), dim3(NTS), 0, st, p);
+    hipLaunchKernelGGL((prop_split_kernel<DK, RULE, false>), dim3(grid), dim3(NTS), 0, st, p);
   return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const ScanParams& p, hipStream_t st) {
+  if (p.rule == kRuleDelta) return launch_t<DK, kRuleDelta>(p, st);
+  if (p.rule == kRuleInner) return launch_t<DK, kRuleInner>(p, st);
+  return launch_t<DK, kRuleAdditive>(p, st);
 }
 
 }  // namespace
 
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t st) {
-  if (p.dk == 64) return p.delta ? launch_t<64, true>(p, st) : launch_t<64, false>(p, st);
-  return p.delta ? launch_t<128, true>(p, st) : launch_t<128, false>(p, st);
+  return p.dk == 64 ? launch_dk<64>(p, st) : launch_dk<128>(p, st);
 }
 
 }  // namespace fwmem

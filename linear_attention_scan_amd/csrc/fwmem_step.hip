@@ -11,6 +11,9 @@
 // state is written back from registers: exactly one read and one write of S.
 // Additive rule ("attention is also an FFN", section 3.2):
 //   S' = diag(gamma) S + b phi(k) v^T,  o = S^T (gamma o q~) + b (phi(k) . q~) v.
+// Inner-product rule (the reading notes above, section 4.3): x, eta and a as for the
+// delta rule, with the value itself written: S' = diag(a) S + eta x v^T,
+//   o = S^T (a o q~) + eta (x . q~) v.
 //
 // Layout: one 1024-thread workgroup per head. Thread (rg, cq) owns float4 column
 // group cq (4 value columns) of rows rg, rg + RG, ... (four rows at d_k = d_v = 128);
@@ -27,8 +30,9 @@ namespace {
 
 constexpr int NT = 1024;
 
-template <typename InT, int DK, int DV, bool DELTA, bool PC>
+template <typename InT, int DK, int DV, int RULE, bool PC>
 __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
+  using R = Rule<RULE>;
   constexpr int TPRd = DV / 4;       // threads per row (float4 each)
   constexpr int RG = NT / TPRd;      // row groups
   constexpr int RPT = DK / RG;       // rows per thread
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     if (elu) { q = phi_elu1(q); k = phi_elu1(k); }
     s_q[i] = q;
     s_k[i] = k;
-    s_x[i] = (DELTA && has && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
+    s_x[i] = (R::shift && has && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
   }
   __syncthreads();
 
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   if (wave == 0) {
     float nx = 0.f, dq = 0.f, lm = 0.f;
     for (int i = lane; i < DK; i += 64) {
-      const float xi = DELTA ? s_x[i] : s_k[i];
+      const float xi = R::shift ? s_x[i] : s_k[i];
       nx += xi * xi;
       dq += xi * s_q[i];
       if (PC && p.lam != nullptr) lm = fmaxf(lm, p.lam[(size_t)bh * DK + i]);
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     lm = wave_max(lm);
     if (lane == 0) {
       float eta = 0.f, a = 1.f;
-      if (DELTA) {
+      if (R::nlms) {
         const float lam = PC ? lm : (p.lam != nullptr ? p.lam[bh] : 0.f);
         if (has) eta = p.beta[bh] / (nx + lam + p.eps);
         a = 1.f - eta * lam;
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   for (int i = tid; i < DK; i += NT) {
     float a = a_sc;
     if (PC) {
-      const float lam = p.lam != nullptr ? p.lam[(size_t)bh * DK + i] : (DELTA ? 0.f : 1.f);
-      a = DELTA ? 1.f - eta * lam : lam;
+      const float lam = p.lam != nullptr ? p.lam[(size_t)bh * DK + i] : (R::nlms ? 0.f : 1.f);
+      a = R::nlms ? 1.f - eta * lam : lam;
     }
     s_a[i] = a;
   }
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   }
   // r (delta) or the written value b*v (additive), and the output.
   const f4 vv = {v4[0], v4[1], v4[2], v4[3]};
-  const f4 r = DELTA ? (vv - P) * eta : vv * eta;  // the written value u
+  const f4 r = R::solve ? (vv - P) * eta : vv * eta;  // the written value u
   const f4 o = W + r * dq;
 
   // New state from registers.
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   for (int j = 0; j < RPT; ++j) {
     const int row = rg + RG * j;
     const float a = s_a[row];
-    const float xi = DELTA ? s_x[row] : s_k[row];
+    const float xi = R::shift ? s_x[row] : s_k[row];
     const f4 n4 = S[j] * a + r * xi;
     __builtin_nontemporal_store(n4, reinterpret_cast<f4*>(Sout + (size_t)row * DV) + cq);
   }
@@ -179,12 +183,15 @@ template <typename InT, int DK, int DV>
 hipError_t launch_t(const StepParams& p, hipStream_t st) {
   const bool pc = (p.flags & kFlagPerChannel) != 0;
   const dim3 grid(p.BH), block(NT);
-  if (p.delta) {
-    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, true, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, true, false>), grid, block, 0, st, p);
+  if (p.rule == kRuleDelta) {
+    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleDelta, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleDelta, false>), grid, block, 0, st, p);
+  } else if (p.rule == kRuleInner) {
+    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleInner, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleInner, false>), grid, block, 0, st, p);
   } else {
-    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, false, false>), grid, block, 0, st, p);
+    if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleAdditive, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleAdditive, false>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }

@@ -90,6 +90,8 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(q=None), F.EINVAL),
     (dict(out=None), F.EINVAL),
     (dict(beta=None), F.EINVAL),                      # delta rule needs beta
+    (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),  # so does the inner-product rule
+    (dict(md=F.mode(rule=3)), F.EINVAL),
     (dict(q=FAKE + 2), F.EALIGN),
     (dict(out=FAKE * 64 + 8), F.EALIGN),
     (dict(beta=FAKE + 2), F.EALIGN),
@@ -125,6 +127,8 @@ def test_empty_batch_is_a_no_op():
     (dict(shp=F.shape(1, 1, 1, 128, 32, F.BF16)), F.EUNSUPPORTED),
     (dict(S_out=None), F.EINVAL),
     (dict(beta=None), F.EINVAL),
+    (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),
+    (dict(md=F.mode(rule=-1)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 7)), F.EINVAL),
     (dict(q=FAKE + 1), F.EALIGN),
     (dict(out=FAKE * 64 + 4), F.EALIGN),

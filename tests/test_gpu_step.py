@@ -24,6 +24,9 @@ def _t(x, bf16=True):
     (wl.RULE_DELTA, True, "f32", 128, 64),
     (wl.RULE_ADDITIVE, False, "bf16", 128, 128),
     (wl.RULE_ADDITIVE, True, "f32", 64, 128),
+    (wl.RULE_INNER, False, "bf16", 128, 128),
+    (wl.RULE_INNER, True, "bf16", 128, 64),
+    (wl.RULE_INNER, False, "f32", 64, 64),
 ])
 def test_step_sequence_matches_oracle(rule, pc, dtype, dk, dv):
     """Several steps from a random S0 with no previous key: step 1 reads only, later
@@ -48,7 +51,7 @@ def test_step_sequence_matches_oracle(rule, pc, dtype, dk, dv):
         if dtype == "bf16":
             q, k, v = wl.round_to_bf16(q), wl.round_to_bf16(k), wl.round_to_bf16(v)
         beta = rng.uniform(0.1, 1.9, size=(B, H)).astype(np.float32)
-        if rule == wl.RULE_DELTA:
+        if rule != wl.RULE_ADDITIVE:
             lam = rng.uniform(0, 0.2, size=(B, H, dk) if pc else (B, H)).astype(np.float32)
         else:
             lam = rng.uniform(0.8, 1.0, size=(B, H, dk) if pc else (B, H)).astype(np.float32)
