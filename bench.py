@@ -32,29 +32,41 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "linear_attention_scan_amd", "csrc")
 
 # HBM traffic per launch of the scan kernels on the default workload (B=4 H=16 T=4096
-# d=128, bf16, delta rule), from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in runs of
-# their own, each scaled by what the same counter reads for a plain 1 GiB device copy in
-# the same run (FETCH_SIZE x2.0, WRITE_SIZE x1.0). A record is reported only while the
+# d=128, bf16, delta rule) and of the decode kernel (B=256 H=32 d=128, state in place),
+# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in runs of their own, each scaled by
+# what the same counter reads for a plain 1 GiB device copy in the same run
+# (FETCH_SIZE x2.0, WRITE_SIZE x1.0). A record is reported only while the
 # kernel's sources still hash to the recorded digest; after any change it is null until
 # the counters are taken again.
 MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "prop_split_kernel"): {
-        "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h"),
+        "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_scan_split.hip": "fb3d107a968905fab1bf69176c016e11fe5766fb95da5c09ca66cb7c496f2fc0",
-            "fwmem_split.h": "79815937c6a25bd5b6f7f0f1c7538b567e6e2ad40fb47736385bf1d89bb51cd2",
+            "fwmem_scan_split.hip": "48789642986e8b3b42164755c4e546834b3abe6f4832b33e6267ac2f7106cc30",
+            "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
         },
-        "fetch_kib": 150219.1, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150224.9, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
-        "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h"),
+        "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_prep_split.hip": "8128dcce33d9595377c92a18e69bb6dadeb4b281dea9c163de592cad6328f63d",
-            "fwmem_split.h": "79815937c6a25bd5b6f7f0f1c7538b567e6e2ad40fb47736385bf1d89bb51cd2",
+            "fwmem_prep_split.hip": "94aa2d7bcab80fc178c7f1582356bd4dddea50e3a262ad95b52297f2fc187084",
+            "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
         },
-        "fetch_kib": 66675.2, "write_kib": 103440.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66675.4, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("decode", "step_kernel"): {
+        "sources": ("fwmem_step.hip", "fwmem_device.h", "fwmem_internal.h"),
+        "sha256": {
+            "fwmem_step.hip": "5b21bd2528d97bd17d952e4b984f9bb92f7b413c5a08599166946a94ee9ba054",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
+        },
+        "fetch_kib": 267969.8, "write_kib": 532893.7, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
@@ -349,6 +361,7 @@ def bench_decode(steps, dev, stream):
             "ms_per_step": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode", "step_kernel"),
                          "bytes_per_launch": nbytes}}
 
 
