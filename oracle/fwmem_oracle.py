@@ -28,6 +28,9 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
   D4  beta_t, lambda_t are indexed by the target's step t.
   D7  additive rule: the `lam` slot carries the retention gamma_t (None = 1) and
       `beta` an optional write scale (None = 1); pairing is same-index.
+  D16 normalised q and k (qk_norm): each is rescaled to length 1 (l2) or sqrt(d_k)
+      (RMSNorm with unit gain and no epsilon), a zero vector stays zero, and the
+      carried key is stored raw.
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -58,13 +61,26 @@ def _heads(a, tail_ndim):
     return a.reshape((-1,) + a.shape[a.ndim - tail_ndim:])
 
 
+def unit_rows(x: np.ndarray, length: float = 1.0) -> np.ndarray:
+    """Each row (last axis) rescaled to the given Euclidean length; a zero row stays
+    zero (reading D16)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x * length, n, out=np.zeros_like(x), where=n > 0)
+
+
 def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None):
+         S0=None, xprev0=None, has0=None, qk_norm=None):
     """Run the recurrence over a whole sequence.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] or None; lam: [B,H,T] (or
     [B,H,T,dk] when per_channel) or None. S0: [B,H,dk,dv] or None (zeros);
     xprev0: [B,H,dk] or None; has0: [B,H] or None (no previous key).
+    qk_norm: None, "l2" or "rms". q_t and k_t are used rescaled to unit length ("l2")
+    or to root-mean-square 1, i.e. length sqrt(d_k) ("rms": RMSNorm with unit gain).
+    [FWA] section 4.5 normalises the query and key projections (RMSNorm by default,
+    l2 in the DeltaNet variants); reading D16. Identity feature map only. The carried
+    key stays the raw k of the last token and is rescaled where it is used.
 
     Returns (o [B,H,T,dv], S [B,H,dk,dv], xprev [B,H,dk], has [B,H]) in float64.
     """
@@ -86,14 +102,25 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     has = np.zeros(N, dtype=bool) if has0 is None else (np.asarray(has0).reshape(N) != 0)
     O = np.zeros((N, T, dv))
 
+    if qk_norm is not None and phi_kind != "identity":
+        raise ValueError("qk_norm takes the identity feature map")
+    if qk_norm is None:
+        unit = lambda a: a
+    elif qk_norm in ("l2", "rms"):
+        length = 1.0 if qk_norm == "l2" else float(np.sqrt(dk))
+        unit = lambda a: unit_rows(a, length)
+    else:
+        raise ValueError(qk_norm)
+
     for t in range(T):
-        qt = phi(Q[:, t], phi_kind)
-        kt = phi(K[:, t], phi_kind)
+        qt = unit(phi(Q[:, t], phi_kind))
+        k_raw = phi(K[:, t], phi_kind)
+        kt = unit(k_raw)
         vt = V[:, t]
         if rule in (RULE_DELTA, RULE_INNER):
             # [FWA] 4.1: the pair written at step t is (phi(k_{t-1}), v_t); with no
             # previous key the pair is (0, v_t) with eta = 0, so nothing happens.
-            x = np.where(has[:, None], xprev, 0.0)
+            x = np.where(has[:, None], unit(xprev), 0.0)
             if Lm is None:
                 lam_t = np.zeros(N)
                 lam_hat = lam_t
@@ -129,7 +156,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
             S = gam * S + b[:, None, None] * kt[:, :, None] * vt[:, None, :]
         else:
             raise ValueError(rule)
-        xprev = kt
+        xprev = k_raw
         has = np.ones(N, dtype=bool)
         # read after write: o_t = S_t^T phi(q_t) ([AFFN] 2.1; [FWA] 4.1)
         O[:, t] = np.einsum("nij,ni->nj", S, qt)
@@ -139,7 +166,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
 
 
 def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None):
+         S0=None, xprev0=None, has0=None, qk_norm=None):
     """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
     (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
     q = np.asarray(q)[:, :, None]
@@ -150,7 +177,7 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         lam = np.asarray(lam)
         lam = lam[:, :, None, :] if per_channel else lam[:, :, None]
     o, S, xp, h = scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind, eps=eps,
-                       per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0)
+                       per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm)
     return o[:, :, 0], S, xp, h
 
 

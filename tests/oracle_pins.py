@@ -503,6 +503,69 @@ def pin_p9_hand_inner(orc):
     assert np.array_equal(xp[0, 0], k[2]) and h[0, 0] == 1
 
 
+def _qk_cases(rng, T, dk, dv):
+    """Raw (unnormalised) inputs with a spread of token norms, and gates for each rule."""
+    q = rng.standard_normal((T, dk)) * rng.uniform(0.2, 5.0, (T, 1))
+    k = rng.standard_normal((T, dk)) * rng.uniform(0.2, 5.0, (T, 1))
+    v = rng.standard_normal((T, dv))
+    beta = rng.uniform(0.1, 1.9, T)
+    lam = {DELTA: rng.uniform(0.0, 0.3, T), INNER: rng.uniform(0.0, 0.3, T),
+           ADD: rng.uniform(0.7, 1.0, T)}
+    return q, k, v, beta, lam
+
+
+def pin_p18_qk_norm_is_the_rule_on_normalised_inputs(orc):
+    """[FWA] 4.5 normalises the query and key projections: with qk_norm the scan equals
+    the plain scan on q and k rescaled here, by an independent route, to RMS 1
+    (RMSNorm with unit gain: divide by sqrt(mean of squares)) or to unit length.
+    The state's carried key is the raw last key (reading D16)."""
+    rng = np.random.default_rng(36)
+    T, dk, dv = 14, 6, 4
+    for rule in (DELTA, INNER, ADD):
+        q, k, v, beta, lam = _qk_cases(rng, T, dk, dv)
+        for mode in ("l2", "rms"):
+            rms_q = np.sqrt(np.mean(q * q, axis=1, keepdims=True))
+            rms_k = np.sqrt(np.mean(k * k, axis=1, keepdims=True))
+            scale = 1.0 if mode == "rms" else 1.0 / np.sqrt(dk)
+            qn, kn = q / rms_q * scale, k / rms_k * scale
+            b = beta if rule != ADD else None
+            o, S, xp, h = orc.scan(_bh(q), _bh(k), _bh(v), None if b is None else _bh(b), _bh(lam[rule]),
+                                   rule=rule, eps=1e-6, qk_norm=mode)
+            o2, S2, _, _ = orc.scan(_bh(qn), _bh(kn), _bh(v), None if b is None else _bh(b),
+                                    _bh(lam[rule]), rule=rule, eps=1e-6)
+            np.testing.assert_allclose(o[0, 0], o2[0, 0], rtol=0, atol=1e-11)
+            np.testing.assert_allclose(S[0, 0], S2[0, 0], rtol=0, atol=1e-11)
+            assert np.array_equal(xp[0, 0], k[-1]) and h[0, 0] == 1
+
+
+def pin_p19_qk_norm_scale_invariance(orc):
+    """A consequence of normalising q and k: multiplying each token's q and k by any
+    positive number changes nothing but the carried raw key, for every rule and across
+    a call boundary that carries the key."""
+    rng = np.random.default_rng(37)
+    T, dk, dv, T1 = 16, 5, 3, 7
+    for rule in (DELTA, INNER, ADD):
+        q, k, v, beta, lam = _qk_cases(rng, T, dk, dv)
+        cq, ck = rng.uniform(0.01, 100.0, (T, 1)), rng.uniform(0.01, 100.0, (T, 1))
+        b = beta if rule != ADD else None
+
+        def run(qq, kk):
+            sl = lambda a, s_: None if a is None else _bh(a[s_])
+            first, second = slice(0, T1), slice(T1, None)
+            o1, S1, x1, h1 = orc.scan(sl(qq, first), sl(kk, first), sl(v, first), sl(b, first),
+                                      sl(lam[rule], first), rule=rule, qk_norm="rms")
+            o2, S2, x2, h2 = orc.scan(sl(qq, second), sl(kk, second), sl(v, second), sl(b, second),
+                                      sl(lam[rule], second), rule=rule, qk_norm="rms", S0=S1,
+                                      xprev0=x1, has0=h1)
+            return np.concatenate([o1[0, 0], o2[0, 0]]), S2[0, 0], x2[0, 0]
+
+        o, S, xp = run(q, k)
+        oc, Sc, xpc = run(q * cq, k * ck)
+        np.testing.assert_allclose(oc, o, rtol=0, atol=1e-10 * max(1.0, np.abs(o).max()))
+        np.testing.assert_allclose(Sc, S, rtol=0, atol=1e-10 * max(1.0, np.abs(S).max()))
+        np.testing.assert_allclose(xpc, k[-1] * ck[-1], rtol=1e-15, atol=0)
+
+
 def pin_relerr_metric(orc):
     """The parity metric max|x - ref| / rms(ref) on a case worked by hand."""
     ref = np.array([3.0, -4.0])          # rms = sqrt((9 + 16)/2) = 5/sqrt(2)
@@ -531,5 +594,7 @@ ALL_PINS = [
     pin_p16_inner_first_step_noop,
     pin_p17_inner_is_shifted_linear_attention,
     pin_p9_hand_inner,
+    pin_p18_qk_norm_is_the_rule_on_normalised_inputs,
+    pin_p19_qk_norm_scale_invariance,
     pin_relerr_metric,
 ]

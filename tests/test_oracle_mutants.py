@@ -15,7 +15,7 @@ from tests import oracle_pins
 MUTANTS = {
     "residual_sign": ('r = vt - np.einsum("nij,ni->nj", S, x)',
                       'r = vt + np.einsum("nij,ni->nj", S, x)'),
-    "same_index_pairing": ("x = np.where(has[:, None], xprev, 0.0)",
+    "same_index_pairing": ("x = np.where(has[:, None], unit(xprev), 0.0)",
                            "x = np.where(has[:, None], kt, 0.0)"),
     "no_ridge_decay": ("decay = 1.0 - (", "decay = 1.0 + 0.0 * ("),
     "no_key_energy": ("den = np.sum(x * x, axis=1) + lam_hat + eps",
@@ -41,6 +41,10 @@ MUTANTS = {
                        "S = S + eta[:, None, None] * x[:, :, None] * vt"),
     "inner_unnormalised_step": ("eta[:, None, None] * x[:, :, None] * vt[:, None, :]",
                                 "Bt[:, t][:, None, None] * x[:, :, None] * vt[:, None, :]"),
+    "qk_norm_skips_carried_key": ("x = np.where(has[:, None], unit(xprev), 0.0)",
+                                  "x = np.where(has[:, None], xprev, 0.0)"),
+    "qk_norm_skips_query": ("qt = unit(phi(Q[:, t], phi_kind))", "qt = phi(Q[:, t], phi_kind)"),
+    "qk_norm_rms_length_one": ('length = 1.0 if qk_norm == "l2" else float(np.sqrt(dk))', "length = 1.0"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
