@@ -192,6 +192,8 @@ def main():
     beta = None if w.beta is None else dev_t(w.beta)
     lam = None if w.lam is None else dev_t(w.lam)
     flags = (F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
+    if w.qk_norm is not None:
+        flags |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
     shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
     md = F.mode(w.rule, flags, w.eps, 0)
     out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.float32, device=dev)
@@ -281,7 +283,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "rule": ("delta", "additive", "inner")[w.rule], "inputs": w.dtype,
-                   "chunk": 64, "seed": 0},
+                   "chunk": 64, "seed": 0, "qk_norm": w.qk_norm},
         "roofline": roofline,
         "kernels": {names[n]: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),
                                "mfma_TFLOPs": round(kk["mfma_TFLOPs"], 2),
@@ -378,7 +380,7 @@ def cpu_baseline(w, min_s=10.0):
         sl = (slice(b, b + 1), slice(None), slice(None))
         orc.scan(w.q[sl], w.k[sl], w.v[sl], None if w.beta is None else w.beta[sl],
                  None if w.lam is None else w.lam[sl], rule=w.rule, phi_kind=w.phi, eps=w.eps,
-                 per_channel=w.per_channel)
+                 per_channel=w.per_channel, qk_norm=w.qk_norm)
 
     n = 0
     with threadpool_limits(limits=1):

@@ -23,7 +23,12 @@
  *   Read (every rule, after the write): o_t = S_t^T phi(q_t).
  *
  * phi is the identity, or elu(x)+1 (the blog post above, section 4.1) with
- * FWMEM_PHI_ELU1. With FWMEM_LAMBDA_PER_CHANNEL, lambda (delta) or gamma
+ * FWMEM_PHI_ELU1. With FWMEM_QK_L2NORM or FWMEM_QK_RMSNORM (identity phi only; the
+ * reading notes above, section 4.5, normalise the query and key projections) the
+ * library normalises q_t and k_t itself, in fp32, before every use: the caller passes
+ * them raw and saves a pass over them. A zero vector stays zero. The state's x_prev
+ * then holds the raw last key, which is normalised where it is used, so every call
+ * of one sequence must pass the same normalisation flag. With FWMEM_LAMBDA_PER_CHANNEL, lambda (delta) or gamma
  * (additive) is a d_k-vector per token: the decay diag(1 - eta_t lambda_t) (resp.
  * diag(gamma_t)) scales the rows of S, and eta's denominator (DELTA, INNER) uses
  * max_i lambda_{t,i}.
@@ -65,8 +70,10 @@ typedef struct ihipStream_t* fwmem_stream; /* the same handle type as hipStream_
 
 typedef enum {
   FWMEM_OK = 0,
-  FWMEM_EINVAL = -1,       /* NULL required pointer, negative size, unknown rule/flag/dtype, bad eps */
-  FWMEM_EUNSUPPORTED = -2, /* a size or chunk length the library has no kernel for */
+  FWMEM_EINVAL = -1,       /* NULL required pointer, negative size, unknown rule/flag/dtype, bad eps,
+                              both QK normalisation flags */
+  FWMEM_EUNSUPPORTED = -2, /* a size or chunk length the library has no kernel for, or a QK
+                              normalisation flag with FWMEM_PHI_ELU1 */
   FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda) */
   FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
   FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
@@ -84,8 +91,11 @@ typedef enum { FWMEM_F32 = 0, FWMEM_BF16 = 1 } fwmem_dtype;
 enum {
   FWMEM_PHI_ELU1 = 1u << 0,           /* phi = elu(x)+1 on q and k; default identity */
   FWMEM_LAMBDA_PER_CHANNEL = 1u << 1, /* lambda/gamma is [B][H][T][dk] instead of [B][H][T] */
-  FWMEM_OUT_BF16 = 1u << 2            /* out is bf16 instead of float32 (adds rounding up to
+  FWMEM_OUT_BF16 = 1u << 2,           /* out is bf16 instead of float32 (adds rounding up to
                                          2^-9 relative per element) */
+  FWMEM_QK_L2NORM = 1u << 3,          /* q_t and k_t are used rescaled to unit length */
+  FWMEM_QK_RMSNORM = 1u << 4          /* q_t and k_t are used rescaled to RMS 1, i.e. length
+                                         sqrt(dk): RMSNorm with unit gain, no epsilon */
 };
 
 typedef struct {

@@ -12,9 +12,23 @@ enum : uint32_t {
   kFlagPhiElu1 = 1u << 0,
   kFlagPerChannel = 1u << 1,
   kFlagOutBf16 = 1u << 2,
+  kFlagQkL2 = 1u << 3,
+  kFlagQkRms = 1u << 4,
 };
 
 constexpr int kChunk = 64;  // scan chunk length (tokens)
+
+// Length that FWMEM_QK_L2NORM / FWMEM_QK_RMSNORM give q_t and k_t (0: not normalised).
+__host__ __device__ inline float qk_length(uint32_t flags, int dk) {
+  if (flags & kFlagQkL2) return 1.f;
+  if (flags & kFlagQkRms) return __builtin_sqrtf((float)dk);
+  return 0.f;
+}
+// Factor that rescales a vector with squared length ss to length len (a zero vector
+// stays zero).
+__host__ __device__ inline float rescale_factor(float ss, float len) {
+  return ss > 0.f ? len / __builtin_sqrtf(ss) : 0.f;
+}
 
 // Write rules (the values of fwmem_rule).
 enum : int { kRuleDelta = 0, kRuleAdditive = 1, kRuleInner = 2 };

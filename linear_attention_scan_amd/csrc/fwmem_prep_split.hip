@@ -9,6 +9,10 @@
 //   M_ts = (Gamma_t / Gamma_s) q_t . x_s          (s <= t)
 // and the per-token row factors fP = eta Gamma_{t-1}, fV = eta, fO = Gamma_t,
 // fU = Gamma_C / Gamma_t with Gamma_C the decay over the whole chunk.
+// With normalised queries and keys (QKN) the raw rows stay the operands: x_t and q_t are
+// used as nx_t x_t and mq_t q_t, so L_ts and M_ts take the factors nx_t nx_s and
+// mq_t nx_s, fP and fU take nx_t, fO takes mq_t, and |x_t|^2 in eta becomes
+// nx_t^2 |x_t|^2. The propagate kernel is unchanged.
 //
 // Steps (4 waves):
 //   1. X and Q rows arrive in LDS by direct loads (rows past the sequence end read as
@@ -91,7 +95,7 @@ __device__ __forceinline__ void split_to_record(const float* src, char* rec, int
   }
 }
 
-template <int DK, int RULE>
+template <int DK, int RULE, bool QKN>
 __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   using RC = RecSplit<DK>;
   using R = Rule<RULE>;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   static_assert(CH * DK * 2 <= kRegion, "tile fits a region");
   // Two regions: X, then L; Q, then M, then T (once M is in the record). 33 KiB in all,
   // so that four workgroups share a CU.
-  __shared__ __align__(16) char smem[2 * kRegion + 4 * CH * 4];
+  __shared__ __align__(16) char smem[2 * kRegion + (QKN ? 7 : 4) * CH * 4];
   u32x4* Xs = reinterpret_cast<u32x4*>(smem);
   u32x4* Qs = reinterpret_cast<u32x4*>(smem + kRegion);
   float* Lf = reinterpret_cast<float*>(smem);            // after the Gram products
@@ -111,6 +115,9 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   float* s_eta = s_diag + CH;
   float* s_g = s_eta + CH;
   float* s_sg = s_g + CH;
+  float* s_qd = s_sg + CH;  // QKN: |q_t|^2, then the rescale factors of x_t and q_t
+  float* s_n = s_qd + CH;
+  float* s_m = s_n + CH;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,10 +166,23 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   }
   __syncthreads();
 
-  // ---- 2. Gram products: jobs over the 10 lower 16x16 tiles of X X^T (shifted pair: its
-  // diagonal gives |x_t|^2, its lower part L for the delta rule) and Q X^T
-  constexpr int NJ = R::shift ? 20 : 10;
+  // ---- 2. Gram products: jobs over the 10 lower 16x16 tiles of X X^T (its diagonal
+  // gives |x_t|^2, its lower part L for the delta rule; needed by the shifted pair and by
+  // QKN), the 10 lower tiles of Q X^T, and with QKN the 4 diagonal tiles of Q Q^T
+  // (|q_t|^2). Job kinds: 0 X X^T, 1 Q X^T, 2 Q Q^T.
+  constexpr int NG = (R::shift || QKN) ? 10 : 0;
+  constexpr int NJ = NG + 10 + (QKN ? 4 : 0);
   constexpr int JPW = (NJ + 3) / 4;
+  auto job_kind = [&](int job) { return job < NG ? 0 : (job < NG + 10 ? 1 : 2); };
+  auto job_tile = [&](int job, int& mt, int& nt) {
+    if (job < NG + 10) {
+      const int tile = job < NG ? job : job - NG;
+      mt = low_mt(tile);
+      nt = low_nt(tile);
+    } else {
+      mt = nt = job - NG - 10;
+    }
+  };
   auto rowfrag = [&](const u32x4* S, int row, int kq) -> bf8 {
     return __builtin_bit_cast(bf8, S[row * NGR + ((4 * kq + g) ^ xswz<DK>(row))]);
   };
@@ -172,15 +192,18 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     const int job = jj * 4 + wave;
     acc[jj] = f4{0.f, 0.f, 0.f, 0.f};
     if (job < NJ) {
-      const bool gram = R::shift && job < 10;
-      const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
-      const u32x4* A = gram ? Xs : Qs;
+      const int kind = job_kind(job);  // wave-uniform
+      int mt, nt;
+      job_tile(job, mt, nt);
+      const u32x4* A = kind == 0 ? Xs : Qs;
+      const u32x4* Bm = kind == 2 ? Qs : Xs;
 #pragma unroll
       for (int kq = 0; kq < NKD; ++kq)
-        mma_bf16(acc[jj], rowfrag(A, 16 * mt + n, kq), rowfrag(Xs, 16 * nt + n, kq));
-      if (gram && mt == nt && (n >> 2) == g) {
+        mma_bf16(acc[jj], rowfrag(A, 16 * mt + n, kq), rowfrag(Bm, 16 * nt + n, kq));
+      if (kind != 1 && mt == nt && (n >> 2) == g) {
         const int i = n & 3;
-        s_diag[16 * mt + n] = i == 0 ? acc[jj][0] : i == 1 ? acc[jj][1] : i == 2 ? acc[jj][2] : acc[jj][3];
+        const float d = i == 0 ? acc[jj][0] : i == 1 ? acc[jj][1] : i == 2 ? acc[jj][2] : acc[jj][3];
+        (kind == 0 ? s_diag : s_qd)[16 * mt + n] = d;
       }
     }
   }
@@ -190,10 +213,21 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   if (wave == 0) {
     const int t = lane, tau = t0 + t;
     const bool active = tau < T;
+    // QKN: x_t and q_t are used rescaled by nx and mq (to length qk_length); the raw bf16
+    // rows stay the MFMA operands and the factors go into the masks and row factors.
+    float nx = 1.f, mq = 1.f, xx = s_diag[t];
+    if (QKN) {
+      const float len = qk_length(p.flags, DK);
+      nx = rescale_factor(s_diag[t], len);
+      mq = rescale_factor(s_qd[t], len);
+      xx = s_diag[t] * nx * nx;
+      s_n[t] = nx;
+      s_m[t] = mq;
+    }
     float eta = 0.f, a = 1.f;
     if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
-      if (hasx) eta = g_beta / (s_diag[t] + g_lam + p.eps);
+      if (hasx) eta = g_beta / (xx + g_lam + p.eps);
       a = 1.f - eta * g_lam;
     } else {
       if (active) eta = g_beta;
@@ -213,10 +247,10 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     }
     const float gC = __shfl(la, CH - 1), sC = __shfl(sg, CH - 1);
     float* fac = reinterpret_cast<float*>(rec + RC::kFac);
-    fac[t] = eta * sprev * __expf(gprev);
+    fac[t] = eta * sprev * __expf(gprev) * nx;
     fac[CH + t] = eta;
-    fac[2 * CH + t] = sg * __expf(la);
-    fac[3 * CH + t] = sC * sg * __expf(gC - la);
+    fac[2 * CH + t] = sg * __expf(la) * mq;
+    fac[3 * CH + t] = sC * sg * __expf(gC - la) * nx;
     // row 4: [Gamma_C, has_prev, Gamma_C of the next chunk, 0...]. Slot 2 of a record is
     // written by the next chunk's workgroup (1 for the last chunk), so that the propagate
     // kernel knows the next decay one chunk early.
@@ -232,13 +266,17 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   // the output fragments cover (row tiles 0 / 2, column tiles 1 / 3). The token scalars
   // of every job are read before the first store (the stores could alias them).
   float sc_g[JPW][4], sc_sg[JPW][4], sc_eta[JPW][4], sc_gp[JPW][4], sc_sp[JPW][4], sc_gs[JPW], sc_ss[JPW];
+  float sc_r[JPW][4], sc_ns[JPW];  // QKN: the row's and the column's rescale factors
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int job = jj * 4 + wave;
-    const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
+    int mt, nt;
+    job_tile(job < NJ ? job : 0, mt, nt);
+    const bool gram = job_kind(job) == 0;
     const int s = 16 * nt + n;
     sc_gs[jj] = s_g[s];
     sc_ss[jj] = s_sg[s];
+    sc_ns[jj] = QKN ? s_n[s] : 1.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * mt + 4 * g + i;
@@ -247,6 +285,7 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
       sc_eta[jj][i] = s_eta[t];
       sc_gp[jj][i] = t ? s_g[t - 1] : 0.f;
       sc_sp[jj][i] = t ? s_sg[t - 1] : 1.f;
+      sc_r[jj][i] = QKN ? (gram ? s_n[t] : s_m[t]) : 1.f;
     }
   }
   // Branch-free per element: the decay ratio is formed for every element and the masked
@@ -254,16 +293,18 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int job = jj * 4 + wave;
-    if (job < NJ && (R::solve || !(R::shift && job < 10))) {
-      const bool gram = R::shift && job < 10;  // wave-uniform
-      const int tile = job % 10, mt = low_mt(tile), nt = low_nt(tile);
+    const int kind = job < NJ ? job_kind(job) : 2;  // wave-uniform
+    if (kind == 1 || (kind == 0 && R::solve)) {
+      const bool gram = kind == 0;
+      int mt, nt;
+      job_tile(job, mt, nt);
       float* dst = gram ? Lf : Mf;
       const int s = 16 * nt + n;
-      const float gs = sc_gs[jj], ss = sc_ss[jj];
+      const float gs = sc_gs[jj], ss = sc_ss[jj] * sc_ns[jj];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g + i;
-        const float coef = gram ? sc_eta[jj][i] * sc_sp[jj][i] : sc_sg[jj][i];
+        const float coef = (gram ? sc_eta[jj][i] * sc_sp[jj][i] : sc_sg[jj][i]) * sc_r[jj][i];
         const float ga = gram ? sc_gp[jj][i] : sc_g[jj][i];
         const bool keep = gram ? (s < t) : (s <= t);
         const float r = __builtin_amdgcn_exp2f((ga - gs) * 1.44269504088896341f);
@@ -342,7 +383,10 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
 template <int DK, int RULE>
 hipError_t launch_t(const ScanParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)p.BH * p.nchunks);
-  hipLaunchKernelGGL((prep_split_kernel<DK, RULE>), dim3(grid), dim3(NTP), 0, st, p);
+  if (p.flags & (kFlagQkL2 | kFlagQkRms))
+    hipLaunchKernelGGL((prep_split_kernel<DK, RULE, true>), dim3(grid), dim3(NTP), 0, st, p);
+  else
+    hipLaunchKernelGGL((prep_split_kernel<DK, RULE, false>), dim3(grid), dim3(NTP), 0, st, p);
   return hipGetLastError();
 }
 

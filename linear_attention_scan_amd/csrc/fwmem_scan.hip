@@ -100,7 +100,7 @@ struct PrepLds {
   static constexpr size_t kOp = (size_t)CH * LDX * sizeof(op_t);
   static constexpr size_t kMat = (size_t)CH * LDF * 4;
   static constexpr size_t kReg = ((kOp > kMat ? kOp : kMat) + 15) / 16 * 16;
-  static constexpr size_t kSmall = 4 * (5 * CH + 4 * NW + 16);
+  static constexpr size_t kSmall = 4 * (8 * CH + 4 * NW + 16);
   static constexpr size_t kBytes = 4 * kReg + kSmall;
 };
 
@@ -125,6 +125,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   float* s_g = s_eta + CH;
   float* s_sg = s_g + CH;
   float* s_red = s_sg + CH;  // 4*NW + 16
+  float* s_qn = s_red + 4 * NW + 16;  // |q_t|^2 (normalised queries and keys only)
+  float* s_nx = s_qn + CH;            // rescale factors of x_t and q_t (1 without)
+  float* s_mq = s_nx + CH;
+  // With normalised queries and keys the raw rows stay the operands: x_t and q_t are used
+  // as nx_t x_t and mq_t q_t, folded into eta, the masks and the row factors.
+  const float qk_len = qk_length(p.flags, DK);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x % p.nchunks;
@@ -178,15 +184,20 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
           for (int j = 0; j < VW; ++j) qr[ps][j] = phi_elu1(qr[ps][j]);
         }
       }
-      float ns = 0.f;
+      float ns = 0.f, nq = 0.f;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
         ns += xr[ps][j] * xr[ps][j];
+        nq += qr[ps][j] * qr[ps][j];
         mx = fmaxf(mx, fabsf(xr[ps][j]));
         mq = fmaxf(mq, fabsf(qr[ps][j]));
       }
       ns = group_sum<TPR>(ns);
-      if (tid % TPR == 0) s_norm[t] = ns;
+      if (qk_len > 0.f) nq = group_sum<TPR>(nq);
+      if (tid % TPR == 0) {
+        s_norm[t] = ns;
+        s_qn[t] = nq;
+      }
     }
     if (Pol::kScaled) {
       sX = pow2_scale(block_max(mx, s_red));
@@ -229,11 +240,19 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     const int t = lane;
     const int tau = t0 + t;
     const bool active = tau < p.T;
+    float nx = 1.f, mqf = 1.f, xx = s_norm[t];
+    if (qk_len > 0.f) {
+      nx = rescale_factor(s_norm[t], qk_len);
+      mqf = rescale_factor(s_qn[t], qk_len);
+      xx = s_norm[t] * nx * nx;
+    }
+    s_nx[t] = nx;
+    s_mq[t] = mqf;
     float eta = 0.f, a = 1.f;
     if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
       const float lam_t = PC ? s_lam[t] : g_lam;
-      if (hasx) eta = g_beta / (s_norm[t] + lam_t + p.eps);
+      if (hasx) eta = g_beta / (xx + lam_t + p.eps);
       a = 1.f - eta * lam_t;
     } else {
       if (active) eta = g_beta;
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         float val = 0.f;
         if (mat == 0) {
           if (s < t) {
-            float f = s_eta[t] * invL;
+            float f = s_eta[t] * invL * s_nx[t] * s_nx[s];
             if (!PC) {
               const float gp = t ? s_g[t - 1] : 0.f;
               const float sp = t ? s_sg[t - 1] : 1.f;
@@ -384,7 +403,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
           }
         } else {
           if (s <= t) {
-            float f = invM;
+            float f = invM * s_mq[t] * s_nx[s];
             if (!PC) f *= s_sg[t] * s_sg[s] * __expf(s_g[t] - s_g[s]);
             val = f * acc[jj][ii];
           }
@@ -495,10 +514,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         fU = (s_sg[CH - 1] * s_sg[tt] * __expf(s_g[CH - 1] - s_g[tt])) / sX;
       }
       float* fac = reinterpret_cast<float*>(rec + RC::kFac);
-      fac[tt] = fP;
+      fac[tt] = fP * s_nx[tt];
       fac[CH + tt] = e;
-      fac[2 * CH + tt] = fO;
-      fac[3 * CH + tt] = fU;
+      fac[2 * CH + tt] = fO * s_mq[tt];
+      fac[3 * CH + tt] = fU * s_nx[tt];
     }
     if (tid == 0) {
       float* scv = reinterpret_cast<float*>(rec + RC::kSc);

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
   __shared__ float s_x[DK], s_q[DK], s_a[DK], s_k[DK];
   __shared__ float s_red[2][NWV][DV];
-  __shared__ float s_sc[4];
+  __shared__ float s_sc[6];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,7 +64,10 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
                : f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Per-head vectors into LDS.
+  // Per-head vectors into LDS. The carried key for the next token is phi(k), stored raw
+  // (before any normalisation); each thread reads its own x_prev entries before it writes
+  // them, so the state may be updated in place.
+  const float qk_len = qk_length(p.flags, DK);
   for (int i = tid; i < DK; i += NT) {
     float q = In<InT>::load1(qp + i);
     float k = In<InT>::load1(kp + i);
@@ -72,21 +75,32 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     s_q[i] = q;
     s_k[i] = k;
     s_x[i] = (R::shift && has && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
+    p.xprev_out[(size_t)bh * DK + i] = k;
   }
   __syncthreads();
 
-  // Scalars: ||x||^2, max lambda (per channel), x.q or k.q; wave 0 reduces.
+  // Scalars: ||x||^2, max lambda (per channel), x.q or k.q; wave 0 reduces. With
+  // normalised queries and keys, x and q are rescaled by mx and mq (to length qk_len).
   if (wave == 0) {
-    float nx = 0.f, dq = 0.f, lm = 0.f;
+    float nx = 0.f, dq = 0.f, lm = 0.f, nq = 0.f;
     for (int i = lane; i < DK; i += 64) {
       const float xi = R::shift ? s_x[i] : s_k[i];
       nx += xi * xi;
       dq += xi * s_q[i];
+      nq += s_q[i] * s_q[i];
       if (PC && p.lam != nullptr) lm = fmaxf(lm, p.lam[(size_t)bh * DK + i]);
     }
     nx = wave_sum(nx);
     dq = wave_sum(dq);
+    nq = wave_sum(nq);
     lm = wave_max(lm);
+    float mx = 1.f, mq = 1.f;
+    if (qk_len > 0.f) {
+      mx = rescale_factor(nx, qk_len);
+      mq = rescale_factor(nq, qk_len);
+      nx *= mx * mx;
+      dq *= mx * mq;
+    }
     if (lane == 0) {
       float eta = 0.f, a = 1.f;
       if (R::nlms) {
@@ -100,11 +114,18 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
       s_sc[0] = eta;
       s_sc[1] = a;
       s_sc[2] = dq;
+      s_sc[3] = mx;
+      s_sc[4] = mq;
     }
   }
   __syncthreads();
   const float eta = s_sc[0], a_sc = s_sc[1], dq = s_sc[2];
   for (int i = tid; i < DK; i += NT) {
+    if (qk_len > 0.f) {
+      s_q[i] *= s_sc[4];
+      if (R::shift) s_x[i] *= s_sc[3];
+      else s_k[i] *= s_sc[3];
+    }
     float a = a_sc;
     if (PC) {
       const float lam = p.lam != nullptr ? p.lam[(size_t)bh * DK + i] : (R::nlms ? 0.f : 1.f);
@@ -175,7 +196,6 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
       *reinterpret_cast<f4*>(static_cast<float*>(p.out) + ob) = o;
     }
   }
-  for (int i = tid; i < DK; i += NT) p.xprev_out[(size_t)bh * DK + i] = s_k[i];
   if (tid == 0) p.has_out[bh] = 1;
 }
 

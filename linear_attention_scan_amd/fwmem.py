@@ -20,6 +20,8 @@ F32, BF16 = 0, 1
 PHI_ELU1 = 1 << 0
 LAMBDA_PER_CHANNEL = 1 << 1
 OUT_BF16 = 1 << 2
+QK_L2NORM = 1 << 3
+QK_RMSNORM = 1 << 4
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",

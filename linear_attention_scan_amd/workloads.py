@@ -29,6 +29,8 @@ Recipes (the names match the workload table of the design document):
                     normalised step, the target written in place of the residual);
                     delta_bf16's distributions (no workload on the pages fixes them).
   inner_f32_small   as delta_f32_small with the inner-product rule.
+  delta_bf16_h16_qknorm  as delta_bf16_h16 with raw q, k ~ N(0,1) (not normalised, then
+                    rounded) that the scan normalises to unit length itself.
   decode            B=256 H=32 d=128, 1000 single-token steps (delta rule).
                     S0 ~ N(0, 0.02) fp32 with no previous key; per step
                     q,k,v ~ N(0,1) bf16 with q,k normalised; beta = sigmoid(N(0,1));
@@ -86,7 +88,7 @@ class ScanInputs:
     dk: int
     dv: int
     dtype: str               # 'bf16' or 'f32': the storage type of q, k, v and out
-    rule: int                # RULE_DELTA or RULE_ADDITIVE
+    rule: int                # RULE_DELTA, RULE_ADDITIVE or RULE_INNER
     phi: str                 # PHI_IDENTITY or PHI_ELU1
     per_channel: bool        # lambda is [B,H,T,dk] instead of [B,H,T]
     eps: float
@@ -98,6 +100,8 @@ class ScanInputs:
     S0: Optional[np.ndarray] = None        # [B,H,dk,dv] float32 or None (= 0)
     xprev0: Optional[np.ndarray] = None    # [B,H,dk] float32 or None
     has0: Optional[np.ndarray] = None      # [B,H] int32 or None
+    qk_norm: Optional[str] = None          # None, 'l2' or 'rms': q, k are raw and the scan
+                                           # normalises them (the library's QK flags)
 
     @property
     def tokens(self) -> int:
@@ -116,7 +120,8 @@ def _normal(rng, shape, mean=0.0, std=1.0):
 def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTITY,
               normalise_qk=True, beta_kind="sigmoid", lam_kind="const",
               lam_const=0.01, lam_mu=-4.0, per_channel=False, gamma_mu=3.0,
-              gamma_sd=0.5, eps=1e-6, s0_std=None, seed=0, name="custom") -> ScanInputs:
+              gamma_sd=0.5, eps=1e-6, s0_std=None, seed=0, name="custom",
+              qk_norm=None) -> ScanInputs:
     """Draw one scan problem.
 
     beta_kind: 'sigmoid' (sigmoid(N(0,1))), 'two_sigmoid' (2*sigmoid(N(0,1))),
@@ -164,7 +169,7 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
         S0 = _normal(rng, (B, H, dk, dv), std=s0_std)
     return ScanInputs(name=name, B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, rule=rule,
                       phi=phi, per_channel=per_channel, eps=eps, q=q, k=k, v=v,
-                      beta=beta, lam=lam, S0=S0)
+                      beta=beta, lam=lam, S0=S0, qk_norm=qk_norm)
 
 
 def delta_f32_small(seed=0, T=256):
@@ -193,6 +198,14 @@ def delta_long_pc(seed=0, B=1, H=8, T=131072, d=128):
     return make_scan(B=B, H=H, T=T, dk=d, dv=d, dtype="bf16", beta_kind="sigmoid",
                      lam_kind="softplus", lam_mu=-5.0, per_channel=True, seed=seed,
                      name="delta_long_pc")
+
+
+def delta_bf16_h16_qknorm(seed=0, B=4, T=4096, d=128):
+    """The throughput workload with raw q, k ~ N(0,1) bf16, normalised by the scan itself
+    (unit length): the same gates as delta_bf16_h16."""
+    return make_scan(B=B, H=16, T=T, dk=d, dv=d, dtype="bf16", beta_kind="two_sigmoid",
+                     lam_kind="softplus", lam_mu=-4.0, normalise_qk=False, qk_norm="l2",
+                     seed=seed, name="delta_bf16_h16_qknorm")
 
 
 def inner_bf16(seed=0, B=4, H=8, T=4096, d=128):
@@ -241,5 +254,6 @@ SCAN_WORKLOADS = {
     "additive_bf16": additive_bf16,
     "delta_long_pc": delta_long_pc,
     "inner_bf16": inner_bf16,
+    "delta_bf16_h16_qknorm": delta_bf16_h16_qknorm,
     "inner_f32_small": inner_f32_small,
 }

@@ -39,6 +39,8 @@ def flags_of(w: wl.ScanInputs, extra=0):
         f |= F.PHI_ELU1
     if w.per_channel:
         f |= F.LAMBDA_PER_CHANNEL
+    if w.qk_norm is not None:
+        f |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
     return f
 
 
@@ -79,7 +81,7 @@ def oracle_scan(w: wl.ScanInputs, t_slice=None, S0=None, xprev0=None, has0=None)
                     None if w.beta is None else w.beta[:, :, sl],
                     None if w.lam is None else w.lam[:, :, sl],
                     rule=w.rule, phi_kind=w.phi, eps=w.eps, per_channel=w.per_channel,
-                    S0=S0, xprev0=xprev0, has0=has0)
+                    S0=S0, xprev0=xprev0, has0=has0, qk_norm=w.qk_norm)
 
 
 def state_np(st):

@@ -92,6 +92,8 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(beta=None), F.EINVAL),                      # delta rule needs beta
     (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),  # so does the inner-product rule
     (dict(md=F.mode(rule=3)), F.EINVAL),
+    (dict(md=F.mode(flags=F.QK_L2NORM | F.QK_RMSNORM)), F.EINVAL),
+    (dict(md=F.mode(flags=F.QK_RMSNORM | F.PHI_ELU1)), F.EUNSUPPORTED),
     (dict(q=FAKE + 2), F.EALIGN),
     (dict(out=FAKE * 64 + 8), F.EALIGN),
     (dict(beta=FAKE + 2), F.EALIGN),
