@@ -71,6 +71,39 @@ struct StatePtrs {
   int32_t* h;
 };
 
+// Workspace of a scan: the (head, chunk) records, and for a segmented scan (P > 1 segments
+// per head, see SegParams) the two virtual state buffers, z and the segment start states.
+struct WsLayout {
+  int P;
+  size_t rec, A0, B0, A1, B1, z, start, total;
+};
+
+WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
+  WsLayout w{};
+  const size_t BH = (size_t)s->B * (size_t)s->H, T = (size_t)s->T;
+  const size_t nchunks = (T + kChunk - 1) / kChunk;
+  const int bf16 = s->dtype == FWMEM_BF16 ? 1 : 0;
+  w.P = T > 0 ? fwmem::scan_segments(BH, T, s->dk, s->dv, bf16, m->flags) : 1;
+  size_t off = align256(BH * nchunks * fwmem::scan_record_bytes(bf16, s->dk, m->flags));
+  w.rec = 0;
+  if (w.P > 1) {
+    const size_t VH = BH * (size_t)w.P, dk = (size_t)s->dk, dv = (size_t)s->dv;
+    const size_t sa = align256(4 * (VH * dk * dk + VH * dk + VH));
+    const size_t sb = align256(4 * (VH * dk * dv + VH * dk + VH));
+    w.A0 = off;
+    w.A1 = w.A0 + sa;
+    w.B0 = w.A1 + sa;
+    w.B1 = w.B0 + sb;
+    off = w.B1 + sb;
+    w.z = off;
+    off += align256(4 * BH * T * dk);
+    w.start = off;
+    off += align256(4 * VH * dk * dv);
+  }
+  w.total = T > 0 ? off : 0;
+  return w;
+}
+
 StatePtrs state_ptrs(const void* base, const Sizes& z) {
   char* b = static_cast<char*>(const_cast<void*>(base));
   if (b == nullptr) return {nullptr, nullptr, nullptr};
@@ -115,9 +148,7 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
   st = check_mode(mode);
   if (st != FWMEM_OK) return st;
   if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
-  const size_t BH = (size_t)shape->B * (size_t)shape->H;
-  const size_t nchunks = ((size_t)shape->T + kChunk - 1) / kChunk;
-  *bytes = BH * nchunks * fwmem::scan_record_bytes(shape->dtype == FWMEM_BF16, shape->dk, mode->flags);
+  *bytes = ws_layout(shape, mode).total;
   return FWMEM_OK;
 }
 
@@ -214,7 +245,83 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   if (T * dmax * 4 > 0x7fffffffu ||
       (size_t)p.nchunks * fwmem::scan_record_bytes(p.bf16, shape->dk, p.flags) > 0x7fffffffu)
     return FWMEM_EUNSUPPORTED;
-  const hipError_t e = fwmem::launch_scan(p, hs, phases);
+
+  const WsLayout wl = ws_layout(shape, mode);
+  if (wl.P == 1) {
+    const hipError_t e = fwmem::launch_scan(p, hs, phases);
+    return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+  }
+
+  // Segmented scan: P segments of each head run as virtual heads (SegParams). The prep
+  // phase sets up the virtual states and builds every record; the propagate phase runs the
+  // local and the transition passes, then chains the segments and fixes up the outputs.
+  char* ws = static_cast<char*>(workspace);
+  const size_t VH = z.BH * (size_t)wl.P, dk = (size_t)shape->dk, dv = (size_t)shape->dv;
+  fwmem::SegParams sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.k = k;
+  sp.S_in = si.S;
+  sp.xprev_in = si.x;
+  sp.has_in = si.h;
+  sp.S_out = so.S;
+  sp.xprev_out = so.x;
+  sp.has_out = so.h;
+  // a virtual state buffer at byte offset o with n value columns: S, x_prev, has_prev
+  auto vstate = [&](size_t o, size_t n, float*& S, float*& x, int32_t*& h) {
+    S = reinterpret_cast<float*>(ws + o);
+    x = S + VH * dk * n;
+    h = reinterpret_cast<int32_t*>(x + VH * dk);
+  };
+  float *A1_x, *B1_x_unused;
+  int32_t *A1_h, *B1_h;
+  vstate(wl.A0, dk, sp.A0_S, sp.A0_x, sp.A0_h);
+  vstate(wl.B0, dv, sp.B0_S, sp.B0_x, sp.B0_h);
+  vstate(wl.A1, dk, sp.A1_S, A1_x, A1_h);
+  vstate(wl.B1, dv, sp.B1_S, sp.B1_x, B1_h);
+  (void)B1_x_unused;
+  sp.z = reinterpret_cast<const float*>(ws + wl.z);
+  sp.S_start = reinterpret_cast<float*>(ws + wl.start);
+  sp.out = static_cast<float*>(out);
+  sp.BH = (int)z.BH;
+  sp.P = wl.P;
+  sp.L = (int)(T / (size_t)wl.P);
+  sp.dk = shape->dk;
+  sp.dv = shape->dv;
+  sp.bf16 = p.bf16;
+  sp.flags = p.flags;
+
+  fwmem::ScanParams pv = p;  // the local pass over the virtual heads
+  pv.BH = (int)VH;
+  pv.T = sp.L;
+  pv.nchunks = sp.L / kChunk;
+  pv.S_in = sp.B0_S;
+  pv.xprev_in = sp.B0_x;
+  pv.has_in = sp.B0_h;
+  pv.S_out = sp.B1_S;
+  pv.xprev_out = sp.B1_x;
+  pv.has_out = B1_h;
+  fwmem::ScanParams pa = pv;  // the transition pass: identity start, zero values
+  pa.v = nullptr;
+  pa.dv = shape->dk;
+  pa.out = const_cast<float*>(sp.z);
+  pa.S_in = sp.A0_S;
+  pa.xprev_in = sp.A0_x;
+  pa.has_in = sp.A0_h;
+  pa.S_out = sp.A1_S;
+  pa.xprev_out = A1_x;
+  pa.has_out = A1_h;
+
+  hipError_t e = hipSuccess;
+  if (phases & 1) {
+    e = fwmem::launch_seg_init(sp, hs);
+    if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 1);
+  }
+  if (e == hipSuccess && (phases & 2)) {
+    e = fwmem::launch_scan(pv, hs, 2);
+    if (e == hipSuccess) e = fwmem::launch_scan(pa, hs, 2);
+    if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
+    if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
+  }
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
 }
 

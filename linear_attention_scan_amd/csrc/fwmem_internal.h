@@ -110,4 +110,51 @@ hipError_t launch_state_copy(const float* S_in, const float* xprev_in, const int
                              float* S_out, float* xprev_out, int32_t* has_out, size_t nS,
                              size_t nX, size_t nH, hipStream_t stream);
 
+// ---- segment-parallel scan (few heads, long sequences)
+//
+// A head's T tokens are cut into P segments of L = T / P tokens. Because q, k, v, the
+// gates and out are [BH][T][...] row-major, segment p of head h is virtual head
+// h * P + p of a [BH * P][L][...] problem, and the ordinary kernels run all segments at
+// once. Two passes over the virtual heads:
+//   local:      from S = 0 (segment 0: the caller's state) with the real values;
+//               gives o_local and the segment's final state B_p;
+//   transition: from S = I with zero values; gives A_p (the segment's linear map
+//               S -> A_p S + B_p) and z_t = A_t^T phi(q_t) for every token.
+// Then S_start(p+1) = A_p S_start(p) + B_p (a short serial chain over segments) and
+// o_t = o_local,t + S_start(p)^T z_t. Each segment's first token takes the previous
+// segment's last key as its carried key.
+struct SegParams {
+  const void* k;          // [BH][T][dk] raw keys (the carried key of each segment)
+  const float* S_in;      // caller's state or null
+  const float* xprev_in;
+  const int32_t* has_in;
+  float* S_out;           // caller's state or null
+  float* xprev_out;
+  int32_t* has_out;
+  // Virtual state buffers (S, then x_prev, then has_prev, as in the ABI's state layout):
+  // the passes start from A0 (transition, S [BH*P][dk][dk]) and B0 (local, S
+  // [BH*P][dk][dv]), written by the set-up kernel, and end in A1 and B1, so a propagate
+  // phase never changes its own inputs.
+  float* A0_S;
+  float* A0_x;
+  int32_t* A0_h;
+  float* B0_S;
+  float* B0_x;
+  int32_t* B0_h;
+  float* A1_S;
+  float* B1_S;
+  float* B1_x;
+  const float* z;         // [BH*P][L][dk]
+  float* S_start;         // [BH*P][dk][dv] (segment p >= 1)
+  float* out;             // [BH][T][dv] float32
+  int BH, P, L, dk, dv, bf16;
+  uint32_t flags;
+};
+// Segment count for a scan of this shape: 1 (no segmentation) unless the propagate
+// grid would leave most of the GPU idle and T splits into equal chunk-aligned segments.
+int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, uint32_t flags);
+hipError_t launch_seg_init(const SegParams& s, hipStream_t st);
+hipError_t launch_seg_combine(const SegParams& s, hipStream_t st);
+hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st);
+
 }  // namespace fwmem

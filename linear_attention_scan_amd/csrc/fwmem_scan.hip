@@ -790,7 +790,8 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       for (int ps = 0; ps < NPV; ++ps) {
         const int tau = tn + ps * RPPv + tid / TPRv;
         pv[ps] = u32x4{0u, 0u, 0u, 0u};
-        if (tau < p.T && grp * 64 + vcol < dv)
+        // a null value pointer means all-zero values (the segmented scan's transition pass)
+        if (tau < p.T && grp * 64 + vcol < dv && p.v != nullptr)
           pv[ps] = ld16(vbase, (uint32_t)(tau * dv + vcol) * (uint32_t)sizeof(InT));
       }
       const u32x4* Tg = reinterpret_cast<const u32x4*>(reinterpret_cast<const op_t*>(rec + RC::kT) + e0);

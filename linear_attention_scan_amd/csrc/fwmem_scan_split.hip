@@ -682,7 +682,9 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     Srcs src;
     src.x = rsrc(SHIFT ? kb - DK : kb, (uint32_t)(p.T * DK * 2));
     src.q = rsrc(qb, (uint32_t)(p.T * DK * 2));
-    src.v = rsrc(vb, (uint32_t)(p.T * dv * 2));
+    // a null value pointer means all-zero values (the transition pass of the segmented
+    // scan): an empty resource reads zeros without touching memory
+    src.v = p.v != nullptr ? rsrc(vb, (uint32_t)(p.T * dv * 2)) : rsrc(qb, 0u);
     src.w = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecSplit<DK>::kBytes));
     issue_chunk<DK, SOLVE, SHIFT>(B0, p, 0, lane, lo, src);
     ChunkRegs<DK, SOLVE> R;
