@@ -114,7 +114,13 @@ typedef struct {
 fwmem_status fwmem_state_bytes(const fwmem_shape* shape, size_t* bytes);
 
 /* Bytes of device workspace fwmem_scan_fwd needs for this shape and mode
- * (0 when T == 0). Its contents need no initialisation and are scratch only. */
+ * (0 when T == 0). Its contents need no initialisation and are scratch only.
+ * For few heads on a long sequence (when the scan would occupy a small part of the
+ * GPU, T splits into 8 or 16 equal segments of at least 512 tokens that are multiples
+ * of 64, and out is float32) the scan runs its segments in parallel and chains them
+ * (the linear map of each segment is computed alongside); the workspace then also
+ * holds two state buffers per segment, one d_k-vector per token and one start state
+ * per segment. */
 fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
                                         size_t* bytes);
 

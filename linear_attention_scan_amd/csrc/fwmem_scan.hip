@@ -557,8 +557,8 @@ struct PropLds {
   static constexpr size_t oT = oQ + kX;
   static constexpr size_t oM = oT + kC;
   static constexpr size_t oV = oM + kC;
-  static constexpr size_t oS = oV + kV;  // small: 5*CH + DK + 4*NW + 16 floats
-  static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 4 * NW + 16);
+  static constexpr size_t oS = oV + kV;  // small: 5*CH + DK + 2*NT floats
+  static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 2 * NT);
 };
 
 template <typename InT, int DK, int RULE, bool PC, bool ELU>
@@ -594,6 +594,8 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   float* s_fac = reinterpret_cast<float*>(smem + L::oS);  // [4][CH]: fP, fV, fO, fU
   float* s_misc = s_fac + 4 * CH;  // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
   float* s_gC = s_misc + CH;       // [DK] per-channel Gamma_C
+  float* s_pg = s_gC + DK;         // [NT] per-channel decay: each thread's segment log-sum
+  uint32_t* s_pp = reinterpret_cast<uint32_t*>(s_pg + NT);  // [NT] and its sign parity
   const float* s_fP = s_fac;
   const float* s_fV = s_fac + CH;
   const float* s_fO = s_fac + 2 * CH;
@@ -815,41 +817,59 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
     if (c < 0) continue;
 
     if (PC) {
-      // per-channel decay folded into the operands: X*Gamma_prev, Q*Gamma, X*Gamma_C/Gamma
-      const int i = tid;
-      if (i < DK) {
-        const int ip = Pol::kpos(i);
-        float gcol[CH];
-        uint64_t par = 0;
-        float gsum = 0.f;
-        uint32_t pr = 0;
+      // per-channel decay folded into the operands: X*Gamma_prev, Q*Gamma, X*Gamma_C/Gamma.
+      // Each channel's 64 tokens are split over TPC threads; the segments' log-sums and
+      // sign parities are combined through LDS into each segment's offset and the chunk
+      // total. Gamma_prev of a token is Gamma of the one before, carried along.
+      constexpr int TPC = NT / DK, SEG = CH / TPC;
+      static_assert(SEG <= 32, "segment parity fits 32 bits");
+      const int i = tid % DK, part = tid / DK, tb = part * SEG;
+      const int ip = Pol::kpos(i);
+      float gl[SEG];
+      uint32_t pl = 0, pr = 0;
+      float gsum = 0.f;
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          const int tau = t0 + t;
-          float lam = R::nlms ? 0.f : 1.f;
-          if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
-          const float a = R::nlms ? 1.f - s_fV[t] * lam : lam;
-          gsum += log_abs_floor(a);
-          pr ^= (a < 0.f) ? 1u : 0u;
-          gcol[t] = gsum;
-          par |= (uint64_t)pr << t;
-        }
-        const float gC = gcol[CH - 1];
-        const uint32_t pC = (uint32_t)(par >> (CH - 1)) & 1u;
-        s_gC[i] = (pC ? -1.f : 1.f) * __expf(gC);
+      for (int u = 0; u < SEG; ++u) {
+        const int tau = t0 + tb + u;
+        float lam = R::nlms ? 0.f : 1.f;
+        if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
+        const float a = R::nlms ? 1.f - s_fV[tb + u] * lam : lam;
+        gsum += log_abs_floor(a);
+        pr ^= (a < 0.f) ? 1u : 0u;
+        gl[u] = gsum;
+        pl |= pr << u;
+      }
+      s_pg[tid] = gsum;
+      s_pp[tid] = pr;
+      __syncthreads();
+      float off = 0.f, gC = 0.f;
+      uint32_t poff = 0, pC = 0;
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          const uint32_t pcur = (uint32_t)(par >> t) & 1u;
-          const uint32_t pprev = t ? (uint32_t)(par >> (t - 1)) & 1u : 0u;
-          const float fprev = (pprev ? -1.f : 1.f) * __expf(t ? gcol[t - 1] : 0.f);
-          const float fcur = (pcur ? -1.f : 1.f) * __expf(gcol[t]);
-          const float fend = ((pC ^ pcur) ? -1.f : 1.f) * __expf(gC - gcol[t]);
-          const float xh = (float)Xs[t * LDX + ip];
-          if constexpr (Pol::kScaled) XU[i * LDT + Pol::kpos(t)] = Pol::cvt(xh * fend);
-          else XU[t * LDX + i] = Pol::cvt(xh * fend);
-          Xs[t * LDX + ip] = Pol::cvt(xh * fprev);
-          Qs[t * LDX + ip] = Pol::cvt((float)Qs[t * LDX + ip] * fcur);
+      for (int w = 0; w < TPC; ++w) {
+        const float g = s_pg[w * DK + i];
+        const uint32_t pp = s_pp[w * DK + i];
+        if (w < part) {
+          off += g;
+          poff ^= pp;
         }
+        gC += g;
+        pC ^= pp;
+      }
+      if (part == 0) s_gC[i] = (pC ? -1.f : 1.f) * __expf(gC);
+      float fprev = (poff ? -1.f : 1.f) * __expf(off);
+#pragma unroll
+      for (int u = 0; u < SEG; ++u) {
+        const int t = tb + u;
+        const float g = off + gl[u];
+        const uint32_t pcur = poff ^ ((pl >> u) & 1u);
+        const float fcur = (pcur ? -1.f : 1.f) * __expf(g);
+        const float fend = ((pC ^ pcur) ? -1.f : 1.f) * __expf(gC - g);
+        const float xh = (float)Xs[t * LDX + ip];
+        if constexpr (Pol::kScaled) XU[i * LDT + Pol::kpos(t)] = Pol::cvt(xh * fend);
+        else XU[t * LDX + i] = Pol::cvt(xh * fend);
+        Xs[t * LDX + ip] = Pol::cvt(xh * fprev);
+        Qs[t * LDX + ip] = Pol::cvt((float)Qs[t * LDX + ip] * fcur);
+        fprev = fcur;
       }
       __syncthreads();
     }

@@ -536,6 +536,11 @@ def pin_p18_qk_norm_is_the_rule_on_normalised_inputs(orc):
             np.testing.assert_allclose(o[0, 0], o2[0, 0], rtol=0, atol=1e-11)
             np.testing.assert_allclose(S[0, 0], S2[0, 0], rtol=0, atol=1e-11)
             assert np.array_equal(xp[0, 0], k[-1]) and h[0, 0] == 1
+    # a zero query or key stays zero: with every key zero, nothing is written
+    q, k, v, beta, lam = _qk_cases(rng, T, dk, dv)
+    o, S, _, _ = orc.scan(_bh(q), _bh(np.zeros_like(k)), _bh(v), _bh(beta), _bh(lam[DELTA]), rule=DELTA,
+                          qk_norm="l2")
+    assert np.all(S == 0.0) and np.all(o == 0.0)
 
 
 def pin_p19_qk_norm_scale_invariance(orc):

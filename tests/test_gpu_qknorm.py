@@ -123,3 +123,13 @@ def test_qknorm_decode_steps(rule, mode):
 @pytest.mark.slow
 def test_qknorm_full_throughput_shape():
     check_scan(wl.delta_bf16_h16_qknorm(seed=0), label="delta_bf16_h16_qknorm B=4 H=16 T=4096")
+
+
+def test_qknorm_zero_rows_stay_zero():
+    """Zero query and key rows (padding tokens) normalise to zero in the oracle (reading
+    D16) and in the library: no division by zero, and the scan matches."""
+    w = _raw("delta", "l2", 1, 2, 200, 128, 128, seed=31)
+    w.q[:, :, 40:50] = 0.0
+    w.k[:, :, 60:75] = 0.0
+    w.k[:, :, -1] = 0.0
+    check_scan(w, label="qk l2 with zero rows")
