@@ -42,31 +42,31 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "prop_split_kernel"): {
         "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_scan_split.hip": "48789642986e8b3b42164755c4e546834b3abe6f4832b33e6267ac2f7106cc30",
+            "fwmem_scan_split.hip": "6bd7442b8699dc5763d11fb0a8e7a2d4820155cc72a7f7149007c955fe4be9f7",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
+            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
         },
-        "fetch_kib": 150224.9, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150225.0, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
         "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_prep_split.hip": "94aa2d7bcab80fc178c7f1582356bd4dddea50e3a262ad95b52297f2fc187084",
+            "fwmem_prep_split.hip": "2ff431ac28443009022ef54714ae852073a65c18725cd9df5a77a0778098ed3d",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
+            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
         },
-        "fetch_kib": 66675.4, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66671.6, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("decode", "step_kernel"): {
         "sources": ("fwmem_step.hip", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_step.hip": "5b21bd2528d97bd17d952e4b984f9bb92f7b413c5a08599166946a94ee9ba054",
+            "fwmem_step.hip": "65f4c64a4128bfc773a29665c3f22c8ba29dcec8573cad513b7f482d6a16ee25",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "edd996ad1beeb5fdd0b82b0509399637e728ea5238c74d72a4166271e059bc3b",
+            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
         },
-        "fetch_kib": 267969.8, "write_kib": 532893.7, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267724.3, "write_kib": 532890.5, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
