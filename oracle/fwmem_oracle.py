@@ -31,6 +31,8 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
   D16 normalised q and k (qk_norm): each is rescaled to length 1 (l2) or sqrt(d_k)
       (RMSNorm with unit gain and no epsilon), a zero vector stays zero, and the
       carried key is stored raw.
+  D17 gate pre-activations (beta_act, lam_act): beta = sigmoid(z) or 2 sigmoid(z); the
+      ridge lambda = softplus(z), the additive retention gamma = sigmoid(z).
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -61,6 +63,18 @@ def _heads(a, tail_ndim):
     return a.reshape((-1,) + a.shape[a.ndim - tail_ndim:])
 
 
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """1 / (1 + e^-z), in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def softplus(z: np.ndarray) -> np.ndarray:
+    """log(1 + e^z), in float64 (z itself where e^z would overflow the sum's precision)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z > 30.0, z, np.log1p(np.exp(np.minimum(z, 30.0))))
+
+
 def unit_rows(x: np.ndarray, length: float = 1.0) -> np.ndarray:
     """Each row (last axis) rescaled to the given Euclidean length; a zero row stays
     zero (reading D16)."""
@@ -70,7 +84,7 @@ def unit_rows(x: np.ndarray, length: float = 1.0) -> np.ndarray:
 
 
 def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None, qk_norm=None):
+         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False):
     """Run the recurrence over a whole sequence.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] or None; lam: [B,H,T] (or
@@ -81,6 +95,11 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     [FWA] section 4.5 normalises the query and key projections (RMSNorm by default,
     l2 in the DeltaNet variants); reading D16. Identity feature map only. The carried
     key stays the raw k of the last token and is rescaled where it is used.
+    beta_act: None, "sigmoid" or "sigmoid2": beta holds pre-activations z and the step
+    size (delta, inner) or write scale (additive) is sigmoid(z) or 2 sigmoid(z), the
+    latter spanning the range (0, 2) of [FWA] section 4.2. lam_act: lam holds
+    pre-activations; the ridge is softplus(z) (delta, inner) and the retention sigmoid(z)
+    (additive). Reading D17.
 
     Returns (o [B,H,T,dv], S [B,H,dk,dv], xprev [B,H,dk], has [B,H]) in float64.
     """
@@ -92,10 +111,14 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     K = _heads(k, 2)
     V = _heads(v, 2)
     Bt = None if beta is None else _heads(beta, 1)
+    if Bt is not None and beta_act is not None:
+        Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)
     if lam is None:
         Lm = None
     else:
         Lm = _heads(lam, 2 if per_channel else 1)
+        if lam_act:
+            Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)
 
     S = np.zeros((N, dk, dv)) if S0 is None else _heads(S0, 2).copy()
     xprev = np.zeros((N, dk)) if xprev0 is None else _heads(xprev0, 1).copy()
@@ -166,7 +189,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
 
 
 def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None, qk_norm=None):
+         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False):
     """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
     (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
     q = np.asarray(q)[:, :, None]
@@ -177,7 +200,8 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         lam = np.asarray(lam)
         lam = lam[:, :, None, :] if per_channel else lam[:, :, None]
     o, S, xp, h = scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind, eps=eps,
-                       per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm)
+                       per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm,
+                       beta_act=beta_act, lam_act=lam_act)
     return o[:, :, 0], S, xp, h
 
 

@@ -571,6 +571,32 @@ def pin_p19_qk_norm_scale_invariance(orc):
         np.testing.assert_allclose(xpc, k[-1] * ck[-1], rtol=1e-15, atol=0)
 
 
+def pin_p20_gate_preactivations(orc):
+    """Gates passed as pre-activations z ([FWA] 4.2 keeps beta in (0, 2); the ridge is
+    nonnegative and the additive retention lies in (0, 1)): the scan equals the plain
+    scan on gates activated here by independent formulas, sigmoid(z) = (1 + tanh(z/2))/2
+    and softplus(z) = logaddexp(0, z); and the special values sigmoid(0) = 1/2,
+    softplus(0) = ln 2 hold."""
+    rng = np.random.default_rng(38)
+    T, dk, dv = 12, 5, 4
+    sig = lambda z: 0.5 * (1.0 + np.tanh(0.5 * z))
+    sp = lambda z: np.logaddexp(0.0, z)
+    assert orc.sigmoid(np.array(0.0)) == 0.5 and abs(orc.softplus(np.array(0.0)) - np.log(2.0)) < 1e-16
+    for rule in (DELTA, INNER, ADD):
+        for per_channel in (False, True):
+            q, k, v = (rng.standard_normal((T, d)) for d in (dk, dk, dv))
+            zb = rng.standard_normal(T) * 2
+            zl = rng.standard_normal((T, dk) if per_channel else T) * 2 - 2
+            for act, scale in (("sigmoid", 1.0), ("sigmoid2", 2.0)):
+                lam_ref = sig(zl) if rule == ADD else sp(zl)
+                o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(zb), _bh(zl), rule=rule,
+                                      per_channel=per_channel, beta_act=act, lam_act=True)
+                o2, S2, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(scale * sig(zb)), _bh(lam_ref),
+                                        rule=rule, per_channel=per_channel)
+                np.testing.assert_allclose(o[0, 0], o2[0, 0], rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(S[0, 0], S2[0, 0], rtol=1e-12, atol=1e-12)
+
+
 def pin_relerr_metric(orc):
     """The parity metric max|x - ref| / rms(ref) on a case worked by hand."""
     ref = np.array([3.0, -4.0])          # rms = sqrt((9 + 16)/2) = 5/sqrt(2)
@@ -601,5 +627,6 @@ ALL_PINS = [
     pin_p9_hand_inner,
     pin_p18_qk_norm_is_the_rule_on_normalised_inputs,
     pin_p19_qk_norm_scale_invariance,
+    pin_p20_gate_preactivations,
     pin_relerr_metric,
 ]

@@ -45,6 +45,9 @@ MUTANTS = {
                                   "x = np.where(has[:, None], xprev, 0.0)"),
     "qk_norm_skips_query": ("qt = unit(phi(Q[:, t], phi_kind))", "qt = phi(Q[:, t], phi_kind)"),
     "qk_norm_rms_length_one": ('length = 1.0 if qk_norm == "l2" else float(np.sqrt(dk))', "length = 1.0"),
+    "retention_uses_softplus": ("Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)",
+                                "Lm = softplus(Lm)"),
+    "beta_range_one": ('Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)', "Bt = sigmoid(Bt)"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
