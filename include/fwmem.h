@@ -71,7 +71,7 @@ typedef struct ihipStream_t* fwmem_stream; /* the same handle type as hipStream_
 typedef enum {
   FWMEM_OK = 0,
   FWMEM_EINVAL = -1,       /* NULL required pointer, negative size, unknown rule/flag/dtype, bad eps,
-                              both QK normalisation flags */
+                              both QK normalisation flags, both beta activations */
   FWMEM_EUNSUPPORTED = -2, /* a size or chunk length the library has no kernel for, or a QK
                               normalisation flag with FWMEM_PHI_ELU1 */
   FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda) */
@@ -94,8 +94,15 @@ enum {
   FWMEM_OUT_BF16 = 1u << 2,           /* out is bf16 instead of float32 (adds rounding up to
                                          2^-9 relative per element) */
   FWMEM_QK_L2NORM = 1u << 3,          /* q_t and k_t are used rescaled to unit length */
-  FWMEM_QK_RMSNORM = 1u << 4          /* q_t and k_t are used rescaled to RMS 1, i.e. length
+  FWMEM_QK_RMSNORM = 1u << 4,         /* q_t and k_t are used rescaled to RMS 1, i.e. length
                                          sqrt(dk): RMSNorm with unit gain, no epsilon */
+  FWMEM_BETA_SIGMOID = 1u << 5,       /* beta holds pre-activations z: beta_t = sigmoid(z_t) */
+  FWMEM_BETA_SIGMOID2 = 1u << 6,      /* beta_t = 2 sigmoid(z_t), the range (0, 2) of the
+                                         normalised step ("Fast Weight Attention for
+                                         Continual Learning" reading notes, section 4.2) */
+  FWMEM_LAMBDA_PREACT = 1u << 7       /* lambda holds pre-activations z: the ridge
+                                         softplus(z) (DELTA, INNER) or the retention
+                                         sigmoid(z) (ADDITIVE), applied per element */
 };
 
 typedef struct {

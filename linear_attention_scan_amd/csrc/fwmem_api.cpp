@@ -14,7 +14,8 @@ namespace {
 using fwmem::kChunk;
 
 constexpr uint32_t kKnownFlags =
-    FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16 | FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM;
+    FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16 | FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM |
+    FWMEM_BETA_SIGMOID | FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -57,6 +58,7 @@ fwmem_status check_mode(const fwmem_mode* m) {
   if ((m->flags & ~kKnownFlags) != 0) return FWMEM_EINVAL;
   // one normalisation at a time, and only of the raw q and k (identity feature map)
   if ((m->flags & FWMEM_QK_L2NORM) && (m->flags & FWMEM_QK_RMSNORM)) return FWMEM_EINVAL;
+  if ((m->flags & FWMEM_BETA_SIGMOID) && (m->flags & FWMEM_BETA_SIGMOID2)) return FWMEM_EINVAL;
   if ((m->flags & (FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM)) && (m->flags & FWMEM_PHI_ELU1))
     return FWMEM_EUNSUPPORTED;
   if (!std::isfinite(m->eps) || m->eps < 0.f) return FWMEM_EINVAL;

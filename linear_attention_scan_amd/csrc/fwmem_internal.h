@@ -14,6 +14,9 @@ enum : uint32_t {
   kFlagOutBf16 = 1u << 2,
   kFlagQkL2 = 1u << 3,
   kFlagQkRms = 1u << 4,
+  kFlagBetaSig = 1u << 5,
+  kFlagBetaSig2 = 1u << 6,
+  kFlagLamAct = 1u << 7,
 };
 
 constexpr int kChunk = 64;  // scan chunk length (tokens)
@@ -24,6 +27,23 @@ __host__ __device__ inline float qk_length(uint32_t flags, int dk) {
   if (flags & kFlagQkRms) return __builtin_sqrtf((float)dk);
   return 0.f;
 }
+// Gate activations (FWMEM_BETA_SIGMOID / FWMEM_BETA_SIGMOID2 / FWMEM_LAMBDA_PREACT): the
+// step size or write scale sigmoid(z) or 2 sigmoid(z); the ridge softplus(z) for the
+// shifted-pair rules (nlms) and the retention sigmoid(z) for the additive rule. Without
+// the flags the gate is used as given.
+__device__ inline float act_beta(float z, uint32_t flags) {
+  if (flags & kFlagBetaSig) return 1.f / (1.f + __expf(-z));
+  if (flags & kFlagBetaSig2) return 2.f / (1.f + __expf(-z));
+  return z;
+}
+__device__ inline float act_lam(float z, uint32_t flags, bool nlms) {
+  if (!(flags & kFlagLamAct)) return z;
+  if (!nlms) return 1.f / (1.f + __expf(-z));
+  return z > 30.f ? z : log1pf(__expf(z));
+}
+// Start of a running maximum of lambda over channels: pre-activations may be negative.
+__device__ inline float lam_max_init(uint32_t flags) { return (flags & kFlagLamAct) ? -__builtin_inff() : 0.f; }
+
 // Factor that rescales a vector with squared length ss to length len (a zero vector
 // stays zero).
 __host__ __device__ inline float rescale_factor(float ss, float len) {

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   }
   float g_beta = 0.f, g_lam = 0.f;
   if (wave == 0 && t0 + lane < T) {
-    g_beta = p.beta != nullptr ? p.beta[rowbase + t0 + lane] : 1.f;
-    if (p.lam != nullptr) g_lam = p.lam[rowbase + t0 + lane];
+    g_beta = p.beta != nullptr ? act_beta(p.beta[rowbase + t0 + lane], p.flags) : 1.f;
+    if (p.lam != nullptr) g_lam = act_lam(p.lam[rowbase + t0 + lane], p.flags, R::nlms);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (R::shift && c == 0 && tid < NGR) {

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   float g_beta = 0.f, g_lam = 0.f;
   if (wave == 0 && t0 + lane < p.T) {
     const size_t ti = rowbase + t0 + lane;
-    g_beta = p.beta != nullptr ? p.beta[ti] : 1.f;
-    if (!PC && p.lam != nullptr) g_lam = p.lam[ti];
+    g_beta = p.beta != nullptr ? act_beta(p.beta[ti], p.flags) : 1.f;
+    if (!PC && p.lam != nullptr) g_lam = act_lam(p.lam[ti], p.flags, R::nlms);
   }
 
   // ---- row staging: x rows (shifted keys for the shifted pair) and q rows, phi
@@ -224,13 +224,14 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     for (int ps = 0; ps < NPL; ++ps) {
       const int t = ps * RPPL + tid / TPRL;
       const int tau = t0 + t;
-      float m = 0.f;
+      float m = lam_max_init(p.flags);
       if (tau < p.T && p.lam != nullptr) {
         const f4 w = *reinterpret_cast<const f4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
         m = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
       }
       m = group_max<TPRL>(m);
-      if (tid % TPRL == 0) s_lam[t] = m;
+      // the activation is monotonic: the max of the activated values is the activated max
+      if (tid % TPRL == 0) s_lam[t] = p.lam != nullptr ? act_lam(m, p.flags, true) : 0.f;
     }
   }
   __syncthreads();
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       for (int t = 0; t < CH; ++t) {
         const int tau = t0 + t;
         float lam = R::nlms ? 0.f : 1.f;
-        if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
+        if (tau < p.T && p.lam != nullptr) lam = act_lam(p.lam[(rowbase + tau) * DK + i], p.flags, R::nlms);
         const float a = R::nlms ? 1.f - s_eta[t] * lam : lam;
         gs += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;
@@ -832,7 +833,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       for (int u = 0; u < SEG; ++u) {
         const int tau = t0 + tb + u;
         float lam = R::nlms ? 0.f : 1.f;
-        if (tau < p.T && p.lam != nullptr) lam = p.lam[(rowbase + tau) * DK + i];
+        if (tau < p.T && p.lam != nullptr) lam = act_lam(p.lam[(rowbase + tau) * DK + i], p.flags, R::nlms);
         const float a = R::nlms ? 1.f - s_fV[tb + u] * lam : lam;
         gsum += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;

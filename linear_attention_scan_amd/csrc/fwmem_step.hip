@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   // Scalars: ||x||^2, max lambda (per channel), x.q or k.q; wave 0 reduces. With
   // normalised queries and keys, x and q are rescaled by mx and mq (to length qk_len).
   if (wave == 0) {
-    float nx = 0.f, dq = 0.f, lm = 0.f, nq = 0.f;
+    float nx = 0.f, dq = 0.f, lm = lam_max_init(p.flags), nq = 0.f;
     for (int i = lane; i < DK; i += 64) {
       const float xi = R::shift ? s_x[i] : s_k[i];
       nx += xi * xi;
@@ -94,6 +94,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     dq = wave_sum(dq);
     nq = wave_sum(nq);
     lm = wave_max(lm);
+    if (PC && p.lam != nullptr) lm = act_lam(lm, p.flags, true);  // monotonic: max commutes
     float mx = 1.f, mq = 1.f;
     if (qk_len > 0.f) {
       mx = rescale_factor(nx, qk_len);
@@ -104,12 +105,13 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     if (lane == 0) {
       float eta = 0.f, a = 1.f;
       if (R::nlms) {
-        const float lam = PC ? lm : (p.lam != nullptr ? p.lam[bh] : 0.f);
-        if (has) eta = p.beta[bh] / (nx + lam + p.eps);
+        const float lam = PC ? (p.lam != nullptr ? lm : 0.f)
+                             : (p.lam != nullptr ? act_lam(p.lam[bh], p.flags, true) : 0.f);
+        if (has) eta = act_beta(p.beta[bh], p.flags) / (nx + lam + p.eps);
         a = 1.f - eta * lam;
       } else {
-        eta = p.beta != nullptr ? p.beta[bh] : 1.f;  // write scale
-        a = (!PC && p.lam != nullptr) ? p.lam[bh] : 1.f;
+        eta = p.beta != nullptr ? act_beta(p.beta[bh], p.flags) : 1.f;  // write scale
+        a = (!PC && p.lam != nullptr) ? act_lam(p.lam[bh], p.flags, false) : 1.f;
       }
       s_sc[0] = eta;
       s_sc[1] = a;
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     }
     float a = a_sc;
     if (PC) {
-      const float lam = p.lam != nullptr ? p.lam[(size_t)bh * DK + i] : (R::nlms ? 0.f : 1.f);
+      const float lam = p.lam != nullptr ? act_lam(p.lam[(size_t)bh * DK + i], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
       a = R::nlms ? 1.f - eta * lam : lam;
     }
     s_a[i] = a;

@@ -22,6 +22,9 @@ LAMBDA_PER_CHANNEL = 1 << 1
 OUT_BF16 = 1 << 2
 QK_L2NORM = 1 << 3
 QK_RMSNORM = 1 << 4
+BETA_SIGMOID = 1 << 5
+BETA_SIGMOID2 = 1 << 6
+LAMBDA_PREACT = 1 << 7
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",

@@ -102,6 +102,11 @@ class ScanInputs:
     has0: Optional[np.ndarray] = None      # [B,H] int32 or None
     qk_norm: Optional[str] = None          # None, 'l2' or 'rms': q, k are raw and the scan
                                            # normalises them (the library's QK flags)
+    beta_pre: Optional[np.ndarray] = None  # the pre-activations the gates were drawn from
+    lam_pre: Optional[np.ndarray] = None
+    beta_act: Optional[str] = None         # how beta follows from beta_pre: 'sigmoid', 'sigmoid2'
+    lam_act: bool = False                  # lam = softplus(lam_pre) (or sigmoid for gamma)
+    gates_pre: bool = False                # hand the library the pre-activations (its gate flags)
 
     @property
     def tokens(self) -> int:
@@ -143,10 +148,14 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
     elif dtype != "f32":
         raise ValueError(dtype)
 
+    beta_pre = lam_pre = beta_act = None
+    lam_act = False
     if beta_kind == "sigmoid":
-        beta = _sigmoid(_normal(rng, (B, H, T)))
+        beta_pre = _normal(rng, (B, H, T))
+        beta, beta_act = _sigmoid(beta_pre), "sigmoid"
     elif beta_kind == "two_sigmoid":
-        beta = (2.0 * _sigmoid(_normal(rng, (B, H, T)))).astype(np.float32)
+        beta_pre = _normal(rng, (B, H, T))
+        beta, beta_act = (2.0 * _sigmoid(beta_pre)).astype(np.float32), "sigmoid2"
     elif beta_kind == "one":
         beta = None
     else:
@@ -156,9 +165,11 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
     if lam_kind == "const":
         lam = np.full(lam_shape, lam_const, dtype=np.float32)
     elif lam_kind == "softplus":
-        lam = _softplus(_normal(rng, lam_shape, mean=lam_mu))
+        lam_pre = _normal(rng, lam_shape, mean=lam_mu)
+        lam, lam_act = _softplus(lam_pre), True
     elif lam_kind == "gamma":
-        lam = _sigmoid(_normal(rng, lam_shape, mean=gamma_mu, std=gamma_sd))
+        lam_pre = _normal(rng, lam_shape, mean=gamma_mu, std=gamma_sd)
+        lam, lam_act = _sigmoid(lam_pre), True
     elif lam_kind == "none":
         lam = None
     else:
@@ -169,7 +180,8 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
         S0 = _normal(rng, (B, H, dk, dv), std=s0_std)
     return ScanInputs(name=name, B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, rule=rule,
                       phi=phi, per_channel=per_channel, eps=eps, q=q, k=k, v=v,
-                      beta=beta, lam=lam, S0=S0, qk_norm=qk_norm)
+                      beta=beta, lam=lam, S0=S0, qk_norm=qk_norm, beta_pre=beta_pre,
+                      lam_pre=lam_pre, beta_act=beta_act, lam_act=lam_act)
 
 
 def delta_f32_small(seed=0, T=256):

@@ -41,7 +41,20 @@ def flags_of(w: wl.ScanInputs, extra=0):
         f |= F.LAMBDA_PER_CHANNEL
     if w.qk_norm is not None:
         f |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
+    if w.gates_pre:
+        if w.beta_act is not None:
+            f |= {"sigmoid": F.BETA_SIGMOID, "sigmoid2": F.BETA_SIGMOID2}[w.beta_act]
+        if w.lam_act:
+            f |= F.LAMBDA_PREACT
     return f
+
+
+def gates_of(w: wl.ScanInputs):
+    """The gate arrays the library receives: the activated gates, or with gates_pre the
+    pre-activations they were drawn from (those that have one)."""
+    beta = w.beta_pre if (w.gates_pre and w.beta_act is not None) else w.beta
+    lam = w.lam_pre if (w.gates_pre and w.lam_act) else w.lam
+    return beta, lam
 
 
 def make_state(B, H, dk, dv, S=None, xprev=None, has=None):
@@ -64,8 +77,9 @@ def gpu_scan(w: wl.ScanInputs, *, t_slice=None, S_in=None, S_out=None, extra_fla
     q = dev_tensor(w.q[:, :, sl], w.dtype)
     k = dev_tensor(w.k[:, :, sl], w.dtype)
     v = dev_tensor(w.v[:, :, sl], w.dtype)
-    beta = f32_tensor(None if w.beta is None else w.beta[:, :, sl])
-    lam = f32_tensor(None if w.lam is None else w.lam[:, :, sl])
+    gb, gl = gates_of(w)
+    beta = f32_tensor(None if gb is None else gb[:, :, sl])
+    lam = f32_tensor(None if gl is None else gl[:, :, sl])
     if S_in is None and w.S0 is not None:
         S_in = make_state(w.B, w.H, w.dk, w.dv, S=w.S0, xprev=w.xprev0, has=w.has0)
     out, st = F.scan_fwd(q, k, v, beta, lam, rule=w.rule, flags=flags_of(w, extra_flags),
@@ -77,11 +91,14 @@ def gpu_scan(w: wl.ScanInputs, *, t_slice=None, S_in=None, S_out=None, extra_fla
 def oracle_scan(w: wl.ScanInputs, t_slice=None, S0=None, xprev0=None, has0=None):
     sl = slice(None) if t_slice is None else t_slice
     S0 = w.S0 if S0 is None else S0
+    gb, gl = gates_of(w)
     return orc.scan(w.q[:, :, sl], w.k[:, :, sl], w.v[:, :, sl],
-                    None if w.beta is None else w.beta[:, :, sl],
-                    None if w.lam is None else w.lam[:, :, sl],
+                    None if gb is None else gb[:, :, sl],
+                    None if gl is None else gl[:, :, sl],
                     rule=w.rule, phi_kind=w.phi, eps=w.eps, per_channel=w.per_channel,
-                    S0=S0, xprev0=xprev0, has0=has0, qk_norm=w.qk_norm)
+                    S0=S0, xprev0=xprev0, has0=has0, qk_norm=w.qk_norm,
+                    beta_act=w.beta_act if (w.gates_pre and gb is w.beta_pre) else None,
+                    lam_act=bool(w.gates_pre and w.lam_act))
 
 
 def state_np(st):

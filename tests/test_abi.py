@@ -94,6 +94,7 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(md=F.mode(rule=3)), F.EINVAL),
     (dict(md=F.mode(flags=F.QK_L2NORM | F.QK_RMSNORM)), F.EINVAL),
     (dict(md=F.mode(flags=F.QK_RMSNORM | F.PHI_ELU1)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.BETA_SIGMOID | F.BETA_SIGMOID2)), F.EINVAL),
     (dict(q=FAKE + 2), F.EALIGN),
     (dict(out=FAKE * 64 + 8), F.EALIGN),
     (dict(beta=FAKE + 2), F.EALIGN),
@@ -131,7 +132,7 @@ def test_empty_batch_is_a_no_op():
     (dict(beta=None), F.EINVAL),
     (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),
     (dict(md=F.mode(rule=-1)), F.EINVAL),
-    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 7)), F.EINVAL),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 12)), F.EINVAL),
     (dict(q=FAKE + 1), F.EALIGN),
     (dict(out=FAKE * 64 + 4), F.EALIGN),
     (dict(S_in=FAKE * 1024 + 64), F.EOVERLAP),
