@@ -45,28 +45,28 @@ MEASURED_TRAFFIC = {
             "fwmem_scan_split.hip": "6bd7442b8699dc5763d11fb0a8e7a2d4820155cc72a7f7149007c955fe4be9f7",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
+            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
         },
-        "fetch_kib": 150225.0, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150225.3, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
         "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_prep_split.hip": "2ff431ac28443009022ef54714ae852073a65c18725cd9df5a77a0778098ed3d",
+            "fwmem_prep_split.hip": "80af25956854a86f4f4f219dd9685f7b9ff1b960af4bd656795ba918127b6573",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
+            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
         },
-        "fetch_kib": 66671.6, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66679.6, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("decode", "step_kernel"): {
         "sources": ("fwmem_step.hip", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_step.hip": "65f4c64a4128bfc773a29665c3f22c8ba29dcec8573cad513b7f482d6a16ee25",
+            "fwmem_step.hip": "508e7f6083e8154860d36d8053a5dc5e51fc02fb4dd2b8f0b032a7cd4cd65270",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "93167d1251f68f250a0a5dcb1475561cff0133a101e9edfad485f59d0dfe6bcf",
+            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
         },
-        "fetch_kib": 267724.3, "write_kib": 532890.5, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267721.8, "write_kib": 532876.9, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
