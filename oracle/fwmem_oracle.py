@@ -33,6 +33,8 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
       carried key is stored raw.
   D17 gate pre-activations (beta_act, lam_act): beta = sigmoid(z) or 2 sigmoid(z); the
       ridge lambda = softplus(z), the additive retention gamma = sigmoid(z).
+  D18 normalised linear attention (znorm): o_t = S_t^T phi(q_t) / (z_t . phi(q_t) + eps)
+      with z decayed like S; z is carried in the carried-key slot of the state.
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -84,7 +86,8 @@ def unit_rows(x: np.ndarray, length: float = 1.0) -> np.ndarray:
 
 
 def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False):
+         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False,
+         znorm=False):
     """Run the recurrence over a whole sequence.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] or None; lam: [B,H,T] (or
@@ -100,6 +103,11 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     latter spanning the range (0, 2) of [FWA] section 4.2. lam_act: lam holds
     pre-activations; the ridge is softplus(z) (delta, inner) and the retention sigmoid(z)
     (additive). Reading D17.
+    znorm: additive rule only. The read is divided by the normaliser,
+    o_t = S_t^T phi(q_t) / (z_t . phi(q_t) + eps), z_t = gamma_t z_{t-1} + beta_t phi(k_t)
+    ([AFFN] section 4.2, with the decay applied to z as well, as that section suggests).
+    z takes the place of the carried key in the state (xprev0 / the returned xprev),
+    since the additive rule never reads that key (reading D18).
 
     Returns (o [B,H,T,dv], S [B,H,dk,dv], xprev [B,H,dk], has [B,H]) in float64.
     """
@@ -134,6 +142,10 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         unit = lambda a: unit_rows(a, length)
     else:
         raise ValueError(qk_norm)
+
+    if znorm and rule != RULE_ADDITIVE:
+        raise ValueError("znorm takes the additive rule")
+    z = xprev.copy() if znorm else None
 
     for t in range(T):
         qt = unit(phi(Q[:, t], phi_kind))
@@ -177,19 +189,24 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
                 gam = Lm[:, t][:, None, None]
             b = np.ones(N) if Bt is None else Bt[:, t]
             S = gam * S + b[:, None, None] * kt[:, :, None] * vt[:, None, :]
+            if znorm:
+                z = gam[:, :, 0] * z + b[:, None] * kt
         else:
             raise ValueError(rule)
-        xprev = k_raw
+        xprev = z if znorm else k_raw
         has = np.ones(N, dtype=bool)
         # read after write: o_t = S_t^T phi(q_t) ([AFFN] 2.1; [FWA] 4.1)
         O[:, t] = np.einsum("nij,ni->nj", S, qt)
+        if znorm:
+            O[:, t] /= (np.sum(z * qt, axis=1) + eps)[:, None]
 
     return (O.reshape(B, H, T, dv), S.reshape(B, H, dk, dv), xprev.reshape(B, H, dk),
             has.reshape(B, H).astype(np.int32))
 
 
 def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
-         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False):
+         S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False,
+         znorm=False):
     """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
     (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
     q = np.asarray(q)[:, :, None]
@@ -201,7 +218,7 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         lam = lam[:, :, None, :] if per_channel else lam[:, :, None]
     o, S, xp, h = scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind, eps=eps,
                        per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm,
-                       beta_act=beta_act, lam_act=lam_act)
+                       beta_act=beta_act, lam_act=lam_act, znorm=znorm)
     return o[:, :, 0], S, xp, h
 
 

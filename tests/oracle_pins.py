@@ -597,6 +597,42 @@ def pin_p20_gate_preactivations(orc):
                 np.testing.assert_allclose(S[0, 0], S2[0, 0], rtol=1e-12, atol=1e-12)
 
 
+def pin_p21_normalised_linear_attention(orc):
+    """[AFFN] 4.2: with the normaliser, the read is the quadratic form divided by its
+    weights, o_t = sum_{j<=t} w_tj v_j / (sum_{j<=t} w_tj + eps) with
+    w_tj = (prod_{s=j+1..t} gamma_s) beta_j (phi(q_t) . phi(k_j)), brute-forced; and with
+    eps = 0 every value equal to one vector c makes every read exactly c (a weighted
+    average of equal values)."""
+    rng = np.random.default_rng(39)
+    T, dk, dv, eps = 11, 5, 4, 1e-3
+    for per_channel in (False, True):
+        q = rng.standard_normal((T, dk))
+        k = rng.standard_normal((T, dk))
+        v = rng.standard_normal((T, dv))
+        beta = rng.uniform(0.2, 1.5, T)
+        gam = rng.uniform(0.6, 1.0, (T, dk) if per_channel else T)
+        o, _, z, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(gam), rule=ADD, phi_kind="elu1",
+                              per_channel=per_channel, eps=eps, znorm=True)
+        fq = np.where(q > 0, q + 1.0, np.exp(np.minimum(q, 0.0)))
+        fk = np.where(k > 0, k + 1.0, np.exp(np.minimum(k, 0.0)))
+        g = gam if per_channel else np.repeat(gam[:, None], dk, axis=1)
+        z_ref = np.zeros(dk)
+        for t in range(T):
+            num, den = np.zeros(dv), 0.0
+            for j in range(t + 1):
+                dec = np.prod(g[j + 1:t + 1], axis=0) if j < t else np.ones(dk)
+                w = beta[j] * float(np.sum(fq[t] * dec * fk[j]))
+                num += w * v[j]
+                den += w
+            np.testing.assert_allclose(o[0, 0, t], num / (den + eps), rtol=1e-11, atol=1e-12)
+            z_ref = g[t] * z_ref + beta[t] * fk[t]
+        np.testing.assert_allclose(z[0, 0], z_ref, rtol=1e-12)
+    c = rng.standard_normal(dv)
+    o, _, _, _ = orc.scan(_bh(q), _bh(k), _bh(np.tile(c, (T, 1))), _bh(beta), _bh(gam[:, 0] if gam.ndim == 2 else gam),
+                          rule=ADD, phi_kind="elu1", eps=0.0, znorm=True)
+    np.testing.assert_allclose(o[0, 0], np.tile(c, (T, 1)), rtol=1e-12, atol=1e-12)
+
+
 def pin_relerr_metric(orc):
     """The parity metric max|x - ref| / rms(ref) on a case worked by hand."""
     ref = np.array([3.0, -4.0])          # rms = sqrt((9 + 16)/2) = 5/sqrt(2)
@@ -628,5 +664,6 @@ ALL_PINS = [
     pin_p18_qk_norm_is_the_rule_on_normalised_inputs,
     pin_p19_qk_norm_scale_invariance,
     pin_p20_gate_preactivations,
+    pin_p21_normalised_linear_attention,
     pin_relerr_metric,
 ]

@@ -48,6 +48,8 @@ MUTANTS = {
     "retention_uses_softplus": ("Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)",
                                 "Lm = softplus(Lm)"),
     "beta_range_one": ('Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)', "Bt = sigmoid(Bt)"),
+    "znorm_no_decay": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = z + b[:, None] * kt"),
+    "znorm_no_beta": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = gam[:, :, 0] * z + kt"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
