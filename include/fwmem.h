@@ -100,9 +100,21 @@ enum {
   FWMEM_BETA_SIGMOID2 = 1u << 6,      /* beta_t = 2 sigmoid(z_t), the range (0, 2) of the
                                          normalised step ("Fast Weight Attention for
                                          Continual Learning" reading notes, section 4.2) */
-  FWMEM_LAMBDA_PREACT = 1u << 7       /* lambda holds pre-activations z: the ridge
+  FWMEM_LAMBDA_PREACT = 1u << 7,      /* lambda holds pre-activations z: the ridge
                                          softplus(z) (DELTA, INNER) or the retention
                                          sigmoid(z) (ADDITIVE), applied per element */
+  FWMEM_ZNORM = 1u << 8               /* normalised linear attention ("attention is also
+                                         an FFN", section 4.2; ADDITIVE only): the
+                                         normaliser z_t = gamma_t z_{t-1} + b_t phi(k~_t)
+                                         (decayed as S is) divides the read,
+                                         o_t = S_t^T q~_t / (z_t . q~_t + eps). z takes
+                                         the state's x_prev slot (read whether or not
+                                         has_prev is set; the additive rule carries no
+                                         key). Scans take it with a scalar decay and
+                                         float32 outputs (else FWMEM_EUNSUPPORTED);
+                                         fwmem_step takes every ADDITIVE mode. The
+                                         caller keeps z . q~ away from -eps, e.g. with
+                                         positive features (elu+1). */
 };
 
 typedef struct {

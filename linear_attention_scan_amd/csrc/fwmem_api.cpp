@@ -15,7 +15,7 @@ using fwmem::kChunk;
 
 constexpr uint32_t kKnownFlags =
     FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16 | FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM |
-    FWMEM_BETA_SIGMOID | FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT;
+    FWMEM_BETA_SIGMOID | FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_ZNORM;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -61,8 +61,20 @@ fwmem_status check_mode(const fwmem_mode* m) {
   if ((m->flags & FWMEM_BETA_SIGMOID) && (m->flags & FWMEM_BETA_SIGMOID2)) return FWMEM_EINVAL;
   if ((m->flags & (FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM)) && (m->flags & FWMEM_PHI_ELU1))
     return FWMEM_EUNSUPPORTED;
+  // the normaliser accumulates the additive rule's writes
+  if ((m->flags & FWMEM_ZNORM) && m->rule != FWMEM_RULE_ADDITIVE) return FWMEM_EUNSUPPORTED;
   if (!std::isfinite(m->eps) || m->eps < 0.f) return FWMEM_EINVAL;
   if (m->chunk != 0 && m->chunk != kChunk) return FWMEM_EUNSUPPORTED;
+  return FWMEM_OK;
+}
+
+// Scans divide their float32 outputs in place and keep one normaliser per key channel
+// only for a scalar decay.
+fwmem_status check_scan_mode(const fwmem_mode* m) {
+  const fwmem_status st = check_mode(m);
+  if (st != FWMEM_OK) return st;
+  if ((m->flags & FWMEM_ZNORM) && (m->flags & (FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16)))
+    return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;
 }
 
@@ -74,10 +86,11 @@ struct StatePtrs {
 };
 
 // Workspace of a scan: the (head, chunk) records, and for a segmented scan (P > 1 segments
-// per head, see SegParams) the two virtual state buffers, z and the segment start states.
+// per head, see SegParams) the two virtual state buffers, z and the segment start states;
+// with FWMEM_ZNORM the normaliser's chunk terms (ZRec) and its value at every chunk entry.
 struct WsLayout {
   int P;
-  size_t rec, A0, B0, A1, B1, z, start, total;
+  size_t rec, A0, B0, A1, B1, z, start, zr, zc, total;
 };
 
 WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
@@ -101,6 +114,12 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
     off += align256(4 * BH * T * dk);
     w.start = off;
     off += align256(4 * VH * dk * dv);
+  }
+  if (m->flags & FWMEM_ZNORM) {
+    w.zr = off;
+    off += align256(4 * BH * nchunks * fwmem::zrec_floats(s->dk));
+    w.zc = off;
+    off += align256(4 * BH * nchunks * (size_t)s->dk);
   }
   w.total = T > 0 ? off : 0;
   return w;
@@ -147,7 +166,7 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
   if (bytes == nullptr) return FWMEM_EINVAL;
   fwmem_status st = check_shape(shape, true);
   if (st != FWMEM_OK) return st;
-  st = check_mode(mode);
+  st = check_scan_mode(mode);
   if (st != FWMEM_OK) return st;
   if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   *bytes = ws_layout(shape, mode).total;
@@ -164,7 +183,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
                        fwmem_stream stream, int phases) {
   fwmem_status st = check_shape(shape, true);
   if (st != FWMEM_OK) return st;
-  st = check_mode(mode);
+  st = check_scan_mode(mode);
   if (st != FWMEM_OK) return st;
   if (!fwmem::scan_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
 
@@ -249,8 +268,37 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
     return FWMEM_EUNSUPPORTED;
 
   const WsLayout wl = ws_layout(shape, mode);
+  // Normalised linear attention: prep writes the chunk terms of z, and after the
+  // propagate kernels z is chained over the chunks of each head and divides the outputs.
+  // Records of virtual heads (segments) are those of the real heads' chunks in order, so
+  // the chain always runs over the real heads.
+  fwmem::ZParams zp;
+  std::memset(&zp, 0, sizeof(zp));
+  if (mode->flags & FWMEM_ZNORM) {
+    char* ws = static_cast<char*>(workspace);
+    p.zrec = reinterpret_cast<float*>(ws + wl.zr);
+    zp.zrec = p.zrec;
+    zp.zc = reinterpret_cast<float*>(ws + wl.zc);
+    zp.z_in = si.x;
+    zp.z_out = so.x;
+    zp.has_out = so.h;
+    zp.q = q;
+    zp.out = static_cast<float*>(out);
+    zp.BH = p.BH;
+    zp.T = p.T;
+    zp.nchunks = p.nchunks;
+    zp.dk = p.dk;
+    zp.dv = p.dv;
+    zp.bf16 = p.bf16;
+    zp.flags = p.flags;
+    zp.eps = p.eps;
+  }
+  auto znorm = [&](hipError_t e) {
+    if (e == hipSuccess && (mode->flags & FWMEM_ZNORM) && (phases & 2)) e = fwmem::launch_znorm(zp, hs);
+    return e;
+  };
   if (wl.P == 1) {
-    const hipError_t e = fwmem::launch_scan(p, hs, phases);
+    const hipError_t e = znorm(fwmem::launch_scan(p, hs, phases));
     return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
   }
 
@@ -324,6 +372,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
     if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
     if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
   }
+  e = znorm(e);
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
 }
 

@@ -17,6 +17,7 @@ enum : uint32_t {
   kFlagBetaSig = 1u << 5,
   kFlagBetaSig2 = 1u << 6,
   kFlagLamAct = 1u << 7,
+  kFlagZnorm = 1u << 8,
 };
 
 constexpr int kChunk = 64;  // scan chunk length (tokens)
@@ -82,6 +83,7 @@ struct ScanParams {
   float* xprev_out;      // [BH][dk] (with S_out)
   int32_t* has_out;      // [BH]     (with S_out)
   char* ws;              // workspace records
+  float* zrec;           // normalised linear attention: per (head, chunk) ZRec, or null
   int BH, T, dk, dv, nchunks;
   int rule;              // kRuleDelta, kRuleAdditive or kRuleInner
   int bf16;              // 1: bf16 inputs, 0: fp32
@@ -174,6 +176,30 @@ struct SegParams {
 // grid would leave most of the GPU idle and T splits into equal chunk-aligned segments.
 int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, uint32_t flags);
 hipError_t launch_seg_init(const SegParams& s, hipStream_t st);
+
+// ---- normalised linear attention (FWMEM_ZNORM; additive rule, scalar decay)
+//
+// Per (head, chunk) the prep kernels write a ZRec of floats:
+//   [0, 64)        den_in[t] = sum_{s<=t} M_ts beta_s    (the chunk's own writes)
+//   [64, 128)      gq[t] = Gamma_t (times q_t's rescale factor with QK normalisation)
+//   128            Gamma_C
+//   [132, 132+dk)  w = sum_s (Gamma_C / Gamma_s) beta_s x_s  (the chunk's write to z)
+// The normaliser at token t of chunk c is den_in[t] + gq[t] (q_t . z_c), z_c the
+// normaliser at chunk entry: z_{c+1} = Gamma_C z_c + w.
+__host__ __device__ inline size_t zrec_floats(int dk) { return (size_t)132 + (size_t)dk; }
+struct ZParams {
+  const float* zrec;       // [BH][nchunks] ZRec
+  float* zc;               // [BH][nchunks][dk] z at chunk entry
+  const float* z_in;       // the state's carried slot, or null (z = 0)
+  float* z_out;            // the state's carried slot, or null
+  int32_t* has_out;
+  const void* q;           // raw q [BH][T][dk]
+  float* out;              // [BH][T][dv] float32, divided in place
+  int BH, T, nchunks, dk, dv, bf16;
+  uint32_t flags;
+  float eps;
+};
+hipError_t launch_znorm(const ZParams& z, hipStream_t st);
 hipError_t launch_seg_combine(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st);
 

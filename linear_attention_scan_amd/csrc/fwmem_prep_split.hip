@@ -321,6 +321,32 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
   }
   __syncthreads();
 
+  // ---- normalised linear attention (additive rule): the chunk's terms of the normaliser
+  // (ZRec): den_in[t] = sum_{s<=t} M_ts b_s, the factor Gamma_t mq_t of q_t . z at chunk
+  // entry, Gamma_C, and the chunk's write sum_s fU_s b_s x_s. Without a solve X keeps its
+  // region.
+  if (!R::solve && p.zrec != nullptr) {
+    float* zr = p.zrec + ((size_t)bh * p.nchunks + c) * zrec_floats(DK);
+    const float gC = s_g[CH - 1], sC = s_sg[CH - 1];
+    if (tid < CH) {
+      float d = 0.f;
+      for (int s = 0; s <= tid; ++s) d += Mf[mat_idx(tid, s)] * s_eta[s];
+      zr[tid] = d;
+      zr[CH + tid] = s_sg[tid] * __expf(s_g[tid]) * (QKN ? s_m[tid] : 1.f);
+      if (tid == 0) zr[2 * CH] = sC * __expf(gC);
+    } else if (tid < CH + DK) {
+      const int i = tid - CH;
+      float w = 0.f;
+      for (int s = 0; s < CH; ++s) {
+        const u32x4 gr = Xs[s * NGR + ((i >> 3) ^ xswz<DK>(s))];
+        const uint32_t word = gr[(i & 7) >> 1];
+        const float x = bf16_bits_to_f32((i & 1) ? word >> 16 : word & 0xffffu);
+        w += s_eta[s] * sC * s_sg[s] * __expf(gC - s_g[s]) * (QKN ? s_n[s] : 1.f) * x;
+      }
+      zr[2 * CH + 4 + i] = w;
+    }
+  }
+
   // ---- 5. M as split A fragments into the record (its region then holds T)
   split_to_record<RC::kM>(Mf, rec, tid);
 

@@ -535,6 +535,27 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       reinterpret_cast<float*>(rec + RC::kX0)[tid] = x0 != nullptr ? x0[tid] : 0.f;
     }
   }
+
+  // Normalised linear attention (additive rule, scalar decay): the chunk's terms of the
+  // normaliser (ZRec): den_in[t] = sum_{s<=t} M_ts b_s, the factor Gamma_t mq_t of
+  // q_t . z at chunk entry, Gamma_C, and the chunk's write sum_s fU_s b_s x_s.
+  if (!PC && p.zrec != nullptr) {
+    float* zr = p.zrec + ((size_t)bh * p.nchunks + c) * zrec_floats(DK);
+    const float gC = s_g[CH - 1], sC = s_sg[CH - 1];
+    if (tid < CH) {
+      float d = 0.f;
+      for (int s = 0; s <= tid; ++s) d += Mf[tid * LDF + s] * s_eta[s];
+      zr[tid] = d;
+      zr[CH + tid] = s_sg[tid] * __expf(s_g[tid]) * s_mq[tid];
+      if (tid == 0) zr[2 * CH] = sC * __expf(gC);
+    } else if (tid < CH + DK) {
+      const int i = tid - CH, ip = Pol::kpos(i);
+      float w = 0.f;
+      for (int s = 0; s < CH; ++s)
+        w += s_eta[s] * sC * s_sg[s] * __expf(gC - s_g[s]) * s_nx[s] * (float)Xs[s * LDX + ip];
+      zr[2 * CH + 4 + i] = w / sX;  // X is held scaled by sX
+    }
+  }
 }
 
 // ================================================================ propagate kernel
@@ -1026,7 +1047,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
         for (int ii = 0; ii < 4; ++ii)
           p.S_out[((size_t)bh * DK + 16 * rt + 4 * g + ii) * dv + c0 + n] = s[rt][ii];
     }
-    if (grp == 0) {
+    if (grp == 0 && (p.flags & kFlagZnorm) == 0) {  // with the normaliser the slot holds z
       for (int i = tid; i < DK; i += NT) {
         float x = In<InT>::load1(kbase + (uint32_t)((p.T - 1) * DK + i));
         if (ELU) x = phi_elu1(x);

@@ -693,7 +693,7 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
       loader_step<DK, SOLVE, SHIFT>(B0, B1, R, p, c, lane, lo, src, rec0);
       if (c + 1 < p.nchunks) loader_step<DK, SOLVE, SHIFT>(B1, B0, R, p, c + 1, lane, lo, src, rec0);
     }
-    if (p.S_out != nullptr && grp == 0) {
+    if (p.S_out != nullptr && grp == 0 && (p.flags & kFlagZnorm) == 0) {  // else the slot holds z
       for (int i = lane; i < DK; i += 64)
         p.xprev_out[(size_t)bh * DK + i] = bf16_bits_to_f32(kb[(uint32_t)((p.T - 1) * DK + i)]);
       if (lane == 0) p.has_out[bh] = 1;

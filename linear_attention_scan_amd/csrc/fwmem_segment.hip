@@ -95,7 +95,8 @@ __global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
     for (int r = 0; r < RP; ++r) s.S_out[((size_t)h * dk + i0 + 16 * r) * dv + j0 + j] = v[r];
     if (j0 == 0) {
       const size_t last = (size_t)h * s.P + s.P - 1;
-      for (int i = threadIdx.x; i < dk; i += NTH) s.xprev_out[(size_t)h * dk + i] = s.B1_x[last * dk + i];
+      if ((s.flags & kFlagZnorm) == 0)  // with the normaliser the slot holds z
+        for (int i = threadIdx.x; i < dk; i += NTH) s.xprev_out[(size_t)h * dk + i] = s.B1_x[last * dk + i];
       if (threadIdx.x == 0) s.has_out[h] = 1;
     }
   }

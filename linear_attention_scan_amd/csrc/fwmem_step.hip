@@ -11,6 +11,8 @@
 // state is written back from registers: exactly one read and one write of S.
 // Additive rule ("attention is also an FFN", section 3.2):
 //   S' = diag(gamma) S + b phi(k) v^T,  o = S^T (gamma o q~) + b (phi(k) . q~) v.
+// With the normaliser (FWMEM_ZNORM, the same page, section 4.2) the state's x_prev slot
+// holds z: z' = gamma o z + b phi(k), and o is divided by z' . q~ + eps.
 // Inner-product rule (the reading notes above, section 4.3): x, eta and a as for the
 // delta rule, with the value itself written: S' = diag(a) S + eta x v^T,
 //   o = S^T (a o q~) + eta (x . q~) v.
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   constexpr int NWV = NT / 64;
   static_assert(DK % RG == 0 && RGW >= 1, "shape");
 
-  __shared__ float s_x[DK], s_q[DK], s_a[DK], s_k[DK];
+  __shared__ float s_x[DK], s_q[DK], s_a[DK], s_k[DK], s_z[DK];
   __shared__ float s_red[2][NWV][DV];
   __shared__ float s_sc[6];
 
@@ -48,6 +50,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cq = tid % TPRd, rg = tid / TPRd;
   const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const bool znorm = !R::solve && !R::shift && (p.flags & kFlagZnorm) != 0;
   const InT* qp = static_cast<const InT*>(p.q) + (size_t)bh * DK;
   const InT* kp = static_cast<const InT*>(p.k) + (size_t)bh * DK;
   const InT* vp = static_cast<const InT*>(p.v) + (size_t)bh * DV;
@@ -65,8 +68,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   }
 
   // Per-head vectors into LDS. The carried key for the next token is phi(k), stored raw
-  // (before any normalisation); each thread reads its own x_prev entries before it writes
-  // them, so the state may be updated in place.
+  // (before any normalisation), or with the normaliser z' (below); each thread reads its
+  // own x_prev entries before it writes them, so the state may be updated in place.
   const float qk_len = qk_length(p.flags, DK);
   for (int i = tid; i < DK; i += NT) {
     float q = In<InT>::load1(qp + i);
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     s_q[i] = q;
     s_k[i] = k;
     s_x[i] = (R::shift && has && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
-    p.xprev_out[(size_t)bh * DK + i] = k;
+    if (znorm) s_z[i] = p.xprev_in != nullptr ? p.xprev_in[(size_t)bh * DK + i] : 0.f;
+    else p.xprev_out[(size_t)bh * DK + i] = k;
   }
   __syncthreads();
 
@@ -134,8 +138,19 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
       a = R::nlms ? 1.f - eta * lam : lam;
     }
     s_a[i] = a;
+    if (znorm) {
+      const float zn = a * s_z[i] + eta * s_k[i];
+      s_z[i] = zn;
+      p.xprev_out[(size_t)bh * DK + i] = zn;
+    }
   }
   __syncthreads();
+  if (znorm && wave == NWV - 1) {
+    float d = 0.f;
+    for (int i = lane; i < DK; i += 64) d += s_z[i] * s_q[i];
+    d = wave_sum(d);
+    if (lane == 0) s_sc[5] = 1.f / (d + p.eps);
+  }
 
   // Column partial sums over this thread's rows: p = S^T x, w = S^T (a o q).
   f4 pp = {0.f, 0.f, 0.f, 0.f}, ww = pp;
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   // r (delta) or the written value b*v (additive), and the output.
   const f4 vv = {v4[0], v4[1], v4[2], v4[3]};
   const f4 r = R::solve ? (vv - P) * eta : vv * eta;  // the written value u
-  const f4 o = W + r * dq;
+  const f4 o = znorm ? (W + r * dq) * s_sc[5] : W + r * dq;
 
   // New state from registers.
   float* Sout = p.S_out + (size_t)bh * DK * DV;

@@ -25,6 +25,7 @@ QK_RMSNORM = 1 << 4
 BETA_SIGMOID = 1 << 5
 BETA_SIGMOID2 = 1 << 6
 LAMBDA_PREACT = 1 << 7
+ZNORM = 1 << 8
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",

@@ -107,6 +107,8 @@ class ScanInputs:
     beta_act: Optional[str] = None         # how beta follows from beta_pre: 'sigmoid', 'sigmoid2'
     lam_act: bool = False                  # lam = softplus(lam_pre) (or sigmoid for gamma)
     gates_pre: bool = False                # hand the library the pre-activations (its gate flags)
+    znorm: bool = False                    # normalised linear attention (additive rule): the
+                                           # read is divided by z . q, z the state's x_prev slot
 
     @property
     def tokens(self) -> int:
@@ -126,7 +128,7 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
               normalise_qk=True, beta_kind="sigmoid", lam_kind="const",
               lam_const=0.01, lam_mu=-4.0, per_channel=False, gamma_mu=3.0,
               gamma_sd=0.5, eps=1e-6, s0_std=None, seed=0, name="custom",
-              qk_norm=None) -> ScanInputs:
+              qk_norm=None, qk_positive=False, znorm=False) -> ScanInputs:
     """Draw one scan problem.
 
     beta_kind: 'sigmoid' (sigmoid(N(0,1))), 'two_sigmoid' (2*sigmoid(N(0,1))),
@@ -135,11 +137,17 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
     lam_kind:  'const' (lam_const everywhere), 'softplus' (softplus(N(lam_mu,1))),
                'gamma' (sigmoid(N(gamma_mu, gamma_sd)), the additive retention),
                'none' (lam = None).
+    qk_positive: q, k drawn as |N(0,1)| (positive features for the identity map, so that
+               the normaliser of znorm stays positive).
+    znorm:     normalised linear attention; with s0_std the initial normaliser z0 (the
+               x_prev slot) is drawn as |N(0,1)| times the initial state's scale.
     """
     rng = np.random.default_rng(seed)
     q = _normal(rng, (B, H, T, dk))
     k = _normal(rng, (B, H, T, dk))
     v = _normal(rng, (B, H, T, dv))
+    if qk_positive:
+        q, k = np.abs(q), np.abs(k)
     if normalise_qk:
         q = _l2_normalise(q)
         k = _l2_normalise(k)
@@ -175,13 +183,16 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
     else:
         raise ValueError(lam_kind)
 
-    S0 = None
+    S0 = xprev0 = None
     if s0_std is not None:
         S0 = _normal(rng, (B, H, dk, dv), std=s0_std)
+        if znorm:
+            xprev0 = np.abs(_normal(rng, (B, H, dk), std=s0_std))
     return ScanInputs(name=name, B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, rule=rule,
                       phi=phi, per_channel=per_channel, eps=eps, q=q, k=k, v=v,
-                      beta=beta, lam=lam, S0=S0, qk_norm=qk_norm, beta_pre=beta_pre,
-                      lam_pre=lam_pre, beta_act=beta_act, lam_act=lam_act)
+                      beta=beta, lam=lam, S0=S0, xprev0=xprev0, qk_norm=qk_norm,
+                      beta_pre=beta_pre, lam_pre=lam_pre, beta_act=beta_act, lam_act=lam_act,
+                      znorm=znorm)
 
 
 def delta_f32_small(seed=0, T=256):
@@ -226,6 +237,14 @@ def inner_bf16(seed=0, B=4, H=8, T=4096, d=128):
                      name="inner_bf16")
 
 
+def additive_znorm_bf16(seed=0, B=2, H=16, T=16384, d=128):
+    """additive_bf16 with the normaliser: linear attention with elu+1 features and a
+    retention gate, each read divided by z . phi(q)."""
+    w = additive_bf16(seed=seed, B=B, H=H, T=T, d=d)
+    w.znorm, w.name = True, "additive_znorm_bf16"
+    return w
+
+
 def inner_f32_small(seed=0, T=256):
     return make_scan(B=1, H=1, T=T, dk=64, dv=64, dtype="f32", rule=RULE_INNER,
                      beta_kind="sigmoid", lam_kind="const", lam_const=0.01, seed=seed,
@@ -268,4 +287,5 @@ SCAN_WORKLOADS = {
     "inner_bf16": inner_bf16,
     "delta_bf16_h16_qknorm": delta_bf16_h16_qknorm,
     "inner_f32_small": inner_f32_small,
+    "additive_znorm_bf16": additive_znorm_bf16,
 }

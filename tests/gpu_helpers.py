@@ -46,6 +46,8 @@ def flags_of(w: wl.ScanInputs, extra=0):
             f |= {"sigmoid": F.BETA_SIGMOID, "sigmoid2": F.BETA_SIGMOID2}[w.beta_act]
         if w.lam_act:
             f |= F.LAMBDA_PREACT
+    if w.znorm:
+        f |= F.ZNORM
     return f
 
 
@@ -91,6 +93,8 @@ def gpu_scan(w: wl.ScanInputs, *, t_slice=None, S_in=None, S_out=None, extra_fla
 def oracle_scan(w: wl.ScanInputs, t_slice=None, S0=None, xprev0=None, has0=None):
     sl = slice(None) if t_slice is None else t_slice
     S0 = w.S0 if S0 is None else S0
+    xprev0 = w.xprev0 if xprev0 is None else xprev0
+    has0 = w.has0 if has0 is None else has0
     gb, gl = gates_of(w)
     return orc.scan(w.q[:, :, sl], w.k[:, :, sl], w.v[:, :, sl],
                     None if gb is None else gb[:, :, sl],
@@ -98,7 +102,7 @@ def oracle_scan(w: wl.ScanInputs, t_slice=None, S0=None, xprev0=None, has0=None)
                     rule=w.rule, phi_kind=w.phi, eps=w.eps, per_channel=w.per_channel,
                     S0=S0, xprev0=xprev0, has0=has0, qk_norm=w.qk_norm,
                     beta_act=w.beta_act if (w.gates_pre and gb is w.beta_pre) else None,
-                    lam_act=bool(w.gates_pre and w.lam_act))
+                    lam_act=bool(w.gates_pre and w.lam_act), znorm=w.znorm)
 
 
 def state_np(st):
@@ -119,7 +123,12 @@ def check_scan(w: wl.ScanInputs, tol=None, label=""):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
     assert eo <= tol, f"err(o)={eo}"
     assert eS <= tol, f"err(S)={eS}"
-    if w.T > 0:
+    if w.znorm:  # the slot holds the normaliser z
+        ex = orc.relerr(x, x_ref)
+        say(f"    err(z)={ex:.3e}")
+        assert ex <= tol, f"err(z)={ex}"
+        assert w.T == 0 or np.all(h == 1)
+    elif w.T > 0:
         if w.phi == wl.PHI_IDENTITY:
             np.testing.assert_array_equal(x, x_ref.astype(np.float32).astype(np.float64))
         else:  # elu+1 is evaluated in fp32 on the GPU

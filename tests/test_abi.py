@@ -53,6 +53,12 @@ def test_state_and_workspace_sizes():
     assert F.workspace_bytes(F.shape(B, H, 0, dk, dv, F.BF16), F.mode()) == 0
     ws32 = F.workspace_bytes(F.shape(B, H, 130, dk, dv, F.F32), F.mode())
     assert ws32 > ws                                  # fp32 operands take more room
+    # the normaliser adds its chunk terms (132 + dk floats) and its value at each chunk entry
+    wa = F.workspace_bytes(F.shape(B, H, 130, dk, dv, F.BF16), F.mode(rule=F.RULE_ADDITIVE))
+    wz = F.workspace_bytes(F.shape(B, H, 130, dk, dv, F.BF16),
+                           F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM))
+    al = lambda n: (n + 255) // 256 * 256
+    assert wz == al(wa) + al(4 * B * H * 3 * (132 + dk)) + al(4 * B * H * 3 * dk)
 
 
 FAKE = 0x10000  # never dereferenced: every case below fails a host check first
@@ -95,6 +101,11 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(md=F.mode(flags=F.QK_L2NORM | F.QK_RMSNORM)), F.EINVAL),
     (dict(md=F.mode(flags=F.QK_RMSNORM | F.PHI_ELU1)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.BETA_SIGMOID | F.BETA_SIGMOID2)), F.EINVAL),
+    # the normaliser takes the additive rule, and scans a scalar decay and float32 outputs
+    (dict(md=F.mode(flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_INNER, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.OUT_BF16)), F.EUNSUPPORTED),
     (dict(q=FAKE + 2), F.EALIGN),
     (dict(out=FAKE * 64 + 8), F.EALIGN),
     (dict(beta=FAKE + 2), F.EALIGN),
@@ -133,6 +144,7 @@ def test_empty_batch_is_a_no_op():
     (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),
     (dict(md=F.mode(rule=-1)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 12)), F.EINVAL),
+    (dict(md=F.mode(rule=F.RULE_DELTA, flags=F.ZNORM)), F.EUNSUPPORTED),
     (dict(q=FAKE + 1), F.EALIGN),
     (dict(out=FAKE * 64 + 4), F.EALIGN),
     (dict(S_in=FAKE * 1024 + 64), F.EOVERLAP),
