@@ -194,6 +194,8 @@ def main():
     flags = (F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
     if w.qk_norm is not None:
         flags |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
+    if w.znorm:
+        flags |= F.ZNORM
     shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
     md = F.mode(w.rule, flags, w.eps, 0)
     out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.float32, device=dev)
@@ -283,7 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "rule": ("delta", "additive", "inner")[w.rule], "inputs": w.dtype,
-                   "chunk": 64, "seed": 0, "qk_norm": w.qk_norm},
+                   "chunk": 64, "seed": 0, "qk_norm": w.qk_norm, "znorm": w.znorm},
         "roofline": roofline,
         "kernels": {names[n]: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),
                                "mfma_TFLOPs": round(kk["mfma_TFLOPs"], 2),

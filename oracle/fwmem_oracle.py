@@ -14,7 +14,8 @@ vectorised only over independent heads (b, h). Sources (page titles as printed):
          section 4.2 (Falcon-1 rule, beta in (0,2), per-step descent lemma,
          NLMS limit), section 4.3 (the inner-product family, Falcon-1A: the same
          shifted pair, step size and decay, with the target written in place of the
-         residual).
+         residual), section 4.5 (RMSNorm of q and k; the ridge coupled to an energy
+         statistic so that the decay does not depend on the input scale).
   [AFFN] hncyxsy.com blog post "attention is also an FFN" (news/211194):
          section 2.1 (S_i = sum_{j<=i} phi(k_j) v_j^T, y_i = phi(q_i)^T S_i),
          section 3.2 (decayed write S_t = lambda S_{t-1} + phi(k_t) v_t^T),
@@ -35,6 +36,9 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
       ridge lambda = softplus(z), the additive retention gamma = sigmoid(z).
   D18 normalised linear attention (znorm): o_t = S_t^T phi(q_t) / (z_t . phi(q_t) + eps)
       with z decayed like S; z is carried in the carried-key slot of the state.
+  D19 scale-coupled ridge (lam_scaled): lambda_t = lambda_bar_t * ||x_t||^2, the energy
+      of the key written at step t (after any normalisation), for every channel of a
+      per-channel lambda.
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -87,7 +91,7 @@ def unit_rows(x: np.ndarray, length: float = 1.0) -> np.ndarray:
 
 def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
          S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False,
-         znorm=False):
+         znorm=False, lam_scaled=False):
     """Run the recurrence over a whole sequence.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] or None; lam: [B,H,T] (or
@@ -108,6 +112,10 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     ([AFFN] section 4.2, with the decay applied to z as well, as that section suggests).
     z takes the place of the carried key in the state (xprev0 / the returned xprev),
     since the additive rule never reads that key (reading D18).
+    lam_scaled: delta and inner rules only. lam (after any activation) is a
+    dimensionless base ridge, multiplied by the energy ||x_t||^2 of the key written at
+    step t ([FWA] section 4.5; reading D19), so that eta_t lambda_t, the decay, is the
+    same for any rescaling of the keys.
 
     Returns (o [B,H,T,dv], S [B,H,dk,dv], xprev [B,H,dk], has [B,H]) in float64.
     """
@@ -145,6 +153,8 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
 
     if znorm and rule != RULE_ADDITIVE:
         raise ValueError("znorm takes the additive rule")
+    if lam_scaled and rule == RULE_ADDITIVE:
+        raise ValueError("lam_scaled takes the delta or inner rule")
     z = xprev.copy() if znorm else None
 
     for t in range(T):
@@ -165,6 +175,10 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
             else:
                 lam_t = Lm[:, t]
                 lam_hat = lam_t
+            if lam_scaled:
+                energy = np.sum(x * x, axis=1)
+                lam_t = lam_t * (energy[:, None] if per_channel else energy)
+                lam_hat = lam_hat * energy
             # [FWA] 3.2 / 4.2: eta_t = beta_t / (||x_t||^2 + lambda_t + eps).
             den = np.sum(x * x, axis=1) + lam_hat + eps
             eta = np.where(has, Bt[:, t] / np.where(has, den, 1.0), 0.0)
@@ -206,7 +220,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
 
 def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel=False,
          S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False,
-         znorm=False):
+         znorm=False, lam_scaled=False):
     """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
     (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
     q = np.asarray(q)[:, :, None]
@@ -218,7 +232,7 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         lam = lam[:, :, None, :] if per_channel else lam[:, :, None]
     o, S, xp, h = scan(q, k, v, beta, lam, rule=rule, phi_kind=phi_kind, eps=eps,
                        per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm,
-                       beta_act=beta_act, lam_act=lam_act, znorm=znorm)
+                       beta_act=beta_act, lam_act=lam_act, znorm=znorm, lam_scaled=lam_scaled)
     return o[:, :, 0], S, xp, h
 
 

@@ -640,6 +640,47 @@ def pin_relerr_metric(orc):
     assert abs(orc.relerr(x, ref) - 0.5 / (5.0 / np.sqrt(2.0))) < 1e-15
 
 
+def pin_p22_scale_coupled_ridge(orc):
+    """[FWA] 4.5: with the ridge coupled to the energy of the written key, the decay
+    does not depend on the input scale. With eps = 0, multiplying every q and k by s > 0
+    (and S0 by 1/s) leaves every read unchanged and divides the state by s: eta scales by
+    1/s^2, eta x by 1/s, eta lambda not at all. Checked for the delta and inner rules, with
+    scalar and per-channel base ridges; the plain ridge lacks the property (checked too).
+    Hand case, one write: x = (3, 4), base ridge 0.2, beta = 1, eps = 0, S0 = (1, 2)^T,
+    v = 10. Then lambda = 0.2 * 25 = 5, eta = 1/30, decay 5/6, and the residual is
+    10 - 11 = -1, so the delta rule gives S = (11/15, 23/15); the inner rule writes v
+    itself and gives S = (11/6, 3)."""
+    rng = np.random.default_rng(40)
+    T, dk, dv, s = 14, 5, 3, 7.3
+    for rule in (DELTA, INNER):
+        for per_channel in (False, True):
+            q, k, v = (rng.standard_normal((T, d)) for d in (dk, dk, dv))
+            beta = rng.uniform(0.2, 1.8, T)
+            lam = rng.uniform(0.05, 0.5, (T, dk) if per_channel else T)
+            S0 = rng.standard_normal((1, 1, dk, dv))
+
+            def run(c, scaled):
+                return orc.scan(_bh(c * q), _bh(c * k), _bh(v), _bh(beta), _bh(lam), rule=rule,
+                                per_channel=per_channel, eps=0.0, S0=S0 / c, lam_scaled=scaled)
+
+            o, S, _, _ = run(1.0, True)
+            o2, S2, _, _ = run(s, True)
+            np.testing.assert_allclose(o2, o, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(S2 * s, S, rtol=1e-10, atol=1e-12)
+            o3 = run(1.0, False)[0]
+            o4 = run(s, False)[0]
+            assert np.max(np.abs(o4 - o3)) > 1e-3
+    q = np.array([[0.0, 1.0], [1.0, 0.0]])
+    k = np.array([[3.0, 4.0], [1.0, 1.0]])
+    v = np.array([[5.0], [10.0]])
+    S0 = np.array([[1.0], [2.0]])[None, None]
+    for rule, S_hand in ((DELTA, [11 / 15, 23 / 15]), (INNER, [11 / 6, 3.0])):
+        o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.ones(2)), _bh(np.array([0.7, 0.2])),
+                              rule=rule, eps=0.0, S0=S0, lam_scaled=True)
+        np.testing.assert_allclose(S[0, 0, :, 0], S_hand, rtol=1e-14)
+        np.testing.assert_allclose(o[0, 0, :, 0], [2.0, S_hand[0]], rtol=1e-14)
+
+
 ALL_PINS = [
     pin_p1_outer_product_store,
     pin_p2_quadratic_form,
@@ -665,5 +706,6 @@ ALL_PINS = [
     pin_p19_qk_norm_scale_invariance,
     pin_p20_gate_preactivations,
     pin_p21_normalised_linear_attention,
+    pin_p22_scale_coupled_ridge,
     pin_relerr_metric,
 ]

@@ -48,6 +48,9 @@ MUTANTS = {
     "retention_uses_softplus": ("Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)",
                                 "Lm = softplus(Lm)"),
     "beta_range_one": ('Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)', "Bt = sigmoid(Bt)"),
+    "ridge_not_scaled": ("lam_t = lam_t * (energy[:, None] if per_channel else energy)", "lam_t = lam_t"),
+    "ridge_hat_not_scaled": ("lam_hat = lam_hat * energy", "lam_hat = lam_hat"),
+    "ridge_scaled_by_norm": ("energy = np.sum(x * x, axis=1)", "energy = np.sqrt(np.sum(x * x, axis=1))"),
     "znorm_no_decay": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = z + b[:, None] * kt"),
     "znorm_no_beta": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = gam[:, :, 0] * z + kt"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
