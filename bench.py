@@ -196,6 +196,8 @@ def main():
         flags |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
     if w.znorm:
         flags |= F.ZNORM
+    if w.lam_scaled:
+        flags |= F.LAMBDA_SCALED
     shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
     md = F.mode(w.rule, flags, w.eps, 0)
     out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.float32, device=dev)

@@ -103,7 +103,7 @@ enum {
   FWMEM_LAMBDA_PREACT = 1u << 7,      /* lambda holds pre-activations z: the ridge
                                          softplus(z) (DELTA, INNER) or the retention
                                          sigmoid(z) (ADDITIVE), applied per element */
-  FWMEM_ZNORM = 1u << 8               /* normalised linear attention ("attention is also
+  FWMEM_ZNORM = 1u << 8,              /* normalised linear attention ("attention is also
                                          an FFN", section 4.2; ADDITIVE only): the
                                          normaliser z_t = gamma_t z_{t-1} + b_t phi(k~_t)
                                          (decayed as S is) divides the read,
@@ -115,6 +115,18 @@ enum {
                                          fwmem_step takes every ADDITIVE mode. The
                                          caller keeps z . q~ away from -eps, e.g. with
                                          positive features (elu+1). */
+  FWMEM_LAMBDA_SCALED = 1u << 9       /* scale-coupled ridge ("Fast Weight Attention for
+                                         Continual Learning" reading notes, section 4.5;
+                                         DELTA and INNER only): lambda (after any
+                                         activation) is a dimensionless base ridge and the
+                                         ridge is lambda_t * ||x_t||^2, the energy of the
+                                         key written at step t (after QK normalisation),
+                                         so that the decay eta_t lambda_t is the same for
+                                         any rescaling of the keys. Per channel, every
+                                         channel is scaled by the same energy and lambda-hat
+                                         is the largest scaled value. Scans take it with a
+                                         scalar lambda (else FWMEM_EUNSUPPORTED);
+                                         fwmem_step takes both. */
 };
 
 typedef struct {

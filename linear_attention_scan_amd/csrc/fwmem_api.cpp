@@ -15,7 +15,8 @@ using fwmem::kChunk;
 
 constexpr uint32_t kKnownFlags =
     FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16 | FWMEM_QK_L2NORM | FWMEM_QK_RMSNORM |
-    FWMEM_BETA_SIGMOID | FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_ZNORM;
+    FWMEM_BETA_SIGMOID | FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_ZNORM |
+    FWMEM_LAMBDA_SCALED;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -63,17 +64,21 @@ fwmem_status check_mode(const fwmem_mode* m) {
     return FWMEM_EUNSUPPORTED;
   // the normaliser accumulates the additive rule's writes
   if ((m->flags & FWMEM_ZNORM) && m->rule != FWMEM_RULE_ADDITIVE) return FWMEM_EUNSUPPORTED;
+  // the additive rule's lambda is a retention, not a ridge
+  if ((m->flags & FWMEM_LAMBDA_SCALED) && m->rule == FWMEM_RULE_ADDITIVE) return FWMEM_EUNSUPPORTED;
   if (!std::isfinite(m->eps) || m->eps < 0.f) return FWMEM_EINVAL;
   if (m->chunk != 0 && m->chunk != kChunk) return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;
 }
 
 // Scans divide their float32 outputs in place and keep one normaliser per key channel
-// only for a scalar decay.
+// only for a scalar decay; they couple the ridge to the key energy for a scalar lambda.
 fwmem_status check_scan_mode(const fwmem_mode* m) {
   const fwmem_status st = check_mode(m);
   if (st != FWMEM_OK) return st;
   if ((m->flags & FWMEM_ZNORM) && (m->flags & (FWMEM_LAMBDA_PER_CHANNEL | FWMEM_OUT_BF16)))
+    return FWMEM_EUNSUPPORTED;
+  if ((m->flags & FWMEM_LAMBDA_SCALED) && (m->flags & FWMEM_LAMBDA_PER_CHANNEL))
     return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;
 }

@@ -18,6 +18,7 @@ enum : uint32_t {
   kFlagBetaSig2 = 1u << 6,
   kFlagLamAct = 1u << 7,
   kFlagZnorm = 1u << 8,
+  kFlagLamScaled = 1u << 9,
 };
 
 constexpr int kChunk = 64;  // scan chunk length (tokens)

@@ -227,8 +227,10 @@ __global__ __launch_bounds__(NTP) void prep_split_kernel(ScanParams p) {
     float eta = 0.f, a = 1.f;
     if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
-      if (hasx) eta = g_beta / (xx + g_lam + p.eps);
-      a = 1.f - eta * g_lam;
+      // scale-coupled ridge: the base ridge times the written key's energy
+      const float lam = (p.flags & kFlagLamScaled) ? g_lam * xx : g_lam;
+      if (hasx) eta = g_beta / (xx + lam + p.eps);
+      a = 1.f - eta * lam;
     } else {
       if (active) eta = g_beta;
       if (active && p.lam != nullptr) a = g_lam;

@@ -252,7 +252,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     float eta = 0.f, a = 1.f;
     if (R::nlms) {
       const bool hasx = active && (tau >= 1 || has_in);
-      const float lam_t = PC ? s_lam[t] : g_lam;
+      // scale-coupled ridge (scalar lambda): the base ridge times the written key's energy
+      const float lam_t = PC ? s_lam[t] : ((p.flags & kFlagLamScaled) ? g_lam * xx : g_lam);
       if (hasx) eta = g_beta / (xx + lam_t + p.eps);
       a = 1.f - eta * lam_t;
     } else {

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
   __shared__ float s_x[DK], s_q[DK], s_a[DK], s_k[DK], s_z[DK];
   __shared__ float s_red[2][NWV][DV];
-  __shared__ float s_sc[6];
+  __shared__ float s_sc[8];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -109,8 +109,11 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     if (lane == 0) {
       float eta = 0.f, a = 1.f;
       if (R::nlms) {
-        const float lam = PC ? (p.lam != nullptr ? lm : 0.f)
-                             : (p.lam != nullptr ? act_lam(p.lam[bh], p.flags, true) : 0.f);
+        // with the scale-coupled ridge, lambda is a base ridge times the key energy nx
+        const float es = (p.flags & kFlagLamScaled) ? nx : 1.f;
+        const float lam = es * (PC ? (p.lam != nullptr ? lm : 0.f)
+                                   : (p.lam != nullptr ? act_lam(p.lam[bh], p.flags, true) : 0.f));
+        s_sc[6] = es;
         if (has) eta = act_beta(p.beta[bh], p.flags) / (nx + lam + p.eps);
         a = 1.f - eta * lam;
       } else {
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     float a = a_sc;
     if (PC) {
       const float lam = p.lam != nullptr ? act_lam(p.lam[(size_t)bh * DK + i], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
-      a = R::nlms ? 1.f - eta * lam : lam;
+      a = R::nlms ? 1.f - eta * s_sc[6] * lam : lam;
     }
     s_a[i] = a;
     if (znorm) {

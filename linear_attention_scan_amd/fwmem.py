@@ -26,6 +26,7 @@ BETA_SIGMOID = 1 << 5
 BETA_SIGMOID2 = 1 << 6
 LAMBDA_PREACT = 1 << 7
 ZNORM = 1 << 8
+LAMBDA_SCALED = 1 << 9
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",

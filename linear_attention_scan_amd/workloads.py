@@ -109,6 +109,7 @@ class ScanInputs:
     gates_pre: bool = False                # hand the library the pre-activations (its gate flags)
     znorm: bool = False                    # normalised linear attention (additive rule): the
                                            # read is divided by z . q, z the state's x_prev slot
+    lam_scaled: bool = False               # lam is a base ridge, times the written key's energy
 
     @property
     def tokens(self) -> int:
@@ -128,7 +129,7 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
               normalise_qk=True, beta_kind="sigmoid", lam_kind="const",
               lam_const=0.01, lam_mu=-4.0, per_channel=False, gamma_mu=3.0,
               gamma_sd=0.5, eps=1e-6, s0_std=None, seed=0, name="custom",
-              qk_norm=None, qk_positive=False, znorm=False) -> ScanInputs:
+              qk_norm=None, qk_positive=False, znorm=False, lam_scaled=False) -> ScanInputs:
     """Draw one scan problem.
 
     beta_kind: 'sigmoid' (sigmoid(N(0,1))), 'two_sigmoid' (2*sigmoid(N(0,1))),
@@ -192,7 +193,7 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
                       phi=phi, per_channel=per_channel, eps=eps, q=q, k=k, v=v,
                       beta=beta, lam=lam, S0=S0, xprev0=xprev0, qk_norm=qk_norm,
                       beta_pre=beta_pre, lam_pre=lam_pre, beta_act=beta_act, lam_act=lam_act,
-                      znorm=znorm)
+                      znorm=znorm, lam_scaled=lam_scaled)
 
 
 def delta_f32_small(seed=0, T=256):

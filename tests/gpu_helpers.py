@@ -48,6 +48,8 @@ def flags_of(w: wl.ScanInputs, extra=0):
             f |= F.LAMBDA_PREACT
     if w.znorm:
         f |= F.ZNORM
+    if w.lam_scaled:
+        f |= F.LAMBDA_SCALED
     return f
 
 
@@ -102,7 +104,8 @@ def oracle_scan(w: wl.ScanInputs, t_slice=None, S0=None, xprev0=None, has0=None)
                     rule=w.rule, phi_kind=w.phi, eps=w.eps, per_channel=w.per_channel,
                     S0=S0, xprev0=xprev0, has0=has0, qk_norm=w.qk_norm,
                     beta_act=w.beta_act if (w.gates_pre and gb is w.beta_pre) else None,
-                    lam_act=bool(w.gates_pre and w.lam_act), znorm=w.znorm)
+                    lam_act=bool(w.gates_pre and w.lam_act), znorm=w.znorm,
+                    lam_scaled=w.lam_scaled)
 
 
 def state_np(st):

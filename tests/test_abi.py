@@ -89,7 +89,7 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(shp=F.shape(1, 1, -3, 128, 128, F.BF16)), F.EINVAL),
     (dict(shp=F.shape(1, 1, 8, 128, 128, 7)), F.EINVAL),
     (dict(md=F.mode(rule=5)), F.EINVAL),
-    (dict(md=F.mode(flags=1 << 9)), F.EINVAL),
+    (dict(md=F.mode(flags=1 << 12)), F.EINVAL),
     (dict(md=F.mode(eps=-1.0)), F.EINVAL),
     (dict(md=F.mode(eps=float("nan"))), F.EINVAL),
     (dict(md=F.mode(chunk=48)), F.EUNSUPPORTED),
@@ -106,6 +106,9 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(md=F.mode(rule=F.RULE_INNER, flags=F.ZNORM)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.OUT_BF16)), F.EUNSUPPORTED),
+    # the scale-coupled ridge: a ridge (delta, inner), and in scans a scalar one
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.LAMBDA_SCALED | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(q=FAKE + 2), F.EALIGN),
     (dict(out=FAKE * 64 + 8), F.EALIGN),
     (dict(beta=FAKE + 2), F.EALIGN),
@@ -145,6 +148,7 @@ def test_empty_batch_is_a_no_op():
     (dict(md=F.mode(rule=-1)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 12)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_DELTA, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
     (dict(q=FAKE + 1), F.EALIGN),
     (dict(out=FAKE * 64 + 4), F.EALIGN),
     (dict(S_in=FAKE * 1024 + 64), F.EOVERLAP),
