@@ -103,12 +103,14 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
   const size_t BH = (size_t)s->B * (size_t)s->H, T = (size_t)s->T;
   const size_t nchunks = (T + kChunk - 1) / kChunk;
   const int bf16 = s->dtype == FWMEM_BF16 ? 1 : 0;
-  w.P = T > 0 ? fwmem::scan_segments(BH, T, s->dk, s->dv, bf16, m->flags) : 1;
+  w.P = T > 0 ? fwmem::scan_segments(BH, T, s->dk, s->dv, bf16, m->rule, m->flags) : 1;
   size_t off = align256(BH * nchunks * fwmem::scan_record_bytes(bf16, s->dk, m->flags));
   w.rec = 0;
   if (w.P > 1) {
     const size_t VH = BH * (size_t)w.P, dk = (size_t)s->dk, dv = (size_t)s->dv;
-    const size_t sa = align256(4 * (VH * dk * dk + VH * dk + VH));
+    // diagonal transitions need no transition states, and gam [BH*T] in place of z
+    const bool diag = fwmem::seg_diagonal(m->rule, m->flags);
+    const size_t sa = diag ? 0 : align256(4 * (VH * dk * dk + VH * dk + VH));
     const size_t sb = align256(4 * (VH * dk * dv + VH * dk + VH));
     w.A0 = off;
     w.A1 = w.A0 + sa;
@@ -116,7 +118,7 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
     w.B1 = w.B0 + sb;
     off = w.B1 + sb;
     w.z = off;
-    off += align256(4 * BH * T * dk);
+    off += align256(4 * BH * T * (diag ? 1 : dk));
     w.start = off;
     off += align256(4 * VH * dk * dv);
   }
@@ -344,6 +346,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   sp.dv = shape->dv;
   sp.bf16 = p.bf16;
   sp.flags = p.flags;
+  sp.diag = fwmem::seg_diagonal(mode->rule, mode->flags) ? 1 : 0;
+  sp.q = q;
+  sp.lam = lambda;
+  sp.gam = reinterpret_cast<float*>(ws + wl.z);
 
   fwmem::ScanParams pv = p;  // the local pass over the virtual heads
   pv.BH = (int)VH;
@@ -369,11 +375,12 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   hipError_t e = hipSuccess;
   if (phases & 1) {
     e = fwmem::launch_seg_init(sp, hs);
+    if (e == hipSuccess && sp.diag) e = fwmem::launch_seg_decay(sp, hs);
     if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 1);
   }
   if (e == hipSuccess && (phases & 2)) {
     e = fwmem::launch_scan(pv, hs, 2);
-    if (e == hipSuccess) e = fwmem::launch_scan(pa, hs, 2);
+    if (e == hipSuccess && !sp.diag) e = fwmem::launch_scan(pa, hs, 2);
     if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
     if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
   }

@@ -170,12 +170,25 @@ struct SegParams {
   const float* z;         // [BH*P][L][dk]
   float* S_start;         // [BH*P][dk][dv] (segment p >= 1)
   float* out;             // [BH][T][dv] float32
+  // Diagonal transitions (additive rule, scalar decay): a segment maps S to
+  // Gamma S + B, so there is no transition pass and no A or z buffer; the fix-up forms
+  // z_t = Gamma_t phi(q~_t) itself from the queries and gam, the decay from the
+  // segment's start through token t.
+  int diag;
+  const void* q;          // [BH][T][dk] raw queries
+  const float* lam;       // [BH][T] retention (or pre-activations), or null (1)
+  float* gam;             // [BH*P][L]
   int BH, P, L, dk, dv, bf16;
   uint32_t flags;
 };
+// A scan whose segments compose by a scalar: the additive rule with a scalar decay.
+__host__ __device__ inline bool seg_diagonal(int rule, uint32_t flags) {
+  return rule == kRuleAdditive && (flags & kFlagPerChannel) == 0;
+}
 // Segment count for a scan of this shape: 1 (no segmentation) unless the propagate
 // grid would leave most of the GPU idle and T splits into equal chunk-aligned segments.
-int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, uint32_t flags);
+int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint32_t flags);
+hipError_t launch_seg_decay(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_init(const SegParams& s, hipStream_t st);
 
 // ---- normalised linear attention (FWMEM_ZNORM; additive rule, scalar decay)

@@ -69,15 +69,17 @@ def test_segmented_nonzero_state_in_place():
     assert np.all(h == 1)
 
 
-def test_segmented_propagate_is_repeatable_after_one_prep():
+@pytest.mark.parametrize("rule", [wl.RULE_DELTA, wl.RULE_ADDITIVE])
+def test_segmented_propagate_is_repeatable_after_one_prep(rule):
     """prep once, then propagate twice: the propagate phase does not change its inputs, so
-    both runs give the same bits (and match the oracle)."""
+    both runs give the same bits (and match the oracle). The additive rule takes the
+    diagonal form."""
     import torch
-    w = _delta(H=2, seed=7)
+    w = _delta(H=2, seed=7) if rule == wl.RULE_DELTA else _delta(H=2, seed=7, rule=rule, lam_kind="gamma")
     q, k, v = (dev_tensor(a, "bf16") for a in (w.q, w.k, w.v))
     beta, lam = f32_tensor(w.beta), f32_tensor(w.lam)
     shp = F.shape(1, 2, w.T, 128, 128, F.BF16)
-    md = F.mode(0, 0, w.eps, 0)
+    md = F.mode(rule, 0, w.eps, 0)
     n = F.workspace_bytes(shp, md)
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     outs = []
@@ -95,3 +97,51 @@ def test_segmented_propagate_is_repeatable_after_one_prep():
     eo = orc.relerr(outs[0].astype(np.float64), o_ref)
     say(f"[segmented] repeat: err(o)={eo:.3e}")
     assert eo <= TOL["bf16"]
+
+
+# ---- diagonal transitions: the additive rule with a scalar decay composes segments by a
+# scalar (the product of the retentions), so there is no transition pass; the fix-up
+# forms Gamma_t phi(q_t) itself.
+
+def test_diagonal_segments_elu1_eight_heads():
+    """Eight heads of 4096 tokens (8 segments each), C3's distributions."""
+    check_scan(wl.make_scan(B=1, H=8, T=4096, dk=128, dv=128, rule=wl.RULE_ADDITIVE, phi=wl.PHI_ELU1,
+                            normalise_qk=False, beta_kind="one", lam_kind="gamma", seed=11,
+                            name="diagonal segments elu1 H=8"))
+
+
+def test_diagonal_segments_split_pair_qk_norm_and_gate_preactivations():
+    """Split pair (bf16 identity); the retention and write scale arrive as
+    pre-activations (the decay kernel activates them), q and k are L2-normalised by the
+    scan (the fix-up rescales the queries)."""
+    w = wl.make_scan(B=1, H=2, T=8192, dk=128, dv=128, rule=wl.RULE_ADDITIVE, normalise_qk=False,
+                     qk_norm="l2", beta_kind="sigmoid", lam_kind="gamma", seed=12,
+                     name="diagonal segments split qk-l2 gates-pre")
+    w.gates_pre = True
+    check_scan(w)
+
+
+def test_diagonal_segments_no_decay_f32():
+    """No retention (gamma = 1), float32, d_k = 64."""
+    check_scan(wl.make_scan(B=1, H=1, T=8192, dk=64, dv=128, dtype="f32", rule=wl.RULE_ADDITIVE,
+                            phi=wl.PHI_ELU1, normalise_qk=False, beta_kind="sigmoid", lam_kind="none",
+                            seed=13, name="diagonal segments f32 no decay"))
+
+
+def test_diagonal_segments_nonzero_state_in_place():
+    w = wl.make_scan(B=1, H=2, T=8192, dk=128, dv=128, rule=wl.RULE_ADDITIVE, phi=wl.PHI_ELU1,
+                     normalise_qk=False, beta_kind="one", lam_kind="gamma", gamma_mu=5.0, seed=14,
+                     name="diagonal segments in place")
+    rng = np.random.default_rng(14)
+    S0 = (rng.standard_normal((1, 2, 128, 128)) * 0.5).astype(np.float32)
+    from tests.gpu_helpers import make_state
+    st = make_state(1, 2, 128, 128, S=S0)
+    say("[segmented diagonal] nonzero S0, in place, slow decay (gamma ~ sigmoid(N(5, 0.5)))")
+    o, st2 = gpu_scan(w, S_in=st, S_out=st)
+    o_ref, S_ref, x_ref, _ = oracle_scan(w, S0=S0)
+    S, x, h = state_np(st2)
+    eo, eS = orc.relerr(o, o_ref), orc.relerr(S, S_ref)
+    say(f"    err(o)={eo:.3e} err(S)={eS:.3e}")
+    assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
+    np.testing.assert_allclose(x, x_ref, rtol=4e-6, atol=1e-30)
+    assert np.all(h == 1)
