@@ -14,7 +14,9 @@ vectorised only over independent heads (b, h). Sources (page titles as printed):
          section 4.2 (Falcon-1 rule, beta in (0,2), per-step descent lemma,
          NLMS limit), section 4.3 (the inner-product family, Falcon-1A: the same
          shifted pair, step size and decay, with the target written in place of the
-         residual), section 4.5 (RMSNorm of q and k; the ridge coupled to an energy
+         residual), section 4.4 (Falcon-2: the squared error separates over the value
+         channels, so each channel takes its own step size with the shared pair),
+         section 4.5 (RMSNorm of q and k; the ridge coupled to an energy
          statistic so that the decay does not depend on the input scale).
   [AFFN] hncyxsy.com blog post "attention is also an FFN" (news/211194):
          section 2.1 (S_i = sum_{j<=i} phi(k_j) v_j^T, y_i = phi(q_i)^T S_i),
@@ -39,6 +41,9 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
   D19 scale-coupled ridge (lam_scaled): lambda_t = lambda_bar_t * ||x_t||^2, the energy
       of the key written at step t (after any normalisation), for every channel of a
       per-channel lambda.
+  D20 per-value-channel rule (Falcon-2): beta is [B,H,T,d_v], lambda a scalar per token;
+      channel j steps by eta_{j,t} = beta_{j,t} / (|x_t|^2 + lambda_t + eps) and decays
+      its own column of S by 1 - eta_{j,t} lambda_t; shifted pair and boundary as D2.
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -50,6 +55,7 @@ import numpy as np
 RULE_DELTA = 0
 RULE_ADDITIVE = 1
 RULE_INNER = 2
+RULE_DELTA_PV = 3
 
 
 def phi(x: np.ndarray, kind: str) -> np.ndarray:
@@ -126,7 +132,7 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
     Q = _heads(q, 2)
     K = _heads(k, 2)
     V = _heads(v, 2)
-    Bt = None if beta is None else _heads(beta, 1)
+    Bt = None if beta is None else _heads(beta, 2 if rule == RULE_DELTA_PV else 1)
     if Bt is not None and beta_act is not None:
         Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)
     if lam is None:
@@ -155,6 +161,8 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
         raise ValueError("znorm takes the additive rule")
     if lam_scaled and rule == RULE_ADDITIVE:
         raise ValueError("lam_scaled takes the delta or inner rule")
+    if rule == RULE_DELTA_PV and per_channel:
+        raise ValueError("the per-value-channel rule takes a scalar lambda")
     z = xprev.copy() if znorm else None
 
     for t in range(T):
@@ -192,6 +200,19 @@ def scan(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
                 # (lambda_t/2)|S|^2 has gradient lambda_t S - x_t y_t^T, so the step
                 # writes the target y_t = v_t itself, with no residual.
                 S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * vt[:, None, :]
+        elif rule == RULE_DELTA_PV:
+            # [FWA] 4.4, Falcon-2: value channel j minimises its own squared error with
+            # its own step eta_{j,t} on the shared pair (x_t, v_t), so the rule is d_v
+            # scalar-step delta rules side by side, each decaying its own column of S
+            # (reading D20).
+            x = unit(xprev) * has[:, None]
+            lam_pv = np.zeros(N) if Lm is None else Lm[:, t]
+            if lam_scaled:
+                lam_pv = lam_pv * np.sum(x * x, axis=1)
+            den_pv = np.sum(x * x, axis=1) + lam_pv + eps
+            eta_pv = np.where(has[:, None], Bt[:, t, :] / np.where(has, den_pv, 1.0)[:, None], 0.0)
+            r_pv = vt - np.einsum("ni,nij->nj", x, S)
+            S = (1.0 - eta_pv * lam_pv[:, None])[:, None, :] * S + x[:, :, None] * (eta_pv * r_pv)[:, None, :]
         elif rule == RULE_ADDITIVE:
             # [AFFN] 3.2: S_t = gamma_t S_{t-1} + phi(k_t) v_t^T (times an optional
             # write scale beta_t, reading D7).
@@ -222,7 +243,8 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
          S0=None, xprev0=None, has0=None, qk_norm=None, beta_act=None, lam_act=False,
          znorm=False, lam_scaled=False):
     """One-token recurrent decode: q, k: [B,H,dk], v: [B,H,dv], beta/lam: [B,H]
-    (lam [B,H,dk] when per_channel). Returns (o [B,H,dv], S, xprev, has)."""
+    (lam [B,H,dk] when per_channel; beta [B,H,dv] for the per-value-channel rule).
+    Returns (o [B,H,dv], S, xprev, has)."""
     q = np.asarray(q)[:, :, None]
     k = np.asarray(k)[:, :, None]
     v = np.asarray(v)[:, :, None]

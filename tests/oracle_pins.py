@@ -681,6 +681,63 @@ def pin_p22_scale_coupled_ridge(orc):
         np.testing.assert_allclose(o[0, 0, :, 0], [2.0, S_hand[0]], rtol=1e-14)
 
 
+def pin_p23_per_value_channel_rule(orc):
+    """[FWA] 4.4 (Falcon-2). Four checks.
+    (a) Equal step sizes on every value channel give the delta rule.
+    (b) The objective separates over the value channels, so column j of the state and
+        of the reads equals a one-column delta rule with that channel's beta (d_k != d_v,
+        so an axis slip cannot hide).
+    (c) The per-step descent lemma holds for every channel's own loss
+        l_j(S) = (v_j - S[:, j] . x)^2 / 2 + lambda |S[:, j]|^2 / 2, for beta_j in (0, 2).
+    (d) Hand case, one write. S0 = [[1, 2], [3, 4]], x = (3, 4), v = (10, 20),
+        beta = (1, 1/2), lambda = 5, eps = 0. Then eta = (1/30, 1/60), the decays are
+        (5/6, 11/12) and r = v - S0^T x = (-5, -2), so S = [[1/3, 26/15], [11/6, 53/15]]."""
+    rng = np.random.default_rng(41)
+    T, dk, dv = 13, 5, 3
+    PV = orc.RULE_DELTA_PV
+    for scaled in (False, True):
+        q, k = rng.standard_normal((T, dk)), rng.standard_normal((T, dk))
+        v = rng.standard_normal((T, dv))
+        lam = rng.uniform(0.01, 0.5, T)
+        S0 = rng.standard_normal((1, 1, dk, dv))
+        b1 = rng.uniform(0.1, 1.9, T)
+        o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(np.repeat(b1[:, None], dv, 1)), _bh(lam),
+                              rule=PV, S0=S0, lam_scaled=scaled)
+        o_d, S_d, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(b1), _bh(lam), rule=DELTA, S0=S0,
+                                  lam_scaled=scaled)
+        np.testing.assert_allclose(o, o_d, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S, S_d, rtol=1e-12, atol=1e-13)
+        bpv = rng.uniform(0.1, 1.9, (T, dv))
+        o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(bpv), _bh(lam), rule=PV, S0=S0,
+                              lam_scaled=scaled)
+        for j in range(dv):
+            o_j, S_j, _, _ = orc.scan(_bh(q), _bh(k), _bh(v[:, j:j + 1]), _bh(bpv[:, j]), _bh(lam),
+                                      rule=DELTA, S0=S0[:, :, :, j:j + 1], lam_scaled=scaled)
+            np.testing.assert_allclose(o[..., j], o_j[..., 0], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(S[..., j], S_j[..., 0], rtol=1e-12, atol=1e-13)
+    for _ in range(200):
+        S = rng.standard_normal((1, 1, dk, dv))
+        xp = rng.standard_normal(dk)
+        vt = rng.standard_normal(dv)
+        bt = rng.uniform(0.01, 1.99, dv)
+        lt = rng.uniform(0.0, 1.0)
+        S1 = orc.step(rng.standard_normal((1, 1, dk)), rng.standard_normal((1, 1, dk)), vt[None, None],
+                      bt[None, None], np.array([[lt]]), rule=PV, eps=0.0, S0=S,
+                      xprev0=xp[None, None], has0=np.array([[1]]))[1]
+        for j in range(dv):
+            loss = lambda M: 0.5 * (vt[j] - M[:, j] @ xp) ** 2 + 0.5 * lt * M[:, j] @ M[:, j]
+            assert loss(S1[0, 0]) <= loss(S[0, 0]) + 1e-12
+    q = np.array([[0.0, 1.0], [1.0, 0.0]])
+    k = np.array([[3.0, 4.0], [1.0, 1.0]])
+    v = np.array([[7.0, 7.0], [10.0, 20.0]])
+    beta = np.array([[0.3, 0.3], [1.0, 0.5]])
+    S0 = np.array([[1.0, 2.0], [3.0, 4.0]])[None, None]
+    o, S, _, _ = orc.scan(_bh(q), _bh(k), _bh(v), _bh(beta), _bh(np.array([0.0, 5.0])), rule=PV,
+                          eps=0.0, S0=S0)
+    np.testing.assert_allclose(S[0, 0], [[1 / 3, 26 / 15], [11 / 6, 53 / 15]], rtol=1e-14)
+    np.testing.assert_allclose(o[0, 0], [[3.0, 4.0], [1 / 3, 26 / 15]], rtol=1e-14)
+
+
 ALL_PINS = [
     pin_p1_outer_product_store,
     pin_p2_quadratic_form,
@@ -707,5 +764,6 @@ ALL_PINS = [
     pin_p20_gate_preactivations,
     pin_p21_normalised_linear_attention,
     pin_p22_scale_coupled_ridge,
+    pin_p23_per_value_channel_rule,
     pin_relerr_metric,
 ]

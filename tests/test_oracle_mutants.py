@@ -48,6 +48,14 @@ MUTANTS = {
     "retention_uses_softplus": ("Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)",
                                 "Lm = softplus(Lm)"),
     "beta_range_one": ('Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)', "Bt = sigmoid(Bt)"),
+    "pv_shared_step": ("Bt[:, t, :] / np.where(has, den_pv, 1.0)[:, None]",
+                       "Bt[:, t, :1] / np.where(has, den_pv, 1.0)[:, None] + 0.0 * Bt[:, t, :]"),
+    "pv_decay_on_rows": ("(1.0 - eta_pv * lam_pv[:, None])[:, None, :] * S",
+                         "(1.0 - eta_pv * lam_pv[:, None])[:, :, None] * S"),
+    "pv_residual_sign": ('r_pv = vt - np.einsum("ni,nij->nj", x, S)', 'r_pv = vt + np.einsum("ni,nij->nj", x, S)'),
+    "pv_no_ridge_in_step": ("den_pv = np.sum(x * x, axis=1) + lam_pv + eps",
+                            "den_pv = np.sum(x * x, axis=1) + eps"),
+    "pv_same_index_pairing": ("x = unit(xprev) * has[:, None]", "x = kt * has[:, None]"),
     "ridge_not_scaled": ("lam_t = lam_t * (energy[:, None] if per_channel else energy)", "lam_t = lam_t"),
     "ridge_hat_not_scaled": ("lam_hat = lam_hat * energy", "lam_hat = lam_hat"),
     "ridge_scaled_by_norm": ("energy = np.sum(x * x, axis=1)", "energy = np.sqrt(np.sum(x * x, axis=1))"),
