@@ -92,7 +92,9 @@ def measured_traffic(workload, kernel):
 def kernel_names(w):
     """Names of the prep and propagate kernels that the library launches for w: bf16
     inputs with the identity feature map and a scalar decay take the split-operand
-    kernels, everything else the general ones."""
+    kernels, everything else the general ones; the per-value-channel rule has its own."""
+    if w.rule == 3:
+        return {"prep": "prep_pv_kernel", "propagate": "prop_pv_kernel"}
     split = w.dtype == "bf16" and not w.per_channel and w.phi != "elu1"
     return ({"prep": "prep_split_kernel", "propagate": "prop_split_kernel"} if split
             else {"prep": "prep_kernel", "propagate": "prop_kernel"})
@@ -101,8 +103,9 @@ def kernel_names(w):
 def compute_dtype(w):
     """Arithmetic type of the scan: the split kernels multiply bf16 operands (hi/lo pairs
     for computed matrices), the general kernels fp16 operands for bf16 inputs and fp32
-    operands for fp32 inputs; all accumulate in fp32."""
-    if w.dtype != "bf16":
+    operands for fp32 inputs (and the per-value-channel rule for both); all accumulate in
+    fp32."""
+    if w.dtype != "bf16" or w.rule == 3:
         return "f32"
     return "bf16" if kernel_names(w)["prep"] == "prep_split_kernel" else "f16"
 
@@ -112,7 +115,7 @@ def scan_bytes_per_token_head(w, out_bytes=4):
     lambda read once, out written once (the state adds d_k*d_v*8 per head per call)."""
     es = 2 if w.dtype == "bf16" else 4
     lam = 0 if w.lam is None else 4 * (w.dk if w.per_channel else 1)
-    beta = 0 if w.beta is None else 4
+    beta = 0 if w.beta is None else 4 * (w.dv if w.rule == 3 else 1)
     return (2 * w.dk + w.dv) * es + beta + lam + w.dv * out_bytes
 
 
@@ -123,6 +126,11 @@ def kernel_bytes(w, which):
     lam = 0 if w.lam is None else 4 * (w.dk if w.per_channel else 1)
     beta = 0 if w.beta is None else 4
     state = w.B * w.H * w.dk * w.dv * 4
+    if w.rule == 3:
+        # prep reads q, k, lambda; propagate reads q, k, v and beta [.., d_v]
+        if which == "prep":
+            return N * (2 * w.dk * es + lam)
+        return N * ((2 * w.dk + w.dv) * es + 4 * w.dv + 4 * w.dv) + 2 * state
     if which == "prep":   # reads q, k, beta, lambda
         return N * (2 * w.dk * es + beta + lam)
     # propagate: reads q, k, v (and lambda when per channel), writes out; state in and out
@@ -141,6 +149,12 @@ def scan_mfma_flops(w, C=64):
     hi/lo operand as two or three MFMAs, and those repeats are not counted."""
     nch = (w.T + C - 1) // C
     units = w.B * w.H * nch
+    if w.rule == 3:
+        # G and P (10 lower tiles each); X S, Q S, X^T W~, and the G W~ / P W~ blocks
+        # (6 and 10 blocks of 16x16x16 per 16 value columns)
+        prep = units * 2 * 10 * 2 * 16 * 16 * w.dk
+        blk = 2 * 16 * 16 * 16 * (w.dv // 16)
+        return prep, units * (3 * 2 * C * w.dk * w.dv + 16 * blk)
     delta = w.rule == 0
     shifted = w.rule != 1
     tile = 2 * 16 * 16 * w.dk
@@ -286,7 +300,7 @@ def main():
         "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
-                   "rule": ("delta", "additive", "inner")[w.rule], "inputs": w.dtype,
+                   "rule": ("delta", "additive", "inner", "delta_pv")[w.rule], "inputs": w.dtype,
                    "chunk": 64, "seed": 0, "qk_norm": w.qk_norm, "znorm": w.znorm},
         "roofline": roofline,
         "kernels": {names[n]: {"ms": round(kk["ms"], 5), "GBs": round(kk["GBs"], 1),

@@ -74,13 +74,26 @@ typedef enum {
                               both QK normalisation flags, both beta activations */
   FWMEM_EUNSUPPORTED = -2, /* a size or chunk length the library has no kernel for, or a QK
                               normalisation flag with FWMEM_PHI_ELU1 */
-  FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda) */
+  FWMEM_EALIGN = -3,       /* a pointer is not 16-byte aligned (4-byte for beta/lambda; a
+                              scan's per-value-channel beta 16-byte) */
   FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
   FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
   FWMEM_EWORKSPACE = -6    /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
 } fwmem_status;
 
-typedef enum { FWMEM_RULE_DELTA = 0, FWMEM_RULE_ADDITIVE = 1, FWMEM_RULE_INNER = 2 } fwmem_rule;
+/* DELTA_PV: the delta rule with one step size per value channel (Falcon-2, "Fast Weight
+ * Attention for Continual Learning" reading notes, section 4.4): the squared error
+ * separates over the value channels, so channel j steps by eta_{j,t} = beta_{j,t} /
+ * (|x_t|^2 + lambda_t + eps) on the shared shifted pair and decays its own column of S by
+ * 1 - eta_{j,t} lambda_t. beta is [B][H][T][d_v] (fwmem_step: [B][H][d_v]); lambda is
+ * scalar per token (FWMEM_LAMBDA_PER_CHANNEL: FWMEM_EUNSUPPORTED). Scans of this rule
+ * take fp32 MFMA operands for both dtypes and are never segmented. */
+typedef enum {
+  FWMEM_RULE_DELTA = 0,
+  FWMEM_RULE_ADDITIVE = 1,
+  FWMEM_RULE_INNER = 2,
+  FWMEM_RULE_DELTA_PV = 3
+} fwmem_rule;
 
 /* Storage type of q, k, v. All products accumulate in fp32. bf16 inputs with the
  * identity feature map and a scalar decay run on bf16 MFMA, with every computed
@@ -164,7 +177,7 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
  *   v      [B][H][T][dv]  dtype      (required)
  *   beta   [B][H][T]      float32    DELTA, INNER: required, beta in (0, 2) expected,
  *                                    never clamped. ADDITIVE: optional write scale
- *                                    (NULL = 1).
+ *                                    (NULL = 1). DELTA_PV: [B][H][T][dv], required.
  *   lambda [B][H][T] or [B][H][T][dk] float32
  *                                    DELTA, INNER: ridge lambda >= 0 (NULL = 0).
  *                                    ADDITIVE: retention gamma in [0, 1] (NULL = 1).
@@ -209,7 +222,8 @@ fwmem_status fwmem_scan_chunk_propagate(const fwmem_shape* shape, const void* q,
  * ("Fast Weight Attention for Continual Learning" reading notes, section 3.2:
  * fixed-size state at inference; the blog post's section 3.1: O(d^2) per step).
  *
- *   q, k [B][H][dk] dtype; v [B][H][dv] dtype; beta [B][H]; lambda [B][H] or
+ *   q, k [B][H][dk] dtype; v [B][H][dv] dtype; beta [B][H] ([B][H][dv] for
+ *   FWMEM_RULE_DELTA_PV); lambda [B][H] or
  *   [B][H][dk]; out [B][H][dv] float32 (bf16 with FWMEM_OUT_BF16).
  *   S_in: state buffer or NULL (zero state); S_out: state buffer (required);
  *   S_in == S_out updates in place. shape->T is ignored.

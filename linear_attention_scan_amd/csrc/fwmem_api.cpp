@@ -54,8 +54,11 @@ fwmem_status check_shape(const fwmem_shape* s, bool need_T) {
 
 fwmem_status check_mode(const fwmem_mode* m) {
   if (m == nullptr) return FWMEM_EINVAL;
-  if (m->rule != FWMEM_RULE_DELTA && m->rule != FWMEM_RULE_ADDITIVE && m->rule != FWMEM_RULE_INNER)
+  if (m->rule != FWMEM_RULE_DELTA && m->rule != FWMEM_RULE_ADDITIVE && m->rule != FWMEM_RULE_INNER &&
+      m->rule != FWMEM_RULE_DELTA_PV)
     return FWMEM_EINVAL;
+  // one step size per value channel, with a scalar ridge
+  if (m->rule == FWMEM_RULE_DELTA_PV && (m->flags & FWMEM_LAMBDA_PER_CHANNEL)) return FWMEM_EUNSUPPORTED;
   if ((m->flags & ~kKnownFlags) != 0) return FWMEM_EINVAL;
   // one normalisation at a time, and only of the raw q and k (identity feature map)
   if ((m->flags & FWMEM_QK_L2NORM) && (m->flags & FWMEM_QK_RMSNORM)) return FWMEM_EINVAL;
@@ -98,13 +101,19 @@ struct WsLayout {
   size_t rec, A0, B0, A1, B1, z, start, zr, zc, total;
 };
 
+size_t record_bytes(int bf16, int dk, const fwmem_mode* m) {
+  return m->rule == FWMEM_RULE_DELTA_PV ? fwmem::scan_pv_record_bytes()
+                                        : fwmem::scan_record_bytes(bf16, dk, m->flags);
+}
+
 WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
   WsLayout w{};
   const size_t BH = (size_t)s->B * (size_t)s->H, T = (size_t)s->T;
   const size_t nchunks = (T + kChunk - 1) / kChunk;
   const int bf16 = s->dtype == FWMEM_BF16 ? 1 : 0;
-  w.P = T > 0 ? fwmem::scan_segments(BH, T, s->dk, s->dv, bf16, m->rule, m->flags) : 1;
-  size_t off = align256(BH * nchunks * fwmem::scan_record_bytes(bf16, s->dk, m->flags));
+  const bool pv = m->rule == FWMEM_RULE_DELTA_PV;
+  w.P = (T > 0 && !pv) ? fwmem::scan_segments(BH, T, s->dk, s->dv, bf16, m->rule, m->flags) : 1;
+  size_t off = align256(BH * nchunks * record_bytes(bf16, s->dk, m));
   w.rec = 0;
   if (w.P > 1) {
     const size_t VH = BH * (size_t)w.P, dk = (size_t)s->dk, dv = (size_t)s->dv;
@@ -208,13 +217,14 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   }
   // alignment
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(workspace, 16) || !aligned(beta, 4) ||
-      !aligned(lambda, pc ? 16 : 4))
+      !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(workspace, 16) ||
+      !aligned(beta, mode->rule == FWMEM_RULE_DELTA_PV ? 16 : 4) || !aligned(lambda, pc ? 16 : 4))
     return FWMEM_EALIGN;
 
   // overlap
   const size_t nq = z.BH * T * shape->dk * es, nv = z.BH * T * shape->dv * es;
-  const size_t nb = z.BH * T * 4, nl = z.BH * T * 4 * (pc ? shape->dk : 1);
+  const bool rule_pv = mode->rule == FWMEM_RULE_DELTA_PV;
+  const size_t nb = z.BH * T * 4 * (rule_pv ? shape->dv : 1), nl = z.BH * T * 4 * (pc ? shape->dk : 1);
   const size_t no = z.BH * T * shape->dv * ((mode->flags & FWMEM_OUT_BF16) ? 2 : 4);
   size_t need = 0;
   st = fwmem_scan_workspace_bytes(shape, mode, &need);
@@ -271,10 +281,14 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   // per-head byte offsets of every buffer (inputs, outputs, records) stay below 2^31
   const size_t dmax = (size_t)(shape->dk > shape->dv ? shape->dk : shape->dv);
   if (T * dmax * 4 > 0x7fffffffu ||
-      (size_t)p.nchunks * fwmem::scan_record_bytes(p.bf16, shape->dk, p.flags) > 0x7fffffffu)
+      (size_t)p.nchunks * record_bytes(p.bf16, shape->dk, mode) > 0x7fffffffu)
     return FWMEM_EUNSUPPORTED;
 
   const WsLayout wl = ws_layout(shape, mode);
+  if (rule_pv) {
+    const hipError_t e = fwmem::launch_scan_pv(p, hs, phases);
+    return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+  }
   // Normalised linear attention: prep writes the chunk terms of z, and after the
   // propagate kernels z is chained over the chunks of each head and divides the outputs.
   // Records of virtual heads (segments) are those of the real heads' chunks in order, so
@@ -439,7 +453,8 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
       !aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(beta, 4) || !aligned(lambda, 4))
     return FWMEM_EALIGN;
   const size_t nq = z.BH * shape->dk * es, nv = z.BH * shape->dv * es;
-  const size_t nb = z.BH * 4, nl = z.BH * 4 * (pc ? shape->dk : 1);
+  const size_t nb = z.BH * 4 * (mode->rule == FWMEM_RULE_DELTA_PV ? shape->dv : 1);
+  const size_t nl = z.BH * 4 * (pc ? shape->dk : 1);
   const size_t no = z.BH * shape->dv * ((mode->flags & FWMEM_OUT_BF16) ? 2 : 4);
   if (S_in != nullptr && S_in != S_out && overlap(S_in, z.state_bytes, S_out, z.state_bytes))
     return FWMEM_EOVERLAP;

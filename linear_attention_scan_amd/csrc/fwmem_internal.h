@@ -53,7 +53,7 @@ __host__ __device__ inline float rescale_factor(float ss, float len) {
 }
 
 // Write rules (the values of fwmem_rule).
-enum : int { kRuleDelta = 0, kRuleAdditive = 1, kRuleInner = 2 };
+enum : int { kRuleDelta = 0, kRuleAdditive = 1, kRuleInner = 2, kRuleDeltaPV = 3 };
 
 // What each rule needs of the kernels:
 //   shift: the written key is the previous token's (x_t = phi(k_{t-1})), with the key
@@ -65,7 +65,7 @@ enum : int { kRuleDelta = 0, kRuleAdditive = 1, kRuleInner = 2 };
 template <int RULE>
 struct Rule {
   static constexpr bool shift = RULE != kRuleAdditive;
-  static constexpr bool solve = RULE == kRuleDelta;
+  static constexpr bool solve = RULE == kRuleDelta || RULE == kRuleDeltaPV;
   static constexpr bool nlms = RULE != kRuleAdditive;
 };
 
@@ -118,6 +118,9 @@ size_t scan_record_bytes(int bf16, int dk, uint32_t flags);
 // propagate kernel (fwmem_scan_split.hip).
 bool scan_split_path(int bf16, uint32_t flags);
 hipError_t launch_prep_split(const ScanParams& p, hipStream_t stream);
+// The per-value-channel rule (fwmem_scan_pv.hip): its record size and both phases.
+size_t scan_pv_record_bytes();
+hipError_t launch_scan_pv(const ScanParams& p, hipStream_t stream, int phases);
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t stream);
 // Whether kernels exist for this size.
 bool scan_supported(int dk, int dv);

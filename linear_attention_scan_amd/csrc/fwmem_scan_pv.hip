@@ -1,0 +1,501 @@
+// Chunked scan of the per-value-channel delta rule (Falcon-2, "Fast Weight Attention for
+// Continual Learning" reading notes, section 4.4): value channel j steps by
+// eta_{j,t} = beta_{j,t} / (|x_t|^2 + lambda_t + eps) on the shared shifted pair and
+// decays its own column of S by a_{j,t} = 1 - eta_{j,t} lambda_t.
+//
+// Chunk algebra, per column j (the column index is dropped), with Gamma_t the product of
+// a over the chunk's tokens 0..t, Gamma^_t = Gamma_t / Gamma_A its value relative to an
+// anchor token A in mid-chunk, and W~ the chunk's writes w_t = eta_t r_t divided by
+// Gamma^_t:
+//   w~_t = c_t (v_t - Gamma_{t-1} (X S0)_t) - c_t Gamma^_{t-1} (G W~)_t,  c_t = eta_t / Gamma^_t
+//   O    = Gamma o (Q S0) + Gamma^ o (P W~)
+//   S'   = Gamma_C S0 + Gamma^_C X^T W~
+// with G_ts = x_t . x_s (s < t) and P_ts = q_t . x_s (s <= t) shared by every column
+// (the update geometry depends on the keys only, as the page notes). Every per-column
+// factor is a row scaling, so all products run on MFMA over the shared X, Q, G, P; only
+// the 16 x 16 diagonal blocks of the triangular system for W~ are solved row by row.
+//
+// Prep (one workgroup per (head, chunk)): G, P and the token scalars into a record.
+// Propagate (one workgroup per (head, 64 value columns), four waves of 16 columns, the
+// state slice in registers): per chunk, stage X, Q, G, P, beta and V in LDS, then the
+// algebra above on fp32 MFMA.
+#include "fwmem_device.h"
+#include "fwmem_internal.h"
+
+namespace fwmem {
+namespace {
+
+constexpr int CH = kChunk;
+constexpr int NT = 256;
+constexpr int LDM = CH + 4;  // float stride of a [CH][CH] matrix
+
+// Record of one (head, chunk), floats: G [CH][CH] (strictly lower), P [CH][CH] (lower),
+// then per token: eta's denominator (infinite where there is no key to write), the
+// ridge lambda_t, and the rescale factors of x_t and q_t (1 without QK normalisation);
+// in chunk 0's record, the carried key (zero without one), so that the propagate kernel
+// never reads the state's x_prev, which a state updated in place overwrites.
+struct RecPV {
+  static constexpr size_t kG = 0;
+  static constexpr size_t kP = kG + CH * CH;
+  static constexpr size_t kDen = kP + CH * CH;
+  static constexpr size_t kLam = kDen + CH;
+  static constexpr size_t kNx = kLam + CH;
+  static constexpr size_t kMq = kNx + CH;
+  static constexpr size_t kX0 = kMq + CH;  // [d_k <= 128]
+  static constexpr size_t kFloats = kX0 + 128;
+  static constexpr size_t kBytes = (4 * kFloats + 255) / 256 * 256;
+};
+
+// C += A B for a 16x16x16 block on fp32 MFMA: lane (g, n) supplies A[n][4g..4g+3] and
+// B[4g+q][n] (the C layout of a previous product); MFMA q sums over K = 4g + q.
+__device__ __forceinline__ void mma_block(f4& acc, const f4& a, const f4& b) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+}
+
+// Stage the chunk's written keys x_t (the previous token's phi(k); for the sequence's
+// first token the carried key x0, or zero when x0 is null) and queries phi(q_t) as fp32
+// rows [CH][LDX], zero past the end, each times its rescale factor when given.
+template <typename InT, int DK, int LDX>
+__device__ __forceinline__ void stage_rows(const ScanParams& p, int bh, int t0, float* Xs, float* Qs,
+                                           const float* x0, const float* sx, const float* sq) {
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const InT* kb = static_cast<const InT*>(p.k) + (size_t)bh * p.T * DK;
+  const InT* qb = static_cast<const InT*>(p.q) + (size_t)bh * p.T * DK;
+  for (int e = threadIdx.x; e < CH * DK; e += NT) {
+    const int t = e / DK, i = e % DK, tau = t0 + t;
+    float x = 0.f, q = 0.f;
+    if (tau < p.T) {
+      if (tau >= 1) {
+        x = In<InT>::load1(kb + (size_t)(tau - 1) * DK + i);
+        if (elu) x = phi_elu1(x);
+      } else if (x0 != nullptr) {
+        x = x0[i];  // the carried key is phi(k) already
+      }
+      q = In<InT>::load1(qb + (size_t)tau * DK + i);
+      if (elu) q = phi_elu1(q);
+    }
+    Xs[t * LDX + i] = sx != nullptr ? x * sx[t] : x;
+    Qs[t * LDX + i] = sq != nullptr ? q * sq[t] : q;
+  }
+}
+
+template <typename InT, int DK>
+__global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
+  constexpr int LDX = DK + 4;
+  __shared__ __align__(16) float Xs[CH * LDX];
+  __shared__ __align__(16) float Qs[CH * LDX];
+  __shared__ float s_nx[CH], s_mq[CH];
+  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  const int t0 = c * CH;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  float* rec = reinterpret_cast<float*>(p.ws + ((size_t)bh * p.nchunks + c) * RecPV::kBytes);
+  const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
+  const float* x0 = (has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+
+  stage_rows<InT, DK, LDX>(p, bh, t0, Xs, Qs, x0, nullptr, nullptr);
+  if (c == 0)
+    for (int i = threadIdx.x; i < DK; i += NT) rec[RecPV::kX0 + i] = x0 != nullptr ? x0[i] : 0.f;
+  __syncthreads();
+  // token scalars (wave 0, lane = token)
+  if (wave == 0) {
+    const int t = lane, tau = t0 + t;
+    float e = 0.f, nq = 0.f;
+    for (int i = 0; i < DK; ++i) {
+      const float x = Xs[t * LDX + ((i + t) % DK)], q = Qs[t * LDX + ((i + t) % DK)];
+      e += x * x;
+      nq += q * q;
+    }
+    const float len = qk_length(p.flags, DK);
+    float nx = 1.f, mq = 1.f;
+    if (len > 0.f) {
+      nx = rescale_factor(e, len);
+      mq = rescale_factor(nq, len);
+      e *= nx * nx;
+    }
+    float lam = 0.f;
+    if (tau < p.T && p.lam != nullptr) lam = act_lam(p.lam[(size_t)bh * p.T + tau], p.flags, true);
+    if (p.flags & kFlagLamScaled) lam *= e;
+    const bool key = tau < p.T && (tau >= 1 || has_in);
+    rec[RecPV::kDen + t] = key ? e + lam + p.eps : __builtin_inff();
+    rec[RecPV::kLam + t] = lam;
+    rec[RecPV::kNx + t] = nx;
+    rec[RecPV::kMq + t] = mq;
+    s_nx[t] = nx;
+    s_mq[t] = mq;
+  }
+  __syncthreads();
+  // G and P: 10 lower 16x16 tiles each; wave w takes tiles w, w+4, ...
+  for (int job = wave; job < 32; job += 4) {
+    const int mat = job >> 4, mt = (job >> 2) & 3, nt = job & 3;  // mat 0: G, 1: P
+    float* dst = rec + (mat == 0 ? RecPV::kG : RecPV::kP);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (mt >= nt) {
+      const float* arow = (mat == 0 ? Xs : Qs) + (16 * mt + n) * LDX;
+      const float* brow = Xs + (16 * nt + n) * LDX;
+#pragma unroll 4
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const f4 a = *reinterpret_cast<const f4*>(arow + 16 * kb + 4 * g);
+        const f4 b = *reinterpret_cast<const f4*>(brow + 16 * kb + 4 * g);
+        mma_block(acc, a, b);
+      }
+    }
+    const int s = 16 * nt + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g + i;
+      const bool keep = mat == 0 ? s < t : s <= t;
+      const float f = (mat == 0 ? s_nx[t] : s_mq[t]) * s_nx[s];
+      dst[t * CH + s] = keep ? f * acc[i] : 0.f;
+    }
+  }
+}
+
+// Exclusive prefix over the column's four lane groups g (lanes n, n+16, n+32, n+48) of a
+// lane total, and the sum over all four.
+__device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, float& excl, int& pexcl,
+                                             float& tot, int& ptot) {
+  excl = 0.f;
+  tot = 0.f;
+  pexcl = 0;
+  ptot = 0;
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    const float u = __shfl(v, 16 * gg + n);
+    const int pu = __shfl(pv, 16 * gg + n);
+    if (gg < g) {
+      excl += u;
+      pexcl ^= pu;
+    }
+    tot += u;
+    ptot ^= pu;
+  }
+}
+
+template <int DK>
+constexpr size_t prop_pv_floats() {
+  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH;
+}
+
+template <typename InT, int DK>
+__global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
+  constexpr int LDX = DK + 4, NRT = DK / 16;
+  static_assert(4 * prop_pv_floats<DK>() <= 160 * 1024, "LDS");
+  __shared__ __align__(16) float smem[prop_pv_floats<DK>()];
+  float* Xs = smem;                 // [CH][LDX] x_t rescaled
+  float* Qs = Xs + CH * LDX;        // [CH][LDX] q_t rescaled
+  float* Gs = Qs + CH * LDX;        // [CH][LDM]
+  float* Ps = Gs + CH * LDM;        // [CH][LDM]
+  float* Bs = Ps + CH * LDM;        // [CH][LDM] beta of the group's 64 columns
+  float* Vs = Bs + CH * LDM;        // [CH][LDM] values of the group's 64 columns
+  float* s_den = Vs + CH * LDM;     // [CH]
+  float* s_lam = s_den + CH;        // [CH]
+  float* s_nx = s_lam + CH;         // [CH]
+  float* s_mq = s_nx + CH;          // [CH]
+
+  const int ngrp = p.dv / 64;
+  const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int dv = p.dv, cw = 16 * wave + n;  // the lane's column within the group
+  const int col = 64 * grp + cw;
+  const size_t rowbase = (size_t)bh * p.T;
+  const InT* vb = static_cast<const InT*>(p.v) + rowbase * dv + 64 * grp;
+  const float* bb = p.beta + rowbase * dv + 64 * grp;
+
+  const float* rec0 = reinterpret_cast<const float*>(p.ws + (size_t)bh * p.nchunks * RecPV::kBytes);
+  f4 s[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[rt][i] = p.S_in != nullptr ? p.S_in[((size_t)bh * DK + 16 * rt + 4 * g + i) * dv + col] : 0.f;
+
+  // Chunk c+1 is loaded into registers (16-byte loads) while chunk c computes, then
+  // written to LDS at the top of the next iteration. X and Q go to LDS as phi(x), phi(q)
+  // without their rescale factors, which scale the products' rows instead.
+  constexpr int VW = In<InT>::VW;
+  constexpr int GPR = DK / VW;             // granules per X / Q row
+  constexpr int NGX = CH * GPR / NT;       // X (and Q) granules per thread
+  constexpr int NGV = CH * (64 / VW) / NT; // value granules per thread
+  static_assert(NGX >= 1 && NGV >= 1, "granules");
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
+  const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
+  u32x4 px[NGX], pq[NGX], pv[NGV];
+  f4 pg[4], pp[4], pb[4];
+  f4 psc = {0.f, 0.f, 0.f, 0.f};  // den, lambda, nx, mq of token tid (tid < CH)
+  uint32_t xzero = 0;             // granules of the carried key (the sequence's first token)
+
+  auto prefetch = [&](int cn) {
+    const int tn = cn * CH;
+    const float* rec = reinterpret_cast<const float*>(p.ws + ((size_t)bh * p.nchunks + cn) * RecPV::kBytes);
+    xzero = 0;
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW, tau = tn + t;
+      px[r] = u32x4{0u, 0u, 0u, 0u};
+      pq[r] = u32x4{0u, 0u, 0u, 0u};
+      if (tau < p.T) {
+        if (tau >= 1) px[r] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(tau - 1) * DK + cc);
+        else xzero |= 1u << r;
+        pq[r] = *reinterpret_cast<const u32x4*>(qbase + (size_t)tau * DK + cc);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gi = tid + NT * r, t = gi / 16, u = (gi % 16) * 4;
+      pg[r] = *reinterpret_cast<const f4*>(rec + RecPV::kG + 4 * gi);
+      pp[r] = *reinterpret_cast<const f4*>(rec + RecPV::kP + 4 * gi);
+      pb[r] = tn + t < p.T ? *reinterpret_cast<const f4*>(bb + (size_t)(tn + t) * dv + u) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = tid + NT * r, t = gi / (64 / VW), u = (gi % (64 / VW)) * VW;
+      pv[r] = tn + t < p.T ? *reinterpret_cast<const u32x4*>(vb + (size_t)(tn + t) * dv + u) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < CH)
+      psc = f4{rec[RecPV::kDen + tid], rec[RecPV::kLam + tid], rec[RecPV::kNx + tid], rec[RecPV::kMq + tid]};
+  };
+
+  prefetch(0);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * CH;
+    // ---- registers -> LDS (chunk c)
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW;
+      float x[VW], q[VW];
+      In<InT>::decode(px[r], x);
+      In<InT>::decode(pq[r], q);
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        if ((xzero >> r) & 1u) x[j] = rec0[RecPV::kX0 + cc + j];  // the carried key, phi(k) already
+        else if (elu) x[j] = phi_elu1(x[j]);
+        if (elu) q[j] = phi_elu1(q[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < VW; j += 4) {
+        *reinterpret_cast<f4*>(Xs + t * LDX + cc + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+        *reinterpret_cast<f4*>(Qs + t * LDX + cc + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gi = tid + NT * r, t = gi / 16, u = (gi % 16) * 4;
+      f4 b = pb[r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = act_beta(b[j], p.flags);
+      *reinterpret_cast<f4*>(Gs + t * LDM + u) = pg[r];
+      *reinterpret_cast<f4*>(Ps + t * LDM + u) = pp[r];
+      *reinterpret_cast<f4*>(Bs + t * LDM + u) = b;  // rows past the end hold act(0); V is 0 there
+    }
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = tid + NT * r, t = gi / (64 / VW), u = (gi % (64 / VW)) * VW;
+      float x[VW];
+      In<InT>::decode(pv[r], x);
+#pragma unroll
+      for (int j = 0; j < VW; j += 4) *reinterpret_cast<f4*>(Vs + t * LDM + u + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+    }
+    if (tid < CH) {
+      s_den[tid] = psc[0];
+      s_lam[tid] = psc[1];
+      s_nx[tid] = psc[2];
+      s_mq[tid] = psc[3];
+    }
+    __syncthreads();
+    if (c + 1 < p.nchunks) prefetch(c + 1);
+
+    // ---- X S0 and Q S0 (C layout: rows 16 mt + 4 g + i, column n), rows rescaled
+    f4 XS[4], QS[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      XS[mt] = f4{0.f, 0.f, 0.f, 0.f};
+      QS[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const f4 ax = *reinterpret_cast<const f4*>(Xs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
+        const f4 aq = *reinterpret_cast<const f4*>(Qs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
+        mma_block(XS[mt], ax, s[rt]);
+        mma_block(QS[mt], aq, s[rt]);
+      }
+      XS[mt] *= *reinterpret_cast<const f4*>(s_nx + 16 * mt + 4 * g);
+      QS[mt] *= *reinterpret_cast<const f4*>(s_mq + 16 * mt + 4 * g);
+    }
+
+    // ---- per (token, column): eta, decay, and the in-chunk log-decay prefix
+    float eta[4][4], la[4][4];
+    int ng[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * g + i;
+        const float e = Bs[t * LDM + cw] / s_den[t];  // 0 where there is no key
+        const float a = 1.f - e * s_lam[t];
+        eta[mt][i] = e;
+        la[mt][i] = log_abs_floor(a);
+        ng[mt][i] = a < 0.f ? 1 : 0;
+      }
+    float gl[4][4];
+    int pg[4][4];
+    {
+      float carry = 0.f;
+      int pcarry = 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float run = 0.f;
+        int prun = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          run += la[mt][i];
+          prun ^= ng[mt][i];
+          gl[mt][i] = run;
+          pg[mt][i] = prun;
+        }
+        float excl, tot;
+        int pexcl, ptot;
+        group_prefix(run, prun, g, n, excl, pexcl, tot, ptot);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gl[mt][i] += carry + excl;
+          pg[mt][i] ^= pcarry ^ pexcl;
+        }
+        carry += tot;
+        pcarry ^= ptot;
+      }
+    }
+    // anchor A = token 31 (row tile 1, g = 3, i = 3); chunk end C = token 63
+    const float gA = __shfl(gl[1][3], 48 + n);
+    const int pA = __shfl(pg[1][3], 48 + n);
+    const float gC = __shfl(gl[3][3], 48 + n);
+    const int pC = __shfl(pg[3][3], 48 + n);
+    const float GamC = (pC ? -1.f : 1.f) * __expf(gC);
+    const float GhC = ((pC ^ pA) ? -1.f : 1.f) * __expf(gC - gA);
+
+    // right-hand sides and row factors of the triangular system
+    float rhs[4][4], ef[4][4], Gam[4][4], Gh[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * g + i;
+        const float gprev = gl[mt][i] - la[mt][i];
+        const int pprev = pg[mt][i] ^ ng[mt][i];
+        Gam[mt][i] = (pg[mt][i] ? -1.f : 1.f) * __expf(gl[mt][i]);
+        Gh[mt][i] = ((pg[mt][i] ^ pA) ? -1.f : 1.f) * __expf(gl[mt][i] - gA);
+        const float Gprev = (pprev ? -1.f : 1.f) * __expf(gprev);
+        const float Ghprev = ((pprev ^ pA) ? -1.f : 1.f) * __expf(gprev - gA);
+        const float cf = eta[mt][i] / Gh[mt][i];
+        rhs[mt][i] = cf * (Vs[t * LDM + cw] - Gprev * XS[mt][i]);
+        ef[mt][i] = cf * Ghprev;
+      }
+
+    // ---- W~ by blocked forward substitution: off-diagonal blocks on MFMA, then the
+    // diagonal block row by row (row r's owner lanes g = r / 4 broadcast its value)
+    f4 W[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bk = 0; bk < bi; ++bk) {
+        const f4 a = *reinterpret_cast<const f4*>(Gs + (16 * bi + n) * LDM + 16 * bk + 4 * g);
+        mma_block(y, a, W[bk]);
+      }
+      f4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = r >> 2, ir = r & 3;
+        const float cand = rhs[bi][ir] - ef[bi][ir] * y[ir];
+        const float wr = __shfl(cand, 16 * gr + n);
+        if (g == gr) w[ir] = wr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i > r) y[i] += Gs[(16 * bi + 4 * g + i) * LDM + 16 * bi + r] * wr;
+      }
+      W[bi] = w;
+    }
+
+    // ---- O = Gamma o (Q S0) + Gamma^ o (P W~), stored
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f4 pw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bk = 0; bk <= mt; ++bk) {
+        const f4 a = *reinterpret_cast<const f4*>(Ps + (16 * mt + n) * LDM + 16 * bk + 4 * g);
+        mma_block(pw, a, W[bk]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tau = t0 + 16 * mt + 4 * g + i;
+        if (tau < p.T) {
+          const float o = Gam[mt][i] * QS[mt][i] + Gh[mt][i] * pw[i];
+          const size_t oi = (rowbase + tau) * dv + col;
+          if (p.flags & kFlagOutBf16) static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_bits(o);
+          else static_cast<float*>(p.out)[oi] = o;
+        }
+      }
+    }
+
+    // ---- S' = Gamma_C S0 + Gamma^_C X^T W~
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f4 a;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = Xs[(16 * kb + 4 * g + q) * LDX + 16 * rt + n];
+        mma_block(acc, a, W[kb] * *reinterpret_cast<const f4*>(s_nx + 16 * kb + 4 * g));
+      }
+      s[rt] = s[rt] * GamC + acc * GhC;
+    }
+    __syncthreads();  // LDS is restaged next chunk
+  }
+
+  if (p.S_out != nullptr) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.S_out[((size_t)bh * DK + 16 * rt + 4 * g + i) * dv + col] = s[rt][i];
+    if (grp == 0) {
+      const bool elu = (p.flags & kFlagPhiElu1) != 0;
+      const InT* kb = static_cast<const InT*>(p.k) + (rowbase + p.T - 1) * DK;
+      for (int i = tid; i < DK; i += NT) {
+        float x = In<InT>::load1(kb + i);
+        if (elu) x = phi_elu1(x);
+        p.xprev_out[(size_t)bh * DK + i] = x;
+      }
+      if (tid == 0) p.has_out[bh] = 1;
+    }
+  }
+}
+
+template <typename InT, int DK>
+hipError_t launch_pv_t(const ScanParams& p, hipStream_t st, int phases) {
+  if (phases & 1) {
+    hipLaunchKernelGGL((prep_pv_kernel<InT, DK>), dim3((unsigned)((size_t)p.BH * p.nchunks)), dim3(NT), 0,
+                       st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    hipLaunchKernelGGL((prop_pv_kernel<InT, DK>), dim3((unsigned)((size_t)p.BH * (p.dv / 64))), dim3(NT),
+                       0, st, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t scan_pv_record_bytes() { return RecPV::kBytes; }
+
+hipError_t launch_scan_pv(const ScanParams& p, hipStream_t st, int phases) {
+  if (p.bf16) return p.dk == 64 ? launch_pv_t<uint16_t, 64>(p, st, phases) : launch_pv_t<uint16_t, 128>(p, st, phases);
+  return p.dk == 64 ? launch_pv_t<float, 64>(p, st, phases) : launch_pv_t<float, 128>(p, st, phases);
+}
+
+}  // namespace fwmem

@@ -51,6 +51,9 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   const int cq = tid % TPRd, rg = tid / TPRd;
   const bool elu = (p.flags & kFlagPhiElu1) != 0;
   const bool znorm = !R::solve && !R::shift && (p.flags & kFlagZnorm) != 0;
+  // per-value-channel rule: eta_j = beta_j / den and the decay 1 - eta_j lambda act on
+  // the columns; the rows carry no decay
+  constexpr bool PV = RULE == kRuleDeltaPV;
   const InT* qp = static_cast<const InT*>(p.q) + (size_t)bh * DK;
   const InT* kp = static_cast<const InT*>(p.k) + (size_t)bh * DK;
   const InT* vp = static_cast<const InT*>(p.v) + (size_t)bh * DV;
@@ -114,8 +117,13 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
         const float lam = es * (PC ? (p.lam != nullptr ? lm : 0.f)
                                    : (p.lam != nullptr ? act_lam(p.lam[bh], p.flags, true) : 0.f));
         s_sc[6] = es;
-        if (has) eta = act_beta(p.beta[bh], p.flags) / (nx + lam + p.eps);
-        a = 1.f - eta * lam;
+        if (PV) {
+          eta = has ? 1.f / (nx + lam + p.eps) : 0.f;  // times each column's beta below
+          a = lam;
+        } else {
+          if (has) eta = act_beta(p.beta[bh], p.flags) / (nx + lam + p.eps);
+          a = 1.f - eta * lam;
+        }
       } else {
         eta = p.beta != nullptr ? act_beta(p.beta[bh], p.flags) : 1.f;  // write scale
         a = (!PC && p.lam != nullptr) ? act_lam(p.lam[bh], p.flags, false) : 1.f;
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
       if (R::shift) s_x[i] *= s_sc[3];
       else s_k[i] *= s_sc[3];
     }
-    float a = a_sc;
+    float a = PV ? 1.f : a_sc;
     if (PC) {
       const float lam = p.lam != nullptr ? act_lam(p.lam[(size_t)bh * DK + i], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
       a = R::nlms ? 1.f - eta * s_sc[6] * lam : lam;
@@ -193,8 +201,20 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
   }
   // r (delta) or the written value b*v (additive), and the output.
   const f4 vv = {v4[0], v4[1], v4[2], v4[3]};
-  const f4 r = R::solve ? (vv - P) * eta : vv * eta;  // the written value u
-  const f4 o = znorm ? (W + r * dq) * s_sc[5] : W + r * dq;
+  f4 r, o, a4 = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (PV) {
+    f4 e4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      e4[e] = act_beta(p.beta[(size_t)bh * DV + 4 * cq + e], p.flags) * eta;
+      a4[e] = 1.f - e4[e] * a_sc;
+    }
+    r = (vv - P) * e4;
+    o = W * a4 + r * dq;  // W = S^T q here
+  } else {
+    r = R::solve ? (vv - P) * eta : vv * eta;  // the written value u
+    o = znorm ? (W + r * dq) * s_sc[5] : W + r * dq;
+  }
 
   // New state from registers.
   float* Sout = p.S_out + (size_t)bh * DK * DV;
@@ -203,7 +223,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     const int row = rg + RG * j;
     const float a = s_a[row];
     const float xi = R::shift ? s_x[row] : s_k[row];
-    const f4 n4 = S[j] * a + r * xi;
+    const f4 n4 = PV ? S[j] * a4 + r * xi : S[j] * a + r * xi;
     __builtin_nontemporal_store(n4, reinterpret_cast<f4*>(Sout + (size_t)row * DV) + cq);
   }
   if (rg == 0) {
@@ -226,6 +246,8 @@ hipError_t launch_t(const StepParams& p, hipStream_t st) {
   if (p.rule == kRuleDelta) {
     if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleDelta, true>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleDelta, false>), grid, block, 0, st, p);
+  } else if (p.rule == kRuleDeltaPV) {
+    hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleDeltaPV, false>), grid, block, 0, st, p);
   } else if (p.rule == kRuleInner) {
     if (pc) hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleInner, true>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((step_kernel<InT, DK, DV, kRuleInner, false>), grid, block, 0, st, p);

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfwmem.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EOVERLAP, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
-RULE_DELTA, RULE_ADDITIVE, RULE_INNER = 0, 1, 2
+RULE_DELTA, RULE_ADDITIVE, RULE_INNER, RULE_DELTA_PV = 0, 1, 2, 3
 F32, BF16 = 0, 1
 PHI_ELU1 = 1 << 0
 LAMBDA_PER_CHANNEL = 1 << 1

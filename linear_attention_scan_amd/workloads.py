@@ -51,6 +51,7 @@ import numpy as np
 RULE_DELTA = 0
 RULE_ADDITIVE = 1
 RULE_INNER = 2
+RULE_DELTA_PV = 3
 PHI_IDENTITY = "identity"
 PHI_ELU1 = "elu1"
 
@@ -88,14 +89,15 @@ class ScanInputs:
     dk: int
     dv: int
     dtype: str               # 'bf16' or 'f32': the storage type of q, k, v and out
-    rule: int                # RULE_DELTA, RULE_ADDITIVE or RULE_INNER
+    rule: int                # RULE_DELTA, RULE_ADDITIVE, RULE_INNER or RULE_DELTA_PV
     phi: str                 # PHI_IDENTITY or PHI_ELU1
     per_channel: bool        # lambda is [B,H,T,dk] instead of [B,H,T]
     eps: float
     q: np.ndarray            # [B,H,T,dk]
     k: np.ndarray            # [B,H,T,dk]
     v: np.ndarray            # [B,H,T,dv]
-    beta: Optional[np.ndarray]   # [B,H,T] float32, or None (= 1, additive only)
+    beta: Optional[np.ndarray]   # [B,H,T] float32 ([B,H,T,dv] for RULE_DELTA_PV), or None
+                                 # (= 1, additive only)
     lam: Optional[np.ndarray]    # [B,H,T] or [B,H,T,dk] float32, or None
     S0: Optional[np.ndarray] = None        # [B,H,dk,dv] float32 or None (= 0)
     xprev0: Optional[np.ndarray] = None    # [B,H,dk] float32 or None
@@ -159,16 +161,17 @@ def make_scan(*, B, H, T, dk, dv, dtype="bf16", rule=RULE_DELTA, phi=PHI_IDENTIT
 
     beta_pre = lam_pre = beta_act = None
     lam_act = False
+    bshape = (B, H, T, dv) if rule == RULE_DELTA_PV else (B, H, T)
     if beta_kind == "sigmoid":
-        beta_pre = _normal(rng, (B, H, T))
+        beta_pre = _normal(rng, bshape)
         beta, beta_act = _sigmoid(beta_pre), "sigmoid"
     elif beta_kind == "two_sigmoid":
-        beta_pre = _normal(rng, (B, H, T))
+        beta_pre = _normal(rng, bshape)
         beta, beta_act = (2.0 * _sigmoid(beta_pre)).astype(np.float32), "sigmoid2"
     elif beta_kind == "one":
         beta = None
     else:
-        beta = np.full((B, H, T), float(beta_kind), dtype=np.float32)
+        beta = np.full(bshape, float(beta_kind), dtype=np.float32)
 
     lam_shape = (B, H, T, dk) if per_channel else (B, H, T)
     if lam_kind == "const":
@@ -246,6 +249,14 @@ def additive_znorm_bf16(seed=0, B=2, H=16, T=16384, d=128):
     return w
 
 
+def delta_pv_bf16_h16(seed=0, B=4, T=4096, d=128):
+    """The throughput workload's shape and distributions with one step size per value
+    channel (Falcon-2): beta = 2 sigmoid(N(0,1)) drawn per (token, value channel)."""
+    return make_scan(B=B, H=16, T=T, dk=d, dv=d, dtype="bf16", rule=RULE_DELTA_PV,
+                     beta_kind="two_sigmoid", lam_kind="softplus", lam_mu=-4.0, seed=seed,
+                     name="delta_pv_bf16_h16")
+
+
 def inner_f32_small(seed=0, T=256):
     return make_scan(B=1, H=1, T=T, dk=64, dv=64, dtype="f32", rule=RULE_INNER,
                      beta_kind="sigmoid", lam_kind="const", lam_const=0.01, seed=seed,
@@ -289,4 +300,5 @@ SCAN_WORKLOADS = {
     "delta_bf16_h16_qknorm": delta_bf16_h16_qknorm,
     "inner_f32_small": inner_f32_small,
     "additive_znorm_bf16": additive_znorm_bf16,
+    "delta_pv_bf16_h16": delta_pv_bf16_h16,
 }

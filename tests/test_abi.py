@@ -97,7 +97,11 @@ def _step(shp=None, md=None, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, lam=None, S_in=N
     (dict(out=None), F.EINVAL),
     (dict(beta=None), F.EINVAL),                      # delta rule needs beta
     (dict(beta=None, md=F.mode(rule=F.RULE_INNER)), F.EINVAL),  # so does the inner-product rule
-    (dict(md=F.mode(rule=3)), F.EINVAL),
+    (dict(md=F.mode(rule=4)), F.EINVAL),
+    # one step size per value channel takes a scalar ridge
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV, flags=F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(beta=None, md=F.mode(rule=F.RULE_DELTA_PV)), F.EINVAL),
+    (dict(beta=FAKE + 4, md=F.mode(rule=F.RULE_DELTA_PV)), F.EALIGN),
     (dict(md=F.mode(flags=F.QK_L2NORM | F.QK_RMSNORM)), F.EINVAL),
     (dict(md=F.mode(flags=F.QK_RMSNORM | F.PHI_ELU1)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.BETA_SIGMOID | F.BETA_SIGMOID2)), F.EINVAL),
@@ -148,6 +152,8 @@ def test_empty_batch_is_a_no_op():
     (dict(md=F.mode(rule=-1)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=1 << 12)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_DELTA, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV, flags=F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(beta=None, md=F.mode(rule=F.RULE_DELTA_PV)), F.EINVAL),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
     (dict(q=FAKE + 1), F.EALIGN),
     (dict(out=FAKE * 64 + 4), F.EALIGN),
