@@ -42,31 +42,31 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "prop_split_kernel"): {
         "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_scan_split.hip": "6bd7442b8699dc5763d11fb0a8e7a2d4820155cc72a7f7149007c955fe4be9f7",
+            "fwmem_scan_split.hip": "78fa1efc6d7f4a7da80b830304d9c1191d3fa6ba07a49bbac57339f58e7c2897",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
+            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
-        "fetch_kib": 150225.3, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150226.7, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
         "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_prep_split.hip": "80af25956854a86f4f4f219dd9685f7b9ff1b960af4bd656795ba918127b6573",
+            "fwmem_prep_split.hip": "3101a25cff5f80c14678715ef955e7813e5203414cf5f028e6a8e885c74a10f8",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
+            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
-        "fetch_kib": 66679.6, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66681.9, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("decode", "step_kernel"): {
         "sources": ("fwmem_step.hip", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_step.hip": "508e7f6083e8154860d36d8053a5dc5e51fc02fb4dd2b8f0b032a7cd4cd65270",
+            "fwmem_step.hip": "abf27317cda12cc5a31bfd56f61be55aedc5758d577a0abf5f1d25a096ca1990",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "42b62caaf20b84594273212dd8162bda91f8f2ad64bdeb8817f46492642cd3ce",
+            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
-        "fetch_kib": 267721.8, "write_kib": 532876.9, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267730.8, "write_kib": 532885.4, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
