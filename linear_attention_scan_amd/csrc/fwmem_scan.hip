@@ -150,6 +150,31 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     g_beta = p.beta != nullptr ? act_beta(p.beta[ti], p.flags) : 1.f;
     if (!PC && p.lam != nullptr) g_lam = act_lam(p.lam[ti], p.flags, R::nlms);
   }
+  // Per-channel lambda is loaded here too, so that its latency overlaps the row loads:
+  // the rows of [CH][DK] for the channel maximum in eta's denominator (lmx), and each
+  // channel's 64 tokens for the column pass (lamv, threads tid < DK).
+  constexpr int TPRL = DK / 4, RPPL = NT / TPRL, NPL = CH / RPPL;
+  f4 lmx[(R::nlms && PC) ? NPL : 1];
+  float lamv[PC ? CH : 1];
+  if constexpr (PC) {
+    if constexpr (R::nlms) {
+#pragma unroll
+      for (int ps = 0; ps < NPL; ++ps) {
+        const int tau = t0 + ps * RPPL + tid / TPRL;
+        const float m0 = lam_max_init(p.flags);
+        lmx[ps] = f4{m0, m0, m0, m0};
+        if (tau < p.T && p.lam != nullptr)
+          lmx[ps] = *reinterpret_cast<const f4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
+      }
+    }
+    if (tid < DK) {
+#pragma unroll
+      for (int t = 0; t < CH; ++t) {
+        const int tau = t0 + t;
+        lamv[t] = (tau < p.T && p.lam != nullptr) ? p.lam[(rowbase + tau) * DK + tid] : 0.f;
+      }
+    }
+  }
 
   // ---- row staging: x rows (shifted keys for the shifted pair) and q rows, phi
   // applied, scaled by one power of two per matrix, into LDS as MFMA operands.
@@ -218,17 +243,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   }
 
   // Per-channel: eta's denominator uses the channel max of lambda.
-  if (R::nlms && PC) {
-    constexpr int TPRL = DK / 4, RPPL = NT / TPRL, NPL = CH / RPPL;
+  if constexpr (R::nlms && PC) {
 #pragma unroll
     for (int ps = 0; ps < NPL; ++ps) {
       const int t = ps * RPPL + tid / TPRL;
-      const int tau = t0 + t;
-      float m = lam_max_init(p.flags);
-      if (tau < p.T && p.lam != nullptr) {
-        const f4 w = *reinterpret_cast<const f4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
-        m = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
-      }
+      const f4 w = lmx[ps];
+      float m = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
       m = group_max<TPRL>(m);
       // the activation is monotonic: the max of the activated values is the activated max
       if (tid % TPRL == 0) s_lam[t] = p.lam != nullptr ? act_lam(m, p.flags, true) : 0.f;
@@ -300,7 +320,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       for (int t = 0; t < CH; ++t) {
         const int tau = t0 + t;
         float lam = R::nlms ? 0.f : 1.f;
-        if (tau < p.T && p.lam != nullptr) lam = act_lam(p.lam[(rowbase + tau) * DK + i], p.flags, R::nlms);
+        if (tau < p.T && p.lam != nullptr) lam = act_lam(lamv[t], p.flags, R::nlms);
         const float a = R::nlms ? 1.f - s_eta[t] * lam : lam;
         gs += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;
@@ -669,6 +689,22 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   const int e0 = tid * EPT;            // T / M: this thread's elements
   u32x4 px[NPX], pq[NPASS], pv[NPV], pt[NVT], pm[NVT];
   f4 pf = {0.f, 0.f, 0.f, 0.f};
+  // Per-channel decay: thread (channel i, part) handles SEG consecutive tokens of its
+  // channel. Their raw lambdas for chunk c are loaded during chunk c-1 (software
+  // pipelined: consumed at the top of the column pass, then reloaded for the next chunk).
+  constexpr int TPC = NT / DK, SEG = CH / TPC;
+  float plam[PC ? SEG : 1];
+  auto load_lam = [&](int tbase) {
+    if constexpr (PC) {
+      const int i = tid % DK, tb = (tid / DK) * SEG;
+#pragma unroll
+      for (int u = 0; u < SEG; ++u) {
+        const int tau = tbase + tb + u;
+        plam[u] = (tau < p.T && p.lam != nullptr) ? p.lam[(rowbase + tau) * DK + i] : 0.f;
+      }
+    }
+  };
+  load_lam(0);
   float psX = 1.f, psQ = 1.f, pinvT = 1.f, pinvM = 1.f, pgC = 1.f;
   uint32_t valid = 0;
 
@@ -844,7 +880,6 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       // Each channel's 64 tokens are split over TPC threads; the segments' log-sums and
       // sign parities are combined through LDS into each segment's offset and the chunk
       // total. Gamma_prev of a token is Gamma of the one before, carried along.
-      constexpr int TPC = NT / DK, SEG = CH / TPC;
       static_assert(SEG <= 32, "segment parity fits 32 bits");
       const int i = tid % DK, part = tid / DK, tb = part * SEG;
       const int ip = Pol::kpos(i);
@@ -855,13 +890,14 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       for (int u = 0; u < SEG; ++u) {
         const int tau = t0 + tb + u;
         float lam = R::nlms ? 0.f : 1.f;
-        if (tau < p.T && p.lam != nullptr) lam = act_lam(p.lam[(rowbase + tau) * DK + i], p.flags, R::nlms);
+        if (tau < p.T && p.lam != nullptr) lam = act_lam(plam[u], p.flags, R::nlms);
         const float a = R::nlms ? 1.f - s_fV[tb + u] * lam : lam;
         gsum += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;
         gl[u] = gsum;
         pl |= pr << u;
       }
+      if (c + 1 < p.nchunks) load_lam(t0 + CH);
       s_pg[tid] = gsum;
       s_pp[tid] = pr;
       __syncthreads();
