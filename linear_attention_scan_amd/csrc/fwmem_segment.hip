@@ -81,68 +81,136 @@ __global__ __launch_bounds__(NTH) void seg_decay_kernel(SegParams s) {
   }
 }
 
-// S_start(p+1) = A_p S_start(p) + B_p (diagonal: Gamma_p S_start(p) + B_p, Gamma_p the
-// segment's last gam), serial over the segments of one head, for one
-// 16-column tile per workgroup (columns evolve independently). S_start(1) is segment 0's
-// final local state, which began at the caller's state. Writes S_start(p) for p >= 1,
-// and the final state, carried key and flag to the caller's state.
-__global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
+// C += A B for a 16x16x16 block on fp32 MFMA: lane (g, n) supplies A[n][4g..4g+3] and
+// B[4g+q][n] (the C layout of a previous product); MFMA q sums over K = 4g + q.
+__device__ __forceinline__ void mma_f32_block(f4& acc, const f4& a, const f4& b) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+}
+
+// Writes of the combine's last step: the caller's final state, carried key and flag.
+__device__ __forceinline__ void combine_final_extras(const SegParams& s, int h, int j0) {
+  if (j0 == 0) {
+    const size_t last = (size_t)h * s.P + s.P - 1;
+    if ((s.flags & kFlagZnorm) == 0)  // with the normaliser the slot holds z
+      for (int i = threadIdx.x; i < s.dk; i += NTH) s.xprev_out[(size_t)h * s.dk + i] = s.B1_x[last * s.dk + i];
+    if (threadIdx.x == 0) s.has_out[h] = 1;
+  }
+}
+
+// Diagonal transitions: S_start(p+1) = Gamma_p S_start(p) + B_p, Gamma_p the segment's last
+// gam; every element on its own, one thread per element of the 16-column tile.
+__device__ void combine_diagonal(const SegParams& s, int h, int j0) {
   const int dk = s.dk, dv = s.dv;
-  const int ntile = dv / 16;
-  const int h = blockIdx.x / ntile, j0 = (blockIdx.x % ntile) * 16;
-  __shared__ float cur[128 * 16];
   const int j = threadIdx.x & 15, i0 = threadIdx.x >> 4;  // rows i0, i0 + 16, ...
-  const int RP = dk / 16;                                  // rows per thread
+  const int RP = dk / 16;
   float v[8];
-  // S_start(1)
   const float* B0 = s.B1_S + (size_t)(h * s.P) * dk * dv;
-  for (int r = 0; r < RP; ++r) {
-    v[r] = B0[(size_t)(i0 + 16 * r) * dv + j0 + j];
-    cur[(i0 + 16 * r) * 16 + j] = v[r];
+  for (int r = 0; r < RP; ++r) v[r] = B0[(size_t)(i0 + 16 * r) * dv + j0 + j];
+  for (int p = 1; p < s.P; ++p) {
+    const size_t vh = (size_t)h * s.P + p;
+    float* St = s.S_start + vh * dk * dv;
+    const float* Bm = s.B1_S + vh * dk * dv;
+    const float gp = s.gam[vh * s.L + s.L - 1];
+    for (int r = 0; r < RP; ++r) {
+      St[(size_t)(i0 + 16 * r) * dv + j0 + j] = v[r];
+      v[r] = gp * v[r] + Bm[(size_t)(i0 + 16 * r) * dv + j0 + j];
+    }
+  }
+  if (s.S_out != nullptr) {
+    for (int r = 0; r < RP; ++r) s.S_out[((size_t)h * dk + i0 + 16 * r) * dv + j0 + j] = v[r];
+    combine_final_extras(s, h, j0);
+  }
+}
+
+// General transitions: S_start(p+1) = A_p S_start(p) + B_p, a [d_k x d_k] x [d_k x 16]
+// product per segment on fp32 MFMA. Wave w owns row tiles w, w + 4 of the tile in C layout;
+// the current start state goes through LDS so that every wave reads all of it as B
+// fragments.
+template <int DK>
+__device__ void combine_general(const SegParams& s, int h, int j0) {
+  constexpr int NRT = DK / 16, RPW = (NRT + 3) / 4;
+  __shared__ float cur[DK * 16];
+  const int dv = s.dv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  f4 v[RPW];
+  const float* B0 = s.B1_S + (size_t)(h * s.P) * DK * dv;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int rt = wave + 4 * r;
+    if (rt < NRT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[r][i] = B0[(size_t)(16 * rt + 4 * g + i) * dv + j0 + n];
+        cur[(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
+      }
+    }
   }
   __syncthreads();
   for (int p = 1; p < s.P; ++p) {
     const size_t vh = (size_t)h * s.P + p;
-    float* St = s.S_start + vh * dk * dv;
-    for (int r = 0; r < RP; ++r) St[(size_t)(i0 + 16 * r) * dv + j0 + j] = v[r];
-    const float* Bm = s.B1_S + vh * dk * dv;
-    float nv[8];
-    if (s.diag) {
-      const float gp = s.gam[vh * s.L + s.L - 1];
-      for (int r = 0; r < RP; ++r) nv[r] = gp * v[r] + Bm[(size_t)(i0 + 16 * r) * dv + j0 + j];
-      for (int r = 0; r < RP; ++r) v[r] = nv[r];
-      continue;  // no exchange through LDS
-    }
-    const float* A = s.A1_S + vh * dk * dk;
-    for (int r = 0; r < RP; ++r) {
-      const int i = i0 + 16 * r;
-      const f4* Ar = reinterpret_cast<const f4*>(A + (size_t)i * dk);
-      float acc0 = 0.f, acc1 = 0.f;
-      for (int k4 = 0; k4 < dk / 4; ++k4) {
-        const f4 a = Ar[k4];
-        acc0 += a[0] * cur[(4 * k4) * 16 + j];
-        acc1 += a[1] * cur[(4 * k4 + 1) * 16 + j];
-        acc0 += a[2] * cur[(4 * k4 + 2) * 16 + j];
-        acc1 += a[3] * cur[(4 * k4 + 3) * 16 + j];
+    float* St = s.S_start + vh * DK * dv;
+    const float* A = s.A1_S + vh * DK * DK;
+    const float* Bm = s.B1_S + vh * DK * dv;
+    f4 bfr[NRT];
+#pragma unroll
+    for (int kb = 0; kb < NRT; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bfr[kb][q] = cur[(16 * kb + 4 * g + q) * 16 + n];
+    f4 nv[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int rt = wave + 4 * r;
+      if (rt < NRT) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb) {
+          const f4 a = *reinterpret_cast<const f4*>(A + (size_t)(16 * rt + n) * DK + 16 * kb + 4 * g);
+          mma_f32_block(acc, a, bfr[kb]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t e = (size_t)(16 * rt + 4 * g + i) * dv + j0 + n;
+          St[e] = v[r][i];
+          nv[r][i] = acc[i] + Bm[e];
+        }
       }
-      nv[r] = acc0 + acc1 + Bm[(size_t)i * dv + j0 + j];
     }
-    __syncthreads();  // every thread has read cur
-    for (int r = 0; r < RP; ++r) {
-      v[r] = nv[r];
-      cur[(i0 + 16 * r) * 16 + j] = v[r];
+    __syncthreads();  // every wave has read cur
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int rt = wave + 4 * r;
+      if (rt < NRT) {
+        v[r] = nv[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
+      }
     }
     __syncthreads();
   }
   if (s.S_out != nullptr) {
-    for (int r = 0; r < RP; ++r) s.S_out[((size_t)h * dk + i0 + 16 * r) * dv + j0 + j] = v[r];
-    if (j0 == 0) {
-      const size_t last = (size_t)h * s.P + s.P - 1;
-      if ((s.flags & kFlagZnorm) == 0)  // with the normaliser the slot holds z
-        for (int i = threadIdx.x; i < dk; i += NTH) s.xprev_out[(size_t)h * dk + i] = s.B1_x[last * dk + i];
-      if (threadIdx.x == 0) s.has_out[h] = 1;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int rt = wave + 4 * r;
+      if (rt < NRT)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.S_out[((size_t)h * DK + 16 * rt + 4 * g + i) * dv + j0 + n] = v[r][i];
     }
+    combine_final_extras(s, h, j0);
   }
+}
+
+// S_start(p+1) = A_p S_start(p) + B_p, serial over the segments of one head, for one
+// 16-column tile per workgroup (columns evolve independently). S_start(1) is segment 0's
+// final local state, which began at the caller's state. Writes S_start(p) for p >= 1, and
+// the final state, carried key and flag to the caller's state.
+__global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
+  const int ntile = s.dv / 16;
+  const int h = blockIdx.x / ntile, j0 = (blockIdx.x % ntile) * 16;
+  if (s.diag) combine_diagonal(s, h, j0);
+  else if (s.dk == 64) combine_general<64>(s, h, j0);
+  else combine_general<128>(s, h, j0);
 }
 
 // out[vh, t, :] += S_start(vh)^T z_t for segments p >= 1, a [64 x dk] x [dk x dv] product
