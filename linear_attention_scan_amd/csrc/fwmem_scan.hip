@@ -151,11 +151,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     if (!PC && p.lam != nullptr) g_lam = act_lam(p.lam[ti], p.flags, R::nlms);
   }
   // Per-channel lambda is loaded here too, so that its latency overlaps the row loads:
-  // the rows of [CH][DK] for the channel maximum in eta's denominator (lmx), and each
-  // channel's 64 tokens for the column pass (lamv, threads tid < DK).
+  // the rows of [CH][DK] for the channel maximum in eta's denominator (lmx), and the
+  // column pass's share (lamv: channel tid % DK, SEGP tokens from (tid / DK) * SEGP).
   constexpr int TPRL = DK / 4, RPPL = NT / TPRL, NPL = CH / RPPL;
+  constexpr int TPP = NT / DK, SEGP = CH / TPP;  // column pass: threads per channel, tokens each
+  static_assert(SEGP <= 32, "segment parity fits 32 bits");
   f4 lmx[(R::nlms && PC) ? NPL : 1];
-  float lamv[PC ? CH : 1];
+  float lamv[PC ? SEGP : 1];
   if constexpr (PC) {
     if constexpr (R::nlms) {
 #pragma unroll
@@ -167,11 +169,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
           lmx[ps] = *reinterpret_cast<const f4*>(p.lam + (rowbase + tau) * DK + (tid % TPRL) * 4);
       }
     }
-    if (tid < DK) {
+    {
+      const int tb = (tid / DK) * SEGP;
 #pragma unroll
-      for (int t = 0; t < CH; ++t) {
-        const int tau = t0 + t;
-        lamv[t] = (tau < p.T && p.lam != nullptr) ? p.lam[(rowbase + tau) * DK + tid] : 0.f;
+      for (int u = 0; u < SEGP; ++u) {
+        const int tau = t0 + tb + u;
+        lamv[u] = (tau < p.T && p.lam != nullptr) ? p.lam[(rowbase + tau) * DK + tid % DK] : 0.f;
       }
     }
   }
@@ -301,72 +304,106 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   float* Ysc = reinterpret_cast<float*>(reg[1]);  // after the Gram, Q is dead
 
   if (PC) {
-    // Column pass, one thread per key channel: Gamma ratios per channel, anchored
-    // at the chunk midpoint so the two factors of Gamma_{t-1}/Gamma_s stay in range.
-    // BX and AM overwrite the raw X and Q in place (each element is read and
-    // written by the same thread); AL goes to region 2.
+    // Column pass: Gamma ratios per channel, anchored at the chunk midpoint so the two
+    // factors of Gamma_{t-1}/Gamma_s stay in range. Each channel's 64 tokens are split over
+    // TPP threads (SEGP consecutive tokens each); the segments' log-sums and sign
+    // parities meet in region 3 (unused until the Gram products) to give each thread its
+    // offset and the anchor. With e_t = exp(g_t - g_A) and s_t its sign, the operands
+    // take AM = s_t e_t q, BX = s_t / e_t x and AL = s_{t-1} e_{t-1} x (e_{-1} = exp(-g_A)).
+    // BX and AM overwrite the raw X and Q in place (each element is read and written by
+    // the same thread); AL goes to region 2.
     op_t* AL = reinterpret_cast<op_t*>(reg[2]);
     op_t* BX = Xs;
     op_t* AM = Qs;
-    float gcol[CH];
-    uint64_t par = 0;
-    float mAL = 0.f, mBX = 0.f, mAM = 0.f;
-    const int i = tid;
+    float* x_tot = reinterpret_cast<float*>(reg[3]);           // [NT] segment log-sums
+    uint32_t* x_par = reinterpret_cast<uint32_t*>(x_tot + NT);  // [NT] segment parities
+    float* x_anc = reinterpret_cast<float*>(x_par + NT);        // [DK] anchor, in-segment part
+    uint32_t* x_apr = reinterpret_cast<uint32_t*>(x_anc + DK);  // [DK]
+    constexpr int TA = CH / 2 - 1;
+    const int i = tid % DK, part = tid / DK, tb = part * SEGP;
     const int ip = Pol::kpos(i);
-    if (i < DK) {
+    float ev[SEGP];
+    uint32_t pl = 0, pr = 0;
+    {
       float gs = 0.f;
-      uint32_t pr = 0;
 #pragma unroll
-      for (int t = 0; t < CH; ++t) {
-        const int tau = t0 + t;
+      for (int u = 0; u < SEGP; ++u) {
+        const int t = tb + u, tau = t0 + t;
         float lam = R::nlms ? 0.f : 1.f;
-        if (tau < p.T && p.lam != nullptr) lam = act_lam(lamv[t], p.flags, R::nlms);
+        if (tau < p.T && p.lam != nullptr) lam = act_lam(lamv[u], p.flags, R::nlms);
         const float a = R::nlms ? 1.f - s_eta[t] * lam : lam;
         gs += log_abs_floor(a);
         pr ^= (a < 0.f) ? 1u : 0u;
-        gcol[t] = gs;
-        par |= (uint64_t)pr << t;
+        ev[u] = gs;  // in-segment prefix for now
+        pl |= pr << u;
+        if (t == TA) {
+          x_anc[i] = gs;
+          x_apr[i] = pr;
+        }
       }
+      x_tot[tid] = gs;
+      x_par[tid] = pr;
     }
-    constexpr int TA = CH / 2 - 1;
-    // Two passes: the first finds the block maxima (for the fp16 scales), the
-    // second writes the scaled operands.
+    __syncthreads();
+    float off = 0.f, anc;
+    uint32_t poff = 0, apr;
+    {
+      constexpr int partA = TA / SEGP;
+      float aoff = 0.f;
+      uint32_t apoff = 0;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+      for (int w = 0; w < TPP; ++w) {
+        const float gw = x_tot[w * DK + i];
+        const uint32_t pw = x_par[w * DK + i];
+        if (w < part) {
+          off += gw;
+          poff ^= pw;
+        }
+        if (w < partA) {
+          aoff += gw;
+          apoff ^= pw;
+        }
+      }
+      anc = aoff + x_anc[i];
+      apr = apoff ^ x_apr[i];
+    }
+    // e_t and its sign (bit u of esg), then the block maxima (for the fp16 scales)
+    uint32_t esg = 0;
+    float eprev = __expf(off - anc);
+    const uint32_t sprev0 = poff ^ apr;
+    float mAL = 0.f, mBX = 0.f, mAM = 0.f;
+#pragma unroll
+    for (int u = 0; u < SEGP; ++u) {
+      const int t = tb + u;
+      ev[u] = __expf(off + ev[u] - anc);
+      esg |= (poff ^ ((pl >> u) & 1u) ^ apr) << u;
+      const float xh = (float)Xs[t * LDX + ip];
+      const float qh = (float)Qs[t * LDX + ip];
+      const float ep = u ? ev[u - 1] : eprev;
+      mAL = fmaxf(mAL, fabsf(xh * ep));
+      mBX = fmaxf(mBX, fabsf(xh / ev[u]));
+      mAM = fmaxf(mAM, fabsf(qh * ev[u]));
+    }
+    {
       float sAL = 1.f, sBX = 1.f, sAM = 1.f;
-      if (pass == 1 && Pol::kScaled) {
+      if (Pol::kScaled) {
         sAL = pow2_scale(block_max(mAL, s_red));
         sBX = pow2_scale(block_max(mBX, s_red + NW));
         sAM = pow2_scale(block_max(mAM, s_red + 2 * NW));
       }
-      if (pass == 1) {
-        invL = 1.f / (sX * sAL * sX * sBX);
-        invM = 1.f / (sQ * sAM * sX * sBX);
-      }
-      if (i < DK) {
-        const float anc = gcol[TA];
-        const uint32_t apr = (uint32_t)(par >> TA) & 1u;
+      invL = 1.f / (sX * sAL * sX * sBX);
+      invM = 1.f / (sQ * sAM * sX * sBX);
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          const float xh = (float)Xs[t * LDX + ip];
-          const float qh = (float)Qs[t * LDX + ip];
-          const float gprev = t ? gcol[t - 1] : 0.f;
-          const uint32_t pprev = t ? (uint32_t)(par >> (t - 1)) & 1u : 0u;
-          const uint32_t pcur = (uint32_t)(par >> t) & 1u;
-          const float fAL = ((pprev ^ apr) ? -1.f : 1.f) * __expf(gprev - anc);
-          const float fBX = ((pcur ^ apr) ? -1.f : 1.f) * __expf(anc - gcol[t]);
-          const float fAM = ((pcur ^ apr) ? -1.f : 1.f) * __expf(gcol[t] - anc);
-          const float vAL = xh * fAL, vBX = xh * fBX, vAM = qh * fAM;
-          if (pass == 0) {
-            mAL = fmaxf(mAL, fabsf(vAL));
-            mBX = fmaxf(mBX, fabsf(vBX));
-            mAM = fmaxf(mAM, fabsf(vAM));
-          } else {
-            if (R::solve) AL[t * LDX + ip] = Pol::cvt(vAL * sAL);
-            BX[t * LDX + ip] = Pol::cvt(vBX * sBX);
-            AM[t * LDX + ip] = Pol::cvt(vAM * sAM);
-          }
-        }
+      for (int u = 0; u < SEGP; ++u) {
+        const int t = tb + u;
+        const float xh = (float)Xs[t * LDX + ip];
+        const float qh = (float)Qs[t * LDX + ip];
+        const float sc = ((esg >> u) & 1u) ? -1.f : 1.f;
+        const float scp = u ? (((esg >> (u - 1)) & 1u) ? -1.f : 1.f) : (sprev0 ? -1.f : 1.f);
+        const float ep = u ? ev[u - 1] : eprev;
+        if (R::solve) AL[t * LDX + ip] = Pol::cvt(xh * scp * ep * sAL);
+        BX[t * LDX + ip] = Pol::cvt(xh * sc / ev[u] * sBX);
+        AM[t * LDX + ip] = Pol::cvt(qh * sc * ev[u] * sAM);
       }
     }
     __syncthreads();
