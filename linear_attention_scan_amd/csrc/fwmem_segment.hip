@@ -220,7 +220,7 @@ __global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
 // 16 NTW (w + 1) - 1 and keeps their S_start fragments in registers across the tiles.
 // Diagonal transitions: z_t = gam_t phi(q~_t), formed here from the queries (feature map
 // and QK normalisation as in the scan); the row factor is applied to the product.
-constexpr int kFixTiles = 8;
+constexpr int kFixTiles = 2;
 
 __device__ __forceinline__ void load_row8(const uint16_t* p, float (&x)[8]) { In<uint16_t>::load(p, x); }
 __device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
