@@ -10,16 +10,32 @@ namespace fwmem {
 namespace {
 
 // z at the entry of every chunk, serially over the chunks of one head (one channel per
-// thread); the final z goes to the state's carried slot.
+// thread); the final z goes to the state's carried slot. The chunk terms are loaded eight
+// chunks ahead of the dependent updates.
 __global__ __launch_bounds__(128) void zchain_kernel(ZParams z) {
   const int bh = blockIdx.x, i = threadIdx.x;
   if (i >= z.dk) return;
   const size_t nf = zrec_floats(z.dk);
+  const float* rec = z.zrec + (size_t)bh * z.nchunks * nf;
+  float* zc = z.zc + (size_t)bh * z.nchunks * z.dk;
   float zi = z.z_in != nullptr ? z.z_in[(size_t)bh * z.dk + i] : 0.f;
-  for (int c = 0; c < z.nchunks; ++c) {
-    const float* r = z.zrec + ((size_t)bh * z.nchunks + c) * nf;
-    z.zc[((size_t)bh * z.nchunks + c) * z.dk + i] = zi;
-    zi = r[128] * zi + r[132 + i];
+  constexpr int U = 8;
+  for (int c0 = 0; c0 < z.nchunks; c0 += U) {
+    float a[U], w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      a[u] = c < z.nchunks ? rec[(size_t)c * nf + 128] : 1.f;
+      w[u] = c < z.nchunks ? rec[(size_t)c * nf + 132 + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      if (c < z.nchunks) {
+        zc[(size_t)c * z.dk + i] = zi;
+        zi = a[u] * zi + w[u];
+      }
+    }
   }
   if (z.z_out != nullptr) {
     z.z_out[(size_t)bh * z.dk + i] = zi;
@@ -27,32 +43,41 @@ __global__ __launch_bounds__(128) void zchain_kernel(ZParams z) {
   }
 }
 
-// out[t, :] /= den_in[t] + gq[t] (phi(q_t) . z_c) + eps for 64 tokens of one head per
-// workgroup; four threads per token.
+// out[t, :] /= den_in[t] + gq[t] (phi(q_t) . z_c) + eps for the 64 tokens of one chunk per
+// workgroup: 16 lanes per token row, so that q and out move in 16-byte pieces along the
+// row (four rows per wave instruction).
 template <typename InT>
 __global__ __launch_bounds__(256) void zfinal_kernel(ZParams z) {
+  constexpr int VW = In<InT>::VW;
   const int bh = blockIdx.x / z.nchunks, c = blockIdx.x % z.nchunks;
-  const int tl = threadIdx.x >> 2, part = threadIdx.x & 3;
-  const int t = c * 64 + tl;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> 4, l16 = lane & 15;
   const bool elu = (z.flags & kFlagPhiElu1) != 0;
   const size_t nf = zrec_floats(z.dk);
   const float* r = z.zrec + ((size_t)bh * z.nchunks + c) * nf;
   const float* zc = z.zc + ((size_t)bh * z.nchunks + c) * z.dk;
-  float dot = 0.f;
-  if (t < z.T) {
-    const InT* qr = static_cast<const InT*>(z.q) + ((size_t)bh * z.T + t) * z.dk;
-    for (int i = part; i < z.dk; i += 4) {
-      float q = In<InT>::load1(qr + i);
-      if (elu) q = phi_elu1(q);
-      dot += q * zc[i];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int tl = wave * 16 + rr * 4 + sub;  // token within the chunk
+    const int t = c * 64 + tl;
+    float dot = 0.f;
+    if (t < z.T) {
+      const InT* qr = static_cast<const InT*>(z.q) + ((size_t)bh * z.T + t) * z.dk;
+      for (int i0 = l16 * VW; i0 < z.dk; i0 += 16 * VW) {
+        float q[VW];
+        In<InT>::load(qr + i0, q);
+#pragma unroll
+        for (int j = 0; j < VW; ++j) dot += (elu ? phi_elu1(q[j]) : q[j]) * zc[i0 + j];
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o);
+    if (t < z.T) {
+      const float inv = 1.f / (r[tl] + r[64 + tl] * dot + z.eps);
+      f4* orow = reinterpret_cast<f4*>(z.out + ((size_t)bh * z.T + t) * z.dv);
+      for (int j4 = l16; j4 < z.dv / 4; j4 += 16) orow[j4] = orow[j4] * inv;
     }
   }
-  dot += __shfl_xor(dot, 1);
-  dot += __shfl_xor(dot, 2);
-  if (t >= z.T) return;
-  const float inv = 1.f / (r[tl] + r[64 + tl] * dot + z.eps);
-  float* o = z.out + ((size_t)bh * z.T + t) * z.dv;
-  for (int j = part; j < z.dv; j += 4) o[j] *= inv;
 }
 
 }  // namespace
