@@ -44,6 +44,9 @@ Readings where the pages leave a step open (listed in the design doc as D1..D14):
   D20 per-value-channel rule (Falcon-2): beta is [B,H,T,d_v], lambda a scalar per token;
       channel j steps by eta_{j,t} = beta_{j,t} / (|x_t|^2 + lambda_t + eps) and decays
       its own column of S by 1 - eta_{j,t} lambda_t; shifted pair and boundary as D2.
+  D21 backward pass (scan_backward): the pages give none; gradients are the reverse-mode
+      derivative of the recurrence as the forward pass states it, with lambda-hat's
+      maximum passing its gradient to the first channel attaining it.
   D15 inner-product rule: the delta rule's shifted pair, eta_t (with D1 for a
       per-channel lambda), decay 1 - eta_t lambda_t and boundary D2; beta is
       required as for the delta rule.
@@ -256,6 +259,154 @@ def step(q, k, v, beta, lam, *, rule, phi_kind="identity", eps=1e-6, per_channel
                        per_channel=per_channel, S0=S0, xprev0=xprev0, has0=has0, qk_norm=qk_norm,
                        beta_act=beta_act, lam_act=lam_act, znorm=znorm, lam_scaled=lam_scaled)
     return o[:, :, 0], S, xp, h
+
+
+def phi_grad(x: np.ndarray, kind: str) -> np.ndarray:
+    """Derivative of the feature map: 1 for the identity; for elu+1, 1 where x > 0 and
+    exp(x) elsewhere."""
+    x = np.asarray(x, dtype=np.float64)
+    if kind == "identity":
+        return np.ones_like(x)
+    if kind == "elu1":
+        return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    raise ValueError(kind)
+
+
+def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
+                  per_channel=False, S0=None, xprev0=None, has0=None):
+    """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
+    for the delta, additive and inner rules with phi identity or elu+1, scalar or
+    per-channel lambda (reading D21: the pages give no backward pass).
+
+    Reverse-mode differentiation of the token recurrence, one head at a time: the forward
+    steps are rerun keeping each step's state and scalars, then undone from the last
+    token to the first, each applying the chain rule to its own formulas
+    (S_t = a_t S_{t-1} + eta_t x_t r_t^T with r_t = v_t - S_{t-1}^T x_t, a_t = 1 - eta_t lambda_t,
+    eta_t = beta_t / (|x_t|^2 + lambda-hat_t + eps); the additive write gamma_t S_{t-1} +
+    beta_t phi(k_t) v_t^T; the read o_t = S_t^T phi(q_t)). lambda-hat's maximum passes its
+    gradient to the first channel attaining it.
+
+    Returns a dict with the gradients "q", "k", "v", "beta", "lam" (None where the input
+    is None), "S0" [B,H,dk,dv] and "xprev0" [B,H,dk], in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    N = B * H
+    Q, K, V = _heads(q, 2), _heads(k, 2), _heads(v, 2)
+    Bt = None if beta is None else _heads(beta, 1)
+    Lm = None if lam is None else _heads(lam, 2 if per_channel else 1)
+    dOh = _heads(dO, 2)
+    dSh = np.zeros((N, dk, dv)) if dS is None else _heads(dS, 2)
+    S_init = np.zeros((N, dk, dv)) if S0 is None else _heads(S0, 2)
+    x_init = np.zeros((N, dk)) if xprev0 is None else _heads(xprev0, 1)
+    h_init = np.zeros(N, dtype=bool) if has0 is None else (np.asarray(has0).reshape(N) != 0)
+    shifted = rule in (RULE_DELTA, RULE_INNER)
+    if not shifted and rule != RULE_ADDITIVE:
+        raise ValueError(rule)
+
+    g = {name: np.zeros_like(a) for name, a in (("q", Q), ("k", K), ("v", V))}
+    g["beta"] = None if Bt is None else np.zeros_like(Bt)
+    g["lam"] = None if Lm is None else np.zeros_like(Lm)
+    g["S0"] = np.zeros((N, dk, dv))
+    g["xprev0"] = np.zeros((N, dk))
+
+    for n in range(N):
+        # forward, keeping what each step's backward needs
+        Sc, xp, hs = S_init[n].copy(), x_init[n].copy(), bool(h_init[n])
+        steps = []
+        for t in range(T):
+            qf, kf, vt = phi(Q[n, t], phi_kind), phi(K[n, t], phi_kind), V[n, t]
+            Sp = Sc
+            if shifted:
+                if not hs:
+                    steps.append(None)          # no key yet: the step neither decays nor writes
+                    Sc = Sp
+                else:
+                    x = xp
+                    if Lm is None:
+                        lt, lhat, imax = 0.0, 0.0, None
+                    elif per_channel:
+                        lt = Lm[n, t]
+                        imax = int(np.argmax(lt))
+                        lhat = lt[imax]
+                    else:
+                        lt, lhat, imax = Lm[n, t], Lm[n, t], None
+                    den = x @ x + lhat + eps
+                    eta = Bt[n, t] / den
+                    a = 1.0 - eta * lt
+                    decay = a[:, None] if per_channel else a
+                    r = vt - Sp.T @ x if rule == RULE_DELTA else vt
+                    Sc = decay * Sp + eta * np.outer(x, r)
+                    steps.append((Sp, x, eta, a, den, lt, imax, r))
+            else:
+                gam = 1.0 if Lm is None else Lm[n, t]
+                b = 1.0 if Bt is None else Bt[n, t]
+                decay = gam[:, None] if per_channel else gam
+                Sc = decay * Sp + b * np.outer(kf, vt)
+                steps.append((Sp, gam, b, kf))
+            steps[-1] = (steps[-1], Sc, qf)
+            xp, hs = kf, True
+
+        # backward: G holds dL/dS_t while step t is undone
+        G = dSh[n].copy()
+        for t in range(T - 1, -1, -1):
+            rec, St, qf = steps[t]
+            g["q"][n, t] += (St @ dOh[n, t]) * phi_grad(Q[n, t], phi_kind)
+            G = G + np.outer(qf, dOh[n, t])
+            if shifted:
+                if rec is None:
+                    continue                    # S_t = S_{t-1}
+                Sp, x, eta, a, den, lt, imax, r = rec
+                da = np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
+                if rule == RULE_DELTA:
+                    deta = x @ G @ r
+                    dr = eta * (G.T @ x)
+                    dx = eta * (G @ r) - Sp @ dr
+                    g["v"][n, t] += dr
+                    G_prev = (a[:, None] if per_channel else a) * G - np.outer(x, dr)
+                else:
+                    deta = x @ G @ V[n, t]
+                    dx = eta * (G @ V[n, t])
+                    g["v"][n, t] += eta * (G.T @ x)
+                    G_prev = (a[:, None] if per_channel else a) * G
+                # a = 1 - eta lambda
+                deta = deta - (np.sum(lt * da) if per_channel else lt * da)
+                dlt = -eta * da
+                # eta = beta / den, den = |x|^2 + lambda-hat + eps
+                g["beta"][n, t] += deta / den
+                dden = -eta * deta / den
+                dx = dx + 2.0 * x * dden
+                if Lm is not None:
+                    if per_channel:
+                        dlt = dlt.copy()
+                        dlt[imax] += dden
+                    else:
+                        dlt = dlt + dden
+                    g["lam"][n, t] += dlt
+                # x_t = phi(k_{t-1}), or the carried key for the sequence's first token
+                if t >= 1:
+                    g["k"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)
+                else:
+                    g["xprev0"][n] += dx
+                G = G_prev
+            else:
+                Sp, gam, b, kf = rec
+                if Lm is not None:
+                    g["lam"][n, t] += np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
+                if Bt is not None:
+                    g["beta"][n, t] += kf @ G @ V[n, t]
+                g["k"][n, t] += b * (G @ V[n, t]) * phi_grad(K[n, t], phi_kind)
+                g["v"][n, t] += b * (G.T @ kf)
+                G = (gam[:, None] if per_channel else gam) * G
+        g["S0"][n] = G
+
+    shapes = {"q": (B, H, T, dk), "k": (B, H, T, dk), "v": (B, H, T, dv),
+              "S0": (B, H, dk, dv), "xprev0": (B, H, dk)}
+    out = {name: g[name].reshape(shp) for name, shp in shapes.items()}
+    out["beta"] = None if g["beta"] is None else g["beta"].reshape(np.asarray(beta).shape)
+    out["lam"] = None if g["lam"] is None else g["lam"].reshape(np.asarray(lam).shape)
+    return out
 
 
 def relerr(x, ref) -> float:

@@ -738,6 +738,67 @@ def pin_p23_per_value_channel_rule(orc):
     np.testing.assert_allclose(o[0, 0], [[3.0, 4.0], [1 / 3, 26 / 15]], rtol=1e-14)
 
 
+def pin_p24_backward(orc):
+    """The backward pass (reading D21) against the forward oracle and closed forms.
+    (a) Central finite differences (h = 1e-6) of L = sum(dO o) + sum(dS S_T) match every
+        gradient (q, k, v, beta, lambda, S0, the carried key) for the delta, inner and
+        additive rules, scalar and per-channel lambda, phi identity and elu+1, from a
+        nonzero state with a carried key.
+    (b) Linear attention (additive, gamma = beta = 1, S0 = 0, identity): brute-force sums
+        dv_j = sum_{t>=j} (q_t . k_j) dO_t, dq_t = sum_{j<=t} k_j (v_j . dO_t),
+        dk_j = sum_{t>=j} q_t (v_j . dO_t).
+    (c) The delta rule's first token at a sequence start writes nothing, so the gradients of
+        its beta and lambda are exactly zero."""
+    rng = np.random.default_rng(42)
+    T, dk, dv = 5, 3, 2
+    for rule in (DELTA, INNER, ADD):
+        for per_channel in (False, True):
+            for phi_kind in ("identity", "elu1"):
+                q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+                v = rng.standard_normal((1, 1, T, dv))
+                lshape = (1, 1, T, dk) if per_channel else (1, 1, T)
+                if rule == ADD:
+                    b, lam = rng.uniform(0.2, 1.5, (1, 1, T)), rng.uniform(0.6, 1.0, lshape)
+                else:
+                    b, lam = rng.uniform(0.2, 1.5, (1, 1, T)), rng.uniform(0.05, 0.5, lshape)
+                dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+                S0, x0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
+                h0 = np.array([[1]])
+                kw = dict(rule=rule, phi_kind=phi_kind, per_channel=per_channel, has0=h0)
+                args = {"q": q, "k": k, "v": v, "beta": b, "lam": lam, "S0": S0, "xprev0": x0}
+
+                def loss(a):
+                    o, S, _, _ = orc.scan(a["q"], a["k"], a["v"], a["beta"], a["lam"], S0=a["S0"],
+                                          xprev0=a["xprev0"], **kw)
+                    return float(np.sum(o * dO) + np.sum(S * dS))
+
+                gr = orc.scan_backward(q, k, v, b, lam, dO, dS, S0=S0, xprev0=x0, **kw)
+                for name, arr in args.items():
+                    for idx in np.ndindex(arr.shape):
+                        a = dict(args)
+                        ap, am = arr.copy(), arr.copy()
+                        ap[idx] += 1e-6
+                        am[idx] -= 1e-6
+                        a[name] = ap
+                        fp = loss(a)
+                        a[name] = am
+                        fd = (fp - loss(a)) / 2e-6
+                        an = gr[name][idx]
+                        assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, per_channel, phi_kind, name, idx, fd, an)
+    q, k = rng.standard_normal((1, 1, 6, 4)), rng.standard_normal((1, 1, 6, 4))
+    v, dO = rng.standard_normal((1, 1, 6, 3)), rng.standard_normal((1, 1, 6, 3))
+    gr = orc.scan_backward(q, k, v, None, None, dO, rule=ADD)
+    Q, K, V, D = q[0, 0], k[0, 0], v[0, 0], dO[0, 0]
+    for j in range(6):
+        np.testing.assert_allclose(gr["v"][0, 0, j], sum((Q[t] @ K[j]) * D[t] for t in range(j, 6)), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(gr["k"][0, 0, j], sum(Q[t] * (V[j] @ D[t]) for t in range(j, 6)), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(gr["q"][0, 0, j], sum(K[i] * (V[i] @ D[j]) for i in range(j + 1)), rtol=1e-12, atol=1e-12)
+    b, lam = rng.uniform(0.2, 1.5, (1, 1, 6)), rng.uniform(0.05, 0.5, (1, 1, 6))
+    gr = orc.scan_backward(q, k, v, b, lam, dO, rng.standard_normal((1, 1, 4, 3)), rule=DELTA,
+                           S0=rng.standard_normal((1, 1, 4, 3)))
+    assert gr["beta"][0, 0, 0] == 0.0 and gr["lam"][0, 0, 0] == 0.0
+
+
 ALL_PINS = [
     pin_p1_outer_product_store,
     pin_p2_quadratic_form,
@@ -765,5 +826,6 @@ ALL_PINS = [
     pin_p21_normalised_linear_attention,
     pin_p22_scale_coupled_ridge,
     pin_p23_per_value_channel_rule,
+    pin_p24_backward,
     pin_relerr_metric,
 ]

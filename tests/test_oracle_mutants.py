@@ -48,6 +48,15 @@ MUTANTS = {
     "retention_uses_softplus": ("Lm = sigmoid(Lm) if rule == RULE_ADDITIVE else softplus(Lm)",
                                 "Lm = softplus(Lm)"),
     "beta_range_one": ('Bt = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act] * sigmoid(Bt)', "Bt = sigmoid(Bt)"),
+    "bwd_no_residual_state_term": ("G_prev = (a[:, None] if per_channel else a) * G - np.outer(x, dr)",
+                                   "G_prev = (a[:, None] if per_channel else a) * G"),
+    "bwd_den_sign": ("dden = -eta * deta / den", "dden = eta * deta / den"),
+    "bwd_no_phi_grad_on_shifted_key": ("g[\"k\"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)",
+                                       "g[\"k\"][n, t - 1] += dx"),
+    "bwd_same_index_key": ("g[\"k\"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)",
+                           "g[\"k\"][n, t] += dx * phi_grad(K[n, t], phi_kind)"),
+    "bwd_lambda_hat_not_routed": ("                        dlt[imax] += dden\n", ""),
+    "bwd_read_after_undo": ("            G = G + np.outer(qf, dOh[n, t])\n", ""),
     "pv_shared_step": ("Bt[:, t, :] / np.where(has, den_pv, 1.0)[:, None]",
                        "Bt[:, t, :1] / np.where(has, den_pv, 1.0)[:, None] + 0.0 * Bt[:, t, :]"),
     "pv_decay_on_rows": ("(1.0 - eta_pv * lam_pv[:, None])[:, None, :] * S",
