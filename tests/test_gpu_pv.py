@@ -124,3 +124,39 @@ def test_pv_decode_sequence(dtype, dk, dv):
     say(f"    err(o)={eo:.3e} err(S)={eS:.3e}")
     assert eo <= TOL["f32"] and eS <= TOL["f32"]
     assert np.all(h == 1)
+
+
+@pytest.mark.parametrize("T", [63, 64, 65, 129])
+def test_pv_chunk_boundaries(T):
+    check_scan(_pv(B=1, H=2, T=T, seed=10 + T))
+
+
+def test_pv_out_bf16_is_rounded_fp32():
+    """bf16 outputs are the fp32 outputs rounded to nearest even."""
+    import torch
+    w = _pv(B=1, H=2, T=200, seed=20)
+    o32, _ = gpu_scan(w)
+    o16, _ = gpu_scan(w, extra_flags=F.OUT_BF16)
+    ref = torch.from_numpy(o32.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(o16, ref.astype(np.float64))
+
+
+def test_pv_scan_then_decode():
+    """A scan's final state continues in decode steps, against the oracle over the whole
+    sequence."""
+    import torch
+    w = _pv(B=1, H=2, T=130, seed=21)
+    say("[pv] scan of 127 tokens, then 3 decode steps")
+    _, st = gpu_scan(w, t_slice=slice(0, 127))
+    outs = []
+    for t in range(127, 130):
+        q, k, v = (dev_tensor(a[:, :, t], "bf16") for a in (w.q, w.k, w.v))
+        o, _ = F.step(q, k, v, f32_tensor(w.beta[:, :, t]), f32_tensor(w.lam[:, :, t]),
+                      rule=wl.RULE_DELTA_PV, eps=w.eps, S_in=st, S_out=st)
+        outs.append(o.float().cpu().numpy())
+    torch.cuda.synchronize()
+    o_ref, S_ref, _, _ = oracle_scan(w)
+    eo = orc.relerr(np.stack(outs, axis=2).astype(np.float64), o_ref[:, :, 127:])
+    eS = orc.relerr(state_np(st)[0], S_ref)
+    say(f"    err(o)={eo:.3e} err(S)={eS:.3e}")
+    assert eo <= TOL["bf16"] and eS <= TOL["bf16"]

@@ -167,3 +167,30 @@ def test_znorm_decode_sequence(phi, pc, dtype, dk, dv):
     say(f"    err(o)={eo:.3e} err(S)={eS:.3e} err(z)={ez:.3e}")
     assert eo <= TOL["f32"] and eS <= TOL["f32"] and ez <= TOL["f32"]
     assert np.all(h == 1)
+
+
+def test_znorm_decode_with_qk_norm():
+    """Decode with the normaliser and L2-normalised raw q, k (positive features)."""
+    import torch
+    B, H, d, steps = 2, 3, 128, 5
+    rng = np.random.default_rng(77)
+    st = F.State(B, H, d, d)
+    S_ref = z_ref = h_ref = None
+    outs, refs = [], []
+    for s in range(steps):
+        q, k = (np.abs(rng.standard_normal((B, H, d))).astype(np.float32) * 3 for _ in range(2))
+        v = rng.standard_normal((B, H, d)).astype(np.float32)
+        q, k, v = wl.round_to_bf16(q), wl.round_to_bf16(k), wl.round_to_bf16(v)
+        lam = rng.uniform(0.8, 1.0, size=(B, H)).astype(np.float32)
+        t = lambda x, b=True: (torch.from_numpy(x).to(torch.bfloat16) if b else torch.from_numpy(x)).cuda()
+        o, _ = F.step(t(q), t(k), t(v), None, t(lam, False), rule=wl.RULE_ADDITIVE,
+                      flags=F.ZNORM | F.QK_L2NORM, eps=1e-6, S_in=st if s else None, S_out=st)
+        outs.append(o.cpu().numpy().astype(np.float64))
+        o_ref, S_ref, z_ref, h_ref = orc.step(q, k, v, None, lam, rule=wl.RULE_ADDITIVE, eps=1e-6,
+                                              S0=S_ref, xprev0=z_ref, has0=h_ref, qk_norm="l2",
+                                              znorm=True)
+        refs.append(o_ref)
+    torch.cuda.synchronize()
+    eo = orc.relerr(np.stack(outs), np.stack(refs))
+    say(f"[znorm step qk-l2] err(o)={eo:.3e}")
+    assert eo <= TOL["f32"]
