@@ -44,8 +44,9 @@
  *   - Supported sizes: d_k and d_v in {64, 128}; chunk (scan) 0 (= 64) or 64;
  *     T * max(d_k, d_v) * 4 < 2^31 (per-head buffers are addressed with 32-bit
  *     offsets); larger sizes return FWMEM_EUNSUPPORTED.
- *   - With bf16 inputs, the identity feature map and scalar decay, a carried key
- *     x_prev enters the scan rounded to bf16 (exact whenever it came from a bf16 key).
+ *   - With bf16 inputs, the identity feature map and scalar decay (or the per-value-
+ *     channel rule), a carried key x_prev enters the scan rounded to bf16 (exact whenever
+ *     it came from a bf16 key).
  *
  * State buffer (one per call side; S_in and S_out may be the same buffer):
  *   bytes [0, 4*BH*dk*dv)                 S       [B][H][dk][dv] float32

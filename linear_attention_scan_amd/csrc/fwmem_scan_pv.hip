@@ -18,9 +18,14 @@
 // Prep (one workgroup per (head, chunk)): G, P and the token scalars into a record.
 // Propagate (one workgroup per (head, 64 value columns), four waves of 16 columns, the
 // state slice in registers): per chunk, stage X, Q, G, P, beta and V in LDS, then the
-// algebra above on fp32 MFMA.
+// algebra above on MFMA: with bf16 inputs and the identity feature map, X and Q are exact
+// bf16 numbers and X S0, Q S0 and X^T W~ run on bf16 MFMA against S0 and W~ split into
+// bf16 hi + lo pairs (fwmem_split.h), which keeps about 16 bits of each; everything else
+// (and every product for other inputs) on fp32 MFMA. The carried key then enters rounded
+// to bf16, as on the split pair.
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
+#include "fwmem_split.h"
 
 namespace fwmem {
 namespace {
@@ -93,10 +98,18 @@ __global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
   float* rec = reinterpret_cast<float*>(p.ws + ((size_t)bh * p.nchunks + c) * RecPV::kBytes);
   const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
   const float* x0 = (has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+  // bf16 inputs with the identity map: the carried key is rounded to bf16 like the keys
+  const bool round_x0 = sizeof(InT) == 2 && (p.flags & kFlagPhiElu1) == 0;
+  __shared__ float s_x0[DK];
+  if (x0 != nullptr) {
+    for (int i = threadIdx.x; i < DK; i += NT)
+      s_x0[i] = round_x0 ? bf16_bits_to_f32(f32_to_bf16_bits(x0[i])) : x0[i];
+    __syncthreads();
+  }
 
-  stage_rows<InT, DK, LDX>(p, bh, t0, Xs, Qs, x0, nullptr, nullptr);
+  stage_rows<InT, DK, LDX>(p, bh, t0, Xs, Qs, x0 != nullptr ? s_x0 : nullptr, nullptr, nullptr);
   if (c == 0)
-    for (int i = threadIdx.x; i < DK; i += NT) rec[RecPV::kX0 + i] = x0 != nullptr ? x0[i] : 0.f;
+    for (int i = threadIdx.x; i < DK; i += NT) rec[RecPV::kX0 + i] = x0 != nullptr ? s_x0[i] : 0.f;
   __syncthreads();
   // token scalars (wave 0, lane = token)
   if (wave == 0) {
@@ -178,13 +191,28 @@ constexpr size_t prop_pv_floats() {
   return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH;
 }
 
-template <typename InT, int DK>
+// 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
+// K block (the order split_c gives the B side): two 8-byte LDS reads at p and p + 16.
+__device__ __forceinline__ bf8 frag_pair(const uint16_t* p) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+  return __builtin_bit_cast(bf8, u32x4{a.x, a.y, b.x, b.y});
+}
+
+template <typename InT, int DK, bool EXACT>
 __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   constexpr int LDX = DK + 4, NRT = DK / 16;
+  static_assert(!EXACT || sizeof(InT) == 2, "exact operands are bf16");
   static_assert(4 * prop_pv_floats<DK>() <= 160 * 1024, "LDS");
   __shared__ __align__(16) float smem[prop_pv_floats<DK>()];
-  float* Xs = smem;                 // [CH][LDX] x_t rescaled
-  float* Qs = Xs + CH * LDX;        // [CH][LDX] q_t rescaled
+  float* Xs = smem;                 // [CH][LDX] phi(x_t) (fp32 operands)
+  float* Qs = Xs + CH * LDX;        // [CH][LDX] phi(q_t)
+  // exact operands in the same space: X and Q rows and X transposed, raw bf16
+  constexpr int LDB = DK + 8, LDT2 = CH + 8;
+  static_assert((2 * CH * LDB + DK * LDT2) * 2 <= 2 * CH * LDX * 4, "bf16 operands fit");
+  uint16_t* Xb = reinterpret_cast<uint16_t*>(smem);  // [CH][LDB]
+  uint16_t* Qb = Xb + CH * LDB;                      // [CH][LDB]
+  uint16_t* XTb = Qb + CH * LDB;                     // [DK][LDT2]
   float* Gs = Qs + CH * LDX;        // [CH][LDM]
   float* Ps = Gs + CH * LDM;        // [CH][LDM]
   float* Bs = Ps + CH * LDM;        // [CH][LDM] beta of the group's 64 columns
@@ -263,8 +291,26 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * CH;
     // ---- registers -> LDS (chunk c)
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int r = 0; r < NGX; ++r) {
+      for (int r = 0; r < NGX; ++r) {
+        const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW;
+        u32x4 w = px[r];
+        if ((xzero >> r) & 1u) {  // the carried key, already bf16-exact in the record
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)f32_to_bf16_bits(rec0[RecPV::kX0 + cc + 2 * j]) |
+                   ((uint32_t)f32_to_bf16_bits(rec0[RecPV::kX0 + cc + 2 * j + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(Xb + t * LDB + cc) = w;
+        *reinterpret_cast<u32x4*>(Qb + t * LDB + cc) = pq[r];
+#pragma unroll
+        for (int j = 0; j < VW; ++j)
+          XTb[(cc + j) * LDT2 + t] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < (EXACT ? 0 : NGX); ++r) {
       const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW;
       float x[VW], q[VW];
       In<InT>::decode(px[r], x);
@@ -310,16 +356,33 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
 
     // ---- X S0 and Q S0 (C layout: rows 16 mt + 4 g + i, column n), rows rescaled
     f4 XS[4], QS[4];
+    bf8 sh[EXACT ? DK / 32 : 1], sl[EXACT ? DK / 32 : 1];
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int kq = 0; kq < DK / 32; ++kq) split_c(s, kq, sh[kq], sl[kq]);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       XS[mt] = f4{0.f, 0.f, 0.f, 0.f};
       QS[mt] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EXACT) {
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const f4 ax = *reinterpret_cast<const f4*>(Xs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
-        const f4 aq = *reinterpret_cast<const f4*>(Qs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
-        mma_block(XS[mt], ax, s[rt]);
-        mma_block(QS[mt], aq, s[rt]);
+        for (int kq = 0; kq < DK / 32; ++kq) {
+          const bf8 ax = frag_pair(Xb + (16 * mt + n) * LDB + 32 * kq + 4 * g);
+          const bf8 aq = frag_pair(Qb + (16 * mt + n) * LDB + 32 * kq + 4 * g);
+          mma_bf16(XS[mt], ax, sh[kq]);
+          mma_bf16(QS[mt], aq, sh[kq]);
+          mma_bf16(XS[mt], ax, sl[kq]);
+          mma_bf16(QS[mt], aq, sl[kq]);
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const f4 ax = *reinterpret_cast<const f4*>(Xs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
+          const f4 aq = *reinterpret_cast<const f4*>(Qs + (16 * mt + n) * LDX + 16 * rt + 4 * g);
+          mma_block(XS[mt], ax, s[rt]);
+          mma_block(QS[mt], aq, s[rt]);
+        }
       }
       XS[mt] *= *reinterpret_cast<const f4*>(s_nx + 16 * mt + 4 * g);
       QS[mt] *= *reinterpret_cast<const f4*>(s_mq + 16 * mt + 4 * g);
@@ -439,18 +502,38 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       }
     }
 
-    // ---- S' = Gamma_C S0 + Gamma^_C X^T W~
+    // ---- S' = Gamma_C S0 + Gamma^_C X^T W~ (W~ rows times the keys' rescale factors)
+    if constexpr (EXACT) {
+      f4 Wn[4];
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) Wn[kb] = W[kb] * *reinterpret_cast<const f4*>(s_nx + 16 * kb + 4 * g);
+      bf8 wh[2], wl[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f4 a;
+      for (int kq = 0; kq < 2; ++kq) split_c(Wn, kq, wh[kq], wl[kq]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = Xs[(16 * kb + 4 * g + q) * LDX + 16 * rt + n];
-        mma_block(acc, a, W[kb] * *reinterpret_cast<const f4*>(s_nx + 16 * kb + 4 * g));
+      for (int rt = 0; rt < NRT; ++rt) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const bf8 a = frag_pair(XTb + (16 * rt + n) * LDT2 + 32 * kq + 4 * g);
+          mma_bf16(acc, a, wh[kq]);
+          mma_bf16(acc, a, wl[kq]);
+        }
+        s[rt] = s[rt] * GamC + acc * GhC;
       }
-      s[rt] = s[rt] * GamC + acc * GhC;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          f4 a;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[q] = Xs[(16 * kb + 4 * g + q) * LDX + 16 * rt + n];
+          mma_block(acc, a, W[kb] * *reinterpret_cast<const f4*>(s_nx + 16 * kb + 4 * g));
+        }
+        s[rt] = s[rt] * GamC + acc * GhC;
+      }
     }
     __syncthreads();  // LDS is restaged next chunk
   }
@@ -482,8 +565,14 @@ hipError_t launch_pv_t(const ScanParams& p, hipStream_t st, int phases) {
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
-    hipLaunchKernelGGL((prop_pv_kernel<InT, DK>), dim3((unsigned)((size_t)p.BH * (p.dv / 64))), dim3(NT),
-                       0, st, p);
+    const dim3 grid((unsigned)((size_t)p.BH * (p.dv / 64)));
+    if constexpr (sizeof(InT) == 2) {
+      if ((p.flags & kFlagPhiElu1) == 0) {
+        hipLaunchKernelGGL((prop_pv_kernel<InT, DK, true>), grid, dim3(NT), 0, st, p);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((prop_pv_kernel<InT, DK, false>), grid, dim3(NT), 0, st, p);
     return hipGetLastError();
   }
   return hipSuccess;
