@@ -188,7 +188,8 @@ __device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, floa
 
 template <int DK>
 constexpr size_t prop_pv_floats() {
-  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH;
+  // X, Q; G, P, beta, V; four token scalars; per wave two [16][17] solve tiles (c, ef)
+  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH + 4 * 2 * 2 * 16 * 17;
 }
 
 // 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
@@ -221,6 +222,8 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   float* s_lam = s_den + CH;        // [CH]
   float* s_nx = s_lam + CH;         // [CH]
   float* s_mq = s_nx + CH;          // [CH]
+  constexpr int LDS17 = 17;         // solve tiles: [16 rows][17] floats, two per wave and buffer
+  float* s_solve = s_mq + CH;       // [4 waves][2 buffers][2: c, ef][16][17]
 
   const int ngrp = p.dv / 64;
   const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
@@ -456,8 +459,12 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
         ef[mt][i] = cf * Ghprev;
       }
 
-    // ---- W~ by blocked forward substitution: off-diagonal blocks on MFMA, then the
-    // diagonal block row by row (row r's owner lanes g = r / 4 broadcast its value)
+    // ---- W~ by blocked forward substitution: the off-diagonal blocks on MFMA; each
+    // diagonal block is solved by one lane per column (lanes g = 0), which takes the
+    // block's right-hand side c = rhs - ef (G_off W~) and its row factors ef through an
+    // LDS tile, reads G by broadcast and keeps the 16 solved values in registers, then
+    // hands them back in the C layout. Two tiles alternate between blocks, so one barrier
+    // before and one after the solve suffice.
     f4 W[4];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
@@ -467,18 +474,33 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
         const f4 a = *reinterpret_cast<const f4*>(Gs + (16 * bi + n) * LDM + 16 * bk + 4 * g);
         mma_block(y, a, W[bk]);
       }
-      f4 w = {0.f, 0.f, 0.f, 0.f};
+      float* tc = s_solve + ((wave * 2 + (bi & 1)) * 2) * 16 * LDS17;  // c tile
+      float* te = tc + 16 * LDS17;                                      // ef tile
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = r >> 2, ir = r & 3;
-        const float cand = rhs[bi][ir] - ef[bi][ir] * y[ir];
-        const float wr = __shfl(cand, 16 * gr + n);
-        if (g == gr) w[ir] = wr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * g + i > r) y[i] += Gs[(16 * bi + 4 * g + i) * LDM + 16 * bi + r] * wr;
+      for (int i = 0; i < 4; ++i) {
+        tc[(4 * g + i) * LDS17 + n] = rhs[bi][i] - ef[bi][i] * y[i];
+        te[(4 * g + i) * LDS17 + n] = ef[bi][i];
       }
-      W[bi] = w;
+      __syncthreads();
+      if (g == 0) {
+        float w[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float* grow = Gs + (16 * bi + r) * LDM + 16 * bi;
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < r; ++s2) {
+            if (s2 & 1) a1 += grow[s2] * w[s2];
+            else a0 += grow[s2] * w[s2];
+          }
+          w[r] = tc[r * LDS17 + n] - te[r * LDS17 + n] * (a0 + a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tc[r * LDS17 + n] = w[r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) W[bi][i] = tc[(4 * g + i) * LDS17 + n];
     }
 
     // ---- O = Gamma o (Q S0) + Gamma^ o (P W~), stored
