@@ -91,7 +91,10 @@ __device__ __forceinline__ float block_max(float v, float* s_red) {
 }
 
 // ================================================================ prep kernel
-template <typename InT, int DK>
+// NREG operand/matrix regions: four for the delta rule; three for the rules without a
+// solve (X, Q and M; the L and T region is never written), so that three workgroups share
+// a CU.
+template <typename InT, int DK, int NREG>
 struct PrepLds {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
@@ -101,7 +104,7 @@ struct PrepLds {
   static constexpr size_t kMat = (size_t)CH * LDF * 4;
   static constexpr size_t kReg = ((kOp > kMat ? kOp : kMat) + 15) / 16 * 16;
   static constexpr size_t kSmall = 4 * (8 * CH + 4 * NW + 16);
-  static constexpr size_t kBytes = 4 * kReg + kSmall;
+  static constexpr size_t kBytes = NREG * kReg + kSmall;
 };
 
 template <typename InT, int DK, int RULE, bool PC, bool ELU>
@@ -110,16 +113,19 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
-  using L = PrepLds<InT, DK>;
+  constexpr int NREG = R::solve ? 4 : 3;
+  using L = PrepLds<InT, DK, NREG>;
   using RC = Rec<InT, DK>;
   using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDF = L::LDF;
   constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
   __shared__ __align__(16) char smem[L::kBytes];
+  // Without a solve, region 3 aliases region 2: only one of them is ever written (the
+  // read mask M, or the column pass's scratch before M exists).
   char* reg[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) reg[r] = smem + r * L::kReg;
-  float* s_norm = reinterpret_cast<float*>(smem + 4 * L::kReg);
+  for (int r = 0; r < 4; ++r) reg[r] = smem + (r < NREG ? r : NREG - 1) * L::kReg;
+  float* s_norm = reinterpret_cast<float*>(smem + NREG * L::kReg);
   float* s_lam = s_norm + CH;
   float* s_eta = s_lam + CH;
   float* s_g = s_eta + CH;
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   const op_t* B_X = Xs;
   float invL = 1.f / (sX * sX);
   float invM = 1.f / (sQ * sX);
-  float* Lf = reinterpret_cast<float*>(reg[2]);
+  float* Lf = reinterpret_cast<float*>(reg[2]);  // delta rule only
   float* Mf = reinterpret_cast<float*>(reg[3]);
   float* Tf = reinterpret_cast<float*>(reg[0]);   // after the Gram, X is dead
   float* Ysc = reinterpret_cast<float*>(reg[1]);  // after the Gram, Q is dead
