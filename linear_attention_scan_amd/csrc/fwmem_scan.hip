@@ -623,7 +623,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
 }
 
 // ================================================================ propagate kernel
-template <typename InT, int DK>
+// T only for the delta rule; per-channel Gamma_C and the column pass's exchange only with
+// per-channel decay. Without either, a bf16 d_k = 128 workgroup takes 80,128 bytes, so two
+// share a CU.
+template <typename InT, int DK, bool SOLVE, bool PCX>
 struct PropLds {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
@@ -641,10 +644,10 @@ struct PropLds {
   static constexpr size_t oXU = oX + kX;
   static constexpr size_t oQ = oXU + kXU;
   static constexpr size_t oT = oQ + kX;
-  static constexpr size_t oM = oT + kC;
+  static constexpr size_t oM = oT + (SOLVE ? kC : 0);
   static constexpr size_t oV = oM + kC;
-  static constexpr size_t oS = oV + kV;  // small: 5*CH + DK + 2*NT floats
-  static constexpr size_t kBytes = oS + 4 * (5 * CH + DK + 2 * NT);
+  static constexpr size_t oS = oV + kV;  // small: 5*CH (+ DK + 2*NT with PCX) floats
+  static constexpr size_t kBytes = oS + 4 * (5 * CH + (PCX ? DK + 2 * NT : 0));
 };
 
 template <typename InT, int DK, int RULE, bool PC, bool ELU>
@@ -653,7 +656,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
-  using L = PropLds<InT, DK>;
+  using L = PropLds<InT, DK, R::solve, PC>;
   using RC = Rec<InT, DK>;
   using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDT = L::LDT, LDC = L::LDC, LDV = L::LDV;

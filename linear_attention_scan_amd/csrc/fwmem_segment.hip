@@ -330,10 +330,14 @@ hipError_t launch_fixup_in(const SegParams& s, unsigned grid, hipStream_t st) {
 int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint32_t flags) {
   (void)dk;
   if (flags & kFlagOutBf16) return 1;
-  const size_t groups = scan_split_path(bf16, flags) ? (size_t)dv / kSplitCols : ((size_t)dv + 63) / 64;
+  const bool split = scan_split_path(bf16, flags);
+  const size_t groups = split ? (size_t)dv / kSplitCols : ((size_t)dv + 63) / 64;
   const size_t wgs = BH * groups;
+  // propagate workgroups resident at once: one per CU, two for the general pair's rules
+  // without a solve or per-channel decay (the diagonal ones), whose LDS fits twice
+  const size_t cap = (!split && seg_diagonal(rule, flags)) ? 512 : 256;
   int P = 1;
-  while (P < 16 && wgs * 2 * P <= 256 && T % (64 * 2 * (size_t)P) == 0 && T / (2 * (size_t)P) >= 512) P *= 2;
+  while (P < 16 && wgs * 2 * P <= cap && T % (64 * 2 * (size_t)P) == 0 && T / (2 * (size_t)P) >= 512) P *= 2;
   // With a transition pass the propagate work doubles, so fewer than 8 segments do not
   // pay (an additive elu+1 scan with 32 heads, T = 16384, ran no faster with 4 before
   // its transitions were made diagonal); diagonal transitions pay from 2.
