@@ -233,6 +233,52 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
                         const float* beta, const float* lambda, const fwmem_mode* mode,
                         const void* S_in, void* out, void* S_out, fwmem_stream stream);
 
+/* Bytes of device workspace fwmem_scan_bwd needs for this shape and mode (0 when T == 0
+ * or B*H == 0): per head, the state at each 64-token chunk start plus 65 chunk-sized
+ * state buffers' worth of scratch, i.e. 4 * ((ceil(T/64) + 64) * dk * dv + 64 * dv)
+ * bytes. Its contents need no initialisation and are scratch only. */
+fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
+                                            size_t* bytes);
+
+/*
+ * Backward pass of fwmem_scan_fwd: for L = <grad_out, out> + <grad_S_out, S_T>, the
+ * gradients of L with respect to q, k, v, beta, lambda and the initial state. The pages
+ * define only the forward recurrence ("Fast Weight Attention for Continual Learning"
+ * reading notes, sections 3.2 and 4.1-4.3; "attention is also an FFN", sections 2.1 and
+ * 3.2); this is its exact reverse-mode derivative, token by token, with the forward
+ * states recomputed from a state kept at every chunk start.
+ *
+ * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE; flags 0 or
+ * FWMEM_PHI_ELU1 (anything else: FWMEM_EUNSUPPORTED); a scalar lambda; dk and dv in
+ * {64, 128}.
+ *
+ *   q, k, v, beta, lambda, S_in: exactly as passed to fwmem_scan_fwd (read only)
+ *   grad_out     [B][H][T][dv] float32  (required when T > 0)
+ *   grad_S_out   state buffer or NULL (zero); only its S part is read: the final
+ *                state's carried key and flag take no gradient
+ *   grad_q, grad_k [B][H][T][dk] float32; grad_v [B][H][T][dv] float32 (required when
+ *                T > 0; every element is written)
+ *   grad_beta, grad_lambda [B][H][T] float32 or NULL (not written). With beta or lambda
+ *                NULL they are the gradients at the default value (write scale 1,
+ *                ridge 0, retention 1).
+ *   grad_S_in    state buffer or NULL: its S part receives dL/dS_0, its x_prev part
+ *                dL/dx_prev (with respect to the carried key as stored, phi already
+ *                applied; zero without a carried key and for the additive rule), its
+ *                has_prev part 0.
+ *   workspace, ws_bytes: device scratch of at least fwmem_scan_bwd_workspace_bytes()
+ *
+ * Outputs must not overlap one another, the inputs or the workspace (FWMEM_EOVERLAP).
+ * grad_v, grad_S_out, grad_S_in, S_in and the workspace must be 16-byte aligned
+ * (FWMEM_EALIGN). Asynchronous on `stream`; allocates nothing.
+ */
+fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void* k,
+                            const void* v, const float* beta, const float* lambda,
+                            const fwmem_mode* mode, const void* S_in, const float* grad_out,
+                            const void* grad_S_out, float* grad_q, float* grad_k,
+                            float* grad_v, float* grad_beta, float* grad_lambda,
+                            void* grad_S_in, void* workspace, size_t ws_bytes,
+                            fwmem_stream stream);
+
 /* A static, human-readable name for a status code. */
 const char* fwmem_strerror(fwmem_status status);
 

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "fwmem_backward.h"
 #include "fwmem_internal.h"
 
 namespace {
@@ -489,6 +490,119 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
   p.eps = mode->eps;
   if (z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
   const hipError_t e = fwmem::launch_step(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
+}
+
+}  // extern "C"
+
+// ---- backward pass
+
+namespace {
+
+fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
+  fwmem_status st = check_shape(shape, true);
+  if (st != FWMEM_OK) return st;
+  st = check_scan_mode(mode);
+  if (st != FWMEM_OK) return st;
+  if (mode->rule == FWMEM_RULE_DELTA_PV || (mode->flags & ~(uint32_t)FWMEM_PHI_ELU1) != 0)
+    return FWMEM_EUNSUPPORTED;
+  if (!fwmem::bwd_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
+  return FWMEM_OK;
+}
+
+size_t bwd_ws_bytes(const fwmem_shape* shape) {
+  const size_t BH = (size_t)shape->B * (size_t)shape->H;
+  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv));
+}
+
+}  // namespace
+
+extern "C" {
+
+fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
+                                            size_t* bytes) {
+  if (bytes == nullptr) return FWMEM_EINVAL;
+  const fwmem_status st = check_bwd(shape, mode);
+  if (st != FWMEM_OK) return st;
+  *bytes = bwd_ws_bytes(shape);
+  return FWMEM_OK;
+}
+
+fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void* k,
+                            const void* v, const float* beta, const float* lambda,
+                            const fwmem_mode* mode, const void* S_in, const float* grad_out,
+                            const void* grad_S_out, float* grad_q, float* grad_k,
+                            float* grad_v, float* grad_beta, float* grad_lambda,
+                            void* grad_S_in, void* workspace, size_t ws_bytes,
+                            fwmem_stream stream) {
+  fwmem_status st = check_bwd(shape, mode);
+  if (st != FWMEM_OK) return st;
+  const Sizes z = sizes_of(shape);
+  const size_t T = (size_t)shape->T;
+  if (z.BH == 0) return FWMEM_OK;
+  const bool needs_beta = mode->rule != FWMEM_RULE_ADDITIVE;
+  if (T > 0 && needs_beta && beta == nullptr) return FWMEM_EINVAL;
+  if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || grad_out == nullptr ||
+                grad_q == nullptr || grad_k == nullptr || grad_v == nullptr))
+    return FWMEM_EINVAL;
+  if (T == 0 && grad_S_in == nullptr) return FWMEM_OK;
+  const size_t need = bwd_ws_bytes(shape);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr)) return FWMEM_EWORKSPACE;
+  const size_t es = esize(shape->dtype);
+  if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(beta, 4) ||
+      !aligned(lambda, 4) || !aligned(grad_out, 4) || !aligned(grad_q, 4) ||
+      !aligned(grad_k, 4) || !aligned(grad_beta, 4) || !aligned(grad_lambda, 4) ||
+      !aligned(grad_v, 16) || !aligned(S_in, 16) || !aligned(grad_S_out, 16) ||
+      !aligned(grad_S_in, 16) || !aligned(workspace, 16))
+    return FWMEM_EALIGN;
+  if (z.BH * T > 0x7fffffffu || z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
+  const size_t nq = z.BH * T * shape->dk * es, nv = z.BH * T * shape->dv * es;
+  const size_t ns = z.BH * T * 4, nsb = z.state_bytes;
+  const size_t ngq = z.BH * T * shape->dk * 4, ngv = z.BH * T * shape->dv * 4;
+  const void* ins[] = {q, k, v, beta, lambda, S_in, grad_out, grad_S_out};
+  const size_t nins[] = {nq, nq, nv, ns, ns, nsb, ngv, nsb};
+  const void* outs[] = {grad_q, grad_k, grad_v, grad_beta, grad_lambda, grad_S_in, workspace};
+  const size_t nouts[] = {ngq, ngq, ngv, ns, ns, nsb, need};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], nouts[i], ins[j], nins[j])) return FWMEM_EOVERLAP;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], nouts[i], outs[j], nouts[j])) return FWMEM_EOVERLAP;
+  }
+
+  const StatePtrs si = state_ptrs(S_in, z), gso = state_ptrs(grad_S_out, z),
+                  gsi = state_ptrs(grad_S_in, z);
+  fwmem::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.lam = lambda;
+  p.S_in = si.S;
+  p.xprev_in = si.x;
+  p.has_in = si.h;
+  p.dout = grad_out;
+  p.dS_out = gso.S;
+  p.gq = grad_q;
+  p.gk = grad_k;
+  p.gv = grad_v;
+  p.gbeta = grad_beta;
+  p.glam = grad_lambda;
+  p.gS0 = gsi.S;
+  p.gx0 = gsi.x;
+  p.gh0 = gsi.h;
+  p.ws = static_cast<float*>(workspace);
+  p.BH = (int)z.BH;
+  p.T = (int)T;
+  p.dk = shape->dk;
+  p.dv = shape->dv;
+  p.nchunks = (int)((T + kChunk - 1) / kChunk);
+  p.rule = mode->rule;
+  p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
+  p.flags = mode->flags;
+  p.eps = mode->eps;
+  const hipError_t e = fwmem::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
 }
 

@@ -1,0 +1,50 @@
+// Internal interface of the scan's backward pass (fwmem_backward.hip), between the C-ABI
+// layer and its launcher. Host code only sees plain structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fwmem {
+
+// Pointers are device pointers; optional ones may be null. Gradients are float32 in the
+// layout of the input they belong to.
+struct BwdParams {
+  const void* q;          // [BH][T][dk]
+  const void* k;          // [BH][T][dk]
+  const void* v;          // [BH][T][dv]
+  const float* beta;      // [BH][T] (optional for the additive rule)
+  const float* lam;       // [BH][T] or null
+  const float* S_in;      // [BH][dk][dv] or null (zeros)
+  const float* xprev_in;  // [BH][dk] or null
+  const int32_t* has_in;  // [BH] or null
+  const float* dout;      // [BH][T][dv]
+  const float* dS_out;    // [BH][dk][dv] or null (zeros)
+  float* gq;              // [BH][T][dk]
+  float* gk;              // [BH][T][dk]
+  float* gv;              // [BH][T][dv]
+  float* gbeta;           // [BH][T] or null (not written)
+  float* glam;            // [BH][T] or null (not written)
+  float* gS0;             // [BH][dk][dv] or null
+  float* gx0;             // [BH][dk] or null (with gS0)
+  int32_t* gh0;           // [BH] or null (with gS0): written 0
+  float* ws;              // per head: chunk-start states, a chunk's states, its residuals
+  int BH, T, dk, dv, nchunks;
+  int rule;  // kRuleDelta, kRuleAdditive or kRuleInner
+  int bf16;
+  uint32_t flags;
+  float eps;
+};
+
+// Workspace floats per head: the state at each of the nchunks chunk starts, the states
+// after each of a chunk's 64 tokens, and the chunk's 64 residuals.
+__host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv) {
+  const size_t nchunks = ((size_t)T + 63) / 64;
+  const size_t SS = (size_t)dk * (size_t)dv;
+  return T > 0 ? (nchunks + 64) * SS + 64 * (size_t)dv : 0;
+}
+bool bwd_supported(int dk, int dv);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fwmem

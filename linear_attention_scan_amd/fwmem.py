@@ -30,7 +30,7 @@ LAMBDA_SCALED = 1 << 9
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",
-            "fwmem_strerror", "fwmem_version"]
+            "fwmem_scan_bwd_workspace_bytes", "fwmem_scan_bwd", "fwmem_strerror", "fwmem_version"]
 PHASE_BOTH, PHASE_PREP, PHASE_PROPAGATE = "fwmem_scan_fwd", "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate"
 
 
@@ -75,6 +75,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fwmem_step.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.POINTER(Mode),
                                vp, vp, vp, vp]
     lib.fwmem_step.restype = ctypes.c_int
+    lib.fwmem_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mode),
+                                                   ctypes.POINTER(sz)]
+    lib.fwmem_scan_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.fwmem_scan_bwd.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.POINTER(Mode),
+                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fwmem_scan_bwd.restype = ctypes.c_int
     lib.fwmem_strerror.argtypes = [ctypes.c_int]
     lib.fwmem_strerror.restype = ctypes.c_char_p
     lib.fwmem_version.argtypes = []
@@ -115,6 +121,14 @@ def workspace_bytes(shp: Shape, md: Mode) -> int:
     return n.value
 
 
+def bwd_workspace_bytes(shp: Shape, md: Mode) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), ctypes.byref(n))
+    if st != OK:
+        raise FwmemError(st, "fwmem_scan_bwd_workspace_bytes")
+    return n.value
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -146,6 +160,17 @@ def step_raw(shp: Shape, q, k, v, beta, lam, md: Mode, S_in, out, S_out, stream=
     """Call fwmem_step with tensors (or raw ints / None) and return the status."""
     return load().fwmem_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(lam),
                              ctypes.byref(md), _ptr(S_in), _ptr(out), _ptr(S_out), _stream(stream))
+
+
+def scan_bwd_raw(shp: Shape, q, k, v, beta, lam, md: Mode, S_in, grad_out, grad_S_out, grad_q,
+                 grad_k, grad_v, grad_beta, grad_lam, grad_S_in, workspace, ws_bytes: int,
+                 stream=None) -> int:
+    """Call fwmem_scan_bwd with tensors (or raw ints / None) and return the status."""
+    return load().fwmem_scan_bwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                 _ptr(lam), ctypes.byref(md), _ptr(S_in), _ptr(grad_out),
+                                 _ptr(grad_S_out), _ptr(grad_q), _ptr(grad_k), _ptr(grad_v),
+                                 _ptr(grad_beta), _ptr(grad_lam), _ptr(grad_S_in),
+                                 _ptr(workspace), int(ws_bytes), _stream(stream))
 
 
 # ----------------------------------------------------------------- torch conveniences
@@ -221,3 +246,35 @@ def step(q, k, v, beta=None, lam=None, *, rule=RULE_DELTA, flags=0, eps=1e-6,
     if st != OK:
         raise FwmemError(st, "fwmem_step")
     return out, S_out
+
+
+def scan_bwd(q, k, v, beta, lam, grad_out, *, rule=RULE_DELTA, flags=0, eps=1e-6,
+             S_in: Optional[State] = None, grad_S_out: Optional[State] = None,
+             workspace=None, stream=None):
+    """Backward pass of scan_fwd for L = <grad_out, out> + <grad_S_out.S, S_T>.
+
+    Allocates the gradients and the workspace. Returns a dict of float32 device tensors:
+    "q", "k", "v", "beta" and "lam" (None where the input is None) and "state" (a State
+    holding dL/dS_0 and dL/dx_prev)."""
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    shp = shape(B, H, T, dk, dv, _dtype_code(q))
+    md = mode(rule, flags, eps, 0)
+    dev = q.device
+    g = {"q": torch.empty((B, H, T, dk), dtype=torch.float32, device=dev),
+         "k": torch.empty((B, H, T, dk), dtype=torch.float32, device=dev),
+         "v": torch.empty((B, H, T, dv), dtype=torch.float32, device=dev),
+         "beta": None if beta is None else torch.empty((B, H, T), dtype=torch.float32, device=dev),
+         "lam": None if lam is None else torch.empty((B, H, T), dtype=torch.float32, device=dev),
+         "state": State(B, H, dk, dv, device=dev)}
+    need = bwd_workspace_bytes(shp, md)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = scan_bwd_raw(shp, q, k, v, beta, lam, md, S_in.buf if S_in is not None else None,
+                      grad_out, grad_S_out.buf if grad_S_out is not None else None, g["q"],
+                      g["k"], g["v"], g["beta"], g["lam"], g["state"].buf, workspace,
+                      workspace.numel(), stream)
+    if st != OK:
+        raise FwmemError(st, "fwmem_scan_bwd")
+    return g

@@ -162,3 +162,61 @@ def test_empty_batch_is_a_no_op():
 ])
 def test_step_rejects(case, expect):
     assert _step(**case) == expect
+
+
+M = 1 << 24  # backward cases: every buffer 16 MiB from the next, none dereferenced
+
+
+def _bwd(shp=None, md=None, q=M, k=2 * M, v=3 * M, beta=4 * M, lam=None, S_in=None, gout=5 * M,
+         gSout=None, gq=6 * M, gk=7 * M, gv=8 * M, gbeta=9 * M, glam=None, gSin=10 * M, ws=11 * M,
+         ws_bytes=1 << 40):
+    shp = shp or F.shape(1, 1, 8, 128, 128, F.BF16)
+    md = md or F.mode()
+    lib = _lib()
+    return lib.fwmem_scan_bwd(ctypes.byref(shp), q, k, v, beta, lam, ctypes.byref(md), S_in, gout,
+                              gSout, gq, gk, gv, gbeta, glam, gSin, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(shp=F.shape(1, 1, 8, 96, 128, F.BF16)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.QK_L2NORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.BETA_SIGMOID)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.OUT_BF16)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=1 << 12)), F.EINVAL),
+    (dict(md=F.mode(rule=7)), F.EINVAL),
+    (dict(beta=None), F.EINVAL),
+    (dict(gout=None), F.EINVAL),
+    (dict(gq=None), F.EINVAL),
+    (dict(gv=None), F.EINVAL),
+    (dict(ws=None), F.EWORKSPACE),
+    (dict(ws_bytes=4096), F.EWORKSPACE),
+    (dict(gv=8 * M + 4), F.EALIGN),
+    (dict(ws=11 * M + 8), F.EALIGN),
+    (dict(gSin=10 * M + 4), F.EALIGN),
+    (dict(gq=1 * M), F.EOVERLAP),         # onto q
+    (dict(gk=6 * M + 64), F.EOVERLAP),    # onto grad_q
+    (dict(ws=8 * M), F.EOVERLAP),         # onto grad_v
+    (dict(gbeta=4 * M), F.EOVERLAP),      # onto beta
+])
+def test_bwd_rejects(case, expect):
+    assert _bwd(**case) == expect
+
+
+def test_bwd_workspace_size_and_empty_batch():
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    shp, md = F.shape(2, 3, 100, 128, 64, F.F32), F.mode(rule=F.RULE_INNER)
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), ctypes.byref(n)) == F.OK
+    want = 4 * 6 * ((2 + 64) * 128 * 64 + 64 * 64)
+    assert n.value == (want + 255) // 256 * 256
+    shp0 = F.shape(2, 3, 0, 128, 64, F.F32)
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp0), ctypes.byref(md), ctypes.byref(n)) == F.OK
+    assert n.value == 0
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), None) == F.EINVAL
+    # B*H == 0: nothing to do, no pointer is needed
+    assert _bwd(shp=F.shape(0, 2, 8, 64, 64, F.F32), q=None, k=None, v=None, gout=None, gq=None,
+                gk=None, gv=None, ws=None) == F.OK

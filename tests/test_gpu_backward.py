@@ -1,0 +1,135 @@
+"""GPU parity of the scan's backward pass (fwmem_scan_bwd) against the oracle's
+scan_backward: every gradient (q, k, v, beta, lambda, the initial state and the carried
+key) for the delta, inner and additive rules, phi identity and elu+1, bf16 and float32
+inputs, carried and fresh states, ragged chunk tails, a lone no-op step and T = 0.
+
+The kernel computes in float32 whatever the input type (bf16 inputs are exact in both),
+so every gradient is held to the float32 bar."""
+import numpy as np
+import pytest
+
+from linear_attention_scan_amd import fwmem as F
+from linear_attention_scan_amd import workloads as wl
+from oracle import fwmem_oracle as orc
+from tests.gpu_helpers import TOL, dev_tensor, f32_tensor, make_state, say
+
+pytestmark = pytest.mark.gpu
+
+RULES = {"delta": wl.RULE_DELTA, "inner": wl.RULE_INNER, "additive": wl.RULE_ADDITIVE}
+
+
+def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None, beta_kind=None):
+    r = RULES[rule]
+    if lam_kind is None:
+        lam_kind = "gamma" if r == wl.RULE_ADDITIVE else "softplus"
+    if beta_kind is None:
+        beta_kind = "sigmoid" if r == wl.RULE_ADDITIVE else "two_sigmoid"
+    w = wl.make_scan(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, rule=r,
+                     phi=wl.PHI_ELU1 if phi == "elu1" else wl.PHI_IDENTITY,
+                     beta_kind=beta_kind, lam_kind=lam_kind, lam_mu=-3.0,
+                     normalise_qk=phi != "elu1", s0_std=0.1 if carried else None, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    dO = rng.standard_normal((B, H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((B, H, dk, dv)) * 0.3).astype(np.float32)
+    xprev0 = has0 = None
+    if carried and r != wl.RULE_ADDITIVE:
+        kp = rng.standard_normal((B, H, dk)).astype(np.float32)
+        kp /= np.linalg.norm(kp, axis=-1, keepdims=True)
+        xprev0 = np.where(kp > 0, kp + 1.0, np.exp(kp)).astype(np.float32) if phi == "elu1" else kp
+        has0 = np.ones((B, H), dtype=np.int32)
+    return w, dO, dS, xprev0, has0
+
+
+def _run(w, dO, dS, xprev0, has0, phi, carried, with_dS=True):
+    flags = F.PHI_ELU1 if phi == "elu1" else 0
+    S_in = None
+    if carried:
+        S_in = make_state(w.B, w.H, w.dk, w.dv, S=w.S0, xprev=xprev0, has=has0)
+    gS = make_state(w.B, w.H, w.dk, w.dv, S=dS) if with_dS else None
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(w.beta), f32_tensor(w.lam), f32_tensor(dO), rule=w.rule,
+                   flags=flags, eps=w.eps, S_in=S_in, grad_S_out=gS)
+    ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS if with_dS else None,
+                            rule=w.rule, phi_kind=phi, eps=w.eps, S0=w.S0 if carried else None,
+                            xprev0=xprev0, has0=has0)
+    return g, ref
+
+
+def _compare(g, ref, tol=TOL["f32"]):
+    got = {"q": g["q"], "k": g["k"], "v": g["v"], "beta": g["beta"], "lam": g["lam"],
+           "S0": g["state"].S, "xprev0": g["state"].x_prev}
+    errs = {}
+    for name, x in got.items():
+        if ref[name] is None:
+            assert x is None, name
+            continue
+        errs[name] = orc.relerr(x.cpu().numpy().astype(np.float64), ref[name])
+    say("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e <= tol, f"grad {name}: {e:.3e} > {tol}"
+    assert np.all(g["state"].has_prev.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("rule,phi,dtype,dk,dv,T,carried", [
+    ("delta", "identity", "bf16", 128, 128, 150, True),
+    ("delta", "identity", "bf16", 128, 128, 150, False),
+    ("delta", "elu1", "f32", 64, 128, 100, False),
+    ("delta", "identity", "f32", 128, 64, 64, True),
+    ("delta", "elu1", "bf16", 64, 64, 200, True),
+    ("inner", "identity", "bf16", 64, 64, 130, True),
+    ("inner", "elu1", "bf16", 128, 128, 90, False),
+    ("inner", "identity", "f32", 64, 128, 65, True),
+    ("additive", "identity", "bf16", 128, 128, 150, True),
+    ("additive", "elu1", "f32", 64, 64, 77, False),
+    ("additive", "elu1", "bf16", 128, 64, 129, True),
+])
+def test_backward_matches_oracle(rule, phi, dtype, dk, dv, T, carried):
+    seed = (dk + dv + T) * 7 + carried
+    say(f"[bwd] {rule} {phi} {dtype} dk={dk} dv={dv} T={T} carried={carried}")
+    w, dO, dS, x0, h0 = _problem(rule, phi, dtype, dk, dv, T, carried, seed)
+    _compare(*_run(w, dO, dS, x0, h0, phi, carried))
+
+
+@pytest.mark.parametrize("rule", ["delta", "inner", "additive"])
+def test_backward_default_gates(rule):
+    """lambda absent (ridge 0 / retention 1) and, for the additive rule, beta absent (write
+    scale 1): their gradients are not asked for and the rest still match."""
+    say(f"[bwd] {rule} without lambda")
+    w, dO, dS, x0, h0 = _problem(rule, "identity", "bf16", 128, 128, 96, True, 5, lam_kind="none",
+                                 beta_kind="one" if rule == "additive" else None)
+    _compare(*_run(w, dO, dS, x0, h0, "identity", True, with_dS=False))
+
+
+def test_backward_lone_noop_step():
+    """T = 1 with no carried key: the delta rule's step neither decays nor writes, so only
+    the read has gradients; the final-state gradient passes straight through."""
+    say("[bwd] delta T=1 no carried key")
+    w, dO, dS, x0, h0 = _problem("delta", "identity", "f32", 64, 64, 1, False, 9)
+    g, ref = _run(w, dO, dS, x0, h0, "identity", False)
+    _compare(g, ref)
+    assert np.all(g["v"].cpu().numpy() == 0) and np.all(g["beta"].cpu().numpy() == 0)
+
+
+def test_backward_empty_sequence():
+    import torch
+    say("[bwd] T = 0")
+    B, H, d = 2, 3, 128
+    dS = np.random.default_rng(3).standard_normal((B, H, d, d)).astype(np.float32)
+    gS = make_state(B, H, d, d, S=dS)
+    e = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    g = F.scan_bwd(e, e, e, torch.empty((B, H, 0), device="cuda"), None,
+                   torch.empty((B, H, 0, d), device="cuda"), rule=wl.RULE_DELTA, grad_S_out=gS)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g["state"].S.cpu().numpy(), dS)
+    assert np.all(g["state"].x_prev.cpu().numpy() == 0)
+
+
+def test_backward_is_deterministic():
+    """Two calls on the same inputs give bit-identical gradients (no atomics)."""
+    say("[bwd] repeatability")
+    w, dO, dS, x0, h0 = _problem("delta", "identity", "bf16", 128, 128, 140, True, 11)
+    g1, _ = _run(w, dO, dS, x0, h0, "identity", True)
+    g2, _ = _run(w, dO, dS, x0, h0, "identity", True)
+    for n in ("q", "k", "v", "beta", "lam"):
+        assert np.array_equal(g1[n].cpu().numpy(), g2[n].cpu().numpy()), n
+    assert np.array_equal(g1["state"].buf.cpu().numpy(), g2["state"].buf.cpu().numpy())
