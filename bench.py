@@ -9,7 +9,9 @@ with bf16 q/k/v (beta = 2 sigmoid(N(0,1)), lambda = softplus(N(-4,1)), seed 0).
 Prints ONE JSON line. `value` comes from K steps timed back to back; `roofline` is for
 the longer of the two kernels, from HIP events recorded around every launch of a second
 run of K steps, on the stream the kernels run on. The decode kernel (fwmem_step at
-B=256, H=32, d=128) is measured in the same run and reported under `decode`.
+B=256, H=32, d=128) is measured in the same run and reported under `decode`, and the
+backward pass (fwmem_scan_bwd) on the same workload, where it supports the workload's
+mode, under `backward`.
 `cpu_baseline` is the fp64 oracle timed on the host (a bounded sample of the same
 workload: whole batch elements, about 10 s).
 
@@ -174,6 +176,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -313,6 +317,9 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(args.decode_steps, dev, stream)
 
+    if not args.no_backward and backward_supported(w):
+        result["backward"] = bench_backward(w, args.backward_steps, dev, stream, q, k, v, beta, lam)
+
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -333,6 +340,66 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(result), flush=True)
+
+
+def backward_supported(w):
+    from linear_attention_scan_amd import workloads as wl
+    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and not w.per_channel
+            and w.qk_norm is None and not w.znorm and not w.lam_scaled and w.dk in (64, 128)
+            and w.dv in (64, 128))
+
+
+def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
+    """fwmem_scan_bwd on the same workload (grad_out ~ N(0,1), zero final-state gradient):
+    the time of one launch, averaged over `steps` launches bracketed by HIP events on the
+    kernel's stream. Algorithmic bytes per (token, head): q, k, v in their input type, the
+    gates, grad_out and the float32 gradients of q, k, v and the gates; per head the
+    initial-state gradient."""
+    import torch
+
+    from linear_attention_scan_amd import fwmem as F
+    from linear_attention_scan_amd import workloads as wl
+    shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
+    flags = F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0
+    md = F.mode(w.rule, flags, w.eps, 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    gout = torch.randn((w.B, w.H, w.T, w.dv), generator=gen, device=dev)
+    gq = torch.empty((w.B, w.H, w.T, w.dk), device=dev)
+    gk, gv = torch.empty_like(gq), torch.empty((w.B, w.H, w.T, w.dv), device=dev)
+    gb = None if beta is None else torch.empty((w.B, w.H, w.T), device=dev)
+    gl = None if lam is None else torch.empty((w.B, w.H, w.T), device=dev)
+    gS = F.State(w.B, w.H, w.dk, w.dv, device=dev)
+    ws_n = F.bwd_workspace_bytes(shp, md)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+
+    def one():
+        st = F.scan_bwd_raw(shp, q, k, v, beta, lam, md, None, gout, None, gq, gk, gv, gb, gl,
+                            gS.buf, ws, ws_n, stream)
+        if st != F.OK:
+            raise F.FwmemError(st, "fwmem_scan_bwd")
+
+    one()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evs[0].record(stream)
+    for _ in range(steps):
+        one()
+    evs[1].record(stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(gk).all()), "non-finite gradient"
+    ms = evs[0].elapsed_time(evs[1]) / steps
+    es = 2 if w.dtype == "bf16" else 4
+    ngates = (beta is not None) + (lam is not None)
+    per_tok = (2 * w.dk + w.dv) * es + 4 * ngates + 4 * w.dv + 4 * (2 * w.dk + w.dv) + 4 * ngates
+    nbytes = w.B * w.H * (w.T * per_tok + w.dk * w.dv * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "bwd_kernel", "steps": steps, "ms": round(ms, 4),
+            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "workspace_bytes": ws_n,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                         "bytes_per_launch": nbytes}}
 
 
 def bench_decode(steps, dev, stream):

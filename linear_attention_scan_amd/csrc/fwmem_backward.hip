@@ -16,12 +16,14 @@
 //             G_{t-1} = gamma G
 // and for the shifted rules the scalar chain through a, eta and the denominator.
 //
-// One persistent 1024-thread workgroup per head, token-serial (a first, simple form; the
-// chunked backward is future work). The state is distributed as in the decode kernel:
-// thread (rg, cq) holds float4 column group cq of rows rg, rg + RG, ... A forward pass
-// stores the state at every chunk start; then, per chunk from the last, the chunk's states
-// after each token are recomputed into the workspace and the chunk's tokens are undone
-// from the last.
+// One persistent 1024-thread workgroup per head, token-serial (the chunked backward is
+// future work). The state is distributed as in the decode kernel: thread (rg, cq) holds
+// float4 column group cq of rows rg, rg + RG, ... A forward pass stores the state at every
+// chunk start in the workspace; then, per chunk from the last, the chunk's states after
+// each token are recomputed into the workspace and the chunk's tokens are undone from the
+// last. Each chunk's keys, queries, values, dO and gates are staged in LDS once, so a
+// token costs one workgroup barrier per pass (the column and scalar sums share it) and
+// the state before the next token to undo is loaded while the current one is undone.
 #include "fwmem_backward.h"
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
@@ -33,6 +35,13 @@ constexpr int NT = 1024;
 constexpr int NWV = NT / 64;
 constexpr int CH = kChunk;
 
+// Per-token scalars of the write: step size (or write scale) eta, decay a, the
+// denominator of eta, the write scale b, and whether the step writes at all.
+struct Sc {
+  float eta, a, den, b;
+  bool key;
+};
+
 template <typename InT, int DK, int DV, int RULE>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using R = Rule<RULE>;
@@ -40,11 +49,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   constexpr int RG = NT / TPRd;  // row groups
   constexpr int RPT = DK / RG;   // rows per thread
   static_assert(DK % RG == 0 && RPT >= 1, "shape");
-  __shared__ float s_x[DK], s_q[DK], s_w[DV];
-  __shared__ float s_col[NWV][DV];
-  __shared__ float s_sum[NWV][2];
-  __shared__ float s_eta[CH], s_a[CH], s_den[CH], s_b[CH];
-  __shared__ float s_n;
+  // One chunk at a time in LDS (147,712 bytes at dk = dv = 128).
+  __shared__ float s_x[CH][DK];   // written keys x_t (phi applied)
+  __shared__ float s_q[CH][DK];   // phi(q_t)
+  __shared__ float s_w[CH][DV];   // v_t; for the delta rule, the residual once recomputed
+  __shared__ float s_do[CH][DV];  // dO_t
+  __shared__ float s_col[2][NWV][DV];
+  __shared__ float s_sum[2][NWV][2];
+  __shared__ float s_n[CH], s_bt[CH], s_lm[CH];
 
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cq = tid % TPRd, rg = tid / TPRd;
@@ -58,24 +70,41 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const size_t SS = (size_t)DK * DV;
   float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV);
   float* cs = ckpt + (size_t)p.nchunks * SS;  // [CH] states after each token of a chunk
-  float* rr = cs + (size_t)CH * SS;           // [CH][DV] residuals of the chunk (delta)
 
   auto phi = [&](float x) { return elu ? phi_elu1(x) : x; };
-  auto dphi = [&](float x) { return elu ? (x > 0.f ? 1.f : __expf(x)) : 1.f; };
+  // phi'(z) from y = phi(z): 1 for the identity; for elu+1, 1 where z > 0 (y > 1) and
+  // exp(z) = y elsewhere
+  auto dphi_of = [&](float y) { return elu ? (y > 1.f ? 1.f : y) : 1.f; };
   auto row = [&](int j) { return rg + RG * j; };
 
-  // sum over the row groups of a per-thread float4 (the thread's four columns)
-  auto colsum = [&](f4 v) -> f4 {
+  // Sums over the workgroup, one barrier: a per-thread float4 (the thread's four
+  // columns) summed over the row groups, and two scalars summed over all threads. The
+  // two LDS buffers alternate, so a buffer is rewritten only after every thread has
+  // passed the barrier of the call in between.
+  int par = 0;
+  auto reduce = [&](f4 v, float a, float b, float& sa, float& sb) -> f4 {
 #pragma unroll
     for (int o = TPRd; o < 64; o <<= 1)
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], o);
-    if (lane < TPRd) *reinterpret_cast<f4*>(&s_col[wave][4 * cq]) = v;
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane < TPRd) *reinterpret_cast<f4*>(&s_col[par][wave][4 * cq]) = v;
+    if (lane == 0) {
+      s_sum[par][wave][0] = a;
+      s_sum[par][wave][1] = b;
+    }
     __syncthreads();
     f4 s = {0.f, 0.f, 0.f, 0.f};
+    sa = 0.f;
+    sb = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) s += *reinterpret_cast<const f4*>(&s_col[w][4 * cq]);
-    __syncthreads();
+    for (int w = 0; w < NWV; ++w) {
+      s += *reinterpret_cast<const f4*>(&s_col[par][w][4 * cq]);
+      sa += s_sum[par][w][0];
+      sb += s_sum[par][w][1];
+    }
+    par ^= 1;
     return s;
   };
   // sum over a row's TPRd consecutive lanes
@@ -83,24 +112,6 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int o = 1; o < TPRd; o <<= 1) v += __shfl_xor(v, o);
     return v;
-  };
-  // sums over the whole workgroup of two values
-  auto fullsum2 = [&](float a, float b, float& sa, float& sb) {
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane == 0) {
-      s_sum[wave][0] = a;
-      s_sum[wave][1] = b;
-    }
-    __syncthreads();
-    sa = 0.f;
-    sb = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      sa += s_sum[w][0];
-      sb += s_sum[w][1];
-    }
-    __syncthreads();
   };
   auto load_state = [&](const float* src, f4 (&S)[RPT]) {
 #pragma unroll
@@ -111,76 +122,88 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < RPT; ++j) *reinterpret_cast<f4*>(dst + (size_t)row(j) * DV + 4 * cq) = S[j];
   };
-  auto load_v = [&](int t) -> f4 {
-    f4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = In<InT>::load1(vb + (size_t)t * DV + 4 * cq + e);
-    return v;
-  };
-  // x_t into s_x (the written key), then its squared norm into s_n
-  auto stage_x = [&](int t) {
-    for (int i = tid; i < DK; i += NT) {
-      float x = 0.f;
-      if (R::shift) {
-        if (t >= 1) x = phi(In<InT>::load1(kb + (size_t)(t - 1) * DK + i));
-        else if (has_in && p.xprev_in != nullptr) x = p.xprev_in[(size_t)bh * DK + i];
-      } else {
-        x = phi(In<InT>::load1(kb + (size_t)t * DK + i));
+  // Tokens [t0, t1) of a chunk into LDS (rows past t1 zero): the written keys and their
+  // squared norms, v and the gates; for the backward also phi(q) and dO.
+  auto stage = [&](int t0, int t1, bool bwd) {
+    for (int idx = tid; idx < CH * DK; idx += NT) {
+      const int u = idx / DK, i = idx % DK, t = t0 + u;
+      float x = 0.f, qq = 0.f;
+      if (t < t1) {
+        if (R::shift) {
+          if (t >= 1) x = phi(In<InT>::load1(kb + (size_t)(t - 1) * DK + i));
+          else if (has_in && p.xprev_in != nullptr) x = p.xprev_in[(size_t)bh * DK + i];
+        } else {
+          x = phi(In<InT>::load1(kb + (size_t)t * DK + i));
+        }
+        if (bwd) qq = phi(In<InT>::load1(qb + (size_t)t * DK + i));
       }
-      s_x[i] = x;
+      s_x[u][i] = x;
+      if (bwd) s_q[u][i] = qq;
+    }
+    for (int idx = tid; idx < CH * DV; idx += NT) {
+      const int u = idx / DV, j = idx % DV, t = t0 + u;
+      s_w[u][j] = t < t1 ? In<InT>::load1(vb + (size_t)t * DV + j) : 0.f;
+      if (bwd) s_do[u][j] = t < t1 ? p.dout[(rb + t) * DV + j] : 0.f;
+    }
+    if (tid < CH) {
+      const int t = t0 + tid;
+      s_bt[tid] = (t < t1 && p.beta != nullptr) ? p.beta[rb + t] : 1.f;
+      s_lm[tid] = (t < t1 && p.lam != nullptr) ? p.lam[rb + t] : (R::nlms ? 0.f : 1.f);
     }
     __syncthreads();
-    if (wave == 0) {
+    for (int u = wave; u < CH; u += NWV) {
       float n = 0.f;
-      for (int i = lane; i < DK; i += 64) n += s_x[i] * s_x[i];
+      for (int i = lane; i < DK; i += 64) n += s_x[u][i] * s_x[u][i];
       n = wave_sum(n);
-      if (lane == 0) s_n = n;
+      if (lane == 0) s_n[u] = n;
     }
     __syncthreads();
   };
-  // one forward step at token t (u = t within its chunk), recording eta, a, den, beta
-  auto fwd_step = [&](int t, int u, f4 (&S)[RPT]) {
-    stage_x(t);
-    float eta, a, den = 1.f, b = 1.f;
+  auto scal = [&](int t, int u) -> Sc {
+    Sc s;
     if (R::nlms) {
-      const bool key = t >= 1 || has_in;
-      const float lam = p.lam != nullptr ? p.lam[rb + t] : 0.f;
-      den = s_n + lam + p.eps;
-      eta = key ? p.beta[rb + t] / den : 0.f;
-      a = 1.f - eta * lam;
+      s.key = t >= 1 || has_in;
+      s.den = s_n[u] + s_lm[u] + p.eps;
+      s.eta = s.key ? s_bt[u] / s.den : 0.f;
+      s.a = 1.f - s.eta * s_lm[u];
+      s.b = 1.f;
     } else {
-      b = p.beta != nullptr ? p.beta[rb + t] : 1.f;
-      eta = b;
-      a = p.lam != nullptr ? p.lam[rb + t] : 1.f;
+      s.key = true;
+      s.den = 1.f;
+      s.b = s_bt[u];
+      s.eta = s.b;
+      s.a = s_lm[u];
     }
-    if (tid == 0) {
-      s_eta[u] = eta;
-      s_a[u] = a;
-      s_den[u] = den;
-      s_b[u] = b;
-    }
-    f4 w = load_v(t);
+    return s;
+  };
+  // One forward step at token t (u within the chunk) on the registers S; for the delta
+  // rule the residual replaces v in s_w[u] (read by every thread before the barrier in
+  // reduce, written by row group 0 after it).
+  auto fwd_tok = [&](int t, int u, f4 (&S)[RPT]) {
+    const Sc s = scal(t, u);
+    f4 w = *reinterpret_cast<const f4*>(&s_w[u][4 * cq]);
     if (R::solve) {
       f4 pp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) pp += S[j] * s_x[row(j)];
-      w = w - colsum(pp);
-      if (rg == 0) *reinterpret_cast<f4*>(rr + (size_t)u * DV + 4 * cq) = w;
+      for (int j = 0; j < RPT; ++j) pp += S[j] * s_x[u][row(j)];
+      float d0, d1;
+      w = w - reduce(pp, 0.f, 0.f, d0, d1);
+      if (rg == 0) *reinterpret_cast<f4*>(&s_w[u][4 * cq]) = w;
     }
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) S[j] = S[j] * a + w * (eta * s_x[row(j)]);
-    __syncthreads();  // s_x is restaged by the next step
+    for (int j = 0; j < RPT; ++j) S[j] = S[j] * s.a + w * (s.eta * s_x[u][row(j)]);
   };
 
   // ---- forward: the state at every chunk start
   f4 S[RPT];
   load_state(p.S_in != nullptr ? p.S_in + (size_t)bh * SS : nullptr, S);
   for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * CH, t1 = min(T, t0 + CH);
     store_state(ckpt + (size_t)c * SS, S);
-    const int t1 = min(T, (c + 1) * CH);
-    for (int t = c * CH; t < t1; ++t) fwd_step(t, t - c * CH, S);
+    stage(t0, t1, false);
+    for (int t = t0; t < t1; ++t) fwd_tok(t, t - t0, S);
+    __syncthreads();  // LDS is restaged for the next chunk
   }
-  __syncthreads();
 
   // ---- backward
   f4 G[RPT];
@@ -188,120 +211,116 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   if (R::shift && T >= 1)  // the last key is written by no step of this call
     for (int i = tid; i < DK; i += NT) p.gk[(rb + T - 1) * DK + i] = 0.f;
   for (int c = p.nchunks - 1; c >= 0; --c) {
-    const int t0 = c * CH, t1 = min(T, t0 + CH);
-    // recompute the chunk's states after each token (and its scalars and residuals)
-    load_state(ckpt + (size_t)c * SS, S);
-    __threadfence_block();
+    const int t0 = c * CH, t1 = min(T, t0 + CH), len = t1 - t0;
+    const float* start = ckpt + (size_t)c * SS;
+    // recompute the chunk's states after each token (the last one stays in S)
+    stage(t0, t1, true);
+    load_state(start, S);
     for (int t = t0; t < t1; ++t) {
-      fwd_step(t, t - t0, S);
-      store_state(cs + (size_t)(t - t0) * SS, S);
+      fwd_tok(t, t - t0, S);
+      if (t + 1 < t1) store_state(cs + (size_t)(t - t0) * SS, S);
     }
-    __threadfence_block();
-    __syncthreads();
-    for (int t = t1 - 1; t >= t0; --t) {
+    __syncthreads();  // the residuals in s_w are read by every thread below
+    // the read's gradient dphi(q_t) = S_t dO_t, from the state after token t: for the
+    // chunk's last token from S, for the others while token t + 1 is undone (its Sp)
+    auto read_grad = [&](int t, const f4 (&St)[RPT]) {
       const int u = t - t0;
-      f4 St[RPT], Sp[RPT];
-      load_state(cs + (size_t)u * SS, St);
-      load_state(u > 0 ? cs + (size_t)(u - 1) * SS : ckpt + (size_t)c * SS, Sp);
-      stage_x(t);
-      for (int i = tid; i < DK; i += NT) s_q[i] = phi(In<InT>::load1(qb + (size_t)t * DK + i));
-      __syncthreads();
-      f4 dO;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dO[e] = p.dout[(rb + t) * DV + 4 * cq + e];
-      // the read: dphi(q) = S_t dO, G += phi(q) dO^T
+      const f4 dO = *reinterpret_cast<const f4*>(&s_do[u][4 * cq]);
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         const f4 m = St[j] * dO;
         const float dqi = rowsum(m[0] + m[1] + m[2] + m[3]);
-        if (cq == 0) p.gq[(rb + t) * DK + row(j)] = dqi * dphi(In<InT>::load1(qb + (size_t)t * DK + row(j)));
-        G[j] += dO * s_q[row(j)];
+        if (cq == 0) p.gq[(rb + t) * DK + row(j)] = dqi * dphi_of(s_q[u][row(j)]);
       }
-      const float eta = s_eta[u], a = s_a[u], den = s_den[u], b = s_b[u];
-      const bool key = !R::shift || t >= 1 || has_in;
-      if (!key) {  // no write: S_t = S_{t-1}; nothing else depends on this step
+    };
+    read_grad(t1 - 1, S);
+    // Sp: the state before token t (after t - 1); nx: before t - 1
+    f4 Sp[RPT];
+    load_state(len >= 2 ? cs + (size_t)(len - 2) * SS : start, Sp);
+    for (int t = t1 - 1; t >= t0; --t) {
+      const int u = t - t0;
+      if (u >= 1) read_grad(t - 1, Sp);
+      const f4 dO = *reinterpret_cast<const f4*>(&s_do[u][4 * cq]);
+      f4 nx[RPT];
+      if (u >= 1) load_state(u >= 2 ? cs + (size_t)(u - 2) * SS : start, nx);
+      else
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) nx[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) G[j] += dO * s_q[u][row(j)];  // the read: G += phi(q) dO^T
+      const Sc s = scal(t, u);
+      if (!s.key) {  // no write: S_t = S_{t-1}; nothing else depends on this step
         if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = f4{0.f, 0.f, 0.f, 0.f};
         if (tid == 0) {
           if (p.gbeta != nullptr) p.gbeta[rb + t] = 0.f;
           if (p.glam != nullptr) p.glam[rb + t] = 0.f;
         }
-        for (int i = tid; i < DK; i += NT)
-          if (p.gx0 != nullptr) p.gx0[(size_t)bh * DK + i] = 0.f;
-        __syncthreads();
-        continue;
-      }
-      // w: the residual (delta) or the value; G w per row; <G, S_{t-1}> and x^T G w
-      const f4 w = R::solve ? *reinterpret_cast<const f4*>(rr + (size_t)u * DV + 4 * cq) : load_v(t);
-      float gw[RPT], da_p = 0.f, xgw_p = 0.f;
-#pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        const f4 m = G[j] * w;
-        gw[j] = rowsum(m[0] + m[1] + m[2] + m[3]);
-        const f4 d = G[j] * Sp[j];
-        da_p += d[0] + d[1] + d[2] + d[3];
-        if (cq == 0) xgw_p += s_x[row(j)] * gw[j];
-      }
-      float da, xgw;
-      fullsum2(da_p, xgw_p, da, xgw);
-      if (R::nlms) {
-        // G^T x (columns), then dx per row
-        f4 gx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) gx += G[j] * s_x[row(j)];
-        const f4 gtx = colsum(gx);
-        const f4 dr = gtx * eta;  // delta: dr; inner: dv
-        float dxv[RPT];
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-          dxv[j] = eta * gw[j];
-          if (R::solve) {
-            const f4 m = Sp[j] * dr;
-            dxv[j] -= rowsum(m[0] + m[1] + m[2] + m[3]);
-          }
-        }
-        if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = dr;
-        // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps
-        const float lam = p.lam != nullptr ? p.lam[rb + t] : 0.f;
-        const float deta = xgw - lam * da;
-        const float dden = -eta * deta / den;
-        if (tid == 0) {
-          if (p.gbeta != nullptr) p.gbeta[rb + t] = deta / den;
-          if (p.glam != nullptr) p.glam[rb + t] = -eta * da + dden;
-        }
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-          if (cq == 0) {
-            const float dx = dxv[j] + 2.f * s_x[row(j)] * dden;
-            if (t >= 1) p.gk[(rb + t - 1) * DK + row(j)] = dx * dphi(In<InT>::load1(kb + (size_t)(t - 1) * DK + row(j)));
-            else if (p.gx0 != nullptr) p.gx0[(size_t)bh * DK + row(j)] = dx;
-          }
-          G[j] = G[j] * a - (R::solve ? dr * s_x[row(j)] : f4{0.f, 0.f, 0.f, 0.f});
-        }
+        if (p.gx0 != nullptr)
+          for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
       } else {
-        // additive: x is phi(k_t), b the write scale, a the retention
+        // w: the residual (delta) or the value; G w per row; <G, S_{t-1}>, x^T G w, G^T x
+        const f4 w = *reinterpret_cast<const f4*>(&s_w[u][4 * cq]);
+        float gw[RPT], da_p = 0.f, xgw_p = 0.f;
         f4 gx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) gx += G[j] * s_x[row(j)];
-        const f4 gtx = colsum(gx);
-        if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = gtx * b;
-        if (tid == 0) {
-          if (p.gbeta != nullptr) p.gbeta[rb + t] = xgw;
-          if (p.glam != nullptr) p.glam[rb + t] = da;
-        }
-#pragma unroll
         for (int j = 0; j < RPT; ++j) {
-          if (cq == 0) p.gk[(rb + t) * DK + row(j)] = b * gw[j] * dphi(In<InT>::load1(kb + (size_t)t * DK + row(j)));
-          G[j] = G[j] * a;
+          const float x = s_x[u][row(j)];
+          const f4 m = G[j] * w;
+          gw[j] = rowsum(m[0] + m[1] + m[2] + m[3]);
+          const f4 d = G[j] * Sp[j];
+          da_p += d[0] + d[1] + d[2] + d[3];
+          if (cq == 0) xgw_p += x * gw[j];
+          gx += G[j] * x;
+        }
+        float da, xgw;
+        const f4 gtx = reduce(gx, da_p, xgw_p, da, xgw);
+        if (R::nlms) {
+          const f4 dr = gtx * s.eta;  // delta: dL/dr; inner: dL/dv
+          if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = dr;
+          // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps
+          const float lam = s_lm[u];
+          const float deta = xgw - lam * da;
+          const float dden = -s.eta * deta / s.den;
+          if (tid == 0) {
+            if (p.gbeta != nullptr) p.gbeta[rb + t] = deta / s.den;
+            if (p.glam != nullptr) p.glam[rb + t] = -s.eta * da + dden;
+          }
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) {
+            const float x = s_x[u][row(j)];
+            float dx = s.eta * gw[j] + 2.f * x * dden;
+            if (R::solve) {
+              const f4 m = Sp[j] * dr;
+              dx -= rowsum(m[0] + m[1] + m[2] + m[3]);
+            }
+            if (cq == 0) {
+              if (t >= 1) p.gk[(rb + t - 1) * DK + row(j)] = dx * dphi_of(x);
+              else if (p.gx0 != nullptr) p.gx0[(size_t)bh * DK + row(j)] = dx;
+            }
+            G[j] = G[j] * s.a - (R::solve ? dr * x : f4{0.f, 0.f, 0.f, 0.f});
+          }
+        } else {
+          // additive: x = phi(k_t), b the write scale, a the retention
+          if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = gtx * s.b;
+          if (tid == 0) {
+            if (p.gbeta != nullptr) p.gbeta[rb + t] = xgw;
+            if (p.glam != nullptr) p.glam[rb + t] = da;
+          }
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) {
+            if (cq == 0) p.gk[(rb + t) * DK + row(j)] = s.b * gw[j] * dphi_of(s_x[u][row(j)]);
+            G[j] = G[j] * s.a;
+          }
         }
       }
-      __syncthreads();  // s_x, s_q are restaged by the next token
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) Sp[j] = nx[j];
     }
+    __syncthreads();  // LDS is restaged for the previous chunk
   }
   if (p.gS0 != nullptr) store_state(p.gS0 + (size_t)bh * SS, G);
   if (p.gh0 != nullptr && tid == 0) p.gh0[bh] = 0;
-  if (!R::shift && p.gx0 != nullptr)
-    for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
-  if (R::shift && T == 0 && p.gx0 != nullptr)
+  if (p.gx0 != nullptr && (!R::shift || T == 0))
     for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
 }
 
