@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "linear_attention_scan_amd", "csrc")
 
-# HBM traffic per launch of the scan kernels on the default workload (B=4 H=16 T=4096
-# d=128, bf16, delta rule) and of the decode kernel (B=256 H=32 d=128, state in place),
+# HBM traffic per launch of the scan kernels and the backward kernel on the default
+# workload (B=4 H=16 T=4096 d=128, bf16, delta rule) and of the decode kernel (B=256 H=32 d=128, state in place),
 # from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in runs of their own, each scaled by
 # what the same counter reads for a plain 1 GiB device copy in the same run
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0). A record is reported only while the
@@ -69,6 +69,16 @@ MEASURED_TRAFFIC = {
             "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
         "fetch_kib": 267730.8, "write_kib": 532885.4, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("delta_bf16_h16", "bwd_kernel"): {
+        "sources": ("fwmem_backward.hip", "fwmem_backward.h", "fwmem_device.h", "fwmem_internal.h"),
+        "sha256": {
+            "fwmem_backward.hip": "790c6c9a792b04bdb7c3727d97a68cc6820439a3bd268130a2633f4919a044d9",
+            "fwmem_backward.h": "92c342f33812dc92af5c4078b88948b12c4c833abf6ee3120bdd6d6b9f7652e3",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
+        },
+        "fetch_kib": 8972945.6, "write_kib": 17186882.5, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
@@ -398,7 +408,8 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "workspace_bytes": ws_n,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+                         "traffic": measured_traffic(w.name, "bwd_kernel"),
                          "bytes_per_launch": nbytes}}
 
 
