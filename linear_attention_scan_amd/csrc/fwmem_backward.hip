@@ -35,10 +35,21 @@ constexpr int NT = 1024;
 constexpr int NWV = NT / 64;
 constexpr int CH = kChunk;
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations are complete
+// before it arrives and the compiler moves no memory access across it, but its global loads
+// stay in flight (__syncthreads would wait for them), so the prefetch of the next state
+// overlaps the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Per-token scalars of the write: step size (or write scale) eta, decay a, the
 // denominator of eta, the write scale b, and whether the step writes at all.
 struct Sc {
-  float eta, a, den, b;
+  float eta, a, den, rden, b;
   bool key;
 };
 
@@ -50,12 +61,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   constexpr int RPT = DK / RG;   // rows per thread
   static_assert(DK % RG == 0 && RPT >= 1, "shape");
   // One chunk at a time in LDS (147,712 bytes at dk = dv = 128).
+  // (float4 accesses: s_w, s_do, s_col and s_tot rows are 16-byte aligned)
   __shared__ float s_x[CH][DK];   // written keys x_t (phi applied)
   __shared__ float s_q[CH][DK];   // phi(q_t)
-  __shared__ float s_w[CH][DV];   // v_t; for the delta rule, the residual once recomputed
-  __shared__ float s_do[CH][DV];  // dO_t
-  __shared__ float s_col[2][NWV][DV];
+  __shared__ __attribute__((aligned(16))) float s_w[CH][DV];   // v_t; delta: the residual once recomputed
+  __shared__ __attribute__((aligned(16))) float s_do[CH][DV];  // dO_t
+  __shared__ __attribute__((aligned(16))) float s_col[2][NWV][DV];
   __shared__ float s_sum[2][NWV][2];
+  __shared__ __attribute__((aligned(16))) float s_tot[2][DV + 4];  // column totals, then the two scalars
   __shared__ float s_n[CH], s_bt[CH], s_lm[CH];
 
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -77,10 +90,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   auto dphi_of = [&](float y) { return elu ? (y > 1.f ? 1.f : y) : 1.f; };
   auto row = [&](int j) { return rg + RG * j; };
 
-  // Sums over the workgroup, one barrier: a per-thread float4 (the thread's four
-  // columns) summed over the row groups, and two scalars summed over all threads. The
-  // two LDS buffers alternate, so a buffer is rewritten only after every thread has
-  // passed the barrier of the call in between.
+  // Sums over the workgroup: a per-thread float4 (the thread's four columns) summed over
+  // the row groups, and two scalars summed over all threads. Each wave leaves its partial
+  // sums in LDS; after a barrier DV + 2 threads add the waves' partials of one value each;
+  // after a second barrier every thread reads the totals. The two sets of LDS buffers
+  // alternate, so a buffer is rewritten only after every thread has passed the barriers
+  // of the call in between.
   int par = 0;
   auto reduce = [&](f4 v, float a, float b, float& sa, float& sb) -> f4 {
 #pragma unroll
@@ -94,16 +109,22 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       s_sum[par][wave][0] = a;
       s_sum[par][wave][1] = b;
     }
-    __syncthreads();
-    f4 s = {0.f, 0.f, 0.f, 0.f};
-    sa = 0.f;
-    sb = 0.f;
+    lds_barrier();
+    if (tid < DV + 2) {
+      float x = 0.f;
+      if (tid < DV) {
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      s += *reinterpret_cast<const f4*>(&s_col[par][w][4 * cq]);
-      sa += s_sum[par][w][0];
-      sb += s_sum[par][w][1];
+        for (int w = 0; w < NWV; ++w) x += s_col[par][w][tid];
+      } else {
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) x += s_sum[par][w][tid - DV];
+      }
+      s_tot[par][tid] = x;
     }
+    lds_barrier();
+    const f4 s = *reinterpret_cast<const f4*>(&s_tot[par][4 * cq]);
+    sa = s_tot[par][DV];
+    sb = s_tot[par][DV + 1];
     par ^= 1;
     return s;
   };
@@ -164,12 +185,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     if (R::nlms) {
       s.key = t >= 1 || has_in;
       s.den = s_n[u] + s_lm[u] + p.eps;
-      s.eta = s.key ? s_bt[u] / s.den : 0.f;
+      s.rden = __builtin_amdgcn_rcpf(s.den);
+      s.eta = s.key ? s_bt[u] * s.rden : 0.f;
       s.a = 1.f - s.eta * s_lm[u];
       s.b = 1.f;
     } else {
       s.key = true;
       s.den = 1.f;
+      s.rden = 1.f;
       s.b = s_bt[u];
       s.eta = s.b;
       s.a = s_lm[u];
@@ -280,9 +303,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps
           const float lam = s_lm[u];
           const float deta = xgw - lam * da;
-          const float dden = -s.eta * deta / s.den;
+          const float dden = -s.eta * deta * s.rden;
           if (tid == 0) {
-            if (p.gbeta != nullptr) p.gbeta[rb + t] = deta / s.den;
+            if (p.gbeta != nullptr) p.gbeta[rb + t] = deta * s.rden;
             if (p.glam != nullptr) p.glam[rb + t] = -s.eta * da + dden;
           }
 #pragma unroll
