@@ -133,3 +133,40 @@ def test_backward_is_deterministic():
     for n in ("q", "k", "v", "beta", "lam"):
         assert np.array_equal(g1[n].cpu().numpy(), g2[n].cpu().numpy()), n
     assert np.array_equal(g1["state"].buf.cpu().numpy(), g2["state"].buf.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("delta_bf16_h16", [(0, 3), (3, 15)]),   # the benchmark shape, B4 H16 T4096
+    ("inner_bf16", [(2, 5)]),                # B4 H8 T4096
+    ("additive_bf16", [(1, 9)]),             # B2 H16 T16384, elu+1
+])
+def test_backward_full_size_sampled_heads(name, heads):
+    """The whole workload at its full size through one backward launch, as bench.py
+    times it (grad_out ~ N(0,1), no final-state gradient); the oracle then follows a
+    few heads on their own (heads are independent), every gradient compared."""
+    import torch
+    w = wl.SCAN_WORKLOADS[name](seed=0)
+    say(f"[bwd full] {name} B={w.B} H={w.H} T={w.T}: oracle on heads {heads}")
+    dO = np.random.default_rng(77).standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
+    flags = F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(w.beta), f32_tensor(w.lam), f32_tensor(dO), rule=w.rule,
+                   flags=flags, eps=w.eps)
+    torch.cuda.synchronize()
+    for b, h in heads:
+        sl = lambda a: None if a is None else a[b:b + 1, h:h + 1]
+        ref = orc.scan_backward(sl(w.q), sl(w.k), sl(w.v), sl(w.beta), sl(w.lam), sl(dO),
+                                rule=w.rule, phi_kind=w.phi, eps=w.eps)
+        got = {n: None if g[n] is None else g[n][b:b + 1, h:h + 1]
+               for n in ("q", "k", "v", "beta", "lam")}
+        errs = {}
+        for n, x in got.items():
+            if ref[n] is None:
+                assert x is None, n
+                continue
+            errs[n] = orc.relerr(x.cpu().numpy().astype(np.float64), ref[n])
+        errs["S0"] = orc.relerr(g["state"].S[b:b + 1, h:h + 1].cpu().numpy().astype(np.float64),
+                                ref["S0"])
+        say(f"    head ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["f32"], f"grad {n}: {e:.3e}"
