@@ -354,9 +354,8 @@ def main():
 
 def backward_supported(w):
     from linear_attention_scan_amd import workloads as wl
-    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and not w.per_channel
-            and w.qk_norm is None and not w.znorm and not w.lam_scaled and w.dk in (64, 128)
-            and w.dv in (64, 128))
+    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and w.qk_norm is None
+            and not w.znorm and not w.lam_scaled and w.dk in (64, 128) and w.dv in (64, 128))
 
 
 def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
@@ -370,7 +369,7 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     from linear_attention_scan_amd import fwmem as F
     from linear_attention_scan_amd import workloads as wl
     shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
-    flags = F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0
+    flags = (F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
     md = F.mode(w.rule, flags, w.eps, 0)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
@@ -378,7 +377,7 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     gq = torch.empty((w.B, w.H, w.T, w.dk), device=dev)
     gk, gv = torch.empty_like(gq), torch.empty((w.B, w.H, w.T, w.dv), device=dev)
     gb = None if beta is None else torch.empty((w.B, w.H, w.T), device=dev)
-    gl = None if lam is None else torch.empty((w.B, w.H, w.T), device=dev)
+    gl = None if lam is None else torch.empty(tuple(lam.shape), device=dev)
     gS = F.State(w.B, w.H, w.dk, w.dv, device=dev)
     ws_n = F.bwd_workspace_bytes(shp, md)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
@@ -400,7 +399,7 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     assert bool(torch.isfinite(gk).all()), "non-finite gradient"
     ms = evs[0].elapsed_time(evs[1]) / steps
     es = 2 if w.dtype == "bf16" else 4
-    ngates = (beta is not None) + (lam is not None)
+    ngates = (beta is not None) + (lam is not None) * (w.dk if w.per_channel else 1)
     per_tok = (2 * w.dk + w.dv) * es + 4 * ngates + 4 * w.dv + 4 * (2 * w.dk + w.dv) + 4 * ngates
     nbytes = w.B * w.H * (w.T * per_tok + w.dk * w.dv * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -234,9 +234,10 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
                         const void* S_in, void* out, void* S_out, fwmem_stream stream);
 
 /* Bytes of device workspace fwmem_scan_bwd needs for this shape and mode (0 when T == 0
- * or B*H == 0): per head, the state at each 64-token chunk start plus 65 chunk-sized
- * state buffers' worth of scratch, i.e. 4 * ((ceil(T/64) + 64) * dk * dv + 64 * dv)
- * bytes. Its contents need no initialisation and are scratch only. */
+ * or B*H == 0): with C = 64 (32 with FWMEM_LAMBDA_PER_CHANNEL), per head the state at
+ * each C-token chunk start plus C more state buffers and C d_v-vectors of scratch, i.e.
+ * 4 * ((ceil(T/C) + C) * dk * dv + C * dv) bytes, rounded up to a multiple of 256.
+ * Its contents need no initialisation and are scratch only. */
 fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
                                             size_t* bytes);
 
@@ -248,9 +249,10 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  * 3.2); this is its exact reverse-mode derivative, token by token, with the forward
  * states recomputed from a state kept at every chunk start.
  *
- * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE; flags 0 or
- * FWMEM_PHI_ELU1 (anything else: FWMEM_EUNSUPPORTED); a scalar lambda; dk and dv in
- * {64, 128}.
+ * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE; flags from
+ * FWMEM_PHI_ELU1 and FWMEM_LAMBDA_PER_CHANNEL (anything else: FWMEM_EUNSUPPORTED); dk
+ * and dv in {64, 128}. With a per-channel lambda, the denominator's gradient goes to the
+ * first channel holding the largest lambda_i.
  *
  *   q, k, v, beta, lambda, S_in: exactly as passed to fwmem_scan_fwd (read only)
  *   grad_out     [B][H][T][dv] float32  (required when T > 0)
@@ -258,9 +260,10 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  *                state's carried key and flag take no gradient
  *   grad_q, grad_k [B][H][T][dk] float32; grad_v [B][H][T][dv] float32 (required when
  *                T > 0; every element is written)
- *   grad_beta, grad_lambda [B][H][T] float32 or NULL (not written). With beta or lambda
- *                NULL they are the gradients at the default value (write scale 1,
- *                ridge 0, retention 1).
+ *   grad_beta    [B][H][T] float32 or NULL (not written)
+ *   grad_lambda  lambda's shape ([B][H][T], or [B][H][T][dk] per channel) float32, or
+ *                NULL (not written). With beta or lambda NULL these are the gradients
+ *                at the default value (write scale 1, ridge 0, retention 1).
  *   grad_S_in    state buffer or NULL: its S part receives dL/dS_0, its x_prev part
  *                dL/dx_prev (with respect to the carried key as stored, phi already
  *                applied; zero without a carried key and for the additive rule), its

@@ -504,15 +504,17 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
   if (st != FWMEM_OK) return st;
   st = check_scan_mode(mode);
   if (st != FWMEM_OK) return st;
-  if (mode->rule == FWMEM_RULE_DELTA_PV || (mode->flags & ~(uint32_t)FWMEM_PHI_ELU1) != 0)
+  if (mode->rule == FWMEM_RULE_DELTA_PV ||
+      (mode->flags & ~(uint32_t)(FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL)) != 0)
     return FWMEM_EUNSUPPORTED;
   if (!fwmem::bwd_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;
 }
 
-size_t bwd_ws_bytes(const fwmem_shape* shape) {
+size_t bwd_ws_bytes(const fwmem_shape* shape, const fwmem_mode* mode) {
   const size_t BH = (size_t)shape->B * (size_t)shape->H;
-  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv));
+  const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
+  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, pc));
 }
 
 }  // namespace
@@ -524,7 +526,7 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
   if (bytes == nullptr) return FWMEM_EINVAL;
   const fwmem_status st = check_bwd(shape, mode);
   if (st != FWMEM_OK) return st;
-  *bytes = bwd_ws_bytes(shape);
+  *bytes = bwd_ws_bytes(shape, mode);
   return FWMEM_OK;
 }
 
@@ -546,7 +548,7 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
                 grad_q == nullptr || grad_k == nullptr || grad_v == nullptr))
     return FWMEM_EINVAL;
   if (T == 0 && grad_S_in == nullptr) return FWMEM_OK;
-  const size_t need = bwd_ws_bytes(shape);
+  const size_t need = bwd_ws_bytes(shape, mode);
   if (ws_bytes < need || (need > 0 && workspace == nullptr)) return FWMEM_EWORKSPACE;
   const size_t es = esize(shape->dtype);
   if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(beta, 4) ||
@@ -558,11 +560,12 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   if (z.BH * T > 0x7fffffffu || z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
   const size_t nq = z.BH * T * shape->dk * es, nv = z.BH * T * shape->dv * es;
   const size_t ns = z.BH * T * 4, nsb = z.state_bytes;
+  const size_t nl = ns * ((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) ? (size_t)shape->dk : 1);
   const size_t ngq = z.BH * T * shape->dk * 4, ngv = z.BH * T * shape->dv * 4;
   const void* ins[] = {q, k, v, beta, lambda, S_in, grad_out, grad_S_out};
-  const size_t nins[] = {nq, nq, nv, ns, ns, nsb, ngv, nsb};
+  const size_t nins[] = {nq, nq, nv, ns, nl, nsb, ngv, nsb};
   const void* outs[] = {grad_q, grad_k, grad_v, grad_beta, grad_lambda, grad_S_in, workspace};
-  const size_t nouts[] = {ngq, ngq, ngv, ns, ns, nsb, need};
+  const size_t nouts[] = {ngq, ngq, ngv, ns, nl, nsb, need};
   for (int i = 0; i < 7; ++i) {
     for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], nouts[i], ins[j], nins[j])) return FWMEM_EOVERLAP;
@@ -597,7 +600,8 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.T = (int)T;
   p.dk = shape->dk;
   p.dv = shape->dv;
-  p.nchunks = (int)((T + kChunk - 1) / kChunk);
+  const int ck = fwmem::bwd_chunk((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0);
+  p.nchunks = (int)((T + ck - 1) / ck);
   p.rule = mode->rule;
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
   p.flags = mode->flags;

@@ -1,6 +1,7 @@
 // Backward pass of the scan: the gradients of L = <dO, o> + <dS_T, S_T> with respect to
 // q, k, v, beta, lambda, the initial state S0 and the carried key, for the delta, inner and
-// additive rules with phi identity or elu+1 and a scalar lambda. The pages give no backward
+// additive rules with phi identity or elu+1 and a scalar or per-channel lambda. The pages
+// give no backward
 // pass; this is the reverse-mode derivative of the recurrence as the forward pass states it
 // ("Fast Weight Attention for Continual Learning" reading notes, sections 3.2, 4.1-4.3;
 // "attention is also an FFN", sections 2.1, 3.2):
@@ -16,8 +17,12 @@
 //             G_{t-1} = gamma G
 // and for the shifted rules the scalar chain through a, eta and the denominator.
 //
+// Per channel, lambda_i scales row i's decay (1 - eta lambda_i, or the retention gamma_i)
+// and eta's denominator takes the largest lambda_i; da and the lambda gradient are then
+// per row.
+//
 // One persistent 1024-thread workgroup per head, token-serial (the chunked backward is
-// future work). The state is distributed as in the decode kernel: thread (rg, cq) holds
+// future work). A chunk here is 64 tokens, 32 with a per-channel lambda. The state is distributed as in the decode kernel: thread (rg, cq) holds
 // float4 column group cq of rows rg, rg + RG, ... A forward pass stores the state at every
 // chunk start in the workspace; then, per chunk from the last, the chunk's states after
 // each token are recomputed into the workspace and the chunk's tokens are undone from the
@@ -33,7 +38,6 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int NWV = NT / 64;
-constexpr int CH = kChunk;
 
 // Workgroup barrier that orders LDS accesses only: this wave's LDS operations are complete
 // before it arrives and the compiler moves no memory access across it, but its global loads
@@ -53,23 +57,29 @@ struct Sc {
   bool key;
 };
 
-template <typename InT, int DK, int DV, int RULE>
+template <typename InT, int DK, int DV, int RULE, bool PCX>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using R = Rule<RULE>;
+  // tokens staged at a time, and between stored states (per-channel lambda, also staged,
+  // halves it to fit LDS)
+  constexpr int CK = bwd_chunk(PCX);
   constexpr int TPRd = DV / 4;   // threads per row
   constexpr int RG = NT / TPRd;  // row groups
   constexpr int RPT = DK / RG;   // rows per thread
   static_assert(DK % RG == 0 && RPT >= 1, "shape");
-  // One chunk at a time in LDS (147,712 bytes at dk = dv = 128).
+  // One chunk at a time in LDS (149,536 bytes at dk = dv = 128; 100,128 with a per-channel
+  // lambda).
   // (float4 accesses: s_w, s_do, s_col and s_tot rows are 16-byte aligned)
-  __shared__ float s_x[CH][DK];   // written keys x_t (phi applied)
-  __shared__ float s_q[CH][DK];   // phi(q_t)
-  __shared__ __attribute__((aligned(16))) float s_w[CH][DV];   // v_t; delta: the residual once recomputed
-  __shared__ __attribute__((aligned(16))) float s_do[CH][DV];  // dO_t
+  __shared__ float s_x[CK][DK];   // written keys x_t (phi applied)
+  __shared__ float s_q[CK][DK];   // phi(q_t)
+  __shared__ __attribute__((aligned(16))) float s_w[CK][DV];   // v_t; delta: the residual once recomputed
+  __shared__ __attribute__((aligned(16))) float s_do[CK][DV];  // dO_t
   __shared__ __attribute__((aligned(16))) float s_col[2][NWV][DV];
   __shared__ float s_sum[2][NWV][2];
   __shared__ __attribute__((aligned(16))) float s_tot[2][DV + 4];  // column totals, then the two scalars
-  __shared__ float s_n[CH], s_bt[CH], s_lm[CH];
+  __shared__ float s_lc[PCX ? CK : 1][PCX ? DK : 1];  // per-channel lambda (or retention)
+  __shared__ float s_n[CK], s_bt[CK], s_lm[CK];  // |x|^2, beta, lambda (per channel: its maximum)
+  __shared__ int s_im[CK];                        // per channel: the first channel at the maximum
 
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cq = tid % TPRd, rg = tid / TPRd;
@@ -81,8 +91,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
   const size_t SS = (size_t)DK * DV;
-  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV);
-  float* cs = ckpt + (size_t)p.nchunks * SS;  // [CH] states after each token of a chunk
+  const int nch = (T + CK - 1) / CK;
+  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV, PCX);
+  float* cs = ckpt + (size_t)nch * SS;  // [CK] states after each token of a chunk
 
   auto phi = [&](float x) { return elu ? phi_elu1(x) : x; };
   // phi'(z) from y = phi(z): 1 for the identity; for elu+1, 1 where z > 0 (y > 1) and
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // Tokens [t0, t1) of a chunk into LDS (rows past t1 zero): the written keys and their
   // squared norms, v and the gates; for the backward also phi(q) and dO.
   auto stage = [&](int t0, int t1, bool bwd) {
-    for (int idx = tid; idx < CH * DK; idx += NT) {
+    for (int idx = tid; idx < CK * DK; idx += NT) {
       const int u = idx / DK, i = idx % DK, t = t0 + u;
       float x = 0.f, qq = 0.f;
       if (t < t1) {
@@ -160,25 +171,56 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
       s_x[u][i] = x;
       if (bwd) s_q[u][i] = qq;
+      if (PCX) s_lc[u][i] = (t < t1 && p.lam != nullptr) ? p.lam[(rb + t) * DK + i] : (R::nlms ? 0.f : 1.f);
     }
-    for (int idx = tid; idx < CH * DV; idx += NT) {
+    for (int idx = tid; idx < CK * DV; idx += NT) {
       const int u = idx / DV, j = idx % DV, t = t0 + u;
       s_w[u][j] = t < t1 ? In<InT>::load1(vb + (size_t)t * DV + j) : 0.f;
       if (bwd) s_do[u][j] = t < t1 ? p.dout[(rb + t) * DV + j] : 0.f;
     }
-    if (tid < CH) {
+    if (tid < CK) {
       const int t = t0 + tid;
       s_bt[tid] = (t < t1 && p.beta != nullptr) ? p.beta[rb + t] : 1.f;
-      s_lm[tid] = (t < t1 && p.lam != nullptr) ? p.lam[rb + t] : (R::nlms ? 0.f : 1.f);
+      if (!PCX) s_lm[tid] = (t < t1 && p.lam != nullptr) ? p.lam[rb + t] : (R::nlms ? 0.f : 1.f);
     }
     __syncthreads();
-    for (int u = wave; u < CH; u += NWV) {
+    for (int u = wave; u < CK; u += NWV) {
       float n = 0.f;
       for (int i = lane; i < DK; i += 64) n += s_x[u][i] * s_x[u][i];
       n = wave_sum(n);
       if (lane == 0) s_n[u] = n;
+      if (PCX && R::nlms) {
+        // the largest lambda over the channels and the first channel holding it
+        float best = s_lc[u][lane];
+        int bi = lane;
+        for (int i = lane + 64; i < DK; i += 64)
+          if (s_lc[u][i] > best) {
+            best = s_lc[u][i];
+            bi = i;
+          }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float ob = __shfl_xor(best, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ob > best || (ob == best && oi < bi)) {
+            best = ob;
+            bi = oi;
+          }
+        }
+        if (lane == 0) {
+          s_lm[u] = best;
+          s_im[u] = bi;
+        }
+      }
     }
     __syncthreads();
+  };
+  // decay of row j at token u: 1 - eta lambda_i (ridge rules) or gamma_i (additive) per
+  // channel, else the token's scalar decay
+  auto arow = [&](const Sc& s, int u, int j) -> float {
+    if (!PCX) return s.a;
+    const float l = s_lc[u][row(j)];
+    return R::nlms ? 1.f - s.eta * l : l;
   };
   auto scal = [&](int t, int u) -> Sc {
     Sc s;
@@ -214,14 +256,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (rg == 0) *reinterpret_cast<f4*>(&s_w[u][4 * cq]) = w;
     }
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) S[j] = S[j] * s.a + w * (s.eta * s_x[u][row(j)]);
+    for (int j = 0; j < RPT; ++j) S[j] = S[j] * arow(s, u, j) + w * (s.eta * s_x[u][row(j)]);
   };
 
   // ---- forward: the state at every chunk start
   f4 S[RPT];
   load_state(p.S_in != nullptr ? p.S_in + (size_t)bh * SS : nullptr, S);
-  for (int c = 0; c < p.nchunks; ++c) {
-    const int t0 = c * CH, t1 = min(T, t0 + CH);
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * CK, t1 = min(T, t0 + CK);
     store_state(ckpt + (size_t)c * SS, S);
     stage(t0, t1, false);
     for (int t = t0; t < t1; ++t) fwd_tok(t, t - t0, S);
@@ -233,8 +275,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   load_state(p.dS_out != nullptr ? p.dS_out + (size_t)bh * SS : nullptr, G);
   if (R::shift && T >= 1)  // the last key is written by no step of this call
     for (int i = tid; i < DK; i += NT) p.gk[(rb + T - 1) * DK + i] = 0.f;
-  for (int c = p.nchunks - 1; c >= 0; --c) {
-    const int t0 = c * CH, t1 = min(T, t0 + CH), len = t1 - t0;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int t0 = c * CK, t1 = min(T, t0 + CK), len = t1 - t0;
     const float* start = ckpt + (size_t)c * SS;
     // recompute the chunk's states after each token (the last one stays in S)
     stage(t0, t1, true);
@@ -276,14 +318,17 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = f4{0.f, 0.f, 0.f, 0.f};
         if (tid == 0) {
           if (p.gbeta != nullptr) p.gbeta[rb + t] = 0.f;
-          if (p.glam != nullptr) p.glam[rb + t] = 0.f;
+          if (p.glam != nullptr && !PCX) p.glam[rb + t] = 0.f;
         }
+        if (PCX && p.glam != nullptr)
+          for (int i = tid; i < DK; i += NT) p.glam[(rb + t) * DK + i] = 0.f;
         if (p.gx0 != nullptr)
           for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
       } else {
-        // w: the residual (delta) or the value; G w per row; <G, S_{t-1}>, x^T G w, G^T x
+        // w: the residual (delta) or the value; G w per row; <G, S_{t-1}> (per channel:
+        // per row, and the ridge rules' sum of lambda_i times it), x^T G w, G^T x
         const f4 w = *reinterpret_cast<const f4*>(&s_w[u][4 * cq]);
-        float gw[RPT], da_p = 0.f, xgw_p = 0.f;
+        float gw[RPT], dar[RPT], da_p = 0.f, xgw_p = 0.f;
         f4 gx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
@@ -291,23 +336,33 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           const f4 m = G[j] * w;
           gw[j] = rowsum(m[0] + m[1] + m[2] + m[3]);
           const f4 d = G[j] * Sp[j];
-          da_p += d[0] + d[1] + d[2] + d[3];
+          if (PCX) {
+            dar[j] = rowsum(d[0] + d[1] + d[2] + d[3]);
+            if (R::nlms && cq == 0) da_p += s_lc[u][row(j)] * dar[j];
+          } else {
+            da_p += d[0] + d[1] + d[2] + d[3];
+          }
           if (cq == 0) xgw_p += x * gw[j];
           gx += G[j] * x;
         }
-        float da, xgw;
+        float da, xgw;  // per channel (ridge rules): da holds sum_i lambda_i da_i
         const f4 gtx = reduce(gx, da_p, xgw_p, da, xgw);
         if (R::nlms) {
           const f4 dr = gtx * s.eta;  // delta: dL/dr; inner: dL/dv
           if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = dr;
-          // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps
-          const float lam = s_lm[u];
-          const float deta = xgw - lam * da;
+          // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps (per channel
+          // a_i = 1 - eta lambda_i and den takes the largest lambda_i, which passes the
+          // denominator's gradient to the first channel holding it)
+          const float deta = xgw - (PCX ? da : s_lm[u] * da);
           const float dden = -s.eta * deta * s.rden;
           if (tid == 0) {
             if (p.gbeta != nullptr) p.gbeta[rb + t] = deta * s.rden;
-            if (p.glam != nullptr) p.glam[rb + t] = -s.eta * da + dden;
+            if (p.glam != nullptr && !PCX) p.glam[rb + t] = -s.eta * da + dden;
           }
+          if (PCX && p.glam != nullptr && cq == 0)
+#pragma unroll
+            for (int j = 0; j < RPT; ++j)
+              p.glam[(rb + t) * DK + row(j)] = -s.eta * dar[j] + (row(j) == s_im[u] ? dden : 0.f);
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
             const float x = s_x[u][row(j)];
@@ -320,19 +375,22 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
               if (t >= 1) p.gk[(rb + t - 1) * DK + row(j)] = dx * dphi_of(x);
               else if (p.gx0 != nullptr) p.gx0[(size_t)bh * DK + row(j)] = dx;
             }
-            G[j] = G[j] * s.a - (R::solve ? dr * x : f4{0.f, 0.f, 0.f, 0.f});
+            G[j] = G[j] * arow(s, u, j) - (R::solve ? dr * x : f4{0.f, 0.f, 0.f, 0.f});
           }
         } else {
           // additive: x = phi(k_t), b the write scale, a the retention
           if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = gtx * s.b;
           if (tid == 0) {
             if (p.gbeta != nullptr) p.gbeta[rb + t] = xgw;
-            if (p.glam != nullptr) p.glam[rb + t] = da;
+            if (p.glam != nullptr && !PCX) p.glam[rb + t] = da;
           }
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
-            if (cq == 0) p.gk[(rb + t) * DK + row(j)] = s.b * gw[j] * dphi_of(s_x[u][row(j)]);
-            G[j] = G[j] * s.a;
+            if (cq == 0) {
+              p.gk[(rb + t) * DK + row(j)] = s.b * gw[j] * dphi_of(s_x[u][row(j)]);
+              if (PCX && p.glam != nullptr) p.glam[(rb + t) * DK + row(j)] = dar[j];
+            }
+            G[j] = G[j] * arow(s, u, j);
           }
         }
       }
@@ -347,13 +405,18 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
 }
 
+template <typename InT, int DK, int DV, bool PCX>
+hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)p.BH), block(NT);
+  if (p.rule == kRuleDelta) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDelta, PCX>), grid, block, 0, st, p);
+  else if (p.rule == kRuleInner) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleInner, PCX>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive, PCX>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
 template <typename InT, int DK, int DV>
 hipError_t launch_t(const BwdParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)p.BH), block(NT);
-  if (p.rule == kRuleDelta) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDelta>), grid, block, 0, st, p);
-  else if (p.rule == kRuleInner) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleInner>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive>), grid, block, 0, st, p);
-  return hipGetLastError();
+  return (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
 }
 
 template <typename InT>

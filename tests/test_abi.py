@@ -180,8 +180,8 @@ def _bwd(shp=None, md=None, q=M, k=2 * M, v=3 * M, beta=4 * M, lam=None, S_in=No
 @pytest.mark.parametrize("case,expect", [
     (dict(shp=F.shape(1, 1, 8, 96, 128, F.BF16)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_DELTA_PV)), F.EUNSUPPORTED),
-    (dict(md=F.mode(flags=F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.QK_L2NORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.QK_RMSNORM | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.BETA_SIGMOID)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.OUT_BF16)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
@@ -217,6 +217,11 @@ def test_bwd_workspace_size_and_empty_batch():
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp0), ctypes.byref(md), ctypes.byref(n)) == F.OK
     assert n.value == 0
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), None) == F.EINVAL
+    # per-channel lambda: 32-token chunks
+    mdp = F.mode(rule=F.RULE_INNER, flags=F.LAMBDA_PER_CHANNEL)
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(mdp), ctypes.byref(n)) == F.OK
+    want = 4 * 6 * ((4 + 32) * 128 * 64 + 32 * 64)
+    assert n.value == (want + 255) // 256 * 256
     # B*H == 0: nothing to do, no pointer is needed
     assert _bwd(shp=F.shape(0, 2, 8, 64, 64, F.F32), q=None, k=None, v=None, gout=None, gq=None,
                 gk=None, gv=None, ws=None) == F.OK

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 RULES = {"delta": wl.RULE_DELTA, "inner": wl.RULE_INNER, "additive": wl.RULE_ADDITIVE}
 
 
-def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None, beta_kind=None):
+def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None, beta_kind=None,
+             per_channel=False):
     r = RULES[rule]
     if lam_kind is None:
         lam_kind = "gamma" if r == wl.RULE_ADDITIVE else "softplus"
@@ -26,7 +27,7 @@ def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None
         beta_kind = "sigmoid" if r == wl.RULE_ADDITIVE else "two_sigmoid"
     w = wl.make_scan(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, rule=r,
                      phi=wl.PHI_ELU1 if phi == "elu1" else wl.PHI_IDENTITY,
-                     beta_kind=beta_kind, lam_kind=lam_kind, lam_mu=-3.0,
+                     beta_kind=beta_kind, lam_kind=lam_kind, lam_mu=-3.0, per_channel=per_channel,
                      normalise_qk=phi != "elu1", s0_std=0.1 if carried else None, seed=seed)
     rng = np.random.default_rng(seed + 1000)
     dO = rng.standard_normal((B, H, T, dv)).astype(np.float32)
@@ -41,7 +42,7 @@ def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None
 
 
 def _run(w, dO, dS, xprev0, has0, phi, carried, with_dS=True):
-    flags = F.PHI_ELU1 if phi == "elu1" else 0
+    flags = (F.PHI_ELU1 if phi == "elu1" else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
     S_in = None
     if carried:
         S_in = make_state(w.B, w.H, w.dk, w.dv, S=w.S0, xprev=xprev0, has=has0)
@@ -50,7 +51,8 @@ def _run(w, dO, dS, xprev0, has0, phi, carried, with_dS=True):
                    f32_tensor(w.beta), f32_tensor(w.lam), f32_tensor(dO), rule=w.rule,
                    flags=flags, eps=w.eps, S_in=S_in, grad_S_out=gS)
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS if with_dS else None,
-                            rule=w.rule, phi_kind=phi, eps=w.eps, S0=w.S0 if carried else None,
+                            rule=w.rule, phi_kind=phi, eps=w.eps, per_channel=w.per_channel,
+                            S0=w.S0 if carried else None,
                             xprev0=xprev0, has0=has0)
     return g, ref
 
@@ -88,6 +90,33 @@ def test_backward_matches_oracle(rule, phi, dtype, dk, dv, T, carried):
     say(f"[bwd] {rule} {phi} {dtype} dk={dk} dv={dv} T={T} carried={carried}")
     w, dO, dS, x0, h0 = _problem(rule, phi, dtype, dk, dv, T, carried, seed)
     _compare(*_run(w, dO, dS, x0, h0, phi, carried))
+
+
+@pytest.mark.parametrize("rule,phi,dtype,dk,dv,T,carried", [
+    ("delta", "identity", "bf16", 128, 128, 100, True),
+    ("delta", "elu1", "f32", 64, 128, 70, False),
+    ("inner", "identity", "bf16", 128, 64, 97, True),
+    ("inner", "elu1", "f32", 64, 64, 33, False),
+    ("additive", "elu1", "bf16", 128, 128, 96, True),
+    ("additive", "identity", "f32", 64, 128, 31, False),
+])
+def test_backward_per_channel_lambda(rule, phi, dtype, dk, dv, T, carried):
+    """lambda [B,H,T,dk]: per-row decays; for the ridge rules the denominator's largest
+    lambda_i takes its gradient. Chunks are 32 tokens here, so T spans several with a
+    ragged tail."""
+    seed = (dk + dv + T) * 5 + carried
+    say(f"[bwd pc] {rule} {phi} {dtype} dk={dk} dv={dv} T={T} carried={carried}")
+    w, dO, dS, x0, h0 = _problem(rule, phi, dtype, dk, dv, T, carried, seed, per_channel=True)
+    _compare(*_run(w, dO, dS, x0, h0, phi, carried))
+
+
+def test_backward_per_channel_tied_maximum():
+    """Several channels share the largest lambda: the denominator's gradient goes to the
+    first of them, as in the oracle."""
+    say("[bwd pc] tied maximum")
+    w, dO, dS, x0, h0 = _problem("delta", "identity", "f32", 64, 64, 40, True, 21, per_channel=True)
+    w.lam[..., 5] = w.lam[..., 17] = w.lam[..., 60] = 5.0   # above every softplus(N(-3, 1)) draw
+    _compare(*_run(w, dO, dS, x0, h0, "identity", True))
 
 
 @pytest.mark.parametrize("rule", ["delta", "inner", "additive"])
