@@ -486,7 +486,14 @@ def cpu_baseline(w, min_s=10.0):
             t = time.perf_counter() - t0
             if t >= min_s:
                 break
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(n * w.T / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model, "blas_threads": 1,
             "sample": f"{n} batch elements of {w.T} tokens x {w.H} heads (batch elements "
                       f"0..{w.B - 1} in turn), fp64 NumPy recurrence, one thread, {t:.1f} s"}
 
