@@ -273,7 +273,8 @@ def phi_grad(x: np.ndarray, kind: str) -> np.ndarray:
 
 
 def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
-                  per_channel=False, S0=None, xprev0=None, has0=None):
+                  per_channel=False, S0=None, xprev0=None, has0=None, beta_act=None,
+                  lam_act=False):
     """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
     for the delta, additive and inner rules with phi identity or elu+1, scalar or
     per-channel lambda (reading D21: the pages give no backward pass).
@@ -286,6 +287,10 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     beta_t phi(k_t) v_t^T; the read o_t = S_t^T phi(q_t)). lambda-hat's maximum passes its
     gradient to the first channel attaining it.
 
+    With beta_act / lam_act (as in scan(), reading D17) beta and lam hold pre-activations
+    z, and their gradients are taken with respect to z: the gate's gradient times the
+    activation's derivative (sigmoid: s(1 - s); 2 sigmoid: 2 s(1 - s); softplus: sigmoid(z)).
+
     Returns a dict with the gradients "q", "k", "v", "beta", "lam" (None where the input
     is None), "S0" [B,H,dk,dv] and "xprev0" [B,H,dk], in float64.
     """
@@ -296,6 +301,19 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     Q, K, V = _heads(q, 2), _heads(k, 2), _heads(v, 2)
     Bt = None if beta is None else _heads(beta, 1)
     Lm = None if lam is None else _heads(lam, 2 if per_channel else 1)
+    # gate activations: the activated gates, and each gate's derivative by its
+    # pre-activation (1 without an activation)
+    dBt = dLm = 1.0
+    if Bt is not None and beta_act is not None:
+        sb = sigmoid(Bt)
+        scale = {"sigmoid": 1.0, "sigmoid2": 2.0}[beta_act]
+        Bt, dBt = scale * sb, scale * sb * (1.0 - sb)
+    if Lm is not None and lam_act:
+        sl = sigmoid(Lm)
+        if rule == RULE_ADDITIVE:
+            Lm, dLm = sl, sl * (1.0 - sl)
+        else:
+            Lm, dLm = softplus(Lm), sl
     dOh = _heads(dO, 2)
     dSh = np.zeros((N, dk, dv)) if dS is None else _heads(dS, 2)
     S_init = np.zeros((N, dk, dv)) if S0 is None else _heads(S0, 2)
@@ -401,6 +419,10 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                 G = (gam[:, None] if per_channel else gam) * G
         g["S0"][n] = G
 
+    if g["beta"] is not None:
+        g["beta"] = g["beta"] * dBt
+    if g["lam"] is not None:
+        g["lam"] = g["lam"] * dLm
     shapes = {"q": (B, H, T, dk), "k": (B, H, T, dk), "v": (B, H, T, dv),
               "S0": (B, H, dk, dv), "xprev0": (B, H, dk)}
     out = {name: g[name].reshape(shp) for name, shp in shapes.items()}

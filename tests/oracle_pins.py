@@ -748,7 +748,10 @@ def pin_p24_backward(orc):
         dv_j = sum_{t>=j} (q_t . k_j) dO_t, dq_t = sum_{j<=t} k_j (v_j . dO_t),
         dk_j = sum_{t>=j} q_t (v_j . dO_t).
     (c) The delta rule's first token at a sequence start writes nothing, so the gradients of
-        its beta and lambda are exactly zero."""
+        its beta and lambda are exactly zero.
+    (d) With gate pre-activations (2 sigmoid or sigmoid for beta; softplus ridge or sigmoid
+        retention for lambda), finite differences in the pre-activations match the
+        gradients, scalar and per channel."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -797,6 +800,31 @@ def pin_p24_backward(orc):
     gr = orc.scan_backward(q, k, v, b, lam, dO, rng.standard_normal((1, 1, 4, 3)), rule=DELTA,
                            S0=rng.standard_normal((1, 1, 4, 3)))
     assert gr["beta"][0, 0, 0] == 0.0 and gr["lam"][0, 0, 0] == 0.0
+    for rule, bact in ((DELTA, "sigmoid2"), (INNER, "sigmoid"), (ADD, "sigmoid")):
+        for per_channel in (False, True):
+            T, dk, dv = 4, 3, 2
+            q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+            v = rng.standard_normal((1, 1, T, dv))
+            zb = rng.standard_normal((1, 1, T))
+            zl = rng.normal(-1.0 if rule != ADD else 2.0, 1.0, (1, 1, T, dk) if per_channel else (1, 1, T))
+            dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+            S0, x0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
+            kw = dict(rule=rule, per_channel=per_channel, has0=np.array([[1]]), S0=S0, xprev0=x0,
+                      beta_act=bact, lam_act=True)
+
+            def loss(b, lam):
+                o, S, _, _ = orc.scan(q, k, v, b, lam, **kw)
+                return float(np.sum(o * dO) + np.sum(S * dS))
+
+            gr = orc.scan_backward(q, k, v, zb, zl, dO, dS, **kw)
+            for name, arr in (("beta", zb), ("lam", zl)):
+                for idx in np.ndindex(arr.shape):
+                    ap, am = arr.copy(), arr.copy()
+                    ap[idx] += 1e-6
+                    am[idx] -= 1e-6
+                    fd = ((loss(ap, zl) - loss(am, zl)) if name == "beta" else (loss(zb, ap) - loss(zb, am))) / 2e-6
+                    an = gr[name][idx]
+                    assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, per_channel, name, idx, fd, an)
 
 
 ALL_PINS = [

@@ -70,6 +70,9 @@ MUTANTS = {
     "ridge_scaled_by_norm": ("energy = np.sum(x * x, axis=1)", "energy = np.sqrt(np.sum(x * x, axis=1))"),
     "znorm_no_decay": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = z + b[:, None] * kt"),
     "znorm_no_beta": ("z = gam[:, :, 0] * z + b[:, None] * kt", "z = gam[:, :, 0] * z + kt"),
+    "bwd_softplus_derivative_dropped": ("Lm, dLm = softplus(Lm), sl", "Lm, dLm = softplus(Lm), 1.0"),
+    "bwd_sigmoid2_derivative_halved": ("Bt, dBt = scale * sb, scale * sb * (1.0 - sb)",
+                                       "Bt, dBt = scale * sb, sb * (1.0 - sb)"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
