@@ -171,7 +171,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
       s_x[u][i] = x;
       if (bwd) s_q[u][i] = qq;
-      if (PCX) s_lc[u][i] = (t < t1 && p.lam != nullptr) ? p.lam[(rb + t) * DK + i] : (R::nlms ? 0.f : 1.f);
+      if (PCX)
+        s_lc[u][i] = (t < t1 && p.lam != nullptr) ? act_lam(p.lam[(rb + t) * DK + i], p.flags, R::nlms)
+                                                   : (R::nlms ? 0.f : 1.f);
     }
     for (int idx = tid; idx < CK * DV; idx += NT) {
       const int u = idx / DV, j = idx % DV, t = t0 + u;
@@ -180,8 +182,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
     if (tid < CK) {
       const int t = t0 + tid;
-      s_bt[tid] = (t < t1 && p.beta != nullptr) ? p.beta[rb + t] : 1.f;
-      if (!PCX) s_lm[tid] = (t < t1 && p.lam != nullptr) ? p.lam[rb + t] : (R::nlms ? 0.f : 1.f);
+      s_bt[tid] = (t < t1 && p.beta != nullptr) ? act_beta(p.beta[rb + t], p.flags) : 1.f;
+      if (!PCX)
+        s_lm[tid] = (t < t1 && p.lam != nullptr) ? act_lam(p.lam[rb + t], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
     }
     __syncthreads();
     for (int u = wave; u < CK; u += NWV) {
@@ -214,6 +217,18 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
     }
     __syncthreads();
+  };
+  // With pre-activated gates the gradients are taken with respect to the pre-activation
+  // z: times the activation's derivative, from the activated value y: sigmoid y (1 - y),
+  // 2 sigmoid y (1 - y / 2), the additive retention y (1 - y), softplus 1 - e^-y.
+  auto dbeta_dz = [&](float y) {
+    if (p.flags & kFlagBetaSig) return y * (1.f - y);
+    if (p.flags & kFlagBetaSig2) return y * (1.f - 0.5f * y);
+    return 1.f;
+  };
+  auto dlam_dz = [&](float y) {
+    if (!(p.flags & kFlagLamAct)) return 1.f;
+    return R::nlms ? -expm1f(-y) : y * (1.f - y);
   };
   // decay of row j at token u: 1 - eta lambda_i (ridge rules) or gamma_i (additive) per
   // channel, else the token's scalar decay
@@ -356,13 +371,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           const float deta = xgw - (PCX ? da : s_lm[u] * da);
           const float dden = -s.eta * deta * s.rden;
           if (tid == 0) {
-            if (p.gbeta != nullptr) p.gbeta[rb + t] = deta * s.rden;
-            if (p.glam != nullptr && !PCX) p.glam[rb + t] = -s.eta * da + dden;
+            if (p.gbeta != nullptr) p.gbeta[rb + t] = deta * s.rden * dbeta_dz(s_bt[u]);
+            if (p.glam != nullptr && !PCX) p.glam[rb + t] = (-s.eta * da + dden) * dlam_dz(s_lm[u]);
           }
           if (PCX && p.glam != nullptr && cq == 0)
 #pragma unroll
             for (int j = 0; j < RPT; ++j)
-              p.glam[(rb + t) * DK + row(j)] = -s.eta * dar[j] + (row(j) == s_im[u] ? dden : 0.f);
+              p.glam[(rb + t) * DK + row(j)] =
+                  (-s.eta * dar[j] + (row(j) == s_im[u] ? dden : 0.f)) * dlam_dz(s_lc[u][row(j)]);
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
             const float x = s_x[u][row(j)];
@@ -381,14 +397,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           // additive: x = phi(k_t), b the write scale, a the retention
           if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = gtx * s.b;
           if (tid == 0) {
-            if (p.gbeta != nullptr) p.gbeta[rb + t] = xgw;
-            if (p.glam != nullptr && !PCX) p.glam[rb + t] = da;
+            if (p.gbeta != nullptr) p.gbeta[rb + t] = xgw * dbeta_dz(s_bt[u]);
+            if (p.glam != nullptr && !PCX) p.glam[rb + t] = da * dlam_dz(s_lm[u]);
           }
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
             if (cq == 0) {
               p.gk[(rb + t) * DK + row(j)] = s.b * gw[j] * dphi_of(s_x[u][row(j)]);
-              if (PCX && p.glam != nullptr) p.glam[(rb + t) * DK + row(j)] = dar[j];
+              if (PCX && p.glam != nullptr) p.glam[(rb + t) * DK + row(j)] = dar[j] * dlam_dz(s_lc[u][row(j)]);
             }
             G[j] = G[j] * arow(s, u, j);
           }

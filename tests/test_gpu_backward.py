@@ -199,3 +199,36 @@ def test_backward_full_size_sampled_heads(name, heads):
         say(f"    head ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL["f32"], f"grad {n}: {e:.3e}"
+
+
+@pytest.mark.parametrize("rule,beta_act,per_channel,dtype,T", [
+    ("delta", "sigmoid2", False, "bf16", 130),
+    ("delta", "sigmoid", True, "f32", 70),
+    ("inner", "sigmoid2", False, "bf16", 100),
+    ("inner", "sigmoid", True, "bf16", 65),
+    ("additive", "sigmoid", False, "bf16", 129),
+    ("additive", None, True, "f32", 40),
+])
+def test_backward_pre_activated_gates(rule, beta_act, per_channel, dtype, T):
+    """Gates given as pre-activations (FWMEM_BETA_SIGMOID(2), FWMEM_LAMBDA_PREACT): the
+    library activates them as it stages them, and returns the gradients with respect to
+    the pre-activations, against the oracle's scan_backward with the same activations."""
+    r = RULES[rule]
+    bkind = {"sigmoid": "sigmoid", "sigmoid2": "two_sigmoid", None: "one"}[beta_act]
+    lkind = "gamma" if r == wl.RULE_ADDITIVE else "softplus"
+    say(f"[bwd gates] {rule} beta={beta_act} pc={per_channel} {dtype} T={T}")
+    w = wl.make_scan(B=2, H=2, T=T, dk=128, dv=64, dtype=dtype, rule=r, beta_kind=bkind,
+                     lam_kind=lkind, lam_mu=-3.0, per_channel=per_channel, s0_std=0.1,
+                     seed=T + 3 * per_channel)
+    rng = np.random.default_rng(T)
+    dO = rng.standard_normal((w.B, w.H, T, w.dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, w.dk, w.dv)) * 0.3).astype(np.float32)
+    flags = (F.LAMBDA_PREACT | (F.LAMBDA_PER_CHANNEL if per_channel else 0)
+             | {"sigmoid": F.BETA_SIGMOID, "sigmoid2": F.BETA_SIGMOID2, None: 0}[beta_act])
+    S_in = make_state(w.B, w.H, w.dk, w.dv, S=w.S0)
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(w.beta_pre), f32_tensor(w.lam_pre), f32_tensor(dO), rule=r,
+                   flags=flags, eps=w.eps, S_in=S_in, grad_S_out=make_state(w.B, w.H, w.dk, w.dv, S=dS))
+    ref = orc.scan_backward(w.q, w.k, w.v, w.beta_pre, w.lam_pre, dO, dS, rule=r, eps=w.eps,
+                            per_channel=per_channel, S0=w.S0, beta_act=beta_act, lam_act=True)
+    _compare(g, ref)
