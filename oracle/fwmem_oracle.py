@@ -272,9 +272,21 @@ def phi_grad(x: np.ndarray, kind: str) -> np.ndarray:
     raise ValueError(kind)
 
 
+def unit_rows_vjp(x: np.ndarray, g: np.ndarray, length: float = 1.0) -> np.ndarray:
+    """The gradient with respect to x of unit_rows(x, length), given the gradient g with
+    respect to its result: (length / |x|) (g - u (u . g)) with u = x / |x|, per row; the
+    map is constant on a zero row, whose gradient is zero."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    u = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    f = np.divide(length, n, out=np.zeros_like(n), where=n > 0)
+    return f * (g - u * np.sum(u * g, axis=-1, keepdims=True))
+
+
 def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
                   per_channel=False, S0=None, xprev0=None, has0=None, beta_act=None,
-                  lam_act=False):
+                  lam_act=False, qk_norm=None):
     """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
     for the delta, additive and inner rules with phi identity or elu+1, scalar or
     per-channel lambda (reading D21: the pages give no backward pass).
@@ -291,9 +303,26 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     z, and their gradients are taken with respect to z: the gate's gradient times the
     activation's derivative (sigmoid: s(1 - s); 2 sigmoid: 2 s(1 - s); softplus: sigmoid(z)).
 
+    With qk_norm ("l2" or "rms", identity phi, as in scan()) q, k and the carried key are
+    raw and the recurrence sees them rescaled to a fixed length: the gradients with respect
+    to the rescaled vectors are taken back through the rescaling (unit_rows_vjp).
+
     Returns a dict with the gradients "q", "k", "v", "beta", "lam" (None where the input
     is None), "S0" [B,H,dk,dv] and "xprev0" [B,H,dk], in float64.
     """
+    if qk_norm is not None:
+        if phi_kind != "identity" or qk_norm not in ("l2", "rms"):
+            raise ValueError("qk_norm takes the identity feature map and 'l2' or 'rms'")
+        length = 1.0 if qk_norm == "l2" else float(np.sqrt(np.asarray(q).shape[-1]))
+        g = scan_backward(unit_rows(q, length), unit_rows(k, length), v, beta, lam, dO, dS,
+                          rule=rule, eps=eps, per_channel=per_channel, S0=S0,
+                          xprev0=None if xprev0 is None else unit_rows(xprev0, length),
+                          has0=has0, beta_act=beta_act, lam_act=lam_act)
+        g["q"] = unit_rows_vjp(q, g["q"], length)
+        g["k"] = unit_rows_vjp(k, g["k"], length)
+        if xprev0 is not None:
+            g["xprev0"] = unit_rows_vjp(xprev0, g["xprev0"], length)
+        return g
     q = np.asarray(q, dtype=np.float64)
     B, H, T, dk = q.shape
     dv = np.asarray(v).shape[-1]

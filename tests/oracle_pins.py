@@ -751,7 +751,10 @@ def pin_p24_backward(orc):
         its beta and lambda are exactly zero.
     (d) With gate pre-activations (2 sigmoid or sigmoid for beta; softplus ridge or sigmoid
         retention for lambda), finite differences in the pre-activations match the
-        gradients, scalar and per channel."""
+        gradients, scalar and per channel.
+    (e) With QK normalisation (l2 and RMS), finite differences in the raw q, k and carried
+        key match their gradients, every rule; and a key scaled by any c > 0 changes
+        nothing, so its gradient is orthogonal to it."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -825,6 +828,39 @@ def pin_p24_backward(orc):
                     fd = ((loss(ap, zl) - loss(am, zl)) if name == "beta" else (loss(zb, ap) - loss(zb, am))) / 2e-6
                     an = gr[name][idx]
                     assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, per_channel, name, idx, fd, an)
+    for rule in (DELTA, INNER, ADD):
+        for qk in ("l2", "rms"):
+            T, dk, dv = 4, 3, 2
+            q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+            v = rng.standard_normal((1, 1, T, dv))
+            b, lam = rng.uniform(0.2, 1.5, (1, 1, T)), rng.uniform(0.6, 1.0, (1, 1, T))
+            dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+            S0, x0 = rng.standard_normal((1, 1, dk, dv)), rng.standard_normal((1, 1, dk))
+            kw = dict(rule=rule, has0=np.array([[1]]), S0=S0, qk_norm=qk)
+            args = {"q": q, "k": k, "xprev0": x0}
+
+            def loss(a):
+                o, S, _, _ = orc.scan(a["q"], a["k"], v, b, lam, xprev0=a["xprev0"], **kw)
+                return float(np.sum(o * dO) + np.sum(S * dS))
+
+            gr = orc.scan_backward(q, k, v, b, lam, dO, dS, xprev0=x0, **kw)
+            for name, arr in args.items():
+                if rule == ADD and name == "xprev0":
+                    continue
+                for idx in np.ndindex(arr.shape):
+                    a = dict(args)
+                    ap, am = arr.copy(), arr.copy()
+                    ap[idx] += 1e-6
+                    am[idx] -= 1e-6
+                    a[name] = ap
+                    fp = loss(a)
+                    a[name] = am
+                    fd = (fp - loss(a)) / 2e-6
+                    an = gr[name][idx]
+                    assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, qk, name, idx, fd, an)
+            for name in ("q", "k"):
+                dots = np.sum(gr[name] * args[name], axis=-1)
+                assert np.all(np.abs(dots) <= 1e-12 * (1.0 + np.abs(gr[name]).sum())), (rule, qk, name)
 
 
 ALL_PINS = [

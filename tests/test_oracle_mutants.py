@@ -73,6 +73,8 @@ MUTANTS = {
     "bwd_softplus_derivative_dropped": ("Lm, dLm = softplus(Lm), sl", "Lm, dLm = softplus(Lm), 1.0"),
     "bwd_sigmoid2_derivative_halved": ("Bt, dBt = scale * sb, scale * sb * (1.0 - sb)",
                                        "Bt, dBt = scale * sb, sb * (1.0 - sb)"),
+    "bwd_norm_projection_dropped": ("return f * (g - u * np.sum(u * g, axis=-1, keepdims=True))",
+                                    "return f * g"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
