@@ -17,6 +17,8 @@
 //             G_{t-1} = gamma G
 // and for the shifted rules the scalar chain through a, eta and the denominator.
 //
+// With QK normalisation, q, k and the carried key are rescaled to a fixed length as they
+// are staged, and a second kernel takes their gradients back through the rescaling.
 // Per channel, lambda_i scales row i's decay (1 - eta lambda_i, or the retention gamma_i)
 // and eta's denominator takes the largest lambda_i; da and the lambda gradient are then
 // per row.
@@ -85,6 +87,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int cq = tid % TPRd, rg = tid / TPRd;
   const int T = p.T;
   const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float qlen = qk_length(p.flags, DK);  // > 0: q, k and the carried key are rescaled
   const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
   const size_t rb = (size_t)bh * T;
   const InT* qb = static_cast<const InT*>(p.q) + rb * DK;
@@ -191,6 +194,20 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       float n = 0.f;
       for (int i = lane; i < DK; i += 64) n += s_x[u][i] * s_x[u][i];
       n = wave_sum(n);
+      if (qlen > 0.f) {
+        // QK normalisation: the row rescaled to length qlen by the wave that measured it
+        float nq = 0.f;
+        if (bwd) {
+          for (int i = lane; i < DK; i += 64) nq += s_q[u][i] * s_q[u][i];
+          nq = wave_sum(nq);
+        }
+        const float fx = rescale_factor(n, qlen), fq = rescale_factor(nq, qlen);
+        for (int i = lane; i < DK; i += 64) {
+          s_x[u][i] *= fx;
+          if (bwd) s_q[u][i] *= fq;
+        }
+        n *= fx * fx;
+      }
       if (lane == 0) s_n[u] = n;
       if (PCX && R::nlms) {
         // the largest lambda over the channels and the first channel holding it
@@ -421,6 +438,45 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
 }
 
+// QK normalisation: the main kernel's q, k and carried-key gradients are with respect to
+// the rescaled vectors y = len x / |x|; with respect to the raw x they are
+// (len / |x|) (g - x (x . g) / |x|^2), zero for a zero row. One wave per vector: the q
+// rows, then the k rows, then the carried keys.
+template <typename InT, int DK>
+__global__ __launch_bounds__(256) void qk_norm_bwd_kernel(BwdParams p, float len) {
+  constexpr int E = DK / 64;
+  const int lane = threadIdx.x & 63;
+  const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t nrow = (size_t)p.BH * (size_t)p.T;
+  const size_t nkey = (p.gx0 != nullptr && p.xprev_in != nullptr) ? (size_t)p.BH : 0;
+  if (r >= 2 * nrow + nkey) return;
+  float x[E], g[E];
+  float* gp;
+  if (r < 2 * nrow) {
+    const InT* src = static_cast<const InT*>(r < nrow ? p.q : p.k) + (r % nrow) * DK;
+    gp = (r < nrow ? p.gq : p.gk) + (r % nrow) * DK;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = In<InT>::load1(src + lane + 64 * e);
+  } else {
+    const size_t b = r - 2 * nrow;
+    gp = p.gx0 + b * DK;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = p.xprev_in[b * DK + lane + 64 * e];
+  }
+  float xx = 0.f, xg = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    g[e] = gp[lane + 64 * e];
+    xx += x[e] * x[e];
+    xg += x[e] * g[e];
+  }
+  xx = wave_sum(xx);
+  xg = wave_sum(xg);
+  const float f = rescale_factor(xx, len), c = xx > 0.f ? xg / xx : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gp[lane + 64 * e] = f * (g[e] - x[e] * c);
+}
+
 template <typename InT, int DK, int DV, bool PCX>
 hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.BH), block(NT);
@@ -432,7 +488,14 @@ hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
 
 template <typename InT, int DK, int DV>
 hipError_t launch_t(const BwdParams& p, hipStream_t st) {
-  return (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
+  const hipError_t e =
+      (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
+  const float len = qk_length(p.flags, DK);
+  if (e != hipSuccess || len <= 0.f) return e;
+  const size_t rows = 2 * (size_t)p.BH * (size_t)p.T + ((p.gx0 != nullptr && p.xprev_in != nullptr) ? p.BH : 0);
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((qk_norm_bwd_kernel<InT, DK>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, p, len);
+  return hipGetLastError();
 }
 
 template <typename InT>

@@ -232,3 +232,38 @@ def test_backward_pre_activated_gates(rule, beta_act, per_channel, dtype, T):
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta_pre, w.lam_pre, dO, dS, rule=r, eps=w.eps,
                             per_channel=per_channel, S0=w.S0, beta_act=beta_act, lam_act=True)
     _compare(g, ref)
+
+
+@pytest.mark.parametrize("rule,qk,dtype,dk,dv,T,per_channel", [
+    ("delta", "l2", "bf16", 128, 128, 130, False),
+    ("delta", "rms", "f32", 64, 128, 70, True),
+    ("inner", "rms", "bf16", 128, 64, 100, False),
+    ("inner", "l2", "f32", 64, 64, 65, False),
+    ("additive", "l2", "bf16", 128, 128, 129, False),
+    ("additive", "rms", "f32", 64, 64, 40, True),
+])
+def test_backward_qk_norm(rule, qk, dtype, dk, dv, T, per_channel):
+    """Raw q, k and a raw carried key, rescaled by the library (FWMEM_QK_L2NORM /
+    FWMEM_QK_RMSNORM): gradients with respect to the raw vectors against the oracle's
+    scan_backward with the same qk_norm."""
+    r = RULES[rule]
+    say(f"[bwd qk] {rule} {qk} {dtype} dk={dk} dv={dv} T={T} pc={per_channel}")
+    w = wl.make_scan(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, rule=r,
+                     beta_kind="sigmoid" if r == wl.RULE_ADDITIVE else "two_sigmoid",
+                     lam_kind="gamma" if r == wl.RULE_ADDITIVE else "softplus", lam_mu=-3.0,
+                     per_channel=per_channel, normalise_qk=False, qk_norm=qk, s0_std=0.1,
+                     seed=T + dk)
+    rng = np.random.default_rng(T + 1)
+    x0 = (rng.standard_normal((w.B, w.H, dk)) * 3).astype(np.float32)   # a raw carried key
+    h0 = np.ones((w.B, w.H), np.int32)
+    dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    flags = ({"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[qk]
+             | (F.LAMBDA_PER_CHANNEL if per_channel else 0))
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(w.beta), f32_tensor(w.lam), f32_tensor(dO), rule=r, flags=flags,
+                   eps=w.eps, S_in=make_state(w.B, w.H, dk, dv, S=w.S0, xprev=x0, has=h0),
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
+    ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS, rule=r, eps=w.eps,
+                            per_channel=per_channel, S0=w.S0, xprev0=x0, has0=h0, qk_norm=qk)
+    _compare(g, ref)
