@@ -286,7 +286,7 @@ def unit_rows_vjp(x: np.ndarray, g: np.ndarray, length: float = 1.0) -> np.ndarr
 
 def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
                   per_channel=False, S0=None, xprev0=None, has0=None, beta_act=None,
-                  lam_act=False, qk_norm=None):
+                  lam_act=False, qk_norm=None, lam_scaled=False):
     """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
     for the delta, additive and inner rules with phi identity or elu+1, scalar or
     per-channel lambda (reading D21: the pages give no backward pass).
@@ -303,6 +303,10 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     z, and their gradients are taken with respect to z: the gate's gradient times the
     activation's derivative (sigmoid: s(1 - s); 2 sigmoid: 2 s(1 - s); softplus: sigmoid(z)).
 
+    With lam_scaled (delta and inner rules, as in scan(), reading D19) the ridge is
+    lambda_t |x_t|^2: lambda's gradient is the scaled ridge's times |x_t|^2, and the key
+    gains 2 x_t (lambda_t . the scaled ridge's gradient).
+
     With qk_norm ("l2" or "rms", identity phi, as in scan()) q, k and the carried key are
     raw and the recurrence sees them rescaled to a fixed length: the gradients with respect
     to the rescaled vectors are taken back through the rescaling (unit_rows_vjp).
@@ -317,7 +321,7 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
         g = scan_backward(unit_rows(q, length), unit_rows(k, length), v, beta, lam, dO, dS,
                           rule=rule, eps=eps, per_channel=per_channel, S0=S0,
                           xprev0=None if xprev0 is None else unit_rows(xprev0, length),
-                          has0=has0, beta_act=beta_act, lam_act=lam_act)
+                          has0=has0, beta_act=beta_act, lam_act=lam_act, lam_scaled=lam_scaled)
         g["q"] = unit_rows_vjp(q, g["q"], length)
         g["k"] = unit_rows_vjp(k, g["k"], length)
         if xprev0 is not None:
@@ -351,6 +355,8 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     shifted = rule in (RULE_DELTA, RULE_INNER)
     if not shifted and rule != RULE_ADDITIVE:
         raise ValueError(rule)
+    if lam_scaled and not shifted:
+        raise ValueError("lam_scaled takes the delta or inner rule")
 
     g = {name: np.zeros_like(a) for name, a in (("q", Q), ("k", K), ("v", V))}
     g["beta"] = None if Bt is None else np.zeros_like(Bt)
@@ -379,13 +385,15 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                         lhat = lt[imax]
                     else:
                         lt, lhat, imax = Lm[n, t], Lm[n, t], None
-                    den = x @ x + lhat + eps
+                    # the ridge the step uses: lambda, or lambda |x|^2 (scale-coupled)
+                    sc = (x @ x) if lam_scaled else 1.0
+                    den = x @ x + lhat * sc + eps
                     eta = Bt[n, t] / den
-                    a = 1.0 - eta * lt
+                    a = 1.0 - eta * lt * sc
                     decay = a[:, None] if per_channel else a
                     r = vt - Sp.T @ x if rule == RULE_DELTA else vt
                     Sc = decay * Sp + eta * np.outer(x, r)
-                    steps.append((Sp, x, eta, a, den, lt, imax, r))
+                    steps.append((Sp, x, eta, a, den, lt, imax, r, sc))
             else:
                 gam = 1.0 if Lm is None else Lm[n, t]
                 b = 1.0 if Bt is None else Bt[n, t]
@@ -404,7 +412,7 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
             if shifted:
                 if rec is None:
                     continue                    # S_t = S_{t-1}
-                Sp, x, eta, a, den, lt, imax, r = rec
+                Sp, x, eta, a, den, lt, imax, r, sc = rec
                 da = np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
                 if rule == RULE_DELTA:
                     deta = x @ G @ r
@@ -417,8 +425,8 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                     dx = eta * (G @ V[n, t])
                     g["v"][n, t] += eta * (G.T @ x)
                     G_prev = (a[:, None] if per_channel else a) * G
-                # a = 1 - eta lambda
-                deta = deta - (np.sum(lt * da) if per_channel else lt * da)
+                # a = 1 - eta lambda (lambda: the ridge the step used, lt * sc)
+                deta = deta - (np.sum(lt * sc * da) if per_channel else lt * sc * da)
                 dlt = -eta * da
                 # eta = beta / den, den = |x|^2 + lambda-hat + eps
                 g["beta"][n, t] += deta / den
@@ -430,7 +438,11 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                         dlt[imax] += dden
                     else:
                         dlt = dlt + dden
-                    g["lam"][n, t] += dlt
+                    # dlt is the gradient of the ridge used; with lam_scaled that ridge is
+                    # lt |x|^2
+                    g["lam"][n, t] += dlt * sc
+                    if lam_scaled:
+                        dx = dx + 2.0 * x * (np.sum(dlt * lt) if per_channel else dlt * lt)
                 # x_t = phi(k_{t-1}), or the carried key for the sequence's first token
                 if t >= 1:
                     g["k"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)

@@ -754,7 +754,10 @@ def pin_p24_backward(orc):
         gradients, scalar and per channel.
     (e) With QK normalisation (l2 and RMS), finite differences in the raw q, k and carried
         key match their gradients, every rule; and a key scaled by any c > 0 changes
-        nothing, so its gradient is orthogonal to it."""
+        nothing, so its gradient is orthogonal to it.
+    (f) With the scale-coupled ridge (lambda |x|^2), finite differences match the gradients
+        of k, the carried key, beta and lambda, delta and inner rules, scalar and per
+        channel."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -861,6 +864,36 @@ def pin_p24_backward(orc):
             for name in ("q", "k"):
                 dots = np.sum(gr[name] * args[name], axis=-1)
                 assert np.all(np.abs(dots) <= 1e-12 * (1.0 + np.abs(gr[name]).sum())), (rule, qk, name)
+    for rule in (DELTA, INNER):
+        for per_channel in (False, True):
+            T, dk, dv = 4, 3, 2
+            q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+            v = rng.standard_normal((1, 1, T, dv))
+            b = rng.uniform(0.2, 1.5, (1, 1, T))
+            lam = rng.uniform(0.05, 0.5, (1, 1, T, dk) if per_channel else (1, 1, T))
+            dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+            S0, x0 = rng.standard_normal((1, 1, dk, dv)), rng.standard_normal((1, 1, dk))
+            kw = dict(rule=rule, per_channel=per_channel, has0=np.array([[1]]), S0=S0,
+                      lam_scaled=True)
+            args = {"k": k, "xprev0": x0, "beta": b, "lam": lam}
+
+            def loss(a):
+                o, S, _, _ = orc.scan(q, a["k"], v, a["beta"], a["lam"], xprev0=a["xprev0"], **kw)
+                return float(np.sum(o * dO) + np.sum(S * dS))
+
+            gr = orc.scan_backward(q, k, v, b, lam, dO, dS, xprev0=x0, **kw)
+            for name, arr in args.items():
+                for idx in np.ndindex(arr.shape):
+                    a = dict(args)
+                    ap, am = arr.copy(), arr.copy()
+                    ap[idx] += 1e-6
+                    am[idx] -= 1e-6
+                    a[name] = ap
+                    fp = loss(a)
+                    a[name] = am
+                    fd = (fp - loss(a)) / 2e-6
+                    an = gr[name][idx]
+                    assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, per_channel, name, idx, fd, an)
 
 
 ALL_PINS = [

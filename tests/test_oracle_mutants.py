@@ -75,6 +75,8 @@ MUTANTS = {
                                        "Bt, dBt = scale * sb, sb * (1.0 - sb)"),
     "bwd_norm_projection_dropped": ("return f * (g - u * np.sum(u * g, axis=-1, keepdims=True))",
                                     "return f * g"),
+    "bwd_scaled_ridge_key_term_dropped": ("dx = dx + 2.0 * x * (np.sum(dlt * lt) if per_channel else dlt * lt)",
+                                          "dx = dx"),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
