@@ -251,8 +251,8 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  *
  * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE; flags from
  * FWMEM_PHI_ELU1, FWMEM_LAMBDA_PER_CHANNEL, FWMEM_BETA_SIGMOID, FWMEM_BETA_SIGMOID2,
- * FWMEM_LAMBDA_PREACT, FWMEM_QK_L2NORM and FWMEM_QK_RMSNORM (anything else:
- * FWMEM_EUNSUPPORTED); dk and dv in {64, 128}. With a per-channel lambda, the
+ * FWMEM_LAMBDA_PREACT, FWMEM_QK_L2NORM, FWMEM_QK_RMSNORM and FWMEM_LAMBDA_SCALED (with a
+ * scalar lambda, as for scans; anything else: FWMEM_EUNSUPPORTED); dk and dv in {64, 128}. With a per-channel lambda, the
  * denominator's gradient goes to the first channel holding the largest lambda_i. With
  * pre-activated gates, grad_beta and grad_lambda are with respect to the pre-activations
  * passed in; with QK normalisation, grad_q, grad_k and the carried key's gradient are with

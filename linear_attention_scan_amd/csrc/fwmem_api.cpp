@@ -507,7 +507,7 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
   if (mode->rule == FWMEM_RULE_DELTA_PV ||
       (mode->flags & ~(uint32_t)(FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_BETA_SIGMOID |
                                  FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_QK_L2NORM |
-                                 FWMEM_QK_RMSNORM)) != 0)
+                                 FWMEM_QK_RMSNORM | FWMEM_LAMBDA_SCALED)) != 0)
     return FWMEM_EUNSUPPORTED;
   if (!fwmem::bwd_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;

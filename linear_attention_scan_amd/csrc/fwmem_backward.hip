@@ -56,6 +56,7 @@ __device__ __forceinline__ void lds_barrier() {
 // denominator of eta, the write scale b, and whether the step writes at all.
 struct Sc {
   float eta, a, den, rden, b;
+  float lsc;  // the ridge's scale: |x|^2 with the scale-coupled ridge, else 1
   bool key;
 };
 
@@ -252,19 +253,21 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   auto arow = [&](const Sc& s, int u, int j) -> float {
     if (!PCX) return s.a;
     const float l = s_lc[u][row(j)];
-    return R::nlms ? 1.f - s.eta * l : l;
+    return R::nlms ? 1.f - s.eta * l * s.lsc : l;
   };
   auto scal = [&](int t, int u) -> Sc {
     Sc s;
     if (R::nlms) {
       s.key = t >= 1 || has_in;
-      s.den = s_n[u] + s_lm[u] + p.eps;
+      s.lsc = (p.flags & kFlagLamScaled) ? s_n[u] : 1.f;
+      s.den = s_n[u] + s_lm[u] * s.lsc + p.eps;
       s.rden = __builtin_amdgcn_rcpf(s.den);
       s.eta = s.key ? s_bt[u] * s.rden : 0.f;
-      s.a = 1.f - s.eta * s_lm[u];
+      s.a = 1.f - s.eta * s_lm[u] * s.lsc;
       s.b = 1.f;
     } else {
       s.key = true;
+      s.lsc = 1.f;
       s.den = 1.f;
       s.rden = 1.f;
       s.b = s_bt[u];
@@ -385,11 +388,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           // a = 1 - eta lambda, eta = beta / den, den = |x|^2 + lambda + eps (per channel
           // a_i = 1 - eta lambda_i and den takes the largest lambda_i, which passes the
           // denominator's gradient to the first channel holding it)
-          const float deta = xgw - (PCX ? da : s_lm[u] * da);
+          // With the scale-coupled ridge the ridge used is lambda |x|^2 (scalar lambda): its
+          // gradient dlr gives lambda's times |x|^2 and adds 2 x lambda dlr to the key's.
+          const float deta = xgw - (PCX ? da : s_lm[u] * s.lsc * da);
           const float dden = -s.eta * deta * s.rden;
+          const float dlr = -s.eta * da + dden;  // scalar lambda: the ridge's gradient
+          const float dxl = (!PCX && (p.flags & kFlagLamScaled)) ? 2.f * dlr * s_lm[u] : 0.f;
           if (tid == 0) {
             if (p.gbeta != nullptr) p.gbeta[rb + t] = deta * s.rden * dbeta_dz(s_bt[u]);
-            if (p.glam != nullptr && !PCX) p.glam[rb + t] = (-s.eta * da + dden) * dlam_dz(s_lm[u]);
+            if (p.glam != nullptr && !PCX) p.glam[rb + t] = dlr * s.lsc * dlam_dz(s_lm[u]);
           }
           if (PCX && p.glam != nullptr && cq == 0)
 #pragma unroll
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
             const float x = s_x[u][row(j)];
-            float dx = s.eta * gw[j] + 2.f * x * dden;
+            float dx = s.eta * gw[j] + x * (2.f * dden + dxl);
             if (R::solve) {
               const f4 m = Sp[j] * dr;
               dx -= rowsum(m[0] + m[1] + m[2] + m[3]);

@@ -181,7 +181,8 @@ def _bwd(shp=None, md=None, q=M, k=2 * M, v=3 * M, beta=4 * M, lam=None, S_in=No
     (dict(shp=F.shape(1, 1, 8, 96, 128, F.BF16)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_DELTA_PV)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.OUT_BF16)), F.EUNSUPPORTED),
-    (dict(md=F.mode(flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
+    (dict(md=F.mode(flags=F.LAMBDA_SCALED | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.QK_L2NORM | F.PHI_ELU1)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=1 << 12)), F.EINVAL),

@@ -267,3 +267,38 @@ def test_backward_qk_norm(rule, qk, dtype, dk, dv, T, per_channel):
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS, rule=r, eps=w.eps,
                             per_channel=per_channel, S0=w.S0, xprev0=x0, has0=h0, qk_norm=qk)
     _compare(g, ref)
+
+
+@pytest.mark.parametrize("rule,dtype,dk,dv,T,extra", [
+    ("delta", "bf16", 128, 128, 130, None),
+    ("delta", "f32", 64, 128, 70, "qk_gates"),
+    ("inner", "bf16", 128, 64, 100, None),
+    ("inner", "f32", 64, 64, 65, "qk_gates"),
+])
+def test_backward_scaled_ridge(rule, dtype, dk, dv, T, extra):
+    """The scale-coupled ridge (FWMEM_LAMBDA_SCALED, lambda |x|^2, scalar lambda), alone
+    and with RMS normalisation of raw q, k and pre-activated gates, against the oracle's
+    scan_backward with the same options."""
+    r = RULES[rule]
+    both = extra == "qk_gates"
+    say(f"[bwd scaled] {rule} {dtype} dk={dk} dv={dv} T={T} extra={extra}")
+    w = wl.make_scan(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, rule=r, beta_kind="two_sigmoid",
+                     lam_kind="softplus", lam_mu=-3.0, normalise_qk=not both,
+                     qk_norm="rms" if both else None, s0_std=0.1, seed=T + 7)
+    rng = np.random.default_rng(T + 2)
+    x0 = (rng.standard_normal((w.B, w.H, dk)) * (3 if both else 0.09)).astype(np.float32)
+    h0 = np.ones((w.B, w.H), np.int32)
+    dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    flags = F.LAMBDA_SCALED | ((F.QK_RMSNORM | F.BETA_SIGMOID2 | F.LAMBDA_PREACT) if both else 0)
+    beta = w.beta_pre if both else w.beta
+    lam = w.lam_pre if both else w.lam
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(beta), f32_tensor(lam), f32_tensor(dO), rule=r, flags=flags, eps=w.eps,
+                   S_in=make_state(w.B, w.H, dk, dv, S=w.S0, xprev=x0, has=h0),
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
+    ref = orc.scan_backward(w.q, w.k, w.v, beta, lam, dO, dS, rule=r, eps=w.eps, S0=w.S0,
+                            xprev0=x0, has0=h0, lam_scaled=True,
+                            qk_norm="rms" if both else None,
+                            beta_act="sigmoid2" if both else None, lam_act=both)
+    _compare(g, ref)
