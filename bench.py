@@ -73,12 +73,12 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "bwd_kernel"): {
         "sources": ("fwmem_backward.hip", "fwmem_backward.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_backward.hip": "f1491370546923d40a86d8014ae2ef28af6a50ebe0f598ba21764ea68c6cad7f",
+            "fwmem_backward.hip": "44bdbd120dbeaf429dedc61b72ce858e7bda2ed0ec88d4fbbe555a799930bc26",
             "fwmem_backward.h": "0513b4703a3efe53fbfa9cdea4e9091375c514aca3084d4c9bd60330d6197900",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
-        "fetch_kib": 8858568.2, "write_kib": 17180785.4, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 8858531.8, "write_kib": 17180693.4, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
