@@ -1,14 +1,13 @@
 // Backward pass of the scan: the gradients of L = <dO, o> + <dS_T, S_T> with respect to
 // q, k, v, beta, lambda, the initial state S0 and the carried key, for the delta, inner and
-// additive rules with phi identity or elu+1 and a scalar or per-channel lambda. The pages
-// give no backward
-// pass; this is the reverse-mode derivative of the recurrence as the forward pass states it
-// ("Fast Weight Attention for Continual Learning" reading notes, sections 3.2, 4.1-4.3;
-// "attention is also an FFN", sections 2.1, 3.2):
+// additive rules with phi identity or elu+1. The pages give no backward pass; this is the
+// reverse-mode derivative of the recurrence as the forward pass states it ("Fast Weight
+// Attention for Continual Learning" reading notes, sections 3.2, 4.1-4.3; "attention is
+// also an FFN", sections 2.1, 3.2):
 //   S_t = a_t S_{t-1} + eta_t x_t w_t^T,  o_t = S_t^T phi(q_t),
-// with w_t = v_t - S_{t-1}^T x_t (delta) or v_t (inner, additive), and for the delta and inner
-// rules a_t = 1 - eta_t lambda_t, eta_t = beta_t / (|x_t|^2 + lambda_t + eps), x_t = phi(k_{t-1}).
-// Undoing step t with G = dL/dS_t:
+// with w_t = v_t - S_{t-1}^T x_t (delta) or v_t (inner, additive), and for the delta and
+// inner rules a_t = 1 - eta_t lambda_t, eta_t = beta_t / (|x_t|^2 + lambda_t + eps),
+// x_t = phi(k_{t-1}). Undoing step t with G = dL/dS_t:
 //   dphi(q_t) = S_t dO_t;  G += phi(q_t) dO_t^T;  da = <G, S_{t-1}>;
 //   delta:    deta = x^T G r, dr = eta G^T x, dx = eta G r - S_{t-1} dr, dv = dr,
 //             G_{t-1} = a G - x dr^T
@@ -17,20 +16,22 @@
 //             G_{t-1} = gamma G
 // and for the shifted rules the scalar chain through a, eta and the denominator.
 //
+// Options: per channel, lambda_i scales row i's decay (1 - eta lambda_i, or the retention
+// gamma_i) and eta's denominator takes the largest lambda_i, so da and the lambda gradient
+// are per row. Pre-activated gates are activated as they are staged and their gradients
+// taken through the activation. The scale-coupled ridge is lambda |x|^2 (scalar lambda).
 // With QK normalisation, q, k and the carried key are rescaled to a fixed length as they
 // are staged, and a second kernel takes their gradients back through the rescaling.
-// Per channel, lambda_i scales row i's decay (1 - eta lambda_i, or the retention gamma_i)
-// and eta's denominator takes the largest lambda_i; da and the lambda gradient are then
-// per row.
 //
 // One persistent 1024-thread workgroup per head, token-serial (the chunked backward is
-// future work). A chunk here is 64 tokens, 32 with a per-channel lambda. The state is distributed as in the decode kernel: thread (rg, cq) holds
-// float4 column group cq of rows rg, rg + RG, ... A forward pass stores the state at every
-// chunk start in the workspace; then, per chunk from the last, the chunk's states after
-// each token are recomputed into the workspace and the chunk's tokens are undone from the
-// last. Each chunk's keys, queries, values, dO and gates are staged in LDS once, so a
-// token costs one workgroup barrier per pass (the column and scalar sums share it) and
-// the state before the next token to undo is loaded while the current one is undone.
+// future work). The state is distributed as in the decode kernel: thread (rg, cq) holds
+// float4 column group cq of rows rg, rg + RG, ... A chunk here is 64 tokens, 32 with a
+// per-channel lambda. A forward pass stores the state at every chunk start in the
+// workspace; then, per chunk from the last, the chunk's states after each token are
+// recomputed into the workspace and the chunk's tokens are undone from the last. Each
+// chunk's keys, queries, values, dO and gates are staged in LDS once; a token's column and
+// scalar sums share one reduction (two LDS-only barriers), and the state before the next
+// token to undo is loaded while the current one is undone.
 #include "fwmem_backward.h"
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       s.rden = 1.f;
       s.b = s_bt[u];
       s.eta = s.b;
-      s.a = s_lm[u];
+      s.a = PCX ? 1.f : s_lm[u];  // per channel the rows' retentions come from s_lc
     }
     return s;
   };
