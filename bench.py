@@ -354,8 +354,8 @@ def main():
 
 def backward_supported(w):
     from linear_attention_scan_amd import workloads as wl
-    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and w.qk_norm is None
-            and not w.znorm and not w.lam_scaled and w.dk in (64, 128) and w.dv in (64, 128))
+    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and not w.znorm
+            and not (w.lam_scaled and w.per_channel) and w.dk in (64, 128) and w.dv in (64, 128))
 
 
 def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
@@ -370,6 +370,10 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     from linear_attention_scan_amd import workloads as wl
     shp = F.shape(w.B, w.H, w.T, w.dk, w.dv, F.BF16 if w.dtype == "bf16" else F.F32)
     flags = (F.PHI_ELU1 if w.phi == wl.PHI_ELU1 else 0) | (F.LAMBDA_PER_CHANNEL if w.per_channel else 0)
+    if w.qk_norm is not None:
+        flags |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
+    if w.lam_scaled:
+        flags |= F.LAMBDA_SCALED
     md = F.mode(w.rule, flags, w.eps, 0)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
