@@ -332,7 +332,8 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     dv = np.asarray(v).shape[-1]
     N = B * H
     Q, K, V = _heads(q, 2), _heads(k, 2), _heads(v, 2)
-    Bt = None if beta is None else _heads(beta, 1)
+    pv = rule == RULE_DELTA_PV
+    Bt = None if beta is None else _heads(beta, 2 if pv else 1)
     Lm = None if lam is None else _heads(lam, 2 if per_channel else 1)
     # gate activations: the activated gates, and each gate's derivative by its
     # pre-activation (1 without an activation)
@@ -352,9 +353,11 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     S_init = np.zeros((N, dk, dv)) if S0 is None else _heads(S0, 2)
     x_init = np.zeros((N, dk)) if xprev0 is None else _heads(xprev0, 1)
     h_init = np.zeros(N, dtype=bool) if has0 is None else (np.asarray(has0).reshape(N) != 0)
-    shifted = rule in (RULE_DELTA, RULE_INNER)
+    shifted = rule in (RULE_DELTA, RULE_INNER, RULE_DELTA_PV)
     if not shifted and rule != RULE_ADDITIVE:
         raise ValueError(rule)
+    if pv and per_channel:
+        raise ValueError("the per-value-channel rule takes a scalar lambda")
     if lam_scaled and not shifted:
         raise ValueError("lam_scaled takes the delta or inner rule")
 
@@ -388,11 +391,14 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                     # the ridge the step uses: lambda, or lambda |x|^2 (scale-coupled)
                     sc = (x @ x) if lam_scaled else 1.0
                     den = x @ x + lhat * sc + eps
-                    eta = Bt[n, t] / den
+                    eta = Bt[n, t] / den                # per value channel: a d_v-vector
                     a = 1.0 - eta * lt * sc
-                    decay = a[:, None] if per_channel else a
-                    r = vt - Sp.T @ x if rule == RULE_DELTA else vt
-                    Sc = decay * Sp + eta * np.outer(x, r)
+                    r = vt - Sp.T @ x if rule != RULE_INNER else vt
+                    if pv:                              # column j decays by a_j, steps by eta_j
+                        Sc = Sp * a[None, :] + np.outer(x, eta * r)
+                    else:
+                        decay = a[:, None] if per_channel else a
+                        Sc = decay * Sp + eta * np.outer(x, r)
                     steps.append((Sp, x, eta, a, den, lt, imax, r, sc))
             else:
                 gam = 1.0 if Lm is None else Lm[n, t]
@@ -413,36 +419,54 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                 if rec is None:
                     continue                    # S_t = S_{t-1}
                 Sp, x, eta, a, den, lt, imax, r, sc = rec
-                da = np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
-                if rule == RULE_DELTA:
-                    deta = x @ G @ r
-                    dr = eta * (G.T @ x)
-                    dx = eta * (G @ r) - Sp @ dr
+                if pv:
+                    # per value channel j: da_j = <G_:j, S_:j>, deta_j = (G^T x)_j r_j - ridge da_j
+                    da = np.sum(G * Sp, axis=0)
+                    gx = G.T @ x
+                    deta = gx * r - lt * sc * da
+                    dr = eta * gx
+                    dx = G @ (eta * r) - Sp @ dr
                     g["v"][n, t] += dr
-                    G_prev = (a[:, None] if per_channel else a) * G - np.outer(x, dr)
+                    g["beta"][n, t] += deta / den
+                    dden = -np.sum(eta * deta) / den
+                    dx = dx + 2.0 * x * dden
+                    if Lm is not None:
+                        dlt = np.sum(-eta * da) + dden   # the gradient of the ridge used
+                        g["lam"][n, t] += dlt * sc
+                        if lam_scaled:
+                            dx = dx + 2.0 * x * dlt * lt
+                    G_prev = G * a[None, :] - np.outer(x, dr)
                 else:
-                    deta = x @ G @ V[n, t]
-                    dx = eta * (G @ V[n, t])
-                    g["v"][n, t] += eta * (G.T @ x)
-                    G_prev = (a[:, None] if per_channel else a) * G
-                # a = 1 - eta lambda (lambda: the ridge the step used, lt * sc)
-                deta = deta - (np.sum(lt * sc * da) if per_channel else lt * sc * da)
-                dlt = -eta * da
-                # eta = beta / den, den = |x|^2 + lambda-hat + eps
-                g["beta"][n, t] += deta / den
-                dden = -eta * deta / den
-                dx = dx + 2.0 * x * dden
-                if Lm is not None:
-                    if per_channel:
-                        dlt = dlt.copy()
-                        dlt[imax] += dden
+                    da = np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
+                    if rule == RULE_DELTA:
+                        deta = x @ G @ r
+                        dr = eta * (G.T @ x)
+                        dx = eta * (G @ r) - Sp @ dr
+                        g["v"][n, t] += dr
+                        G_prev = (a[:, None] if per_channel else a) * G - np.outer(x, dr)
                     else:
-                        dlt = dlt + dden
-                    # dlt is the gradient of the ridge used; with lam_scaled that ridge is
-                    # lt |x|^2
-                    g["lam"][n, t] += dlt * sc
-                    if lam_scaled:
-                        dx = dx + 2.0 * x * (np.sum(dlt * lt) if per_channel else dlt * lt)
+                        deta = x @ G @ V[n, t]
+                        dx = eta * (G @ V[n, t])
+                        g["v"][n, t] += eta * (G.T @ x)
+                        G_prev = (a[:, None] if per_channel else a) * G
+                    # a = 1 - eta lambda (lambda: the ridge the step used, lt * sc)
+                    deta = deta - (np.sum(lt * sc * da) if per_channel else lt * sc * da)
+                    dlt = -eta * da
+                    # eta = beta / den, den = |x|^2 + lambda-hat + eps
+                    g["beta"][n, t] += deta / den
+                    dden = -eta * deta / den
+                    dx = dx + 2.0 * x * dden
+                    if Lm is not None:
+                        if per_channel:
+                            dlt = dlt.copy()
+                            dlt[imax] += dden
+                        else:
+                            dlt = dlt + dden
+                        # dlt is the gradient of the ridge used; with lam_scaled that ridge is
+                        # lt |x|^2
+                        g["lam"][n, t] += dlt * sc
+                        if lam_scaled:
+                            dx = dx + 2.0 * x * (np.sum(dlt * lt) if per_channel else dlt * lt)
                 # x_t = phi(k_{t-1}), or the carried key for the sequence's first token
                 if t >= 1:
                     g["k"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)

@@ -757,7 +757,11 @@ def pin_p24_backward(orc):
         nothing, so its gradient is orthogonal to it.
     (f) With the scale-coupled ridge (lambda |x|^2), finite differences match the gradients
         of k, the carried key, beta and lambda, delta and inner rules, scalar and per
-        channel."""
+        channel.
+    (g) The per-value-channel rule: finite differences match every gradient (q, k, v, the
+        per-channel beta, lambda, S0, the carried key), plain, with elu+1, and with the
+        scale-coupled ridge and pre-activated gates; with every beta_j equal it is the
+        delta rule, and so are its gradients (beta's summed over j)."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -894,6 +898,49 @@ def pin_p24_backward(orc):
                     fd = (fp - loss(a)) / 2e-6
                     an = gr[name][idx]
                     assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (rule, per_channel, name, idx, fd, an)
+
+    PV = orc.RULE_DELTA_PV
+    for variant in ("plain", "elu1", "scaled_gates"):
+        T, dk, dv = 4, 3, 2
+        q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+        v = rng.standard_normal((1, 1, T, dv))
+        if variant == "scaled_gates":
+            b, lam = rng.standard_normal((1, 1, T, dv)), rng.normal(-1.0, 1.0, (1, 1, T))
+        else:
+            b, lam = rng.uniform(0.2, 1.5, (1, 1, T, dv)), rng.uniform(0.05, 0.5, (1, 1, T))
+        dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+        S0, x0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
+        kw = dict(rule=PV, has0=np.array([[1]]), phi_kind="elu1" if variant == "elu1" else "identity")
+        if variant == "scaled_gates":
+            kw.update(lam_scaled=True, beta_act="sigmoid2", lam_act=True)
+        args = {"q": q, "k": k, "v": v, "beta": b, "lam": lam, "S0": S0, "xprev0": x0}
+
+        def loss(a):
+            o, S, _, _ = orc.scan(a["q"], a["k"], a["v"], a["beta"], a["lam"], S0=a["S0"],
+                                  xprev0=a["xprev0"], **kw)
+            return float(np.sum(o * dO) + np.sum(S * dS))
+
+        gr = orc.scan_backward(q, k, v, b, lam, dO, dS, S0=S0, xprev0=x0, **kw)
+        for name, arr in args.items():
+            for idx in np.ndindex(arr.shape):
+                a = dict(args)
+                ap, am = arr.copy(), arr.copy()
+                ap[idx] += 1e-6
+                am[idx] -= 1e-6
+                a[name] = ap
+                fp = loss(a)
+                a[name] = am
+                fd = (fp - loss(a)) / 2e-6
+                an = gr[name][idx]
+                assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (variant, name, idx, fd, an)
+    # equal steps on every value channel: the delta rule
+    b1 = rng.uniform(0.2, 1.5, (1, 1, T))
+    bpv = np.repeat(b1[..., None], dv, axis=-1)
+    g_pv = orc.scan_backward(q, k, v, bpv, lam, dO, dS, rule=PV, S0=S0, xprev0=x0, has0=np.array([[1]]))
+    g_d = orc.scan_backward(q, k, v, b1, lam, dO, dS, rule=DELTA, S0=S0, xprev0=x0, has0=np.array([[1]]))
+    for name in ("q", "k", "v", "lam", "S0", "xprev0"):
+        np.testing.assert_allclose(g_pv[name], g_d[name], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g_pv["beta"].sum(axis=-1), g_d["beta"], rtol=1e-12, atol=1e-12)
 
 
 ALL_PINS = [
