@@ -504,8 +504,7 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
   if (st != FWMEM_OK) return st;
   st = check_scan_mode(mode);
   if (st != FWMEM_OK) return st;
-  if (mode->rule == FWMEM_RULE_DELTA_PV ||
-      (mode->flags & ~(uint32_t)(FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_BETA_SIGMOID |
+  if ((mode->flags & ~(uint32_t)(FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_BETA_SIGMOID |
                                  FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_QK_L2NORM |
                                  FWMEM_QK_RMSNORM | FWMEM_LAMBDA_SCALED)) != 0)
     return FWMEM_EUNSUPPORTED;
@@ -515,8 +514,8 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
 
 size_t bwd_ws_bytes(const fwmem_shape* shape, const fwmem_mode* mode) {
   const size_t BH = (size_t)shape->B * (size_t)shape->H;
-  const bool pc = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0;
-  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, pc));
+  const bool small = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || mode->rule == FWMEM_RULE_DELTA_PV;
+  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, small));
 }
 
 }  // namespace
@@ -555,6 +554,7 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   const size_t es = esize(shape->dtype);
   if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(beta, 4) ||
       !aligned(lambda, 4) || !aligned(grad_out, 4) || !aligned(grad_q, 4) ||
+      (mode->rule == FWMEM_RULE_DELTA_PV && !aligned(grad_beta, 16)) ||
       !aligned(grad_k, 4) || !aligned(grad_beta, 4) || !aligned(grad_lambda, 4) ||
       !aligned(grad_v, 16) || !aligned(S_in, 16) || !aligned(grad_S_out, 16) ||
       !aligned(grad_S_in, 16) || !aligned(workspace, 16))
@@ -563,11 +563,13 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   const size_t nq = z.BH * T * shape->dk * es, nv = z.BH * T * shape->dv * es;
   const size_t ns = z.BH * T * 4, nsb = z.state_bytes;
   const size_t nl = ns * ((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) ? (size_t)shape->dk : 1);
+  const bool rule_pv = mode->rule == FWMEM_RULE_DELTA_PV;
+  const size_t nb = ns * (rule_pv ? (size_t)shape->dv : 1);  // beta: per value channel
   const size_t ngq = z.BH * T * shape->dk * 4, ngv = z.BH * T * shape->dv * 4;
   const void* ins[] = {q, k, v, beta, lambda, S_in, grad_out, grad_S_out};
-  const size_t nins[] = {nq, nq, nv, ns, nl, nsb, ngv, nsb};
+  const size_t nins[] = {nq, nq, nv, nb, nl, nsb, ngv, nsb};
   const void* outs[] = {grad_q, grad_k, grad_v, grad_beta, grad_lambda, grad_S_in, workspace};
-  const size_t nouts[] = {ngq, ngq, ngv, ns, nl, nsb, need};
+  const size_t nouts[] = {ngq, ngq, ngv, nb, nl, nsb, need};
   for (int i = 0; i < 7; ++i) {
     for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], nouts[i], ins[j], nins[j])) return FWMEM_EOVERLAP;
@@ -602,7 +604,7 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.T = (int)T;
   p.dk = shape->dk;
   p.dv = shape->dv;
-  const int ck = fwmem::bwd_chunk((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0);
+  const int ck = fwmem::bwd_chunk((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || rule_pv);
   p.nchunks = (int)((T + ck - 1) / ck);
   p.rule = mode->rule;
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;

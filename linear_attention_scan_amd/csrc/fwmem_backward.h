@@ -14,7 +14,7 @@ struct BwdParams {
   const void* q;          // [BH][T][dk]
   const void* k;          // [BH][T][dk]
   const void* v;          // [BH][T][dv]
-  const float* beta;      // [BH][T] (optional for the additive rule)
+  const float* beta;      // [BH][T] ([BH][T][dv] per value channel; optional for the additive rule)
   const float* lam;       // [BH][T] ([BH][T][dk] with kFlagPerChannel) or null
   const float* S_in;      // [BH][dk][dv] or null (zeros)
   const float* xprev_in;  // [BH][dk] or null
@@ -24,26 +24,27 @@ struct BwdParams {
   float* gq;              // [BH][T][dk]
   float* gk;              // [BH][T][dk]
   float* gv;              // [BH][T][dv]
-  float* gbeta;           // [BH][T] or null (not written)
+  float* gbeta;           // beta's shape, or null (not written)
   float* glam;            // lam's shape, or null (not written)
   float* gS0;             // [BH][dk][dv] or null
   float* gx0;             // [BH][dk] or null (with gS0)
   int32_t* gh0;           // [BH] or null (with gS0): written 0
   float* ws;              // per head: chunk-start states, then one chunk's states
   int BH, T, dk, dv, nchunks;
-  int rule;  // kRuleDelta, kRuleAdditive or kRuleInner
+  int rule;  // kRuleDelta, kRuleAdditive, kRuleInner or kRuleDeltaPV
   int bf16;
   uint32_t flags;
   float eps;
 };
 
 // Tokens the backward stages at a time and between the states it keeps: 64, or 32 with a
-// per-channel lambda (whose staged values would not fit LDS with 64).
-__host__ __device__ constexpr int bwd_chunk(bool per_channel) { return per_channel ? 32 : 64; }
+// per-channel lambda or a per-value-channel beta (whose staged values would not fit LDS
+// with 64).
+__host__ __device__ constexpr int bwd_chunk(bool small) { return small ? 32 : 64; }
 // Workspace floats per head: the state at each chunk start, the states after each of a
 // chunk's tokens, and a chunk's worth of d_v-vectors.
-__host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv, bool per_channel) {
-  const size_t ck = (size_t)bwd_chunk(per_channel);
+__host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv, bool small) {
+  const size_t ck = (size_t)bwd_chunk(small);
   const size_t nchunks = ((size_t)T + ck - 1) / ck;
   const size_t SS = (size_t)dk * (size_t)dv;
   return T > 0 ? (nchunks + ck) * SS + ck * (size_t)dv : 0;

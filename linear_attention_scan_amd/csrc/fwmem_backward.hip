@@ -64,9 +64,10 @@ struct Sc {
 template <typename InT, int DK, int DV, int RULE, bool PCX>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using R = Rule<RULE>;
-  // tokens staged at a time, and between stored states (per-channel lambda, also staged,
-  // halves it to fit LDS)
-  constexpr int CK = bwd_chunk(PCX);
+  constexpr bool PV = RULE == kRuleDeltaPV;  // one step size per value column
+  // tokens staged at a time, and between stored states (a per-channel lambda or a
+  // per-column beta, also staged, halves it to fit LDS)
+  constexpr int CK = bwd_chunk(PCX || PV);
   constexpr int TPRd = DV / 4;   // threads per row
   constexpr int RG = NT / TPRd;  // row groups
   constexpr int RPT = DK / RG;   // rows per thread
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ float s_sum[2][NWV][2];
   __shared__ __attribute__((aligned(16))) float s_tot[2][DV + 4];  // column totals, then the two scalars
   __shared__ float s_lc[PCX ? CK : 1][PCX ? DK : 1];  // per-channel lambda (or retention)
+  __shared__ __attribute__((aligned(16))) float s_bc[PV ? CK : 1][PV ? DV : 4];  // per-column beta
   __shared__ float s_n[CK], s_bt[CK], s_lm[CK];  // |x|^2, beta, lambda (per channel: its maximum)
   __shared__ int s_im[CK];                        // per channel: the first channel at the maximum
 
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
   const size_t SS = (size_t)DK * DV;
   const int nch = (T + CK - 1) / CK;
-  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV, PCX);
+  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV, PCX || PV);
   float* cs = ckpt + (size_t)nch * SS;  // [CK] states after each token of a chunk
 
   auto phi = [&](float x) { return elu ? phi_elu1(x) : x; };
@@ -184,10 +186,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       const int u = idx / DV, j = idx % DV, t = t0 + u;
       s_w[u][j] = t < t1 ? In<InT>::load1(vb + (size_t)t * DV + j) : 0.f;
       if (bwd) s_do[u][j] = t < t1 ? p.dout[(rb + t) * DV + j] : 0.f;
+      if constexpr (PV) s_bc[u][j] = t < t1 ? act_beta(p.beta[(rb + t) * DV + j], p.flags) : 1.f;
     }
     if (tid < CK) {
       const int t = t0 + tid;
-      s_bt[tid] = (t < t1 && p.beta != nullptr) ? act_beta(p.beta[rb + t], p.flags) : 1.f;
+      s_bt[tid] = (!PV && t < t1 && p.beta != nullptr) ? act_beta(p.beta[rb + t], p.flags) : 1.f;
       if (!PCX)
         s_lm[tid] = (t < t1 && p.lam != nullptr) ? act_lam(p.lam[rb + t], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
     }
@@ -291,6 +294,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       w = w - reduce(pp, 0.f, 0.f, d0, d1);
       if (rg == 0) *reinterpret_cast<f4*>(&s_w[u][4 * cq]) = w;
     }
+    if constexpr (PV) {  // column c decays by 1 - eta_c lambda and steps by eta_c
+      const f4 e4 = s.key ? *reinterpret_cast<const f4*>(&s_bc[u][4 * cq]) * s.rden : f4{0.f, 0.f, 0.f, 0.f};
+      const f4 a4 = 1.f - e4 * (s_lm[u] * s.lsc);
+      const f4 ew = e4 * w;
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) S[j] = S[j] * a4 + ew * s_x[u][row(j)];
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < RPT; ++j) S[j] = S[j] * arow(s, u, j) + w * (s.eta * s_x[u][row(j)]);
   };
@@ -353,13 +364,61 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (!s.key) {  // no write: S_t = S_{t-1}; nothing else depends on this step
         if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = f4{0.f, 0.f, 0.f, 0.f};
         if (tid == 0) {
-          if (p.gbeta != nullptr) p.gbeta[rb + t] = 0.f;
+          if (p.gbeta != nullptr && !PV) p.gbeta[rb + t] = 0.f;
           if (p.glam != nullptr && !PCX) p.glam[rb + t] = 0.f;
         }
+        if constexpr (PV)
+          if (p.gbeta != nullptr && rg == 0)
+            *reinterpret_cast<f4*>(p.gbeta + (rb + t) * DV + 4 * cq) = f4{0.f, 0.f, 0.f, 0.f};
         if (PCX && p.glam != nullptr)
           for (int i = tid; i < DK; i += NT) p.glam[(rb + t) * DK + i] = 0.f;
         if (p.gx0 != nullptr)
           for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
+      } else if constexpr (PV) {
+        // per value column c: da_c = <G_:c, S_{t-1}:c>, deta_c = (G^T x)_c r_c - ridge da_c,
+        // dr_c = eta_c (G^T x)_c; eta's shared denominator takes sum_c eta_c deta_c
+        const f4 w = *reinterpret_cast<const f4*>(&s_w[u][4 * cq]);  // the residual
+        f4 gx = {0.f, 0.f, 0.f, 0.f}, dap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+          gx += G[j] * s_x[u][row(j)];
+          dap += G[j] * Sp[j];
+        }
+        float d0, d1;
+        const f4 gtx = reduce(gx, 0.f, 0.f, d0, d1);
+        const f4 da4 = reduce(dap, 0.f, 0.f, d0, d1);
+        const f4 b4 = *reinterpret_cast<const f4*>(&s_bc[u][4 * cq]);
+        const f4 e4 = b4 * s.rden;
+        const float ridge = s_lm[u] * s.lsc;
+        const f4 a4 = 1.f - e4 * ridge;
+        const f4 deta = gtx * w - da4 * ridge;
+        const f4 dr = e4 * gtx;
+        if (rg == 0) {
+          *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = dr;
+          if (p.gbeta != nullptr) {
+            f4 gb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gb[e] = deta[e] * s.rden * dbeta_dz(b4[e]);
+            *reinterpret_cast<f4*>(p.gbeta + (rb + t) * DV + 4 * cq) = gb;
+          }
+        }
+        const f4 ed = e4 * deta, ea = e4 * da4;
+        const float dden = -rowsum(ed[0] + ed[1] + ed[2] + ed[3]) * s.rden;
+        const float dlr = -rowsum(ea[0] + ea[1] + ea[2] + ea[3]) + dden;  // the ridge's gradient
+        const float dxl = (p.flags & kFlagLamScaled) ? 2.f * dlr * s_lm[u] : 0.f;
+        if (tid == 0 && p.glam != nullptr) p.glam[rb + t] = dlr * s.lsc * dlam_dz(s_lm[u]);
+        const f4 ew = e4 * w;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+          const float x = s_x[u][row(j)];
+          const f4 m = G[j] * ew - Sp[j] * dr;
+          const float dx = rowsum(m[0] + m[1] + m[2] + m[3]) + x * (2.f * dden + dxl);
+          if (cq == 0) {
+            if (t >= 1) p.gk[(rb + t - 1) * DK + row(j)] = dx * dphi_of(x);
+            else if (p.gx0 != nullptr) p.gx0[(size_t)bh * DK + row(j)] = dx;
+          }
+          G[j] = G[j] * a4 - dr * x;
+        }
       } else {
         // w: the residual (delta) or the value; G w per row; <G, S_{t-1}> (per channel:
         // per row, and the ridge rules' sum of lambda_i times it), x^T G w, G^T x
@@ -489,6 +548,8 @@ template <typename InT, int DK, int DV, bool PCX>
 hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.BH), block(NT);
   if (p.rule == kRuleDelta) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDelta, PCX>), grid, block, 0, st, p);
+  else if (!PCX && p.rule == kRuleDeltaPV)
+    hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDeltaPV, false>), grid, block, 0, st, p);
   else if (p.rule == kRuleInner) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleInner, PCX>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive, PCX>), grid, block, 0, st, p);
   return hipGetLastError();

@@ -265,7 +265,7 @@ def scan_bwd(q, k, v, beta, lam, grad_out, *, rule=RULE_DELTA, flags=0, eps=1e-6
     g = {"q": torch.empty((B, H, T, dk), dtype=torch.float32, device=dev),
          "k": torch.empty((B, H, T, dk), dtype=torch.float32, device=dev),
          "v": torch.empty((B, H, T, dv), dtype=torch.float32, device=dev),
-         "beta": None if beta is None else torch.empty((B, H, T), dtype=torch.float32, device=dev),
+         "beta": None if beta is None else torch.empty(tuple(beta.shape), dtype=torch.float32, device=dev),
          "lam": None if lam is None else torch.empty(tuple(lam.shape), dtype=torch.float32, device=dev),
          "state": State(B, H, dk, dv, device=dev)}
     need = bwd_workspace_bytes(shp, md)

@@ -179,7 +179,10 @@ def _bwd(shp=None, md=None, q=M, k=2 * M, v=3 * M, beta=4 * M, lam=None, S_in=No
 
 @pytest.mark.parametrize("case,expect", [
     (dict(shp=F.shape(1, 1, 8, 96, 128, F.BF16)), F.EUNSUPPORTED),
-    (dict(md=F.mode(rule=F.RULE_DELTA_PV)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV, flags=F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV), gbeta=9 * M + 4), F.EALIGN),   # per-column beta: float4
+    (dict(md=F.mode(rule=F.RULE_DELTA_PV), gbeta=4 * M + 64), F.EOVERLAP),  # onto beta [.., dv]
     (dict(md=F.mode(flags=F.OUT_BF16)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.LAMBDA_SCALED | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
@@ -211,6 +214,11 @@ def test_bwd_workspace_size_and_empty_batch():
     shp, md = F.shape(2, 3, 100, 128, 64, F.F32), F.mode(rule=F.RULE_INNER)
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), ctypes.byref(n)) == F.OK
     want = 4 * 6 * ((2 + 64) * 128 * 64 + 64 * 64)
+    assert n.value == (want + 255) // 256 * 256
+    # the per-value-channel rule: 32-token chunks as well
+    mdv = F.mode(rule=F.RULE_DELTA_PV)
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(mdv), ctypes.byref(n)) == F.OK
+    want = 4 * 6 * ((4 + 32) * 128 * 64 + 32 * 64)
     assert n.value == (want + 255) // 256 * 256
     shp0 = F.shape(2, 3, 0, 128, 64, F.F32)
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp0), ctypes.byref(md), ctypes.byref(n)) == F.OK

@@ -302,3 +302,45 @@ def test_backward_scaled_ridge(rule, dtype, dk, dv, T, extra):
                             qk_norm="rms" if both else None,
                             beta_act="sigmoid2" if both else None, lam_act=both)
     _compare(g, ref)
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T,extra", [
+    ("bf16", 128, 128, 130, None),
+    ("f32", 64, 128, 70, "elu1"),
+    ("bf16", 128, 64, 97, "rms_scaled_gates"),
+    ("f32", 64, 64, 33, None),
+])
+def test_backward_per_value_channel(dtype, dk, dv, T, extra):
+    """FWMEM_RULE_DELTA_PV: beta [B,H,T,dv], one step size and decay per value column;
+    every gradient (beta's per column) against the oracle's scan_backward, plain, with
+    elu+1, and with RMS normalisation, the scale-coupled ridge and pre-activated gates."""
+    r = wl.RULE_DELTA_PV
+    opts = extra == "rms_scaled_gates"
+    phi = "elu1" if extra == "elu1" else "identity"
+    say(f"[bwd pv] {dtype} dk={dk} dv={dv} T={T} extra={extra}")
+    w = wl.make_scan(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, rule=r, beta_kind="two_sigmoid",
+                     lam_kind="softplus", lam_mu=-3.0,
+                     phi=wl.PHI_ELU1 if phi == "elu1" else wl.PHI_IDENTITY,
+                     normalise_qk=not opts and phi != "elu1", qk_norm="rms" if opts else None,
+                     s0_std=0.1, seed=T + dv)
+    rng = np.random.default_rng(T + 3)
+    kp = rng.standard_normal((w.B, w.H, dk)).astype(np.float32)
+    x0 = (kp * 3 if opts else kp / np.linalg.norm(kp, axis=-1, keepdims=True)).astype(np.float32)
+    if phi == "elu1":
+        x0 = np.where(x0 > 0, x0 + 1.0, np.exp(x0)).astype(np.float32)
+    h0 = np.ones((w.B, w.H), np.int32)
+    dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    flags = ((F.PHI_ELU1 if phi == "elu1" else 0)
+             | ((F.QK_RMSNORM | F.LAMBDA_SCALED | F.BETA_SIGMOID2 | F.LAMBDA_PREACT) if opts else 0))
+    beta = w.beta_pre if opts else w.beta
+    lam = w.lam_pre if opts else w.lam
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(beta), f32_tensor(lam), f32_tensor(dO), rule=r, flags=flags, eps=w.eps,
+                   S_in=make_state(w.B, w.H, dk, dv, S=w.S0, xprev=x0, has=h0),
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
+    assert tuple(g["beta"].shape) == (w.B, w.H, T, dv)
+    ref = orc.scan_backward(w.q, w.k, w.v, beta, lam, dO, dS, rule=r, phi_kind=phi, eps=w.eps,
+                            S0=w.S0, xprev0=x0, has0=h0, qk_norm="rms" if opts else None,
+                            lam_scaled=opts, beta_act="sigmoid2" if opts else None, lam_act=opts)
+    _compare(g, ref)
