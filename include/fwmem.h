@@ -234,7 +234,8 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
                         const void* S_in, void* out, void* S_out, fwmem_stream stream);
 
 /* Bytes of device workspace fwmem_scan_bwd needs for this shape and mode (0 when T == 0
- * or B*H == 0): with C = 64 (32 with FWMEM_LAMBDA_PER_CHANNEL), per head the state at
+ * or B*H == 0): with C = 64 (32 with FWMEM_LAMBDA_PER_CHANNEL or FWMEM_RULE_DELTA_PV), per
+ * head the state at
  * each C-token chunk start plus C more state buffers and C d_v-vectors of scratch, i.e.
  * 4 * ((ceil(T/C) + C) * dk * dv + C * dv) bytes, rounded up to a multiple of 256.
  * Its contents need no initialisation and are scratch only. */
@@ -249,7 +250,8 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  * 3.2); this is its exact reverse-mode derivative, token by token, with the forward
  * states recomputed from a state kept at every chunk start.
  *
- * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE; flags from
+ * Supported: FWMEM_RULE_DELTA, FWMEM_RULE_INNER, FWMEM_RULE_ADDITIVE, FWMEM_RULE_DELTA_PV
+ * (beta and grad_beta [B][H][T][dv], grad_beta 16-byte aligned); flags from
  * FWMEM_PHI_ELU1, FWMEM_LAMBDA_PER_CHANNEL, FWMEM_BETA_SIGMOID, FWMEM_BETA_SIGMOID2,
  * FWMEM_LAMBDA_PREACT, FWMEM_QK_L2NORM, FWMEM_QK_RMSNORM and FWMEM_LAMBDA_SCALED (with a
  * scalar lambda, as for scans; anything else: FWMEM_EUNSUPPORTED); dk and dv in {64, 128}. With a per-channel lambda, the
