@@ -1,6 +1,7 @@
 // Backward pass of the scan: the gradients of L = <dO, o> + <dS_T, S_T> with respect to
-// q, k, v, beta, lambda, the initial state S0 and the carried key, for the delta, inner and
-// additive rules with phi identity or elu+1. The pages give no backward pass; this is the
+// q, k, v, beta, lambda, the initial state S0 and the carried key, for the delta, inner,
+// additive and per-value-channel rules with phi identity or elu+1. The pages give no
+// backward pass; this is the
 // reverse-mode derivative of the recurrence as the forward pass states it ("Fast Weight
 // Attention for Continual Learning" reading notes, sections 3.2, 4.1-4.3; "attention is
 // also an FFN", sections 2.1, 3.2):
@@ -16,6 +17,8 @@
 //             G_{t-1} = gamma G
 // and for the shifted rules the scalar chain through a, eta and the denominator.
 //
+// The per-value-channel rule gives column c its own step eta_c and decay 1 - eta_c lambda,
+// so da, deta and the beta gradient are per column.
 // Options: per channel, lambda_i scales row i's decay (1 - eta lambda_i, or the retention
 // gamma_i) and eta's denominator takes the largest lambda_i, so da and the lambda gradient
 // are per row. Pre-activated gates are activated as they are staged and their gradients
