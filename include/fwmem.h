@@ -254,7 +254,8 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  * (beta and grad_beta [B][H][T][dv], grad_beta 16-byte aligned); flags from
  * FWMEM_PHI_ELU1, FWMEM_LAMBDA_PER_CHANNEL, FWMEM_BETA_SIGMOID, FWMEM_BETA_SIGMOID2,
  * FWMEM_LAMBDA_PREACT, FWMEM_QK_L2NORM, FWMEM_QK_RMSNORM and FWMEM_LAMBDA_SCALED (with a
- * scalar lambda, as for scans; anything else: FWMEM_EUNSUPPORTED); dk and dv in {64, 128}. With a per-channel lambda, the
+ * scalar lambda, as for scans). Anything else, FWMEM_ZNORM included, returns
+ * FWMEM_EUNSUPPORTED. dk and dv in {64, 128}. With a per-channel lambda, the
  * denominator's gradient goes to the first channel holding the largest lambda_i. With
  * pre-activated gates, grad_beta and grad_lambda are with respect to the pre-activations
  * passed in; with QK normalisation, grad_q, grad_k and the carried key's gradient are with
@@ -266,7 +267,8 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  *                state's carried key and flag take no gradient
  *   grad_q, grad_k [B][H][T][dk] float32; grad_v [B][H][T][dv] float32 (required when
  *                T > 0; every element is written)
- *   grad_beta    [B][H][T] float32 or NULL (not written)
+ *   grad_beta    beta's shape ([B][H][T], or [B][H][T][dv] per value channel) float32,
+ *                or NULL (not written)
  *   grad_lambda  lambda's shape ([B][H][T], or [B][H][T][dk] per channel) float32, or
  *                NULL (not written). With beta or lambda NULL these are the gradients
  *                at the default value (write scale 1, ridge 0, retention 1).
