@@ -286,7 +286,7 @@ def unit_rows_vjp(x: np.ndarray, g: np.ndarray, length: float = 1.0) -> np.ndarr
 
 def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
                   per_channel=False, S0=None, xprev0=None, has0=None, beta_act=None,
-                  lam_act=False, qk_norm=None, lam_scaled=False):
+                  lam_act=False, qk_norm=None, lam_scaled=False, znorm=False):
     """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
     for the delta, additive and inner rules with phi identity or elu+1, scalar or
     per-channel lambda (reading D21: the pages give no backward pass).
@@ -307,6 +307,12 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     lambda_t |x_t|^2: lambda's gradient is the scaled ridge's times |x_t|^2, and the key
     gains 2 x_t (lambda_t . the scaled ridge's gradient).
 
+    With znorm (additive rule, as in scan(), reading D18) o_t = S_t^T q / (z_t . q + eps):
+    the read passes dO_t / den_t to S_t and -(dO_t . o_t) / den_t to den_t, hence q_t z_t
+    terms, a gradient G_z of z_t carried back like G (z_t = gamma_t z_{t-1} + beta_t k_t),
+    and the initial z (the state's carried-key slot) receives G_z as "xprev0". The final z
+    takes no gradient.
+
     With qk_norm ("l2" or "rms", identity phi, as in scan()) q, k and the carried key are
     raw and the recurrence sees them rescaled to a fixed length: the gradients with respect
     to the rescaled vectors are taken back through the rescaling (unit_rows_vjp).
@@ -321,7 +327,8 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
         g = scan_backward(unit_rows(q, length), unit_rows(k, length), v, beta, lam, dO, dS,
                           rule=rule, eps=eps, per_channel=per_channel, S0=S0,
                           xprev0=None if xprev0 is None else unit_rows(xprev0, length),
-                          has0=has0, beta_act=beta_act, lam_act=lam_act, lam_scaled=lam_scaled)
+                          has0=has0, beta_act=beta_act, lam_act=lam_act, lam_scaled=lam_scaled,
+                          znorm=znorm)
         g["q"] = unit_rows_vjp(q, g["q"], length)
         g["k"] = unit_rows_vjp(k, g["k"], length)
         if xprev0 is not None:
@@ -360,6 +367,8 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
         raise ValueError("the per-value-channel rule takes a scalar lambda")
     if lam_scaled and not shifted:
         raise ValueError("lam_scaled takes the delta or inner rule")
+    if znorm and rule != RULE_ADDITIVE:
+        raise ValueError("znorm takes the additive rule")
 
     g = {name: np.zeros_like(a) for name, a in (("q", Q), ("k", K), ("v", V))}
     g["beta"] = None if Bt is None else np.zeros_like(Bt)
@@ -370,6 +379,7 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     for n in range(N):
         # forward, keeping what each step's backward needs
         Sc, xp, hs = S_init[n].copy(), x_init[n].copy(), bool(h_init[n])
+        zc = x_init[n].copy()                   # znorm: z lives in the carried-key slot
         steps = []
         for t in range(T):
             qf, kf, vt = phi(Q[n, t], phi_kind), phi(K[n, t], phi_kind), V[n, t]
@@ -405,16 +415,29 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                 b = 1.0 if Bt is None else Bt[n, t]
                 decay = gam[:, None] if per_channel else gam
                 Sc = decay * Sp + b * np.outer(kf, vt)
-                steps.append((Sp, gam, b, kf))
+                zp = zc
+                if znorm:
+                    zc = gam * zp + b * kf               # gam: a scalar, or per channel
+                steps.append((Sp, gam, b, kf, zp, zc))
             steps[-1] = (steps[-1], Sc, qf)
             xp, hs = kf, True
 
-        # backward: G holds dL/dS_t while step t is undone
+        # backward: G holds dL/dS_t (and Gz dL/dz_t) while step t is undone
         G = dSh[n].copy()
+        Gz = np.zeros(dk)
         for t in range(T - 1, -1, -1):
             rec, St, qf = steps[t]
-            g["q"][n, t] += (St @ dOh[n, t]) * phi_grad(Q[n, t], phi_kind)
-            G = G + np.outer(qf, dOh[n, t])
+            if znorm:
+                zt = rec[5]
+                den = zt @ qf + eps
+                dnum = dOh[n, t] / den
+                dden = -(dOh[n, t] @ (St.T @ qf)) / (den * den)
+                g["q"][n, t] += (St @ dnum + zt * dden) * phi_grad(Q[n, t], phi_kind)
+                G = G + np.outer(qf, dnum)
+                Gz = Gz + qf * dden
+            else:
+                g["q"][n, t] += (St @ dOh[n, t]) * phi_grad(Q[n, t], phi_kind)
+                G = G + np.outer(qf, dOh[n, t])
             if shifted:
                 if rec is None:
                     continue                    # S_t = S_{t-1}
@@ -474,15 +497,20 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                     g["xprev0"][n] += dx
                 G = G_prev
             else:
-                Sp, gam, b, kf = rec
+                Sp, gam, b, kf, zp, _ = rec
                 if Lm is not None:
                     g["lam"][n, t] += np.sum(G * Sp, axis=1) if per_channel else np.sum(G * Sp)
+                    if znorm:
+                        g["lam"][n, t] += Gz * zp if per_channel else Gz @ zp
                 if Bt is not None:
-                    g["beta"][n, t] += kf @ G @ V[n, t]
-                g["k"][n, t] += b * (G @ V[n, t]) * phi_grad(K[n, t], phi_kind)
+                    g["beta"][n, t] += kf @ G @ V[n, t] + (Gz @ kf if znorm else 0.0)
+                g["k"][n, t] += b * (G @ V[n, t] + Gz) * phi_grad(K[n, t], phi_kind)
                 g["v"][n, t] += b * (G.T @ kf)
                 G = (gam[:, None] if per_channel else gam) * G
+                Gz = gam * Gz
         g["S0"][n] = G
+        if znorm:
+            g["xprev0"][n] = Gz
 
     if g["beta"] is not None:
         g["beta"] = g["beta"] * dBt

@@ -761,7 +761,10 @@ def pin_p24_backward(orc):
     (g) The per-value-channel rule: finite differences match every gradient (q, k, v, the
         per-channel beta, lambda, S0, the carried key), plain, with elu+1, and with the
         scale-coupled ridge and pre-activated gates; with every beta_j equal it is the
-        delta rule, and so are its gradients (beta's summed over j)."""
+        delta rule, and so are its gradients (beta's summed over j).
+    (h) Normalised linear attention (additive, znorm): finite differences match every
+        gradient (q, k, v, beta, gamma, S0 and the initial z), scalar and per-channel
+        retention, positive identity features and elu+1."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -941,6 +944,39 @@ def pin_p24_backward(orc):
     for name in ("q", "k", "v", "lam", "S0", "xprev0"):
         np.testing.assert_allclose(g_pv[name], g_d[name], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(g_pv["beta"].sum(axis=-1), g_d["beta"], rtol=1e-12, atol=1e-12)
+
+    for per_channel in (False, True):
+        for phi_kind in ("identity", "elu1"):
+            T, dk, dv = 4, 3, 2
+            q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
+            if phi_kind == "identity":
+                q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
+            v = rng.standard_normal((1, 1, T, dv))
+            b = rng.uniform(0.2, 1.5, (1, 1, T))
+            lam = rng.uniform(0.6, 1.0, (1, 1, T, dk) if per_channel else (1, 1, T))
+            dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
+            S0, z0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
+            kw = dict(rule=ADD, per_channel=per_channel, phi_kind=phi_kind, znorm=True)
+            args = {"q": q, "k": k, "v": v, "beta": b, "lam": lam, "S0": S0, "xprev0": z0}
+
+            def loss(a):
+                o, S, _, _ = orc.scan(a["q"], a["k"], a["v"], a["beta"], a["lam"], S0=a["S0"],
+                                      xprev0=a["xprev0"], **kw)
+                return float(np.sum(o * dO) + np.sum(S * dS))
+
+            gr = orc.scan_backward(q, k, v, b, lam, dO, dS, S0=S0, xprev0=z0, **kw)
+            for name, arr in args.items():
+                for idx in np.ndindex(arr.shape):
+                    a = dict(args)
+                    ap, am = arr.copy(), arr.copy()
+                    ap[idx] += 1e-6
+                    am[idx] -= 1e-6
+                    a[name] = ap
+                    fp = loss(a)
+                    a[name] = am
+                    fd = (fp - loss(a)) / 2e-6
+                    an = gr[name][idx]
+                    assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (per_channel, phi_kind, name, idx, fd, an)
 
 
 ALL_PINS = [

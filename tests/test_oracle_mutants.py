@@ -56,7 +56,7 @@ MUTANTS = {
     "bwd_same_index_key": ("g[\"k\"][n, t - 1] += dx * phi_grad(K[n, t - 1], phi_kind)",
                            "g[\"k\"][n, t] += dx * phi_grad(K[n, t], phi_kind)"),
     "bwd_lambda_hat_not_routed": ("                            dlt[imax] += dden\n", ""),
-    "bwd_read_after_undo": ("            G = G + np.outer(qf, dOh[n, t])\n", ""),
+    "bwd_read_after_undo": ("                G = G + np.outer(qf, dOh[n, t])\n", ""),
     "pv_shared_step": ("Bt[:, t, :] / np.where(has, den_pv, 1.0)[:, None]",
                        "Bt[:, t, :1] / np.where(has, den_pv, 1.0)[:, None] + 0.0 * Bt[:, t, :]"),
     "pv_decay_on_rows": ("(1.0 - eta_pv * lam_pv[:, None])[:, None, :] * S",
@@ -78,6 +78,7 @@ MUTANTS = {
     "bwd_scaled_ridge_key_term_dropped": ("dx = dx + 2.0 * x * (np.sum(dlt * lt) if per_channel else dlt * lt)",
                                           "dx = dx"),
     "bwd_pv_decay_on_rows": ("G_prev = G * a[None, :] - np.outer(x, dr)", "G_prev = G * a[:, None] - np.outer(x, dr)"),
+    "bwd_znorm_z_not_decayed": ("                Gz = gam * Gz\n", ""),
     "decay_after_write": ("S = decay[:, :, None] * S + eta[:, None, None] * x[:, :, None] * r[:, None, :]",
                           "S = decay[:, :, None] * (S + eta[:, None, None] * x[:, :, None] * r[:, None, :])"),
 }
