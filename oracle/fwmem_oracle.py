@@ -324,14 +324,16 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
         if phi_kind != "identity" or qk_norm not in ("l2", "rms"):
             raise ValueError("qk_norm takes the identity feature map and 'l2' or 'rms'")
         length = 1.0 if qk_norm == "l2" else float(np.sqrt(np.asarray(q).shape[-1]))
+        # with znorm the carried slot holds z, not a key: it is not rescaled
+        key0 = xprev0 is not None and not znorm
         g = scan_backward(unit_rows(q, length), unit_rows(k, length), v, beta, lam, dO, dS,
                           rule=rule, eps=eps, per_channel=per_channel, S0=S0,
-                          xprev0=None if xprev0 is None else unit_rows(xprev0, length),
+                          xprev0=unit_rows(xprev0, length) if key0 else xprev0,
                           has0=has0, beta_act=beta_act, lam_act=lam_act, lam_scaled=lam_scaled,
                           znorm=znorm)
         g["q"] = unit_rows_vjp(q, g["q"], length)
         g["k"] = unit_rows_vjp(k, g["k"], length)
-        if xprev0 is not None:
+        if key0:
             g["xprev0"] = unit_rows_vjp(xprev0, g["xprev0"], length)
         return g
     q = np.asarray(q, dtype=np.float64)

@@ -764,7 +764,8 @@ def pin_p24_backward(orc):
         delta rule, and so are its gradients (beta's summed over j).
     (h) Normalised linear attention (additive, znorm): finite differences match every
         gradient (q, k, v, beta, gamma, S0 and the initial z), scalar and per-channel
-        retention, positive identity features and elu+1."""
+        retention, positive identity features (raw or l2-normalised by the scan, which
+        leaves z itself unscaled) and elu+1."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -946,17 +947,19 @@ def pin_p24_backward(orc):
     np.testing.assert_allclose(g_pv["beta"].sum(axis=-1), g_d["beta"], rtol=1e-12, atol=1e-12)
 
     for per_channel in (False, True):
-        for phi_kind in ("identity", "elu1"):
+        for phi_kind in ("identity", "elu1", "identity_l2"):
             T, dk, dv = 4, 3, 2
             q, k = rng.standard_normal((1, 1, T, dk)), rng.standard_normal((1, 1, T, dk))
-            if phi_kind == "identity":
+            if phi_kind != "elu1":
                 q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
             v = rng.standard_normal((1, 1, T, dv))
             b = rng.uniform(0.2, 1.5, (1, 1, T))
             lam = rng.uniform(0.6, 1.0, (1, 1, T, dk) if per_channel else (1, 1, T))
             dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
             S0, z0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
-            kw = dict(rule=ADD, per_channel=per_channel, phi_kind=phi_kind, znorm=True)
+            kw = dict(rule=ADD, per_channel=per_channel, znorm=True,
+                      phi_kind="elu1" if phi_kind == "elu1" else "identity",
+                      qk_norm="l2" if phi_kind == "identity_l2" else None)
             args = {"q": q, "k": k, "v": v, "beta": b, "lam": lam, "S0": S0, "xprev0": z0}
 
             def loss(a):
