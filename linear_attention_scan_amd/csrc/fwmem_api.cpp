@@ -506,7 +506,7 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
   if (st != FWMEM_OK) return st;
   if ((mode->flags & ~(uint32_t)(FWMEM_PHI_ELU1 | FWMEM_LAMBDA_PER_CHANNEL | FWMEM_BETA_SIGMOID |
                                  FWMEM_BETA_SIGMOID2 | FWMEM_LAMBDA_PREACT | FWMEM_QK_L2NORM |
-                                 FWMEM_QK_RMSNORM | FWMEM_LAMBDA_SCALED)) != 0)
+                                 FWMEM_QK_RMSNORM | FWMEM_LAMBDA_SCALED | FWMEM_ZNORM)) != 0)
     return FWMEM_EUNSUPPORTED;
   if (!fwmem::bwd_supported(shape->dk, shape->dv)) return FWMEM_EUNSUPPORTED;
   return FWMEM_OK;
@@ -514,8 +514,9 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
 
 size_t bwd_ws_bytes(const fwmem_shape* shape, const fwmem_mode* mode) {
   const size_t BH = (size_t)shape->B * (size_t)shape->H;
-  const bool small = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || mode->rule == FWMEM_RULE_DELTA_PV;
-  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, small));
+  const bool zn = (mode->flags & FWMEM_ZNORM) != 0;
+  const bool small = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || mode->rule == FWMEM_RULE_DELTA_PV || zn;
+  return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, small, zn));
 }
 
 }  // namespace
@@ -604,7 +605,7 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.T = (int)T;
   p.dk = shape->dk;
   p.dv = shape->dv;
-  const int ck = fwmem::bwd_chunk((mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || rule_pv);
+  const int ck = fwmem::bwd_chunk((mode->flags & (FWMEM_LAMBDA_PER_CHANNEL | FWMEM_ZNORM)) != 0 || rule_pv);
   p.nchunks = (int)((T + ck - 1) / ck);
   p.rule = mode->rule;
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;

@@ -38,16 +38,17 @@ struct BwdParams {
 };
 
 // Tokens the backward stages at a time and between the states it keeps: 64, or 32 with a
-// per-channel lambda or a per-value-channel beta (whose staged values would not fit LDS
-// with 64).
+// per-channel lambda, a per-value-channel beta or the normaliser (whose staged values
+// would not fit LDS with 64).
 __host__ __device__ constexpr int bwd_chunk(bool small) { return small ? 32 : 64; }
 // Workspace floats per head: the state at each chunk start, the states after each of a
 // chunk's tokens, and a chunk's worth of d_v-vectors.
-__host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv, bool small) {
+// With the normaliser (znorm), also its value at each chunk start.
+__host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv, bool small, bool znorm) {
   const size_t ck = (size_t)bwd_chunk(small);
   const size_t nchunks = ((size_t)T + ck - 1) / ck;
   const size_t SS = (size_t)dk * (size_t)dv;
-  return T > 0 ? (nchunks + ck) * SS + ck * (size_t)dv : 0;
+  return T > 0 ? (nchunks + ck) * SS + ck * (size_t)dv + (znorm ? nchunks * (size_t)dk : 0) : 0;
 }
 bool bwd_supported(int dk, int dv);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);

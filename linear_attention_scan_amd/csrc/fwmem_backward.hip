@@ -64,13 +64,14 @@ struct Sc {
   bool key;
 };
 
-template <typename InT, int DK, int DV, int RULE, bool PCX>
+template <typename InT, int DK, int DV, int RULE, bool PCX, bool ZN>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using R = Rule<RULE>;
   constexpr bool PV = RULE == kRuleDeltaPV;  // one step size per value column
   // tokens staged at a time, and between stored states (a per-channel lambda or a
   // per-column beta, also staged, halves it to fit LDS)
-  constexpr int CK = bwd_chunk(PCX || PV);
+  constexpr int CK = bwd_chunk(PCX || PV || ZN);
+  static_assert(!ZN || (RULE == kRuleAdditive && !PCX), "the normaliser: additive rule, scalar decay");
   constexpr int TPRd = DV / 4;   // threads per row
   constexpr int RG = NT / TPRd;  // row groups
   constexpr int RPT = DK / RG;   // rows per thread
@@ -89,6 +90,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float s_bc[PV ? CK : 1][PV ? DV : 4];  // per-column beta
   __shared__ float s_n[CK], s_bt[CK], s_lm[CK];  // |x|^2, beta, lambda (per channel: its maximum)
   __shared__ int s_im[CK];                        // per channel: the first channel at the maximum
+  // the normaliser: z after each of the chunk's tokens, before its first, and z_t . q_t + eps
+  __shared__ float s_z[ZN ? CK : 1][ZN ? DK : 1], s_z0[ZN ? DK : 1], s_den[ZN ? CK : 1];
 
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cq = tid % TPRd, rg = tid / TPRd;
@@ -102,8 +105,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
   const size_t SS = (size_t)DK * DV;
   const int nch = (T + CK - 1) / CK;
-  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV, PCX || PV);
+  float* ckpt = p.ws + (size_t)bh * bwd_floats_per_head(T, DK, DV, PCX || PV || ZN, ZN);
   float* cs = ckpt + (size_t)nch * SS;  // [CK] states after each token of a chunk
+  float* zck = cs + (size_t)CK * SS + (size_t)CK * DV;  // ZN: [nch][DK] z at each chunk start
 
   auto phi = [&](float x) { return elu ? phi_elu1(x) : x; };
   // phi'(z) from y = phi(z): 1 for the identity; for elu+1, 1 where z > 0 (y > 1) and
@@ -309,20 +313,40 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int j = 0; j < RPT; ++j) S[j] = S[j] * arow(s, u, j) + w * (s.eta * s_x[u][row(j)]);
   };
 
-  // ---- forward: the state at every chunk start
+  // the normaliser on the thread's rows (ZN): z_t = gamma_t z_{t-1} + beta_t phi(k_t)
+  float zr[RPT];
+  auto zstep = [&](int u) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) zr[j] = s_lm[u] * zr[j] + s_bt[u] * s_x[u][row(j)];
+  };
+
+  // ---- forward: the state (and z) at every chunk start
   f4 S[RPT];
   load_state(p.S_in != nullptr ? p.S_in + (size_t)bh * SS : nullptr, S);
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) zr[j] = (ZN && p.xprev_in != nullptr) ? p.xprev_in[(size_t)bh * DK + row(j)] : 0.f;
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * CK, t1 = min(T, t0 + CK);
     store_state(ckpt + (size_t)c * SS, S);
+    if constexpr (ZN)
+      if (cq == 0)
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) zck[(size_t)c * DK + row(j)] = zr[j];
     stage(t0, t1, false);
-    for (int t = t0; t < t1; ++t) fwd_tok(t, t - t0, S);
+    for (int t = t0; t < t1; ++t) {
+      fwd_tok(t, t - t0, S);
+      if constexpr (ZN) zstep(t - t0);
+    }
     __syncthreads();  // LDS is restaged for the next chunk
   }
 
   // ---- backward
   f4 G[RPT];
   load_state(p.dS_out != nullptr ? p.dS_out + (size_t)bh * SS : nullptr, G);
+  float Gz[RPT];         // ZN: dL/dz_t on the thread's rows
+  float dden_pend = 0.f;  // ZN: the normaliser's gradient of the token whose read was last undone
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) Gz[j] = 0.f;
   if (R::shift && T >= 1)  // the last key is written by no step of this call
     for (int i = tid; i < DK; i += NT) p.gk[(rb + T - 1) * DK + i] = 0.f;
   for (int c = nch - 1; c >= 0; --c) {
@@ -331,16 +355,57 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     // recompute the chunk's states after each token (the last one stays in S)
     stage(t0, t1, true);
     load_state(start, S);
+    if constexpr (ZN) {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        zr[j] = zck[(size_t)c * DK + row(j)];
+        if (cq == 0) s_z0[row(j)] = zr[j];
+      }
+    }
     for (int t = t0; t < t1; ++t) {
       fwd_tok(t, t - t0, S);
       if (t + 1 < t1) store_state(cs + (size_t)(t - t0) * SS, S);
+      if constexpr (ZN) {
+        zstep(t - t0);
+        if (cq == 0)
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) s_z[t - t0][row(j)] = zr[j];
+      }
     }
-    __syncthreads();  // the residuals in s_w are read by every thread below
+    __syncthreads();  // the residuals in s_w (and z in s_z) are read by every thread below
+    if constexpr (ZN) {
+      for (int u = wave; u < t1 - t0; u += NWV) {
+        float d = 0.f;
+        for (int i = lane; i < DK; i += 64) d += s_z[u][i] * s_q[u][i];
+        d = wave_sum(d);
+        if (lane == 0) s_den[u] = d + p.eps;
+      }
+      __syncthreads();
+    }
     // the read's gradient dphi(q_t) = S_t dO_t, from the state after token t: for the
     // chunk's last token from S, for the others while token t + 1 is undone (its Sp)
     auto read_grad = [&](int t, const f4 (&St)[RPT]) {
       const int u = t - t0;
       const f4 dO = *reinterpret_cast<const f4*>(&s_do[u][4 * cq]);
+      if constexpr (ZN) {
+        // o = num / den with num = S_t^T q, den = z_t . q + eps: dnum = dO / den and
+        // dden = -(dO . num) / den^2, so dq = S_t dnum + z_t dden
+        f4 nq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) nq += St[j] * s_q[u][row(j)];
+        float d0, d1;
+        const f4 num = reduce(nq, 0.f, 0.f, d0, d1);
+        const float rd = 1.f / s_den[u];
+        const f4 m0 = dO * num;
+        dden_pend = -rowsum(m0[0] + m0[1] + m0[2] + m0[3]) * rd * rd;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+          const f4 m = St[j] * dO;
+          const float dqi = rowsum(m[0] + m[1] + m[2] + m[3]) * rd + s_z[u][row(j)] * dden_pend;
+          if (cq == 0) p.gq[(rb + t) * DK + row(j)] = dqi * dphi_of(s_q[u][row(j)]);
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         const f4 m = St[j] * dO;
@@ -354,6 +419,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     load_state(len >= 2 ? cs + (size_t)(len - 2) * SS : start, Sp);
     for (int t = t1 - 1; t >= t0; --t) {
       const int u = t - t0;
+      const float dden_t = dden_pend;  // ZN: set when token t's read was undone
       if (u >= 1) read_grad(t - 1, Sp);
       const f4 dO = *reinterpret_cast<const f4*>(&s_do[u][4 * cq]);
       f4 nx[RPT];
@@ -361,8 +427,17 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       else
 #pragma unroll
         for (int j = 0; j < RPT; ++j) nx[j] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (ZN) {  // the read: G += phi(q) (dO / den)^T, G_z += phi(q) dden
+        const f4 dn = dO * (1.f / s_den[u]);
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) G[j] += dO * s_q[u][row(j)];  // the read: G += phi(q) dO^T
+        for (int j = 0; j < RPT; ++j) {
+          G[j] += dn * s_q[u][row(j)];
+          Gz[j] += s_q[u][row(j)] * dden_t;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) G[j] += dO * s_q[u][row(j)];  // the read: G += phi(q) dO^T
+      }
       const Sc s = scal(t, u);
       if (!s.key) {  // no write: S_t = S_{t-1}; nothing else depends on this step
         if (rg == 0) *reinterpret_cast<f4*>(p.gv + (rb + t) * DV + 4 * cq) = f4{0.f, 0.f, 0.f, 0.f};
@@ -442,6 +517,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           }
           if (cq == 0) xgw_p += x * gw[j];
           gx += G[j] * x;
+          if constexpr (ZN)  // z_t = gamma z_{t-1} + beta x: G_z joins da and x^T G w
+            if (cq == 0) {
+              da_p += Gz[j] * (u >= 1 ? s_z[u - 1][row(j)] : s_z0[row(j)]);
+              xgw_p += Gz[j] * x;
+            }
         }
         float da, xgw;  // per channel (ridge rules): da holds sum_i lambda_i da_i
         const f4 gtx = reduce(gx, da_p, xgw_p, da, xgw);
@@ -490,10 +570,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
           for (int j = 0; j < RPT; ++j) {
             if (cq == 0) {
-              p.gk[(rb + t) * DK + row(j)] = s.b * gw[j] * dphi_of(s_x[u][row(j)]);
+              p.gk[(rb + t) * DK + row(j)] = s.b * (gw[j] + (ZN ? Gz[j] : 0.f)) * dphi_of(s_x[u][row(j)]);
               if (PCX && p.glam != nullptr) p.glam[(rb + t) * DK + row(j)] = dar[j] * dlam_dz(s_lc[u][row(j)]);
             }
             G[j] = G[j] * arow(s, u, j);
+            if constexpr (ZN) Gz[j] *= s.a;
           }
         }
       }
@@ -504,8 +585,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   }
   if (p.gS0 != nullptr) store_state(p.gS0 + (size_t)bh * SS, G);
   if (p.gh0 != nullptr && tid == 0) p.gh0[bh] = 0;
-  if (p.gx0 != nullptr && (!R::shift || T == 0))
+  if constexpr (ZN) {  // the initial normaliser's gradient (the carried-key slot holds z)
+    if (p.gx0 != nullptr && cq == 0)
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) p.gx0[(size_t)bh * DK + row(j)] = Gz[j];
+  } else if (p.gx0 != nullptr && (!R::shift || T == 0)) {
     for (int i = tid; i < DK; i += NT) p.gx0[(size_t)bh * DK + i] = 0.f;
+  }
 }
 
 // QK normalisation: the main kernel's q, k and carried-key gradients are with respect to
@@ -518,7 +604,8 @@ __global__ __launch_bounds__(256) void qk_norm_bwd_kernel(BwdParams p, float len
   const int lane = threadIdx.x & 63;
   const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const size_t nrow = (size_t)p.BH * (size_t)p.T;
-  const size_t nkey = (p.gx0 != nullptr && p.xprev_in != nullptr) ? (size_t)p.BH : 0;
+  // the carried-key slot holds z with the normaliser: no key rows then
+  const size_t nkey = (p.gx0 != nullptr && p.xprev_in != nullptr && !(p.flags & kFlagZnorm)) ? (size_t)p.BH : 0;
   if (r >= 2 * nrow + nkey) return;
   float x[E], g[E];
   float* gp;
@@ -550,11 +637,13 @@ __global__ __launch_bounds__(256) void qk_norm_bwd_kernel(BwdParams p, float len
 template <typename InT, int DK, int DV, bool PCX>
 hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.BH), block(NT);
-  if (p.rule == kRuleDelta) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDelta, PCX>), grid, block, 0, st, p);
+  if (p.rule == kRuleDelta) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDelta, PCX, false>), grid, block, 0, st, p);
   else if (!PCX && p.rule == kRuleDeltaPV)
-    hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDeltaPV, false>), grid, block, 0, st, p);
-  else if (p.rule == kRuleInner) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleInner, PCX>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive, PCX>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleDeltaPV, false, false>), grid, block, 0, st, p);
+  else if (p.rule == kRuleInner) hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleInner, PCX, false>), grid, block, 0, st, p);
+  else if (!PCX && (p.flags & kFlagZnorm))
+    hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive, false, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((bwd_kernel<InT, DK, DV, kRuleAdditive, PCX, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -564,7 +653,8 @@ hipError_t launch_t(const BwdParams& p, hipStream_t st) {
       (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
   const float len = qk_length(p.flags, DK);
   if (e != hipSuccess || len <= 0.f) return e;
-  const size_t rows = 2 * (size_t)p.BH * (size_t)p.T + ((p.gx0 != nullptr && p.xprev_in != nullptr) ? p.BH : 0);
+  const size_t rows = 2 * (size_t)p.BH * (size_t)p.T +
+                      ((p.gx0 != nullptr && p.xprev_in != nullptr && !(p.flags & kFlagZnorm)) ? p.BH : 0);
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((qk_norm_bwd_kernel<InT, DK>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, p, len);
   return hipGetLastError();

@@ -187,7 +187,8 @@ def _bwd(shp=None, md=None, q=M, k=2 * M, v=3 * M, beta=4 * M, lam=None, S_in=No
     (dict(md=F.mode(flags=F.LAMBDA_SCALED | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
     (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.LAMBDA_SCALED)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=F.QK_L2NORM | F.PHI_ELU1)), F.EUNSUPPORTED),
-    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.LAMBDA_PER_CHANNEL)), F.EUNSUPPORTED),
+    (dict(md=F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM | F.OUT_BF16)), F.EUNSUPPORTED),
     (dict(md=F.mode(flags=1 << 12)), F.EINVAL),
     (dict(md=F.mode(rule=7)), F.EINVAL),
     (dict(beta=None), F.EINVAL),

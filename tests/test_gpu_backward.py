@@ -344,3 +344,38 @@ def test_backward_per_value_channel(dtype, dk, dv, T, extra):
                             S0=w.S0, xprev0=x0, has0=h0, qk_norm="rms" if opts else None,
                             lam_scaled=opts, beta_act="sigmoid2" if opts else None, lam_act=opts)
     _compare(g, ref)
+
+
+@pytest.mark.parametrize("phi,dtype,dk,dv,T,extra", [
+    ("identity", "bf16", 128, 128, 130, None),
+    ("elu1", "f32", 64, 128, 70, None),
+    ("identity", "bf16", 128, 64, 97, "qk_gates"),
+    ("elu1", "bf16", 64, 64, 33, None),
+])
+def test_backward_normaliser(phi, dtype, dk, dv, T, extra):
+    """Normalised linear attention (FWMEM_ZNORM, additive rule): o = S^T q / (z.q + eps).
+    Every gradient, the initial z's (the carried-key slot) included, against the oracle's
+    scan_backward, from a nonzero S0 and z0; positive features keep z.q away from zero."""
+    r = wl.RULE_ADDITIVE
+    both = extra == "qk_gates"
+    say(f"[bwd znorm] {phi} {dtype} dk={dk} dv={dv} T={T} extra={extra}")
+    w = wl.make_scan(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, rule=r, beta_kind="sigmoid",
+                     lam_kind="gamma", phi=wl.PHI_ELU1 if phi == "elu1" else wl.PHI_IDENTITY,
+                     normalise_qk=phi != "elu1" and not both, qk_positive=phi != "elu1",
+                     qk_norm="l2" if both else None, znorm=True, s0_std=0.05, seed=T + dk)
+    rng = np.random.default_rng(T + 5)
+    dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    flags = (F.ZNORM | (F.PHI_ELU1 if phi == "elu1" else 0)
+             | ((F.QK_L2NORM | F.BETA_SIGMOID | F.LAMBDA_PREACT) if both else 0))
+    beta = w.beta_pre if both else w.beta
+    lam = w.lam_pre if both else w.lam
+    g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
+                   f32_tensor(beta), f32_tensor(lam), f32_tensor(dO), rule=r, flags=flags, eps=w.eps,
+                   S_in=make_state(w.B, w.H, dk, dv, S=w.S0, xprev=w.xprev0),
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
+    ref = orc.scan_backward(w.q, w.k, w.v, beta, lam, dO, dS, rule=r, phi_kind=phi, eps=w.eps,
+                            S0=w.S0, xprev0=w.xprev0, znorm=True, qk_norm="l2" if both else None,
+                            beta_act="sigmoid" if both else None, lam_act=both)
+    assert np.any(ref["xprev0"] != 0)
+    _compare(g, ref)
