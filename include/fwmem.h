@@ -234,10 +234,11 @@ fwmem_status fwmem_step(const fwmem_shape* shape, const void* q, const void* k, 
                         const void* S_in, void* out, void* S_out, fwmem_stream stream);
 
 /* Bytes of device workspace fwmem_scan_bwd needs for this shape and mode (0 when T == 0
- * or B*H == 0): with C = 64 (32 with FWMEM_LAMBDA_PER_CHANNEL or FWMEM_RULE_DELTA_PV), per
- * head the state at
+ * or B*H == 0): with C = 64 (32 with FWMEM_LAMBDA_PER_CHANNEL, FWMEM_RULE_DELTA_PV or
+ * FWMEM_ZNORM), per head the state at
  * each C-token chunk start plus C more state buffers and C d_v-vectors of scratch, i.e.
- * 4 * ((ceil(T/C) + C) * dk * dv + C * dv) bytes, rounded up to a multiple of 256.
+ * 4 * ((ceil(T/C) + C) * dk * dv + C * dv) bytes, plus 4 * ceil(T/C) * dk with
+ * FWMEM_ZNORM (the normaliser at each chunk start), rounded up to a multiple of 256.
  * Its contents need no initialisation and are scratch only. */
 fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
                                             size_t* bytes);
@@ -254,7 +255,8 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  * (beta and grad_beta [B][H][T][dv], grad_beta 16-byte aligned); flags from
  * FWMEM_PHI_ELU1, FWMEM_LAMBDA_PER_CHANNEL, FWMEM_BETA_SIGMOID, FWMEM_BETA_SIGMOID2,
  * FWMEM_LAMBDA_PREACT, FWMEM_QK_L2NORM, FWMEM_QK_RMSNORM and FWMEM_LAMBDA_SCALED (with a
- * scalar lambda, as for scans). Anything else, FWMEM_ZNORM included, returns
+ * scalar lambda, as for scans) and FWMEM_ZNORM (additive, scalar decay; the initial
+ * normaliser's gradient goes to grad_S_in's x_prev part). Anything else returns
  * FWMEM_EUNSUPPORTED. dk and dv in {64, 128}. With a per-channel lambda, the
  * denominator's gradient goes to the first channel holding the largest lambda_i. With
  * pre-activated gates, grad_beta and grad_lambda are with respect to the pre-activations

@@ -221,6 +221,11 @@ def test_bwd_workspace_size_and_empty_batch():
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(mdv), ctypes.byref(n)) == F.OK
     want = 4 * 6 * ((4 + 32) * 128 * 64 + 32 * 64)
     assert n.value == (want + 255) // 256 * 256
+    # the normaliser: 32-token chunks and its value at each chunk start
+    mdz = F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM)
+    assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(mdz), ctypes.byref(n)) == F.OK
+    want = 4 * 6 * ((4 + 32) * 128 * 64 + 32 * 64 + 4 * 128)
+    assert n.value == (want + 255) // 256 * 256
     shp0 = F.shape(2, 3, 0, 128, 64, F.F32)
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp0), ctypes.byref(md), ctypes.byref(n)) == F.OK
     assert n.value == 0
