@@ -73,12 +73,12 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "bwd_kernel"): {
         "sources": ("fwmem_backward.hip", "fwmem_backward.h", "fwmem_device.h", "fwmem_internal.h"),
         "sha256": {
-            "fwmem_backward.hip": "0ff49c7304e71e8bc700213ffbab18da1255d2959bc52574c582437bf89df7e8",
-            "fwmem_backward.h": "b7c82954d2b76f09f42bac1af327de1fc16ff1f2bd921f42e2527f4b992a4bc1",
+            "fwmem_backward.hip": "fd34818f82f71db48853bb977d773b4eaee98e057f37ae9ecb69527bf37f7c99",
+            "fwmem_backward.h": "c209129737af1e679f0105b55a50b7dcada68045815cabec88ea0b1b4371a665",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
         },
-        "fetch_kib": 8858542.4, "write_kib": 17180706.2, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 8834051.8, "write_kib": 17180908.5, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 

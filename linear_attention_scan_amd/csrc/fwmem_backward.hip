@@ -24,12 +24,14 @@
 // are per row. Pre-activated gates are activated as they are staged and their gradients
 // taken through the activation. The scale-coupled ridge is lambda |x|^2 (scalar lambda).
 // With QK normalisation, q, k and the carried key are rescaled to a fixed length as they
-// are staged, and a second kernel takes their gradients back through the rescaling.
+// are staged, and a second kernel takes their gradients back through the rescaling. With
+// the normaliser (additive rule), o_t = S_t^T q_t / (z_t . q_t + eps): a gradient of z is
+// carried back beside G, and the chunk's z values are recomputed into LDS.
 //
 // One persistent 1024-thread workgroup per head, token-serial (the chunked backward is
 // future work). The state is distributed as in the decode kernel: thread (rg, cq) holds
 // float4 column group cq of rows rg, rg + RG, ... A chunk here is 64 tokens, 32 with a
-// per-channel lambda. A forward pass stores the state at every chunk start in the
+// per-channel lambda, a per-column beta or the normaliser. A forward pass stores the state at every chunk start in the
 // workspace; then, per chunk from the last, the chunk's states after each token are
 // recomputed into the workspace and the chunk's tokens are undone from the last. Each
 // chunk's keys, queries, values, dO and gates are staged in LDS once; a token's column and
