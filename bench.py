@@ -123,12 +123,40 @@ def compute_dtype(w):
 
 
 def scan_bytes_per_token_head(w, out_bytes=4):
-    """Algorithmic HBM bytes of the scan per (token, head): q, k, v read once, beta and
-    lambda read once, out written once (the state adds d_k*d_v*8 per head per call)."""
+    """HBM bytes of the scan per (token, head) with o written as float32 (the library's
+    default output): q, k, v read once, beta and lambda read once, out written once (the
+    state adds d_k*d_v*8 per head per call)."""
     es = 2 if w.dtype == "bf16" else 4
     lam = 0 if w.lam is None else 4 * (w.dk if w.per_channel else 1)
     beta = 0 if w.beta is None else 4 * (w.dv if w.rule == 3 else 1)
     return (2 * w.dk + w.dv) * es + beta + lam + w.dv * out_bytes
+
+
+def algorithmic_bytes_per_token_head(w):
+    """Algorithmic HBM bytes per (token, head) as the hot-path scope table counts them:
+    q, k, v read once and o written once, all in the input type (3d*s + d*s), plus the
+    float32 gates (4 for a scalar gate, 4*d_k for a per-channel lambda, 4*d_v for a
+    per-value-channel beta). At d = 128 with bf16 inputs and both gates: 1032 B."""
+    es = 2 if w.dtype == "bf16" else 4
+    return scan_bytes_per_token_head(w, out_bytes=es)
+
+
+def algorithmic_flops_per_token_head(w, C=64):
+    """Flops per (token, head) of the chunked form, counting only the triangular halves of
+    the in-chunk products: 3 C d_k + 2 C d_v + 6 d_k d_v with the delta rule's solve, and
+    C (d_k + d_v) + 4 d_k d_v without one (additive and inner-product rules)."""
+    if w.rule in (0, 3):
+        return 3 * C * w.dk + 2 * C * w.dv + 6 * w.dk * w.dv
+    return C * (w.dk + w.dv) + 4 * w.dk * w.dv
+
+
+def executed_flops_per_token_head(w, C=64):
+    """MFMA flops per (token, head) that the chunked form executes at chunk length C (whole
+    16x16 tiles): 6 C d_k + 4 C d_v + 6 d_k d_v + C^2/3 with the solve, 2 C (d_k + d_v) +
+    4 d_k d_v without. Used for the arithmetic intensity of the attainable roofline."""
+    if w.rule in (0, 3):
+        return 6 * C * w.dk + 4 * C * w.dv + 6 * w.dk * w.dv + C * C / 3
+    return 2 * C * (w.dk + w.dv) + 4 * w.dk * w.dv
 
 
 def kernel_bytes(w, which):
@@ -188,8 +216,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--no-copy-calibration", action="store_true",
+                    help="skip the plain 1 GiB device copy (the measured-bandwidth reference, "
+                         "also the HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -285,18 +314,45 @@ def main():
         kk["mfma_TFLOPs"] = kk["mfma_flops"] / (kk["ms"] * 1e-3) / 1e12
     dom = max(kern, key=lambda n: kern[n]["ms"])
     names = kernel_names(w)
+    copy_gbs = None if args.no_copy_calibration else copy_bandwidth(dev, stream)
+
+    # roofline of the dominant kernel on the algorithmic bytes of the whole scan (q, k, v,
+    # o in the input type, the gates), over that kernel's average launch duration
+    units = w.B * w.H * w.T
+    algo_b = algorithmic_bytes_per_token_head(w) * units
+    algo_f = algorithmic_flops_per_token_head(w) * units
+    exec_f = executed_flops_per_token_head(w) * units
+    dom_s = kern[dom]["ms"] * 1e-3
+    step_s = ms_step * 1e-3
+    achieved = algo_b / dom_s / 1e9
+    # attainable roofline: the longer of the HBM time of the algorithmic bytes and the
+    # MFMA time of the executed flops, against the measured time
+    t_attain = max(algo_b / (HBM_PEAK_GBS * 1e9), exec_f / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    # the same kernel on the bytes it really moves with the library's float32 output and
+    # the state read and written once
+    b32 = kern[dom]["bytes"]
     roofline = {
         "bound": "hbm",
         "kernel": names[dom],
-        "achieved": round(kern[dom]["GBs"], 2),
+        "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(kern[dom]["GBs"] / HBM_PEAK_GBS, 4),
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(w.name, names[dom]),
-        "algorithmic_bytes": kern[dom]["bytes"],
+        "algorithmic_bytes": algo_b,
+        "bytes_per_token_head": algorithmic_bytes_per_token_head(w),
         "launch_ms": round(kern[dom]["ms"], 5),
-        "mfma_TFLOPs": round(kern[dom]["mfma_TFLOPs"], 2),
-        "mfma_frac": round(kern[dom]["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "whole_step_frac": round(algo_b / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "copy_GBs": copy_gbs,
+        "frac_of_copy": None if copy_gbs is None else round(achieved / copy_gbs, 4),
+        "attainable_frac": round(t_attain / dom_s, 4),
+        "attainable_frac_whole_step": round(t_attain / step_s, 4),
+        "algorithmic_flops": algo_f,
+        "mfma_TFLOPs": round(algo_f / dom_s / 1e12, 2),
+        "mfma_frac": round(algo_f / dom_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "mfma_frac_whole_step": round(algo_f / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "fp32_out": {"bytes": b32, "achieved": round(b32 / dom_s / 1e9, 2),
+                     "frac": round(b32 / dom_s / 1e9 / HBM_PEAK_GBS, 4)},
     }
     whole_bytes = w.B * w.H * w.T * scan_bytes_per_token_head(w) + 2 * w.B * w.H * w.dk * w.dv * 4
 
@@ -330,32 +386,39 @@ def main():
     if not args.no_backward and backward_supported(w):
         result["backward"] = bench_backward(w, args.backward_steps, dev, stream, q, k, v, beta, lam)
 
-    if args.copy_calibration:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            b.copy_(a)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["copy_calibration"] = {"bytes_per_copy": 2 * n,
-                                      "GBs": round(2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
-
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(result), flush=True)
 
 
+def copy_bandwidth(dev, stream):
+    """GB/s of a plain 1 GiB device-to-device copy (bytes read plus bytes written), five
+    copies between two HIP events after three untimed ones. Its kernel is also the
+    calibration of the HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return round(gbs, 1)
+
+
 def backward_supported(w):
-    from linear_attention_scan_amd import workloads as wl
-    return (w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE) and not w.znorm
-            and not (w.lam_scaled and w.per_channel) and w.dk in (64, 128) and w.dv in (64, 128))
+    """Whether fwmem_scan_bwd takes the workload's mode: every rule, with the scale-coupled
+    ridge only for a scalar lambda and the normaliser only for a scalar decay."""
+    return (not (w.lam_scaled and w.per_channel) and not (w.znorm and w.per_channel)
+            and w.dk in (64, 128) and w.dv in (64, 128))
 
 
 def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
@@ -374,13 +437,15 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
         flags |= {"l2": F.QK_L2NORM, "rms": F.QK_RMSNORM}[w.qk_norm]
     if w.lam_scaled:
         flags |= F.LAMBDA_SCALED
+    if w.znorm:
+        flags |= F.ZNORM
     md = F.mode(w.rule, flags, w.eps, 0)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
     gout = torch.randn((w.B, w.H, w.T, w.dv), generator=gen, device=dev)
     gq = torch.empty((w.B, w.H, w.T, w.dk), device=dev)
     gk, gv = torch.empty_like(gq), torch.empty((w.B, w.H, w.T, w.dv), device=dev)
-    gb = None if beta is None else torch.empty((w.B, w.H, w.T), device=dev)
+    gb = None if beta is None else torch.empty(tuple(beta.shape), device=dev)
     gl = None if lam is None else torch.empty(tuple(lam.shape), device=dev)
     gS = F.State(w.B, w.H, w.dk, w.dv, device=dev)
     ws_n = F.bwd_workspace_bytes(shp, md)
@@ -403,7 +468,8 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     assert bool(torch.isfinite(gk).all()), "non-finite gradient"
     ms = evs[0].elapsed_time(evs[1]) / steps
     es = 2 if w.dtype == "bf16" else 4
-    ngates = (beta is not None) + (lam is not None) * (w.dk if w.per_channel else 1)
+    ngates = ((beta is not None) * (w.dv if w.rule == 3 else 1)
+              + (lam is not None) * (w.dk if w.per_channel else 1))
     per_tok = (2 * w.dk + w.dv) * es + 4 * ngates + 4 * w.dv + 4 * (2 * w.dk + w.dv) + 4 * ngates
     nbytes = w.B * w.H * (w.T * per_tok + w.dk * w.dv * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -477,9 +543,12 @@ def cpu_baseline(w, min_s=10.0):
 
     def run(b):
         sl = (slice(b, b + 1), slice(None), slice(None))
+        # the same computation as the GPU run: the activated gates the library is handed,
+        # and every option the workload sets
         orc.scan(w.q[sl], w.k[sl], w.v[sl], None if w.beta is None else w.beta[sl],
                  None if w.lam is None else w.lam[sl], rule=w.rule, phi_kind=w.phi, eps=w.eps,
-                 per_channel=w.per_channel, qk_norm=w.qk_norm)
+                 per_channel=w.per_channel, qk_norm=w.qk_norm, znorm=w.znorm,
+                 lam_scaled=w.lam_scaled)
 
     n = 0
     with threadpool_limits(limits=1):
