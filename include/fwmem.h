@@ -79,7 +79,9 @@ typedef enum {
                               scan's per-value-channel beta 16-byte) */
   FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
   FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
-  FWMEM_EWORKSPACE = -6    /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
+  FWMEM_EWORKSPACE = -6,   /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
+  FWMEM_EWAIT = -7         /* fwmem_check_device: a bounded wait inside a kernel gave up since
+                              the last check; the outputs of the calls in between are wrong */
 } fwmem_status;
 
 /* DELTA_PV: the delta rule with one step size per value channel (Falcon-2, "Fast Weight
@@ -292,10 +294,26 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
                             void* grad_S_in, void* workspace, size_t ws_bytes,
                             fwmem_stream stream);
 
+/*
+ * Device-side failure report. The split propagate kernel (bf16 inputs, identity feature
+ * map, scalar decay) hands data between its waves through LDS flags, and every such wait
+ * is bounded (2^22 polls, far beyond any correct run). A wait that reaches the bound lets
+ * the kernel finish, with wrong values for that chunk, and sets a sticky status word of
+ * the GPU. This call synchronises `stream` (the only entry point that does), reads the
+ * current GPU's word and clears it: FWMEM_OK (no wait gave up since the last check),
+ * FWMEM_EWAIT, or FWMEM_ELAUNCH (the word could not be read). No passage of the pages
+ * defines this; it guards the kernels' own synchronisation.
+ *
+ * Test hook: with the environment variable FWMEM_TEST_WAIT_TIMEOUT=n (0 < n < 2^22) set
+ * when a scan is called, its waits give up after n polls (they wait for a value no wave
+ * writes), so that the report can be checked without a real failure.
+ */
+fwmem_status fwmem_check_device(fwmem_stream stream);
+
 /* A static, human-readable name for a status code. */
 const char* fwmem_strerror(fwmem_status status);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, e.g. "0.2.0". */
 const char* fwmem_version(void);
 
 #ifdef __cplusplus

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "fwmem_backward.h"
@@ -153,9 +154,31 @@ size_t esize(int dtype) { return dtype == FWMEM_BF16 ? 2 : 4; }
 
 }  // namespace
 
+namespace fwmem {
+void wait_config(int* polls, int* bias) {
+  *polls = 1 << 22;
+  *bias = 0;
+  const char* e = std::getenv("FWMEM_TEST_WAIT_TIMEOUT");
+  if (e != nullptr) {
+    const long n = std::strtol(e, nullptr, 10);
+    if (n > 0 && n < (1 << 22)) {
+      *polls = (int)n;
+      *bias = 1 << 30;
+    }
+  }
+}
+}  // namespace fwmem
+
 extern "C" {
 
-const char* fwmem_version(void) { return "0.1.0"; }
+const char* fwmem_version(void) { return "0.2.0"; }
+
+fwmem_status fwmem_check_device(fwmem_stream stream) {
+  int v = 0;
+  if (fwmem::read_wait_status(reinterpret_cast<hipStream_t>(stream), &v) != hipSuccess)
+    return FWMEM_ELAUNCH;
+  return v != 0 ? FWMEM_EWAIT : FWMEM_OK;
+}
 
 const char* fwmem_strerror(fwmem_status st) {
   switch (st) {
@@ -166,6 +189,7 @@ const char* fwmem_strerror(fwmem_status st) {
     case FWMEM_EOVERLAP: return "overlapping buffers";
     case FWMEM_ELAUNCH: return "kernel launch failed";
     case FWMEM_EWORKSPACE: return "workspace missing or too small";
+    case FWMEM_EWAIT: return "a kernel's bounded wait gave up: results since the last check are wrong";
   }
   return "unknown status";
 }
@@ -278,6 +302,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
   p.flags = mode->flags;
   p.eps = mode->eps;
+  fwmem::wait_config(&p.wait_polls, &p.wait_bias);
   if (z.BH > 0x7fffffff / 8 || (size_t)p.nchunks * z.BH > 0x7fffffffu) return FWMEM_EUNSUPPORTED;
   // per-head byte offsets of every buffer (inputs, outputs, records) stay below 2^31
   const size_t dmax = (size_t)(shape->dk > shape->dv ? shape->dk : shape->dv);

@@ -90,6 +90,9 @@ struct ScanParams {
   int bf16;              // 1: bf16 inputs, 0: fp32
   uint32_t flags;
   float eps;
+  // bounded waits of the split propagate kernel: polls before giving up, and an offset
+  // added to the awaited value (0; a test sets it so that every wait gives up)
+  int wait_polls, wait_bias;
 };
 
 struct StepParams {
@@ -122,6 +125,13 @@ hipError_t launch_prep_split(const ScanParams& p, hipStream_t stream);
 size_t scan_pv_record_bytes();
 hipError_t launch_scan_pv(const ScanParams& p, hipStream_t stream, int phases);
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t stream);
+// Polls of a bounded wait before it gives up, and the offset of the awaited value: from
+// FWMEM_TEST_WAIT_TIMEOUT=n (n > 0, a test's setting: every wait gives up after n polls),
+// else 2^22 and 0.
+void wait_config(int* polls, int* bias);
+// Synchronises `stream`, reads the current device's sticky wait status into *value and
+// clears it if it was set.
+hipError_t read_wait_status(hipStream_t stream, int* value);
 // Whether kernels exist for this size.
 bool scan_supported(int dk, int dv);
 bool step_supported(int dk, int dv);

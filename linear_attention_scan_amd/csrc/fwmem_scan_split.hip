@@ -36,6 +36,7 @@
 #include "fwmem_internal.h"
 #include "fwmem_split.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace fwmem {
@@ -236,14 +237,29 @@ __device__ __forceinline__ lds_flag_ptr flag_ptr(int* f) {
   return (lds_flag_ptr)(uintptr_t)(uint32_t)reinterpret_cast<uintptr_t>(f);
 }
 
+// Sticky status of this device: nonzero once a bounded wait of a propagate kernel gave
+// up (fwmem_check_device reads and clears it).
+__device__ int g_wait_status;
+
 // Polls an LDS flag until it holds v. The writer sets it within the same chunk period,
-// so a correct run never reaches the poll limit; the limit only bounds the wait.
-__device__ __forceinline__ void wait_flag(int* f, int v) {
+// so a correct run never reaches the poll limit; the limit only bounds the wait. A wait
+// that reaches it goes on (the chunk's values are then wrong, but every wave keeps to the
+// same barriers and the kernel ends) and records the failure in g_wait_status, by a
+// vector store from one lane. `bias` is 0, except in a test that forces every wait to
+// give up after a few polls by waiting for a value no wave writes.
+__device__ __forceinline__ void wait_flag(int* f, int v, const ScanParams& p) {
   lds_flag_ptr fp = flag_ptr(f);
-  for (int i = 0; i < (1 << 22); ++i) {
-    if (__builtin_amdgcn_readfirstlane(*fp) == v) break;
+  const int target = v + p.wait_bias;
+  bool done = false;
+  for (int i = 0; i < p.wait_polls; ++i) {
+    if (__builtin_amdgcn_readfirstlane(*fp) == target) {
+      done = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (!done && (threadIdx.x & 63) == 0)
+    __hip_atomic_store(&g_wait_status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("" ::: "memory");
 }
 
@@ -373,7 +389,8 @@ __device__ __forceinline__ float vf(const s4& h, int i) {
 // Gamma_C' S' with Gamma_C' the next chunk's decay (1 after the last chunk) and Sh/Sl
 // the split of S'.
 template <int DK, bool SOLVE>
-__device__ __forceinline__ void alpha_step(const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H, int c, bool last,
+__device__ __forceinline__ void alpha_step(const ScanParams& p, const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H,
+                                           int c, bool last,
                                            const Lane& L, f4 (&acc)[DK / 16], u32x4 (&Sh)[DK / 32],
                                            u32x4 (&Sl)[DK / 32]) {
   constexpr int NKD = DK / 32;  // K blocks over d_k
@@ -534,7 +551,7 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, SOLVE>& B, Handoff
   });
   // beta raised sflag early in this period; the split state for the next chunk goes to
   // the hand-off slot K block by K block as it completes
-  if (!last) wait_flag(&H.sflag[L.tile], c + 1);
+  if (!last) wait_flag(&H.sflag[L.tile], c + 1, p);
   static_for<0, NE0 + 4>([&](auto I) {
     constexpr int i = I, rt = i / 2, part = i % 2;
     if constexpr (i < NE0) mma_w(acc[rt], xtjoin(xth[rt][1][0], xth[rt][1][1]), part ? Wl[1] : Wh[1]);
@@ -572,7 +589,8 @@ __device__ __forceinline__ void alpha_step(const SplitBuf<DK, SOLVE>& B, Handoff
 
 // ---- beta: the outputs of one tile for chunk c
 template <int DK, bool SOLVE, bool OBF>
-__device__ __forceinline__ void beta_step(const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H, int c, const Lane& L,
+__device__ __forceinline__ void beta_step(const ScanParams& p, const SplitBuf<DK, SOLVE>& B, Handoff<DK>& H,
+                                          int c, const Lane& L,
                                           int dv, uint32_t vo, __amdgpu_buffer_rsrc_t ro) {
   constexpr int NKD = DK / 32;
   const Frags<DK, SOLVE> F{B, L};
@@ -620,7 +638,7 @@ __device__ __forceinline__ void beta_step(const SplitBuf<DK, SOLVE>& B, Handoff<
   for (int m = 0; m < 4; ++m) Om[m] *= for_[m];
 
   // ---- C: U from alpha, its split, and O += M U (18 MFMAs)
-  wait_flag(&H.uflag[L.tile], c + 1);
+  wait_flag(&H.uflag[L.tile], c + 1, p);
   f4 U[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) U[m] = H.u[L.tile][m][L.lane];
@@ -731,8 +749,8 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     set_flag(&H.uflag[L.tile], 0);
 
     for (int c = 0; c < p.nchunks; c += 2) {
-      alpha_step<DK, SOLVE>(B0, H, c, c + 1 == p.nchunks, L, acc, Sh, Sl);
-      if (c + 1 < p.nchunks) alpha_step<DK, SOLVE>(B1, H, c + 1, c + 2 == p.nchunks, L, acc, Sh, Sl);
+      alpha_step<DK, SOLVE>(p, B0, H, c, c + 1 == p.nchunks, L, acc, Sh, Sl);
+      if (c + 1 < p.nchunks) alpha_step<DK, SOLVE>(p, B1, H, c + 1, c + 2 == p.nchunks, L, acc, Sh, Sl);
     }
     // after the last chunk acc holds S' (its next-chunk decay is 1)
     if (p.S_out != nullptr) {
@@ -750,8 +768,8 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
       rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes);
   const uint32_t vo = (uint32_t)(8 * L.g * dv + col) * oes;
   for (int c = 0; c < p.nchunks; c += 2) {
-    beta_step<DK, SOLVE, OBF>(B0, H, c, L, dv, vo, ro);
-    if (c + 1 < p.nchunks) beta_step<DK, SOLVE, OBF>(B1, H, c + 1, L, dv, vo, ro);
+    beta_step<DK, SOLVE, OBF>(p, B0, H, c, L, dv, vo, ro);
+    if (c + 1 < p.nchunks) beta_step<DK, SOLVE, OBF>(p, B1, H, c + 1, L, dv, vo, ro);
   }
 }
 
@@ -777,6 +795,38 @@ hipError_t launch_dk(const ScanParams& p, hipStream_t st) {
 
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t st) {
   return p.dk == 64 ? launch_dk<64>(p, st) : launch_dk<128>(p, st);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct StatusWord {
+  std::once_flag once;
+  int* ptr = nullptr;
+};
+StatusWord g_status[kMaxDevices];
+}  // namespace
+
+hipError_t read_wait_status(hipStream_t st, int* value) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StatusWord& w = g_status[dev];
+  std::call_once(w.once, [&w]() {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(g_wait_status)) == hipSuccess) w.ptr = static_cast<int*>(a);
+  });
+  if (w.ptr == nullptr) return hipErrorInvalidSymbol;
+  int h = 0;
+  e = hipMemcpyAsync(&h, w.ptr, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && h != 0) {
+    static const int zero = 0;
+    e = hipMemcpyAsync(w.ptr, &zero, sizeof(int), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  *value = h;
+  return e;
 }
 
 }  // namespace fwmem

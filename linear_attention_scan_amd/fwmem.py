@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfwmem.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EOVERLAP, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
+EWAIT = -7
 RULE_DELTA, RULE_ADDITIVE, RULE_INNER, RULE_DELTA_PV = 0, 1, 2, 3
 F32, BF16 = 0, 1
 PHI_ELU1 = 1 << 0
@@ -30,7 +31,8 @@ LAMBDA_SCALED = 1 << 9
 
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",
-            "fwmem_scan_bwd_workspace_bytes", "fwmem_scan_bwd", "fwmem_strerror", "fwmem_version"]
+            "fwmem_scan_bwd_workspace_bytes", "fwmem_scan_bwd", "fwmem_strerror", "fwmem_version",
+            "fwmem_check_device"]
 PHASE_BOTH, PHASE_PREP, PHASE_PROPAGATE = "fwmem_scan_fwd", "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate"
 
 
@@ -81,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fwmem_scan_bwd.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.POINTER(Mode),
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fwmem_scan_bwd.restype = ctypes.c_int
+    lib.fwmem_check_device.argtypes = [vp]
+    lib.fwmem_check_device.restype = ctypes.c_int
     lib.fwmem_strerror.argtypes = [ctypes.c_int]
     lib.fwmem_strerror.restype = ctypes.c_char_p
     lib.fwmem_version.argtypes = []
@@ -95,6 +99,12 @@ def strerror(status: int) -> str:
 
 def version() -> str:
     return load().fwmem_version().decode()
+
+
+def check_device(stream=None) -> int:
+    """fwmem_check_device: synchronise the stream, read and clear the GPU's sticky wait
+    status; returns OK or EWAIT (ELAUNCH if it could not be read)."""
+    return load().fwmem_check_device(_stream(stream))
 
 
 def shape(B, H, T, dk, dv, dtype) -> Shape:

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     _lib()
     assert re.match(r"^\d+\.\d+\.\d+$", F.version())
-    for code in (F.OK, F.EINVAL, F.EUNSUPPORTED, F.EALIGN, F.EOVERLAP, F.ELAUNCH, F.EWORKSPACE):
+    for code in (F.OK, F.EINVAL, F.EUNSUPPORTED, F.EALIGN, F.EOVERLAP, F.ELAUNCH, F.EWORKSPACE,
+                 F.EWAIT):
         assert F.strerror(code) and F.strerror(code) != "unknown status"
     assert F.strerror(123) == "unknown status"
 
@@ -238,3 +239,4 @@ def test_bwd_workspace_size_and_empty_batch():
     # B*H == 0: nothing to do, no pointer is needed
     assert _bwd(shp=F.shape(0, 2, 8, 64, 64, F.F32), q=None, k=None, v=None, gout=None, gq=None,
                 gk=None, gv=None, ws=None) == F.OK
+
