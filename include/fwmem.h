@@ -267,8 +267,10 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  *
  *   q, k, v, beta, lambda, S_in: exactly as passed to fwmem_scan_fwd (read only)
  *   grad_out     [B][H][T][dv] float32  (required when T > 0)
- *   grad_S_out   state buffer or NULL (zero); only its S part is read: the final
- *                state's carried key and flag take no gradient
+ *   grad_S_out   state buffer or NULL (zero); its S part is read, and with FWMEM_ZNORM
+ *                its x_prev part (the gradient of the final normaliser z_T, which the
+ *                forward call leaves there); the final carried key and flag take no
+ *                gradient
  *   grad_q, grad_k [B][H][T][dk] float32; grad_v [B][H][T][dv] float32 (required when
  *                T > 0; every element is written)
  *   grad_beta    beta's shape ([B][H][T], or [B][H][T][dv] per value channel) float32,

@@ -618,6 +618,7 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.dout = grad_out;
   p.dS_out = gso.S;
   p.gq = grad_q;
+  p.dz_out = (mode->flags & FWMEM_ZNORM) ? gso.x : nullptr;
   p.gk = grad_k;
   p.gv = grad_v;
   p.gbeta = grad_beta;

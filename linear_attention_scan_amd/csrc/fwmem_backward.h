@@ -21,6 +21,7 @@ struct BwdParams {
   const int32_t* has_in;  // [BH] or null
   const float* dout;      // [BH][T][dv]
   const float* dS_out;    // [BH][dk][dv] or null (zeros)
+  const float* dz_out;    // [BH][dk] the final normaliser's gradient (normaliser only), or null
   float* gq;              // [BH][T][dk]
   float* gk;              // [BH][T][dk]
   float* gv;              // [BH][T][dv]

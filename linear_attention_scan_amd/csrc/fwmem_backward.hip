@@ -347,8 +347,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   load_state(p.dS_out != nullptr ? p.dS_out + (size_t)bh * SS : nullptr, G);
   float Gz[RPT];         // ZN: dL/dz_t on the thread's rows
   float dden_pend = 0.f;  // ZN: the normaliser's gradient of the token whose read was last undone
+  // the final normaliser is an output (the state's carried-key slot): its gradient starts G_z
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) Gz[j] = 0.f;
+  for (int j = 0; j < RPT; ++j) Gz[j] = (ZN && p.dz_out != nullptr) ? p.dz_out[(size_t)bh * DK + row(j)] : 0.f;
   if (R::shift && T >= 1)  // the last key is written by no step of this call
     for (int i = tid; i < DK; i += NT) p.gk[(rb + T - 1) * DK + i] = 0.f;
   for (int c = nch - 1; c >= 0; --c) {

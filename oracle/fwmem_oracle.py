@@ -286,8 +286,9 @@ def unit_rows_vjp(x: np.ndarray, g: np.ndarray, length: float = 1.0) -> np.ndarr
 
 def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity", eps=1e-6,
                   per_channel=False, S0=None, xprev0=None, has0=None, beta_act=None,
-                  lam_act=False, qk_norm=None, lam_scaled=False, znorm=False):
-    """Gradients of L = sum(dO * o) + sum(dS * S_T) with respect to every input of scan(),
+                  lam_act=False, qk_norm=None, lam_scaled=False, znorm=False, dz=None):
+    """Gradients of L = sum(dO * o) + sum(dS * S_T) (+ sum(dz * z_T) with znorm) with respect
+    to every input of scan(),
     for the delta, additive and inner rules with phi identity or elu+1, scalar or
     per-channel lambda (reading D21: the pages give no backward pass).
 
@@ -311,7 +312,9 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
     the read passes dO_t / den_t to S_t and -(dO_t . o_t) / den_t to den_t, hence q_t z_t
     terms, a gradient G_z of z_t carried back like G (z_t = gamma_t z_{t-1} + beta_t k_t),
     and the initial z (the state's carried-key slot) receives G_z as "xprev0". The final z
-    takes no gradient.
+    is an output of the scan (the returned state's carried-key slot), so dz [B,H,dk] (None:
+    zero), the gradient of L with respect to it, starts G_z; a sequence split over calls
+    then chains like one call.
 
     With qk_norm ("l2" or "rms", identity phi, as in scan()) q, k and the carried key are
     raw and the recurrence sees them rescaled to a fixed length: the gradients with respect
@@ -330,7 +333,7 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
                           rule=rule, eps=eps, per_channel=per_channel, S0=S0,
                           xprev0=unit_rows(xprev0, length) if key0 else xprev0,
                           has0=has0, beta_act=beta_act, lam_act=lam_act, lam_scaled=lam_scaled,
-                          znorm=znorm)
+                          znorm=znorm, dz=dz)
         g["q"] = unit_rows_vjp(q, g["q"], length)
         g["k"] = unit_rows_vjp(k, g["k"], length)
         if key0:
@@ -371,6 +374,12 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
         raise ValueError("lam_scaled takes the delta or inner rule")
     if znorm and rule != RULE_ADDITIVE:
         raise ValueError("znorm takes the additive rule")
+    if dz is not None and not znorm:
+        raise ValueError("dz is the gradient of the final normaliser (znorm)")
+    dzh = np.zeros((N, dk)) if dz is None else _heads(dz, 1)
+    if dz is not None and not znorm:
+        raise ValueError("dz is the gradient of the final normaliser (znorm)")
+    dzh = np.zeros((N, dk)) if dz is None else _heads(dz, 1)
 
     g = {name: np.zeros_like(a) for name, a in (("q", Q), ("k", K), ("v", V))}
     g["beta"] = None if Bt is None else np.zeros_like(Bt)
@@ -426,7 +435,7 @@ def scan_backward(q, k, v, beta, lam, dO, dS=None, *, rule, phi_kind="identity",
 
         # backward: G holds dL/dS_t (and Gz dL/dz_t) while step t is undone
         G = dSh[n].copy()
-        Gz = np.zeros(dk)
+        Gz = dzh[n].copy()
         for t in range(T - 1, -1, -1):
             rec, St, qf = steps[t]
             if znorm:

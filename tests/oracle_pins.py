@@ -762,10 +762,12 @@ def pin_p24_backward(orc):
         per-channel beta, lambda, S0, the carried key), plain, with elu+1, and with the
         scale-coupled ridge and pre-activated gates; with every beta_j equal it is the
         delta rule, and so are its gradients (beta's summed over j).
-    (h) Normalised linear attention (additive, znorm): finite differences match every
-        gradient (q, k, v, beta, gamma, S0 and the initial z), scalar and per-channel
-        retention, positive identity features (raw or l2-normalised by the scan, which
-        leaves z itself unscaled) and elu+1."""
+    (h) Normalised linear attention (additive, znorm): finite differences of
+        L + sum(dz z_T) match every gradient (q, k, v, beta, gamma, S0 and the initial z),
+        scalar and per-channel retention, positive identity features (raw or l2-normalised
+        by the scan, which leaves z itself unscaled) and elu+1; and a sequence split over
+        two calls, the second call's state gradient fed to the first as its (dS, dz),
+        gives the one-call gradients."""
     rng = np.random.default_rng(42)
     T, dk, dv = 5, 3, 2
     for rule in (DELTA, INNER, ADD):
@@ -957,17 +959,35 @@ def pin_p24_backward(orc):
             lam = rng.uniform(0.6, 1.0, (1, 1, T, dk) if per_channel else (1, 1, T))
             dO, dS = rng.standard_normal((1, 1, T, dv)), rng.standard_normal((1, 1, dk, dv))
             S0, z0 = rng.standard_normal((1, 1, dk, dv)), rng.uniform(0.2, 1.0, (1, 1, dk))
+            dz = rng.standard_normal((1, 1, dk))
             kw = dict(rule=ADD, per_channel=per_channel, znorm=True,
                       phi_kind="elu1" if phi_kind == "elu1" else "identity",
                       qk_norm="l2" if phi_kind == "identity_l2" else None)
             args = {"q": q, "k": k, "v": v, "beta": b, "lam": lam, "S0": S0, "xprev0": z0}
 
             def loss(a):
-                o, S, _, _ = orc.scan(a["q"], a["k"], a["v"], a["beta"], a["lam"], S0=a["S0"],
-                                      xprev0=a["xprev0"], **kw)
-                return float(np.sum(o * dO) + np.sum(S * dS))
+                o, S, zT, _ = orc.scan(a["q"], a["k"], a["v"], a["beta"], a["lam"], S0=a["S0"],
+                                       xprev0=a["xprev0"], **kw)
+                return float(np.sum(o * dO) + np.sum(S * dS) + np.sum(zT * dz))
 
-            gr = orc.scan_backward(q, k, v, b, lam, dO, dS, S0=S0, xprev0=z0, **kw)
+            gr = orc.scan_backward(q, k, v, b, lam, dO, dS, S0=S0, xprev0=z0, dz=dz, **kw)
+            # two calls: the second call's gradients of its initial S and z are the first
+            # call's (dS, dz)
+            T1 = 2
+            cut = lambda x, a, e: x[:, :, a:e]
+            _, S1, z1, h1 = orc.scan(cut(q, 0, T1), cut(k, 0, T1), cut(v, 0, T1), cut(b, 0, T1),
+                                     cut(lam, 0, T1), S0=S0, xprev0=z0, **kw)
+            g2 = orc.scan_backward(cut(q, T1, T), cut(k, T1, T), cut(v, T1, T), cut(b, T1, T),
+                                   cut(lam, T1, T), cut(dO, T1, T), dS, S0=S1, xprev0=z1,
+                                   has0=h1, dz=dz, **kw)
+            g1 = orc.scan_backward(cut(q, 0, T1), cut(k, 0, T1), cut(v, 0, T1), cut(b, 0, T1),
+                                   cut(lam, 0, T1), cut(dO, 0, T1), g2["S0"], S0=S0, xprev0=z0,
+                                   dz=g2["xprev0"], **kw)
+            for name in ("q", "k", "v", "beta", "lam"):
+                both = np.concatenate([g1[name], g2[name]], axis=2)
+                np.testing.assert_allclose(both, gr[name], rtol=1e-10, atol=1e-12)
+            for name in ("S0", "xprev0"):
+                np.testing.assert_allclose(g1[name], gr[name], rtol=1e-10, atol=1e-12)
             for name, arr in args.items():
                 for idx in np.ndindex(arr.shape):
                     a = dict(args)

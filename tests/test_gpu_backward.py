@@ -366,6 +366,7 @@ def test_backward_normaliser(phi, dtype, dk, dv, T, extra):
     rng = np.random.default_rng(T + 5)
     dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
     dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    dz = (rng.standard_normal((w.B, w.H, dk)) * 0.3).astype(np.float32)  # the final z's gradient
     flags = (F.ZNORM | (F.PHI_ELU1 if phi == "elu1" else 0)
              | ((F.QK_L2NORM | F.BETA_SIGMOID | F.LAMBDA_PREACT) if both else 0))
     beta = w.beta_pre if both else w.beta
@@ -373,9 +374,52 @@ def test_backward_normaliser(phi, dtype, dk, dv, T, extra):
     g = F.scan_bwd(dev_tensor(w.q, w.dtype), dev_tensor(w.k, w.dtype), dev_tensor(w.v, w.dtype),
                    f32_tensor(beta), f32_tensor(lam), f32_tensor(dO), rule=r, flags=flags, eps=w.eps,
                    S_in=make_state(w.B, w.H, dk, dv, S=w.S0, xprev=w.xprev0),
-                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS, xprev=dz))
     ref = orc.scan_backward(w.q, w.k, w.v, beta, lam, dO, dS, rule=r, phi_kind=phi, eps=w.eps,
                             S0=w.S0, xprev0=w.xprev0, znorm=True, qk_norm="l2" if both else None,
-                            beta_act="sigmoid" if both else None, lam_act=both)
+                            beta_act="sigmoid" if both else None, lam_act=both, dz=dz)
     assert np.any(ref["xprev0"] != 0)
     _compare(g, ref)
+
+
+def test_backward_normaliser_chains_over_calls():
+    """A normalised linear-attention sequence split over two calls: the backward of the
+    second call (from the first call's final state), then the backward of the first call
+    with the second's grad_S_in as its grad_S_out (the S part and the normaliser's
+    gradient in the x_prev part), gives the gradients of one call over the whole
+    sequence. fp32 inputs, so that the forward state handed between the calls is as
+    exact as the backward's own recomputation."""
+    r, dk, dv, T, T1 = wl.RULE_ADDITIVE, 64, 128, 150, 70
+    w = wl.make_scan(B=2, H=2, T=T, dk=dk, dv=dv, dtype="f32", rule=r, beta_kind="sigmoid",
+                     lam_kind="gamma", phi=wl.PHI_ELU1, normalise_qk=False, znorm=True,
+                     s0_std=0.05, seed=11)
+    rng = np.random.default_rng(12)
+    dO = rng.standard_normal((w.B, w.H, T, dv)).astype(np.float32)
+    dS = (rng.standard_normal((w.B, w.H, dk, dv)) * 0.3).astype(np.float32)
+    dz = (rng.standard_normal((w.B, w.H, dk)) * 0.3).astype(np.float32)
+    flags = F.ZNORM | F.PHI_ELU1
+    dev = lambda x, a, e: dev_tensor(np.ascontiguousarray(x[:, :, a:e]), "f32")
+    S0 = lambda: make_state(w.B, w.H, dk, dv, S=w.S0, xprev=w.xprev0)
+    say("[bwd znorm chain] one call")
+    g = F.scan_bwd(dev(w.q, 0, T), dev(w.k, 0, T), dev(w.v, 0, T), dev(w.beta, 0, T),
+                   dev(w.lam, 0, T), dev(dO, 0, T), rule=r, flags=flags, eps=w.eps, S_in=S0(),
+                   grad_S_out=make_state(w.B, w.H, dk, dv, S=dS, xprev=dz))
+    say("[bwd znorm chain] forward of the first part, then the two backward calls")
+    _, S1 = F.scan_fwd(dev(w.q, 0, T1), dev(w.k, 0, T1), dev(w.v, 0, T1), dev(w.beta, 0, T1),
+                       dev(w.lam, 0, T1), rule=r, flags=flags, eps=w.eps, S_in=S0())
+    g2 = F.scan_bwd(dev(w.q, T1, T), dev(w.k, T1, T), dev(w.v, T1, T), dev(w.beta, T1, T),
+                    dev(w.lam, T1, T), dev(dO, T1, T), rule=r, flags=flags, eps=w.eps, S_in=S1,
+                    grad_S_out=make_state(w.B, w.H, dk, dv, S=dS, xprev=dz))
+    g1 = F.scan_bwd(dev(w.q, 0, T1), dev(w.k, 0, T1), dev(w.v, 0, T1), dev(w.beta, 0, T1),
+                    dev(w.lam, 0, T1), dev(dO, 0, T1), rule=r, flags=flags, eps=w.eps, S_in=S0(),
+                    grad_S_out=g2["state"])
+    ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS, rule=r, phi_kind="elu1",
+                            eps=w.eps, S0=w.S0, xprev0=w.xprev0, znorm=True, dz=dz)
+    _compare(g, ref)
+    for name in ("q", "k", "v", "beta", "lam"):
+        both_parts = np.concatenate([g1[name].cpu().numpy(), g2[name].cpu().numpy()], axis=2)
+        e = orc.relerr(both_parts, g[name].cpu().numpy())
+        assert e <= TOL["f32"], (name, e)
+    for name in ("S", "x_prev"):
+        e = orc.relerr(getattr(g1["state"], name).cpu().numpy(), getattr(g["state"], name).cpu().numpy())
+        assert e <= TOL["f32"], (name, e)
