@@ -280,8 +280,10 @@ fwmem_status fwmem_scan_bwd_workspace_bytes(const fwmem_shape* shape, const fwme
  *                at the default value (write scale 1, ridge 0, retention 1).
  *   grad_S_in    state buffer or NULL: its S part receives dL/dS_0, its x_prev part
  *                dL/dx_prev (with respect to the carried key as stored, phi already
- *                applied; zero without a carried key and for the additive rule), its
- *                has_prev part 0.
+ *                applied; zero without a carried key and for the additive rule), or
+ *                with FWMEM_ZNORM dL/dz_0 (the initial normaliser), its has_prev part 0.
+ *                So a sequence split over calls chains: feeding one call's grad_S_in
+ *                to the previous call as its grad_S_out gives the one-call gradients.
  *   workspace, ws_bytes: device scratch of at least fwmem_scan_bwd_workspace_bytes()
  *
  * Outputs must not overlap one another, the inputs or the workspace (FWMEM_EOVERLAP).
