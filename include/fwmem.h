@@ -35,7 +35,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are caller-owned DEVICE pointers, dense, row-major, in
- *     the layouts given below. The library never allocates, frees or synchronises.
+ *     the layouts given below. The library never allocates, frees or synchronises
+ *     (fwmem_scan_fwd_noalloc's workspace is a fixed array the library image holds).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream).
  *     Argument errors are reported before anything is enqueued; device faults appear
  *     at the caller's next synchronisation. No exception crosses this interface.
@@ -80,8 +81,10 @@ typedef enum {
   FWMEM_EOVERLAP = -4,     /* S_in and S_out partly overlap, or out overlaps an input/state */
   FWMEM_ELAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
   FWMEM_EWORKSPACE = -6,   /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
-  FWMEM_EWAIT = -7         /* fwmem_check_device: a bounded wait inside a kernel gave up since
+  FWMEM_EWAIT = -7,        /* fwmem_check_device: a bounded wait inside a kernel gave up since
                               the last check; the outputs of the calls in between are wrong */
+  FWMEM_ESCRATCH = -8      /* fwmem_scan_fwd_noalloc: the call needs more workspace than the
+                              library's fixed device scratch (FWMEM_NOALLOC_SCRATCH_BYTES) */
 } fwmem_status;
 
 /* DELTA_PV: the delta rule with one step size per value channel (Falcon-2, "Fast Weight
@@ -219,6 +222,31 @@ fwmem_status fwmem_scan_chunk_propagate(const fwmem_shape* shape, const void* q,
                                         const fwmem_mode* mode, const void* S_in, void* out,
                                         void* S_out, void* workspace, size_t ws_bytes,
                                         fwmem_stream stream);
+
+/*
+ * fwmem_scan_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * checks and results as fwmem_scan_fwd without the workspace pair: the workspace is a
+ * fixed device array inside the library, FWMEM_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held from the first call on that GPU until the process ends. This call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine); its first call on a
+ * GPU looks up the array's device address there.
+ *
+ * Limit: a call whose fwmem_scan_workspace_bytes() exceeds FWMEM_NOALLOC_SCRATCH_BYTES
+ * returns FWMEM_ESCRATCH before anything is enqueued (the bf16 delta rule at d = 128
+ * needs 26,112 bytes per head and 64-token chunk: 2,570 (head, chunk) pairs fit, e.g.
+ * B*H = 32 heads of T = 4096). FWMEM_ELAUNCH: no current device, or the array's address
+ * could not be found.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ * (nothing in it needs clearing between calls). Calls that overlap in time on one GPU,
+ * from two streams or two host threads, race on it and must be serialised by the caller.
+ */
+#define FWMEM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fwmem_status fwmem_scan_fwd_noalloc(const fwmem_shape* shape, const void* q, const void* k,
+                                    const void* v, const float* beta, const float* lambda,
+                                    const fwmem_mode* mode, const void* S_in, void* out,
+                                    void* S_out, fwmem_stream stream);
 
 /*
  * One-token recurrent decode: the same recurrence for a single token per head

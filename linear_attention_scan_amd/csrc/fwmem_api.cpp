@@ -189,6 +189,7 @@ const char* fwmem_strerror(fwmem_status st) {
     case FWMEM_EOVERLAP: return "overlapping buffers";
     case FWMEM_ELAUNCH: return "kernel launch failed";
     case FWMEM_EWORKSPACE: return "workspace missing or too small";
+    case FWMEM_ESCRATCH: return "the call needs more workspace than the fixed device scratch holds";
     case FWMEM_EWAIT: return "a kernel's bounded wait gave up: results since the last check are wrong";
   }
   return "unknown status";
@@ -617,8 +618,8 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.has_in = si.h;
   p.dout = grad_out;
   p.dS_out = gso.S;
-  p.gq = grad_q;
   p.dz_out = (mode->flags & FWMEM_ZNORM) ? gso.x : nullptr;
+  p.gq = grad_q;
   p.gk = grad_k;
   p.gv = grad_v;
   p.gbeta = grad_beta;

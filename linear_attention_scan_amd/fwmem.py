@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfwmem.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EOVERLAP, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
-EWAIT = -7
+EWAIT, ESCRATCH = -7, -8
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FWMEM_NOALLOC_SCRATCH_BYTES
 RULE_DELTA, RULE_ADDITIVE, RULE_INNER, RULE_DELTA_PV = 0, 1, 2, 3
 F32, BF16 = 0, 1
 PHI_ELU1 = 1 << 0
@@ -32,7 +33,7 @@ LAMBDA_SCALED = 1 << 9
 EXPORTED = ["fwmem_state_bytes", "fwmem_scan_workspace_bytes", "fwmem_scan_fwd",
             "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate", "fwmem_step",
             "fwmem_scan_bwd_workspace_bytes", "fwmem_scan_bwd", "fwmem_strerror", "fwmem_version",
-            "fwmem_check_device"]
+            "fwmem_scan_fwd_noalloc", "fwmem_check_device"]
 PHASE_BOTH, PHASE_PREP, PHASE_PROPAGATE = "fwmem_scan_fwd", "fwmem_scan_chunk_prep", "fwmem_scan_chunk_propagate"
 
 
@@ -74,6 +75,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.POINTER(Mode), vp, vp, vp,
                        vp, sz, vp]
         fn.restype = ctypes.c_int
+    lib.fwmem_scan_fwd_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp,
+                                           ctypes.POINTER(Mode), vp, vp, vp, vp]
+    lib.fwmem_scan_fwd_noalloc.restype = ctypes.c_int
     lib.fwmem_step.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, ctypes.POINTER(Mode),
                                vp, vp, vp, vp]
     lib.fwmem_step.restype = ctypes.c_int
@@ -164,6 +168,15 @@ def scan_fwd_raw(shp: Shape, q, k, v, beta, lam, md: Mode, S_in, out, S_out, wor
     return fn(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(lam),
               ctypes.byref(md), _ptr(S_in), _ptr(out), _ptr(S_out), _ptr(workspace),
               int(ws_bytes), _stream(stream))
+
+
+def scan_fwd_noalloc_raw(shp: Shape, q, k, v, beta, lam, md: Mode, S_in, out, S_out,
+                         stream=None) -> int:
+    """Call fwmem_scan_fwd_noalloc (the scan with the library's fixed device scratch as its
+    workspace) with tensors (or raw ints / None) and return the status."""
+    return load().fwmem_scan_fwd_noalloc(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(beta), _ptr(lam), ctypes.byref(md), _ptr(S_in),
+                                         _ptr(out), _ptr(S_out), _stream(stream))
 
 
 def step_raw(shp: Shape, q, k, v, beta, lam, md: Mode, S_in, out, S_out, stream=None) -> int:

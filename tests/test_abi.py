@@ -38,7 +38,7 @@ def test_version_and_strerror():
     _lib()
     assert re.match(r"^\d+\.\d+\.\d+$", F.version())
     for code in (F.OK, F.EINVAL, F.EUNSUPPORTED, F.EALIGN, F.EOVERLAP, F.ELAUNCH, F.EWORKSPACE,
-                 F.EWAIT):
+                 F.ESCRATCH, F.EWAIT):
         assert F.strerror(code) and F.strerror(code) != "unknown status"
     assert F.strerror(123) == "unknown status"
 
@@ -240,3 +240,16 @@ def test_bwd_workspace_size_and_empty_batch():
     assert _bwd(shp=F.shape(0, 2, 8, 64, 64, F.F32), q=None, k=None, v=None, gout=None, gq=None,
                 gk=None, gv=None, ws=None) == F.OK
 
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch():
+    # host-side check, before any device call: 64 bf16 heads of T = 4096 at d = 128 need
+    # about 107 MB of workspace, beyond the 64 MiB scratch
+    _lib()
+    shp = F.shape(4, 16, 4096, 128, 128, F.BF16)
+    md = F.mode(F.RULE_DELTA, 0, 1e-6, 0)
+    assert F.workspace_bytes(shp, md) > F.NOALLOC_SCRATCH_BYTES
+    st = F.scan_fwd_noalloc_raw(shp, 16, 16, 16, 16, 16, md, None, 16, None, stream=0)
+    assert st == F.ESCRATCH
+    # argument errors come first, as for fwmem_scan_fwd
+    bad = F.mode(7, 0, 1e-6, 0)
+    assert F.scan_fwd_noalloc_raw(shp, 16, 16, 16, 16, 16, bad, None, 16, None, stream=0) == F.EINVAL
