@@ -540,6 +540,8 @@ fwmem_status check_bwd(const fwmem_shape* shape, const fwmem_mode* mode) {
 
 size_t bwd_ws_bytes(const fwmem_shape* shape, const fwmem_mode* mode) {
   const size_t BH = (size_t)shape->B * (size_t)shape->H;
+  if (fwmem::bwd_chunked(mode->rule, mode->flags, shape->T))
+    return align256(4 * BH * fwmem::bwd_chunk_floats_per_head(shape->T, shape->dk, shape->dv));
   const bool zn = (mode->flags & FWMEM_ZNORM) != 0;
   const bool small = (mode->flags & FWMEM_LAMBDA_PER_CHANNEL) != 0 || mode->rule == FWMEM_RULE_DELTA_PV || zn;
   return align256(4 * BH * fwmem::bwd_floats_per_head(shape->T, shape->dk, shape->dv, small, zn));
@@ -638,7 +640,9 @@ fwmem_status fwmem_scan_bwd(const fwmem_shape* shape, const void* q, const void*
   p.bf16 = shape->dtype == FWMEM_BF16 ? 1 : 0;
   p.flags = mode->flags;
   p.eps = mode->eps;
-  const hipError_t e = fwmem::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fwmem::bwd_chunked(p.rule, p.flags, p.T) ? fwmem::launch_bwd_chunked(p, hs)
+                                                                : fwmem::launch_bwd(p, hs);
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
 }
 

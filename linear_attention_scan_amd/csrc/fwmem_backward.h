@@ -53,5 +53,15 @@ __host__ __device__ inline size_t bwd_floats_per_head(int T, int dk, int dv, boo
 }
 bool bwd_supported(int dk, int dv);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// QK normalisation: maps the q, k and carried-key gradients, taken with respect to the
+// rescaled vectors, back to the raw ones in place (nothing without the flags).
+hipError_t launch_qk_norm_bwd(const BwdParams& p, hipStream_t stream);
+
+// The chunk-parallel backward (fwmem_backward_chunk.hip): the delta, inner and additive
+// rules with a scalar decay and without the normaliser, T >= 1. Its workspace per head:
+// one record and two states per 64-token chunk.
+bool bwd_chunked(int rule, uint32_t flags, int T);
+size_t bwd_chunk_floats_per_head(int T, int dk, int dv);
+hipError_t launch_bwd_chunked(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fwmem

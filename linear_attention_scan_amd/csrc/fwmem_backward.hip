@@ -650,17 +650,23 @@ hipError_t launch_pc(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename InT, int DK, int DV>
-hipError_t launch_t(const BwdParams& p, hipStream_t st) {
-  const hipError_t e =
-      (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
+template <typename InT, int DK>
+hipError_t launch_qk(const BwdParams& p, hipStream_t st) {
   const float len = qk_length(p.flags, DK);
-  if (e != hipSuccess || len <= 0.f) return e;
+  if (len <= 0.f) return hipSuccess;
   const size_t rows = 2 * (size_t)p.BH * (size_t)p.T +
                       ((p.gx0 != nullptr && p.xprev_in != nullptr && !(p.flags & kFlagZnorm)) ? p.BH : 0);
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((qk_norm_bwd_kernel<InT, DK>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, p, len);
   return hipGetLastError();
+}
+
+template <typename InT, int DK, int DV>
+hipError_t launch_t(const BwdParams& p, hipStream_t st) {
+  const hipError_t e =
+      (p.flags & kFlagPerChannel) ? launch_pc<InT, DK, DV, true>(p, st) : launch_pc<InT, DK, DV, false>(p, st);
+  if (e != hipSuccess) return e;
+  return launch_qk<InT, DK>(p, st);
 }
 
 template <typename InT>
@@ -678,6 +684,12 @@ bool bwd_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   if (p.BH == 0) return hipSuccess;
   return p.bf16 ? launch_in<uint16_t>(p, st) : launch_in<float>(p, st);
+}
+
+hipError_t launch_qk_norm_bwd(const BwdParams& p, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  if (p.bf16) return p.dk == 64 ? launch_qk<uint16_t, 64>(p, st) : launch_qk<uint16_t, 128>(p, st);
+  return p.dk == 64 ? launch_qk<float, 64>(p, st) : launch_qk<float, 128>(p, st);
 }
 
 }  // namespace fwmem

@@ -1,0 +1,1057 @@
+// Chunk-parallel backward pass of the scan for the delta, inner and additive rules with a
+// scalar decay (phi identity or elu+1, QK normalisation, pre-activated gates, the
+// scale-coupled ridge), on fp32 MFMA. The pages give no backward pass; this is the
+// reverse-mode derivative of the chunk form of the forward recurrence ("Fast Weight
+// Attention for Continual Learning" reading notes, section 4.4: an intra-chunk
+// triangular solve, a short inter-chunk recurrence, parallel outputs), laid out the
+// same way: a parallel prep, one short serial recurrence per direction, and a parallel
+// gradient pass.
+//
+// Per head, chunks of C = 64 tokens; inside a chunk Gamma_t = a_1 ... a_t (the decays,
+// carried as a log-sum with a sign parity), Gamma_end the chunk's total, D_ts =
+// Gamma_t / Gamma_s (s <= t), D'_ts = Gamma_{t-1} / Gamma_s (s < t), eta the step size
+// (the write scale f = beta for the additive rule). With entry state S and exit S':
+//   L = diag(eta) (D' o X X^T),  T = (I + L)^-1,  M = D o (Q X^T)
+//   U = T diag(eta) (V - diag(Gamma_prev) X S)      (delta)    U = diag(f) V (inner, additive)
+//   O = diag(Gamma) Q S + M U,   S' = Gamma_end S + X^T diag(Gamma_end / Gamma) U.
+// Backward, from the exit gradient dS' and the chunk's dO:
+//   dU = M^T dO + diag(Gamma_end / Gamma) X dS',   dR = T^T dU (delta)
+//   dS = Gamma_end dS' + Q^T diag(Gamma) dO - X^T diag(eta Gamma_prev) dR
+// and the gradients of Q, X, V, eta and of the log decays, per chunk.
+//
+// Kernels:
+//   prep   (head, chunk): X, Q rows; token scalars; X X^T and Q X^T on MFMA; the masks;
+//          T = (I + L)^-1 (blocked, 16x16 diagonal blocks by substitution) -> record;
+//   state  (head, 32 value columns), serial over chunks: S at every chunk start;
+//   dstate (head, 32 value columns), serial from the last chunk: every chunk's exit
+//          gradient dS' and dL/dS_0;
+//   grad   (head, chunk): every input gradient, streaming 32-column value blocks.
+#include "fwmem_backward.h"
+#include "fwmem_device.h"
+#include "fwmem_internal.h"
+
+namespace fwmem {
+namespace {
+
+constexpr int CB = 64;        // tokens per chunk
+constexpr int LDC = CB + 4;   // row stride (floats) of an LDS tile with CB columns
+constexpr int NCOL = 32;      // value columns of a state workgroup and of a gradient block
+constexpr int LDU = NCOL + 4;  // row stride of a [CB][NCOL] LDS tile
+
+// Per-token scalars of a record ([kNSc][CB] floats).
+enum {
+  kScGam,    // Gamma_t
+  kScGprev,  // Gamma_{t-1}
+  kScGend,   // Gamma_end / Gamma_t
+  kScE,      // eta_t (the write scale f_t for the additive rule); 0 without a write
+  kScA,      // a_t, the decay
+  kScDen,    // eta's denominator |x_t|^2 + lambda_used + eps
+  kScLu,     // lambda_used (lambda_t, or lambda_t |x_t|^2 with the scale-coupled ridge)
+  kScN,      // |x_t|^2
+  kScBeta,   // beta_t (activated)
+  kScLam,    // lambda_t (activated; the retention for the additive rule)
+  kScKey,    // 1 where the token writes (a key exists and t < T), else 0
+  kScG,      // g_t = log|Gamma_t|
+  kScPar,    // sign parity of Gamma_t (0 or 1)
+  kNSc
+};
+
+struct BRec {
+  static constexpr size_t kT = 0;              // [CB][CB] T = (I + L)^-1 (delta rule)
+  static constexpr size_t kM = kT + CB * CB;   // [CB][CB] M = D o (Q X^T)
+  static constexpr size_t kLp = kM + CB * CB;  // [CB][CB] D' o (X X^T), strictly lower
+  static constexpr size_t kSc = kLp + CB * CB;
+  static constexpr size_t kMisc = kSc + (size_t)kNSc * CB;  // [0] Gamma_end
+  static constexpr size_t kFloats = (kMisc + 64 + 63) / 64 * 64;
+};
+
+// ---- fp32 MFMA tile products (v_mfma_f32_16x16x4f32). A 16x16 accumulator tile in C
+// layout holds rows 4g+i (i = 0..3) of column n in lane 16g+n. Instruction i of a K block
+// of 16 gives lane group g the K index 4g+i, for A and B alike, so the four instructions
+// cover the block whatever order the unit sums its K slots in.
+__device__ __forceinline__ void mfma4(f4& acc, const f4& a, const f4& b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+}
+
+// acc += A B over K in [k0, k1) (multiples of 16). A: AT == false: row r at a + r*lda with
+// K contiguous; AT == true: A[r][k] = a[k*lda + r]. B: BN == false: column n at
+// b + n*ldb with K contiguous (B^T row-major); BN == true: B[k][n] = b[k*ldb + n].
+template <bool AT, bool BN>
+__device__ __forceinline__ void mm(f4& acc, const float* a, int lda, const float* b, int ldb, int k0, int k1,
+                                   int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  for (int k = k0; k < k1; k += 16) {
+    f4 av, bv;
+    if constexpr (AT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = a[(k + 4 * g + i) * lda + n];
+    } else {
+      av = *reinterpret_cast<const f4*>(a + n * lda + k + 4 * g);
+    }
+    if constexpr (BN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[i] = b[(k + 4 * g + i) * ldb + n];
+    } else {
+      bv = *reinterpret_cast<const f4*>(b + n * ldb + k + 4 * g);
+    }
+    mfma4(acc, av, bv);
+  }
+}
+
+// C-layout tile -> LDS: transposed (dst[col][row], one 16-byte store) or natural.
+__device__ __forceinline__ void store_t(float* dst, int ld, int r0, int c0, const f4& v, int lane) {
+  *reinterpret_cast<f4*>(dst + (c0 + (lane & 15)) * ld + r0 + 4 * (lane >> 4)) = v;
+}
+__device__ __forceinline__ void store_n(float* dst, int ld, int r0, int c0, const f4& v, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(r0 + 4 * (lane >> 4) + i) * ld + c0 + (lane & 15)] = v[i];
+}
+
+// Sum over the 16 lanes of a lane group (the 16 columns of a C-layout tile).
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float sgn(int par) { return par ? -1.f : 1.f; }
+
+// Written keys x_t and (WANT_Q) read queries phi(q_t) of chunk c as fp32 rows [CB][DK + 4]:
+// the shift to the previous token's key (and the carried key before a call's first token),
+// phi and QK normalisation applied; rows of tokens past T are zero. Ends with a barrier.
+template <typename InT, int DK, bool SHIFT, bool WANT_X, bool WANT_Q, int NTH>
+__device__ void stage_rows(const BwdParams& p, int bh, int c, float* Xs, float* Qs, bool has_in) {
+  constexpr int LDX = DK + 4, VW = 16 / (int)sizeof(InT), GPR = DK / VW;
+  const int tid = threadIdx.x;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const size_t rb = (size_t)bh * p.T;
+  const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
+  const InT* qb = static_cast<const InT*>(p.q) + rb * DK;
+  for (int idx = tid; idx < CB * GPR; idx += NTH) {
+    const int t = idx / GPR, i0 = (idx % GPR) * VW, tau = c * CB + t;
+    float x[VW], q[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) x[e] = q[e] = 0.f;
+    if (tau < p.T) {
+      if constexpr (WANT_X) {
+        if (SHIFT && tau == 0) {
+          if (has_in && p.xprev_in != nullptr) {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) x[e] = p.xprev_in[(size_t)bh * DK + i0 + e];  // phi applied
+          }
+        } else {
+          In<InT>::load(kb + (size_t)(SHIFT ? tau - 1 : tau) * DK + i0, x);
+          if (elu) {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+          }
+        }
+      }
+      if constexpr (WANT_Q) {
+        In<InT>::load(qb + (size_t)tau * DK + i0, q);
+        if (elu) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) q[e] = phi_elu1(q[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VW; e += 4) {
+      if (WANT_X) *reinterpret_cast<f4*>(Xs + t * LDX + i0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+      if (WANT_Q) *reinterpret_cast<f4*>(Qs + t * LDX + i0 + e) = f4{q[e], q[e + 1], q[e + 2], q[e + 3]};
+    }
+  }
+  __syncthreads();
+  const float len = qk_length(p.flags, DK);
+  if (len > 0.f) {
+    // QK normalisation: each row rescaled to length len by one wave
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int t = wave; t < CB; t += NTH / 64) {
+      float nx = 0.f, nq = 0.f;
+      for (int i = lane; i < DK; i += 64) {
+        if (WANT_X) nx += Xs[t * LDX + i] * Xs[t * LDX + i];
+        if (WANT_Q) nq += Qs[t * LDX + i] * Qs[t * LDX + i];
+      }
+      nx = wave_sum(nx);
+      nq = wave_sum(nq);
+      const float fx = rescale_factor(nx, len), fq = rescale_factor(nq, len);
+      for (int i = lane; i < DK; i += 64) {
+        if (WANT_X) Xs[t * LDX + i] *= fx;
+        if (WANT_Q) Qs[t * LDX + i] *= fq;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ bool head_has_key(const BwdParams& p, int bh) {
+  return p.has_in != nullptr && p.has_in[bh] != 0;
+}
+
+// ================================================================ prep: one (head, chunk)
+template <typename InT, int DK, int RULE>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, float* recs) {
+  using R = Rule<RULE>;
+  constexpr int LDX = DK + 4;
+  // X and Q rows; after the products Lp, M, T ([CB][LDC] each) and Y ([16][LDC])
+  constexpr int kRows = 2 * CB * LDX, kTiles = 3 * CB * LDC + 16 * LDC;
+  __shared__ __align__(16) float sm[kRows > kTiles ? kRows : kTiles];
+  __shared__ float s_g[CB], s_gp[CB], s_e[CB];
+  __shared__ int s_par[CB], s_parp[CB];
+  float* Xs = sm;
+  float* Qs = sm + CB * LDX;
+  const int nch = (p.T + CB - 1) / CB;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool has_in = head_has_key(p, bh);
+  float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+  float* sc = rec + BRec::kSc;
+  stage_rows<InT, DK, R::shift, true, true, 256>(p, bh, c, Xs, Qs, has_in);
+
+  if (wave == 0) {
+    const int t = lane, tau = c * CB + t;
+    const bool valid = tau < p.T;
+    float n = 0.f;
+    for (int i = 0; i < DK; ++i) n += Xs[t * LDX + i] * Xs[t * LDX + i];
+    const size_t gi = (size_t)bh * p.T + (size_t)(valid ? tau : 0);
+    const float beta = (valid && p.beta != nullptr) ? act_beta(p.beta[gi], p.flags) : 1.f;
+    const float lam = (valid && p.lam != nullptr) ? act_lam(p.lam[gi], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
+    float e, a, den = 1.f, lu = 0.f;
+    bool key;
+    if constexpr (R::nlms) {
+      key = valid && (tau >= 1 || has_in);
+      lu = (p.flags & kFlagLamScaled) ? lam * n : lam;
+      den = n + lu + p.eps;
+      e = key ? beta / den : 0.f;
+      a = key ? 1.f - e * lu : 1.f;
+    } else {
+      key = valid;
+      e = valid ? beta : 0.f;
+      a = valid ? lam : 1.f;
+    }
+    float la = log_abs_floor(a);
+    int ng = a < 0.f ? 1 : 0;
+    wave_prefix(la, ng);
+    const float gend = __shfl(la, 63);
+    const int pend = __shfl(ng, 63) & 1;
+    const int par = ng & 1;
+    // shuffles on every lane (a lane left out of a shuffle gives its readers no value)
+    const float lsh = __shfl_up(la, 1);
+    const int nsh = __shfl_up(ng, 1);
+    const float gprev = t > 0 ? lsh : 0.f;
+    const int pprev = t > 0 ? (nsh & 1) : 0;
+    s_g[t] = la;
+    s_gp[t] = gprev;
+    s_par[t] = par;
+    s_parp[t] = pprev;
+    s_e[t] = e;
+    sc[kScGam * CB + t] = sgn(par) * __expf(la);
+    sc[kScGprev * CB + t] = sgn(pprev) * __expf(gprev);
+    sc[kScGend * CB + t] = sgn(pend ^ par) * __expf(gend - la);
+    sc[kScE * CB + t] = e;
+    sc[kScA * CB + t] = a;
+    sc[kScDen * CB + t] = den;
+    sc[kScLu * CB + t] = lu;
+    sc[kScN * CB + t] = n;
+    sc[kScBeta * CB + t] = beta;
+    sc[kScLam * CB + t] = lam;
+    sc[kScKey * CB + t] = key ? 1.f : 0.f;
+    sc[kScG * CB + t] = la;
+    sc[kScPar * CB + t] = (float)par;
+    if (t == 0) rec[BRec::kMisc] = sgn(pend) * __expf(gend);
+  }
+
+  // X X^T (shifted-pair rules and the delta rule's solve) and Q X^T: the ten lower tiles of
+  // each, five per wave
+  constexpr int NPROD = R::solve ? 2 : 1;
+  constexpr int NTILE = 10 * NPROD;
+  f4 acc[5];
+  int tm[5], ts[5], tp[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int id = wave * 5 + k;
+    acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+    tp[k] = -1;
+    if (id < NTILE) {
+      const int prod = id / 10, tile = id % 10;
+      const int m = tile < 1 ? 0 : (tile < 3 ? 1 : (tile < 6 ? 2 : 3));
+      const int s = tile - m * (m + 1) / 2;
+      tm[k] = m;
+      ts[k] = s;
+      tp[k] = (NPROD == 1) ? 1 : prod;  // 0: X X^T, 1: Q X^T
+      mm<false, false>(acc[k], (tp[k] == 0 ? Xs : Qs) + 16 * m * LDX, LDX, Xs + 16 * s * LDX, LDX, 0, DK, lane);
+    }
+  }
+  __syncthreads();  // X and Q are no longer read; the scalars are in LDS
+
+  // masked tiles into LDS: Lp = D' o G (strictly lower), M = D o P (lower with diagonal)
+  float* Lps = sm;
+  float* Ms = sm + CB * LDC;
+  float* Ts = sm + 2 * CB * LDC;
+  float* Ys = sm + 3 * CB * LDC;  // [16][LDC]
+  for (int i = tid; i < (R::solve ? 3 : 1) * CB * LDC; i += 256) (R::solve ? sm : Ms)[i] = 0.f;
+  __syncthreads();
+  {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      if (tp[k] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tm[k] + 4 * g + i, s = 16 * ts[k] + n;
+        if (tp[k] == 0) {
+          if (s < t) Lps[t * LDC + s] = sgn(s_parp[t] ^ s_par[s]) * __expf(s_gp[t] - s_g[s]) * acc[k][i];
+        } else {
+          if (s <= t) Ms[t * LDC + s] = sgn(s_par[t] ^ s_par[s]) * __expf(s_g[t] - s_g[s]) * acc[k][i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  if constexpr (R::solve) {
+    // T = (I + L)^-1 with L_ts = eta_t Lp_ts. Diagonal 16x16 blocks: wave b, lane j < 16
+    // substitutes down column j of block b.
+    if (lane < 16) {
+      const int b = wave, j = lane;
+      for (int r = 0; r < 16; ++r) {
+        const int tr = 16 * b + r;
+        float v = r == j ? 1.f : 0.f;
+        for (int k = j; k < r; ++k) v -= s_e[tr] * Lps[tr * LDC + 16 * b + k] * Ts[(16 * b + k) * LDC + 16 * b + j];
+        Ts[tr * LDC + 16 * b + j] = r >= j ? v : 0.f;
+      }
+    }
+    __syncthreads();
+    // below the diagonal, by row blocks: T_i,: = -T_ii (sum_{k<i} L_ik T_k,:)
+    for (int ib = 1; ib < 4; ++ib) {
+      const int ncol = 16 * ib;
+      for (int e = tid; e < 16 * ncol; e += 256) {
+        const int r = e / ncol, col = e % ncol, tr = 16 * ib + r;
+        float y = 0.f;
+        for (int k = col; k < ncol; ++k) y += Lps[tr * LDC + k] * Ts[k * LDC + col];
+        Ys[r * LDC + col] = s_e[tr] * y;
+      }
+      __syncthreads();
+      for (int e = tid; e < 16 * ncol; e += 256) {
+        const int r = e / ncol, col = e % ncol, tr = 16 * ib + r;
+        float y = 0.f;
+        for (int m = 0; m <= r; ++m) y += Ts[tr * LDC + 16 * ib + m] * Ys[m * LDC + col];
+        Ts[tr * LDC + col] = -y;
+      }
+      __syncthreads();
+    }
+  }
+
+  // the record: T and Lp (delta rule), M
+  for (int e = tid; e < CB * CB / 4; e += 256) {
+    const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+    *reinterpret_cast<f4*>(rec + BRec::kM + r * CB + c4) = *reinterpret_cast<const f4*>(Ms + r * LDC + c4);
+    if constexpr (R::solve) {
+      *reinterpret_cast<f4*>(rec + BRec::kT + r * CB + c4) = *reinterpret_cast<const f4*>(Ts + r * LDC + c4);
+      *reinterpret_cast<f4*>(rec + BRec::kLp + r * CB + c4) = *reinterpret_cast<const f4*>(Lps + r * LDC + c4);
+    }
+  }
+}
+
+// Workgroup -> (head, 32-column group) of the serial kernels: the groups of one head sit on
+// one XCD (blocks are dealt round-robin over the 8 XCDs) and share its L2.
+__device__ __forceinline__ bool state_block(const BwdParams& p, int ngrp, int& bh, int& grp) {
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  grp = slot % ngrp;
+  bh = (slot / ngrp) * 8 + xcd;
+  return bh < p.BH;
+}
+
+// ====================================================== state: S at every chunk start
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float* recs, float* Sch) {
+  using R = Rule<RULE>;
+  constexpr int LDX = DK + 4, NRT = DK / 16, RPW = NRT / 4;  // row tiles of S per wave
+  __shared__ __align__(16) float Xs[CB * LDX];
+  __shared__ __align__(16) float Ts[R::solve ? CB * LDC : 4];
+  __shared__ __align__(16) float Bt[NCOL * LDX];  // S^T [NCOL][DK], then W^T [NCOL][LDC]
+  __shared__ __align__(16) float Rt[R::solve ? NCOL * LDC : 4];
+  __shared__ __align__(16) float s_fac[4][CB];  // eta Gamma_prev, eta (or f), Gamma_end / Gamma; [3][0] Gamma_end
+  int bh, grp;
+  if (!state_block(p, DV / NCOL, bh, grp)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int nch = (p.T + CB - 1) / CB;
+  const bool has_in = head_has_key(p, bh);
+  const int col0 = grp * NCOL;
+  const size_t SS = (size_t)DK * DV;
+
+  f4 S[RPW][2];
+#pragma unroll
+  for (int a = 0; a < RPW; ++a)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (w + 4 * a) + 4 * g + i;
+        S[a][ct][i] = p.S_in != nullptr ? p.S_in[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * ct + n] : 0.f;
+      }
+  const InT* vb = static_cast<const InT*>(p.v) + (size_t)bh * p.T * DV;
+
+  for (int c = 0; c < nch; ++c) {
+    float* Sc = Sch + ((size_t)bh * nch + c) * SS;
+#pragma unroll
+    for (int a = 0; a < RPW; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Sc[(size_t)(16 * (w + 4 * a) + 4 * g + i) * DV + col0 + 16 * ct + n] = S[a][ct][i];
+    if (c + 1 == nch) break;  // the state after the last chunk is not needed
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    __syncthreads();  // the previous chunk's LDS reads are done
+    if constexpr (R::solve) {
+      for (int e = tid; e < CB * CB / 4; e += 256) {
+        const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+        *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4);
+      }
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      const float e = sc[kScE * CB + tid];
+      s_fac[0][tid] = e * sc[kScGprev * CB + tid];
+      s_fac[1][tid] = e;
+      s_fac[2][tid] = sc[kScGend * CB + tid];
+      if (tid == 0) s_fac[3][0] = rec[BRec::kMisc];
+    }
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int a = 0; a < RPW; ++a)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDX, 16 * (w + 4 * a), 16 * ct, S[a][ct], lane);
+    }
+    stage_rows<InT, DK, R::shift, true, false, 256>(p, bh, c, Xs, nullptr, has_in);
+
+    // this wave's token tile w: values, then W = fU U with U = T R (delta) or fV V
+    float vv[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tau = c * CB + 16 * w + 4 * g + i;
+        vv[ct][i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + col0 + 16 * ct + n) : 0.f;
+      }
+    f4 W[2];
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f4 xs = {0.f, 0.f, 0.f, 0.f};
+        mm<false, false>(xs, Xs + 16 * w * LDX, LDX, Bt + 16 * ct * LDX, LDX, 0, DK, lane);
+        f4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * w + 4 * g + i;
+          r[i] = s_fac[1][t] * vv[ct][i] - s_fac[0][t] * xs[i];
+        }
+        store_t(Rt, LDC, 16 * w, 16 * ct, r, lane);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f4 u = {0.f, 0.f, 0.f, 0.f};
+        mm<false, false>(u, Ts + 16 * w * LDC, LDC, Rt + 16 * ct * LDC, LDC, 0, 16 * w + 16, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) W[ct][i] = s_fac[2][16 * w + 4 * g + i] * u[i];
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * w + 4 * g + i;
+          W[ct][i] = s_fac[2][t] * s_fac[1][t] * vv[ct][i];
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDC, 16 * w, 16 * ct, W[ct], lane);
+    __syncthreads();
+    // S' = Gamma_end S + X^T W
+    const float gend = s_fac[3][0];
+#pragma unroll
+    for (int a = 0; a < RPW; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        S[a][ct] *= gend;
+        mm<true, false>(S[a][ct], Xs + 16 * (w + 4 * a), LDX, Bt + 16 * ct * LDC, LDC, 0, CB, lane);
+      }
+  }
+}
+
+// ================================================= dstate: the exit gradient of every chunk
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const float* recs, float* dSch) {
+  using R = Rule<RULE>;
+  constexpr int LDX = DK + 4, NRT = DK / 16;
+  // dS tiles: 2 * NRT over 8 waves (DK 128: row tile w, both column tiles; DK 64: row tile
+  // w % 4, column tile w / 4)
+  constexpr int NTW = NRT / 4;
+  __shared__ __align__(16) float Xs[CB * LDX];
+  __shared__ __align__(16) float Qs[CB * LDX];
+  __shared__ __align__(16) float Ts[R::solve ? CB * LDC : 4];
+  __shared__ __align__(16) float Ms[CB * LDC];
+  __shared__ __align__(16) float dOt[NCOL * LDC];  // dO^T of the column group
+  __shared__ __align__(16) float Bt[NCOL * LDX];   // dS^T, then (delta) (eta Gamma_prev dR)^T
+  __shared__ __align__(16) float dUt[R::solve ? NCOL * LDC : 4];
+  __shared__ __align__(16) float s_fac[4][CB];  // Gamma, eta Gamma_prev, Gamma_end / Gamma; [3][0] Gamma_end
+  int bh, grp;
+  if (!state_block(p, DV / NCOL, bh, grp)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int nch = (p.T + CB - 1) / CB;
+  const bool has_in = head_has_key(p, bh);
+  const int col0 = grp * NCOL;
+  const size_t SS = (size_t)DK * DV;
+  auto tile_rt = [&](int a) { return NTW == 2 ? w : (w & 3); };
+  auto tile_ct = [&](int a) { return NTW == 2 ? a : (w >> 2); };
+
+  f4 dS[NTW];
+#pragma unroll
+  for (int a = 0; a < NTW; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tile_rt(a) + 4 * g + i;
+      dS[a][i] = p.dS_out != nullptr ? p.dS_out[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * tile_ct(a) + n] : 0.f;
+    }
+  const int m = w & 3, ctw = w >> 2;  // this wave's (token tile, column tile) of dU and dR
+
+  for (int c = nch - 1; c >= 0; --c) {
+    float* dSc = dSch + ((size_t)bh * nch + c) * SS;
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dSc[(size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    __syncthreads();
+    for (int e = tid; e < CB * CB / 4; e += 512) {
+      const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+      *reinterpret_cast<f4*>(Ms + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kM + r * CB + c4);
+      if constexpr (R::solve)
+        *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4);
+    }
+    for (int e = tid; e < CB * NCOL; e += 512) {
+      const int t = e / NCOL, v = e % NCOL, tau = c * CB + t;
+      dOt[v * LDC + t] = tau < p.T ? p.dout[((size_t)bh * p.T + tau) * DV + col0 + v] : 0.f;
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      s_fac[0][tid] = sc[kScGam * CB + tid];
+      s_fac[1][tid] = sc[kScE * CB + tid] * sc[kScGprev * CB + tid];
+      s_fac[2][tid] = sc[kScGend * CB + tid];
+      if (tid == 0) s_fac[3][0] = rec[BRec::kMisc];
+    }
+#pragma unroll
+    for (int a = 0; a < NTW; ++a) store_t(Bt, LDX, 16 * tile_rt(a), 16 * tile_ct(a), dS[a], lane);
+    stage_rows<InT, DK, R::shift, true, true, 512>(p, bh, c, Xs, Qs, has_in);
+
+    if constexpr (R::solve) {
+      // dU = M^T dO + (Gamma_end / Gamma) X dS' for token tile m, column tile ctw (only the
+      // delta rule's state gradient goes through the writes)
+      f4 du = {0.f, 0.f, 0.f, 0.f};
+      mm<false, false>(du, Xs + 16 * m * LDX, LDX, Bt + 16 * ctw * LDX, LDX, 0, DK, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] *= s_fac[2][16 * m + 4 * g + i];
+      mm<true, false>(du, Ms + 16 * m, LDC, dOt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+      store_t(dUt, LDC, 16 * m, 16 * ctw, du, lane);
+      __syncthreads();  // dU complete; dS^T no longer read
+      f4 dr = {0.f, 0.f, 0.f, 0.f};
+      mm<true, false>(dr, Ts + 16 * m, LDC, dUt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dr[i] *= s_fac[1][16 * m + 4 * g + i];
+      store_t(Bt, LDC, 16 * m, 16 * ctw, dr, lane);
+      __syncthreads();
+    }
+    // dS = Gamma_end dS' + Q^T diag(Gamma) dO - X^T (eta Gamma_prev dR)
+    const float gend = s_fac[3][0];
+#pragma unroll
+    for (int a = 0; a < NTW; ++a) {
+      const int rt = tile_rt(a), ct = tile_ct(a);
+      dS[a] *= gend;
+      for (int k = 0; k < CB; k += 16) {
+        f4 av, bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = Qs[(k + 4 * g + i) * LDX + 16 * rt + n];
+        bv = *reinterpret_cast<const f4*>(dOt + (16 * ct + n) * LDC + k + 4 * g) *
+             *reinterpret_cast<const f4*>(&s_fac[0][k + 4 * g]);
+        mfma4(dS[a], av, bv);
+      }
+      if constexpr (R::solve) {
+        f4 t = {0.f, 0.f, 0.f, 0.f};
+        mm<true, false>(t, Xs + 16 * rt, LDX, Bt + 16 * ct * LDC, LDC, 0, CB, lane);
+        dS[a] -= t;
+      }
+    }
+  }
+  if (p.gS0 != nullptr) {
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.gS0[(size_t)bh * SS + (size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
+    if (grp == 0 && tid == 0 && p.gh0 != nullptr) p.gh0[bh] = 0;
+  }
+}
+
+// ==================================================== grad: every gradient of one chunk
+// Partial per-token sums, each slot written by one lane per token (no atomics).
+enum {
+  kPdQ0, kPdQ1,      // q_t . dQ1_t (two halves of the d_k tiles)
+  kPdXR0, kPdXR1,    // x_t . dXR_t (to the log decay of token t-1)
+  kPh0, kPh1,        // h_t = x_t . dXS_t
+  kPMr,              // row sums of dMm o M
+  kPMc0,             // column sums of dMm o M by the wave of row tile 0..3 (4 slots)
+  kPLr = kPMc0 + 4,  // row sums of dLm o L (to token t-1)
+  kPLc0,             // column sums of dLm o L (4 slots)
+  kPeL = kPLc0 + 4,  // row sums of dLm o Lp (eta's gradient through L)
+  kPe0, kPe1,        // eta's (or f's) gradient through the values, by column tile
+  kNP
+};
+
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float* recs, const float* Sch,
+                                                        const float* dSch) {
+  using R = Rule<RULE>;
+  constexpr bool SOLVE = R::solve;
+  constexpr int LDX = DK + 4, NDT = DK / 16, DPW = NDT / 2;  // d_k tiles per wave
+  constexpr int NBLK = DV / NCOL;
+  // LDS: X, T, M, and a region for one value block (phase 1) or Q, A1, W (phase 2)
+  constexpr int kBlk1 = 2 * NCOL * LDX + 3 * NCOL * LDC + 2 * CB * LDU;
+  constexpr int kBlk2 = CB * LDX + 2 * CB * LDC;
+  constexpr int kBlk = kBlk1 > kBlk2 ? kBlk1 : kBlk2;
+  __shared__ __align__(16) float Xs[CB * LDX];
+  __shared__ __align__(16) float Ts[SOLVE ? CB * LDC : 4];  // T, then Lp
+  __shared__ __align__(16) float Ms[CB * LDC];
+  __shared__ __align__(16) float blk[kBlk];
+  __shared__ float s_sc[kNSc][CB];
+  __shared__ float s_p[kNP][CB];
+  __shared__ float s_dn[CB];
+  __shared__ float s_red[8];
+  float* St = blk;                     // S^T of the block [NCOL][DK]
+  float* dSt = St + NCOL * LDX;        // dS'^T
+  float* dOt = dSt + NCOL * LDX;       // dO^T [NCOL][CB]
+  float* Rt = dOt + NCOL * LDC;        // R^T (delta)
+  float* dUt = Rt + NCOL * LDC;        // dU^T (delta)
+  float* Un = dUt + NCOL * LDC;        // U [CB][NCOL]
+  float* dRn = Un + CB * LDU;          // dR [CB][NCOL] (delta)
+  float* Qs = blk;                     // phase 2: Q [CB][DK]
+  float* A1 = blk + CB * LDX;          // dMm o D [CB][CB]
+  float* Wn = A1 + CB * LDC;           // dLm o eta D' [CB][CB] (delta)
+
+  const int nch = (p.T + CB - 1) / CB;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+  const bool has_in = head_has_key(p, bh);
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const int t0 = c * CB;
+  const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+  const float* Sc = Sch + ((size_t)bh * nch + c) * SS;
+  const float* dSc = dSch + ((size_t)bh * nch + c) * SS;
+  const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
+
+  for (int e = tid; e < CB * CB / 4; e += 512) {
+    const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+    *reinterpret_cast<f4*>(Ms + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kM + r * CB + c4);
+    if constexpr (SOLVE)
+      *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4);
+  }
+  for (int e = tid; e < kNSc * CB; e += 512) (&s_sc[0][0])[e] = rec[BRec::kSc + e];
+  for (int e = tid; e < kNP * CB; e += 512) (&s_p[0][0])[e] = 0.f;
+  stage_rows<InT, DK, R::shift, true, false, 512>(p, bh, c, Xs, nullptr, has_in);
+
+  const int m = w & 3, ctw = w >> 2;  // token tile and column tile of this wave's block outputs
+  // accumulators over the value blocks
+  f4 aMm[4], aQ1[DPW], aXR[DPW], aXS[DPW];  // aMm: dMm (w < 4) or dLm (w >= 4) tiles (m, s <= m)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aMm[s] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) aQ1[d] = aXR[d] = aXS[d] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 pe = {0.f, 0.f, 0.f, 0.f};  // eta's gradient through the values, this lane's rows
+  float sds = 0.f;               // <dS', S> partial
+
+  auto fac = [&](int k, int t) { return s_sc[k][t]; };
+
+  for (int jb = 0; jb < NBLK; ++jb) {
+    const int col0 = jb * NCOL;
+    // the block's S^T, dS'^T, dO^T
+    for (int e = tid; e < DK * NCOL / 4; e += 512) {
+      const int r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
+      const f4 s4 = *reinterpret_cast<const f4*>(Sc + (size_t)r * DV + col0 + v4);
+      const f4 d4 = *reinterpret_cast<const f4*>(dSc + (size_t)r * DV + col0 + v4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        St[(v4 + i) * LDX + r] = s4[i];
+        dSt[(v4 + i) * LDX + r] = d4[i];
+        sds += s4[i] * d4[i];
+      }
+    }
+    for (int e = tid; e < CB * NCOL; e += 512) {
+      const int t = e / NCOL, v = e % NCOL, tau = t0 + t;
+      dOt[v * LDC + t] = tau < p.T ? p.dout[(rb + tau) * DV + col0 + v] : 0.f;
+    }
+    float vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = t0 + 16 * m + 4 * g + i;
+      vv[i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + col0 + 16 * ctw + n) : 0.f;
+    }
+    __syncthreads();
+
+    f4 rhat;  // delta: V - Gamma_prev X S
+    if constexpr (SOLVE) {
+      f4 xs = {0.f, 0.f, 0.f, 0.f};
+      mm<false, false>(xs, Xs + 16 * m * LDX, LDX, St + 16 * ctw * LDX, LDX, 0, DK, lane);
+      f4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        rhat[i] = vv[i] - fac(kScGprev, t) * xs[i];
+        r[i] = fac(kScE, t) * rhat[i];
+      }
+      store_t(Rt, LDC, 16 * m, 16 * ctw, r, lane);
+    } else {
+      f4 u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = fac(kScE, 16 * m + 4 * g + i) * vv[i];
+      store_n(Un, LDU, 16 * m, 16 * ctw, u, lane);
+    }
+    // dU = M^T dO + (Gamma_end / Gamma) X dS'
+    f4 du = {0.f, 0.f, 0.f, 0.f};
+    mm<false, false>(du, Xs + 16 * m * LDX, LDX, dSt + 16 * ctw * LDX, LDX, 0, DK, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) du[i] *= fac(kScGend, 16 * m + 4 * g + i);
+    mm<true, false>(du, Ms + 16 * m, LDC, dOt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+    if constexpr (SOLVE) {
+      store_t(dUt, LDC, 16 * m, 16 * ctw, du, lane);
+      __syncthreads();
+      f4 u = {0.f, 0.f, 0.f, 0.f};
+      mm<false, false>(u, Ts + 16 * m * LDC, LDC, Rt + 16 * ctw * LDC, LDC, 0, 16 * m + 16, lane);
+      store_n(Un, LDU, 16 * m, 16 * ctw, u, lane);
+      f4 dr = {0.f, 0.f, 0.f, 0.f};
+      mm<true, false>(dr, Ts + 16 * m, LDC, dUt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+      store_n(dRn, LDU, 16 * m, 16 * ctw, dr, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i, tau = t0 + t;
+        pe[i] += dr[i] * rhat[i];
+        if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * dr[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i, tau = t0 + t;
+        pe[i] += du[i] * vv[i];
+        if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * du[i];
+      }
+    }
+    __syncthreads();
+
+    // accumulate over the block's columns: dMm = dO U^T (w < 4), dLm = -dR U^T (w >= 4),
+    // dQ1 = dO S^T, dXR = dR S^T, dXS = U dS'^T
+    if (w < 4) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s <= m) mm<true, false>(aMm[s], dOt + 16 * m, LDC, Un + 16 * s * LDU, LDU, 0, NCOL, lane);
+    } else if constexpr (SOLVE) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s <= m) mm<false, false>(aMm[s], dRn + 16 * m * LDU, LDU, Un + 16 * s * LDU, LDU, 0, NCOL, lane);
+    }
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dt = ctw * DPW + d;
+      mm<true, true>(aQ1[d], dOt + 16 * m, LDC, St + 16 * dt, LDX, 0, NCOL, lane);
+      if constexpr (SOLVE) mm<false, true>(aXR[d], dRn + 16 * m * LDU, LDU, St + 16 * dt, LDX, 0, NCOL, lane);
+      mm<false, true>(aXS[d], Un + 16 * m * LDU, LDU, dSt + 16 * dt, LDX, 0, NCOL, lane);
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2
+  // <dS', S> over the workgroup
+  sds = wave_sum(sds);
+  if (lane == 0) s_red[w] = sds;
+  // eta's (or f's) gradient through the values: this lane's four rows, summed over columns
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = sum16(pe[i]);
+    if (n == 0) s_p[kPe0 + ctw][16 * m + 4 * g + i] = v;
+  }
+  // row dots with the state-coupled terms, after their row factors
+  {
+    float pq[4] = {0.f, 0.f, 0.f, 0.f}, pr[4] = {0.f, 0.f, 0.f, 0.f}, ph[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        aQ1[d][i] *= fac(kScGam, t);
+        aXR[d][i] *= -fac(kScE, t) * fac(kScGprev, t);
+        aXS[d][i] *= fac(kScGend, t);
+        const float x = Xs[t * LDX + dc];
+        pr[i] += x * aXR[d][i];
+        ph[i] += x * aXS[d][i];
+      }
+    }
+    // q . dQ1 needs Q, staged below; keep the x dots now
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = sum16(pr[i]), h = sum16(ph[i]);
+      if (n == 0) {
+        s_p[kPdXR0 + ctw][16 * m + 4 * g + i] = r;
+        s_p[kPh0 + ctw][16 * m + 4 * g + i] = h;
+      }
+      pq[i] = 0.f;
+    }
+    __syncthreads();  // phase-1 block buffers free
+    stage_rows<InT, DK, R::shift, false, true, 512>(p, bh, c, nullptr, Qs, has_in);
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pq[i] += Qs[(16 * m + 4 * g + i) * LDX + dc] * aQ1[d][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q = sum16(pq[i]);
+      if (n == 0) s_p[kPdQ0 + ctw][16 * m + 4 * g + i] = q;
+    }
+  }
+  // A1 = dMm o D with the row and column sums of dMm o M (waves 0-3), W = dLm o eta D' with
+  // the row and column sums of dLm o L and the row sums of dLm o Lp (waves 4-7); Lp
+  // replaces T in LDS
+  if constexpr (SOLVE) {
+    __syncthreads();  // T no longer read
+    for (int e = tid; e < CB * CB / 4; e += 512) {
+      const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+      *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kLp + r * CB + c4);
+    }
+  }
+  for (int e = tid; e < CB * LDC; e += 512) {
+    A1[e] = 0.f;
+    if (SOLVE) Wn[e] = 0.f;
+  }
+  __syncthreads();
+  {
+    const float* gl = s_sc[kScG];
+    const float* pa = s_sc[kScPar];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f}, rs2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s > m) continue;
+      float cs = 0.f;
+      const int sc = 16 * s + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        if (w < 4) {
+          if (sc <= t) {
+            const float d = sgn((int)pa[t] ^ (int)pa[sc]) * __expf(gl[t] - gl[sc]);
+            const float v = aMm[s][i];
+            A1[t * LDC + sc] = v * d;
+            const float pm = v * Ms[t * LDC + sc];
+            rs[i] += pm;
+            cs += pm;
+          }
+        } else if constexpr (SOLVE) {
+          if (sc < t) {
+            const float dl = -aMm[s][i];  // dLm = -dR U^T (the waves accumulated dR U^T)
+            const float lp = Ts[t * LDC + sc];  // D'_ts (x_t . x_s)
+            const float e = fac(kScE, t);
+            const float dp = sgn((int)pa[t - 1] ^ (int)pa[sc]) * __expf(gl[t - 1] - gl[sc]);  // D'_ts
+            Wn[t * LDC + sc] = dl * e * dp;
+            rs[i] += dl * e * lp;   // dLm o L
+            rs2[i] += dl * lp;      // dLm o Lp
+            cs += dl * e * lp;
+          }
+        }
+      }
+      // column sums over this tile's 16 rows: the four lane groups
+      cs += __shfl_xor(cs, 16);
+      cs += __shfl_xor(cs, 32);
+      if (g == 0) {
+        if (w < 4) s_p[kPMc0 + m][sc] += cs;
+        else if (SOLVE) s_p[kPLc0 + m][sc] += cs;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = sum16(rs[i]), b = sum16(rs2[i]);
+      if (n == 0) {
+        const int t = 16 * m + 4 * g + i;
+        if (w < 4) s_p[kPMr][t] = a;
+        else if (SOLVE) {
+          s_p[kPLr][t] = a;
+          s_p[kPeL][t] = b;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // dQ = dQ1 + A1 X;  dX = dXR + dXS + A1^T Q + W X + W^T X (this wave: token tile m, d_k
+  // tiles ctw * DPW ...)
+  f4 dQ[DPW], dX[DPW];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int dt = ctw * DPW + d;
+    dQ[d] = aQ1[d];
+    mm<false, true>(dQ[d], A1 + 16 * m * LDC, LDC, Xs + 16 * dt, LDX, 0, 16 * m + 16, lane);
+    dX[d] = aXR[d] + aXS[d];
+    mm<true, true>(dX[d], A1 + 16 * m, LDC, Qs + 16 * dt, LDX, 16 * m, CB, lane);
+    if constexpr (SOLVE) {
+      mm<false, true>(dX[d], Wn + 16 * m * LDC, LDC, Xs + 16 * dt, LDX, 0, 16 * m + 16, lane);
+      mm<true, true>(dX[d], Wn + 16 * m, LDC, Xs + 16 * dt, LDX, 16 * m, CB, lane);
+    }
+  }
+
+  // the log decays' gradient, its suffix sums, and the scalar chain (wave 0, lane = token)
+  if (w == 0) {
+    const int t = lane;
+    const float hsum = wave_sum(s_p[kPh0][t] + s_p[kPh1][t]);
+    float dg = s_p[kPdQ0][t] + s_p[kPdQ1][t] - s_p[kPh0][t] - s_p[kPh1][t] + s_p[kPMr][t];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dg -= s_p[kPMc0 + k][t];
+    if (t + 1 < CB) dg += s_p[kPdXR0][t + 1] + s_p[kPdXR1][t + 1];
+    if constexpr (SOLVE) {
+      if (t + 1 < CB) dg += s_p[kPLr][t + 1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dg -= s_p[kPLc0 + k][t];
+    }
+    if (t == CB - 1) {
+      float sd = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sd += s_red[k];
+      dg += hsum + rec[BRec::kMisc] * sd;
+    }
+    // suffix sums: dl_t = sum_{t' >= t} dg_t'
+    float dl = dg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(dl, o);
+      if (t + o < 64) dl += y;
+    }
+    const float a = fac(kScA, t);
+    const float af = (a < 0.f ? -1.f : 1.f) * fmaxf(fabsf(a), 1e-30f);
+    const float da = dl / af;
+    const int tau = t0 + t;
+    float dn = 0.f;
+    if (tau < p.T) {
+      const float beta = fac(kScBeta, t), lam = fac(kScLam, t);
+      const bool key = fac(kScKey, t) != 0.f;
+      float gb = 0.f, gl = 0.f;
+      if constexpr (R::nlms) {
+        if (key) {
+          const float e = fac(kScE, t), den = fac(kScDen, t), lu = fac(kScLu, t), nx = fac(kScN, t);
+          float de = s_p[kPe0][t] + s_p[kPe1][t];
+          if (SOLVE) de += s_p[kPeL][t];
+          de -= lu * da;
+          gb = de / den;
+          const float dden = -e * de / den;
+          const float dlu = -e * da + dden;
+          const bool scaled = (p.flags & kFlagLamScaled) != 0;
+          dn = dden + (scaled ? lam * dlu : 0.f);
+          gl = dlu * (scaled ? nx : 1.f);
+        }
+      } else {
+        gb = s_p[kPe0][t] + s_p[kPe1][t];
+        gl = da;
+      }
+      // with pre-activated gates: the gradient with respect to the pre-activation
+      if (p.flags & kFlagBetaSig) gb *= beta * (1.f - beta);
+      else if (p.flags & kFlagBetaSig2) gb *= beta * (1.f - 0.5f * beta);
+      if (p.flags & kFlagLamAct) gl *= R::nlms ? -expm1f(-lam) : lam * (1.f - lam);
+      if (p.gbeta != nullptr) p.gbeta[rb + tau] = gb;
+      if (p.glam != nullptr) p.glam[rb + tau] = gl;
+    }
+    s_dn[t] = dn;
+  }
+  __syncthreads();
+
+  // the feature maps' derivative from the staged values y = phi(z): 1 for the identity;
+  // for elu+1, 1 where y > 1 (z > 0) and y = exp(z) elsewhere
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  auto dphi = [&](float y) { return elu ? (y > 1.f ? 1.f : y) : 1.f; };
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * m + 4 * g + i, tau = t0 + t;
+      const float x = Xs[t * LDX + dc];
+      const float gx = dX[d][i] + 2.f * s_dn[t] * x;
+      if (tau < p.T) p.gq[(rb + tau) * DK + dc] = dQ[d][i] * dphi(Qs[t * LDX + dc]);
+      if constexpr (R::shift) {
+        // x_t is the key of token tau - 1 (the carried key before the first token)
+        if (tau >= 1 && tau < p.T) p.gk[(rb + tau - 1) * DK + dc] = gx * dphi(x);
+        else if (tau == 0 && p.gx0 != nullptr) p.gx0[(size_t)bh * DK + dc] = has_in ? gx : 0.f;
+      } else {
+        if (tau < p.T) p.gk[(rb + tau) * DK + dc] = gx * dphi(x);
+      }
+    }
+  }
+  if constexpr (R::shift) {
+    // the last key is written by no step of this call
+    if (c == nch - 1)
+      for (int i = tid; i < DK; i += 512) p.gk[(rb + p.T - 1) * DK + i] = 0.f;
+  } else {
+    if (c == 0 && p.gx0 != nullptr)
+      for (int i = tid; i < DK; i += 512) p.gx0[(size_t)bh * DK + i] = 0.f;
+  }
+}
+
+template <typename InT, int DK, int DV, int RULE>
+hipError_t launch_rule(const BwdParams& p, float* ws, hipStream_t st) {
+  const int nch = (p.T + CB - 1) / CB;
+  const size_t nrec = (size_t)p.BH * nch;
+  float* recs = ws;
+  float* Sch = recs + nrec * BRec::kFloats;
+  float* dSch = Sch + nrec * (size_t)DK * DV;
+  const unsigned ngrid = (unsigned)(8 * (DV / NCOL) * ((p.BH + 7) / 8));
+  hipLaunchKernelGGL((bwd_prep_kernel<InT, DK, RULE>), dim3((unsigned)nrec), dim3(256), 0, st, p, recs);
+  hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch);
+  hipLaunchKernelGGL((bwd_dstate_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch);
+  hipLaunchKernelGGL((bwd_grad_kernel<InT, DK, DV, RULE>), dim3((unsigned)nrec), dim3(512), 0, st, p, recs, Sch,
+                     dSch);
+  return hipGetLastError();
+}
+
+template <typename InT, int DK, int DV>
+hipError_t launch_dims(const BwdParams& p, float* ws, hipStream_t st) {
+  if (p.rule == kRuleDelta) return launch_rule<InT, DK, DV, kRuleDelta>(p, ws, st);
+  if (p.rule == kRuleInner) return launch_rule<InT, DK, DV, kRuleInner>(p, ws, st);
+  return launch_rule<InT, DK, DV, kRuleAdditive>(p, ws, st);
+}
+
+template <typename InT>
+hipError_t launch_in(const BwdParams& p, float* ws, hipStream_t st) {
+  if (p.dk == 64 && p.dv == 64) return launch_dims<InT, 64, 64>(p, ws, st);
+  if (p.dk == 64 && p.dv == 128) return launch_dims<InT, 64, 128>(p, ws, st);
+  if (p.dk == 128 && p.dv == 64) return launch_dims<InT, 128, 64>(p, ws, st);
+  return launch_dims<InT, 128, 128>(p, ws, st);
+}
+
+}  // namespace
+
+bool bwd_chunked(int rule, uint32_t flags, int T) {
+  return T > 0 && (rule == kRuleDelta || rule == kRuleInner || rule == kRuleAdditive) &&
+         (flags & (kFlagPerChannel | kFlagZnorm)) == 0;
+}
+
+size_t bwd_chunk_floats_per_head(int T, int dk, int dv) {
+  const size_t nch = ((size_t)T + CB - 1) / CB;
+  return nch * (BRec::kFloats + 2 * (size_t)dk * (size_t)dv);
+}
+
+hipError_t launch_bwd_chunked(const BwdParams& p, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  const hipError_t e = p.bf16 ? launch_in<uint16_t>(p, p.ws, st) : launch_in<float>(p, p.ws, st);
+  if (e != hipSuccess) return e;
+  return launch_qk_norm_bwd(p, st);
+}
+
+}  // namespace fwmem
