@@ -423,10 +423,11 @@ def backward_supported(w):
 
 def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     """fwmem_scan_bwd on the same workload (grad_out ~ N(0,1), zero final-state gradient):
-    the time of one launch, averaged over `steps` launches bracketed by HIP events on the
-    kernel's stream. Algorithmic bytes per (token, head): q, k, v in their input type, the
-    gates, grad_out and the float32 gradients of q, k, v and the gates; per head the
-    initial-state gradient."""
+    the time of one call (all its kernels), averaged over `steps` calls bracketed by HIP
+    events on the kernels' stream. Algorithmic bytes per (token, head): q, k, v in their input
+    type, the gates, grad_out and the float32 gradients of q, k, v and the gates; per head the
+    initial-state gradient. `traffic` sums the counter records of the call's kernels while
+    every one of them is unchanged."""
     import torch
 
     from linear_attention_scan_amd import fwmem as F
@@ -467,19 +468,29 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(gk).all()), "non-finite gradient"
     ms = evs[0].elapsed_time(evs[1]) / steps
+    # the chunk-parallel kernels take the scalar-decay delta, inner and additive rules without
+    # the normaliser; every other mode runs the token-serial kernel
+    chunked = w.rule in (0, 1, 2) and not w.per_channel and not w.znorm
+    kernels = (["bwd_prep_kernel", "bwd_state_kernel", "bwd_dstate_kernel", "bwd_grad_kernel"]
+               if chunked else ["bwd_kernel"])
+    if w.qk_norm is not None:
+        kernels.append("qk_norm_bwd_kernel")
+    traffic = None
+    if all(measured_traffic(w.name, kname) is not None for kname in kernels):
+        traffic = sum(measured_traffic(w.name, kname) for kname in kernels)
     es = 2 if w.dtype == "bf16" else 4
     ngates = ((beta is not None) * (w.dv if w.rule == 3 else 1)
               + (lam is not None) * (w.dk if w.per_channel else 1))
     per_tok = (2 * w.dk + w.dv) * es + 4 * ngates + 4 * w.dv + 4 * (2 * w.dk + w.dv) + 4 * ngates
     nbytes = w.B * w.H * (w.T * per_tok + w.dk * w.dv * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kernel": "bwd_kernel", "steps": steps, "ms": round(ms, 4),
+    return {"path": "chunked" if chunked else "token-serial", "kernels": kernels,
+            "steps": steps, "ms": round(ms, 4),
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "workspace_bytes": ws_n,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
-                         "traffic": measured_traffic(w.name, "bwd_kernel"),
-                         "bytes_per_launch": nbytes}}
+                         "traffic": traffic, "bytes_per_launch": nbytes}}
 
 
 def bench_decode(steps, dev, stream):
