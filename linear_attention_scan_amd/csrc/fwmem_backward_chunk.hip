@@ -185,6 +185,61 @@ __device__ void stage_rows(const BwdParams& p, int bh, int c, float* Xs, float* 
   }
 }
 
+// Raw rows of one chunk held in registers between their load and their use, so that a
+// serial kernel loads chunk c+-1 while it computes chunk c. Thread tid holds 16-byte groups
+// tid + NTH j (j < NG) of the [CB][DK] row block; a row's GPR groups sit in GPR consecutive
+// lanes, so a row's squared norm is a sum over those lanes.
+template <typename InT, int DK, int NTH>
+struct Rows {
+  static constexpr int VW = 16 / (int)sizeof(InT), GPR = DK / VW, NG = CB * GPR / NTH;
+  static_assert(NG >= 1 && CB * GPR % NTH == 0, "row groups");
+  u32x4 w[NG];
+  uint32_t valid;
+  // rows src[tau] for tokens tau = tau0 + t, t < CB; zero where tau is outside [lo, hi)
+  __device__ __forceinline__ void load(const InT* src, int tau0, int lo, int hi) {
+    valid = 0;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW, tau = tau0 + t;
+      w[j] = u32x4{0u, 0u, 0u, 0u};
+      if (tau >= lo && tau < hi) {
+        w[j] = *reinterpret_cast<const u32x4*>(src + (size_t)tau * DK + i0);
+        valid |= 1u << j;
+      }
+    }
+  }
+  // fp32 rows into dst [CB][DK + 4]: phi = elu+1 on loaded rows (elu), row `patch` replaced
+  // by the vector pv (the carried key, phi applied; zero when pv is null), every row then
+  // rescaled to length len (QK normalisation, len > 0). Zero rows stay zero.
+  __device__ __forceinline__ void commit(float* dst, bool elu, float len, int patch, const float* pv) const {
+    constexpr int LDX = DK + 4;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW;
+      float x[VW];
+      In<InT>::decode(w[j], x);
+      if (t == patch) {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) x[e] = pv != nullptr ? pv[i0 + e] : 0.f;
+      } else if (elu && ((valid >> j) & 1u)) {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+      }
+      if (len > 0.f) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
+        ss = group_sum<GPR>(ss);
+        const float f = rescale_factor(ss, len);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) x[e] *= f;
+      }
+#pragma unroll
+      for (int e = 0; e < VW; e += 4) *reinterpret_cast<f4*>(dst + t * LDX + i0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+    }
+  }
+};
+
 __device__ __forceinline__ bool head_has_key(const BwdParams& p, int bh) {
   return p.has_in != nullptr && p.has_in[bh] != 0;
 }
@@ -197,7 +252,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, float* recs)
   // X and Q rows; after the products Lp, M, T ([CB][LDC] each) and Y ([16][LDC])
   constexpr int kRows = 2 * CB * LDX, kTiles = 3 * CB * LDC + 16 * LDC;
   __shared__ __align__(16) float sm[kRows > kTiles ? kRows : kTiles];
-  __shared__ float s_g[CB], s_gp[CB], s_e[CB];
+  __shared__ float s_g[CB], s_gp[CB], s_e[CB], s_n[CB];
   __shared__ int s_par[CB], s_parp[CB];
   float* Xs = sm;
   float* Qs = sm + CB * LDX;
@@ -209,11 +264,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, float* recs)
   float* sc = rec + BRec::kSc;
   stage_rows<InT, DK, R::shift, true, true, 256>(p, bh, c, Xs, Qs, has_in);
 
+  {
+    // |x_t|^2: four threads a row
+    const int t = tid >> 2, part = tid & 3;
+    float nn = 0.f;
+#pragma unroll 8
+    for (int i = part; i < DK; i += 4) nn += Xs[t * LDX + i] * Xs[t * LDX + i];
+    nn += __shfl_xor(nn, 1);
+    nn += __shfl_xor(nn, 2);
+    if (part == 0) s_n[t] = nn;
+  }
+  __syncthreads();
   if (wave == 0) {
     const int t = lane, tau = c * CB + t;
     const bool valid = tau < p.T;
-    float n = 0.f;
-    for (int i = 0; i < DK; ++i) n += Xs[t * LDX + i] * Xs[t * LDX + i];
+    const float n = s_n[t];
     const size_t gi = (size_t)bh * p.T + (size_t)(valid ? tau : 0);
     const float beta = (valid && p.beta != nullptr) ? act_beta(p.beta[gi], p.flags) : 1.f;
     const float lam = (valid && p.lam != nullptr) ? act_lam(p.lam[gi], p.flags, R::nlms) : (R::nlms ? 0.f : 1.f);
@@ -312,32 +377,37 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, float* recs)
 
   if constexpr (R::solve) {
     // T = (I + L)^-1 with L_ts = eta_t Lp_ts. Diagonal 16x16 blocks: wave b, lane j < 16
-    // substitutes down column j of block b.
+    // substitutes down column j of block b, the column in registers.
     if (lane < 16) {
       const int b = wave, j = lane;
+      float col[16];
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tr = 16 * b + r;
-        float v = r == j ? 1.f : 0.f;
-        for (int k = j; k < r; ++k) v -= s_e[tr] * Lps[tr * LDC + 16 * b + k] * Ts[(16 * b + k) * LDC + 16 * b + j];
-        Ts[tr * LDC + 16 * b + j] = r >= j ? v : 0.f;
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < r; ++k) v += Lps[tr * LDC + 16 * b + k] * col[k];
+        col[r] = r < j ? 0.f : (r == j ? 1.f : -s_e[tr] * v);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Ts[(16 * b + r) * LDC + 16 * b + j] = col[r];
     }
     __syncthreads();
-    // below the diagonal, by row blocks: T_i,: = -T_ii (sum_{k<i} L_ik T_k,:)
+    // below the diagonal, by row blocks i: Y_j = diag(eta) sum_{k<i} Lp_ik T_kj, then
+    // T_ij = -T_ii Y_j, one 16x16 tile j < i per wave on MFMA
     for (int ib = 1; ib < 4; ++ib) {
-      const int ncol = 16 * ib;
-      for (int e = tid; e < 16 * ncol; e += 256) {
-        const int r = e / ncol, col = e % ncol, tr = 16 * ib + r;
-        float y = 0.f;
-        for (int k = col; k < ncol; ++k) y += Lps[tr * LDC + k] * Ts[k * LDC + col];
-        Ys[r * LDC + col] = s_e[tr] * y;
+      if (wave < ib) {
+        f4 y = {0.f, 0.f, 0.f, 0.f};
+        mm<false, true>(y, Lps + 16 * ib * LDC, LDC, Ts + 16 * wave, LDC, 16 * wave, 16 * ib, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] *= s_e[16 * ib + 4 * (lane >> 4) + i];
+        store_n(Ys, LDC, 0, 16 * wave, y, lane);
       }
       __syncthreads();
-      for (int e = tid; e < 16 * ncol; e += 256) {
-        const int r = e / ncol, col = e % ncol, tr = 16 * ib + r;
-        float y = 0.f;
-        for (int m = 0; m <= r; ++m) y += Ts[tr * LDC + 16 * ib + m] * Ys[m * LDC + col];
-        Ts[tr * LDC + col] = -y;
+      if (wave < ib) {
+        f4 t = {0.f, 0.f, 0.f, 0.f};
+        mm<false, true>(t, Ts + 16 * ib * LDC + 16 * ib, LDC, Ys + 16 * wave, LDC, 0, 16, lane);
+        store_n(Ts, LDC, 16 * ib, 16 * wave, -t, lane);
       }
       __syncthreads();
     }
@@ -364,22 +434,31 @@ __device__ __forceinline__ bool state_block(const BwdParams& p, int ngrp, int& b
 }
 
 // ====================================================== state: S at every chunk start
+// Chunk c+1's rows, record and values are loaded into registers while chunk c computes.
 template <typename InT, int DK, int DV, int RULE>
-__global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float* recs, float* Sch) {
+__global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float* recs, float* Sch, float* Rh) {
   using R = Rule<RULE>;
   constexpr int LDX = DK + 4, NRT = DK / 16, RPW = NRT / 4;  // row tiles of S per wave
+  constexpr int VWv = 16 / (int)sizeof(InT), NVG = CB * NCOL / VWv;  // value groups
+  constexpr int NVJ = (NVG + 255) / 256;
   __shared__ __align__(16) float Xs[CB * LDX];
   __shared__ __align__(16) float Ts[R::solve ? CB * LDC : 4];
   __shared__ __align__(16) float Bt[NCOL * LDX];  // S^T [NCOL][DK], then W^T [NCOL][LDC]
   __shared__ __align__(16) float Rt[R::solve ? NCOL * LDC : 4];
-  __shared__ __align__(16) float s_fac[4][CB];  // eta Gamma_prev, eta (or f), Gamma_end / Gamma; [3][0] Gamma_end
+  __shared__ __align__(16) float Vs[CB * LDU];    // the chunk's values [CB][NCOL]
+  // eta Gamma_prev, eta (or f), Gamma_end / Gamma, Gamma_prev; [4][0] Gamma_end
+  __shared__ float s_fac[5][CB];
   int bh, grp;
   if (!state_block(p, DV / NCOL, bh, grp)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
   const int nch = (p.T + CB - 1) / CB;
   const bool has_in = head_has_key(p, bh);
   const int col0 = grp * NCOL;
-  const size_t SS = (size_t)DK * DV;
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
+  const InT* vb = static_cast<const InT*>(p.v) + rb * DV + col0;
 
   f4 S[RPW][2];
 #pragma unroll
@@ -391,7 +470,63 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
         const int r = 16 * (w + 4 * a) + 4 * g + i;
         S[a][ct][i] = p.S_in != nullptr ? p.S_in[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * ct + n] : 0.f;
       }
-  const InT* vb = static_cast<const InT*>(p.v) + (size_t)bh * p.T * DV;
+
+  // registers of the next chunk: rows, T (16 floats a thread), values, scalars
+  Rows<InT, DK, 256> rows;
+  f4 pt[4];
+  u32x4 pv[NVJ];
+  float pf[5];
+  auto load = [&](int c) {
+    // row t is the key of token c CB + t - 1 for the shifted pair (token 0's is the carried key)
+    rows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 16 * tid + 4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < NVJ; ++j) {
+      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv, tau = c * CB + t;
+      pv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < NVG && tau < p.T) pv[j] = *reinterpret_cast<const u32x4*>(vb + (size_t)tau * DV + v0);
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      const float e = sc[kScE * CB + tid];
+      pf[0] = e * sc[kScGprev * CB + tid];
+      pf[1] = e;
+      pf[2] = sc[kScGend * CB + tid];
+      pf[3] = sc[kScGprev * CB + tid];
+      pf[4] = rec[BRec::kMisc];
+    }
+  };
+  auto commit = [&](int c) {
+    // the carried key (phi applied) before the call's first token
+    const float* x0 = (R::shift && has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+    rows.commit(Xs, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<f4*>(Ts + (tid >> 2) * LDC + 16 * (tid & 3) + 4 * j) = pt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NVJ; ++j) {
+      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv;
+      if (idx < NVG) {
+        float x[VWv];
+        In<InT>::decode(pv[j], x);
+#pragma unroll
+        for (int e = 0; e < VWv; e += 4) *reinterpret_cast<f4*>(Vs + t * LDU + v0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+      }
+    }
+    if (tid < CB) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s_fac[k][tid] = pf[k];
+      if (tid == 0) s_fac[4][0] = pf[4];
+    }
+  };
+  // the delta rule needs every chunk's data (R-hat of the last chunk too), the others
+  // every chunk's but the last
+  if (R::solve || nch > 1) load(0);
 
   for (int c = 0; c < nch; ++c) {
     float* Sc = Sch + ((size_t)bh * nch + c) * SS;
@@ -402,42 +537,23 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           Sc[(size_t)(16 * (w + 4 * a) + 4 * g + i) * DV + col0 + 16 * ct + n] = S[a][ct][i];
-    if (c + 1 == nch) break;  // the state after the last chunk is not needed
-    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    if (!R::solve && c + 1 == nch) break;  // the state after the last chunk is not needed
     __syncthreads();  // the previous chunk's LDS reads are done
-    if constexpr (R::solve) {
-      for (int e = tid; e < CB * CB / 4; e += 256) {
-        const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
-        *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4);
-      }
-    }
-    if (tid < CB) {
-      const float* sc = rec + BRec::kSc;
-      const float e = sc[kScE * CB + tid];
-      s_fac[0][tid] = e * sc[kScGprev * CB + tid];
-      s_fac[1][tid] = e;
-      s_fac[2][tid] = sc[kScGend * CB + tid];
-      if (tid == 0) s_fac[3][0] = rec[BRec::kMisc];
-    }
+    commit(c);
     if constexpr (R::solve) {
 #pragma unroll
       for (int a = 0; a < RPW; ++a)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDX, 16 * (w + 4 * a), 16 * ct, S[a][ct], lane);
     }
-    stage_rows<InT, DK, R::shift, true, false, 256>(p, bh, c, Xs, nullptr, has_in);
+    __syncthreads();
+    if (c + 1 < nch && (R::solve || c + 2 < nch)) load(c + 1);
 
-    // this wave's token tile w: values, then W = fU U with U = T R (delta) or fV V
-    float vv[2][4];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tau = c * CB + 16 * w + 4 * g + i;
-        vv[ct][i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + col0 + 16 * ct + n) : 0.f;
-      }
+    // this wave's token tile w: W = fU U with U = T R (delta) or fV V
     f4 W[2];
     if constexpr (R::solve) {
+      // R-hat = V - Gamma_prev X S, kept for the gradient pass, and R = eta R-hat
+      float* rh = Rh + ((size_t)bh * nch + c) * CB * DV + col0;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         f4 xs = {0.f, 0.f, 0.f, 0.f};
@@ -446,10 +562,13 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * w + 4 * g + i;
-          r[i] = s_fac[1][t] * vv[ct][i] - s_fac[0][t] * xs[i];
+          const float rhat = Vs[t * LDU + 16 * ct + n] - s_fac[3][t] * xs[i];
+          rh[(size_t)t * DV + 16 * ct + n] = rhat;
+          r[i] = s_fac[1][t] * rhat;
         }
         store_t(Rt, LDC, 16 * w, 16 * ct, r, lane);
       }
+      if (c + 1 == nch) break;  // the state after the last chunk is not needed
       __syncthreads();
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -464,14 +583,14 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * w + 4 * g + i;
-          W[ct][i] = s_fac[2][t] * s_fac[1][t] * vv[ct][i];
+          W[ct][i] = s_fac[2][t] * s_fac[1][t] * Vs[t * LDU + 16 * ct + n];
         }
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDC, 16 * w, 16 * ct, W[ct], lane);
     __syncthreads();
     // S' = Gamma_end S + X^T W
-    const float gend = s_fac[3][0];
+    const float gend = s_fac[4][0];
 #pragma unroll
     for (int a = 0; a < RPW; ++a)
 #pragma unroll
@@ -483,8 +602,9 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
 }
 
 // ================================================= dstate: the exit gradient of every chunk
+// Chunk c-1's rows, records and dO are loaded into registers while chunk c computes.
 template <typename InT, int DK, int DV, int RULE>
-__global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const float* recs, float* dSch) {
+__global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const float* recs, float* dSch, float* dRw) {
   using R = Rule<RULE>;
   constexpr int LDX = DK + 4, NRT = DK / 16;
   // dS tiles: 2 * NRT over 8 waves (DK 128: row tile w, both column tiles; DK 64: row tile
@@ -493,7 +613,7 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
   __shared__ __align__(16) float Xs[CB * LDX];
   __shared__ __align__(16) float Qs[CB * LDX];
   __shared__ __align__(16) float Ts[R::solve ? CB * LDC : 4];
-  __shared__ __align__(16) float Ms[CB * LDC];
+  __shared__ __align__(16) float Ms[R::solve ? CB * LDC : 4];
   __shared__ __align__(16) float dOt[NCOL * LDC];  // dO^T of the column group
   __shared__ __align__(16) float Bt[NCOL * LDX];   // dS^T, then (delta) (eta Gamma_prev dR)^T
   __shared__ __align__(16) float dUt[R::solve ? NCOL * LDC : 4];
@@ -504,7 +624,12 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
   const int nch = (p.T + CB - 1) / CB;
   const bool has_in = head_has_key(p, bh);
   const int col0 = grp * NCOL;
-  const size_t SS = (size_t)DK * DV;
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
+  const InT* qb = static_cast<const InT*>(p.q) + rb * DK;
+  const float* dob = p.dout + rb * DV + col0;
   auto tile_rt = [&](int a) { return NTW == 2 ? w : (w & 3); };
   auto tile_ct = [&](int a) { return NTW == 2 ? a : (w >> 2); };
 
@@ -518,6 +643,58 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
     }
   const int m = w & 3, ctw = w >> 2;  // this wave's (token tile, column tile) of dU and dR
 
+  // registers of the next chunk: X and Q rows, T and M (8 floats a thread each), dO (4), scalars
+  Rows<InT, DK, 512> xrows, qrows;
+  f4 pt[2], pm[2], pd;
+  float pf[4];
+  auto load = [&](int c) {
+    xrows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
+    qrows.load(qb, c * CB, 0, p.T);
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 8 * tid + 4 * j);
+        pm[j] = *reinterpret_cast<const f4*>(rec + BRec::kM + 8 * tid + 4 * j);
+      }
+    }
+    {
+      const int t = tid / (NCOL / 4), v0 = (tid % (NCOL / 4)) * 4, tau = c * CB + t;
+      pd = tau < p.T ? *reinterpret_cast<const f4*>(dob + (size_t)tau * DV + v0) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      pf[0] = sc[kScGam * CB + tid];
+      pf[1] = sc[kScE * CB + tid] * sc[kScGprev * CB + tid];
+      pf[2] = sc[kScGend * CB + tid];
+      pf[3] = rec[BRec::kMisc];
+    }
+  };
+  auto commit = [&](int c) {
+    const float* x0 = (R::shift && has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+    xrows.commit(Xs, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
+    qrows.commit(Qs, elu, len, -1, nullptr);
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        *reinterpret_cast<f4*>(Ts + (tid >> 3) * LDC + 8 * (tid & 7) + 4 * j) = pt[j];
+        *reinterpret_cast<f4*>(Ms + (tid >> 3) * LDC + 8 * (tid & 7) + 4 * j) = pm[j];
+      }
+    }
+    {
+      const int t = tid / (NCOL / 4), v0 = (tid % (NCOL / 4)) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dOt[(v0 + i) * LDC + t] = pd[i];
+    }
+    if (tid < CB) {
+      s_fac[0][tid] = pf[0];
+      s_fac[1][tid] = pf[1];
+      s_fac[2][tid] = pf[2];
+      if (tid == 0) s_fac[3][0] = pf[3];
+    }
+  };
+  load(nch - 1);
+
   for (int c = nch - 1; c >= 0; --c) {
     float* dSc = dSch + ((size_t)bh * nch + c) * SS;
 #pragma unroll
@@ -525,28 +702,12 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         dSc[(size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
-    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
-    __syncthreads();
-    for (int e = tid; e < CB * CB / 4; e += 512) {
-      const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
-      *reinterpret_cast<f4*>(Ms + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kM + r * CB + c4);
-      if constexpr (R::solve)
-        *reinterpret_cast<f4*>(Ts + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4);
-    }
-    for (int e = tid; e < CB * NCOL; e += 512) {
-      const int t = e / NCOL, v = e % NCOL, tau = c * CB + t;
-      dOt[v * LDC + t] = tau < p.T ? p.dout[((size_t)bh * p.T + tau) * DV + col0 + v] : 0.f;
-    }
-    if (tid < CB) {
-      const float* sc = rec + BRec::kSc;
-      s_fac[0][tid] = sc[kScGam * CB + tid];
-      s_fac[1][tid] = sc[kScE * CB + tid] * sc[kScGprev * CB + tid];
-      s_fac[2][tid] = sc[kScGend * CB + tid];
-      if (tid == 0) s_fac[3][0] = rec[BRec::kMisc];
-    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+    commit(c);
 #pragma unroll
     for (int a = 0; a < NTW; ++a) store_t(Bt, LDX, 16 * tile_rt(a), 16 * tile_ct(a), dS[a], lane);
-    stage_rows<InT, DK, R::shift, true, true, 512>(p, bh, c, Xs, Qs, has_in);
+    __syncthreads();
+    if (c >= 1) load(c - 1);
 
     if constexpr (R::solve) {
       // dU = M^T dO + (Gamma_end / Gamma) X dS' for token tile m, column tile ctw (only the
@@ -560,8 +721,13 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
       __syncthreads();  // dU complete; dS^T no longer read
       f4 dr = {0.f, 0.f, 0.f, 0.f};
       mm<true, false>(dr, Ts + 16 * m, LDC, dUt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+      // dR, kept for the gradient pass
+      float* drw = dRw + ((size_t)bh * nch + c) * CB * DV + col0 + 16 * ctw + n;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dr[i] *= s_fac[1][16 * m + 4 * g + i];
+      for (int i = 0; i < 4; ++i) {
+        drw[(size_t)(16 * m + 4 * g + i) * DV] = dr[i];
+        dr[i] *= s_fac[1][16 * m + 4 * g + i];
+      }
       store_t(Bt, LDC, 16 * m, 16 * ctw, dr, lane);
       __syncthreads();
     }
@@ -613,13 +779,17 @@ enum {
 
 template <typename InT, int DK, int DV, int RULE>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float* recs, const float* Sch,
-                                                        const float* dSch) {
+                                                        const float* dSch, const float* Rh, const float* dRw) {
   using R = Rule<RULE>;
   constexpr bool SOLVE = R::solve;
   constexpr int LDX = DK + 4, NDT = DK / 16, DPW = NDT / 2;  // d_k tiles per wave
   constexpr int NBLK = DV / NCOL;
-  // LDS: X, T, M, and a region for one value block (phase 1) or Q, A1, W (phase 2)
-  constexpr int kBlk1 = 2 * NCOL * LDX + 3 * NCOL * LDC + 2 * CB * LDU;
+  // LDS: X, T, M, and a region for one value block (phase 1) or Q, A1, W (phase 2). A value
+  // block: S and dS' [DK][NCOL], dO and U [CB][NCOL] in natural layout (every K = d_v
+  // product reads 16-byte operand runs); the delta rule adds dR [CB][NCOL] and R^T
+  // [NCOL][CB] (from the state passes' R-hat and dR), the other rules dS'^T [NCOL][DK] and
+  // dO^T [NCOL][CB] for dU = M^T dO + (Gamma_end / Gamma) X dS'.
+  constexpr int kBlk1 = 2 * DK * LDU + 2 * CB * LDU + (SOLVE ? CB * LDU + NCOL * LDC : NCOL * LDX + NCOL * LDC);
   constexpr int kBlk2 = CB * LDX + 2 * CB * LDC;
   constexpr int kBlk = kBlk1 > kBlk2 ? kBlk1 : kBlk2;
   __shared__ __align__(16) float Xs[CB * LDX];
@@ -630,13 +800,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
   __shared__ float s_p[kNP][CB];
   __shared__ float s_dn[CB];
   __shared__ float s_red[8];
-  float* St = blk;                     // S^T of the block [NCOL][DK]
-  float* dSt = St + NCOL * LDX;        // dS'^T
-  float* dOt = dSt + NCOL * LDX;       // dO^T [NCOL][CB]
-  float* Rt = dOt + NCOL * LDC;        // R^T (delta)
-  float* dUt = Rt + NCOL * LDC;        // dU^T (delta)
-  float* Un = dUt + NCOL * LDC;        // U [CB][NCOL]
+  float* Sn = blk;                     // S block [DK][NCOL]
+  float* dSn = Sn + DK * LDU;          // dS' block
+  float* dOn = dSn + DK * LDU;         // dO [CB][NCOL]
+  float* Un = dOn + CB * LDU;          // U [CB][NCOL]
   float* dRn = Un + CB * LDU;          // dR [CB][NCOL] (delta)
+  float* Rt = dRn + CB * LDU;          // R^T [NCOL][CB] (delta)
+  float* dSt = Un + CB * LDU;          // dS'^T [NCOL][DK] (other rules)
+  float* dOt = dSt + NCOL * LDX;       // dO^T [NCOL][CB] (other rules)
   float* Qs = blk;                     // phase 2: Q [CB][DK]
   float* A1 = blk + CB * LDX;          // dMm o D [CB][CB]
   float* Wn = A1 + CB * LDC;           // dLm o eta D' [CB][CB] (delta)
@@ -650,6 +821,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
   const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
   const float* Sc = Sch + ((size_t)bh * nch + c) * SS;
   const float* dSc = dSch + ((size_t)bh * nch + c) * SS;
+  const float* rhc = Rh + ((size_t)bh * nch + c) * CB * DV;
+  const float* drc = dRw + ((size_t)bh * nch + c) * CB * DV;
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
 
   for (int e = tid; e < CB * CB / 4; e += 512) {
@@ -674,76 +847,97 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
 
   auto fac = [&](int k, int t) { return s_sc[k][t]; };
 
-  for (int jb = 0; jb < NBLK; ++jb) {
+  // the next value block in registers: S and dS' (NSJ f4 a thread each), dO and (delta) dR
+  // (one f4 each), and this lane's four values of R-hat (delta) or V (other rules)
+  constexpr int NSJ = DK * NCOL / 4 / 512;
+  f4 ps[NSJ], pds[NSJ], pdo, pdr;
+  float pv4[4];
+  auto load_blk = [&](int jb) {
     const int col0 = jb * NCOL;
-    // the block's S^T, dS'^T, dO^T
-    for (int e = tid; e < DK * NCOL / 4; e += 512) {
-      const int r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
-      const f4 s4 = *reinterpret_cast<const f4*>(Sc + (size_t)r * DV + col0 + v4);
-      const f4 d4 = *reinterpret_cast<const f4*>(dSc + (size_t)r * DV + col0 + v4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        St[(v4 + i) * LDX + r] = s4[i];
-        dSt[(v4 + i) * LDX + r] = d4[i];
-        sds += s4[i] * d4[i];
-      }
+    for (int j = 0; j < NSJ; ++j) {
+      const int e = tid + 512 * j, r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
+      ps[j] = *reinterpret_cast<const f4*>(Sc + (size_t)r * DV + col0 + v4);
+      pds[j] = *reinterpret_cast<const f4*>(dSc + (size_t)r * DV + col0 + v4);
     }
-    for (int e = tid; e < CB * NCOL; e += 512) {
-      const int t = e / NCOL, v = e % NCOL, tau = t0 + t;
-      dOt[v * LDC + t] = tau < p.T ? p.dout[(rb + tau) * DV + col0 + v] : 0.f;
+    {
+      const int t = tid / (NCOL / 4), v4 = (tid % (NCOL / 4)) * 4, tau = t0 + t;
+      pdo = tau < p.T ? *reinterpret_cast<const f4*>(p.dout + (rb + tau) * DV + col0 + v4) : f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SOLVE) pdr = *reinterpret_cast<const f4*>(drc + (size_t)t * DV + col0 + v4);
     }
-    float vv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tau = t0 + 16 * m + 4 * g + i;
-      vv[i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + col0 + 16 * ctw + n) : 0.f;
+      const int t = 16 * m + 4 * g + i, tau = t0 + t, cc = col0 + 16 * ctw + n;
+      if constexpr (SOLVE) pv4[i] = rhc[(size_t)t * DV + cc];
+      else pv4[i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + cc) : 0.f;
     }
-    __syncthreads();
+  };
+  load_blk(0);
 
-    f4 rhat;  // delta: V - Gamma_prev X S
-    if constexpr (SOLVE) {
-      f4 xs = {0.f, 0.f, 0.f, 0.f};
-      mm<false, false>(xs, Xs + 16 * m * LDX, LDX, St + 16 * ctw * LDX, LDX, 0, DK, lane);
-      f4 r;
+  for (int jb = 0; jb < NBLK; ++jb) {
+    const int col0 = jb * NCOL;
+    // the block into LDS from registers
+#pragma unroll
+    for (int j = 0; j < NSJ; ++j) {
+      const int e = tid + 512 * j, r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
+      *reinterpret_cast<f4*>(Sn + r * LDU + v4) = ps[j];
+      *reinterpret_cast<f4*>(dSn + r * LDU + v4) = pds[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * m + 4 * g + i;
-        rhat[i] = vv[i] - fac(kScGprev, t) * xs[i];
-        r[i] = fac(kScE, t) * rhat[i];
+        sds += ps[j][i] * pds[j][i];
+        if (!SOLVE) dSt[(v4 + i) * LDX + r] = pds[j][i];
       }
+    }
+    {
+      const int t = tid / (NCOL / 4), v4 = (tid % (NCOL / 4)) * 4;
+      *reinterpret_cast<f4*>(dOn + t * LDU + v4) = pdo;
+      if constexpr (SOLVE) {
+        *reinterpret_cast<f4*>(dRn + t * LDU + v4) = pdr;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dOt[(v4 + i) * LDC + t] = pdo[i];
+      }
+    }
+    float v4r[4];  // R-hat (delta) or V, this lane's rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4r[i] = pv4[i];
+    if constexpr (SOLVE) {
+      f4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = fac(kScE, 16 * m + 4 * g + i) * v4r[i];
       store_t(Rt, LDC, 16 * m, 16 * ctw, r, lane);
     } else {
       f4 u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = fac(kScE, 16 * m + 4 * g + i) * vv[i];
+      for (int i = 0; i < 4; ++i) u[i] = fac(kScE, 16 * m + 4 * g + i) * v4r[i];
       store_n(Un, LDU, 16 * m, 16 * ctw, u, lane);
     }
-    // dU = M^T dO + (Gamma_end / Gamma) X dS'
-    f4 du = {0.f, 0.f, 0.f, 0.f};
-    mm<false, false>(du, Xs + 16 * m * LDX, LDX, dSt + 16 * ctw * LDX, LDX, 0, DK, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) du[i] *= fac(kScGend, 16 * m + 4 * g + i);
-    mm<true, false>(du, Ms + 16 * m, LDC, dOt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
+    __syncthreads();
+    if (jb + 1 < NBLK) load_blk(jb + 1);
+
     if constexpr (SOLVE) {
-      store_t(dUt, LDC, 16 * m, 16 * ctw, du, lane);
-      __syncthreads();
+      // U = T R; dV = eta dR; eta's gradient through R-hat
       f4 u = {0.f, 0.f, 0.f, 0.f};
       mm<false, false>(u, Ts + 16 * m * LDC, LDC, Rt + 16 * ctw * LDC, LDC, 0, 16 * m + 16, lane);
       store_n(Un, LDU, 16 * m, 16 * ctw, u, lane);
-      f4 dr = {0.f, 0.f, 0.f, 0.f};
-      mm<true, false>(dr, Ts + 16 * m, LDC, dUt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
-      store_n(dRn, LDU, 16 * m, 16 * ctw, dr, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * g + i, tau = t0 + t;
-        pe[i] += dr[i] * rhat[i];
-        if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * dr[i];
+        const float dr = dRn[t * LDU + 16 * ctw + n];
+        pe[i] += dr * v4r[i];
+        if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * dr;
       }
     } else {
+      // dU = M^T dO + (Gamma_end / Gamma) X dS'; dV = f dU; f's gradient through V
+      f4 du = {0.f, 0.f, 0.f, 0.f};
+      mm<false, false>(du, Xs + 16 * m * LDX, LDX, dSt + 16 * ctw * LDX, LDX, 0, DK, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] *= fac(kScGend, 16 * m + 4 * g + i);
+      mm<true, false>(du, Ms + 16 * m, LDC, dOt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * g + i, tau = t0 + t;
-        pe[i] += du[i] * vv[i];
+        pe[i] += du[i] * v4r[i];
         if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * du[i];
       }
     }
@@ -754,7 +948,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
     if (w < 4) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        if (s <= m) mm<true, false>(aMm[s], dOt + 16 * m, LDC, Un + 16 * s * LDU, LDU, 0, NCOL, lane);
+        if (s <= m) mm<false, false>(aMm[s], dOn + 16 * m * LDU, LDU, Un + 16 * s * LDU, LDU, 0, NCOL, lane);
     } else if constexpr (SOLVE) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -763,9 +957,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
 #pragma unroll
     for (int d = 0; d < DPW; ++d) {
       const int dt = ctw * DPW + d;
-      mm<true, true>(aQ1[d], dOt + 16 * m, LDC, St + 16 * dt, LDX, 0, NCOL, lane);
-      if constexpr (SOLVE) mm<false, true>(aXR[d], dRn + 16 * m * LDU, LDU, St + 16 * dt, LDX, 0, NCOL, lane);
-      mm<false, true>(aXS[d], Un + 16 * m * LDU, LDU, dSt + 16 * dt, LDX, 0, NCOL, lane);
+      mm<false, false>(aQ1[d], dOn + 16 * m * LDU, LDU, Sn + 16 * dt * LDU, LDU, 0, NCOL, lane);
+      if constexpr (SOLVE) mm<false, false>(aXR[d], dRn + 16 * m * LDU, LDU, Sn + 16 * dt * LDU, LDU, 0, NCOL, lane);
+      mm<false, false>(aXS[d], Un + 16 * m * LDU, LDU, dSn + 16 * dt * LDU, LDU, 0, NCOL, lane);
     }
     __syncthreads();
   }
@@ -1011,12 +1205,14 @@ hipError_t launch_rule(const BwdParams& p, float* ws, hipStream_t st) {
   float* recs = ws;
   float* Sch = recs + nrec * BRec::kFloats;
   float* dSch = Sch + nrec * (size_t)DK * DV;
+  float* Rh = dSch + nrec * (size_t)DK * DV;  // R-hat of every chunk [CB][DV] (delta rule)
+  float* dRw = Rh + nrec * (size_t)CB * DV;   // dR of every chunk (delta rule)
   const unsigned ngrid = (unsigned)(8 * (DV / NCOL) * ((p.BH + 7) / 8));
   hipLaunchKernelGGL((bwd_prep_kernel<InT, DK, RULE>), dim3((unsigned)nrec), dim3(256), 0, st, p, recs);
-  hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch);
-  hipLaunchKernelGGL((bwd_dstate_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch);
+  hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
+  hipLaunchKernelGGL((bwd_dstate_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch, dRw);
   hipLaunchKernelGGL((bwd_grad_kernel<InT, DK, DV, RULE>), dim3((unsigned)nrec), dim3(512), 0, st, p, recs, Sch,
-                     dSch);
+                     dSch, Rh, dRw);
   return hipGetLastError();
 }
 
@@ -1044,7 +1240,7 @@ bool bwd_chunked(int rule, uint32_t flags, int T) {
 
 size_t bwd_chunk_floats_per_head(int T, int dk, int dv) {
   const size_t nch = ((size_t)T + CB - 1) / CB;
-  return nch * (BRec::kFloats + 2 * (size_t)dk * (size_t)dv);
+  return nch * (BRec::kFloats + 2 * (size_t)dk * (size_t)dv + 2 * (size_t)CB * (size_t)dv);
 }
 
 hipError_t launch_bwd_chunked(const BwdParams& p, hipStream_t st) {

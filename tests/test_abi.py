@@ -217,8 +217,9 @@ def test_bwd_workspace_size_and_empty_batch():
     assert lib.fwmem_scan_bwd_workspace_bytes(ctypes.byref(shp), ctypes.byref(md), ctypes.byref(n)) == F.OK
     # the chunk-parallel backward (scalar decay, no normaliser): per 64-token chunk one
     # record of 13,184 floats (three 64x64 matrices, 13 rows of per-token scalars and one
-    # row of chunk values, padded to a multiple of 64) and two d_k x d_v states
-    want = 4 * 6 * 2 * (13184 + 2 * 128 * 64)
+    # row of chunk values, padded to a multiple of 64), two d_k x d_v states and two
+    # 64 x d_v blocks
+    want = 4 * 6 * 2 * (13184 + 2 * 128 * 64 + 2 * 64 * 64)
     assert n.value == (want + 255) // 256 * 256
     # the per-value-channel rule: 32-token chunks as well
     mdv = F.mode(rule=F.RULE_DELTA_PV)
