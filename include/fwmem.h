@@ -83,8 +83,10 @@ typedef enum {
   FWMEM_EWORKSPACE = -6,   /* workspace NULL or smaller than fwmem_scan_workspace_bytes() */
   FWMEM_EWAIT = -7,        /* fwmem_check_device: a bounded wait inside a kernel gave up since
                               the last check; the outputs of the calls in between are wrong */
-  FWMEM_ESCRATCH = -8      /* fwmem_scan_fwd_noalloc: the call needs more workspace than the
+  FWMEM_ESCRATCH = -8,     /* fwmem_scan_fwd_noalloc: the call needs more workspace than the
                               library's fixed device scratch (FWMEM_NOALLOC_SCRATCH_BYTES) */
+  FWMEM_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int32 value a valid
+                              fwmem_status, so that any code can be passed to fwmem_strerror */
 } fwmem_status;
 
 /* DELTA_PV: the delta rule with one step size per value channel (Falcon-2, "Fast Weight

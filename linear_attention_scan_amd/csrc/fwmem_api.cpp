@@ -191,6 +191,7 @@ const char* fwmem_strerror(fwmem_status st) {
     case FWMEM_EWORKSPACE: return "workspace missing or too small";
     case FWMEM_ESCRATCH: return "the call needs more workspace than the fixed device scratch holds";
     case FWMEM_EWAIT: return "a kernel's bounded wait gave up: results since the last check are wrong";
+    case FWMEM_STATUS_MAX_ENUM: break;
   }
   return "unknown status";
 }

@@ -108,6 +108,18 @@ __device__ __forceinline__ void store_n(float* dst, int ld, int r0, int c0, cons
   for (int i = 0; i < 4; ++i) dst[(r0 + 4 * (lane >> 4) + i) * ld + c0 + (lane & 15)] = v[i];
 }
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations complete
+// before it arrives and the compiler moves no memory access across it, but its global loads
+// stay in flight (__syncthreads would wait for them), so the prefetch of the next chunk or
+// value block overlaps the barriers of the current one. Global memory is never shared
+// between the threads of a workgroup in these kernels.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum over the 16 lanes of a lane group (the 16 columns of a C-layout tile).
 __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
@@ -538,7 +550,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
         for (int i = 0; i < 4; ++i)
           Sc[(size_t)(16 * (w + 4 * a) + 4 * g + i) * DV + col0 + 16 * ct + n] = S[a][ct][i];
     if (!R::solve && c + 1 == nch) break;  // the state after the last chunk is not needed
-    __syncthreads();  // the previous chunk's LDS reads are done
+    lds_barrier();  // the previous chunk's LDS reads are done
     commit(c);
     if constexpr (R::solve) {
 #pragma unroll
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDX, 16 * (w + 4 * a), 16 * ct, S[a][ct], lane);
     }
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < nch && (R::solve || c + 2 < nch)) load(c + 1);
 
     // this wave's token tile w: W = fU U with U = T R (delta) or fV V
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
         store_t(Rt, LDC, 16 * w, 16 * ct, r, lane);
       }
       if (c + 1 == nch) break;  // the state after the last chunk is not needed
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         f4 u = {0.f, 0.f, 0.f, 0.f};
@@ -588,7 +600,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(BwdParams p, const float
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) store_t(Bt, LDC, 16 * w, 16 * ct, W[ct], lane);
-    __syncthreads();
+    lds_barrier();
     // S' = Gamma_end S + X^T W
     const float gend = s_fac[4][0];
 #pragma unroll
@@ -702,11 +714,11 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         dSc[(size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
-    __syncthreads();  // the previous chunk's LDS reads are done
+    lds_barrier();  // the previous chunk's LDS reads are done
     commit(c);
 #pragma unroll
     for (int a = 0; a < NTW; ++a) store_t(Bt, LDX, 16 * tile_rt(a), 16 * tile_ct(a), dS[a], lane);
-    __syncthreads();
+    lds_barrier();
     if (c >= 1) load(c - 1);
 
     if constexpr (R::solve) {
@@ -718,7 +730,7 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
       for (int i = 0; i < 4; ++i) du[i] *= s_fac[2][16 * m + 4 * g + i];
       mm<true, false>(du, Ms + 16 * m, LDC, dOt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
       store_t(dUt, LDC, 16 * m, 16 * ctw, du, lane);
-      __syncthreads();  // dU complete; dS^T no longer read
+      lds_barrier();  // dU complete; dS^T no longer read
       f4 dr = {0.f, 0.f, 0.f, 0.f};
       mm<true, false>(dr, Ts + 16 * m, LDC, dUt + 16 * ctw * LDC, LDC, 16 * m, CB, lane);
       // dR, kept for the gradient pass
@@ -729,7 +741,7 @@ __global__ __launch_bounds__(512) void bwd_dstate_kernel(BwdParams p, const floa
         dr[i] *= s_fac[1][16 * m + 4 * g + i];
       }
       store_t(Bt, LDC, 16 * m, 16 * ctw, dr, lane);
-      __syncthreads();
+      lds_barrier();
     }
     // dS = Gamma_end dS' + Q^T diag(Gamma) dO - X^T (eta Gamma_prev dR)
     const float gend = s_fac[3][0];
@@ -912,7 +924,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
       for (int i = 0; i < 4; ++i) u[i] = fac(kScE, 16 * m + 4 * g + i) * v4r[i];
       store_n(Un, LDU, 16 * m, 16 * ctw, u, lane);
     }
-    __syncthreads();
+    lds_barrier();
     if (jb + 1 < NBLK) load_blk(jb + 1);
 
     if constexpr (SOLVE) {
@@ -941,7 +953,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
         if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * du[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // accumulate over the block's columns: dMm = dO U^T (w < 4), dLm = -dR U^T (w >= 4),
     // dQ1 = dO S^T, dXR = dR S^T, dXS = U dS'^T
@@ -961,7 +973,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
       if constexpr (SOLVE) mm<false, false>(aXR[d], dRn + 16 * m * LDU, LDU, Sn + 16 * dt * LDU, LDU, 0, NCOL, lane);
       mm<false, false>(aXS[d], Un + 16 * m * LDU, LDU, dSn + 16 * dt * LDU, LDU, 0, NCOL, lane);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- phase 2

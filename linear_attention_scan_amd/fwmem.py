@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfwmem.so")
+# FWMEM_LIB names another build of the same library (the host-sanitizer build of the ABI
+# checks); by default the in-tree libfwmem.so
+LIB_PATH = os.environ.get("FWMEM_LIB") or os.path.join(PKG, "libfwmem.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EOVERLAP, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 EWAIT, ESCRATCH = -7, -8

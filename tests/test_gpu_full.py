@@ -15,28 +15,35 @@ from tests.gpu_helpers import TOL, check_scan, say
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def test_full_delta_bf16():
-    check_scan(wl.delta_bf16(seed=0), label="delta_bf16 B=4 H=8 T=4096")
+SEEDS = [0, 1, 2]  # the parity seeds of the workload recipes
 
 
-def test_full_delta_bf16_h16():
-    check_scan(wl.delta_bf16_h16(seed=1), label="delta_bf16_h16 B=4 H=16 T=4096")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_delta_bf16(seed):
+    check_scan(wl.delta_bf16(seed=seed), label=f"delta_bf16 B=4 H=8 T=4096 seed={seed}")
 
 
-def test_full_additive_bf16():
-    check_scan(wl.additive_bf16(seed=0), label="additive_bf16 B=2 H=16 T=16384")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_delta_bf16_h16(seed):
+    check_scan(wl.delta_bf16_h16(seed=seed), label=f"delta_bf16_h16 B=4 H=16 T=4096 seed={seed}")
 
 
-def test_full_delta_long_per_channel():
-    check_scan(wl.delta_long_pc(seed=0), label="delta_long_pc B=1 H=8 T=131072")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_additive_bf16(seed):
+    check_scan(wl.additive_bf16(seed=seed), label=f"additive_bf16 B=2 H=16 T=16384 seed={seed}")
 
 
-def test_full_decode_1000_steps():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_delta_long_per_channel(seed):
+    check_scan(wl.delta_long_pc(seed=seed), label=f"delta_long_pc B=1 H=8 T=131072 seed={seed}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_decode_1000_steps(seed):
     import torch
     B, H, d, steps = 256, 32, 128, 1000
-    seed = 0
-    sample = np.arange(0, B * H, 97)            # 85 heads spread over the batch
-    say(f"[decode] B={B} H={H} d={d} steps={steps}, oracle on {len(sample)} heads")
+    sample = np.arange(seed, B * H, 97)         # 85 heads spread over the batch
+    say(f"[decode] B={B} H={H} d={d} steps={steps} seed={seed}, oracle on {len(sample)} heads")
     S0 = wl.decode_state0(seed, B, H, d)
     st_a = F.State(B, H, d, d)
     st_a.S.copy_(torch.from_numpy(S0))
