@@ -33,8 +33,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "linear_attention_scan_amd", "csrc")
 
-# HBM traffic per launch of the scan kernels and the backward kernel on the default
-# workload (B=4 H=16 T=4096 d=128, bf16, delta rule) and of the decode kernel (B=256 H=32 d=128, state in place),
+# HBM traffic per launch of the scan kernels and the chunk-parallel backward's kernels on the
+# default workload (B=4 H=16 T=4096 d=128, bf16, delta rule) and of the decode kernel
+# (B=256 H=32 d=128, state in place),
 # from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in runs of their own, each scaled by
 # what the same counter reads for a plain 1 GiB device copy in the same run
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0). A record is reported only while the
@@ -42,43 +43,73 @@ CSRC = os.path.join(ROOT, "linear_attention_scan_amd", "csrc")
 # the counters are taken again.
 MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "prop_split_kernel"): {
-        "sources": ("fwmem_scan_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
+        "sources": ('fwmem_scan_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_scan_split.hip": "78fa1efc6d7f4a7da80b830304d9c1191d3fa6ba07a49bbac57339f58e7c2897",
+            "fwmem_scan_split.hip": "888db0e0e31bca242ef147c8412775f748ed947fd0abc340b58805efbbd84eab",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
         },
-        "fetch_kib": 150226.7, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150223.0, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
-        "sources": ("fwmem_prep_split.hip", "fwmem_split.h", "fwmem_device.h", "fwmem_internal.h"),
+        "sources": ('fwmem_prep_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
             "fwmem_prep_split.hip": "3101a25cff5f80c14678715ef955e7813e5203414cf5f028e6a8e885c74a10f8",
             "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
         },
-        "fetch_kib": 66681.9, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66681.5, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("decode", "step_kernel"): {
-        "sources": ("fwmem_step.hip", "fwmem_device.h", "fwmem_internal.h"),
+        "sources": ('fwmem_step.hip', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
             "fwmem_step.hip": "abf27317cda12cc5a31bfd56f61be55aedc5758d577a0abf5f1d25a096ca1990",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
         },
-        "fetch_kib": 267730.8, "write_kib": 532885.4, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267738.3, "write_kib": 532868.2, "read_factor": 2.0, "write_factor": 1.0,
     },
-    ("delta_bf16_h16", "bwd_kernel"): {
-        "sources": ("fwmem_backward.hip", "fwmem_backward.h", "fwmem_device.h", "fwmem_internal.h"),
+    ("delta_bf16_h16", "bwd_prep_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward.hip": "fd34818f82f71db48853bb977d773b4eaee98e057f37ae9ecb69527bf37f7c99",
-            "fwmem_backward.h": "c209129737af1e679f0105b55a50b7dcada68045815cabec88ea0b1b4371a665",
+            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c6958b66fe352267aab814e5110b60d6623efc1eaf3d246dbbb03ab14e6a2853",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
         },
-        "fetch_kib": 8834051.8, "write_kib": 17180908.5, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66691.1, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("delta_bf16_h16", "bwd_state_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+        "sha256": {
+            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+        },
+        "fetch_kib": 100168.2, "write_kib": 393216.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("delta_bf16_h16", "bwd_dstate_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+        "sha256": {
+            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+        },
+        "fetch_kib": 198986.3, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
+    },
+    ("delta_bf16_h16", "bwd_grad_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+        "sha256": {
+            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
+            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+        },
+        "fetch_kib": 629702.2, "write_kib": 395610.6, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
