@@ -165,6 +165,26 @@ __global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
   }
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS operations so far have completed; the compiler
+// moves no memory access across it.
+__device__ __forceinline__ void lds_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+
+// Sign of a parity bit applied to x.
+__device__ __forceinline__ float with_sign(float x, int parity) {
+  return __int_as_float(__float_as_int(x) ^ (parity << 31));
+}
+
+// Gate activation of beta with a hardware reciprocal (the fused variants of act_beta).
+__device__ __forceinline__ float act_beta_pv(float z, uint32_t flags) {
+  if (flags & kFlagBetaSig) return __builtin_amdgcn_rcpf(1.f + __expf(-z));
+  if (flags & kFlagBetaSig2) return 2.f * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+  return z;
+}
+
 // Exclusive prefix over the column's four lane groups g (lanes n, n+16, n+32, n+48) of a
 // lane total, and the sum over all four.
 __device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, float& excl, int& pexcl,
@@ -188,8 +208,8 @@ __device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, floa
 
 template <int DK>
 constexpr size_t prop_pv_floats() {
-  // X, Q; G, P, beta, V; four token scalars; per wave two [16][17] solve tiles (c, ef)
-  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH + 4 * 2 * 2 * 16 * 17;
+  // X, Q; G, P, beta, V; four token scalars; per wave a [16 columns][4] hand-off slot
+  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH + 4 * 64;
 }
 
 // 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
@@ -200,6 +220,20 @@ __device__ __forceinline__ bf8 frag_pair(const uint16_t* p) {
   return __builtin_bit_cast(bf8, u32x4{a.x, a.y, b.x, b.y});
 }
 
+// The same A fragment (K slots 4g..4g+3 and 16+4g..16+4g+3) of X^T, rows d_k 16 rt + n,
+// K = tokens, from the row-major X rows by two LDS transpose reads. Within each group of
+// 16 lanes, lane 4r + c points at 4 values of token row r, columns 4c..4c+3, and lane
+// 4c + e receives column 4c + e of the four rows. `p` is this lane's address for the first
+// four K slots (token 32 kq + 4g + (n >> 2), column 16 rt + 4 (n & 3)); the other four are
+// 16 rows further on.
+__device__ __forceinline__ bf8 xt_frag(const uint16_t* p, int ld) {
+  typedef short s8v __attribute__((ext_vector_type(8)));
+  const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)p);
+  const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)(p + 16 * ld));
+  const s8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf8, r);
+}
+
 template <typename InT, int DK, bool EXACT>
 __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   constexpr int LDX = DK + 4, NRT = DK / 16;
@@ -208,22 +242,21 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   __shared__ __align__(16) float smem[prop_pv_floats<DK>()];
   float* Xs = smem;                 // [CH][LDX] phi(x_t) (fp32 operands)
   float* Qs = Xs + CH * LDX;        // [CH][LDX] phi(q_t)
-  // exact operands in the same space: X and Q rows and X transposed, raw bf16
-  constexpr int LDB = DK + 8, LDT2 = CH + 8;
-  static_assert((2 * CH * LDB + DK * LDT2) * 2 <= 2 * CH * LDX * 4, "bf16 operands fit");
+  // exact operands in the same space: X and Q rows, raw bf16 (X^T operands are read
+  // from the X rows with the LDS transpose read)
+  constexpr int LDB = DK + 8;
+  static_assert(2 * CH * LDB * 2 <= 2 * CH * LDX * 4, "bf16 operands fit");
   uint16_t* Xb = reinterpret_cast<uint16_t*>(smem);  // [CH][LDB]
   uint16_t* Qb = Xb + CH * LDB;                      // [CH][LDB]
-  uint16_t* XTb = Qb + CH * LDB;                     // [DK][LDT2]
   float* Gs = Qs + CH * LDX;        // [CH][LDM]
   float* Ps = Gs + CH * LDM;        // [CH][LDM]
   float* Bs = Ps + CH * LDM;        // [CH][LDM] beta of the group's 64 columns
   float* Vs = Bs + CH * LDM;        // [CH][LDM] values of the group's 64 columns
-  float* s_den = Vs + CH * LDM;     // [CH]
-  float* s_lam = s_den + CH;        // [CH]
+  float* s_rden = Vs + CH * LDM;    // [CH] 1 / eta's denominator (0 where no key is written)
+  float* s_lam = s_rden + CH;       // [CH]
   float* s_nx = s_lam + CH;         // [CH]
   float* s_mq = s_nx + CH;          // [CH]
-  constexpr int LDS17 = 17;         // solve tiles: [16 rows][17] floats, two per wave and buffer
-  float* s_solve = s_mq + CH;       // [4 waves][2 buffers][2: c, ef][16][17]
+  float* s_wb = s_mq + CH;          // [4 waves][16 columns][4]: solved rows handed to later rows
 
   const int ngrp = p.dv / 64;
   const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
@@ -307,9 +340,6 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
         }
         *reinterpret_cast<u32x4*>(Xb + t * LDB + cc) = w;
         *reinterpret_cast<u32x4*>(Qb + t * LDB + cc) = pq[r];
-#pragma unroll
-        for (int j = 0; j < VW; ++j)
-          XTb[(cc + j) * LDT2 + t] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
       }
     }
 #pragma unroll
@@ -335,7 +365,7 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       const int gi = tid + NT * r, t = gi / 16, u = (gi % 16) * 4;
       f4 b = pb[r];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = act_beta(b[j], p.flags);
+      for (int j = 0; j < 4; ++j) b[j] = act_beta_pv(b[j], p.flags);
       *reinterpret_cast<f4*>(Gs + t * LDM + u) = pg[r];
       *reinterpret_cast<f4*>(Ps + t * LDM + u) = pp[r];
       *reinterpret_cast<f4*>(Bs + t * LDM + u) = b;  // rows past the end hold act(0); V is 0 there
@@ -349,7 +379,7 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       for (int j = 0; j < VW; j += 4) *reinterpret_cast<f4*>(Vs + t * LDM + u + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
     }
     if (tid < CH) {
-      s_den[tid] = psc[0];
+      s_rden[tid] = 1.f / psc[0];
       s_lam[tid] = psc[1];
       s_nx[tid] = psc[2];
       s_mq[tid] = psc[3];
@@ -391,7 +421,7 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       QS[mt] *= *reinterpret_cast<const f4*>(s_mq + 16 * mt + 4 * g);
     }
 
-    // ---- per (token, column): eta, decay, and the in-chunk log-decay prefix
+    // ---- per (token, column): eta, decay, and the in-chunk prefix of log2 |decay|
     float eta[4][4], la[4][4];
     int ng[4][4];
 #pragma unroll
@@ -399,10 +429,10 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g + i;
-        const float e = Bs[t * LDM + cw] / s_den[t];  // 0 where there is no key
+        const float e = Bs[t * LDM + cw] * s_rden[t];  // 0 where there is no key
         const float a = 1.f - e * s_lam[t];
         eta[mt][i] = e;
-        la[mt][i] = log_abs_floor(a);
+        la[mt][i] = __builtin_amdgcn_logf(fmaxf(fabsf(a), 1e-30f));
         ng[mt][i] = a < 0.f ? 1 : 0;
       }
     float gl[4][4];
@@ -438,80 +468,105 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
     const int pA = __shfl(pg[1][3], 48 + n);
     const float gC = __shfl(gl[3][3], 48 + n);
     const int pC = __shfl(pg[3][3], 48 + n);
-    const float GamC = (pC ? -1.f : 1.f) * __expf(gC);
-    const float GhC = ((pC ^ pA) ? -1.f : 1.f) * __expf(gC - gA);
+    const float GamC = with_sign(__builtin_amdgcn_exp2f(gC), pC);
+    const float GhC = with_sign(__builtin_amdgcn_exp2f(gC - gA), pC ^ pA);
 
-    // right-hand sides and row factors of the triangular system
+    // right-hand sides and row factors of the triangular system. The factors of token
+    // t-1 are those of the lane's previous row, except in its first row, where they are
+    // formed from the prefix before token t.
     float rhs[4][4], ef[4][4], Gam[4][4], Gh[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g + i;
-        const float gprev = gl[mt][i] - la[mt][i];
-        const int pprev = pg[mt][i] ^ ng[mt][i];
-        Gam[mt][i] = (pg[mt][i] ? -1.f : 1.f) * __expf(gl[mt][i]);
-        Gh[mt][i] = ((pg[mt][i] ^ pA) ? -1.f : 1.f) * __expf(gl[mt][i] - gA);
-        const float Gprev = (pprev ? -1.f : 1.f) * __expf(gprev);
-        const float Ghprev = ((pprev ^ pA) ? -1.f : 1.f) * __expf(gprev - gA);
-        const float cf = eta[mt][i] / Gh[mt][i];
+        const int pa = pg[mt][i] ^ pA;
+        Gam[mt][i] = with_sign(__builtin_amdgcn_exp2f(gl[mt][i]), pg[mt][i]);
+        Gh[mt][i] = with_sign(__builtin_amdgcn_exp2f(gl[mt][i] - gA), pa);
+        float Gprev, Ghprev;
+        if (i == 0) {
+          const float gprev = gl[mt][i] - la[mt][i];
+          const int pprev = pg[mt][i] ^ ng[mt][i];
+          Gprev = with_sign(__builtin_amdgcn_exp2f(gprev), pprev);
+          Ghprev = with_sign(__builtin_amdgcn_exp2f(gprev - gA), pprev ^ pA);
+        } else {
+          Gprev = Gam[mt][i - 1];
+          Ghprev = Gh[mt][i - 1];
+        }
+        const float cf = eta[mt][i] * with_sign(__builtin_amdgcn_exp2f(gA - gl[mt][i]), pa);  // eta / Gh
         rhs[mt][i] = cf * (Vs[t * LDM + cw] - Gprev * XS[mt][i]);
         ef[mt][i] = cf * Ghprev;
       }
 
-    // ---- W~ by blocked forward substitution: the off-diagonal blocks on MFMA; each
-    // diagonal block is solved by one lane per column (lanes g = 0), which takes the
-    // block's right-hand side c = rhs - ef (G_off W~) and its row factors ef through an
-    // LDS tile, reads G by broadcast and keeps the 16 solved values in registers, then
-    // hands them back in the C layout. Two tiles alternate between blocks, so one barrier
-    // before and one after the solve suffice.
-    f4 W[4];
+    // ---- W~ by blocked forward substitution. The off-diagonal 16 x 16 blocks run on
+    // fp32 MFMA: once block bk is solved, its product with G goes into the running sums
+    // y of every later block, so a block waits only for the products of the block just
+    // before it. Inside a diagonal block the rows go in four groups of four, each held
+    // by one lane group (lane (g, n) owns rows 4g..4g+3 of column n): group gp solves its
+    // 4 x 4 lower-triangular block in registers and puts the four values in this wave's
+    // LDS slot, and the later groups read them for their column and subtract ef (G w).
+    // The slot belongs to the wave and its LDS operations complete in order, so no
+    // barrier is needed; the G rows of each step are read before the step's wait.
+    float* wslot = s_wb + 64 * wave;  // [16 columns][4]
+    f4 W[4], y[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) y[bi] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
-      f4 y = {0.f, 0.f, 0.f, 0.f};
+      f4 cv;
 #pragma unroll
-      for (int bk = 0; bk < bi; ++bk) {
-        const f4 a = *reinterpret_cast<const f4*>(Gs + (16 * bi + n) * LDM + 16 * bk + 4 * g);
-        mma_block(y, a, W[bk]);
-      }
-      float* tc = s_solve + ((wave * 2 + (bi & 1)) * 2) * 16 * LDS17;  // c tile
-      float* te = tc + 16 * LDS17;                                      // ef tile
+      for (int i = 0; i < 4; ++i) cv[i] = rhs[bi][i] - ef[bi][i] * y[bi][i];
+      // this lane's rows of the diagonal block: G[16 bi + 4 g + i][16 bi + ...]
+      const float* gd = Gs + (16 * bi + 4 * g) * LDM + 16 * bi;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tc[(4 * g + i) * LDS17 + n] = rhs[bi][i] - ef[bi][i] * y[i];
-        te[(4 * g + i) * LDS17 + n] = ef[bi][i];
-      }
-      __syncthreads();
-      if (g == 0) {
-        float w[16];
+      for (int gp = 0; gp < 4; ++gp) {
+        // the rows of group gp's own block, and this lane's rows against group gp
+        f4 rg[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float* grow = Gs + (16 * bi + r) * LDM + 16 * bi;
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < r; ++s2) {
-            if (s2 & 1) a1 += grow[s2] * w[s2];
-            else a0 += grow[s2] * w[s2];
-          }
-          w[r] = tc[r * LDS17 + n] - te[r * LDS17 + n] * (a0 + a1);
+        for (int i = 0; i < 4; ++i) rg[i] = *reinterpret_cast<const f4*>(gd + i * LDM + 4 * gp);
+        if (g == gp) {
+          cv[1] -= ef[bi][1] * (rg[1][0] * cv[0]);
+          cv[2] -= ef[bi][2] * (rg[2][0] * cv[0] + rg[2][1] * cv[1]);
+          cv[3] -= ef[bi][3] * (rg[3][0] * cv[0] + rg[3][1] * cv[1] + rg[3][2] * cv[2]);
+          *reinterpret_cast<f4*>(wslot + 4 * n) = cv;
         }
+        if (gp == 3) break;
+        lds_wait();
+        if (g > gp) {
+          const f4 w = *reinterpret_cast<const f4*>(wslot + 4 * n);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tc[r * LDS17 + n] = w[r];
+          for (int i = 0; i < 4; ++i)
+            cv[i] -= ef[bi][i] * (rg[i][0] * w[0] + rg[i][1] * w[1] + rg[i][2] * w[2] + rg[i][3] * w[3]);
+        }
+        asm volatile("" ::: "memory");  // the next step's slot write stays after this read
       }
-      __syncthreads();
+      W[bi] = cv;
+      // this block's share of the later blocks' sums
 #pragma unroll
-      for (int i = 0; i < 4; ++i) W[bi][i] = tc[(4 * g + i) * LDS17 + n];
+      for (int bl = bi + 1; bl < 4; ++bl) {
+        const f4 a = *reinterpret_cast<const f4*>(Gs + (16 * bl + n) * LDM + 16 * bi + 4 * g);
+        mma_block(y[bl], a, W[bi]);
+      }
     }
 
     // ---- O = Gamma o (Q S0) + Gamma^ o (P W~), stored
+    // P W~ with the products of the four row tiles interleaved (independent sums)
+    f4 pws[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) pws[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      f4 a[4];
+#pragma unroll
+      for (int mt = bk; mt < 4; ++mt) a[mt] = *reinterpret_cast<const f4*>(Ps + (16 * mt + n) * LDM + 16 * bk + 4 * g);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mt = bk; mt < 4; ++mt) pws[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][q], W[bk][q], pws[mt], 0, 0, 0);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f4 pw = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int bk = 0; bk <= mt; ++bk) {
-        const f4 a = *reinterpret_cast<const f4*>(Ps + (16 * mt + n) * LDM + 16 * bk + 4 * g);
-        mma_block(pw, a, W[bk]);
-      }
+      const f4 pw = pws[mt];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tau = t0 + 16 * mt + 4 * g + i;
@@ -537,7 +592,7 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq) {
-          const bf8 a = frag_pair(XTb + (16 * rt + n) * LDT2 + 32 * kq + 4 * g);
+          const bf8 a = xt_frag(Xb + (32 * kq + 4 * g + (n >> 2)) * LDB + 16 * rt + 4 * (n & 3), LDB);
           mma_bf16(acc, a, wh[kq]);
           mma_bf16(acc, a, wl[kq]);
         }
