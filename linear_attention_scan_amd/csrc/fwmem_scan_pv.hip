@@ -27,6 +27,8 @@
 #include "fwmem_internal.h"
 #include "fwmem_split.h"
 
+#include <type_traits>
+
 namespace fwmem {
 namespace {
 
@@ -58,68 +60,107 @@ __device__ __forceinline__ void mma_block(f4& acc, const f4& a, const f4& b) {
   for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
 }
 
-// Stage the chunk's written keys x_t (the previous token's phi(k); for the sequence's
-// first token the carried key x0, or zero when x0 is null) and queries phi(q_t) as fp32
-// rows [CH][LDX], zero past the end, each times its rescale factor when given.
-template <typename InT, int DK, int LDX>
-__device__ __forceinline__ void stage_rows(const ScanParams& p, int bh, int t0, float* Xs, float* Qs,
-                                           const float* x0, const float* sx, const float* sq) {
-  const bool elu = (p.flags & kFlagPhiElu1) != 0;
-  const InT* kb = static_cast<const InT*>(p.k) + (size_t)bh * p.T * DK;
-  const InT* qb = static_cast<const InT*>(p.q) + (size_t)bh * p.T * DK;
-  for (int e = threadIdx.x; e < CH * DK; e += NT) {
-    const int t = e / DK, i = e % DK, tau = t0 + t;
-    float x = 0.f, q = 0.f;
-    if (tau < p.T) {
-      if (tau >= 1) {
-        x = In<InT>::load1(kb + (size_t)(tau - 1) * DK + i);
-        if (elu) x = phi_elu1(x);
-      } else if (x0 != nullptr) {
-        x = x0[i];  // the carried key is phi(k) already
-      }
-      q = In<InT>::load1(qb + (size_t)tau * DK + i);
-      if (elu) q = phi_elu1(q);
-    }
-    Xs[t * LDX + i] = sx != nullptr ? x * sx[t] : x;
-    Qs[t * LDX + i] = sq != nullptr ? q * sq[t] : q;
-  }
-}
-
-template <typename InT, int DK>
+// One (head, chunk) of prep: the chunk's written keys x_t (the previous token's phi(k);
+// for the sequence's first token the carried key, or zero without one) and queries
+// phi(q_t) arrive by 16-byte loads, each thread taking NG granules; their squared norms
+// are summed over the threads of a row. With bf16 inputs and the identity map
+// (EXACT) the rows stay raw bf16 in LDS and G and P run on bf16 MFMA (exact products,
+// fp32 sums); otherwise the rows are staged as fp32 and the products run on fp32 MFMA.
+template <typename InT, int DK, bool EXACT>
 __global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
-  constexpr int LDX = DK + 4;
-  __shared__ __align__(16) float Xs[CH * LDX];
-  __shared__ __align__(16) float Qs[CH * LDX];
-  __shared__ float s_nx[CH], s_mq[CH];
+  static_assert(!EXACT || sizeof(InT) == 2, "exact operands are bf16");
+  constexpr int LDX = DK + 4;  // fp32 row stride
+  constexpr int LDB = DK + 8;  // bf16 row stride
+  __shared__ __align__(16) float smem[EXACT ? CH * LDB : 2 * CH * LDX];
+  float* Xs = smem;
+  float* Qs = smem + CH * LDX;
+  uint16_t* Xb = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Qb = Xb + CH * LDB;
+  __shared__ float s_e[CH], s_nq[CH], s_nx[CH], s_mq[CH];
+  __shared__ float s_x0[DK];
   const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
   const int t0 = c * CH;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
   float* rec = reinterpret_cast<float*>(p.ws + ((size_t)bh * p.nchunks + c) * RecPV::kBytes);
   const bool has_in = p.has_in != nullptr && p.has_in[bh] != 0;
-  const float* x0 = (has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+  // the carried key is only read by the sequence's first token (chunk 0)
+  const bool x0 = c == 0 && has_in && p.xprev_in != nullptr;
   // bf16 inputs with the identity map: the carried key is rounded to bf16 like the keys
   const bool round_x0 = sizeof(InT) == 2 && (p.flags & kFlagPhiElu1) == 0;
-  __shared__ float s_x0[DK];
-  if (x0 != nullptr) {
-    for (int i = threadIdx.x; i < DK; i += NT)
-      s_x0[i] = round_x0 ? bf16_bits_to_f32(f32_to_bf16_bits(x0[i])) : x0[i];
+  if (x0) {
+    for (int i = tid; i < DK; i += NT) {
+      const float v = p.xprev_in[(size_t)bh * DK + i];
+      s_x0[i] = round_x0 ? bf16_bits_to_f32(f32_to_bf16_bits(v)) : v;
+    }
     __syncthreads();
   }
-
-  stage_rows<InT, DK, LDX>(p, bh, t0, Xs, Qs, x0 != nullptr ? s_x0 : nullptr, nullptr, nullptr);
   if (c == 0)
-    for (int i = threadIdx.x; i < DK; i += NT) rec[RecPV::kX0 + i] = x0 != nullptr ? s_x0[i] : 0.f;
+    for (int i = tid; i < DK; i += NT) rec[RecPV::kX0 + i] = x0 ? s_x0[i] : 0.f;
+
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  constexpr int VW = In<InT>::VW;
+  constexpr int GPR = DK / VW;       // granules per row
+  constexpr int NG = CH * GPR / NT;  // granules per thread
+  static_assert(NG >= 1 && GPR <= 64, "granules");
+  const InT* kb = static_cast<const InT*>(p.k) + (size_t)bh * p.T * DK;
+  const InT* qb = static_cast<const InT*>(p.q) + (size_t)bh * p.T * DK;
+#pragma unroll
+  for (int r = 0; r < NG; ++r) {
+    const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW, tau = t0 + t;
+    u32x4 wx = {0u, 0u, 0u, 0u}, wq = {0u, 0u, 0u, 0u};
+    const bool first = tau == 0;
+    if (tau < p.T) {
+      if (tau >= 1) wx = *reinterpret_cast<const u32x4*>(kb + (size_t)(tau - 1) * DK + cc);
+      wq = *reinterpret_cast<const u32x4*>(qb + (size_t)tau * DK + cc);
+    }
+    float x[VW], q[VW];
+    In<InT>::decode(wx, x);
+    In<InT>::decode(wq, q);
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+      if (first) x[j] = x0 ? s_x0[cc + j] : 0.f;  // phi(k) already
+      else if (elu && tau < p.T) x[j] = phi_elu1(x[j]);
+      if (elu && tau < p.T) q[j] = phi_elu1(q[j]);
+    }
+    float ex = 0.f, eq = 0.f;
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+      ex += x[j] * x[j];
+      eq += q[j] * q[j];
+    }
+    if constexpr (EXACT) {
+      if (first) {  // the rounded carried key, exact in bf16
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wx[j] = (uint32_t)f32_to_bf16_bits(x[2 * j]) | ((uint32_t)f32_to_bf16_bits(x[2 * j + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(Xb + t * LDB + cc) = wx;
+      *reinterpret_cast<u32x4*>(Qb + t * LDB + cc) = wq;
+    } else {
+#pragma unroll
+      for (int j = 0; j < VW; j += 4) {
+        *reinterpret_cast<f4*>(Xs + t * LDX + cc + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+        *reinterpret_cast<f4*>(Qs + t * LDX + cc + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+      }
+    }
+    // the row's threads are GPR consecutive lanes
+#pragma unroll
+    for (int o = 1; o < GPR; o <<= 1) {
+      ex += __shfl_xor(ex, o);
+      eq += __shfl_xor(eq, o);
+    }
+    if (gi % GPR == 0) {
+      s_e[t] = ex;
+      s_nq[t] = eq;
+    }
+  }
   __syncthreads();
   // token scalars (wave 0, lane = token)
   if (wave == 0) {
     const int t = lane, tau = t0 + t;
-    float e = 0.f, nq = 0.f;
-    for (int i = 0; i < DK; ++i) {
-      const float x = Xs[t * LDX + ((i + t) % DK)], q = Qs[t * LDX + ((i + t) % DK)];
-      e += x * x;
-      nq += q * q;
-    }
+    float e = s_e[t];
+    const float nq = s_nq[t];
     const float len = qk_length(p.flags, DK);
     float nx = 1.f, mq = 1.f;
     if (len > 0.f) {
@@ -145,32 +186,58 @@ __global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
     float* dst = rec + (mat == 0 ? RecPV::kG : RecPV::kP);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     if (mt >= nt) {
-      const float* arow = (mat == 0 ? Xs : Qs) + (16 * mt + n) * LDX;
-      const float* brow = Xs + (16 * nt + n) * LDX;
+      if constexpr (EXACT) {
+        // A: rows 16 mt + n, K slots 8g..8g+7 of each 32-wide block; B likewise from X
+        const uint16_t* arow = (mat == 0 ? Xb : Qb) + (16 * mt + n) * LDB + 8 * g;
+        const uint16_t* brow = Xb + (16 * nt + n) * LDB + 8 * g;
+#pragma unroll
+        for (int kq = 0; kq < DK / 32; ++kq)
+          mma_bf16(acc, *reinterpret_cast<const bf8*>(arow + 32 * kq), *reinterpret_cast<const bf8*>(brow + 32 * kq));
+      } else {
+        const float* arow = (mat == 0 ? Xs : Qs) + (16 * mt + n) * LDX;
+        const float* brow = Xs + (16 * nt + n) * LDX;
 #pragma unroll 4
-      for (int kb = 0; kb < DK / 16; ++kb) {
-        const f4 a = *reinterpret_cast<const f4*>(arow + 16 * kb + 4 * g);
-        const f4 b = *reinterpret_cast<const f4*>(brow + 16 * kb + 4 * g);
-        mma_block(acc, a, b);
+        for (int kq = 0; kq < DK / 16; ++kq) {
+          const f4 a = *reinterpret_cast<const f4*>(arow + 16 * kq + 4 * g);
+          const f4 b = *reinterpret_cast<const f4*>(brow + 16 * kq + 4 * g);
+          mma_block(acc, a, b);
+        }
       }
     }
-    const int s = 16 * nt + n;
+    const int s2 = 16 * nt + n;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * mt + 4 * g + i;
-      const bool keep = mat == 0 ? s < t : s <= t;
-      const float f = (mat == 0 ? s_nx[t] : s_mq[t]) * s_nx[s];
-      dst[t * CH + s] = keep ? f * acc[i] : 0.f;
+      const bool keep = mat == 0 ? s2 < t : s2 <= t;
+      const float f = (mat == 0 ? s_nx[t] : s_mq[t]) * s_nx[s2];
+      dst[t * CH + s2] = keep ? f * acc[i] : 0.f;
     }
   }
 }
 
-// s_waitcnt lgkmcnt(0): this wave's LDS operations so far have completed; the compiler
-// moves no memory access across it.
-__device__ __forceinline__ void lds_wait() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// The value of lane group gp (lanes 16 gp .. 16 gp + 15) in every lane group, lane n of
+// each group taking lane n of group gp: v_permlane16_swap exchanges the odd 16-lane rows
+// of its first operand with the even rows of its second, and v_permlane32_swap the upper
+// 32 lanes of its first operand with the lower 32 of its second. From x in both operands,
+// the first swap leaves rows (0, 0, 2, 2) in its first result and (1, 1, 3, 3) in its
+// second; swapping either with itself across the halves leaves rows (0, 0, 0, 0) or
+// (1, 1, 1, 1) in the first result and (2, 2, 2, 2) or (3, 3, 3, 3) in the second.
+// Every lane must be active.
+template <int GP>
+__device__ __forceinline__ float group_bcast(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t y = (GP & 1) ? a[1] : a[0];
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float((GP & 2) ? b[1] : b[0]);
 }
 
 // Sign of a parity bit applied to x.
@@ -208,8 +275,8 @@ __device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, floa
 
 template <int DK>
 constexpr size_t prop_pv_floats() {
-  // X, Q; G, P, beta, V; four token scalars; per wave a [16 columns][4] hand-off slot
-  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH + 4 * 64;
+  // X, Q; G, P, beta, V; four token scalars
+  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH;
 }
 
 // 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
@@ -256,7 +323,6 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   float* s_lam = s_rden + CH;       // [CH]
   float* s_nx = s_lam + CH;         // [CH]
   float* s_mq = s_nx + CH;          // [CH]
-  float* s_wb = s_mq + CH;          // [4 waves][16 columns][4]: solved rows handed to later rows
 
   const int ngrp = p.dv / 64;
   const int bh = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
@@ -503,11 +569,8 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
     // y of every later block, so a block waits only for the products of the block just
     // before it. Inside a diagonal block the rows go in four groups of four, each held
     // by one lane group (lane (g, n) owns rows 4g..4g+3 of column n): group gp solves its
-    // 4 x 4 lower-triangular block in registers and puts the four values in this wave's
-    // LDS slot, and the later groups read them for their column and subtract ef (G w).
-    // The slot belongs to the wave and its LDS operations complete in order, so no
-    // barrier is needed; the G rows of each step are read before the step's wait.
-    float* wslot = s_wb + 64 * wave;  // [16 columns][4]
+    // 4 x 4 lower-triangular block in registers, lane swaps hand its four values to the
+    // other groups of the column, and the later groups subtract ef (G w).
     f4 W[4], y[4];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) y[bi] = f4{0.f, 0.f, 0.f, 0.f};
@@ -518,8 +581,8 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       for (int i = 0; i < 4; ++i) cv[i] = rhs[bi][i] - ef[bi][i] * y[bi][i];
       // this lane's rows of the diagonal block: G[16 bi + 4 g + i][16 bi + ...]
       const float* gd = Gs + (16 * bi + 4 * g) * LDM + 16 * bi;
-#pragma unroll
-      for (int gp = 0; gp < 4; ++gp) {
+      static_for<0, 4>([&](auto GPc) {
+        constexpr int gp = GPc;
         // the rows of group gp's own block, and this lane's rows against group gp
         f4 rg[4];
 #pragma unroll
@@ -528,18 +591,18 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
           cv[1] -= ef[bi][1] * (rg[1][0] * cv[0]);
           cv[2] -= ef[bi][2] * (rg[2][0] * cv[0] + rg[2][1] * cv[1]);
           cv[3] -= ef[bi][3] * (rg[3][0] * cv[0] + rg[3][1] * cv[1] + rg[3][2] * cv[2]);
-          *reinterpret_cast<f4*>(wslot + 4 * n) = cv;
         }
-        if (gp == 3) break;
-        lds_wait();
-        if (g > gp) {
-          const f4 w = *reinterpret_cast<const f4*>(wslot + 4 * n);
+        if constexpr (gp < 3) {
+          f4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            cv[i] -= ef[bi][i] * (rg[i][0] * w[0] + rg[i][1] * w[1] + rg[i][2] * w[2] + rg[i][3] * w[3]);
+          for (int j = 0; j < 4; ++j) w[j] = group_bcast<gp>(cv[j]);
+          if (g > gp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              cv[i] -= ef[bi][i] * (rg[i][0] * w[0] + rg[i][1] * w[1] + rg[i][2] * w[2] + rg[i][3] * w[3]);
+          }
         }
-        asm volatile("" ::: "memory");  // the next step's slot write stays after this read
-      }
+      });
       W[bi] = cv;
       // this block's share of the later blocks' sums
 #pragma unroll
@@ -636,8 +699,11 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
 template <typename InT, int DK>
 hipError_t launch_pv_t(const ScanParams& p, hipStream_t st, int phases) {
   if (phases & 1) {
-    hipLaunchKernelGGL((prep_pv_kernel<InT, DK>), dim3((unsigned)((size_t)p.BH * p.nchunks)), dim3(NT), 0,
-                       st, p);
+    const dim3 pgrid((unsigned)((size_t)p.BH * p.nchunks));
+    bool exact = false;
+    if constexpr (sizeof(InT) == 2) exact = (p.flags & kFlagPhiElu1) == 0;
+    if (exact) hipLaunchKernelGGL((prep_pv_kernel<InT, DK, sizeof(InT) == 2>), pgrid, dim3(NT), 0, st, p);
+    else hipLaunchKernelGGL((prep_pv_kernel<InT, DK, false>), pgrid, dim3(NT), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
