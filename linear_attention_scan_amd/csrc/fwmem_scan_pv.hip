@@ -36,7 +36,9 @@ constexpr int CH = kChunk;
 constexpr int NT = 256;
 constexpr int LDM = CH + 4;  // float stride of a [CH][CH] matrix
 
-// Record of one (head, chunk), floats: G [CH][CH] (strictly lower), P [CH][CH] (lower),
+// Record of one (head, chunk), floats: G [CH][CH] (strictly lower), P [CH][CH] (lower; with
+// bf16 inputs and the identity map, the same bytes hold P as bf16 hi and lo halves,
+// [2][CH][CH], for the propagate's bf16 products),
 // then per token: eta's denominator (infinite where there is no key to write), the
 // ridge lambda_t, and the rescale factors of x_t and q_t (1 without QK normalisation);
 // in chunk 0's record, the carried key (zero without one), so that the propagate kernel
@@ -210,7 +212,15 @@ __global__ __launch_bounds__(NT) void prep_pv_kernel(ScanParams p) {
       const int t = 16 * mt + 4 * g + i;
       const bool keep = mat == 0 ? s2 < t : s2 <= t;
       const float f = (mat == 0 ? s_nx[t] : s_mq[t]) * s_nx[s2];
-      dst[t * CH + s2] = keep ? f * acc[i] : 0.f;
+      const float v = keep ? f * acc[i] : 0.f;
+      if (EXACT && mat == 1) {
+        uint16_t* ph = reinterpret_cast<uint16_t*>(dst);
+        const uint16_t h = f32_to_bf16_bits(v);
+        ph[t * CH + s2] = h;
+        ph[CH * CH + t * CH + s2] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+      } else {
+        dst[t * CH + s2] = v;
+      }
     }
   }
 }
@@ -275,8 +285,8 @@ __device__ __forceinline__ void group_prefix(float v, int pv, int g, int n, floa
 
 template <int DK>
 constexpr size_t prop_pv_floats() {
-  // X, Q; G, P, beta, V; four token scalars
-  return 2 * (size_t)CH * (DK + 4) + 4 * (size_t)CH * LDM + 4 * CH;
+  // X, Q; G, P (fp32, or bf16 hi and lo rows of CH + 8), beta, V; four token scalars
+  return 2 * (size_t)CH * (DK + 4) + 3 * (size_t)CH * LDM + (size_t)CH * (CH + 8) + 4 * CH;
 }
 
 // 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
@@ -316,8 +326,11 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   uint16_t* Xb = reinterpret_cast<uint16_t*>(smem);  // [CH][LDB]
   uint16_t* Qb = Xb + CH * LDB;                      // [CH][LDB]
   float* Gs = Qs + CH * LDX;        // [CH][LDM]
-  float* Ps = Gs + CH * LDM;        // [CH][LDM]
-  float* Bs = Ps + CH * LDM;        // [CH][LDM] beta of the group's 64 columns
+  float* Ps = Gs + CH * LDM;        // [CH][LDM] (fp32 operands)
+  constexpr int LDPB = CH + 8;      // bf16 P rows (exact operands): hi [CH][LDPB], then lo
+  static_assert(CH * LDM <= CH * LDPB, "P space");
+  uint16_t* Pb = reinterpret_cast<uint16_t*>(Ps);
+  float* Bs = Ps + CH * LDPB;       // [CH][LDM] beta of the group's 64 columns
   float* Vs = Bs + CH * LDM;        // [CH][LDM] values of the group's 64 columns
   float* s_rden = Vs + CH * LDM;    // [CH] 1 / eta's denominator (0 where no key is written)
   float* s_lam = s_rden + CH;       // [CH]
@@ -433,7 +446,12 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = act_beta_pv(b[j], p.flags);
       *reinterpret_cast<f4*>(Gs + t * LDM + u) = pg[r];
-      *reinterpret_cast<f4*>(Ps + t * LDM + u) = pp[r];
+      if constexpr (EXACT) {  // granule gi of the record's [2][CH][CH] bf16 P
+        const int h = gi / (CH * CH / 8), rem = gi % (CH * CH / 8);
+        *reinterpret_cast<f4*>(Pb + h * CH * LDPB + (rem / 8) * LDPB + (rem % 8) * 8) = pp[r];
+      } else {
+        *reinterpret_cast<f4*>(Ps + t * LDM + u) = pp[r];
+      }
       *reinterpret_cast<f4*>(Bs + t * LDM + u) = b;  // rows past the end hold act(0); V is 0 there
     }
 #pragma unroll
@@ -579,14 +597,22 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
       f4 cv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cv[i] = rhs[bi][i] - ef[bi][i] * y[bi][i];
-      // this lane's rows of the diagonal block: G[16 bi + 4 g + i][16 bi + ...]
+      // this lane's rows of the diagonal block: G[16 bi + 4 g + i][16 bi + ...]; the rows
+      // against group gp + 1 are read while step gp computes
       const float* gd = Gs + (16 * bi + 4 * g) * LDM + 16 * bi;
+      f4 rgn[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rgn[i] = *reinterpret_cast<const f4*>(gd + i * LDM);
       static_for<0, 4>([&](auto GPc) {
         constexpr int gp = GPc;
         // the rows of group gp's own block, and this lane's rows against group gp
         f4 rg[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rg[i] = *reinterpret_cast<const f4*>(gd + i * LDM + 4 * gp);
+        for (int i = 0; i < 4; ++i) rg[i] = rgn[i];
+        if constexpr (gp < 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rgn[i] = *reinterpret_cast<const f4*>(gd + i * LDM + 4 * (gp + 1));
+        }
         if (g == gp) {
           cv[1] -= ef[bi][1] * (rg[1][0] * cv[0]);
           cv[2] -= ef[bi][2] * (rg[2][0] * cv[0] + rg[2][1] * cv[1]);
@@ -613,19 +639,36 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
     }
 
     // ---- O = Gamma o (Q S0) + Gamma^ o (P W~), stored
-    // P W~ with the products of the four row tiles interleaved (independent sums)
+    // P W~ with the products of the four row tiles interleaved (independent sums): on
+    // bf16 MFMA with P and W~ split into hi and lo halves (exact operands), else fp32
     f4 pws[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) pws[mt] = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (EXACT) {
+      bf8 wph[2], wpl[2];
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      f4 a[4];
+      for (int kq = 0; kq < 2; ++kq) split_c(W, kq, wph[kq], wpl[kq]);
 #pragma unroll
-      for (int mt = bk; mt < 4; ++mt) a[mt] = *reinterpret_cast<const f4*>(Ps + (16 * mt + n) * LDM + 16 * bk + 4 * g);
+      for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int part = 0; part < 3; ++part)
 #pragma unroll
-        for (int mt = bk; mt < 4; ++mt) pws[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][q], W[bk][q], pws[mt], 0, 0, 0);
+          for (int mt = 2 * kq; mt < 4; ++mt) {  // K block kq reaches row tiles 2 kq and up
+            const bf8 a = frag_pair(Pb + (part == 2 ? CH * LDPB : 0) + (16 * mt + n) * LDPB + 32 * kq + 4 * g);
+            mma_bf16(pws[mt], a, part == 1 ? wpl[kq] : wph[kq]);
+          }
+    } else {
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) {
+        f4 a[4];
+#pragma unroll
+        for (int mt = bk; mt < 4; ++mt) a[mt] = *reinterpret_cast<const f4*>(Ps + (16 * mt + n) * LDM + 16 * bk + 4 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int mt = bk; mt < 4; ++mt)
+            pws[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][q], W[bk][q], pws[mt], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
