@@ -250,6 +250,12 @@ __device__ __forceinline__ float group_bcast(float x) {
   return __uint_as_float((GP & 2) ? b[1] : b[0]);
 }
 
+// 16-byte buffer load: the hardware range check of the resource turns offsets past its
+// end into zeros.
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Sign of a parity bit applied to x.
 __device__ __forceinline__ float with_sign(float x, int parity) {
   return __int_as_float(__float_as_int(x) ^ (parity << 31));
@@ -348,6 +354,11 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   const float* bb = p.beta + rowbase * dv + 64 * grp;
 
   const float* rec0 = reinterpret_cast<const float*>(p.ws + (size_t)bh * p.nchunks * RecPV::kBytes);
+  constexpr uint32_t OES = 4;  // output element bytes (fp32; bf16 output halves it)
+  const bool obf = (p.flags & kFlagOutBf16) != 0;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const char*>(p.out) + rowbase * dv * (obf ? 2 : OES),
+                                         (uint32_t)(p.T * dv) * (obf ? 2u : OES));
+  const uint32_t olane = (uint32_t)(4 * g * dv + col);  // element offset of the lane's first row
   f4 s[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
@@ -371,35 +382,56 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   f4 psc = {0.f, 0.f, 0.f, 0.f};  // den, lambda, nx, mq of token tid (tid < CH)
   uint32_t xzero = 0;             // granules of the carried key (the sequence's first token)
 
+  // Buffer resources of the head's rows; rows past the sequence end read as zeros. The key
+  // resource starts one row early (x_t is the key before token t); the sequence's first
+  // token reads out of range and takes the carried key instead.
+  constexpr int ES = sizeof(InT);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kbase - DK, (uint32_t)(p.T * DK * ES));
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qbase, (uint32_t)(p.T * DK * ES));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vb, (uint32_t)((p.T * dv - 64 * grp) * ES));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(bb, (uint32_t)((p.T * dv - 64 * grp) * 4));
+  const __amdgpu_buffer_rsrc_t rw = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecPV::kBytes));
+  uint32_t ox[NGX], ob[4], ov[NGV];  // loop-invariant lane offsets (bytes from the chunk's first row)
+#pragma unroll
+  for (int r = 0; r < NGX; ++r) {
+    const int gi = tid + NT * r;
+    ox[r] = (uint32_t)(((gi / GPR) * DK + (gi % GPR) * VW) * ES);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gi = tid + NT * r;
+    ob[r] = (uint32_t)(((gi / 16) * dv + (gi % 16) * 4) * 4);
+  }
+#pragma unroll
+  for (int r = 0; r < NGV; ++r) {
+    const int gi = tid + NT * r;
+    ov[r] = (uint32_t)(((gi / (64 / VW)) * dv + (gi % (64 / VW)) * VW) * ES);
+  }
+
   auto prefetch = [&](int cn) {
-    const int tn = cn * CH;
-    const float* rec = reinterpret_cast<const float*>(p.ws + ((size_t)bh * p.nchunks + cn) * RecPV::kBytes);
+    const uint32_t sx = (uint32_t)(cn * CH * DK * ES), sv = (uint32_t)(cn * CH * dv);
+    const uint32_t sw = (uint32_t)((size_t)cn * RecPV::kBytes);
     xzero = 0;
 #pragma unroll
     for (int r = 0; r < NGX; ++r) {
-      const int gi = tid + NT * r, t = gi / GPR, cc = (gi % GPR) * VW, tau = tn + t;
-      px[r] = u32x4{0u, 0u, 0u, 0u};
-      pq[r] = u32x4{0u, 0u, 0u, 0u};
-      if (tau < p.T) {
-        if (tau >= 1) px[r] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(tau - 1) * DK + cc);
-        else xzero |= 1u << r;
-        pq[r] = *reinterpret_cast<const u32x4*>(qbase + (size_t)tau * DK + cc);
-      }
+      const bool first = cn == 0 && tid + NT * r < GPR;  // token 0 of the sequence
+      px[r] = bload16(rk, first ? 0x80000000u : ox[r], sx);
+      pq[r] = bload16(rq, ox[r], sx);
+      if (first) xzero |= 1u << r;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int gi = tid + NT * r, t = gi / 16, u = (gi % 16) * 4;
-      pg[r] = *reinterpret_cast<const f4*>(rec + RecPV::kG + 4 * gi);
-      pp[r] = *reinterpret_cast<const f4*>(rec + RecPV::kP + 4 * gi);
-      pb[r] = tn + t < p.T ? *reinterpret_cast<const f4*>(bb + (size_t)(tn + t) * dv + u) : f4{0.f, 0.f, 0.f, 0.f};
+      const uint32_t o = (uint32_t)(16 * (tid + NT * r));
+      pg[r] = __builtin_bit_cast(f4, bload16(rw, (uint32_t)(4 * RecPV::kG) + o, sw));
+      pp[r] = __builtin_bit_cast(f4, bload16(rw, (uint32_t)(4 * RecPV::kP) + o, sw));
+      pb[r] = __builtin_bit_cast(f4, bload16(rb, ob[r], sv * 4u));
     }
 #pragma unroll
-    for (int r = 0; r < NGV; ++r) {
-      const int gi = tid + NT * r, t = gi / (64 / VW), u = (gi % (64 / VW)) * VW;
-      pv[r] = tn + t < p.T ? *reinterpret_cast<const u32x4*>(vb + (size_t)(tn + t) * dv + u) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < CH)
+    for (int r = 0; r < NGV; ++r) pv[r] = bload16(rv, ov[r], sv * (uint32_t)ES);
+    if (tid < CH) {
+      const float* rec = reinterpret_cast<const float*>(p.ws + ((size_t)bh * p.nchunks + cn) * RecPV::kBytes);
       psc = f4{rec[RecPV::kDen + tid], rec[RecPV::kLam + tid], rec[RecPV::kNx + tid], rec[RecPV::kMq + tid]};
+    }
   };
 
   prefetch(0);
@@ -673,15 +705,13 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const f4 pw = pws[mt];
+      // rows past the sequence end fall outside the output resource
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tau = t0 + 16 * mt + 4 * g + i;
-        if (tau < p.T) {
-          const float o = Gam[mt][i] * QS[mt][i] + Gh[mt][i] * pw[i];
-          const size_t oi = (rowbase + tau) * dv + col;
-          if (p.flags & kFlagOutBf16) static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16_bits(o);
-          else static_cast<float*>(p.out)[oi] = o;
-        }
+        const float o = Gam[mt][i] * QS[mt][i] + Gh[mt][i] * pw[i];
+        const uint32_t so = (uint32_t)((t0 + 16 * mt + i) * dv);
+        if (obf) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o), ro, 2u * olane, 2u * so, 0);
+        else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ro, OES * olane, OES * so, 0);
       }
     }
 
