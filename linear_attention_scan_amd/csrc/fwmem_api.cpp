@@ -352,8 +352,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   }
 
   // Segmented scan: P segments of each head run as virtual heads (SegParams). The prep
-  // phase sets up the virtual states and builds every record; the propagate phase runs the
-  // local and the transition passes, then chains the segments and fixes up the outputs.
+  // phase sets up the virtual states and builds every record. With diagonal transitions
+  // the propagate phase forms each segment's own state, chains the segments and runs one
+  // pass from the true start states; otherwise it runs the local and the transition
+  // passes, then chains the segments and fixes up the outputs.
   char* ws = static_cast<char*>(workspace);
   const size_t VH = z.BH * (size_t)wl.P, dk = (size_t)shape->dk, dv = (size_t)shape->dv;
   fwmem::SegParams sp;
@@ -390,8 +392,14 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   sp.flags = p.flags;
   sp.diag = fwmem::seg_diagonal(mode->rule, mode->flags) ? 1 : 0;
   sp.q = q;
+  sp.v = v;
+  sp.beta = beta;
   sp.lam = lambda;
   sp.gam = reinterpret_cast<float*>(ws + wl.z);
+  // Diagonal transitions form each segment's own state directly and chain the segments
+  // first; the combine then writes the start states where the propagate pass starts.
+  sp.state_first = sp.diag;
+  if (sp.state_first) sp.S_start = sp.B0_S;
 
   fwmem::ScanParams pv = p;  // the local pass over the virtual heads
   pv.BH = (int)VH;
@@ -421,10 +429,17 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
     if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 1);
   }
   if (e == hipSuccess && (phases & 2)) {
-    e = fwmem::launch_scan(pv, hs, 2);
-    if (e == hipSuccess && !sp.diag) e = fwmem::launch_scan(pa, hs, 2);
-    if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
-    if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
+    if (sp.state_first) {
+      e = fwmem::launch_seg_state(sp, hs);
+      if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
+      if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 2);
+      if (e == hipSuccess) e = fwmem::launch_seg_extras(sp, hs);
+    } else {
+      e = fwmem::launch_scan(pv, hs, 2);
+      if (e == hipSuccess) e = fwmem::launch_scan(pa, hs, 2);
+      if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
+      if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
+    }
   }
   e = znorm(e);
   return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;

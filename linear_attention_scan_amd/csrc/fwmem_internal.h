@@ -189,8 +189,14 @@ struct SegParams {
   // segment's start through token t.
   int diag;
   const void* q;          // [BH][T][dk] raw queries
+  const void* v;          // [BH][T][dv] values
+  const float* beta;      // [BH][T] write scales (or pre-activations), or null (1)
   const float* lam;       // [BH][T] retention (or pre-activations), or null (1)
   float* gam;             // [BH*P][L]
+  // Diagonal transitions: the segments' own states come from seg_state before the
+  // propagate pass (B1 holds them, the combine writes each start state into B0 and the
+  // pass starts there), so the outputs need no fix-up.
+  int state_first;
   int BH, P, L, dk, dv, bf16;
   uint32_t flags;
 };
@@ -229,5 +235,7 @@ struct ZParams {
 hipError_t launch_znorm(const ZParams& z, hipStream_t st);
 hipError_t launch_seg_combine(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st);
+hipError_t launch_seg_state(const SegParams& s, hipStream_t st);
+hipError_t launch_seg_extras(const SegParams& s, hipStream_t st);
 
 }  // namespace fwmem

@@ -119,7 +119,7 @@ __device__ void combine_diagonal(const SegParams& s, int h, int j0) {
   }
   if (s.S_out != nullptr) {
     for (int r = 0; r < RP; ++r) s.S_out[((size_t)h * dk + i0 + 16 * r) * dv + j0 + j] = v[r];
-    combine_final_extras(s, h, j0);
+    if (!s.state_first) combine_final_extras(s, h, j0);
   }
 }
 
@@ -316,6 +316,223 @@ __global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
   }
 }
 
+// Eight K slots of a bf16 MFMA operand from a row-major [token][column] tile by two LDS
+// transpose reads: within each group of 16 lanes, lane 4r + c points at four values of
+// token row r, columns 4c..4c+3, and lane 4c + e receives column 4c + e of the four rows.
+// `p` is this lane's address for the first four K slots; `step` (elements) reaches the
+// rows of the other four.
+__device__ __forceinline__ bf8 tr_pair(const uint16_t* p, int step) {
+  typedef short s8v __attribute__((ext_vector_type(8)));
+  const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)p);
+  const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)(p + step));
+  const s8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf8, r);
+}
+
+// Diagonal transitions: each segment's own contribution to the state,
+//   B_p = sum_t (product of the retentions after t in the segment) beta_t x_t v_t^T,
+// plus Gamma_p S_in for segment 0, a [d_k x L] x [L x d_v] product per segment, so that
+// the combine gives every segment its start state before any output is formed. One
+// workgroup per segment walks its 64-token blocks from the end backwards, carrying the
+// product of the retentions after the block. x_t = phi(k_t) (times its QK factor) and
+// w_t v_t go to LDS as bf16 hi and lo rows; each of the eight waves owns a share of the
+// [d_k x d_v] result's 16 x 16 tiles, on bf16 MFMA with the split products
+// hi.hi, hi.lo and lo.hi, and reads the X^T and W operands with the LDS transpose read
+// (two reads of four tokens give a fragment's eight K slots).
+constexpr int kStateThreads = 512;
+
+template <typename InT, int DK, int DV>
+__global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
+  constexpr int LDX = DK + 8, LDW = DV + 8;  // bf16 row strides
+  constexpr int NT = kStateThreads, NW = NT / 64;
+  // wave w owns NMT d_k row tiles from mt0 against NNW value tiles from nt0
+  constexpr int NMTT = DK / 16;                        // d_k row tiles
+  constexpr int WPM = NW >= NMTT ? NW / NMTT : 1;      // waves that share a row tile
+  constexpr int NMT = NMTT >= NW ? NMTT / NW : 1;
+  constexpr int NNW = DV / 16 / WPM;
+  constexpr int VW = In<InT>::VW;
+  constexpr int GX = DK / VW, GV = DV / VW;  // 16-byte granules per row
+  constexpr int NGX = 64 * GX / NT, NGV = 64 * GV / NT;
+  static_assert(NGX >= 1 && NGV >= 1 && GX <= 64 && NNW >= 1, "granules");
+  __shared__ __align__(16) uint16_t xs[2][64 * LDX];  // hi, lo
+  __shared__ __align__(16) uint16_t ws[2][64 * LDW];
+  __shared__ float s_w[64];
+  __shared__ float s_tot;
+  const size_t vh = blockIdx.x;
+  const int p = (int)(vh % s.P), L = s.L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int mt0 = (wave / WPM) * NMT, nt0 = (wave % WPM) * NNW;
+  const bool elu = (s.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(s.flags, DK);
+  const InT* kb = static_cast<const InT*>(s.k) + vh * L * DK;
+  const InT* vb = static_cast<const InT*>(s.v) + vh * L * DV;
+  const float* lam = s.lam != nullptr ? s.lam + vh * L : nullptr;
+  const float* bet = s.beta != nullptr ? s.beta + vh * L : nullptr;
+
+  f4 acc[NMT][NNW];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NNW; ++nt) acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+  float carry = 1.f;  // product of the retentions after the current block
+  u32x4 rk[NGX], rv[NGV];
+  auto load_rows = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = tid + NT * r;
+      rk[r] = *reinterpret_cast<const u32x4*>(kb + (size_t)(t0 + gi / GX) * DK + (gi % GX) * VW);
+    }
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = tid + NT * r;
+      rv[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)(t0 + gi / GV) * DV + (gi % GV) * VW);
+    }
+  };
+  const int nblk = L / 64;
+  load_rows((nblk - 1) * 64);
+  for (int blk = nblk - 1; blk >= 0; --blk) {
+    const int t0 = blk * 64;
+    // token weights: w_t = beta_t times the retentions after t (inside the block, then
+    // after it); the block's product of retentions for the carry
+    if (wave == 0) {
+      const float gm = lam != nullptr ? act_lam(lam[t0 + lane], s.flags, false) : 1.f;
+      const float bt = bet != nullptr ? act_beta(bet[t0 + lane], s.flags) : 1.f;
+      float suf = gm;  // inclusive suffix product over lanes lane..63
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_down(suf, o);
+        if (lane + o < 64) suf *= u;
+      }
+      float after = __shfl_down(suf, 1);  // tokens after this one inside the block
+      if (lane == 63) after = 1.f;
+      s_w[lane] = bt * after * carry;
+      if (lane == 0) s_tot = suf;
+    }
+    __syncthreads();  // s_w; the previous block's operand reads are done
+    // rows of this block into LDS: phi(k) with its QK factor, and w v, split hi / lo
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = tid + NT * r, t = gi / GX, cc = (gi % GX) * VW;
+      float x[VW];
+      In<InT>::decode(rk[r], x);
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        if (elu) x[j] = phi_elu1(x[j]);
+        ss += x[j] * x[j];
+      }
+      if (len > 0.f) {
+        ss = group_sum<GX>(ss);
+        const float f = rescale_factor(ss, len);
+#pragma unroll
+        for (int j = 0; j < VW; ++j) x[j] *= f;
+      }
+#pragma unroll
+      for (int j = 0; j < VW; j += 8 < VW ? 8 : VW) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (j + e < VW) ? x[j + e] : 0.f;
+        bf8 hh, ll;
+        split8(y, hh, ll);
+        if (VW >= 8) {
+          *reinterpret_cast<bf8*>(&xs[0][t * LDX + cc + j]) = hh;
+          *reinterpret_cast<bf8*>(&xs[1][t * LDX + cc + j]) = ll;
+        } else {
+          typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<bf4*>(&xs[0][t * LDX + cc + j]) = bf4{hh[0], hh[1], hh[2], hh[3]};
+          *reinterpret_cast<bf4*>(&xs[1][t * LDX + cc + j]) = bf4{ll[0], ll[1], ll[2], ll[3]};
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = tid + NT * r, t = gi / GV, cc = (gi % GV) * VW;
+      float x[VW];
+      In<InT>::decode(rv[r], x);
+      const float wt = s_w[t];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) x[j] *= wt;
+#pragma unroll
+      for (int j = 0; j < VW; j += 8 < VW ? 8 : VW) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (j + e < VW) ? x[j + e] : 0.f;
+        bf8 hh, ll;
+        split8(y, hh, ll);
+        if (VW >= 8) {
+          *reinterpret_cast<bf8*>(&ws[0][t * LDW + cc + j]) = hh;
+          *reinterpret_cast<bf8*>(&ws[1][t * LDW + cc + j]) = ll;
+        } else {
+          typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<bf4*>(&ws[0][t * LDW + cc + j]) = bf4{hh[0], hh[1], hh[2], hh[3]};
+          *reinterpret_cast<bf4*>(&ws[1][t * LDW + cc + j]) = bf4{ll[0], ll[1], ll[2], ll[3]};
+        }
+      }
+    }
+    const float tot = s_tot;
+    __syncthreads();  // the block's operands are in LDS
+    if (blk > 0) load_rows(t0 - 64);
+    // B_p += X^T W over the block's two 32-token K blocks
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const int row = 32 * kq + 8 * g + (n >> 2);  // token row of this lane's first read
+      bf8 ah[NMT], al[NMT];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int col = 16 * (mt0 + mt) + 4 * (n & 3);
+        ah[mt] = tr_pair(&xs[0][row * LDX + col], 4 * LDX);
+        al[mt] = tr_pair(&xs[1][row * LDX + col], 4 * LDX);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NNW; ++nt) {
+        const int col = 16 * (nt0 + nt) + 4 * (n & 3);
+        const bf8 bhi = tr_pair(&ws[0][row * LDW + col], 4 * LDW);
+        const bf8 blo = tr_pair(&ws[1][row * LDW + col], 4 * LDW);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          mma_bf16(acc[mt][nt], ah[mt], bhi);
+          mma_bf16(acc[mt][nt], ah[mt], blo);
+          mma_bf16(acc[mt][nt], al[mt], bhi);
+        }
+      }
+    }
+    carry *= tot;
+  }
+  // segment 0 also carries the caller's state through the segment's decay
+  float* Bo = s.B1_S + vh * DK * DV;
+  const float* S0 = p == 0 ? s.B0_S + vh * DK * DV : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NNW; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t e = (size_t)(16 * (mt0 + mt) + 4 * g + i) * DV + 16 * (nt0 + nt) + n;
+        Bo[e] = acc[mt][nt][i] + (S0 != nullptr ? carry * S0[e] : 0.f);
+      }
+}
+
+// The caller's carried key and flag after a segmented scan whose combine ran before the
+// propagate pass (diagonal transitions): the last segment's key, written by that pass.
+__global__ __launch_bounds__(NTH) void seg_extras_kernel(SegParams s) {
+  const int h = blockIdx.x;
+  const size_t last = (size_t)h * s.P + s.P - 1;
+  if ((s.flags & kFlagZnorm) == 0)  // with the normaliser the slot holds z
+    for (int i = threadIdx.x; i < s.dk; i += NTH) s.xprev_out[(size_t)h * s.dk + i] = s.B1_x[last * s.dk + i];
+  if (threadIdx.x == 0) s.has_out[h] = 1;
+}
+
+template <typename InT>
+hipError_t launch_state_in(const SegParams& s, unsigned grid, hipStream_t st) {
+  const dim3 blk(kStateThreads);
+  if (s.dk == 64 && s.dv == 64) hipLaunchKernelGGL((seg_state_kernel<InT, 64, 64>), dim3(grid), blk, 0, st, s);
+  else if (s.dk == 64) hipLaunchKernelGGL((seg_state_kernel<InT, 64, 128>), dim3(grid), blk, 0, st, s);
+  else if (s.dv == 64) hipLaunchKernelGGL((seg_state_kernel<InT, 128, 64>), dim3(grid), blk, 0, st, s);
+  else hipLaunchKernelGGL((seg_state_kernel<InT, 128, 128>), dim3(grid), blk, 0, st, s);
+  return hipGetLastError();
+}
+
 template <typename InT>
 hipError_t launch_fixup_in(const SegParams& s, unsigned grid, hipStream_t st) {
   if (s.dk == 64 && s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<InT, 64, 64>), dim3(grid), dim3(NTH), 0, st, s);
@@ -359,6 +576,17 @@ hipError_t launch_seg_init(const SegParams& s, hipStream_t st) {
 
 hipError_t launch_seg_combine(const SegParams& s, hipStream_t st) {
   hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(s.BH * (s.dv / 16))), dim3(NTH), 0, st, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_state(const SegParams& s, hipStream_t st) {
+  const unsigned grid = (unsigned)((size_t)s.BH * s.P);
+  return s.bf16 ? launch_state_in<uint16_t>(s, grid, st) : launch_state_in<float>(s, grid, st);
+}
+
+hipError_t launch_seg_extras(const SegParams& s, hipStream_t st) {
+  if (s.S_out == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(seg_extras_kernel, dim3((unsigned)s.BH), dim3(NTH), 0, st, s);
   return hipGetLastError();
 }
 
