@@ -167,12 +167,16 @@ fwmem_status fwmem_state_bytes(const fwmem_shape* shape, size_t* bytes);
 
 /* Bytes of device workspace fwmem_scan_fwd needs for this shape and mode
  * (0 when T == 0). Its contents need no initialisation and are scratch only.
+ * Per (head, chunk) records for the prep phase, except for the additive rule with
+ * FWMEM_PHI_ELU1 on bf16 inputs, a scalar retention and no normaliser, whose one fused
+ * kernel keeps none (the size is then 0 unless the scan is segmented).
  * For few heads on a long sequence (when the scan would occupy a small part of the
- * GPU, T splits into 8 or 16 equal segments of at least 512 tokens that are multiples
- * of 64, and out is float32) the scan runs its segments in parallel and chains them
- * (the linear map of each segment is computed alongside); the workspace then also
- * holds two state buffers per segment, one d_k-vector per token and one start state
- * per segment. */
+ * GPU, T splits into equal segments of at least 512 tokens that are multiples of 64,
+ * and out is float32) the scan runs its segments in parallel and chains them. With a
+ * scalar retention (the additive rule without FWMEM_LAMBDA_PER_CHANNEL) the workspace
+ * then also holds two state buffers and one float per segment; otherwise (the linear
+ * map of each segment is computed alongside) four state buffers per segment, one
+ * d_k-vector per token and one start state per segment. */
 fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mode* mode,
                                         size_t* bytes);
 
@@ -195,6 +199,7 @@ fwmem_status fwmem_scan_workspace_bytes(const fwmem_shape* shape, const fwmem_mo
  *   out    [B][H][T][dv]  float32 (bf16 with FWMEM_OUT_BF16)   (required when T > 0)
  *   S_out  state buffer or NULL (final state not written); may equal S_in
  *   workspace, ws_bytes: device scratch of at least fwmem_scan_workspace_bytes()
+ *          (workspace may be NULL when that size is 0)
  *
  * After the call S_out holds S_T, x_prev = phi(k_T) and has_prev = 1 (T > 0), so a
  * later scan or fwmem_step continues the same sequence.
@@ -213,6 +218,9 @@ fwmem_status fwmem_scan_fwd(const fwmem_shape* shape, const void* q, const void*
  *              lambda and the carried key of S_in; writes only the workspace.
  *   propagate: the inter-chunk recurrence, serial along T: reads q, k, v, lambda,
  *              S_in and the workspace that prep wrote; writes out and S_out.
+ * The additive rule with FWMEM_PHI_ELU1 on bf16 inputs, a scalar retention and no
+ * normaliser runs all its per-chunk work in one fused kernel of the propagate phase;
+ * prep then only sets up the segments of a segmented scan (or does nothing).
  */
 fwmem_status fwmem_scan_chunk_prep(const fwmem_shape* shape, const void* q, const void* k,
                                    const void* v, const float* beta, const float* lambda,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfwmem.so")
 SOURCES = ["fwmem_api.cpp", "fwmem_scan.hip", "fwmem_scan_split.hip", "fwmem_prep_split.hip", "fwmem_step.hip",
-           "fwmem_segment.hip", "fwmem_znorm.hip", "fwmem_scan_pv.hip", "fwmem_backward.hip", "fwmem_backward_chunk.hip",
+           "fwmem_segment.hip", "fwmem_znorm.hip", "fwmem_scan_pv.hip", "fwmem_scan_add.hip", "fwmem_backward.hip", "fwmem_backward_chunk.hip",
            "fwmem_noalloc.hip"]
 ARCH = "gfx950"
 

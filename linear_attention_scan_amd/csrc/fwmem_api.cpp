@@ -104,6 +104,7 @@ struct WsLayout {
 };
 
 size_t record_bytes(int bf16, int dk, const fwmem_mode* m) {
+  if (fwmem::scan_add_path(bf16, m->rule, m->flags)) return 0;  // the fused kernel keeps no records
   return m->rule == FWMEM_RULE_DELTA_PV ? fwmem::scan_pv_record_bytes()
                                         : fwmem::scan_record_bytes(bf16, dk, m->flags);
 }
@@ -119,7 +120,8 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
   w.rec = 0;
   if (w.P > 1) {
     const size_t VH = BH * (size_t)w.P, dk = (size_t)s->dk, dv = (size_t)s->dv;
-    // diagonal transitions need no transition states, and gam [BH*T] in place of z
+    // diagonal transitions need no transition states, gam [BH*P] (each segment's decay)
+    // in place of z, and no separate start states (the combine writes them into B0)
     const bool diag = fwmem::seg_diagonal(m->rule, m->flags);
     const size_t sa = diag ? 0 : align256(4 * (VH * dk * dk + VH * dk + VH));
     const size_t sb = align256(4 * (VH * dk * dv + VH * dk + VH));
@@ -129,9 +131,9 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
     w.B1 = w.B0 + sb;
     off = w.B1 + sb;
     w.z = off;
-    off += align256(4 * BH * T * (diag ? 1 : dk));
+    off += align256(4 * (diag ? VH : BH * T * dk));
     w.start = off;
-    off += align256(4 * VH * dk * dv);
+    if (!diag) off += align256(4 * VH * dk * dv);
   }
   if (m->flags & FWMEM_ZNORM) {
     w.zr = off;
@@ -278,7 +280,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
                                                   z.nH, hs);
     return e == hipSuccess ? FWMEM_OK : FWMEM_ELAUNCH;
   }
-  if (workspace == nullptr || ws_bytes < need) return FWMEM_EWORKSPACE;
+  if (ws_bytes < need || (need > 0 && workspace == nullptr)) return FWMEM_EWORKSPACE;
 
   fwmem::ScanParams p;
   std::memset(&p, 0, sizeof(p));
@@ -398,8 +400,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   sp.gam = reinterpret_cast<float*>(ws + wl.z);
   // Diagonal transitions form each segment's own state directly and chain the segments
   // first; the combine then writes the start states where the propagate pass starts.
-  sp.state_first = sp.diag;
-  if (sp.state_first) sp.S_start = sp.B0_S;
+  if (sp.diag) sp.S_start = sp.B0_S;
 
   fwmem::ScanParams pv = p;  // the local pass over the virtual heads
   pv.BH = (int)VH;
@@ -425,11 +426,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   hipError_t e = hipSuccess;
   if (phases & 1) {
     e = fwmem::launch_seg_init(sp, hs);
-    if (e == hipSuccess && sp.diag) e = fwmem::launch_seg_decay(sp, hs);
     if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 1);
   }
   if (e == hipSuccess && (phases & 2)) {
-    if (sp.state_first) {
+    if (sp.diag) {
       e = fwmem::launch_seg_state(sp, hs);
       if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
       if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 2);

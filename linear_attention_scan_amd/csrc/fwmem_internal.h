@@ -125,6 +125,11 @@ hipError_t launch_prep_split(const ScanParams& p, hipStream_t stream);
 size_t scan_pv_record_bytes();
 hipError_t launch_scan_pv(const ScanParams& p, hipStream_t stream, int phases);
 hipError_t launch_prop_split(const ScanParams& p, hipStream_t stream);
+// The additive rule with elu + 1 features and a scalar retention on bf16 inputs
+// (without the normaliser) runs as one fused kernel per head (fwmem_scan_add.hip): the
+// prep phase does nothing, the propagate phase everything, and no record is written.
+bool scan_add_path(int bf16, int rule, uint32_t flags);
+hipError_t launch_scan_add(const ScanParams& p, hipStream_t stream);
 // Polls of a bounded wait before it gives up, and the offset of the awaited value: from
 // FWMEM_TEST_WAIT_TIMEOUT=n (n > 0, a test's setting: every wait gives up after n polls),
 // else 2^22 and 0.
@@ -184,19 +189,16 @@ struct SegParams {
   float* S_start;         // [BH*P][dk][dv] (segment p >= 1)
   float* out;             // [BH][T][dv] float32
   // Diagonal transitions (additive rule, scalar decay): a segment maps S to
-  // Gamma S + B, so there is no transition pass and no A or z buffer; the fix-up forms
-  // z_t = Gamma_t phi(q~_t) itself from the queries and gam, the decay from the
-  // segment's start through token t.
+  // Gamma_p S + B_p, so there is no transition pass and no A or z buffer. The segments'
+  // own states B_p come from seg_state before the propagate pass (B1 holds them, the
+  // combine writes each start state into B0 and the pass starts there), so the outputs
+  // need no fix-up.
   int diag;
   const void* q;          // [BH][T][dk] raw queries
   const void* v;          // [BH][T][dv] values
   const float* beta;      // [BH][T] write scales (or pre-activations), or null (1)
   const float* lam;       // [BH][T] retention (or pre-activations), or null (1)
-  float* gam;             // [BH*P][L]
-  // Diagonal transitions: the segments' own states come from seg_state before the
-  // propagate pass (B1 holds them, the combine writes each start state into B0 and the
-  // pass starts there), so the outputs need no fix-up.
-  int state_first;
+  float* gam;             // [BH*P] each segment's decay Gamma_p (diagonal transitions)
   int BH, P, L, dk, dv, bf16;
   uint32_t flags;
 };
@@ -207,7 +209,6 @@ __host__ __device__ inline bool seg_diagonal(int rule, uint32_t flags) {
 // Segment count for a scan of this shape: 1 (no segmentation) unless the propagate
 // grid would leave most of the GPU idle and T splits into equal chunk-aligned segments.
 int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint32_t flags);
-hipError_t launch_seg_decay(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_init(const SegParams& s, hipStream_t st);
 
 // ---- normalised linear attention (FWMEM_ZNORM; additive rule, scalar decay)

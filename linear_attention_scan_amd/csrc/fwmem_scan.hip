@@ -1215,6 +1215,7 @@ static hipError_t launch_scan_dk(const ScanParams& p, hipStream_t st, int ph) {
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t st, int phases) {
+  if (scan_add_path(p.bf16, p.rule, p.flags)) return (phases & 2) ? launch_scan_add(p, st) : hipSuccess;
   if (p.bf16)
     return p.dk == 64 ? launch_scan_dk<uint16_t, 64>(p, st, phases) : launch_scan_dk<uint16_t, 128>(p, st, phases);
   return p.dk == 64 ? launch_scan_dk<float, 64>(p, st, phases) : launch_scan_dk<float, 128>(p, st, phases);

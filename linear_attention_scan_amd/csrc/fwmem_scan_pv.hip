@@ -250,17 +250,6 @@ __device__ __forceinline__ float group_bcast(float x) {
   return __uint_as_float((GP & 2) ? b[1] : b[0]);
 }
 
-// 16-byte buffer load: the hardware range check of the resource turns offsets past its
-// end into zeros.
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// Sign of a parity bit applied to x.
-__device__ __forceinline__ float with_sign(float x, int parity) {
-  return __int_as_float(__float_as_int(x) ^ (parity << 31));
-}
-
 // Gate activation of beta with a hardware reciprocal (the fused variants of act_beta).
 __device__ __forceinline__ float act_beta_pv(float z, uint32_t flags) {
   if (flags & kFlagBetaSig) return __builtin_amdgcn_rcpf(1.f + __expf(-z));
@@ -293,28 +282,6 @@ template <int DK>
 constexpr size_t prop_pv_floats() {
   // X, Q; G, P (fp32, or bf16 hi and lo rows of CH + 8), beta, V; four token scalars
   return 2 * (size_t)CH * (DK + 4) + 3 * (size_t)CH * LDM + (size_t)CH * (CH + 8) + 4 * CH;
-}
-
-// 8 bf16 values of an A fragment whose K slots are 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide
-// K block (the order split_c gives the B side): two 8-byte LDS reads at p and p + 16.
-__device__ __forceinline__ bf8 frag_pair(const uint16_t* p) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p);
-  const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
-  return __builtin_bit_cast(bf8, u32x4{a.x, a.y, b.x, b.y});
-}
-
-// The same A fragment (K slots 4g..4g+3 and 16+4g..16+4g+3) of X^T, rows d_k 16 rt + n,
-// K = tokens, from the row-major X rows by two LDS transpose reads. Within each group of
-// 16 lanes, lane 4r + c points at 4 values of token row r, columns 4c..4c+3, and lane
-// 4c + e receives column 4c + e of the four rows. `p` is this lane's address for the first
-// four K slots (token 32 kq + 4g + (n >> 2), column 16 rt + 4 (n & 3)); the other four are
-// 16 rows further on.
-__device__ __forceinline__ bf8 xt_frag(const uint16_t* p, int ld) {
-  typedef short s8v __attribute__((ext_vector_type(8)));
-  const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)p);
-  const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(const void*)(p + 16 * ld));
-  const s8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf8, r);
 }
 
 template <typename InT, int DK, bool EXACT>

@@ -26,7 +26,10 @@ __global__ __launch_bounds__(NTH) void seg_init_kernel(SegParams s) {
   float* B = s.B0_S + (size_t)vh * dk * dv;
   float* A = s.A0_S + (size_t)vh * dk * dk;
   const float* Sin = (p == 0 && s.S_in != nullptr) ? s.S_in + (size_t)h * dk * dv : nullptr;
-  for (int e = threadIdx.x; e < dk * dv; e += NTH) B[e] = Sin != nullptr ? Sin[e] : 0.f;
+  // with the segment states formed first, the combine writes the start states of the
+  // later segments
+  if (p == 0 || !s.diag)
+    for (int e = threadIdx.x; e < dk * dv; e += NTH) B[e] = Sin != nullptr ? Sin[e] : 0.f;
   if (!s.diag)
     for (int e = threadIdx.x; e < dk * dk; e += NTH) A[e] = (e / dk == e % dk) ? 1.f : 0.f;
   const InT* kprev = static_cast<const InT*>(s.k) + ((size_t)vh * s.L - 1) * dk;  // p >= 1 only
@@ -48,39 +51,6 @@ __global__ __launch_bounds__(NTH) void seg_init_kernel(SegParams s) {
   }
 }
 
-// Diagonal transitions: gam[vh][t] = product of the retentions of the segment's tokens
-// 0..t, as a running product over chunks of 256 tokens (one token per thread, a prefix
-// product inside each wave, then across the four waves). A product that underflows
-// stands for a start state the segment has forgotten.
-__global__ __launch_bounds__(NTH) void seg_decay_kernel(SegParams s) {
-  const size_t vh = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ float wtot[NTH / 64];
-  const float* lam = s.lam != nullptr ? s.lam + vh * s.L : nullptr;
-  float* gam = s.gam + vh * s.L;
-  float carry = 1.f;
-  for (int base = 0; base < s.L; base += NTH) {
-    const int t = base + threadIdx.x;
-    float g = 1.f;
-    if (t < s.L && lam != nullptr) g = act_lam(lam[t], s.flags, false);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float u = __shfl_up(g, o);
-      if (lane >= o) g *= u;
-    }
-    if (lane == 63) wtot[wave] = g;
-    __syncthreads();
-    float pre = carry;
-    for (int w = 0; w < wave; ++w) pre *= wtot[w];
-    g *= pre;
-    if (t < s.L) gam[t] = g;
-    float tot = carry;
-    for (int w = 0; w < NTH / 64; ++w) tot *= wtot[w];
-    carry = tot;
-    __syncthreads();  // wtot is rewritten next round
-  }
-}
-
 // C += A B for a 16x16x16 block on fp32 MFMA: lane (g, n) supplies A[n][4g..4g+3] and
 // B[4g+q][n] (the C layout of a previous product); MFMA q sums over K = 4g + q.
 __device__ __forceinline__ void mma_f32_block(f4& acc, const f4& a, const f4& b) {
@@ -98,29 +68,22 @@ __device__ __forceinline__ void combine_final_extras(const SegParams& s, int h, 
   }
 }
 
-// Diagonal transitions: S_start(p+1) = Gamma_p S_start(p) + B_p, Gamma_p the segment's last
-// gam; every element on its own, one thread per element of the 16-column tile.
-__device__ void combine_diagonal(const SegParams& s, int h, int j0) {
-  const int dk = s.dk, dv = s.dv;
-  const int j = threadIdx.x & 15, i0 = threadIdx.x >> 4;  // rows i0, i0 + 16, ...
-  const int RP = dk / 16;
-  float v[8];
-  const float* B0 = s.B1_S + (size_t)(h * s.P) * dk * dv;
-  for (int r = 0; r < RP; ++r) v[r] = B0[(size_t)(i0 + 16 * r) * dv + j0 + j];
+// Diagonal transitions with the segment states formed first: S_start(p+1) = Gamma_p
+// S_start(p) + B_p, every element on its own, four consecutive elements per thread (one
+// 16-byte access per segment). Gamma_p is the segment's decay, from seg_state_kernel.
+__global__ __launch_bounds__(NTH) void seg_combine_diag_kernel(SegParams s) {
+  const size_t n = (size_t)s.dk * s.dv;  // a multiple of 4 NTH
+  const size_t nb = n / (4 * NTH);
+  const size_t h = blockIdx.x / nb;
+  const size_t e = ((blockIdx.x % nb) * NTH + threadIdx.x) * 4;
+  f4 v = *reinterpret_cast<const f4*>(s.B1_S + h * s.P * n + e);
   for (int p = 1; p < s.P; ++p) {
-    const size_t vh = (size_t)h * s.P + p;
-    float* St = s.S_start + vh * dk * dv;
-    const float* Bm = s.B1_S + vh * dk * dv;
-    const float gp = s.gam[vh * s.L + s.L - 1];
-    for (int r = 0; r < RP; ++r) {
-      St[(size_t)(i0 + 16 * r) * dv + j0 + j] = v[r];
-      v[r] = gp * v[r] + Bm[(size_t)(i0 + 16 * r) * dv + j0 + j];
-    }
+    const size_t vh = h * s.P + p;
+    *reinterpret_cast<f4*>(s.S_start + vh * n + e) = v;
+    const float gp = s.gam[vh];
+    v = gp * v + *reinterpret_cast<const f4*>(s.B1_S + vh * n + e);
   }
-  if (s.S_out != nullptr) {
-    for (int r = 0; r < RP; ++r) s.S_out[((size_t)h * dk + i0 + 16 * r) * dv + j0 + j] = v[r];
-    if (!s.state_first) combine_final_extras(s, h, j0);
-  }
+  if (s.S_out != nullptr) *reinterpret_cast<f4*>(s.S_out + h * n + e) = v;
 }
 
 // General transitions: S_start(p+1) = A_p S_start(p) + B_p, a [d_k x d_k] x [d_k x 16]
@@ -208,8 +171,7 @@ __device__ void combine_general(const SegParams& s, int h, int j0) {
 __global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
   const int ntile = s.dv / 16;
   const int h = blockIdx.x / ntile, j0 = (blockIdx.x % ntile) * 16;
-  if (s.diag) combine_diagonal(s, h, j0);
-  else if (s.dk == 64) combine_general<64>(s, h, j0);
+  if (s.dk == 64) combine_general<64>(s, h, j0);
   else combine_general<128>(s, h, j0);
 }
 
@@ -218,11 +180,8 @@ __global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
 // hi.lo and lo.hi keep about 16 bits of each factor). One workgroup per (virtual head,
 // group of up to kFixTiles token tiles); wave w owns value columns 16 NTW w ..
 // 16 NTW (w + 1) - 1 and keeps their S_start fragments in registers across the tiles.
-// Diagonal transitions: z_t = gam_t phi(q~_t), formed here from the queries (feature map
-// and QK normalisation as in the scan); the row factor is applied to the product.
 constexpr int kFixTiles = 2;
 
-__device__ __forceinline__ void load_row8(const uint16_t* p, float (&x)[8]) { In<uint16_t>::load(p, x); }
 __device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
   float a[4], b[4];
   In<float>::load(p, a);
@@ -234,7 +193,7 @@ __device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
   }
 }
 
-template <typename InT, int DK, int DV>
+template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
   constexpr int NKQ = DK / 32, NTW = DV / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -263,8 +222,6 @@ __global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
       }
     }
   }
-  const bool elu = (s.flags & kFlagPhiElu1) != 0;
-  const float len = qk_length(s.flags, DK);
   const int tt1 = min(ntb, (tg + 1) * kFixTiles);
   for (int tt = tg * kFixTiles; tt < tt1; ++tt) {
     const size_t row0 = vh * s.L + (size_t)tt * 64;
@@ -275,20 +232,10 @@ __global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
       f4 acc[NTW];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-      float ss = 0.f;
 #pragma unroll
       for (int kq = 0; kq < NKQ; ++kq) {
         float x[8];
-        if (s.diag) {
-          load_row8(static_cast<const InT*>(s.q) + row * DK + 32 * kq + 8 * g, x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (elu) x[e] = phi_elu1(x[e]);
-            ss += x[e] * x[e];
-          }
-        } else {
-          load_row8(s.z + row * DK + 32 * kq + 8 * g, x);
-        }
+        load_row8(s.z + row * DK + 32 * kq + 8 * g, x);
         bf8 ah, al;
         split8(x, ah, al);
 #pragma unroll
@@ -298,19 +245,12 @@ __global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
           mma_bf16(acc[j], al, bh[j][kq]);
         }
       }
-      float f = 1.f;
-      if (s.diag) {
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        f = s.gam[row] * (len > 0.f ? rescale_factor(ss, len) : 1.f);
-      }
-      // acc[j][i] is token 16 mt + 4 g + i, whose factor lane 4 g + i holds
+      // acc[j][i] is token 16 mt + 4 g + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float fi = __shfl(f, 4 * g + i);
         float* o = s.out + (row0 + 16 * mt + 4 * g + i) * DV + n;
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) o[16 * (NTW * wave + j)] += acc[j][i] * fi;
+        for (int j = 0; j < NTW; ++j) o[16 * (NTW * wave + j)] += acc[j][i];
       }
     }
   }
@@ -377,7 +317,12 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
     for (int nt = 0; nt < NNW; ++nt) acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
   float carry = 1.f;  // product of the retentions after the current block
   u32x4 rk[NGX], rv[NGV];
+  float rgm = 1.f, rbt = 1.f;  // raw gates of token lane of the block (wave 0)
   auto load_rows = [&](int t0) {
+    if (wave == 0) {
+      if (lam != nullptr) rgm = lam[t0 + lane];
+      if (bet != nullptr) rbt = bet[t0 + lane];
+    }
 #pragma unroll
     for (int r = 0; r < NGX; ++r) {
       const int gi = tid + NT * r;
@@ -396,8 +341,8 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
     // token weights: w_t = beta_t times the retentions after t (inside the block, then
     // after it); the block's product of retentions for the carry
     if (wave == 0) {
-      const float gm = lam != nullptr ? act_lam(lam[t0 + lane], s.flags, false) : 1.f;
-      const float bt = bet != nullptr ? act_beta(bet[t0 + lane], s.flags) : 1.f;
+      const float gm = lam != nullptr ? act_lam(rgm, s.flags, false) : 1.f;
+      const float bt = bet != nullptr ? act_beta(rbt, s.flags) : 1.f;
       float suf = gm;  // inclusive suffix product over lanes lane..63
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -471,7 +416,7 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
       }
     }
     const float tot = s_tot;
-    __syncthreads();  // the block's operands are in LDS
+    __syncthreads();  // the block's operands are in LDS; the gates are consumed
     if (blk > 0) load_rows(t0 - 64);
     // B_p += X^T W over the block's two 32-token K blocks
 #pragma unroll
@@ -499,6 +444,8 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
     }
     carry *= tot;
   }
+  // the segment's decay for the combine
+  if (tid == 0) s.gam[vh] = carry;
   // segment 0 also carries the caller's state through the segment's decay
   float* Bo = s.B1_S + vh * DK * DV;
   const float* S0 = p == 0 ? s.B0_S + vh * DK * DV : nullptr;
@@ -533,12 +480,11 @@ hipError_t launch_state_in(const SegParams& s, unsigned grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename InT>
-hipError_t launch_fixup_in(const SegParams& s, unsigned grid, hipStream_t st) {
-  if (s.dk == 64 && s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<InT, 64, 64>), dim3(grid), dim3(NTH), 0, st, s);
-  else if (s.dk == 64) hipLaunchKernelGGL((seg_fixup_kernel<InT, 64, 128>), dim3(grid), dim3(NTH), 0, st, s);
-  else if (s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<InT, 128, 64>), dim3(grid), dim3(NTH), 0, st, s);
-  else hipLaunchKernelGGL((seg_fixup_kernel<InT, 128, 128>), dim3(grid), dim3(NTH), 0, st, s);
+hipError_t launch_fixup_dims(const SegParams& s, unsigned grid, hipStream_t st) {
+  if (s.dk == 64 && s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<64, 64>), dim3(grid), dim3(NTH), 0, st, s);
+  else if (s.dk == 64) hipLaunchKernelGGL((seg_fixup_kernel<64, 128>), dim3(grid), dim3(NTH), 0, st, s);
+  else if (s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<128, 64>), dim3(grid), dim3(NTH), 0, st, s);
+  else hipLaunchKernelGGL((seg_fixup_kernel<128, 128>), dim3(grid), dim3(NTH), 0, st, s);
   return hipGetLastError();
 }
 
@@ -548,11 +494,12 @@ int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint3
   (void)dk;
   if (flags & kFlagOutBf16) return 1;
   const bool split = scan_split_path(bf16, flags);
-  const size_t groups = split ? (size_t)dv / kSplitCols : ((size_t)dv + 63) / 64;
+  const bool fused = scan_add_path(bf16, rule, flags);
+  const size_t groups = fused ? 1 : split ? (size_t)dv / kSplitCols : ((size_t)dv + 63) / 64;
   const size_t wgs = BH * groups;
-  // propagate workgroups resident at once: one per CU, two for the general pair's rules
+  // propagate workgroups resident at once: one per CU; two for the general pair's rules
   // without a solve or per-channel decay (the diagonal ones), whose LDS fits twice
-  const size_t cap = (!split && seg_diagonal(rule, flags)) ? 512 : 256;
+  const size_t cap = (!fused && !split && seg_diagonal(rule, flags)) ? 512 : 256;
   int P = 1;
   while (P < 16 && wgs * 2 * P <= cap && T % (64 * 2 * (size_t)P) == 0 && T / (2 * (size_t)P) >= 512) P *= 2;
   // With a transition pass the propagate work doubles, so fewer than 8 segments do not
@@ -560,11 +507,6 @@ int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint3
   // its transitions were made diagonal); diagonal transitions pay from 2.
   if (seg_diagonal(rule, flags)) return P;
   return P >= 8 ? P : 1;
-}
-
-hipError_t launch_seg_decay(const SegParams& s, hipStream_t st) {
-  hipLaunchKernelGGL(seg_decay_kernel, dim3((unsigned)((size_t)s.BH * s.P)), dim3(NTH), 0, st, s);
-  return hipGetLastError();
 }
 
 hipError_t launch_seg_init(const SegParams& s, hipStream_t st) {
@@ -575,6 +517,11 @@ hipError_t launch_seg_init(const SegParams& s, hipStream_t st) {
 }
 
 hipError_t launch_seg_combine(const SegParams& s, hipStream_t st) {
+  if (s.diag) {
+    const size_t nb = (size_t)s.dk * s.dv / (4 * NTH);
+    hipLaunchKernelGGL(seg_combine_diag_kernel, dim3((unsigned)(s.BH * nb)), dim3(NTH), 0, st, s);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(s.BH * (s.dv / 16))), dim3(NTH), 0, st, s);
   return hipGetLastError();
 }
@@ -594,8 +541,7 @@ hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st) {
   const size_t ngrp = ((size_t)s.L / 64 + kFixTiles - 1) / kFixTiles;
   const size_t n = (size_t)s.BH * (s.P - 1) * ngrp;
   if (n == 0) return hipSuccess;
-  // the queries (diagonal transitions) are read in the input type; z is float32
-  return s.bf16 ? launch_fixup_in<uint16_t>(s, (unsigned)n, st) : launch_fixup_in<float>(s, (unsigned)n, st);
+  return launch_fixup_dims(s, (unsigned)n, st);
 }
 
 }  // namespace fwmem

@@ -60,6 +60,14 @@ def test_state_and_workspace_sizes():
                            F.mode(rule=F.RULE_ADDITIVE, flags=F.ZNORM))
     al = lambda n: (n + 255) // 256 * 256
     assert wz == al(wa) + al(4 * B * H * 3 * (132 + dk)) + al(4 * B * H * 3 * dk)
+    # the fused additive elu+1 kernel (bf16, scalar retention) keeps no records; segmented
+    # (2 heads of T = 16384: 16 segments), it needs two virtual states and one float per segment
+    assert F.workspace_bytes(F.shape(B, H, 130, dk, dv, F.BF16),
+                             F.mode(rule=F.RULE_ADDITIVE, flags=F.PHI_ELU1)) == 0
+    wseg = F.workspace_bytes(F.shape(1, 2, 16384, 128, 128, F.BF16),
+                             F.mode(rule=F.RULE_ADDITIVE, flags=F.PHI_ELU1))
+    VH = 2 * 16
+    assert wseg == 2 * al(4 * (VH * 128 * 128 + VH * 128 + VH)) + al(4 * VH)
 
 
 FAKE = 0x10000  # never dereferenced: every case below fails a host check first

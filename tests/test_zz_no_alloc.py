@@ -46,11 +46,10 @@ def _both(w):
 
 def test_noalloc_matches_the_workspace_entry_point_twice():
     # the first call fills more of the scratch than the second: a delta-rule scan on the
-    # split pair, then a smaller additive elu+1 scan (general pair, other head sizes)
+    # split pair, then a smaller delta-rule elu+1 scan (general pair, other head sizes)
     cases = [wl.delta_bf16(seed=0, B=2, H=4, T=1000),
-             wl.make_scan(B=1, H=2, T=130, dk=64, dv=128, dtype="bf16", rule=wl.RULE_ADDITIVE,
-                          phi=wl.PHI_ELU1, beta_kind="sigmoid", lam_kind="gamma",
-                          normalise_qk=False, seed=3)]
+             wl.make_scan(B=1, H=2, T=130, dk=64, dv=128, dtype="bf16", phi=wl.PHI_ELU1,
+                          beta_kind="sigmoid", lam_kind="softplus", normalise_qk=False, seed=3)]
     sizes = []
     for w in cases:
         say(f"noalloc: rule {w.rule} B{w.B} H{w.H} T{w.T} dk{w.dk} dv{w.dv}")
