@@ -736,6 +736,486 @@ __global__ __launch_bounds__(NT) void prop_pv_kernel(ScanParams p) {
   }
 }
 
+// ---- the propagate with its roles split (bf16 inputs, identity map): one workgroup per
+// (head, 32 value columns), so that every CU holds one and each of its four waves has a
+// SIMD of its own. Waves 0 and 1 hold the state (X S, Q S, P W~, the outputs and the S
+// update), waves 2 and 3 solve the triangular systems; waves w and w + 2 own value columns
+// 16 w .. 16 w + 15 of the group.
+// Three workgroup barriers per chunk:
+//   [A] state: X S -> hand-off         solver: its per-(token, column) factors
+//   [B] solver: right-hand sides and W~ -> hand-off
+//       state: Q S, its own factors (Gamma, Gamma^), the previous chunk's outputs, the
+//              next chunk's X into LDS
+//   [C] state: the S update, the next chunk's Q and P into LDS
+//       solver: the next chunk's G, V and token scalars into LDS
+// so that the solve, the longest serial part of a chunk, runs beside the output work, and
+// the chain from one chunk's W~ to the next chunk's X S holds only the S update. Each role
+// loads the next chunk's rows into registers early in the chunk. X, P and the token
+// scalars have two LDS buffers, since the state waves still read this chunk's after [C]
+// (P until [C] of the next chunk); G and V are read by the solver waves alone, Q only
+// between [B] and [C].
+template <int DK>
+struct Pv2Lds {
+  static constexpr int LDB = DK + 8, LDPB = CH + 8, LDV2 = 32 + 4;
+  static constexpr size_t kX = 0;                                  // uint16 [2][CH][LDB]
+  static constexpr size_t kQ = kX + 2 * (size_t)CH * LDB * 2;      // uint16 [CH][LDB]
+  static constexpr size_t kP = kQ + (size_t)CH * LDB * 2;          // uint16 [2][2][CH][LDPB] (buffer, hi/lo)
+  static constexpr size_t kG = kP + 4 * (size_t)CH * LDPB * 2;     // float [CH][LDM]
+  static constexpr size_t kV = kG + (size_t)CH * LDM * 4;          // float [CH][LDV2]
+  static constexpr size_t kSc = kV + (size_t)CH * LDV2 * 4;        // float [2][4][CH]: 1/den, lambda, nx, mq
+  static constexpr size_t kH1 = kSc + 2 * 4 * (size_t)CH * 4;      // f4 [2 waves][4][64 lanes]: X S
+  static constexpr size_t kH2 = kH1 + 2 * 4 * 64 * 16;             // f4 [2 waves][4][64 lanes]: W~
+  static constexpr size_t kBytes = kH2 + 2 * 4 * 64 * 16;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void prop_pv2_kernel(ScanParams p) {
+  using L = Pv2Lds<DK>;
+  constexpr int NR = 128;  // threads per role
+  constexpr int NRT = DK / 16, LDB = L::LDB, LDPB = L::LDPB, LDV2 = L::LDV2;
+  static_assert(L::kBytes <= 160 * 1024, "LDS");
+  __shared__ __align__(16) char smem[L::kBytes];
+  uint16_t* const Xb0 = reinterpret_cast<uint16_t*>(smem + L::kX);
+  uint16_t* const Qb = reinterpret_cast<uint16_t*>(smem + L::kQ);
+  uint16_t* const Pb0 = reinterpret_cast<uint16_t*>(smem + L::kP);
+  float* const Gs = reinterpret_cast<float*>(smem + L::kG);
+  float* const Vs = reinterpret_cast<float*>(smem + L::kV);
+  float* const Sc0 = reinterpret_cast<float*>(smem + L::kSc);
+  f4* const H1 = reinterpret_cast<f4*>(smem + L::kH1);
+  f4* const H2 = reinterpret_cast<f4*>(smem + L::kH2);
+
+  // The column groups of a head read the same rows and records. Workgroups are dealt to
+  // the eight XCDs in turn, so with a multiple of eight heads, groups of one head take
+  // workgroup indices eight apart and share an XCD's L2.
+  const int ngrp = p.dv / 32, blk = blockIdx.x;
+  const bool xcd = (p.BH & 7) == 0;
+  const int bh = xcd ? (blk / (8 * ngrp)) * 8 + (blk & 7) : blk / ngrp;
+  const int grp = xcd ? (blk >> 3) % ngrp : blk % ngrp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool solver = wave >= 2;
+  const int w4 = wave & 1, rt_id = tid & (NR - 1);  // wave and thread index within the role
+  const int g = lane >> 4, n = lane & 15;
+  const int dv = p.dv, cw = 16 * w4 + n;  // the lane's column within the group
+  const int col = 32 * grp + cw;
+  const size_t rowbase = (size_t)bh * p.T;
+  constexpr int ES = 2;
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + rowbase * DK;
+  const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + rowbase * DK;
+  const uint16_t* vb = static_cast<const uint16_t*>(p.v) + rowbase * dv + 32 * grp;
+  const float* bb = p.beta + rowbase * dv + 32 * grp;
+  const float* rec0 = reinterpret_cast<const float*>(p.ws + (size_t)bh * p.nchunks * RecPV::kBytes);
+  const bool obf = (p.flags & kFlagOutBf16) != 0;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const char*>(p.out) + rowbase * dv * (obf ? 2 : 4),
+                                         (uint32_t)(p.T * dv) * (obf ? 2u : 4u));
+  const uint32_t olane = (uint32_t)(4 * g * dv + col);
+
+  // Buffer resources of the head's rows; rows past the sequence end read as zeros. The key
+  // resource starts one row early (x_t is the key before token t); the sequence's first
+  // token reads out of range and takes the carried key from the record.
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kbase - DK, (uint32_t)(p.T * DK * ES));
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qbase, (uint32_t)(p.T * DK * ES));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vb, (uint32_t)((p.T * dv - 32 * grp) * ES));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(bb, (uint32_t)((p.T * dv - 32 * grp) * 4));
+  const __amdgpu_buffer_rsrc_t rw = rsrc(rec0, (uint32_t)((size_t)p.nchunks * RecPV::kBytes));
+
+  // ---- registers of the next chunk's rows, and each role's raw beta of the lane's rows
+  // 16 mt + 4 g + i, column col, for the next chunk
+  constexpr int GPR = DK / 8;               // granules per X / Q row
+  constexpr int NGX = CH * GPR / NR;        // X (and Q) granules per thread
+  static_assert(NGX >= 1 && (CH * GPR) % NR == 0, "granules");
+  constexpr int NGM = CH * CH / 4 / NR;  // granules of a [CH][CH] fp32 matrix (or the bf16 P pair) per thread
+  constexpr int NGV = CH * 4 / NR;       // value granules per thread (four per 32-column row)
+  u32x4 px[NGX], pq[NGX], pp[NGM], pg[NGM], pv[NGV];
+  f4 psc = {0.f, 0.f, 0.f, 0.f};
+  uint32_t xzero = 0;
+  auto load_beta = [&](int cn, float (&bq)[4][4]) {
+    const uint32_t sv = (uint32_t)(cn * CH * dv);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bq[mt][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rb, (uint32_t)(((16 * mt + 4 * g + i) * dv + cw) * 4), sv * 4u, 0));
+  };
+  // the rows of chunk cn into registers: X, Q, P (state role), G, V, token scalars (solver)
+  auto prefetch_state = [&](int cn) {
+    const uint32_t sx = (uint32_t)(cn * CH * DK * ES);
+    const uint32_t sw = (uint32_t)((size_t)cn * RecPV::kBytes);
+    xzero = 0;
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = rt_id + NR * r;
+      const bool first = cn == 0 && gi < GPR;  // token 0 of the sequence
+      const uint32_t o = (uint32_t)(((gi / GPR) * DK + (gi % GPR) * 8) * ES);
+      px[r] = bload16(rk, first ? 0x80000000u : o, sx);
+      pq[r] = bload16(rq, o, sx);
+      if (first) xzero |= 1u << r;
+    }
+#pragma unroll
+    for (int r = 0; r < NGM; ++r)
+      pp[r] = bload16(rw, (uint32_t)(4 * RecPV::kP) + (uint32_t)(16 * (rt_id + NR * r)), sw);
+  };
+  auto prefetch_solver = [&](int cn) {
+    const uint32_t sv = (uint32_t)(cn * CH * dv);
+    const uint32_t sw = (uint32_t)((size_t)cn * RecPV::kBytes);
+#pragma unroll
+    for (int r = 0; r < NGM; ++r)
+      pg[r] = bload16(rw, (uint32_t)(4 * RecPV::kG) + (uint32_t)(16 * (rt_id + NR * r)), sw);
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = rt_id + NR * r;
+      pv[r] = bload16(rv, (uint32_t)(((gi / 4) * dv + (gi % 4) * 8) * ES), sv * (uint32_t)ES);
+    }
+    if (rt_id < CH) {
+      const float* rec = reinterpret_cast<const float*>(p.ws + ((size_t)bh * p.nchunks + cn) * RecPV::kBytes);
+      psc = f4{rec[RecPV::kDen + rt_id], rec[RecPV::kLam + rt_id], rec[RecPV::kNx + rt_id], rec[RecPV::kMq + rt_id]};
+    }
+  };
+  // registers -> LDS for chunk cn (its X, P and token-scalar buffers cn & 1)
+  auto stage_x = [&](int cn) {
+    uint16_t* Xb = Xb0 + (cn & 1) * CH * LDB;
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = rt_id + NR * r, t = gi / GPR, cc = (gi % GPR) * 8;
+      u32x4 w = px[r];
+      if ((xzero >> r) & 1u) {  // the carried key, already bf16-exact in the record
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = (uint32_t)f32_to_bf16_bits(rec0[RecPV::kX0 + cc + 2 * j]) |
+                 ((uint32_t)f32_to_bf16_bits(rec0[RecPV::kX0 + cc + 2 * j + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(Xb + t * LDB + cc) = w;
+    }
+  };
+  auto stage_qp = [&](int cn) {
+    uint16_t* Pb = Pb0 + (cn & 1) * 2 * CH * LDPB;
+#pragma unroll
+    for (int r = 0; r < NGX; ++r) {
+      const int gi = rt_id + NR * r;
+      *reinterpret_cast<u32x4*>(Qb + (gi / GPR) * LDB + (gi % GPR) * 8) = pq[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NGM; ++r) {  // granule gi of the record's [2][CH][CH] bf16 P
+      const int gi = rt_id + NR * r, h = gi / (CH * CH / 8), rem = gi % (CH * CH / 8);
+      *reinterpret_cast<u32x4*>(Pb + h * CH * LDPB + (rem / 8) * LDPB + (rem % 8) * 8) = pp[r];
+    }
+  };
+  auto stage_solver = [&](int cn) {
+#pragma unroll
+    for (int r = 0; r < NGM; ++r) {
+      const int gi = rt_id + NR * r;
+      *reinterpret_cast<u32x4*>(Gs + (gi / 16) * LDM + (gi % 16) * 4) = pg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NGV; ++r) {
+      const int gi = rt_id + NR * r, t = gi / 4, u = (gi % 4) * 8;
+      float x[8];
+      In<uint16_t>::decode(pv[r], x);
+      *reinterpret_cast<f4*>(Vs + t * LDV2 + u) = f4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f4*>(Vs + t * LDV2 + u + 4) = f4{x[4], x[5], x[6], x[7]};
+    }
+    if (rt_id < CH) {
+      float* sc = Sc0 + (cn & 1) * 4 * CH;
+      sc[rt_id] = 1.f / psc[0];
+      sc[CH + rt_id] = psc[1];
+      sc[2 * CH + rt_id] = psc[2];
+      sc[3 * CH + rt_id] = psc[3];
+    }
+  };
+
+  // ---- per (token, column) factors of chunk cn: eta, and the in-chunk prefix of log2 |a|
+  // (a sum over the lane's rows and the column's four lane groups, with a sign parity)
+  float eta[4][4], gl[4][4], la[4][4];
+  int pgr[4][4], ngr[4][4];
+  float gA = 0.f, gC = 0.f;
+  int pA = 0, pC = 0;
+  auto prefix = [&](const float (&bq)[4][4], const float* sc) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * g + i;
+        const float e = act_beta_pv(bq[mt][i], p.flags) * sc[t];  // 0 where there is no key
+        const float a = 1.f - e * sc[CH + t];
+        eta[mt][i] = e;
+        la[mt][i] = __builtin_amdgcn_logf(fmaxf(fabsf(a), 1e-30f));
+        ngr[mt][i] = a < 0.f ? 1 : 0;
+      }
+    float carry = 0.f;
+    int pcarry = 0;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float run = 0.f;
+      int prun = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        run += la[mt][i];
+        prun ^= ngr[mt][i];
+        gl[mt][i] = run;
+        pgr[mt][i] = prun;
+      }
+      float excl, tot;
+      int pexcl, ptot;
+      group_prefix(run, prun, g, n, excl, pexcl, tot, ptot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gl[mt][i] += carry + excl;
+        pgr[mt][i] ^= pcarry ^ pexcl;
+      }
+      carry += tot;
+      pcarry ^= ptot;
+    }
+    // anchor A = token 31 (row tile 1, g = 3, i = 3); chunk end C = token 63
+    gA = __shfl(gl[1][3], 48 + n);
+    pA = __shfl(pgr[1][3], 48 + n);
+    gC = __shfl(gl[3][3], 48 + n);
+    pC = __shfl(pgr[3][3], 48 + n);
+  };
+
+  if (solver) {
+    float bq[4][4];
+    prefetch_solver(0);
+    stage_solver(0);
+    load_beta(0, bq);
+    for (int c = 0; c < p.nchunks; ++c) {
+      const float* sc = Sc0 + (c & 1) * 4 * CH;
+      __syncthreads();  // [A] chunk c is in LDS
+      if (c + 1 < p.nchunks) prefetch_solver(c + 1);
+      // ---- the factors of the triangular system: rhs = cf V - gp (X S), ef = cf Gh_{t-1},
+      // with cf = eta / Gh. The factors of token t-1 are those of the lane's previous row,
+      // except in its first row, where they are formed from the prefix before token t.
+      float cfv[4][4], gpv[4][4], ef[4][4];
+      prefix(bq, sc);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pa = pgr[mt][i] ^ pA;
+          float gprev;
+          int pprev;
+          if (i == 0) {
+            gprev = gl[mt][i] - la[mt][i];
+            pprev = pgr[mt][i] ^ ngr[mt][i];
+          } else {
+            gprev = gl[mt][i - 1];
+            pprev = pgr[mt][i - 1];
+          }
+          const float cf = eta[mt][i] * with_sign(__builtin_amdgcn_exp2f(gA - gl[mt][i]), pa);  // eta / Gh
+          cfv[mt][i] = cf;
+          gpv[mt][i] = cf * with_sign(__builtin_amdgcn_exp2f(gprev), pprev);
+          ef[mt][i] = cf * with_sign(__builtin_amdgcn_exp2f(gprev - gA), pprev ^ pA);
+        }
+      __syncthreads();  // [B] X S0 handed over
+      // ---- right-hand sides, then W~ by blocked forward substitution. The off-diagonal
+      // 16 x 16 blocks run on fp32 MFMA: once block bk is solved, its product with G goes
+      // into the running sums y of every later block. Inside a diagonal block the rows go
+      // in four groups of four, each held by one lane group (lane (g, n) owns rows
+      // 4g..4g+3 of column n): group gp solves its 4 x 4 lower-triangular block in
+      // registers, lane swaps hand its four values to the other groups of the column, and
+      // the later groups subtract ef (G w).
+      float rhs[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f4 xs = H1[(w4 * 4 + mt) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rhs[mt][i] = cfv[mt][i] * Vs[(16 * mt + 4 * g + i) * LDV2 + cw] - gpv[mt][i] * xs[i];
+      }
+      f4 W[4], y[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) y[bi] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f4 cv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[i] = rhs[bi][i] - ef[bi][i] * y[bi][i];
+        const float* gd = Gs + (16 * bi + 4 * g) * LDM + 16 * bi;
+        f4 rgn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rgn[i] = *reinterpret_cast<const f4*>(gd + i * LDM);
+        static_for<0, 4>([&](auto GPc) {
+          constexpr int gp = GPc;
+          f4 rg[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rg[i] = rgn[i];
+          if constexpr (gp < 3) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rgn[i] = *reinterpret_cast<const f4*>(gd + i * LDM + 4 * (gp + 1));
+          }
+          if (g == gp) {
+            cv[1] -= ef[bi][1] * (rg[1][0] * cv[0]);
+            cv[2] -= ef[bi][2] * (rg[2][0] * cv[0] + rg[2][1] * cv[1]);
+            cv[3] -= ef[bi][3] * (rg[3][0] * cv[0] + rg[3][1] * cv[1] + rg[3][2] * cv[2]);
+          }
+          if constexpr (gp < 3) {
+            f4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = group_bcast<gp>(cv[j]);
+            if (g > gp) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                cv[i] -= ef[bi][i] * (rg[i][0] * w[0] + rg[i][1] * w[1] + rg[i][2] * w[2] + rg[i][3] * w[3]);
+            }
+          }
+        });
+        W[bi] = cv;
+        H2[(w4 * 4 + bi) * 64 + lane] = cv;
+#pragma unroll
+        for (int bl = bi + 1; bl < 4; ++bl) {
+          const f4 a = *reinterpret_cast<const f4*>(Gs + (16 * bl + n) * LDM + 16 * bi + 4 * g);
+          mma_block(y[bl], a, W[bi]);
+        }
+      }
+      __syncthreads();  // [C] W~ handed over; G and V are free
+      if (c + 1 < p.nchunks) {
+        stage_solver(c + 1);
+        load_beta(c + 1, bq);
+      }
+    }
+    if (grp == 0 && p.S_out != nullptr) {
+      const uint16_t* kl = kbase + (size_t)(p.T - 1) * DK;
+      for (int i = rt_id; i < DK; i += NR) p.xprev_out[(size_t)bh * DK + i] = In<uint16_t>::load1(kl + i);
+      if (rt_id == 0) p.has_out[bh] = 1;
+    }
+  } else {
+    f4 s[NRT];  // the state slice
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[rt][i] = p.S_in != nullptr ? p.S_in[((size_t)bh * DK + 16 * rt + 4 * g + i) * dv + col] : 0.f;
+    float bq[4][4];
+    prefetch_state(0);
+    stage_x(0);
+    stage_qp(0);
+    load_beta(0, bq);
+    // The outputs of chunk c are formed while the solver works on chunk c + 1, from what
+    // chunk c leaves: its W~, Q S0, factors, and P (whose LDS buffer the solver rewrites
+    // only after [C] of chunk c + 1).
+    f4 Wp[4], QSp[4];
+    float Gamp[4][4], Ghp[4][4];
+    auto outputs = [&](int cp) {
+      const uint16_t* Pb = Pb0 + (cp & 1) * 2 * CH * LDPB;
+      f4 pws[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) pws[mt] = f4{0.f, 0.f, 0.f, 0.f};
+      bf8 wph[2], wpl[2];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) split_c(Wp, kq, wph[kq], wpl[kq]);
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int mt = 2 * kq; mt < 4; ++mt) {  // K block kq reaches row tiles 2 kq and up
+            const bf8 a = frag_pair(Pb + (part == 2 ? CH * LDPB : 0) + (16 * mt + n) * LDPB + 32 * kq + 4 * g);
+            mma_bf16(pws[mt], a, part == 1 ? wpl[kq] : wph[kq]);
+          }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = Gamp[mt][i] * QSp[mt][i] + Ghp[mt][i] * pws[mt][i];
+          const uint32_t so = (uint32_t)((cp * CH + 16 * mt + i) * dv);
+          if (obf) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o), ro, 2u * olane, 2u * so, 0);
+          else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ro, 4u * olane, 4u * so, 0);
+        }
+    };
+    for (int c = 0; c < p.nchunks; ++c) {
+      const uint16_t* Xb = Xb0 + (c & 1) * CH * LDB;
+      const float* sc = Sc0 + (c & 1) * 4 * CH;
+      const float* s_nx = sc + 2 * CH;
+      const float* s_mq = sc + 3 * CH;
+      __syncthreads();  // [A] chunk c is in LDS
+      // ---- X S0 (C layout: rows 16 mt + 4 g + i, column n), rows rescaled -> hand-off
+      bf8 sh[DK / 32], sl[DK / 32];
+#pragma unroll
+      for (int kq = 0; kq < DK / 32; ++kq) split_c(s, kq, sh[kq], sl[kq]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < DK / 32; ++kq) {
+          const bf8 ax = frag_pair(Xb + (16 * mt + n) * LDB + 32 * kq + 4 * g);
+          mma_bf16(xs, ax, sh[kq]);
+          mma_bf16(xs, ax, sl[kq]);
+        }
+        H1[(w4 * 4 + mt) * 64 + lane] = xs * *reinterpret_cast<const f4*>(s_nx + 16 * mt + 4 * g);
+      }
+      if (c + 1 < p.nchunks) prefetch_state(c + 1);
+      __syncthreads();  // [B] X S0 handed over
+      // ---- Q S0, rows rescaled; the decay factors Gamma and Gamma^ of the outputs and
+      // the update; then the previous chunk's outputs
+      f4 QS[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        QS[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < DK / 32; ++kq) {
+          const bf8 aq = frag_pair(Qb + (16 * mt + n) * LDB + 32 * kq + 4 * g);
+          mma_bf16(QS[mt], aq, sh[kq]);
+          mma_bf16(QS[mt], aq, sl[kq]);
+        }
+        QS[mt] *= *reinterpret_cast<const f4*>(s_mq + 16 * mt + 4 * g);
+      }
+      float Gam[4][4], Gh[4][4];
+      prefix(bq, sc);
+      const float GamC = with_sign(__builtin_amdgcn_exp2f(gC), pC);
+      const float GhC = with_sign(__builtin_amdgcn_exp2f(gC - gA), pC ^ pA);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Gam[mt][i] = with_sign(__builtin_amdgcn_exp2f(gl[mt][i]), pgr[mt][i]);
+          Gh[mt][i] = with_sign(__builtin_amdgcn_exp2f(gl[mt][i] - gA), pgr[mt][i] ^ pA);
+        }
+      if (c + 1 < p.nchunks) load_beta(c + 1, bq);
+      if (c > 0) outputs(c - 1);
+      if (c + 1 < p.nchunks) stage_x(c + 1);
+      __syncthreads();  // [C] W~ handed over
+      f4 W[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) W[bi] = H2[(w4 * 4 + bi) * 64 + lane];
+      // ---- S' = Gamma_C S0 + Gamma^_C X^T W~ (W~ rows times the keys' rescale factors)
+      f4 Wn[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Wn[kb] = W[kb] * *reinterpret_cast<const f4*>(s_nx + 16 * kb + 4 * g);
+      bf8 wh[2], wl[2];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) split_c(Wn, kq, wh[kq], wl[kq]);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const bf8 a = xt_frag(Xb + (32 * kq + 4 * g + (n >> 2)) * LDB + 16 * rt + 4 * (n & 3), LDB);
+          mma_bf16(acc, a, wh[kq]);
+          mma_bf16(acc, a, wl[kq]);
+        }
+        s[rt] = s[rt] * GamC + acc * GhC;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        Wp[mt] = W[mt];
+        QSp[mt] = QS[mt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Gamp[mt][i] = Gam[mt][i];
+          Ghp[mt][i] = Gh[mt][i];
+        }
+      }
+      if (c + 1 < p.nchunks) stage_qp(c + 1);
+    }
+    if (p.nchunks > 0) outputs(p.nchunks - 1);
+    if (p.S_out != nullptr) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.S_out[((size_t)bh * DK + 16 * rt + 4 * g + i) * dv + col] = s[rt][i];
+    }
+  }
+}
+
 template <typename InT, int DK>
 hipError_t launch_pv_t(const ScanParams& p, hipStream_t st, int phases) {
   if (phases & 1) {
@@ -751,7 +1231,7 @@ hipError_t launch_pv_t(const ScanParams& p, hipStream_t st, int phases) {
     const dim3 grid((unsigned)((size_t)p.BH * (p.dv / 64)));
     if constexpr (sizeof(InT) == 2) {
       if ((p.flags & kFlagPhiElu1) == 0) {
-        hipLaunchKernelGGL((prop_pv_kernel<InT, DK, true>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((prop_pv2_kernel<DK>), dim3((unsigned)((size_t)p.BH * (p.dv / 32))), dim3(256), 0, st, p);
         return hipGetLastError();
       }
     }

@@ -34,6 +34,18 @@ def test_full_additive_bf16(seed):
 
 
 @pytest.mark.parametrize("seed", SEEDS)
+def test_full_delta_pv_bf16_h16(seed):
+    check_scan(wl.delta_pv_bf16_h16(seed=seed),
+               label=f"delta_pv_bf16_h16 B=4 H=16 T=4096 (per-value-channel step) seed={seed}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_full_additive_znorm_bf16(seed):
+    check_scan(wl.additive_znorm_bf16(seed=seed),
+               label=f"additive_znorm_bf16 B=2 H=16 T=16384 (normaliser) seed={seed}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
 def test_full_delta_long_per_channel(seed):
     check_scan(wl.delta_long_pc(seed=seed), label=f"delta_long_pc B=1 H=8 T=131072 seed={seed}")
 
