@@ -135,7 +135,9 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
     w.start = off;
     if (!diag) off += align256(4 * VH * dk * dv);
   }
-  if (m->flags & FWMEM_ZNORM) {
+  // the normaliser's chunk terms and chunk-entry values (the fused additive kernel carries
+  // the normaliser itself)
+  if ((m->flags & FWMEM_ZNORM) && !fwmem::scan_add_path(bf16, m->rule, m->flags)) {
     w.zr = off;
     off += align256(4 * BH * nchunks * fwmem::zrec_floats(s->dk));
     w.zc = off;
@@ -322,10 +324,12 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   // Normalised linear attention: prep writes the chunk terms of z, and after the
   // propagate kernels z is chained over the chunks of each head and divides the outputs.
   // Records of virtual heads (segments) are those of the real heads' chunks in order, so
-  // the chain always runs over the real heads.
+  // the chain always runs over the real heads. The fused additive kernel (elu + 1 on bf16)
+  // carries z as one more column itself and needs none of this.
   fwmem::ZParams zp;
   std::memset(&zp, 0, sizeof(zp));
-  if (mode->flags & FWMEM_ZNORM) {
+  const bool zkern = (mode->flags & FWMEM_ZNORM) && !fwmem::scan_add_path(p.bf16, mode->rule, mode->flags);
+  if (zkern) {
     char* ws = static_cast<char*>(workspace);
     p.zrec = reinterpret_cast<float*>(ws + wl.zr);
     zp.zrec = p.zrec;
@@ -345,7 +349,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
     zp.eps = p.eps;
   }
   auto znorm = [&](hipError_t e) {
-    if (e == hipSuccess && (mode->flags & FWMEM_ZNORM) && (phases & 2)) e = fwmem::launch_znorm(zp, hs);
+    if (e == hipSuccess && zkern && (phases & 2)) e = fwmem::launch_znorm(zp, hs);
     return e;
   };
   if (wl.P == 1) {
@@ -393,6 +397,7 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   sp.bf16 = p.bf16;
   sp.flags = p.flags;
   sp.diag = fwmem::seg_diagonal(mode->rule, mode->flags) ? 1 : 0;
+  sp.zfused = (mode->flags & FWMEM_ZNORM) && fwmem::scan_add_path(p.bf16, mode->rule, mode->flags) ? 1 : 0;
   sp.q = q;
   sp.v = v;
   sp.beta = beta;

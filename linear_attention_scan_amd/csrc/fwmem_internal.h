@@ -199,6 +199,9 @@ struct SegParams {
   const float* beta;      // [BH][T] write scales (or pre-activations), or null (1)
   const float* lam;       // [BH][T] retention (or pre-activations), or null (1)
   float* gam;             // [BH*P] each segment's decay Gamma_p (diagonal transitions)
+  // The normaliser with the fused additive pass: seg_state leaves each segment's change of
+  // z in B1_x, the combine chains z into B0_x, and the pass carries it from there.
+  int zfused;
   int BH, P, L, dk, dv, bf16;
   uint32_t flags;
 };

@@ -21,6 +21,13 @@
 //
 // Per chunk and workgroup: the next chunk's rows are loaded into registers while this
 // one computes; two barriers (after staging, after the P fragments).
+//
+// The normaliser ("attention is also an FFN", section 4.2): o_t = S_t^T phi(q_t) /
+// (z_t . phi(q_t) + eps) with z_t = gamma_t z_{t-1} + beta_t phi(k_t), z carried in the
+// state's key slot. In the chunk's terms, z_t . phi(q_t) = g_t (phi(q_t) . z) + the row
+// sum of P o D, and z' = g_C z + sum_s w_s phi(k_s). The waves that form the P fragments
+// add up their rows' sums, every wave takes a share of the dot products phi(q_t) . z and of
+// the sums w_s phi(k_s) (LDS atomics), and the outputs are divided before they are stored.
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
 #include "fwmem_split.h"
@@ -40,7 +47,13 @@ struct AddLds {
   static constexpr size_t kV = kK + (size_t)NPL * CH * LDQ * 2;       // uint16 [CH][LDV]
   static constexpr size_t kP = kV + (size_t)CH * LDV * 2;             // [kTriFrags][hi, lo][64 lanes] x 16 B
   static constexpr size_t kS = kP + (size_t)kTriFrags * 2 * 64 * 16;  // float l, beta, g, w [CH]; int parity [CH]
-  static constexpr size_t kBytes = kS + 5 * CH * 4;
+  // the normaliser: z at the chunk start (two buffers), the chunk's sum w_s phi(k_s),
+  // phi(q_t) . z, and the row sums of P o D by fragment
+  static constexpr size_t kZ = kS + 5 * CH * 4;                       // float [2][DK]
+  static constexpr size_t kZn = kZ + 2 * DK * 4;                      // float [DK]
+  static constexpr size_t kQz = kZn + DK * 4;                         // float [CH]
+  static constexpr size_t kRs = kQz + CH * 4;                         // float [kTriFrags][16]
+  static constexpr size_t kBytes = kRs + kTriFrags * 16 * 4;
 };
 
 __device__ __forceinline__ float bf8_at(const bf8& v, int j) {
@@ -62,7 +75,7 @@ __device__ __forceinline__ void lane_prefix(float& la, int& ng) {
   }
 }
 
-template <int DK, int DV, bool ELU>
+template <int DK, int DV, bool ELU, bool ZN>
 __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
   using L = AddLds<DK, DV, ELU>;
   constexpr int NT = 4 * DV, NW = DV / 16, NRT = DK / 16, NKB = DK / 32;
@@ -78,6 +91,10 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
   float* s_g = s_b + CH;                                // g_t (signed)
   float* s_w = s_g + CH;                                // beta_t g_C / g_t (signed)
   int* s_par = reinterpret_cast<int*>(s_w + CH);        // sign parity of the prefix
+  float* s_z = reinterpret_cast<float*>(smem + L::kZ);
+  float* s_zn = reinterpret_cast<float*>(smem + L::kZn);
+  float* s_qz = reinterpret_cast<float*>(smem + L::kQz);
+  float* s_rs = reinterpret_cast<float*>(smem + L::kRs);
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -141,6 +158,14 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       }
     }
   };
+
+  // the normaliser: thread tid < DK keeps z[tid]
+  float zreg = 0.f;
+  if (ZN && tid < DK) {
+    zreg = p.xprev_in != nullptr ? p.xprev_in[(size_t)bh * DK + tid] : 0.f;
+    s_z[tid] = zreg;
+    s_zn[tid] = 0.f;
+  }
 
   prefetch(0);
   for (int c = 0; c < p.nchunks; ++c) {
@@ -227,6 +252,50 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       split8(x, hi, lo);
       Pf[(2 * f) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
       Pf[(2 * f + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+      if constexpr (ZN) {  // this fragment's part of the row sums of P o D, rows 16 mt + n
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rs += x[j];
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        if (g == 0) s_rs[16 * f + n] = rs;
+      }
+    }
+
+    if constexpr (ZN) {
+      // phi(q_t) . z: TPT threads per token, each over DK / TPT dimensions of the split rows
+      constexpr int TPT = NT / CH, DPT = DK / TPT;
+      const float* zc = s_z + (c & 1) * DK;
+      {
+        const int t = tid / TPT, d0 = (tid % TPT) * DPT;
+        float a = 0.f;
+#pragma unroll
+        for (int d = 0; d < DPT; d += 8) {
+          const u32x4 h = *reinterpret_cast<const u32x4*>(Qs + t * LDQ + d0 + d);
+          const u32x4 l = *reinterpret_cast<const u32x4*>(Qs + CH * LDQ + t * LDQ + d0 + d);
+          const f4 z0 = *reinterpret_cast<const f4*>(zc + d0 + d), z1 = *reinterpret_cast<const f4*>(zc + d0 + d + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t wh = h[j >> 1], wl = l[j >> 1];
+            const float q = bf16_bits_to_f32((j & 1) ? wh >> 16 : wh & 0xffffu) +
+                            bf16_bits_to_f32((j & 1) ? wl >> 16 : wl & 0xffffu);
+            a += q * (j < 4 ? z0[j] : z1[j - 4]);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < TPT; o <<= 1) a += __shfl_xor(a, o);
+        if (tid % TPT == 0) s_qz[t] = a;
+      }
+      // sum_s w_s phi(k_s): thread (d, part) over the part's CH * DK / NT tokens
+      {
+        constexpr int NPART = NT / DK, TPP = CH / NPART;
+        const int d = tid % DK, t0p = (tid / DK) * TPP;
+        float a = 0.f;
+#pragma unroll 4
+        for (int t = t0p; t < t0p + TPP; ++t)
+          a += s_w[t] * (bf16_bits_to_f32(Ks[t * LDQ + d]) + bf16_bits_to_f32(Ks[CH * LDQ + t * LDQ + d]));
+        atomicAdd(&s_zn[d], a);
+      }
     }
 
     // ---- O = diag(g) (Q S) (C layout: rows 16 mt + 4 g + i, column n)
@@ -296,6 +365,25 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       mma_bf16(O[mt], __builtin_bit_cast(bf8, Pf[(2 * f) * 64 + lane]), vf[kq]);
       mma_bf16(O[mt], __builtin_bit_cast(bf8, Pf[(2 * f + 1) * 64 + lane]), vf[kq]);
     }
+    if constexpr (ZN) {
+      // z_t . phi(q_t) = g_t (phi(q_t) . z) + the row sums of P o D (fragments f of row tile mt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * mt + 4 * g + i, r = 4 * g + i;
+          float den = s_g[t] * s_qz[t];
+#pragma unroll
+          for (int f = 0; f < kTriFrags; ++f)
+            if (tri_m(f) == mt) den += s_rs[16 * f + r];
+          O[mt][i] *= __builtin_amdgcn_rcpf(den + p.eps);
+        }
+      if (tid < DK) {  // z at the next chunk's start
+        zreg = s_g[CH - 1] * zreg + s_zn[tid];
+        s_z[((c + 1) & 1) * DK + tid] = zreg;
+        s_zn[tid] = 0.f;
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -311,7 +399,10 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.S_out[((size_t)bh * DK + 16 * rt + 4 * g + i) * DV + col] = s[rt][i];
-    if ((p.flags & kFlagZnorm) == 0) {  // with the normaliser the slot holds z
+    if (ZN) {  // with the normaliser the key slot holds z
+      if (tid < DK) p.xprev_out[(size_t)bh * DK + tid] = zreg;
+      if (tid == 0) p.has_out[bh] = 1;
+    } else {
       const uint16_t* kl = kbase + (size_t)(p.T - 1) * DK;
       for (int i = tid; i < DK; i += NT) {
         float x = In<uint16_t>::load1(kl + i);
@@ -326,16 +417,15 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
 template <int DK, int DV>
 hipError_t launch_add_t(const ScanParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.BH), block(4 * DV);
-  if (p.flags & kFlagPhiElu1) hipLaunchKernelGGL((add_kernel<DK, DV, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((add_kernel<DK, DV, false>), grid, block, 0, st, p);
+  if (p.flags & kFlagZnorm) hipLaunchKernelGGL((add_kernel<DK, DV, true, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((add_kernel<DK, DV, true, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool scan_add_path(int bf16, int rule, uint32_t flags) {
-  return bf16 != 0 && rule == kRuleAdditive && (flags & kFlagPhiElu1) != 0 &&
-         (flags & (kFlagPerChannel | kFlagZnorm)) == 0;
+  return bf16 != 0 && rule == kRuleAdditive && (flags & kFlagPhiElu1) != 0 && (flags & kFlagPerChannel) == 0;
 }
 
 hipError_t launch_scan_add(const ScanParams& p, hipStream_t st) {

@@ -84,6 +84,16 @@ __global__ __launch_bounds__(NTH) void seg_combine_diag_kernel(SegParams s) {
     v = gp * v + *reinterpret_cast<const f4*>(s.B1_S + vh * n + e);
   }
   if (s.S_out != nullptr) *reinterpret_cast<f4*>(s.S_out + h * n + e) = v;
+  // the normaliser's start values, chained the same way (its key slot)
+  if (s.zfused && blockIdx.x % nb == 0 && (int)threadIdx.x < s.dk) {
+    const size_t i = threadIdx.x;
+    float vz = s.B1_x[h * s.P * s.dk + i];
+    for (int p = 1; p < s.P; ++p) {
+      const size_t vh = h * s.P + p;
+      s.B0_x[vh * s.dk + i] = vz;
+      vz = s.gam[vh] * vz + s.B1_x[vh * s.dk + i];
+    }
+  }
 }
 
 // General transitions: S_start(p+1) = A_p S_start(p) + B_p, a [d_k x d_k] x [d_k x 16]
@@ -298,9 +308,15 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
   __shared__ __align__(16) uint16_t ws[2][64 * LDW];
   __shared__ float s_w[64];
   __shared__ float s_tot;
+  __shared__ float s_zb[NW][DK];  // with the normaliser: each wave's part of sum_t w_t x_t
   const size_t vh = blockIdx.x;
   const int p = (int)(vh % s.P), L = s.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // with the normaliser, thread tid adds up w_t x_t over its rows for the VW columns of
+  // granule tid % GX (the same granule in every row it stages)
+  float zp[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) zp[j] = 0.f;
   const int g = lane >> 4, n = lane & 15;
   const int mt0 = (wave / WPM) * NMT, nt0 = (wave % WPM) * NNW;
   const bool elu = (s.flags & kFlagPhiElu1) != 0;
@@ -373,6 +389,11 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
 #pragma unroll
         for (int j = 0; j < VW; ++j) x[j] *= f;
       }
+      if (s.zfused) {  // the normaliser's share: w_t x_t
+        const float wt = s_w[t];
+#pragma unroll
+        for (int j = 0; j < VW; ++j) zp[j] += wt * x[j];
+      }
 #pragma unroll
       for (int j = 0; j < VW; j += 8 < VW ? 8 : VW) {
         float y[8];
@@ -444,8 +465,26 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
     }
     carry *= tot;
   }
-  // the segment's decay for the combine
+  // the segment's decay for the combine; with the normaliser, the segment's own change of z
+  // (plus Gamma_0 z_in for segment 0) in its key slot
   if (tid == 0) s.gam[vh] = carry;
+  if (s.zfused) {  // (uniform: every wave reaches the barrier)
+    static_assert(NT % GX == 0 && GX <= 64, "one granule column per thread");
+#pragma unroll
+    for (int o = GX; o < 64; o <<= 1)
+#pragma unroll
+      for (int j = 0; j < VW; ++j) zp[j] += __shfl_xor(zp[j], o);
+    if (lane < GX)
+#pragma unroll
+      for (int j = 0; j < VW; ++j) s_zb[wave][lane * VW + j] = zp[j];
+    __syncthreads();
+    if (tid < DK) {
+      float zb = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) zb += s_zb[w][tid];
+      s.B1_x[vh * DK + tid] = zb + (p == 0 ? carry * s.B0_x[vh * DK + tid] : 0.f);
+    }
+  }
   // segment 0 also carries the caller's state through the segment's decay
   float* Bo = s.B1_S + vh * DK * DV;
   const float* S0 = p == 0 ? s.B0_S + vh * DK * DV : nullptr;
@@ -465,7 +504,9 @@ __global__ __launch_bounds__(kStateThreads) void seg_state_kernel(SegParams s) {
 __global__ __launch_bounds__(NTH) void seg_extras_kernel(SegParams s) {
   const int h = blockIdx.x;
   const size_t last = (size_t)h * s.P + s.P - 1;
-  if ((s.flags & kFlagZnorm) == 0)  // with the normaliser the slot holds z
+  // the last segment's key, or with the normaliser of the fused pass its final z (without
+  // the fused pass the normaliser's own kernels write z)
+  if ((s.flags & kFlagZnorm) == 0 || s.zfused)
     for (int i = threadIdx.x; i < s.dk; i += NTH) s.xprev_out[(size_t)h * s.dk + i] = s.B1_x[last * s.dk + i];
   if (threadIdx.x == 0) s.has_out[h] = 1;
 }

@@ -101,3 +101,65 @@ def test_fused_additive_repeatable():
     b, sb = gpu_scan(w)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(state_np(sa)[0], state_np(sb)[0])
+
+
+# ---- the normaliser carried by the fused kernel (z_t . phi(q_t) + eps divides each read)
+
+def additive_elu_z(B, H, T, dk=128, dv=128, seed=0, **kw):
+    w = additive_elu(B, H, T, dk, dv, kw.pop("beta_kind", "one"), seed=seed,
+                     name=f"fused additive znorm {dk}x{dv} T={T}")
+    w.znorm = True
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_fused_znorm_dims(dk, dv):
+    check_scan(additive_elu_z(2, 2, 333, dk, dv, seed=40 + dk + dv, beta_kind="sigmoid"), tol=TOL_SPLIT)
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 200])
+def test_fused_znorm_short(T):
+    check_scan(additive_elu_z(1, 2, T, seed=50 + T), tol=TOL_SPLIT)
+
+
+def test_fused_znorm_carried_state_in_place():
+    """Nonzero S0 and z0 (the key slot), the state updated in place."""
+    from tests.gpu_helpers import make_state
+    w = additive_elu_z(1, 2, 450, seed=60)
+    rng = np.random.default_rng(61)
+    w.S0 = (rng.standard_normal((1, 2, 128, 128)) * 0.05).astype(np.float32)
+    w.xprev0 = np.abs(rng.standard_normal((1, 2, 128)) * 0.5).astype(np.float32)
+    st = make_state(w.B, w.H, w.dk, w.dv, S=w.S0, xprev=w.xprev0)
+    say("[scan] fused additive znorm, carried S0 and z0, in place")
+    o, st2 = gpu_scan(w, S_in=st, S_out=st)
+    o_ref, S_ref, z_ref, _ = oracle_scan(w)
+    S, z, h = state_np(st2)
+    eo, eS, ez = orc.relerr(o, o_ref), orc.relerr(S, S_ref), orc.relerr(z, z_ref)
+    say(f"    err(o)={eo:.3e} err(S)={eS:.3e} err(z)={ez:.3e}")
+    assert eo <= TOL_SPLIT and eS <= TOL_SPLIT and ez <= TOL_SPLIT
+    assert np.all(h == 1)
+
+
+def test_fused_znorm_two_calls():
+    w = additive_elu_z(1, 2, 700, seed=62)
+    say("[scan] fused additive znorm, two calls cut at 300")
+    o1, st = gpu_scan(w, t_slice=slice(0, 300))
+    o2, st2 = gpu_scan(w, t_slice=slice(300, None), S_in=st)
+    o_ref, S_ref, z_ref, _ = oracle_scan(w)
+    S, z, _ = state_np(st2)
+    eo = orc.relerr(np.concatenate([o1, o2], axis=2), o_ref)
+    eS, ez = orc.relerr(S, S_ref), orc.relerr(z, z_ref)
+    say(f"    err(o)={eo:.3e} err(S)={eS:.3e} err(z)={ez:.3e}")
+    assert eo <= TOL_SPLIT and eS <= TOL_SPLIT and ez <= TOL_SPLIT
+
+
+def test_fused_znorm_segmented():
+    """Segments with the normaliser: each segment's change of z from the state pass, z
+    chained by the combine, then one fused pass per segment; nonzero S0 and z0."""
+    w = additive_elu_z(1, 2, 8192, seed=63, beta_kind="sigmoid")
+    rng = np.random.default_rng(64)
+    w.S0 = (rng.standard_normal((1, 2, 128, 128)) * 0.05).astype(np.float32)
+    w.xprev0 = np.abs(rng.standard_normal((1, 2, 128)) * 0.5).astype(np.float32)
+    check_scan(w, tol=TOL_SPLIT)
