@@ -53,7 +53,10 @@ struct AddLds {
   static constexpr size_t kZn = kZ + 2 * DK * 4;                      // float [DK]
   static constexpr size_t kQz = kZn + DK * 4;                         // float [CH]
   static constexpr size_t kRs = kQz + CH * 4;                         // float [kTriFrags][16]
-  static constexpr size_t kBytes = kRs + kTriFrags * 16 * 4;
+  // each wave's outputs, turned from the accumulator layout into rows for 16-byte stores
+  static constexpr int LDO = 16 + 4;
+  static constexpr size_t kO = kRs + kTriFrags * 16 * 4;              // float [DV / 16][CH][LDO]
+  static constexpr size_t kBytes = kO + (size_t)(DV / 16) * CH * LDO * 4;
 };
 
 __device__ __forceinline__ float bf8_at(const bf8& v, int j) {
@@ -100,6 +103,7 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
   const int col = 16 * wave + n;  // the lane's value column
+  float* s_o = reinterpret_cast<float*>(smem + L::kO) + wave * CH * L::LDO;  // this wave's output rows
   const size_t rowbase = (size_t)bh * p.T;
   const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + rowbase * DK;
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + rowbase * DK;
@@ -112,7 +116,6 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
   const uint32_t oes = obf ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t ro =
       rsrc(static_cast<const char*>(p.out) + rowbase * DV * oes, (uint32_t)((size_t)p.T * DV * oes));
-  const uint32_t olane = (uint32_t)(4 * g * DV + col);  // element offset of the lane's first row
 
   f4 s[NRT];
 #pragma unroll
@@ -152,9 +155,9 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       const int tau = cn * CH + tid;
       gbeta = 0.f;  // past the end: no write and no decay
       ggam = 1.f;
-      if (tau < p.T) {
-        gbeta = p.beta != nullptr ? act_beta(p.beta[rowbase + tau], p.flags) : 1.f;
-        ggam = p.lam != nullptr ? act_lam(p.lam[rowbase + tau], p.flags, false) : 1.f;
+      if (tau < p.T) {  // raw here; activated when staged, so the loads stay in flight
+        gbeta = p.beta != nullptr ? p.beta[rowbase + tau] : 1.f;
+        ggam = p.lam != nullptr ? p.lam[rowbase + tau] : 1.f;
       }
     }
   };
@@ -201,23 +204,29 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       *reinterpret_cast<u32x4*>(Vs + (gi / GV) * LDV + (gi % GV) * 8) = pv[r];
     }
     if (wave == 0) {
-      float la = __builtin_amdgcn_logf(fmaxf(fabsf(ggam), 1e-30f));
-      int ng = ggam < 0.f ? 1 : 0;
+      const bool live = c * CH + lane < p.T;
+      const float gb = live && p.beta != nullptr ? act_beta(gbeta, p.flags) : gbeta;
+      const float gm = live && p.lam != nullptr ? act_lam(ggam, p.flags, false) : ggam;
+      float la = __builtin_amdgcn_logf(fmaxf(fabsf(gm), 1e-30f));
+      int ng = gm < 0.f ? 1 : 0;
       lane_prefix(la, ng);
       const float lc = __shfl(la, CH - 1);
       const int pc = __shfl(ng, CH - 1) & 1;
       s_l[lane] = la;
       s_par[lane] = ng & 1;
-      s_b[lane] = gbeta;
+      s_b[lane] = gb;
       s_g[lane] = with_sign(__builtin_amdgcn_exp2f(la), ng & 1);
-      s_w[lane] = gbeta * with_sign(__builtin_amdgcn_exp2f(lc - la), pc ^ (ng & 1));
+      s_w[lane] = gb * with_sign(__builtin_amdgcn_exp2f(lc - la), pc ^ (ng & 1));
     }
     __syncthreads();
     if (c + 1 < p.nchunks) prefetch(c + 1);
 
     // ---- P^T tiles (rows s, columns t) of the lower triangle, masked: fragment f of the
     // P V operand (row tile mt, token block kq) is the tile pair (2 kq, mt), (2 kq + 1, mt)
-    for (int f = wave; f < kTriFrags; f += NW) {
+    // fragments f = 1, 2, 4, 5 hold two tiles, 0 and 3 one; waves w and w + 4 share a SIMD
+    for (int fi = wave; fi < kTriFrags; fi += NW) {
+      constexpr int kOrder[kTriFrags] = {1, 2, 4, 5, 3, 0};
+      const int f = kOrder[fi];
       const int mt = tri_m(f), kq = tri_kb(f);
       const int t = 16 * mt + n;
       const float lt = s_l[t];
@@ -384,14 +393,33 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
         s_zn[tid] = 0.f;
       }
     }
+    // ---- the outputs through the wave's own LDS rows: lane r then stores row t0 + r of the
+    // wave's 16 columns in 16-byte pieces (the wave's LDS operations complete in order)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t so = (uint32_t)((t0 + 16 * mt + i) * DV);
-        if (obf) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(O[mt][i]), ro, 2u * olane, 2u * so, 0);
-        else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[mt][i]), ro, 4u * olane, 4u * so, 0);
+      for (int i = 0; i < 4; ++i) s_o[(16 * mt + 4 * g + i) * L::LDO + n] = O[mt][i];
+    {
+      f4 r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const f4*>(s_o + lane * L::LDO + 4 * j);
+      const uint32_t so = (uint32_t)((t0 + lane) * DV + 16 * wave);  // element offset of the row piece
+      if (obf) {
+        u32x4 b[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          b[j >> 1][2 * (j & 1)] = (uint32_t)f32_to_bf16_bits(r[j][0]) | ((uint32_t)f32_to_bf16_bits(r[j][1]) << 16);
+          b[j >> 1][2 * (j & 1) + 1] = (uint32_t)f32_to_bf16_bits(r[j][2]) | ((uint32_t)f32_to_bf16_bits(r[j][3]) << 16);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b[h]), ro, 2u * so + 16u * h, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r[j]), ro, 4u * so + 16u * j, 0, 0);
       }
+    }
   }
 
   if (p.S_out != nullptr) {
