@@ -135,22 +135,31 @@ def measured_traffic(workload, kernel):
 def kernel_names(w):
     """Names of the prep and propagate kernels that the library launches for w: bf16
     inputs with the identity feature map and a scalar decay take the split-operand
-    kernels, everything else the general ones; the per-value-channel rule has its own."""
+    kernels; the additive rule with elu+1 on bf16 (scalar retention) one fused kernel in
+    the propagate phase (its prep phase only sets up segments); everything else the
+    general ones; the per-value-channel rule its own (state and solver waves for bf16 with
+    the identity map)."""
     if w.rule == 3:
-        return {"prep": "prep_pv_kernel", "propagate": "prop_pv_kernel"}
+        pv2 = w.dtype == "bf16" and w.phi != "elu1"
+        return {"prep": "prep_pv_kernel", "propagate": "prop_pv2_kernel" if pv2 else "prop_pv_kernel"}
+    if w.rule == 1 and w.dtype == "bf16" and w.phi == "elu1" and not w.per_channel:
+        return {"prep": "seg_init_kernel", "propagate": "add_kernel"}
     split = w.dtype == "bf16" and not w.per_channel and w.phi != "elu1"
     return ({"prep": "prep_split_kernel", "propagate": "prop_split_kernel"} if split
             else {"prep": "prep_kernel", "propagate": "prop_kernel"})
 
 
 def compute_dtype(w):
-    """Arithmetic type of the scan: the split kernels multiply bf16 operands (hi/lo pairs
-    for computed matrices), the general kernels fp16 operands for bf16 inputs and fp32
-    operands for fp32 inputs (and the per-value-channel rule for both); all accumulate in
-    fp32."""
-    if w.dtype != "bf16" or w.rule == 3:
+    """Arithmetic type of the scan: the split kernels, the fused additive kernel and the
+    per-value-channel state and solver waves multiply bf16 operands (hi/lo pairs for
+    computed matrices), the general kernels fp16 operands for bf16 inputs, fp32 inputs
+    (and the per-value-channel rule on them) fp32 operands; all accumulate in fp32."""
+    if w.dtype != "bf16":
         return "f32"
-    return "bf16" if kernel_names(w)["prep"] == "prep_split_kernel" else "f16"
+    prop = kernel_names(w)["propagate"]
+    if w.rule == 3:
+        return "bf16" if prop == "prop_pv2_kernel" else "f32"
+    return "bf16" if prop in ("prop_split_kernel", "add_kernel") else "f16"
 
 
 def scan_bytes_per_token_head(w, out_bytes=4):
