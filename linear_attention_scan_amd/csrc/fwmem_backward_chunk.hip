@@ -29,6 +29,7 @@
 #include "fwmem_backward.h"
 #include "fwmem_device.h"
 #include "fwmem_internal.h"
+#include "fwmem_split.h"
 
 namespace fwmem {
 namespace {
@@ -250,6 +251,8 @@ struct Rows {
       for (int e = 0; e < VW; e += 4) *reinterpret_cast<f4*>(dst + t * LDX + i0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
     }
   }
+  // The same rows as bf16 hi/lo planes [CB][DK + 8] (hi at dst, lo a plane further on).
+  __device__ __forceinline__ void commit_split(uint16_t* dst, bool elu, float len, int patch, const float* pv) const;
 };
 
 __device__ __forceinline__ bool head_has_key(const BwdParams& p, int bh) {
@@ -789,8 +792,9 @@ enum {
   kNP
 };
 
+// Gradient pass on fp32 MFMA (float32 inputs, whose gradients are held to float32 accuracy).
 template <typename InT, int DK, int DV, int RULE>
-__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float* recs, const float* Sch,
+__global__ __launch_bounds__(512) void bwd_grad_f32_kernel(BwdParams p, const float* recs, const float* Sch,
                                                         const float* dSch, const float* Rh, const float* dRw) {
   using R = Rule<RULE>;
   constexpr bool SOLVE = R::solve;
@@ -1210,6 +1214,954 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
   }
 }
 
+// ---- bf16 split operands of the gradient pass. A matrix formed in fp32 is held in LDS as
+// two bf16 planes of one row-major layout, hi = bf16(x) and lo = bf16(x - hi): 16
+// significant bits over fp32's exponent range. A product with both operands split is
+// Ah Bh + Ah Bl + Al Bh on v_mfma_f32_16x16x32_bf16 with fp32 accumulation (Al Bl lies
+// below the fp32 rounding of the result); an exact bf16 operand (raw bf16 keys and queries
+// with the identity map and no QK rescaling) has a zero lo plane and takes two products.
+// Plane rows are padded by 8 elements, so the row stride is an odd multiple of 16 bytes
+// modulo 256 and the 16 rows of a fragment read fall in distinct bank groups.
+//
+// Fragments follow the K-slot order of frag_pair / xt_frag: slots 0..3 carry K = 4g..4g+3
+// and slots 4..7 K = 16+4g..16+4g+3 of a 32-wide K block (g = lane / 16), for A and B alike.
+__device__ __forceinline__ uint16_t bf_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ __forceinline__ void put_split(uint16_t* hi, int plane, int idx, float x) {
+  const uint16_t h = bf_bits(x);
+  hi[idx] = h;
+  hi[plane + idx] = bf_bits(x - bf16_bits_to_f32(h));
+}
+
+// four consecutive elements (idx a multiple of 4): one 8-byte store per plane
+__device__ __forceinline__ void put_split4(uint16_t* hi, int plane, int idx, const f4& x) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = bf_bits(x[i]);
+    l[i] = bf_bits(x[i] - bf16_bits_to_f32(h[i]));
+  }
+  *reinterpret_cast<uint2*>(hi + idx) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  *reinterpret_cast<uint2*>(hi + plane + idx) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// the fp32 value hi + lo of element idx
+__device__ __forceinline__ float get_split(const uint16_t* hi, int plane, int idx) {
+  return bf16_bits_to_f32(hi[idx]) + bf16_bits_to_f32(hi[plane + idx]);
+}
+
+struct SFrag {
+  bf8 h, l;
+};
+
+// Operand row r (A row, or B column) of the K block at k0, from planes stored with K
+// contiguous (element [r][k] at r * ld + k).
+__device__ __forceinline__ SFrag fk(const uint16_t* hi, int plane, int ld, int r, int k0, int g) {
+  return SFrag{frag_pair(hi + r * ld + k0 + 4 * g), frag_pair(hi + plane + r * ld + k0 + 4 * g)};
+}
+// Operand rows r0..r0+15 of the K block at k0, from planes stored K-major (element [k][r]
+// at k * ld + r), by the LDS transpose read.
+__device__ __forceinline__ SFrag ft(const uint16_t* hi, int plane, int ld, int r0, int k0, int g, int n) {
+  const int o = (k0 + 4 * g + (n >> 2)) * ld + r0 + 4 * (n & 3);
+  return SFrag{xt_frag(hi + o, ld), xt_frag(hi + plane + o, ld)};
+}
+
+// acc += A B with both operands split
+__device__ __forceinline__ void mma3(f4& acc, const SFrag& a, const SFrag& b) {
+  mma_bf16(acc, a.l, b.h);
+  mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+// acc += A B where B's lo plane is zero when bex (an exact bf16 operand)
+__device__ __forceinline__ void mma3x(f4& acc, const SFrag& a, const SFrag& b, bool bex) {
+  mma_bf16(acc, a.l, b.h);
+  if (!bex) mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+
+template <typename InT, int DK, int NTH>
+__device__ __forceinline__ void Rows<InT, DK, NTH>::commit_split(uint16_t* dst, bool elu, float len, int patch,
+                                                                 const float* pv) const {
+  constexpr int LX = DK + 8, PX = CB * LX;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW;
+    float x[VW];
+    In<InT>::decode(w[j], x);
+    if (t == patch) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] = pv != nullptr ? pv[i0 + e] : 0.f;
+    } else if (elu && ((valid >> j) & 1u)) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+    }
+    if (len > 0.f) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
+      ss = group_sum<GPR>(ss);
+      const float f = rescale_factor(ss, len);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] *= f;
+    }
+#pragma unroll
+    for (int e = 0; e < VW; e += 4) put_split4(dst, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
+  }
+}
+
+// acc += A B with B split and A exact when aex (its lo plane zero)
+__device__ __forceinline__ void mma3a(f4& acc, const SFrag& a, const SFrag& b, bool aex) {
+  if (!aex) mma_bf16(acc, a.l, b.h);
+  mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+
+// Written keys x_t (Q == false) or read queries phi(q_t) (Q == true) of chunk c as split
+// planes [CB][DK + 8]: the shift to the previous token's key (and the carried key before a
+// call's first token), phi and QK normalisation applied; rows of tokens past T are zero.
+// A row's 16-byte groups sit in GPR consecutive lanes, so its norm is a lane-group sum.
+template <typename InT, int DK, bool SHIFT, bool Q, int NTH>
+__device__ void stage_split(const BwdParams& p, int bh, int c, uint16_t* hi, bool has_in) {
+  constexpr int LX = DK + 8, PX = CB * LX, VW = 16 / (int)sizeof(InT), GPR = DK / VW;
+  static_assert(CB * GPR % NTH == 0 && 64 % GPR == 0, "row groups");
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const size_t rb = (size_t)bh * p.T;
+  const InT* src = static_cast<const InT*>(Q ? p.q : p.k) + rb * DK;
+#pragma unroll
+  for (int j = 0; j < CB * GPR / NTH; ++j) {
+    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW, tau = c * CB + t;
+    float x[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) x[e] = 0.f;
+    if (tau < p.T) {
+      if (!Q && SHIFT && tau == 0) {
+        if (has_in && p.xprev_in != nullptr) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) x[e] = p.xprev_in[(size_t)bh * DK + i0 + e];  // phi applied
+        }
+      } else {
+        In<InT>::load(src + (size_t)(!Q && SHIFT ? tau - 1 : tau) * DK + i0, x);
+        if (elu) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+        }
+      }
+    }
+    if (len > 0.f) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
+      ss = group_sum<GPR>(ss);
+      const float f = rescale_factor(ss, len);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] *= f;
+    }
+#pragma unroll
+    for (int e = 0; e < VW; e += 4) put_split4(hi, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
+  }
+}
+
+// Gradient pass on bf16 MFMA with split operands (bf16 inputs).
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float* recs, const float* Sch,
+                                                        const float* dSch, const float* Rh, const float* dRw) {
+  using R = Rule<RULE>;
+  constexpr bool SOLVE = R::solve;
+  constexpr int NDT = DK / 16, DPW = NDT / 2;  // d_k tiles, and those of one wave
+  constexpr int NBLK = DV / NCOL;
+  // bf16 plane row strides and plane sizes (elements)
+  constexpr int LX = DK + 8, LC = CB + 8, LB = NCOL + 8;
+  constexpr int PX = CB * LX, PC = CB * LC, PS = DK * LB, PB = CB * LB;
+  // Block region. Phase 1 (one 32-column value block): S and dS' [DK][NCOL], dO and U
+  // [CB][NCOL], for the delta rule also dR and R = eta R-hat [CB][NCOL]. Phase 2: Q
+  // [CB][DK], A1 = dMm o D [CB][CB], for the delta rule W = dLm o eta D' [CB][CB].
+  constexpr int kBlk1 = 4 * PS + 2 * (SOLVE ? 4 : 2) * PB;
+  constexpr int kBlk2 = 2 * PX + 2 * (SOLVE ? 2 : 1) * PC;
+  constexpr int kBlk = kBlk1 > kBlk2 ? kBlk1 : kBlk2;
+  static_assert(2 * PC * 2 >= CB * LDC * 4, "Lp fits the T planes");
+  __shared__ __align__(16) uint16_t Xp[2 * PX];
+  __shared__ __align__(16) uint16_t Tp[2 * PC];  // T (delta rule) or M (other rules); then Lp fp32
+  __shared__ __align__(16) float Ms[CB * LDC];   // M in fp32 (the decay gradient's sums)
+  __shared__ __align__(16) uint16_t blk[kBlk];
+  __shared__ float s_sc[kNSc][CB];
+  __shared__ float s_p[kNP][CB];
+  __shared__ float s_dn[CB];
+  __shared__ float s_red[8];
+  uint16_t* Sp = blk;
+  uint16_t* dSp = Sp + 2 * PS;
+  uint16_t* dOp = dSp + 2 * PS;
+  uint16_t* Up = dOp + 2 * PB;
+  uint16_t* dRp = Up + 2 * PB;  // delta
+  uint16_t* Rp = dRp + 2 * PB;  // delta
+  uint16_t* Qp = blk;           // phase 2
+  uint16_t* A1p = Qp + 2 * PX;
+  uint16_t* Wp = A1p + 2 * PC;  // delta
+  float* Lp = reinterpret_cast<float*>(Tp);
+
+  const int nch = (p.T + CB - 1) / CB;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_in = head_has_key(p, bh);
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  // raw bf16 keys and queries with the identity map are exact bf16 operands; the carried key
+  // (fp32, row 0 of chunk 0 for the shifted rules) need not be
+  const bool xex = sizeof(InT) == 2 && !elu && !(qk_length(p.flags, DK) > 0.f) && !(R::shift && c == 0 && has_in);
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const int t0 = c * CB;
+  const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+  const float* Sc = Sch + ((size_t)bh * nch + c) * SS;
+  const float* dSc = dSch + ((size_t)bh * nch + c) * SS;
+  const float* rhc = Rh + ((size_t)bh * nch + c) * CB * DV;
+  const float* drc = dRw + ((size_t)bh * nch + c) * CB * DV;
+  const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
+
+  for (int e = tid; e < CB * CB / 4; e += 512) {
+    const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+    const f4 mv = *reinterpret_cast<const f4*>(rec + BRec::kM + r * CB + c4);
+    *reinterpret_cast<f4*>(Ms + r * LDC + c4) = mv;
+    put_split4(Tp, PC, r * LC + c4, SOLVE ? *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4) : mv);
+  }
+  for (int e = tid; e < kNSc * CB; e += 512) (&s_sc[0][0])[e] = rec[BRec::kSc + e];
+  for (int e = tid; e < kNP * CB; e += 512) (&s_p[0][0])[e] = 0.f;
+  stage_split<InT, DK, R::shift, false, 512>(p, bh, c, Xp, has_in);
+  __syncthreads();
+
+  const int m = w & 3, ctw = w >> 2;  // token tile and column tile of this wave's block outputs
+  // accumulators over the value blocks
+  f4 aMm[4], aQ1[DPW], aXR[DPW], aXS[DPW];  // aMm: dMm (w < 4) or dLm (w >= 4) tiles (m, s <= m)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aMm[s] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) aQ1[d] = aXR[d] = aXS[d] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 pe = {0.f, 0.f, 0.f, 0.f};  // eta's gradient through V (other rules: this lane's C-tile rows)
+  float pe1 = 0.f;               // eta's gradient through R-hat (delta: this thread's row)
+  float sds = 0.f;               // <dS', S> partial
+
+  auto fac = [&](int k, int t) { return s_sc[k][t]; };
+
+  // The next value block in registers. S and dS' (NSJ float4 a thread each) and dO: thread
+  // tid holds float4 tid % 8 of row tid / 8. The delta rule adds dR and R-hat in the dO
+  // layout; the other rules take this lane's four values of V in C-tile layout.
+  constexpr int NSJ = DK * NCOL / 4 / 512;
+  static_assert(NSJ >= 1 && CB * NCOL / 4 == 512, "value block layout");
+  const int bt = tid / (NCOL / 4), bv4 = (tid % (NCOL / 4)) * 4, btau = t0 + bt;
+  f4 ps[NSJ], pds[NSJ], pdo, pdr, prh;
+  float pv4[4];
+  auto load_blk = [&](int jb) {
+    const int col0 = jb * NCOL;
+#pragma unroll
+    for (int j = 0; j < NSJ; ++j) {
+      const int e = tid + 512 * j, r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
+      ps[j] = *reinterpret_cast<const f4*>(Sc + (size_t)r * DV + col0 + v4);
+      pds[j] = *reinterpret_cast<const f4*>(dSc + (size_t)r * DV + col0 + v4);
+    }
+    pdo = btau < p.T ? *reinterpret_cast<const f4*>(p.dout + (rb + btau) * DV + col0 + bv4) : f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SOLVE) {
+      pdr = *reinterpret_cast<const f4*>(drc + (size_t)bt * DV + col0 + bv4);
+      prh = *reinterpret_cast<const f4*>(rhc + (size_t)bt * DV + col0 + bv4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i, tau = t0 + t, cc = col0 + 16 * ctw + n;
+        pv4[i] = tau < p.T ? In<InT>::load1(vb + (size_t)tau * DV + cc) : 0.f;
+      }
+    }
+  };
+  load_blk(0);
+
+  for (int jb = 0; jb < NBLK; ++jb) {
+    const int col0 = jb * NCOL;
+    // the block into LDS planes from registers
+#pragma unroll
+    for (int j = 0; j < NSJ; ++j) {
+      const int e = tid + 512 * j, r = e / (NCOL / 4), v4 = (e % (NCOL / 4)) * 4;
+      put_split4(Sp, PS, r * LB + v4, ps[j]);
+      put_split4(dSp, PS, r * LB + v4, pds[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sds += ps[j][i] * pds[j][i];
+    }
+    put_split4(dOp, PB, bt * LB + bv4, pdo);
+    if constexpr (SOLVE) {
+      // R = eta R-hat; dV = eta dR; eta's gradient through R-hat
+      const float e = fac(kScE, bt);
+      put_split4(dRp, PB, bt * LB + bv4, pdr);
+      put_split4(Rp, PB, bt * LB + bv4, f4{e * prh[0], e * prh[1], e * prh[2], e * prh[3]});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe1 += pdr[i] * prh[i];
+      if (btau < p.T)
+        *reinterpret_cast<f4*>(p.gv + (rb + btau) * DV + col0 + bv4) = f4{e * pdr[0], e * pdr[1], e * pdr[2], e * pdr[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        put_split(Up, PB, t * LB + 16 * ctw + n, fac(kScE, t) * pv4[i]);
+      }
+    }
+    float v4r[4];  // V, this lane's C-tile rows (other rules)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4r[i] = pv4[i];
+    lds_barrier();
+    if (jb + 1 < NBLK) load_blk(jb + 1);
+
+    if constexpr (SOLVE) {
+      // U = T R, tile (m, ctw): K blocks 0 .. m/2 (T is lower triangular)
+      f4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (m >> 1)) mma3(u, fk(Tp, PC, LC, 16 * m + n, 32 * kb, g), ft(Rp, PB, LB, 16 * ctw, 32 * kb, g, n));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) put_split(Up, PB, (16 * m + 4 * g + i) * LB + 16 * ctw + n, u[i]);
+    } else {
+      // dU = (Gamma_end / Gamma) X dS' + M^T dO; dV = f dU; f's gradient through V
+      f4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        const SFrag x = fk(Xp, PX, LX, 16 * m + n, 32 * kb, g);
+        const SFrag b = ft(dSp, PS, LB, 16 * ctw, 32 * kb, g, n);
+        mma_bf16(du, x.h, b.l);
+        if (!xex) mma_bf16(du, x.l, b.h);
+        mma_bf16(du, x.h, b.h);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] *= fac(kScGend, 16 * m + 4 * g + i);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb >= (m >> 1)) mma3(du, ft(Tp, PC, LC, 16 * m, 32 * kb, g, n), ft(dOp, PB, LB, 16 * ctw, 32 * kb, g, n));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i, tau = t0 + t;
+        pe[i] += du[i] * v4r[i];
+        if (tau < p.T) p.gv[(rb + tau) * DV + col0 + 16 * ctw + n] = fac(kScE, t) * du[i];
+      }
+    }
+    lds_barrier();
+
+    // accumulate over the block's 32 columns (one K block): dMm = dO U^T (w < 4), dLm =
+    // -dR U^T (w >= 4), dQ1 = dO S^T, dXR = dR S^T, dXS = U dS'^T
+    {
+      const SFrag fdo = fk(dOp, PB, LB, 16 * m + n, 0, g);
+      const SFrag fu = fk(Up, PB, LB, 16 * m + n, 0, g);
+      SFrag fdr;
+      if constexpr (SOLVE) fdr = fk(dRp, PB, LB, 16 * m + n, 0, g);
+      if (w < 4) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (s <= m) mma3(aMm[s], fdo, fk(Up, PB, LB, 16 * s + n, 0, g));
+      } else if constexpr (SOLVE) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (s <= m) mma3(aMm[s], fdr, fk(Up, PB, LB, 16 * s + n, 0, g));
+      }
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int dt = ctw * DPW + d;
+        const SFrag fs = fk(Sp, PS, LB, 16 * dt + n, 0, g);
+        mma3(aQ1[d], fdo, fs);
+        if constexpr (SOLVE) mma3(aXR[d], fdr, fs);
+        mma3(aXS[d], fu, fk(dSp, PS, LB, 16 * dt + n, 0, g));
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- phase 2
+  // <dS', S> over the workgroup
+  sds = wave_sum(sds);
+  if (lane == 0) s_red[w] = sds;
+  // eta's (or f's) gradient through the values
+  if constexpr (SOLVE) {
+    pe1 = group_sum<NCOL / 4>(pe1);
+    if (tid % (NCOL / 4) == 0) s_p[kPe0][bt] = pe1;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = sum16(pe[i]);
+      if (n == 0) s_p[kPe0 + ctw][16 * m + 4 * g + i] = v;
+    }
+  }
+  // row dots with the state-coupled terms, after their row factors
+  {
+    float pq[4] = {0.f, 0.f, 0.f, 0.f}, pr[4] = {0.f, 0.f, 0.f, 0.f}, ph[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        aQ1[d][i] *= fac(kScGam, t);
+        aXR[d][i] *= -fac(kScE, t) * fac(kScGprev, t);
+        aXS[d][i] *= fac(kScGend, t);
+        const float x = get_split(Xp, PX, t * LX + dc);
+        pr[i] += x * aXR[d][i];
+        ph[i] += x * aXS[d][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = sum16(pr[i]), h = sum16(ph[i]);
+      if (n == 0) {
+        s_p[kPdXR0 + ctw][16 * m + 4 * g + i] = r;
+        s_p[kPh0 + ctw][16 * m + 4 * g + i] = h;
+      }
+    }
+    __syncthreads();  // phase-1 block buffers and (delta rule) T free
+    stage_split<InT, DK, R::shift, true, 512>(p, bh, c, Qp, has_in);
+    if constexpr (SOLVE) {
+      for (int e = tid; e < CB * CB / 4; e += 512) {
+        const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+        *reinterpret_cast<f4*>(Lp + r * LDC + c4) = *reinterpret_cast<const f4*>(rec + BRec::kLp + r * CB + c4);
+      }
+    }
+    for (int e = tid; e < 2 * (SOLVE ? 2 : 1) * PC / 8; e += 512) reinterpret_cast<u32x4*>(A1p)[e] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pq[i] += get_split(Qp, PX, (16 * m + 4 * g + i) * LX + dc) * aQ1[d][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q = sum16(pq[i]);
+      if (n == 0) s_p[kPdQ0 + ctw][16 * m + 4 * g + i] = q;
+    }
+  }
+  // A1 = dMm o D with the row and column sums of dMm o M (waves 0-3), W = dLm o eta D' with
+  // the row and column sums of dLm o L and the row sums of dLm o Lp (waves 4-7)
+  {
+    const float* gl = s_sc[kScG];
+    const float* pa = s_sc[kScPar];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f}, rs2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s > m) continue;
+      float cs = 0.f;
+      const int sc = 16 * s + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        if (w < 4) {
+          if (sc <= t) {
+            const float d = sgn((int)pa[t] ^ (int)pa[sc]) * __expf(gl[t] - gl[sc]);
+            const float v = aMm[s][i];
+            put_split(A1p, PC, t * LC + sc, v * d);
+            const float pm = v * Ms[t * LDC + sc];
+            rs[i] += pm;
+            cs += pm;
+          }
+        } else if constexpr (SOLVE) {
+          if (sc < t) {
+            const float dl = -aMm[s][i];  // dLm = -dR U^T (the waves accumulated dR U^T)
+            const float lp = Lp[t * LDC + sc];  // D'_ts (x_t . x_s)
+            const float e = fac(kScE, t);
+            const float dp = sgn((int)pa[t - 1] ^ (int)pa[sc]) * __expf(gl[t - 1] - gl[sc]);  // D'_ts
+            put_split(Wp, PC, t * LC + sc, dl * e * dp);
+            rs[i] += dl * e * lp;   // dLm o L
+            rs2[i] += dl * lp;      // dLm o Lp
+            cs += dl * e * lp;
+          }
+        }
+      }
+      // column sums over this tile's 16 rows: the four lane groups
+      cs += __shfl_xor(cs, 16);
+      cs += __shfl_xor(cs, 32);
+      if (g == 0) {
+        if (w < 4) s_p[kPMc0 + m][sc] += cs;
+        else if (SOLVE) s_p[kPLc0 + m][sc] += cs;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = sum16(rs[i]), b = sum16(rs2[i]);
+      if (n == 0) {
+        const int t = 16 * m + 4 * g + i;
+        if (w < 4) s_p[kPMr][t] = a;
+        else if (SOLVE) {
+          s_p[kPLr][t] = a;
+          s_p[kPeL][t] = b;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // dQ = dQ1 + A1 X;  dX = dXR + dXS + A1^T Q + W X + W^T X (this wave: token tile m, d_k
+  // tiles ctw * DPW ...). Row-tile m's K block is m / 2: A1 X and W X take K blocks up to
+  // it (s <= t), A1^T Q and W^T X the blocks from it on (t >= s).
+  f4 dQ[DPW], dX[DPW];
+  {
+    const int km = m >> 1;
+    SFrag a1[2], a1t[2], wf[2], wft[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb <= km) {
+        a1[kb] = fk(A1p, PC, LC, 16 * m + n, 32 * kb, g);
+        if constexpr (SOLVE) wf[kb] = fk(Wp, PC, LC, 16 * m + n, 32 * kb, g);
+      }
+      if (kb >= km) {
+        a1t[kb] = ft(A1p, PC, LC, 16 * m, 32 * kb, g, n);
+        if constexpr (SOLVE) wft[kb] = ft(Wp, PC, LC, 16 * m, 32 * kb, g, n);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dt = ctw * DPW + d;
+      dQ[d] = aQ1[d];
+      dX[d] = aXR[d] + aXS[d];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const SFrag bx = ft(Xp, PX, LX, 16 * dt, 32 * kb, g, n);
+        if (kb <= km) {
+          mma3x(dQ[d], a1[kb], bx, xex);
+          if constexpr (SOLVE) mma3x(dX[d], wf[kb], bx, xex);
+        }
+        if (kb >= km) {
+          mma3x(dX[d], a1t[kb], ft(Qp, PX, LX, 16 * dt, 32 * kb, g, n), xex);
+          if constexpr (SOLVE) mma3x(dX[d], wft[kb], bx, xex);
+        }
+      }
+    }
+  }
+
+  // the log decays' gradient, its suffix sums, and the scalar chain (wave 0, lane = token)
+  if (w == 0) {
+    const int t = lane;
+    const float hsum = wave_sum(s_p[kPh0][t] + s_p[kPh1][t]);
+    float dg = s_p[kPdQ0][t] + s_p[kPdQ1][t] - s_p[kPh0][t] - s_p[kPh1][t] + s_p[kPMr][t];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dg -= s_p[kPMc0 + k][t];
+    if (t + 1 < CB) dg += s_p[kPdXR0][t + 1] + s_p[kPdXR1][t + 1];
+    if constexpr (SOLVE) {
+      if (t + 1 < CB) dg += s_p[kPLr][t + 1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dg -= s_p[kPLc0 + k][t];
+    }
+    if (t == CB - 1) {
+      float sd = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sd += s_red[k];
+      dg += hsum + rec[BRec::kMisc] * sd;
+    }
+    // suffix sums: dl_t = sum_{t' >= t} dg_t'
+    float dl = dg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(dl, o);
+      if (t + o < 64) dl += y;
+    }
+    const float a = fac(kScA, t);
+    const float af = (a < 0.f ? -1.f : 1.f) * fmaxf(fabsf(a), 1e-30f);
+    const float da = dl / af;
+    const int tau = t0 + t;
+    float dn = 0.f;
+    if (tau < p.T) {
+      const float beta = fac(kScBeta, t), lam = fac(kScLam, t);
+      const bool key = fac(kScKey, t) != 0.f;
+      float gb = 0.f, gl = 0.f;
+      if constexpr (R::nlms) {
+        if (key) {
+          const float e = fac(kScE, t), den = fac(kScDen, t), lu = fac(kScLu, t), nx = fac(kScN, t);
+          float de = s_p[kPe0][t] + s_p[kPe1][t];
+          if (SOLVE) de += s_p[kPeL][t];
+          de -= lu * da;
+          gb = de / den;
+          const float dden = -e * de / den;
+          const float dlu = -e * da + dden;
+          const bool scaled = (p.flags & kFlagLamScaled) != 0;
+          dn = dden + (scaled ? lam * dlu : 0.f);
+          gl = dlu * (scaled ? nx : 1.f);
+        }
+      } else {
+        gb = s_p[kPe0][t] + s_p[kPe1][t];
+        gl = da;
+      }
+      // with pre-activated gates: the gradient with respect to the pre-activation
+      if (p.flags & kFlagBetaSig) gb *= beta * (1.f - beta);
+      else if (p.flags & kFlagBetaSig2) gb *= beta * (1.f - 0.5f * beta);
+      if (p.flags & kFlagLamAct) gl *= R::nlms ? -expm1f(-lam) : lam * (1.f - lam);
+      if (p.gbeta != nullptr) p.gbeta[rb + tau] = gb;
+      if (p.glam != nullptr) p.glam[rb + tau] = gl;
+    }
+    s_dn[t] = dn;
+  }
+  __syncthreads();
+
+  // the feature maps' derivative from the staged values y = phi(z): 1 for the identity;
+  // for elu+1, 1 where y > 1 (z > 0) and y = exp(z) elsewhere
+  auto dphi = [&](float y) { return elu ? (y > 1.f ? 1.f : y) : 1.f; };
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int dc = 16 * (ctw * DPW + d) + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * m + 4 * g + i, tau = t0 + t;
+      const float x = get_split(Xp, PX, t * LX + dc);
+      const float gx = dX[d][i] + 2.f * s_dn[t] * x;
+      if (tau < p.T) p.gq[(rb + tau) * DK + dc] = dQ[d][i] * dphi(get_split(Qp, PX, t * LX + dc));
+      if constexpr (R::shift) {
+        // x_t is the key of token tau - 1 (the carried key before the first token)
+        if (tau >= 1 && tau < p.T) p.gk[(rb + tau - 1) * DK + dc] = gx * dphi(x);
+        else if (tau == 0 && p.gx0 != nullptr) p.gx0[(size_t)bh * DK + dc] = has_in ? gx : 0.f;
+      } else {
+        if (tau < p.T) p.gk[(rb + tau) * DK + dc] = gx * dphi(x);
+      }
+    }
+  }
+  if constexpr (R::shift) {
+    // the last key is written by no step of this call
+    if (c == nch - 1)
+      for (int i = tid; i < DK; i += 512) p.gk[(rb + p.T - 1) * DK + i] = 0.f;
+  } else {
+    if (c == 0 && p.gx0 != nullptr)
+      for (int i = tid; i < DK; i += 512) p.gx0[(size_t)bh * DK + i] = 0.f;
+  }
+}
+
+// ====================== state and dstate on bf16 MFMA with split operands (bf16 inputs)
+// The chunk steps of bwd_state_kernel and bwd_dstate_kernel with every product on
+// v_mfma_f32_16x16x32_bf16: the keys and queries as split planes (exact bf16 for raw keys
+// and queries with the identity map; the carried key of chunk 0 is fp32), S, R, W, T, M,
+// dS, dO, dU and dR as hi/lo planes.
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(256) void bwd_state_bf_kernel(BwdParams p, const float* recs, float* Sch, float* Rh) {
+  using R = Rule<RULE>;
+  constexpr int NRT = DK / 16, RPW = NRT / 4;  // row tiles of S per wave
+  constexpr int VWv = 16 / (int)sizeof(InT), NVG = CB * NCOL / VWv;  // value groups
+  constexpr int NVJ = (NVG + 255) / 256;
+  constexpr int LX = DK + 8, LC = CB + 8, PX = CB * LX, PT = CB * LC, PB = NCOL * LX, PW = NCOL * LC;
+  __shared__ __align__(16) uint16_t Xp[2 * PX];
+  __shared__ __align__(16) uint16_t Tp[R::solve ? 2 * PT : 8];
+  __shared__ __align__(16) uint16_t Bp[2 * PB];                 // S^T [NCOL][DK], then W^T [NCOL][CB]
+  __shared__ __align__(16) uint16_t Rp[R::solve ? 2 * PW : 8];  // R^T [NCOL][CB]
+  __shared__ __align__(16) float Vs[CB * LDU];                  // the chunk's values [CB][NCOL]
+  // eta Gamma_prev, eta (or f), Gamma_end / Gamma, Gamma_prev; [4][0] Gamma_end
+  __shared__ float s_fac[5][CB];
+  int bh, grp;
+  if (!state_block(p, DV / NCOL, bh, grp)) return;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = (p.T + CB - 1) / CB;
+  const bool has_in = head_has_key(p, bh);
+  const int col0 = grp * NCOL;
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
+  const InT* vb = static_cast<const InT*>(p.v) + rb * DV + col0;
+
+  f4 S[RPW][2];
+#pragma unroll
+  for (int a = 0; a < RPW; ++a)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (w + 4 * a) + 4 * g + i;
+        S[a][ct][i] = p.S_in != nullptr ? p.S_in[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * ct + n] : 0.f;
+      }
+
+  // registers of the next chunk: rows, T (16 floats a thread), values, scalars
+  Rows<InT, DK, 256> rows;
+  f4 pt[4];
+  u32x4 pv[NVJ];
+  float pf[5];
+  auto load = [&](int c) {
+    rows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 16 * tid + 4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < NVJ; ++j) {
+      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv, tau = c * CB + t;
+      pv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < NVG && tau < p.T) pv[j] = *reinterpret_cast<const u32x4*>(vb + (size_t)tau * DV + v0);
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      const float e = sc[kScE * CB + tid];
+      pf[0] = e * sc[kScGprev * CB + tid];
+      pf[1] = e;
+      pf[2] = sc[kScGend * CB + tid];
+      pf[3] = sc[kScGprev * CB + tid];
+      pf[4] = rec[BRec::kMisc];
+    }
+  };
+  auto commit = [&](int c) {
+    const float* x0 = (R::shift && has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+    rows.commit_split(Xp, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put_split4(Tp, PT, (tid >> 2) * LC + 16 * (tid & 3) + 4 * j, pt[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NVJ; ++j) {
+      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv;
+      if (idx < NVG) {
+        float x[VWv];
+        In<InT>::decode(pv[j], x);
+#pragma unroll
+        for (int e = 0; e < VWv; e += 4) *reinterpret_cast<f4*>(Vs + t * LDU + v0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+      }
+    }
+    if (tid < CB) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s_fac[k][tid] = pf[k];
+      if (tid == 0) s_fac[4][0] = pf[4];
+    }
+  };
+  if (R::solve || nch > 1) load(0);
+
+  for (int c = 0; c < nch; ++c) {
+    float* Sc = Sch + ((size_t)bh * nch + c) * SS;
+#pragma unroll
+    for (int a = 0; a < RPW; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Sc[(size_t)(16 * (w + 4 * a) + 4 * g + i) * DV + col0 + 16 * ct + n] = S[a][ct][i];
+    if (!R::solve && c + 1 == nch) break;  // the state after the last chunk is not needed
+    lds_barrier();  // the previous chunk's LDS reads are done
+    commit(c);
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int a = 0; a < RPW; ++a)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) put_split4(Bp, PB, (16 * ct + n) * LX + 16 * (w + 4 * a) + 4 * g, S[a][ct]);
+    }
+    lds_barrier();
+    if (c + 1 < nch && (R::solve || c + 2 < nch)) load(c + 1);
+    const bool xex = !elu && !(len > 0.f) && !(R::shift && c == 0 && has_in);
+
+    // this wave's token tile w: W = fU U with U = T R (delta) or fV V
+    f4 W[2];
+    if constexpr (R::solve) {
+      // R-hat = V - Gamma_prev X S, kept for the gradient pass, and R = eta R-hat
+      float* rh = Rh + ((size_t)bh * nch + c) * CB * DV + col0;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+          mma3a(xs, fk(Xp, PX, LX, 16 * w + n, 32 * kb, g), fk(Bp, PB, LX, 16 * ct + n, 32 * kb, g), xex);
+        f4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * w + 4 * g + i;
+          const float rhat = Vs[t * LDU + 16 * ct + n] - s_fac[3][t] * xs[i];
+          rh[(size_t)t * DV + 16 * ct + n] = rhat;
+          r[i] = s_fac[1][t] * rhat;
+        }
+        put_split4(Rp, PW, (16 * ct + n) * LC + 16 * w + 4 * g, r);
+      }
+      if (c + 1 == nch) break;  // the state after the last chunk is not needed
+      lds_barrier();
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb <= (w >> 1)) mma3(u, fk(Tp, PT, LC, 16 * w + n, 32 * kb, g), fk(Rp, PW, LC, 16 * ct + n, 32 * kb, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) W[ct][i] = s_fac[2][16 * w + 4 * g + i] * u[i];
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * w + 4 * g + i;
+          W[ct][i] = s_fac[2][t] * s_fac[1][t] * Vs[t * LDU + 16 * ct + n];
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) put_split4(Bp, PW, (16 * ct + n) * LC + 16 * w + 4 * g, W[ct]);
+    lds_barrier();
+    // S' = Gamma_end S + X^T W
+    const float gend = s_fac[4][0];
+#pragma unroll
+    for (int a = 0; a < RPW; ++a)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        S[a][ct] *= gend;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma3a(S[a][ct], ft(Xp, PX, LX, 16 * (w + 4 * a), 32 * kb, g, n), fk(Bp, PW, LC, 16 * ct + n, 32 * kb, g), xex);
+      }
+  }
+}
+
+template <typename InT, int DK, int DV, int RULE>
+__global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const float* recs, float* dSch, float* dRw) {
+  using R = Rule<RULE>;
+  constexpr int NRT = DK / 16;
+  constexpr int NTW = NRT / 4;  // dS tiles of a wave (DK 128: row tile w, both column tiles; DK 64: one)
+  constexpr int LX = DK + 8, LC = CB + 8, PX = CB * LX, PT = CB * LC, PB = NCOL * LX, PW = NCOL * LC;
+  __shared__ __align__(16) uint16_t Xp[2 * PX];
+  __shared__ __align__(16) uint16_t Qp[2 * PX];
+  __shared__ __align__(16) uint16_t Tp[R::solve ? 2 * PT : 8];
+  __shared__ __align__(16) uint16_t Mp[R::solve ? 2 * PT : 8];
+  __shared__ __align__(16) uint16_t dOp[2 * PW];  // dO^T of the column group [NCOL][CB]
+  __shared__ __align__(16) uint16_t gOp[2 * PW];  // (Gamma o dO)^T
+  __shared__ __align__(16) uint16_t Bp[2 * PB];   // dS^T [NCOL][DK], then (delta) -(eta Gamma_prev dR)^T [NCOL][CB]
+  __shared__ __align__(16) uint16_t dUp[R::solve ? 2 * PW : 8];
+  __shared__ float s_fac[4][CB];  // Gamma, eta Gamma_prev, Gamma_end / Gamma; [3][0] Gamma_end
+  int bh, grp;
+  if (!state_block(p, DV / NCOL, bh, grp)) return;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = (p.T + CB - 1) / CB;
+  const bool has_in = head_has_key(p, bh);
+  const int col0 = grp * NCOL;
+  const size_t SS = (size_t)DK * DV, rb = (size_t)bh * p.T;
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const bool qex = !elu && !(len > 0.f);
+  const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
+  const InT* qb = static_cast<const InT*>(p.q) + rb * DK;
+  const float* dob = p.dout + rb * DV + col0;
+  auto tile_rt = [&](int a) { return NTW == 2 ? w : (w & 3); };
+  auto tile_ct = [&](int a) { return NTW == 2 ? a : (w >> 2); };
+
+  f4 dS[NTW];
+#pragma unroll
+  for (int a = 0; a < NTW; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tile_rt(a) + 4 * g + i;
+      dS[a][i] = p.dS_out != nullptr ? p.dS_out[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * tile_ct(a) + n] : 0.f;
+    }
+  const int m = w & 3, ctw = w >> 2;  // this wave's (token tile, column tile) of dU and dR
+
+  // registers of the next chunk: X and Q rows, T and M (8 floats a thread each), dO (4), scalars
+  Rows<InT, DK, 512> xrows, qrows;
+  f4 pt[2], pm[2], pd;
+  float pf[4], pgam;
+  auto load = [&](int c) {
+    xrows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
+    qrows.load(qb, c * CB, 0, p.T);
+    const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 8 * tid + 4 * j);
+        pm[j] = *reinterpret_cast<const f4*>(rec + BRec::kM + 8 * tid + 4 * j);
+      }
+    }
+    {
+      const int t = tid / (NCOL / 4), v0 = (tid % (NCOL / 4)) * 4, tau = c * CB + t;
+      pd = tau < p.T ? *reinterpret_cast<const f4*>(dob + (size_t)tau * DV + v0) : f4{0.f, 0.f, 0.f, 0.f};
+      pgam = rec[BRec::kSc + kScGam * CB + t];
+    }
+    if (tid < CB) {
+      const float* sc = rec + BRec::kSc;
+      pf[0] = sc[kScGam * CB + tid];
+      pf[1] = sc[kScE * CB + tid] * sc[kScGprev * CB + tid];
+      pf[2] = sc[kScGend * CB + tid];
+      pf[3] = rec[BRec::kMisc];
+    }
+  };
+  auto commit = [&](int c) {
+    const float* x0 = (R::shift && has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
+    xrows.commit_split(Xp, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
+    qrows.commit_split(Qp, elu, len, -1, nullptr);
+    if constexpr (R::solve) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        put_split4(Tp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pt[j]);
+        put_split4(Mp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pm[j]);
+      }
+    }
+    {
+      const int t = tid / (NCOL / 4), v0 = (tid % (NCOL / 4)) * 4;
+      const float gam = pgam;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        put_split(dOp, PW, (v0 + i) * LC + t, pd[i]);
+        put_split(gOp, PW, (v0 + i) * LC + t, gam * pd[i]);
+      }
+    }
+    if (tid < CB) {
+      s_fac[0][tid] = pf[0];
+      s_fac[1][tid] = pf[1];
+      s_fac[2][tid] = pf[2];
+      if (tid == 0) s_fac[3][0] = pf[3];
+    }
+  };
+  load(nch - 1);
+
+  for (int c = nch - 1; c >= 0; --c) {
+    float* dSc = dSch + ((size_t)bh * nch + c) * SS;
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dSc[(size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
+    lds_barrier();  // the previous chunk's LDS reads are done
+    commit(c);
+#pragma unroll
+    for (int a = 0; a < NTW; ++a) put_split4(Bp, PB, (16 * tile_ct(a) + n) * LX + 16 * tile_rt(a) + 4 * g, dS[a]);
+    lds_barrier();
+    if (c >= 1) load(c - 1);
+    const bool xex = qex && !(R::shift && c == 0 && has_in);
+
+    if constexpr (R::solve) {
+      // dU = M^T dO + (Gamma_end / Gamma) X dS' for token tile m, column tile ctw (only the
+      // delta rule's state gradient goes through the writes)
+      f4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        mma3a(du, fk(Xp, PX, LX, 16 * m + n, 32 * kb, g), fk(Bp, PB, LX, 16 * ctw + n, 32 * kb, g), xex);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] *= s_fac[2][16 * m + 4 * g + i];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb >= (m >> 1)) mma3(du, ft(Mp, PT, LC, 16 * m, 32 * kb, g, n), fk(dOp, PW, LC, 16 * ctw + n, 32 * kb, g));
+      put_split4(dUp, PW, (16 * ctw + n) * LC + 16 * m + 4 * g, du);
+      lds_barrier();  // dU complete; dS^T no longer read
+      // dR = T^T dU
+      f4 dr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb >= (m >> 1)) mma3(dr, ft(Tp, PT, LC, 16 * m, 32 * kb, g, n), fk(dUp, PW, LC, 16 * ctw + n, 32 * kb, g));
+      // dR, kept for the gradient pass
+      float* drw = dRw + ((size_t)bh * nch + c) * CB * DV + col0 + 16 * ctw + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        drw[(size_t)(16 * m + 4 * g + i) * DV] = dr[i];
+        dr[i] *= -s_fac[1][16 * m + 4 * g + i];
+      }
+      put_split4(Bp, PW, (16 * ctw + n) * LC + 16 * m + 4 * g, dr);
+      lds_barrier();
+    }
+    // dS = Gamma_end dS' + Q^T diag(Gamma) dO - X^T (eta Gamma_prev dR)
+    const float gend = s_fac[3][0];
+#pragma unroll
+    for (int a = 0; a < NTW; ++a) {
+      const int rt = tile_rt(a), ct = tile_ct(a);
+      dS[a] *= gend;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        mma3a(dS[a], ft(Qp, PX, LX, 16 * rt, 32 * kb, g, n), fk(gOp, PW, LC, 16 * ct + n, 32 * kb, g), qex);
+        if constexpr (R::solve)
+          mma3a(dS[a], ft(Xp, PX, LX, 16 * rt, 32 * kb, g, n), fk(Bp, PW, LC, 16 * ct + n, 32 * kb, g), xex);
+      }
+    }
+  }
+  if (p.gS0 != nullptr) {
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.gS0[(size_t)bh * SS + (size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = dS[a][i];
+    if (grp == 0 && tid == 0 && p.gh0 != nullptr) p.gh0[bh] = 0;
+  }
+}
+
 template <typename InT, int DK, int DV, int RULE>
 hipError_t launch_rule(const BwdParams& p, float* ws, hipStream_t st) {
   const int nch = (p.T + CB - 1) / CB;
@@ -1221,10 +2173,19 @@ hipError_t launch_rule(const BwdParams& p, float* ws, hipStream_t st) {
   float* dRw = Rh + nrec * (size_t)CB * DV;   // dR of every chunk (delta rule)
   const unsigned ngrid = (unsigned)(8 * (DV / NCOL) * ((p.BH + 7) / 8));
   hipLaunchKernelGGL((bwd_prep_kernel<InT, DK, RULE>), dim3((unsigned)nrec), dim3(256), 0, st, p, recs);
-  hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
-  hipLaunchKernelGGL((bwd_dstate_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch, dRw);
-  hipLaunchKernelGGL((bwd_grad_kernel<InT, DK, DV, RULE>), dim3((unsigned)nrec), dim3(512), 0, st, p, recs, Sch,
-                     dSch, Rh, dRw);
+  if constexpr (sizeof(InT) == 2) {
+    hipLaunchKernelGGL((bwd_state_bf_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
+    hipLaunchKernelGGL((bwd_dstate_bf_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch, dRw);
+  } else {
+    hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
+    hipLaunchKernelGGL((bwd_dstate_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch, dRw);
+  }
+  if constexpr (sizeof(InT) == 2)
+    hipLaunchKernelGGL((bwd_grad_kernel<InT, DK, DV, RULE>), dim3((unsigned)nrec), dim3(512), 0, st, p, recs, Sch,
+                       dSch, Rh, dRw);
+  else
+    hipLaunchKernelGGL((bwd_grad_f32_kernel<InT, DK, DV, RULE>), dim3((unsigned)nrec), dim3(512), 0, st, p, recs,
+                       Sch, dSch, Rh, dRw);
   return hipGetLastError();
 }
 

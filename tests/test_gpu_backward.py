@@ -3,8 +3,13 @@ scan_backward: every gradient (q, k, v, beta, lambda, the initial state and the 
 key) for the delta, inner and additive rules, phi identity and elu+1, bf16 and float32
 inputs, carried and fresh states, ragged chunk tails, a lone no-op step and T = 0.
 
-The kernel computes in float32 whatever the input type (bf16 inputs are exact in both),
-so every gradient is held to the float32 bar."""
+With float32 inputs every product runs in float32 and every gradient is held to the
+float32 bar (1e-4). With bf16 inputs the chunk-parallel kernels (delta, inner and additive
+rules with a scalar decay, no normaliser) carry every operand that is not an exact bf16
+input as a bf16 hi + lo pair, about 16 bits of each factor, as the split forward kernels
+do: those gradients are held to 1e-3 of rms, inside the 2e-2 bound for bf16 inputs. The
+token-serial kernel (per-channel lambda, the per-value-channel rule, the normaliser) stays
+float32 and keeps the float32 bar."""
 import numpy as np
 import pytest
 
@@ -16,6 +21,14 @@ from tests.gpu_helpers import TOL, dev_tensor, f32_tensor, make_state, say
 pytestmark = pytest.mark.gpu
 
 RULES = {"delta": wl.RULE_DELTA, "inner": wl.RULE_INNER, "additive": wl.RULE_ADDITIVE}
+TOL_SPLIT = 1e-3
+
+
+def _tol(w):
+    """The bar for w's gradients: 1e-3 where the split-operand chunked kernels serve it."""
+    split = (w.dtype == "bf16" and w.rule in (wl.RULE_DELTA, wl.RULE_INNER, wl.RULE_ADDITIVE)
+             and not w.per_channel and not getattr(w, "znorm", False))
+    return TOL_SPLIT if split else TOL["f32"]
 
 
 def _problem(rule, phi, dtype, dk, dv, T, carried, seed, B=2, H=2, lam_kind=None, beta_kind=None,
@@ -54,10 +67,11 @@ def _run(w, dO, dS, xprev0, has0, phi, carried, with_dS=True):
                             rule=w.rule, phi_kind=phi, eps=w.eps, per_channel=w.per_channel,
                             S0=w.S0 if carried else None,
                             xprev0=xprev0, has0=has0)
-    return g, ref
+    return g, ref, w
 
 
-def _compare(g, ref, tol=TOL["f32"]):
+def _compare(g, ref, w, tol=None):
+    tol = _tol(w) if tol is None else tol
     got = {"q": g["q"], "k": g["k"], "v": g["v"], "beta": g["beta"], "lam": g["lam"],
            "S0": g["state"].S, "xprev0": g["state"].x_prev}
     errs = {}
@@ -134,8 +148,8 @@ def test_backward_lone_noop_step():
     the read has gradients; the final-state gradient passes straight through."""
     say("[bwd] delta T=1 no carried key")
     w, dO, dS, x0, h0 = _problem("delta", "identity", "f32", 64, 64, 1, False, 9)
-    g, ref = _run(w, dO, dS, x0, h0, "identity", False)
-    _compare(g, ref)
+    g, ref, _ = _run(w, dO, dS, x0, h0, "identity", False)
+    _compare(g, ref, w)
     assert np.all(g["v"].cpu().numpy() == 0) and np.all(g["beta"].cpu().numpy() == 0)
 
 
@@ -157,8 +171,8 @@ def test_backward_is_deterministic():
     """Two calls on the same inputs give bit-identical gradients (no atomics)."""
     say("[bwd] repeatability")
     w, dO, dS, x0, h0 = _problem("delta", "identity", "bf16", 128, 128, 140, True, 11)
-    g1, _ = _run(w, dO, dS, x0, h0, "identity", True)
-    g2, _ = _run(w, dO, dS, x0, h0, "identity", True)
+    g1 = _run(w, dO, dS, x0, h0, "identity", True)[0]
+    g2 = _run(w, dO, dS, x0, h0, "identity", True)[0]
     for n in ("q", "k", "v", "beta", "lam"):
         assert np.array_equal(g1[n].cpu().numpy(), g2[n].cpu().numpy()), n
     assert np.array_equal(g1["state"].buf.cpu().numpy(), g2["state"].buf.cpu().numpy())
@@ -198,7 +212,7 @@ def test_backward_full_size_sampled_heads(name, heads):
                                 ref["S0"])
         say(f"    head ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
-            assert e <= TOL["f32"], f"grad {n}: {e:.3e}"
+            assert e <= _tol(w), f"grad {n}: {e:.3e}"
 
 
 @pytest.mark.parametrize("rule,beta_act,per_channel,dtype,T", [
@@ -231,7 +245,7 @@ def test_backward_pre_activated_gates(rule, beta_act, per_channel, dtype, T):
                    flags=flags, eps=w.eps, S_in=S_in, grad_S_out=make_state(w.B, w.H, w.dk, w.dv, S=dS))
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta_pre, w.lam_pre, dO, dS, rule=r, eps=w.eps,
                             per_channel=per_channel, S0=w.S0, beta_act=beta_act, lam_act=True)
-    _compare(g, ref)
+    _compare(g, ref, w)
 
 
 @pytest.mark.parametrize("rule,qk,dtype,dk,dv,T,per_channel", [
@@ -266,7 +280,7 @@ def test_backward_qk_norm(rule, qk, dtype, dk, dv, T, per_channel):
                    grad_S_out=make_state(w.B, w.H, dk, dv, S=dS))
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS, rule=r, eps=w.eps,
                             per_channel=per_channel, S0=w.S0, xprev0=x0, has0=h0, qk_norm=qk)
-    _compare(g, ref)
+    _compare(g, ref, w)
 
 
 @pytest.mark.parametrize("rule,dtype,dk,dv,T,extra", [
@@ -301,7 +315,7 @@ def test_backward_scaled_ridge(rule, dtype, dk, dv, T, extra):
                             xprev0=x0, has0=h0, lam_scaled=True,
                             qk_norm="rms" if both else None,
                             beta_act="sigmoid2" if both else None, lam_act=both)
-    _compare(g, ref)
+    _compare(g, ref, w)
 
 
 @pytest.mark.parametrize("dtype,dk,dv,T,extra", [
@@ -343,7 +357,7 @@ def test_backward_per_value_channel(dtype, dk, dv, T, extra):
     ref = orc.scan_backward(w.q, w.k, w.v, beta, lam, dO, dS, rule=r, phi_kind=phi, eps=w.eps,
                             S0=w.S0, xprev0=x0, has0=h0, qk_norm="rms" if opts else None,
                             lam_scaled=opts, beta_act="sigmoid2" if opts else None, lam_act=opts)
-    _compare(g, ref)
+    _compare(g, ref, w)
 
 
 @pytest.mark.parametrize("phi,dtype,dk,dv,T,extra", [
@@ -379,7 +393,7 @@ def test_backward_normaliser(phi, dtype, dk, dv, T, extra):
                             S0=w.S0, xprev0=w.xprev0, znorm=True, qk_norm="l2" if both else None,
                             beta_act="sigmoid" if both else None, lam_act=both, dz=dz)
     assert np.any(ref["xprev0"] != 0)
-    _compare(g, ref)
+    _compare(g, ref, w)
 
 
 def test_backward_normaliser_chains_over_calls():
@@ -415,7 +429,7 @@ def test_backward_normaliser_chains_over_calls():
                     grad_S_out=g2["state"])
     ref = orc.scan_backward(w.q, w.k, w.v, w.beta, w.lam, dO, dS, rule=r, phi_kind="elu1",
                             eps=w.eps, S0=w.S0, xprev0=w.xprev0, znorm=True, dz=dz)
-    _compare(g, ref)
+    _compare(g, ref, w)
     for name in ("q", "k", "v", "beta", "lam"):
         both_parts = np.concatenate([g1[name].cpu().numpy(), g2[name].cpu().numpy()], axis=2)
         e = orc.relerr(both_parts, g[name].cpu().numpy())
