@@ -46,19 +46,19 @@ MEASURED_TRAFFIC = {
         "sources": ('fwmem_scan_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
             "fwmem_scan_split.hip": "888db0e0e31bca242ef147c8412775f748ed947fd0abc340b58805efbbd84eab",
-            "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 150223.0, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150222.9, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
         "sources": ('fwmem_prep_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
             "fwmem_prep_split.hip": "3101a25cff5f80c14678715ef955e7813e5203414cf5f028e6a8e885c74a10f8",
-            "fwmem_split.h": "fd7ad40e1646fe0235dcb48eeb3eb8a83c69fd5dbd10d7109f1ca9f8fdb8adea",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
         "fetch_kib": 66681.5, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
@@ -67,49 +67,53 @@ MEASURED_TRAFFIC = {
         "sha256": {
             "fwmem_step.hip": "abf27317cda12cc5a31bfd56f61be55aedc5758d577a0abf5f1d25a096ca1990",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 267738.3, "write_kib": 532868.2, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267738.3, "write_kib": 532861.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_prep_kernel"): {
-        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 66691.1, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66695.2, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
     },
-    ("delta_bf16_h16", "bwd_state_kernel"): {
-        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+    ("delta_bf16_h16", "bwd_state_bf_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 100168.2, "write_kib": 393216.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 100197.7, "write_kib": 393216.1, "read_factor": 2.0, "write_factor": 1.0,
     },
-    ("delta_bf16_h16", "bwd_dstate_kernel"): {
-        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+    ("delta_bf16_h16", "bwd_dstate_bf_kernel"): {
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 198986.3, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 199002.8, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_grad_kernel"): {
-        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_device.h', 'fwmem_internal.h'),
+        "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "3c15b68255e3014a42b6a4f1240551e65edc0d6fb6cc17f8b6c392a4f0ef5aee",
+            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
+            "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "c80ee3bfba61c5f9615132db2750593c3f26fa427ff1adca33784d8c04b0ddff",
+            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 629702.2, "write_kib": 395610.6, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 629742.5, "write_kib": 395491.6, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
@@ -511,8 +515,12 @@ def bench_backward(w, steps, dev, stream, q, k, v, beta, lam):
     # the chunk-parallel kernels take the scalar-decay delta, inner and additive rules without
     # the normaliser; every other mode runs the token-serial kernel
     chunked = w.rule in (0, 1, 2) and not w.per_channel and not w.znorm
-    kernels = (["bwd_prep_kernel", "bwd_state_kernel", "bwd_dstate_kernel", "bwd_grad_kernel"]
-               if chunked else ["bwd_kernel"])
+    if chunked and w.dtype == "bf16":  # split operands on bf16 MFMA
+        kernels = ["bwd_prep_kernel", "bwd_state_bf_kernel", "bwd_dstate_bf_kernel", "bwd_grad_kernel"]
+    elif chunked:  # float32 inputs: float32 MFMA
+        kernels = ["bwd_prep_kernel", "bwd_state_kernel", "bwd_dstate_kernel", "bwd_grad_f32_kernel"]
+    else:
+        kernels = ["bwd_kernel"]
     if w.qk_norm is not None:
         kernels.append("qk_norm_bwd_kernel")
     traffic = None

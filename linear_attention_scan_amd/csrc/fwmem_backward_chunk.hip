@@ -1825,11 +1825,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
 // and queries with the identity map; the carried key of chunk 0 is fp32), S, R, W, T, M,
 // dS, dO, dU and dR as hi/lo planes.
 template <typename InT, int DK, int DV, int RULE>
-__global__ __launch_bounds__(256) void bwd_state_bf_kernel(BwdParams p, const float* recs, float* Sch, float* Rh) {
+__global__ __launch_bounds__(512) void bwd_state_bf_kernel(BwdParams p, const float* recs, float* Sch, float* Rh) {
   using R = Rule<RULE>;
-  constexpr int NRT = DK / 16, RPW = NRT / 4;  // row tiles of S per wave
+  constexpr int NRT = DK / 16;
+  constexpr int NTW = NRT / 4;  // S tiles of a wave (DK 128: row tile w, both column tiles; DK 64: one)
   constexpr int VWv = 16 / (int)sizeof(InT), NVG = CB * NCOL / VWv;  // value groups
-  constexpr int NVJ = (NVG + 255) / 256;
+  static_assert(NVG <= 512, "value groups");
   constexpr int LX = DK + 8, LC = CB + 8, PX = CB * LX, PT = CB * LC, PB = NCOL * LX, PW = NCOL * LC;
   __shared__ __align__(16) uint16_t Xp[2 * PX];
   __shared__ __align__(16) uint16_t Tp[R::solve ? 2 * PT : 8];
@@ -1850,35 +1851,36 @@ __global__ __launch_bounds__(256) void bwd_state_bf_kernel(BwdParams p, const fl
   const float len = qk_length(p.flags, DK);
   const InT* kb = static_cast<const InT*>(p.k) + rb * DK;
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV + col0;
+  auto tile_rt = [&](int a) { return NTW == 2 ? w : (w & 3); };
+  auto tile_ct = [&](int a) { return NTW == 2 ? a : (w >> 2); };
+  const int m = w & 3, ctw = w >> 2;  // this wave's (token tile, column tile) of X S, R and U
 
-  f4 S[RPW][2];
+  f4 S[NTW];
 #pragma unroll
-  for (int a = 0; a < RPW; ++a)
+  for (int a = 0; a < NTW; ++a)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * (w + 4 * a) + 4 * g + i;
-        S[a][ct][i] = p.S_in != nullptr ? p.S_in[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * ct + n] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tile_rt(a) + 4 * g + i;
+      S[a][i] = p.S_in != nullptr ? p.S_in[(size_t)bh * SS + (size_t)r * DV + col0 + 16 * tile_ct(a) + n] : 0.f;
+    }
 
-  // registers of the next chunk: rows, T (16 floats a thread), values, scalars
-  Rows<InT, DK, 256> rows;
-  f4 pt[4];
-  u32x4 pv[NVJ];
+  // registers of the next chunk: rows, T (8 floats a thread), values, scalars
+  Rows<InT, DK, 512> rows;
+  f4 pt[2];
+  u32x4 pv;
   float pf[5];
   auto load = [&](int c) {
+    // row t is the key of token c CB + t - 1 for the shifted pair (token 0's is the carried key)
     rows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
     const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
     if constexpr (R::solve) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 16 * tid + 4 * j);
+      for (int j = 0; j < 2; ++j) pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 8 * tid + 4 * j);
     }
-#pragma unroll
-    for (int j = 0; j < NVJ; ++j) {
-      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv, tau = c * CB + t;
-      pv[j] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < NVG && tau < p.T) pv[j] = *reinterpret_cast<const u32x4*>(vb + (size_t)tau * DV + v0);
+    {
+      const int t = tid / (NCOL / VWv), v0 = (tid % (NCOL / VWv)) * VWv, tau = c * CB + t;
+      pv = u32x4{0u, 0u, 0u, 0u};
+      if (tid < NVG && tau < p.T) pv = *reinterpret_cast<const u32x4*>(vb + (size_t)tau * DV + v0);
     }
     if (tid < CB) {
       const float* sc = rec + BRec::kSc;
@@ -1891,21 +1893,19 @@ __global__ __launch_bounds__(256) void bwd_state_bf_kernel(BwdParams p, const fl
     }
   };
   auto commit = [&](int c) {
+    // the carried key (phi applied) before the call's first token
     const float* x0 = (R::shift && has_in && p.xprev_in != nullptr) ? p.xprev_in + (size_t)bh * DK : nullptr;
     rows.commit_split(Xp, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
     if constexpr (R::solve) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) put_split4(Tp, PT, (tid >> 2) * LC + 16 * (tid & 3) + 4 * j, pt[j]);
+      for (int j = 0; j < 2; ++j) put_split4(Tp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pt[j]);
     }
+    if (tid < NVG) {
+      const int t = tid / (NCOL / VWv), v0 = (tid % (NCOL / VWv)) * VWv;
+      float x[VWv];
+      In<InT>::decode(pv, x);
 #pragma unroll
-    for (int j = 0; j < NVJ; ++j) {
-      const int idx = tid + 256 * j, t = idx / (NCOL / VWv), v0 = (idx % (NCOL / VWv)) * VWv;
-      if (idx < NVG) {
-        float x[VWv];
-        In<InT>::decode(pv[j], x);
-#pragma unroll
-        for (int e = 0; e < VWv; e += 4) *reinterpret_cast<f4*>(Vs + t * LDU + v0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
-      }
+      for (int e = 0; e < VWv; e += 4) *reinterpret_cast<f4*>(Vs + t * LDU + v0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
     }
     if (tid < CB) {
 #pragma unroll
@@ -1913,85 +1913,72 @@ __global__ __launch_bounds__(256) void bwd_state_bf_kernel(BwdParams p, const fl
       if (tid == 0) s_fac[4][0] = pf[4];
     }
   };
+  // the delta rule needs every chunk's data (R-hat of the last chunk too), the others
+  // every chunk's but the last
   if (R::solve || nch > 1) load(0);
 
   for (int c = 0; c < nch; ++c) {
     float* Sc = Sch + ((size_t)bh * nch + c) * SS;
 #pragma unroll
-    for (int a = 0; a < RPW; ++a)
+    for (int a = 0; a < NTW; ++a)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Sc[(size_t)(16 * (w + 4 * a) + 4 * g + i) * DV + col0 + 16 * ct + n] = S[a][ct][i];
+      for (int i = 0; i < 4; ++i)
+        Sc[(size_t)(16 * tile_rt(a) + 4 * g + i) * DV + col0 + 16 * tile_ct(a) + n] = S[a][i];
     if (!R::solve && c + 1 == nch) break;  // the state after the last chunk is not needed
     lds_barrier();  // the previous chunk's LDS reads are done
     commit(c);
     if constexpr (R::solve) {
 #pragma unroll
-      for (int a = 0; a < RPW; ++a)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) put_split4(Bp, PB, (16 * ct + n) * LX + 16 * (w + 4 * a) + 4 * g, S[a][ct]);
+      for (int a = 0; a < NTW; ++a) put_split4(Bp, PB, (16 * tile_ct(a) + n) * LX + 16 * tile_rt(a) + 4 * g, S[a]);
     }
     lds_barrier();
     if (c + 1 < nch && (R::solve || c + 2 < nch)) load(c + 1);
     const bool xex = !elu && !(len > 0.f) && !(R::shift && c == 0 && has_in);
 
-    // this wave's token tile w: W = fU U with U = T R (delta) or fV V
-    f4 W[2];
+    // this wave's tile (m, ctw): W = fU U with U = T R (delta) or fV V
+    f4 W;
     if constexpr (R::solve) {
       // R-hat = V - Gamma_prev X S, kept for the gradient pass, and R = eta R-hat
       float* rh = Rh + ((size_t)bh * nch + c) * CB * DV + col0;
+      f4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f4 xs = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < DK / 32; ++kb)
+        mma3a(xs, fk(Xp, PX, LX, 16 * m + n, 32 * kb, g), fk(Bp, PB, LX, 16 * ctw + n, 32 * kb, g), xex);
+      f4 r;
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-          mma3a(xs, fk(Xp, PX, LX, 16 * w + n, 32 * kb, g), fk(Bp, PB, LX, 16 * ct + n, 32 * kb, g), xex);
-        f4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * w + 4 * g + i;
-          const float rhat = Vs[t * LDU + 16 * ct + n] - s_fac[3][t] * xs[i];
-          rh[(size_t)t * DV + 16 * ct + n] = rhat;
-          r[i] = s_fac[1][t] * rhat;
-        }
-        put_split4(Rp, PW, (16 * ct + n) * LC + 16 * w + 4 * g, r);
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        const float rhat = Vs[t * LDU + 16 * ctw + n] - s_fac[3][t] * xs[i];
+        rh[(size_t)t * DV + 16 * ctw + n] = rhat;
+        r[i] = s_fac[1][t] * rhat;
       }
+      put_split4(Rp, PW, (16 * ctw + n) * LC + 16 * m + 4 * g, r);
       if (c + 1 == nch) break;  // the state after the last chunk is not needed
       lds_barrier();
+      f4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f4 u = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (m >> 1)) mma3(u, fk(Tp, PT, LC, 16 * m + n, 32 * kb, g), fk(Rp, PW, LC, 16 * ctw + n, 32 * kb, g));
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          if (kb <= (w >> 1)) mma3(u, fk(Tp, PT, LC, 16 * w + n, 32 * kb, g), fk(Rp, PW, LC, 16 * ct + n, 32 * kb, g));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) W[ct][i] = s_fac[2][16 * w + 4 * g + i] * u[i];
-      }
+      for (int i = 0; i < 4; ++i) W[i] = s_fac[2][16 * m + 4 * g + i] * u[i];
     } else {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * w + 4 * g + i;
-          W[ct][i] = s_fac[2][t] * s_fac[1][t] * Vs[t * LDU + 16 * ct + n];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * g + i;
+        W[i] = s_fac[2][t] * s_fac[1][t] * Vs[t * LDU + 16 * ctw + n];
+      }
     }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) put_split4(Bp, PW, (16 * ct + n) * LC + 16 * w + 4 * g, W[ct]);
+    put_split4(Bp, PW, (16 * ctw + n) * LC + 16 * m + 4 * g, W);
     lds_barrier();
     // S' = Gamma_end S + X^T W
     const float gend = s_fac[4][0];
 #pragma unroll
-    for (int a = 0; a < RPW; ++a)
+    for (int a = 0; a < NTW; ++a) {
+      S[a] *= gend;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        S[a][ct] *= gend;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma3a(S[a][ct], ft(Xp, PX, LX, 16 * (w + 4 * a), 32 * kb, g, n), fk(Bp, PW, LC, 16 * ct + n, 32 * kb, g), xex);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        mma3a(S[a], ft(Xp, PX, LX, 16 * tile_rt(a), 32 * kb, g, n), fk(Bp, PW, LC, 16 * tile_ct(a) + n, 32 * kb, g), xex);
+    }
   }
 }
 
@@ -2174,7 +2161,7 @@ hipError_t launch_rule(const BwdParams& p, float* ws, hipStream_t st) {
   const unsigned ngrid = (unsigned)(8 * (DV / NCOL) * ((p.BH + 7) / 8));
   hipLaunchKernelGGL((bwd_prep_kernel<InT, DK, RULE>), dim3((unsigned)nrec), dim3(256), 0, st, p, recs);
   if constexpr (sizeof(InT) == 2) {
-    hipLaunchKernelGGL((bwd_state_bf_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
+    hipLaunchKernelGGL((bwd_state_bf_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, Sch, Rh);
     hipLaunchKernelGGL((bwd_dstate_bf_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(512), 0, st, p, recs, dSch, dRw);
   } else {
     hipLaunchKernelGGL((bwd_state_kernel<InT, DK, DV, RULE>), dim3(ngrid), dim3(256), 0, st, p, recs, Sch, Rh);
