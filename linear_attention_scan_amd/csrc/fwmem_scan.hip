@@ -45,7 +45,7 @@ template <typename InT>
 using PolOf = typename In<InT>::Pol;
 
 // ---------------------------------------------------------------- workspace record
-template <typename InT, int DK>
+template <typename InT, int DK, bool PC = false>
 struct Rec {
   using op_t = typename PolOf<InT>::op_t;
   // T and M rows in the policy's LDS operand order (copied verbatim into LDS)
@@ -57,7 +57,18 @@ struct Rec {
   static constexpr size_t kX0 = kFac + 16 * CH;                     // float [DK] key before token 0
   // 1/sT, 1/sM, has_prev, Gamma_C (scalar decay), sX, sQ
   static constexpr size_t kSc = kX0 + 4 * DK;                       // float [8]
-  static constexpr size_t kBytes = (kSc + 32 + 255) / 256 * 256;
+  static constexpr size_t kBase = (kSc + 32 + 255) / 256 * 256;
+  // Per-channel decay with fp16 operands (bf16 inputs): the chunk's operands with the
+  // decay folded in, formed once by prep (fp16 [CH][DK], natural channel order, scaled by
+  // sX or sQ like the rows they come from), then the per-channel Gamma_C:
+  //   X~ = X o Gamma_prev (rows of X S),  X^ = X o Gamma_C / Gamma (the update's X^T),
+  //   Q~ = Q o Gamma (the read).
+  static constexpr bool kOps = PC && PolOf<InT>::kScaled;
+  static constexpr size_t kPX = kBase;
+  static constexpr size_t kPU = kPX + 2 * CH * DK;
+  static constexpr size_t kPQ = kPU + 2 * CH * DK;
+  static constexpr size_t kPG = kPQ + 2 * CH * DK;  // float [DK]
+  static constexpr size_t kBytes = kOps ? (kPG + 4 * DK + 255) / 256 * 256 : kBase;
 };
 
 // Thread layout of a [CH][DK] row staging: 16-byte loads of VW elements.
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   using frag_t = typename Pol::frag_t;
   constexpr int NREG = R::solve ? 4 : 3;
   using L = PrepLds<InT, DK, NREG>;
-  using RC = Rec<InT, DK>;
+  using RC = Rec<InT, DK, PC>;
   using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDF = L::LDF;
   constexpr int VW = Rw::VW, TPR = Rw::TPR, RPP = Rw::RPP, NPASS = Rw::NPASS;
@@ -147,6 +158,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   const float* x0 = (R::shift && has_in) ? p.xprev_in + (size_t)bh * DK : nullptr;
   const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
   const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
+  char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
 
   // Token gates for wave 0 (lane = token), loaded first so their latency overlaps
   // the row loads.
@@ -351,8 +363,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       x_par[tid] = pr;
     }
     __syncthreads();
-    float off = 0.f, anc;
-    uint32_t poff = 0, apr;
+    float off = 0.f, anc, gtot = 0.f;
+    uint32_t poff = 0, apr, ptot = 0;
     {
       constexpr int partA = TA / SEGP;
       float aoff = 0.f;
@@ -369,9 +381,35 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
           aoff += gw;
           apoff ^= pw;
         }
+        gtot += gw;
+        ptot ^= pw;
       }
       anc = aoff + x_anc[i];
       apr = apoff ^ x_apr[i];
+    }
+    if constexpr (RC::kOps) {
+      // The propagate step's operands, from the decay since the chunk start: Gamma_t =
+      // exp(off + in-segment prefix) with its sign, Gamma_prev the one before (1 before
+      // the first token), Gamma_C the chunk's total. Formed from the staged rows (already
+      // scaled by sX, sQ), in the same order of operations the propagate kernel would use.
+      _Float16* px = reinterpret_cast<_Float16*>(rec + RC::kPX);
+      _Float16* pu = reinterpret_cast<_Float16*>(rec + RC::kPU);
+      _Float16* pq = reinterpret_cast<_Float16*>(rec + RC::kPQ);
+      float fprev = (poff ? -1.f : 1.f) * __expf(off);
+#pragma unroll
+      for (int u = 0; u < SEGP; ++u) {
+        const int t = tb + u;
+        const float g = off + ev[u];
+        const uint32_t pcur = poff ^ ((pl >> u) & 1u);
+        const float fcur = (pcur ? -1.f : 1.f) * __expf(g);
+        const float fend = ((ptot ^ pcur) ? -1.f : 1.f) * __expf(gtot - g);
+        const float xh = (float)Xs[t * LDX + ip];
+        px[t * DK + i] = Pol::cvt(xh * fprev);
+        pu[t * DK + i] = Pol::cvt(xh * fend);
+        pq[t * DK + i] = Pol::cvt((float)Qs[t * LDX + ip] * fcur);
+        fprev = fcur;
+      }
+      if (part == 0) reinterpret_cast<float*>(rec + RC::kPG)[i] = (ptot ? -1.f : 1.f) * __expf(gtot);
     }
     // e_t and its sign (bit u of esg), then the block maxima (for the fp16 scales)
     uint32_t esg = 0;
@@ -533,7 +571,6 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   }
 
   // Write T (delta rule) and M, scaled and in operand order, plus the token factors.
-  char* rec = p.ws + ((size_t)bh * p.nchunks + c) * RC::kBytes;
   {
     const int t = tid >> 2, c0 = (tid & 3) * 16;
     float tv[16], mv[16];
@@ -657,7 +694,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
   using L = PropLds<InT, DK, R::solve, PC>;
-  using RC = Rec<InT, DK>;
+  using RC = Rec<InT, DK, PC>;
   using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDT = L::LDT, LDC = L::LDC, LDV = L::LDV;
   constexpr int KB = Pol::KB;
@@ -739,9 +776,14 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   // channel. Their raw lambdas for chunk c are loaded during chunk c-1 (software
   // pipelined: consumed at the top of the column pass, then reloaded for the next chunk).
   constexpr int TPC = NT / DK, SEG = CH / TPC;
-  float plam[PC ? SEG : 1];
+  // With fp16 operands the prep kernel has folded the per-channel decay into the chunk's
+  // operands (X~, X^, Q~ and Gamma_C in the record): staging copies them, no lambda is read.
+  constexpr bool OPS = RC::kOps;
+  float plam[(PC && !OPS) ? SEG : 1];
+  u32x4 pxu[OPS ? NPX : 1];
+  float pgc = 1.f;
   auto load_lam = [&](int tbase) {
-    if constexpr (PC) {
+    if constexpr (PC && !OPS) {
       const int i = tid % DK, tb = (tid / DK) * SEG;
 #pragma unroll
       for (int u = 0; u < SEG; ++u) {
@@ -766,23 +808,32 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
           const int task = tid + NT * r;
           const int cg = (task & 3) + 4 * (task >> 7), tp = (task >> 2) & 31;
           frag_t xo[2];
+          if constexpr (OPS) {
+            // X~ rows into Xs; the update's operand X^ into the transposed copy
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int t = 2 * tp + h;
-            float x[VW];
-            In<InT>::decode(px[2 * r + h], x);
-            if (R::shift && t0 + t == 0) {
-#pragma unroll
-              for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[8 * cg + j] : 0.f;
-            } else if (ELU && (valid >> (2 * r + h) & 1u)) {
-#pragma unroll
-              for (int j = 0; j < VW; ++j) x[j] = phi_elu1(x[j]);
+            for (int h = 0; h < 2; ++h) {
+              Pol::store_run(Xs + (2 * tp + h) * LDX, 8 * cg, __builtin_bit_cast(frag_t, px[2 * r + h]));
+              xo[h] = __builtin_bit_cast(frag_t, pxu[2 * r + h]);
             }
+          } else {
 #pragma unroll
-            for (int j = 0; j < VW; ++j) xo[h][j] = Pol::cvt(x[j] * psX);
-            Pol::store_run(Xs + t * LDX, 8 * cg, xo[h]);
+            for (int h = 0; h < 2; ++h) {
+              const int t = 2 * tp + h;
+              float x[VW];
+              In<InT>::decode(px[2 * r + h], x);
+              if (R::shift && t0 + t == 0) {
+#pragma unroll
+                for (int j = 0; j < VW; ++j) x[j] = x0 != nullptr ? x0[8 * cg + j] : 0.f;
+              } else if (ELU && (valid >> (2 * r + h) & 1u)) {
+#pragma unroll
+                for (int j = 0; j < VW; ++j) x[j] = phi_elu1(x[j]);
+              }
+#pragma unroll
+              for (int j = 0; j < VW; ++j) xo[h][j] = Pol::cvt(x[j] * psX);
+              Pol::store_run(Xs + t * LDX, 8 * cg, xo[h]);
+            }
           }
-          if (!PC) {
+          if (!PC || OPS) {
             const int tp2 = Pol::kpos(2 * tp);  // tokens 2tp, 2tp+1 are adjacent
 #pragma unroll
             for (int j = 0; j < VW; ++j)
@@ -812,17 +863,22 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) {
         const int t = ps * RPP + tid / TPR;
-        float qv[VW];
-        In<InT>::decode(pq[ps], qv);
-        if (ELU && (valid >> (16 + ps) & 1u)) {
+        if constexpr (OPS) {
+          Pol::store_run(Qs + t * LDX, col, __builtin_bit_cast(frag_t, pq[ps]));
+        } else {
+          float qv[VW];
+          In<InT>::decode(pq[ps], qv);
+          if (ELU && (valid >> (16 + ps) & 1u)) {
 #pragma unroll
-          for (int j = 0; j < VW; ++j) qv[j] = phi_elu1(qv[j]);
+            for (int j = 0; j < VW; ++j) qv[j] = phi_elu1(qv[j]);
+          }
+          frag_t qo;
+#pragma unroll
+          for (int j = 0; j < VW; ++j) qo[j] = Pol::cvt(qv[j] * psQ);
+          Pol::store_run(Qs + t * LDX, col, qo);
         }
-        frag_t qo;
-#pragma unroll
-        for (int j = 0; j < VW; ++j) qo[j] = Pol::cvt(qv[j] * psQ);
-        Pol::store_run(Qs + t * LDX, col, qo);
       }
+      if (OPS && tid < DK) s_gC[tid] = pgc;
 #pragma unroll
       for (int ps = 0; ps < NPV; ++ps) {
         const int t = ps * RPPv + tid / TPRv;
@@ -856,7 +912,21 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
       const int tn = t0 + CH;
       const char* rec = rec0 + (size_t)(c + 1) * RC::kBytes;
       valid = 0;
-      if constexpr (Pol::kScaled) {
+      if constexpr (OPS) {
+        // the record holds every row of the chunk (zero past the sequence end)
+#pragma unroll
+        for (int r = 0; r < NXT; ++r) {
+          const int task = tid + NT * r;
+          const int cg = (task & 3) + 4 * (task >> 7), tp = (task >> 2) & 31;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t off = (uint32_t)((2 * tp + h) * DK + 8 * cg) * 2u;
+            px[2 * r + h] = ld16(rec + RC::kPX, off);
+            pxu[2 * r + h] = ld16(rec + RC::kPU, off);
+          }
+        }
+        if (tid < DK) pgc = reinterpret_cast<const float*>(rec + RC::kPG)[tid];
+      } else if constexpr (Pol::kScaled) {
 #pragma unroll
         for (int r = 0; r < NXT; ++r) {
           const int task = tid + NT * r;
@@ -887,10 +957,14 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) {
         const int tau = tn + ps * RPP + tid / TPR;
-        pq[ps] = u32x4{0u, 0u, 0u, 0u};
-        if (tau < p.T) {
-          pq[ps] = ld16(qbase, (uint32_t)(tau * DK + col) * (uint32_t)sizeof(InT));
-          valid |= 1u << (16 + ps);
+        if constexpr (OPS) {
+          pq[ps] = ld16(rec + RC::kPQ, (uint32_t)((ps * RPP + tid / TPR) * DK + col) * 2u);
+        } else {
+          pq[ps] = u32x4{0u, 0u, 0u, 0u};
+          if (tau < p.T) {
+            pq[ps] = ld16(qbase, (uint32_t)(tau * DK + col) * (uint32_t)sizeof(InT));
+            valid |= 1u << (16 + ps);
+          }
         }
       }
 #pragma unroll
@@ -921,7 +995,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
     }
     if (c < 0) continue;
 
-    if (PC) {
+    if (PC && !OPS) {
       // per-channel decay folded into the operands: X*Gamma_prev, Q*Gamma, X*Gamma_C/Gamma.
       // Each channel's 64 tokens are split over TPC threads; the segments' log-sums and
       // sign parities are combined through LDS into each segment's offset and the chunk
@@ -1160,6 +1234,8 @@ bool scan_split_path(int bf16, uint32_t flags) {
 
 size_t scan_record_bytes(int bf16, int dk, uint32_t flags) {
   if (scan_split_path(bf16, flags)) return dk == 64 ? RecSplit<64>::kBytes : RecSplit<128>::kBytes;
+  if (bf16 && (flags & kFlagPerChannel))
+    return dk == 64 ? Rec<uint16_t, 64, true>::kBytes : Rec<uint16_t, 128, true>::kBytes;
   if (bf16) return dk == 64 ? Rec<uint16_t, 64>::kBytes : Rec<uint16_t, 128>::kBytes;
   return dk == 64 ? Rec<float, 64>::kBytes : Rec<float, 128>::kBytes;
 }
