@@ -255,6 +255,162 @@ struct Rows {
   __device__ __forceinline__ void commit_split(uint16_t* dst, bool elu, float len, int patch, const float* pv) const;
 };
 
+// ---- bf16 split operands of the gradient pass. A matrix formed in fp32 is held in LDS as
+// two bf16 planes of one row-major layout, hi = bf16(x) and lo = bf16(x - hi): 16
+// significant bits over fp32's exponent range. A product with both operands split is
+// Ah Bh + Ah Bl + Al Bh on v_mfma_f32_16x16x32_bf16 with fp32 accumulation (Al Bl lies
+// below the fp32 rounding of the result); an exact bf16 operand (raw bf16 keys and queries
+// with the identity map and no QK rescaling) has a zero lo plane and takes two products.
+// Plane rows are padded by 8 elements, so the row stride is an odd multiple of 16 bytes
+// modulo 256 and the 16 rows of a fragment read fall in distinct bank groups.
+//
+// Fragments follow the K-slot order of frag_pair / xt_frag: slots 0..3 carry K = 4g..4g+3
+// and slots 4..7 K = 16+4g..16+4g+3 of a 32-wide K block (g = lane / 16), for A and B alike.
+__device__ __forceinline__ uint16_t bf_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ __forceinline__ void put_split(uint16_t* hi, int plane, int idx, float x) {
+  const uint16_t h = bf_bits(x);
+  hi[idx] = h;
+  hi[plane + idx] = bf_bits(x - bf16_bits_to_f32(h));
+}
+
+// four consecutive elements (idx a multiple of 4): one 8-byte store per plane
+__device__ __forceinline__ void put_split4(uint16_t* hi, int plane, int idx, const f4& x) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = bf_bits(x[i]);
+    l[i] = bf_bits(x[i] - bf16_bits_to_f32(h[i]));
+  }
+  *reinterpret_cast<uint2*>(hi + idx) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  *reinterpret_cast<uint2*>(hi + plane + idx) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// the fp32 value hi + lo of element idx
+__device__ __forceinline__ float get_split(const uint16_t* hi, int plane, int idx) {
+  return bf16_bits_to_f32(hi[idx]) + bf16_bits_to_f32(hi[plane + idx]);
+}
+
+struct SFrag {
+  bf8 h, l;
+};
+
+// Operand row r (A row, or B column) of the K block at k0, from planes stored with K
+// contiguous (element [r][k] at r * ld + k).
+__device__ __forceinline__ SFrag fk(const uint16_t* hi, int plane, int ld, int r, int k0, int g) {
+  return SFrag{frag_pair(hi + r * ld + k0 + 4 * g), frag_pair(hi + plane + r * ld + k0 + 4 * g)};
+}
+// Operand rows r0..r0+15 of the K block at k0, from planes stored K-major (element [k][r]
+// at k * ld + r), by the LDS transpose read.
+__device__ __forceinline__ SFrag ft(const uint16_t* hi, int plane, int ld, int r0, int k0, int g, int n) {
+  const int o = (k0 + 4 * g + (n >> 2)) * ld + r0 + 4 * (n & 3);
+  return SFrag{xt_frag(hi + o, ld), xt_frag(hi + plane + o, ld)};
+}
+
+// acc += A B with both operands split
+__device__ __forceinline__ void mma3(f4& acc, const SFrag& a, const SFrag& b) {
+  mma_bf16(acc, a.l, b.h);
+  mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+// acc += A B where B's lo plane is zero when bex (an exact bf16 operand)
+__device__ __forceinline__ void mma3x(f4& acc, const SFrag& a, const SFrag& b, bool bex) {
+  mma_bf16(acc, a.l, b.h);
+  if (!bex) mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+
+template <typename InT, int DK, int NTH>
+__device__ __forceinline__ void Rows<InT, DK, NTH>::commit_split(uint16_t* dst, bool elu, float len, int patch,
+                                                                 const float* pv) const {
+  constexpr int LX = DK + 8, PX = CB * LX;
+  // raw bf16 rows with the identity map and no rescaling are their own hi plane
+  const bool exact = sizeof(InT) == 2 && !elu && !(len > 0.f);
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW;
+    if (exact && t != patch) {
+      static_assert(VW == 8 || sizeof(InT) != 2, "one 16-byte group of bf16");
+      *reinterpret_cast<u32x4*>(dst + t * LX + i0) = w[j];
+      *reinterpret_cast<u32x4*>(dst + PX + t * LX + i0) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
+    float x[VW];
+    In<InT>::decode(w[j], x);
+    if (t == patch) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] = pv != nullptr ? pv[i0 + e] : 0.f;
+    } else if (elu && ((valid >> j) & 1u)) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+    }
+    if (len > 0.f) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
+      ss = group_sum<GPR>(ss);
+      const float f = rescale_factor(ss, len);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] *= f;
+    }
+#pragma unroll
+    for (int e = 0; e < VW; e += 4) put_split4(dst, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
+  }
+}
+
+// acc += A B with B split and A exact when aex (its lo plane zero)
+__device__ __forceinline__ void mma3a(f4& acc, const SFrag& a, const SFrag& b, bool aex) {
+  if (!aex) mma_bf16(acc, a.l, b.h);
+  mma_bf16(acc, a.h, b.l);
+  mma_bf16(acc, a.h, b.h);
+}
+
+// Written keys x_t (Q == false) or read queries phi(q_t) (Q == true) of chunk c as split
+// planes [CB][DK + 8]: the shift to the previous token's key (and the carried key before a
+// call's first token), phi and QK normalisation applied; rows of tokens past T are zero.
+// A row's 16-byte groups sit in GPR consecutive lanes, so its norm is a lane-group sum.
+template <typename InT, int DK, bool SHIFT, bool Q, int NTH>
+__device__ void stage_split(const BwdParams& p, int bh, int c, uint16_t* hi, bool has_in) {
+  constexpr int LX = DK + 8, PX = CB * LX, VW = 16 / (int)sizeof(InT), GPR = DK / VW;
+  static_assert(CB * GPR % NTH == 0 && 64 % GPR == 0, "row groups");
+  const bool elu = (p.flags & kFlagPhiElu1) != 0;
+  const float len = qk_length(p.flags, DK);
+  const size_t rb = (size_t)bh * p.T;
+  const InT* src = static_cast<const InT*>(Q ? p.q : p.k) + rb * DK;
+#pragma unroll
+  for (int j = 0; j < CB * GPR / NTH; ++j) {
+    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW, tau = c * CB + t;
+    float x[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) x[e] = 0.f;
+    if (tau < p.T) {
+      if (!Q && SHIFT && tau == 0) {
+        if (has_in && p.xprev_in != nullptr) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) x[e] = p.xprev_in[(size_t)bh * DK + i0 + e];  // phi applied
+        }
+      } else {
+        In<InT>::load(src + (size_t)(!Q && SHIFT ? tau - 1 : tau) * DK + i0, x);
+        if (elu) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
+        }
+      }
+    }
+    if (len > 0.f) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
+      ss = group_sum<GPR>(ss);
+      const float f = rescale_factor(ss, len);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] *= f;
+    }
+#pragma unroll
+    for (int e = 0; e < VW; e += 4) put_split4(hi, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
+  }
+}
+
 __device__ __forceinline__ bool head_has_key(const BwdParams& p, int bh) {
   return p.has_in != nullptr && p.has_in[bh] != 0;
 }
@@ -428,12 +584,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, float* recs)
     }
   }
 
-  // the record: T and Lp (delta rule), M
+  // the record: T and Lp (delta rule), M. With bf16 inputs T and M are stored as bf16 hi
+  // and lo planes ([CB][CB] each, in the float region's bytes), the operands of the split
+  // kernels, so that each column-group workgroup copies them instead of splitting them.
   for (int e = tid; e < CB * CB / 4; e += 256) {
     const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
-    *reinterpret_cast<f4*>(rec + BRec::kM + r * CB + c4) = *reinterpret_cast<const f4*>(Ms + r * LDC + c4);
+    const f4 mv = *reinterpret_cast<const f4*>(Ms + r * LDC + c4);
+    if constexpr (sizeof(InT) == 2) put_split4(reinterpret_cast<uint16_t*>(rec + BRec::kM), CB * CB, r * CB + c4, mv);
+    else *reinterpret_cast<f4*>(rec + BRec::kM + r * CB + c4) = mv;
     if constexpr (R::solve) {
-      *reinterpret_cast<f4*>(rec + BRec::kT + r * CB + c4) = *reinterpret_cast<const f4*>(Ts + r * LDC + c4);
+      const f4 tv = *reinterpret_cast<const f4*>(Ts + r * LDC + c4);
+      if constexpr (sizeof(InT) == 2) put_split4(reinterpret_cast<uint16_t*>(rec + BRec::kT), CB * CB, r * CB + c4, tv);
+      else *reinterpret_cast<f4*>(rec + BRec::kT + r * CB + c4) = tv;
       *reinterpret_cast<f4*>(rec + BRec::kLp + r * CB + c4) = *reinterpret_cast<const f4*>(Lps + r * LDC + c4);
     }
   }
@@ -1214,154 +1376,6 @@ __global__ __launch_bounds__(512) void bwd_grad_f32_kernel(BwdParams p, const fl
   }
 }
 
-// ---- bf16 split operands of the gradient pass. A matrix formed in fp32 is held in LDS as
-// two bf16 planes of one row-major layout, hi = bf16(x) and lo = bf16(x - hi): 16
-// significant bits over fp32's exponent range. A product with both operands split is
-// Ah Bh + Ah Bl + Al Bh on v_mfma_f32_16x16x32_bf16 with fp32 accumulation (Al Bl lies
-// below the fp32 rounding of the result); an exact bf16 operand (raw bf16 keys and queries
-// with the identity map and no QK rescaling) has a zero lo plane and takes two products.
-// Plane rows are padded by 8 elements, so the row stride is an odd multiple of 16 bytes
-// modulo 256 and the 16 rows of a fragment read fall in distinct bank groups.
-//
-// Fragments follow the K-slot order of frag_pair / xt_frag: slots 0..3 carry K = 4g..4g+3
-// and slots 4..7 K = 16+4g..16+4g+3 of a 32-wide K block (g = lane / 16), for A and B alike.
-__device__ __forceinline__ uint16_t bf_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-__device__ __forceinline__ void put_split(uint16_t* hi, int plane, int idx, float x) {
-  const uint16_t h = bf_bits(x);
-  hi[idx] = h;
-  hi[plane + idx] = bf_bits(x - bf16_bits_to_f32(h));
-}
-
-// four consecutive elements (idx a multiple of 4): one 8-byte store per plane
-__device__ __forceinline__ void put_split4(uint16_t* hi, int plane, int idx, const f4& x) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = bf_bits(x[i]);
-    l[i] = bf_bits(x[i] - bf16_bits_to_f32(h[i]));
-  }
-  *reinterpret_cast<uint2*>(hi + idx) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  *reinterpret_cast<uint2*>(hi + plane + idx) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-}
-
-// the fp32 value hi + lo of element idx
-__device__ __forceinline__ float get_split(const uint16_t* hi, int plane, int idx) {
-  return bf16_bits_to_f32(hi[idx]) + bf16_bits_to_f32(hi[plane + idx]);
-}
-
-struct SFrag {
-  bf8 h, l;
-};
-
-// Operand row r (A row, or B column) of the K block at k0, from planes stored with K
-// contiguous (element [r][k] at r * ld + k).
-__device__ __forceinline__ SFrag fk(const uint16_t* hi, int plane, int ld, int r, int k0, int g) {
-  return SFrag{frag_pair(hi + r * ld + k0 + 4 * g), frag_pair(hi + plane + r * ld + k0 + 4 * g)};
-}
-// Operand rows r0..r0+15 of the K block at k0, from planes stored K-major (element [k][r]
-// at k * ld + r), by the LDS transpose read.
-__device__ __forceinline__ SFrag ft(const uint16_t* hi, int plane, int ld, int r0, int k0, int g, int n) {
-  const int o = (k0 + 4 * g + (n >> 2)) * ld + r0 + 4 * (n & 3);
-  return SFrag{xt_frag(hi + o, ld), xt_frag(hi + plane + o, ld)};
-}
-
-// acc += A B with both operands split
-__device__ __forceinline__ void mma3(f4& acc, const SFrag& a, const SFrag& b) {
-  mma_bf16(acc, a.l, b.h);
-  mma_bf16(acc, a.h, b.l);
-  mma_bf16(acc, a.h, b.h);
-}
-// acc += A B where B's lo plane is zero when bex (an exact bf16 operand)
-__device__ __forceinline__ void mma3x(f4& acc, const SFrag& a, const SFrag& b, bool bex) {
-  mma_bf16(acc, a.l, b.h);
-  if (!bex) mma_bf16(acc, a.h, b.l);
-  mma_bf16(acc, a.h, b.h);
-}
-
-template <typename InT, int DK, int NTH>
-__device__ __forceinline__ void Rows<InT, DK, NTH>::commit_split(uint16_t* dst, bool elu, float len, int patch,
-                                                                 const float* pv) const {
-  constexpr int LX = DK + 8, PX = CB * LX;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW;
-    float x[VW];
-    In<InT>::decode(w[j], x);
-    if (t == patch) {
-#pragma unroll
-      for (int e = 0; e < VW; ++e) x[e] = pv != nullptr ? pv[i0 + e] : 0.f;
-    } else if (elu && ((valid >> j) & 1u)) {
-#pragma unroll
-      for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
-    }
-    if (len > 0.f) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
-      ss = group_sum<GPR>(ss);
-      const float f = rescale_factor(ss, len);
-#pragma unroll
-      for (int e = 0; e < VW; ++e) x[e] *= f;
-    }
-#pragma unroll
-    for (int e = 0; e < VW; e += 4) put_split4(dst, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
-  }
-}
-
-// acc += A B with B split and A exact when aex (its lo plane zero)
-__device__ __forceinline__ void mma3a(f4& acc, const SFrag& a, const SFrag& b, bool aex) {
-  if (!aex) mma_bf16(acc, a.l, b.h);
-  mma_bf16(acc, a.h, b.l);
-  mma_bf16(acc, a.h, b.h);
-}
-
-// Written keys x_t (Q == false) or read queries phi(q_t) (Q == true) of chunk c as split
-// planes [CB][DK + 8]: the shift to the previous token's key (and the carried key before a
-// call's first token), phi and QK normalisation applied; rows of tokens past T are zero.
-// A row's 16-byte groups sit in GPR consecutive lanes, so its norm is a lane-group sum.
-template <typename InT, int DK, bool SHIFT, bool Q, int NTH>
-__device__ void stage_split(const BwdParams& p, int bh, int c, uint16_t* hi, bool has_in) {
-  constexpr int LX = DK + 8, PX = CB * LX, VW = 16 / (int)sizeof(InT), GPR = DK / VW;
-  static_assert(CB * GPR % NTH == 0 && 64 % GPR == 0, "row groups");
-  const bool elu = (p.flags & kFlagPhiElu1) != 0;
-  const float len = qk_length(p.flags, DK);
-  const size_t rb = (size_t)bh * p.T;
-  const InT* src = static_cast<const InT*>(Q ? p.q : p.k) + rb * DK;
-#pragma unroll
-  for (int j = 0; j < CB * GPR / NTH; ++j) {
-    const int idx = threadIdx.x + NTH * j, t = idx / GPR, i0 = (idx % GPR) * VW, tau = c * CB + t;
-    float x[VW];
-#pragma unroll
-    for (int e = 0; e < VW; ++e) x[e] = 0.f;
-    if (tau < p.T) {
-      if (!Q && SHIFT && tau == 0) {
-        if (has_in && p.xprev_in != nullptr) {
-#pragma unroll
-          for (int e = 0; e < VW; ++e) x[e] = p.xprev_in[(size_t)bh * DK + i0 + e];  // phi applied
-        }
-      } else {
-        In<InT>::load(src + (size_t)(!Q && SHIFT ? tau - 1 : tau) * DK + i0, x);
-        if (elu) {
-#pragma unroll
-          for (int e = 0; e < VW; ++e) x[e] = phi_elu1(x[e]);
-        }
-      }
-    }
-    if (len > 0.f) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < VW; ++e) ss += x[e] * x[e];
-      ss = group_sum<GPR>(ss);
-      const float f = rescale_factor(ss, len);
-#pragma unroll
-      for (int e = 0; e < VW; ++e) x[e] *= f;
-    }
-#pragma unroll
-    for (int e = 0; e < VW; e += 4) put_split4(hi, PX, t * LX + i0 + e, f4{x[e], x[e + 1], x[e + 2], x[e + 3]});
-  }
-}
-
 // Gradient pass on bf16 MFMA with split operands (bf16 inputs).
 template <typename InT, int DK, int DV, int RULE>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float* recs, const float* Sch,
@@ -1417,11 +1431,24 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdParams p, const float*
   const float* drc = dRw + ((size_t)bh * nch + c) * CB * DV;
   const InT* vb = static_cast<const InT*>(p.v) + rb * DV;
 
-  for (int e = tid; e < CB * CB / 4; e += 512) {
-    const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
-    const f4 mv = *reinterpret_cast<const f4*>(rec + BRec::kM + r * CB + c4);
-    *reinterpret_cast<f4*>(Ms + r * LDC + c4) = mv;
-    put_split4(Tp, PC, r * LC + c4, SOLVE ? *reinterpret_cast<const f4*>(rec + BRec::kT + r * CB + c4) : mv);
+  {
+    // T (delta rule) or M planes from the record; M also as fp32 hi + lo
+    const uint16_t* mpl = reinterpret_cast<const uint16_t*>(rec + BRec::kM);
+    const uint16_t* tpl = reinterpret_cast<const uint16_t*>(rec + (SOLVE ? BRec::kT : BRec::kM));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // plane j: CB rows of CB / 8 16-byte groups, one group a thread
+      const int r = tid / (CB / 8), c8 = (tid % (CB / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Tp + j * PC + r * LC + c8) =
+          *reinterpret_cast<const u32x4*>(tpl + j * CB * CB + r * CB + c8);
+    }
+    for (int e = tid; e < CB * CB / 4; e += 512) {
+      const int r = e / (CB / 4), c4 = (e % (CB / 4)) * 4;
+      const uint2 h = *reinterpret_cast<const uint2*>(mpl + r * CB + c4);
+      const uint2 l = *reinterpret_cast<const uint2*>(mpl + CB * CB + r * CB + c4);
+      *reinterpret_cast<f4*>(Ms + r * LDC + c4) =
+          f4{bf16_bits_to_f32(h.x & 0xffffu) + bf16_bits_to_f32(l.x & 0xffffu), bf16_bits_to_f32(h.x >> 16) + bf16_bits_to_f32(l.x >> 16),
+             bf16_bits_to_f32(h.y & 0xffffu) + bf16_bits_to_f32(l.y & 0xffffu), bf16_bits_to_f32(h.y >> 16) + bf16_bits_to_f32(l.y >> 16)};
+    }
   }
   for (int e = tid; e < kNSc * CB; e += 512) (&s_sc[0][0])[e] = rec[BRec::kSc + e];
   for (int e = tid; e < kNP * CB; e += 512) (&s_p[0][0])[e] = 0.f;
@@ -1866,7 +1893,7 @@ __global__ __launch_bounds__(512) void bwd_state_bf_kernel(BwdParams p, const fl
 
   // registers of the next chunk: rows, T (8 floats a thread), values, scalars
   Rows<InT, DK, 512> rows;
-  f4 pt[2];
+  u32x4 pt[2];  // T planes: one 16-byte group of each
   u32x4 pv;
   float pf[5];
   auto load = [&](int c) {
@@ -1875,7 +1902,8 @@ __global__ __launch_bounds__(512) void bwd_state_bf_kernel(BwdParams p, const fl
     const float* rec = recs + ((size_t)bh * nch + c) * BRec::kFloats;
     if constexpr (R::solve) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 8 * tid + 4 * j);
+      for (int j = 0; j < 2; ++j)
+        pt[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(rec + BRec::kT) + j * CB * CB + 8 * tid);
     }
     {
       const int t = tid / (NCOL / VWv), v0 = (tid % (NCOL / VWv)) * VWv, tau = c * CB + t;
@@ -1898,7 +1926,7 @@ __global__ __launch_bounds__(512) void bwd_state_bf_kernel(BwdParams p, const fl
     rows.commit_split(Xp, elu, len, (R::shift && c == 0) ? 0 : -1, x0);
     if constexpr (R::solve) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) put_split4(Tp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pt[j]);
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(Tp + j * PT + (tid >> 3) * LC + 8 * (tid & 7)) = pt[j];
     }
     if (tid < NVG) {
       const int t = tid / (NCOL / VWv), v0 = (tid % (NCOL / VWv)) * VWv;
@@ -1987,13 +2015,14 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
   using R = Rule<RULE>;
   constexpr int NRT = DK / 16;
   constexpr int NTW = NRT / 4;  // dS tiles of a wave (DK 128: row tile w, both column tiles; DK 64: one)
-  constexpr int LX = DK + 8, LC = CB + 8, PX = CB * LX, PT = CB * LC, PB = NCOL * LX, PW = NCOL * LC;
+  constexpr int LX = DK + 8, LC = CB + 8, LB = NCOL + 8;
+  constexpr int PX = CB * LX, PT = CB * LC, PB = NCOL * LX, PW = NCOL * LC, PO = CB * LB;
   __shared__ __align__(16) uint16_t Xp[2 * PX];
   __shared__ __align__(16) uint16_t Qp[2 * PX];
   __shared__ __align__(16) uint16_t Tp[R::solve ? 2 * PT : 8];
   __shared__ __align__(16) uint16_t Mp[R::solve ? 2 * PT : 8];
-  __shared__ __align__(16) uint16_t dOp[2 * PW];  // dO^T of the column group [NCOL][CB]
-  __shared__ __align__(16) uint16_t gOp[2 * PW];  // (Gamma o dO)^T
+  __shared__ __align__(16) uint16_t dOp[2 * PO];  // dO of the column group [CB][NCOL]
+  __shared__ __align__(16) uint16_t gOp[2 * PO];  // Gamma o dO
   __shared__ __align__(16) uint16_t Bp[2 * PB];   // dS^T [NCOL][DK], then (delta) -(eta Gamma_prev dR)^T [NCOL][CB]
   __shared__ __align__(16) uint16_t dUp[R::solve ? 2 * PW : 8];
   __shared__ float s_fac[4][CB];  // Gamma, eta Gamma_prev, Gamma_end / Gamma; [3][0] Gamma_end
@@ -2026,7 +2055,8 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
 
   // registers of the next chunk: X and Q rows, T and M (8 floats a thread each), dO (4), scalars
   Rows<InT, DK, 512> xrows, qrows;
-  f4 pt[2], pm[2], pd;
+  u32x4 pt[2], pm[2];  // T and M planes: one 16-byte group of each
+  f4 pd;
   float pf[4], pgam;
   auto load = [&](int c) {
     xrows.load(kb - (R::shift ? DK : 0), c * CB, R::shift ? 1 : 0, p.T);
@@ -2035,8 +2065,8 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
     if constexpr (R::solve) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        pt[j] = *reinterpret_cast<const f4*>(rec + BRec::kT + 8 * tid + 4 * j);
-        pm[j] = *reinterpret_cast<const f4*>(rec + BRec::kM + 8 * tid + 4 * j);
+        pt[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(rec + BRec::kT) + j * CB * CB + 8 * tid);
+        pm[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(rec + BRec::kM) + j * CB * CB + 8 * tid);
       }
     }
     {
@@ -2059,18 +2089,14 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
     if constexpr (R::solve) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        put_split4(Tp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pt[j]);
-        put_split4(Mp, PT, (tid >> 3) * LC + 8 * (tid & 7) + 4 * j, pm[j]);
+        *reinterpret_cast<u32x4*>(Tp + j * PT + (tid >> 3) * LC + 8 * (tid & 7)) = pt[j];
+        *reinterpret_cast<u32x4*>(Mp + j * PT + (tid >> 3) * LC + 8 * (tid & 7)) = pm[j];
       }
     }
     {
       const int t = tid / (NCOL / 4), v0 = (tid % (NCOL / 4)) * 4;
-      const float gam = pgam;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        put_split(dOp, PW, (v0 + i) * LC + t, pd[i]);
-        put_split(gOp, PW, (v0 + i) * LC + t, gam * pd[i]);
-      }
+      put_split4(dOp, PO, t * LB + v0, pd);
+      put_split4(gOp, PO, t * LB + v0, f4{pgam * pd[0], pgam * pd[1], pgam * pd[2], pgam * pd[3]});
     }
     if (tid < CB) {
       s_fac[0][tid] = pf[0];
@@ -2107,7 +2133,7 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
       for (int i = 0; i < 4; ++i) du[i] *= s_fac[2][16 * m + 4 * g + i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb >= (m >> 1)) mma3(du, ft(Mp, PT, LC, 16 * m, 32 * kb, g, n), fk(dOp, PW, LC, 16 * ctw + n, 32 * kb, g));
+        if (kb >= (m >> 1)) mma3(du, ft(Mp, PT, LC, 16 * m, 32 * kb, g, n), ft(dOp, PO, LB, 16 * ctw, 32 * kb, g, n));
       put_split4(dUp, PW, (16 * ctw + n) * LC + 16 * m + 4 * g, du);
       lds_barrier();  // dU complete; dS^T no longer read
       // dR = T^T dU
@@ -2133,7 +2159,7 @@ __global__ __launch_bounds__(512) void bwd_dstate_bf_kernel(BwdParams p, const f
       dS[a] *= gend;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        mma3a(dS[a], ft(Qp, PX, LX, 16 * rt, 32 * kb, g, n), fk(gOp, PW, LC, 16 * ct + n, 32 * kb, g), qex);
+        mma3a(dS[a], ft(Qp, PX, LX, 16 * rt, 32 * kb, g, n), ft(gOp, PO, LB, 16 * ct, 32 * kb, g, n), qex);
         if constexpr (R::solve)
           mma3a(dS[a], ft(Xp, PX, LX, 16 * rt, 32 * kb, g, n), fk(Bp, PW, LC, 16 * ct + n, 32 * kb, g), xex);
       }
