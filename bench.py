@@ -74,46 +74,46 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "bwd_prep_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
+            "fwmem_backward_chunk.hip": "43a1c156089b10bfe6ac36cfe3d57721a366030ccd20b0939aaf8266446dc921",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 66695.2, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66694.9, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_state_bf_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
+            "fwmem_backward_chunk.hip": "43a1c156089b10bfe6ac36cfe3d57721a366030ccd20b0939aaf8266446dc921",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 100197.7, "write_kib": 393216.1, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 100195.2, "write_kib": 393218.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_dstate_bf_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
+            "fwmem_backward_chunk.hip": "43a1c156089b10bfe6ac36cfe3d57721a366030ccd20b0939aaf8266446dc921",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 199002.8, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 199003.2, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_grad_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_backward_chunk.hip": "c3b88aa73489de4830563b738f2a886cf25be7436610a3d2cdeb766152fa426e",
+            "fwmem_backward_chunk.hip": "43a1c156089b10bfe6ac36cfe3d57721a366030ccd20b0939aaf8266446dc921",
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
             "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
         },
-        "fetch_kib": 629742.5, "write_kib": 395491.6, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 629742.8, "write_kib": 395446.7, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
