@@ -101,6 +101,35 @@ __device__ __forceinline__ float block_max(float v, float* s_red) {
   return m;
 }
 
+// Column block J of T = (I + L)^-1 (64 x 64, fp32, row stride LD) below the diagonal, given
+// its diagonal blocks D_b = T_bb in Tf: T_iJ = -D_i sum_{k=J}^{i-1} L_ik T_kJ for i = J+1..3, on
+// v_mfma_f32_16x16x4f32 (lane (g, n) supplies A[n][4g..4g+3] and B[4g..4g+3][n]; a C-layout
+// tile is a B operand as it stands).
+template <int J, int LD>
+__device__ __forceinline__ void t_column_block(const float* Lf, float* Tf, int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  f4 Tc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Tc[J][q] = Tf[(16 * J + 4 * g + q) * LD + 16 * J + n];
+#pragma unroll
+  for (int i = J + 1; i < 4; ++i) {
+    f4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = J; k < i; ++k) {
+      const f4 a = *reinterpret_cast<const f4*>(Lf + (16 * i + n) * LD + 16 * k + 4 * g);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], Tc[k][q], y, 0, 0, 0);
+    }
+    const f4 d = *reinterpret_cast<const f4*>(Tf + (16 * i + n) * LD + 16 * i + 4 * g);
+    f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t = __builtin_amdgcn_mfma_f32_16x16x4f32(d[q], y[q], t, 0, 0, 0);
+    Tc[i] = -t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Tf[(16 * i + 4 * g + q) * LD + 16 * J + n] = -t[q];
+  }
+}
+
 // ================================================================ prep kernel
 // NREG operand/matrix regions: four for the delta rule; three for the rules without a
 // solve (X, Q and M; the L and T region is never written), so that three workgroups share
@@ -319,7 +348,6 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
   float* Lf = reinterpret_cast<float*>(reg[2]);  // delta rule only
   float* Mf = reinterpret_cast<float*>(reg[3]);
   float* Tf = reinterpret_cast<float*>(reg[0]);   // after the Gram, X is dead
-  float* Ysc = reinterpret_cast<float*>(reg[1]);  // after the Gram, Q is dead
 
   if (PC) {
     // Column pass: Gamma ratios per channel, anchored at the chunk midpoint so the two
@@ -457,7 +485,6 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     Lf = reinterpret_cast<float*>(reg[3]);
     Mf = reinterpret_cast<float*>(reg[0]);
     Tf = reinterpret_cast<float*>(reg[2]);
-    Ysc = reinterpret_cast<float*>(reg[1]);
   }
 
   // Gram products on MFMA: 16 tiles of each 64x64 product (upper tiles are zero).
@@ -544,30 +571,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       }
     }
     __syncthreads();
-    const int r = tid >> 4, cc = tid & 15;
-#pragma unroll
-    for (int bi = 1; bi < NB; ++bi) {
-      // Y_bj = sum_{bk=bj}^{bi-1} L_{bi,bk} T_{bk,bj}
-      for (int bj = 0; bj < bi; ++bj) {
-        float y = 0.f;
-        for (int bk = bj; bk < bi; ++bk) {
-          const float* lrow = Lf + (16 * bi + r) * LDF + 16 * bk;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) y += lrow[m] * Tf[(16 * bk + m) * LDF + 16 * bj + cc];
-        }
-        Ysc[bj * 256 + r * 16 + cc] = y;
-      }
-      __syncthreads();
-      // T_{bi,bj} = -T_{bi,bi} Y_bj
-      for (int bj = 0; bj < bi; ++bj) {
-        float y = 0.f;
-        const float* trow = Tf + (16 * bi + r) * LDF + 16 * bi;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) y += trow[m] * Ysc[bj * 256 + m * 16 + cc];
-        Tf[(16 * bi + r) * LDF + 16 * bj + cc] = -y;
-      }
-      __syncthreads();
-    }
+    // Below the diagonal on fp32 MFMA: wave j forms column block j top-down,
+    //   T_ij = -D_i sum_{k=j}^{i-1} L_ik T_kj,
+    // keeping the column's blocks in registers (C layout, which is the B operand's layout),
+    // so no further synchronisation is needed.
+    static_assert(NB == 4, "four 16-row blocks");
+    if (wave == 0) t_column_block<0, LDF>(Lf, Tf, lane);
+    else if (wave == 1) t_column_block<1, LDF>(Lf, Tf, lane);
+    else if (wave == 2) t_column_block<2, LDF>(Lf, Tf, lane);
+    __syncthreads();
   }
 
   // Write T (delta rule) and M, scaled and in operand order, plus the token factors.
