@@ -673,9 +673,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
 
 // ================================================================ propagate kernel
 // T only for the delta rule; per-channel Gamma_C and the column pass's exchange only with
-// per-channel decay. Without either, a bf16 d_k = 128 workgroup takes 80,128 bytes, so two
-// share a CU.
-template <typename InT, int DK, bool SOLVE, bool PCX>
+// per-channel decay (PCX: 1 the per-channel Gamma_C, 2 also the column pass's exchange). With
+// bf16 inputs the value tile holds the raw bf16 values, and a d_k = 128 workgroup stays under
+// 80 KiB (two share a CU) except with the column pass.
+template <typename InT, int DK, bool SOLVE, int PCX>
 struct PropLds {
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
@@ -684,29 +685,31 @@ struct PropLds {
   // 4-byte token-pair writes of 8-channel groups in distinct banks.
   static constexpr int LDT = CH + 4;
   static constexpr int LDC = CH + Pol::kPad;  // [CH][CH] operands
-  static constexpr int LDV = 64 + 4;          // [CH][64] fp32 value tile
+  static constexpr int LDV = 64 + 16 / (int)sizeof(InT);  // [CH][64] value tile, input type
   static constexpr size_t kX = (size_t)CH * LDX * sizeof(op_t);
   static constexpr size_t kXU = Pol::kScaled ? (size_t)DK * LDT * sizeof(op_t) : kX;
   static constexpr size_t kC = (size_t)CH * LDC * sizeof(op_t);
-  static constexpr size_t kV = (size_t)CH * LDV * 4;
+  static constexpr size_t kV = (size_t)CH * LDV * sizeof(InT);
   static constexpr size_t oX = 0;
   static constexpr size_t oXU = oX + kX;
   static constexpr size_t oQ = oXU + kXU;
   static constexpr size_t oT = oQ + kX;
   static constexpr size_t oM = oT + (SOLVE ? kC : 0);
   static constexpr size_t oV = oM + kC;
-  static constexpr size_t oS = oV + kV;  // small: 5*CH (+ DK + 2*NT with PCX) floats
-  static constexpr size_t kBytes = oS + 4 * (5 * CH + (PCX ? DK + 2 * NT : 0));
+  static constexpr size_t oS = oV + kV;  // small: 5*CH (+ DK, + 2*NT) floats
+  static constexpr size_t kBytes = oS + 4 * (5 * CH + (PCX >= 1 ? DK : 0) + (PCX >= 2 ? 2 * NT : 0));
 };
 
+// With bf16 inputs two workgroups share a CU where the LDS allows it (two waves per SIMD, so
+// each hides the other's LDS and memory latency): the register budget is held to 256 a wave.
 template <typename InT, int DK, int RULE, bool PC, bool ELU>
-__global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
+__global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(ScanParams p) {
   using R = Rule<RULE>;
   using Pol = PolOf<InT>;
   using op_t = typename Pol::op_t;
   using frag_t = typename Pol::frag_t;
-  using L = PropLds<InT, DK, R::solve, PC>;
   using RC = Rec<InT, DK, PC>;
+  using L = PropLds<InT, DK, R::solve, PC ? (RC::kOps ? 1 : 2) : 0>;
   using Rw = Rows<InT, DK>;
   constexpr int LDX = L::LDX, LDT = L::LDT, LDC = L::LDC, LDV = L::LDV;
   constexpr int KB = Pol::KB;
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
   op_t* Qs = reinterpret_cast<op_t*>(smem + L::oQ);
   op_t* Ts = reinterpret_cast<op_t*>(smem + L::oT);
   op_t* Ms = reinterpret_cast<op_t*>(smem + L::oM);
-  float* Vs = reinterpret_cast<float*>(smem + L::oV);
+  InT* Vs = reinterpret_cast<InT*>(smem + L::oV);
   float* s_fac = reinterpret_cast<float*>(smem + L::oS);  // [4][CH]: fP, fV, fO, fU
   float* s_misc = s_fac + 4 * CH;  // [0] Gamma_C (scalar decay), [1] 1/sT, [2] 1/sM
   float* s_gC = s_misc + CH;       // [DK] per-channel Gamma_C
@@ -894,11 +897,8 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
       for (int ps = 0; ps < NPV; ++ps) {
         const int t = ps * RPPv + tid / TPRv;
-        float x[VW];
-        In<InT>::decode(pv[ps], x);
-#pragma unroll
-        for (int j = 0; j < VW; j += 4)
-          *reinterpret_cast<f4*>(Vs + t * LDV + vcol + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+        // the raw input values (16 bytes a thread)
+        *reinterpret_cast<u32x4*>(Vs + t * LDV + vcol) = pv[ps];
       }
       const int rr = e0 / CH, cc2 = e0 % CH;
 #pragma unroll
@@ -1097,7 +1097,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * mt + 4 * g + ii;
-            const float r = fac4(s_fV, mt)[ii] * Vs[t * LDV + wave * 16 + n] -
+            const float r = fac4(s_fV, mt)[ii] * In<InT>::load1(Vs + t * LDV + wave * 16 + n) -
                             fac4(s_fP, mt)[ii] * isS * P[mt][ii];
             P[mt][ii] = r;
             mr = fmaxf(mr, fabsf(r));
@@ -1123,7 +1123,7 @@ __global__ __launch_bounds__(NT) void prop_kernel(ScanParams p) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * mt + 4 * g + ii;
-            U[mt][ii] = fac4(s_fV, mt)[ii] * Vs[t * LDV + wave * 16 + n];
+            U[mt][ii] = fac4(s_fV, mt)[ii] * In<InT>::load1(Vs + t * LDV + wave * 16 + n);
           }
       }
 

@@ -538,11 +538,13 @@ int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint3
   const bool fused = scan_add_path(bf16, rule, flags);
   const size_t groups = fused ? 1 : split ? (size_t)dv / kSplitCols : ((size_t)dv + 63) / 64;
   const size_t wgs = BH * groups;
-  // propagate workgroups resident at once: one per CU; two for the general pair's rules
-  // without a solve or per-channel decay (the diagonal ones), whose LDS fits twice
-  const size_t cap = (!fused && !split && seg_diagonal(rule, flags)) ? 512 : 256;
+  // propagate workgroups resident at once: one per CU; two for the general pair with bf16
+  // inputs (and its diagonal rules), whose workgroups fit twice in a CU's LDS and registers
+  const bool twice = !fused && !split && (bf16 || seg_diagonal(rule, flags));
+  const size_t cap = twice ? 512 : 256;
+  const int pmax = (twice && bf16) ? 32 : 16;
   int P = 1;
-  while (P < 16 && wgs * 2 * P <= cap && T % (64 * 2 * (size_t)P) == 0 && T / (2 * (size_t)P) >= 512) P *= 2;
+  while (P < pmax && wgs * 2 * P <= cap && T % (64 * 2 * (size_t)P) == 0 && T / (2 * (size_t)P) >= 512) P *= 2;
   // With a transition pass the propagate work doubles, so fewer than 8 segments do not
   // pay (an additive elu+1 scan with 32 heads, T = 16384, ran no faster with 4 before
   // its transitions were made diagonal); diagonal transitions pay from 2.
