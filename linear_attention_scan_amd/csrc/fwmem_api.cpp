@@ -96,11 +96,11 @@ struct StatePtrs {
 };
 
 // Workspace of a scan: the (head, chunk) records, and for a segmented scan (P > 1 segments
-// per head, see SegParams) the two virtual state buffers, z and the segment start states;
-// with FWMEM_ZNORM the normaliser's chunk terms (ZRec) and its value at every chunk entry.
+// per head, see SegParams) the virtual state buffers and each segment's decay; with
+// FWMEM_ZNORM the normaliser's chunk terms (ZRec) and its value at every chunk entry.
 struct WsLayout {
   int P;
-  size_t rec, A0, B0, A1, B1, z, start, zr, zc, total;
+  size_t rec, A0, B0, A1, B1, z, zr, zc, total;
 };
 
 size_t record_bytes(int bf16, int dk, const fwmem_mode* m) {
@@ -120,8 +120,8 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
   w.rec = 0;
   if (w.P > 1) {
     const size_t VH = BH * (size_t)w.P, dk = (size_t)s->dk, dv = (size_t)s->dv;
-    // diagonal transitions need no transition states, gam [BH*P] (each segment's decay)
-    // in place of z, and no separate start states (the combine writes them into B0)
+    // diagonal transitions need no transition states; gam [BH*P] holds each segment's
+    // decay; the combine writes the segments' start states into B0 in both cases
     const bool diag = fwmem::seg_diagonal(m->rule, m->flags);
     const size_t sa = diag ? 0 : align256(4 * (VH * dk * dk + VH * dk + VH));
     const size_t sb = align256(4 * (VH * dk * dv + VH * dk + VH));
@@ -131,9 +131,7 @@ WsLayout ws_layout(const fwmem_shape* s, const fwmem_mode* m) {
     w.B1 = w.B0 + sb;
     off = w.B1 + sb;
     w.z = off;
-    off += align256(4 * (diag ? VH : BH * T * dk));
-    w.start = off;
-    if (!diag) off += align256(4 * VH * dk * dv);
+    off += align256(4 * VH);
   }
   // the normaliser's chunk terms and chunk-entry values (the fused additive kernel carries
   // the normaliser itself)
@@ -358,10 +356,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   }
 
   // Segmented scan: P segments of each head run as virtual heads (SegParams). The prep
-  // phase sets up the virtual states and builds every record. With diagonal transitions
-  // the propagate phase forms each segment's own state, chains the segments and runs one
-  // pass from the true start states; otherwise it runs the local and the transition
-  // passes, then chains the segments and fixes up the outputs.
+  // phase sets up the virtual states and builds every record. The propagate phase forms
+  // each segment's own state change (with diagonal transitions directly; otherwise by a
+  // local and a transition pass that compute states only), chains the segments, and runs
+  // one pass from the true start states that writes the outputs.
   char* ws = static_cast<char*>(workspace);
   const size_t VH = z.BH * (size_t)wl.P, dk = (size_t)shape->dk, dv = (size_t)shape->dv;
   fwmem::SegParams sp;
@@ -386,8 +384,6 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   vstate(wl.A1, dk, sp.A1_S, A1_x, A1_h);
   vstate(wl.B1, dv, sp.B1_S, sp.B1_x, B1_h);
   (void)B1_x_unused;
-  sp.z = reinterpret_cast<const float*>(ws + wl.z);
-  sp.S_start = reinterpret_cast<float*>(ws + wl.start);
   sp.out = static_cast<float*>(out);
   sp.BH = (int)z.BH;
   sp.P = wl.P;
@@ -403,11 +399,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   sp.beta = beta;
   sp.lam = lambda;
   sp.gam = reinterpret_cast<float*>(ws + wl.z);
-  // Diagonal transitions form each segment's own state directly and chain the segments
-  // first; the combine then writes the start states where the propagate pass starts.
-  if (sp.diag) sp.S_start = sp.B0_S;
+  // the combine writes the start states where the output pass starts
+  sp.S_start = sp.B0_S;
 
-  fwmem::ScanParams pv = p;  // the local pass over the virtual heads
+  fwmem::ScanParams pv = p;  // the output pass over the virtual heads, from the start states in B0
   pv.BH = (int)VH;
   pv.T = sp.L;
   pv.nchunks = sp.L / kChunk;
@@ -417,10 +412,13 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
   pv.S_out = sp.B1_S;
   pv.xprev_out = sp.B1_x;
   pv.has_out = B1_h;
-  fwmem::ScanParams pa = pv;  // the transition pass: identity start, zero values
+  fwmem::ScanParams pl = pv;  // the local pass: each segment's own state from zero, no outputs
+  pl.out = nullptr;
+  pl.S_in = nullptr;
+  fwmem::ScanParams pa = pv;  // the transition pass: identity start, zero values, no outputs
   pa.v = nullptr;
   pa.dv = shape->dk;
-  pa.out = const_cast<float*>(sp.z);
+  pa.out = nullptr;
   pa.S_in = sp.A0_S;
   pa.xprev_in = sp.A0_x;
   pa.has_in = sp.A0_h;
@@ -440,10 +438,10 @@ fwmem_status scan_impl(const fwmem_shape* shape, const void* q, const void* k, c
       if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 2);
       if (e == hipSuccess) e = fwmem::launch_seg_extras(sp, hs);
     } else {
-      e = fwmem::launch_scan(pv, hs, 2);
+      e = fwmem::launch_scan(pl, hs, 2);
       if (e == hipSuccess) e = fwmem::launch_scan(pa, hs, 2);
       if (e == hipSuccess) e = fwmem::launch_seg_combine(sp, hs);
-      if (e == hipSuccess) e = fwmem::launch_seg_fixup(sp, hs);
+      if (e == hipSuccess) e = fwmem::launch_scan(pv, hs, 2);
     }
   }
   e = znorm(e);

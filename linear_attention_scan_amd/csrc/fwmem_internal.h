@@ -156,14 +156,15 @@ hipError_t launch_state_copy(const float* S_in, const float* xprev_in, const int
 // A head's T tokens are cut into P segments of L = T / P tokens. Because q, k, v, the
 // gates and out are [BH][T][...] row-major, segment p of head h is virtual head
 // h * P + p of a [BH * P][L][...] problem, and the ordinary kernels run all segments at
-// once. Two passes over the virtual heads:
-//   local:      from S = 0 (segment 0: the caller's state) with the real values;
-//               gives o_local and the segment's final state B_p;
+// once. Two state passes over the virtual heads (no outputs):
+//   local:      from S = 0 with the real values; gives the segment's own state B_p;
 //   transition: from S = I with zero values; gives A_p (the segment's linear map
-//               S -> A_p S + B_p) and z_t = A_t^T phi(q_t) for every token.
-// Then S_start(p+1) = A_p S_start(p) + B_p (a short serial chain over segments) and
-// o_t = o_local,t + S_start(p)^T z_t. Each segment's first token takes the previous
-// segment's last key as its carried key.
+//               S -> A_p S + B_p).
+// Then S_start(p+1) = A_p S_start(p) + B_p (a short serial chain over segments from
+// S_start(0), the caller's state), written into B0, and one pass over the virtual heads
+// from those start states writes the outputs. No pass of the propagate phase reads what
+// another writes before the combine, so the phase can run again after one prep. Each segment's first token takes the previous segment's last key as its
+// carried key.
 struct SegParams {
   const void* k;          // [BH][T][dk] raw keys (the carried key of each segment)
   const float* S_in;      // caller's state or null
@@ -185,14 +186,11 @@ struct SegParams {
   float* A1_S;
   float* B1_S;
   float* B1_x;
-  const float* z;         // [BH*P][L][dk]
-  float* S_start;         // [BH*P][dk][dv] (segment p >= 1)
+  float* S_start;         // [BH*P][dk][dv] (segment p >= 1): B0_S
   float* out;             // [BH][T][dv] float32
   // Diagonal transitions (additive rule, scalar decay): a segment maps S to
-  // Gamma_p S + B_p, so there is no transition pass and no A or z buffer. The segments'
-  // own states B_p come from seg_state before the propagate pass (B1 holds them, the
-  // combine writes each start state into B0 and the pass starts there), so the outputs
-  // need no fix-up.
+  // Gamma_p S + B_p, so there is no transition pass and no A buffer; the segments' own
+  // states B_p come from seg_state (B1 holds them).
   int diag;
   const void* q;          // [BH][T][dk] raw queries
   const void* v;          // [BH][T][dv] values
@@ -238,7 +236,6 @@ struct ZParams {
 };
 hipError_t launch_znorm(const ZParams& z, hipStream_t st);
 hipError_t launch_seg_combine(const SegParams& s, hipStream_t st);
-hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_state(const SegParams& s, hipStream_t st);
 hipError_t launch_seg_extras(const SegParams& s, hipStream_t st);
 

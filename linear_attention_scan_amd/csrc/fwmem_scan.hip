@@ -758,6 +758,9 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
   const int dv = p.dv;
   const size_t rowbase = (size_t)bh * p.T;
   const bool out_bf16 = (p.flags & kFlagOutBf16) != 0;
+  // A null output pointer asks for the state alone (the segmented scan's state passes):
+  // the read (Q S + M U) and its operands are skipped.
+  const bool want_out = p.out != nullptr;
   // per-head base pointers; every per-thread offset below fits in 32 bits
   const InT* kbase = static_cast<const InT*>(p.k) + rowbase * DK;
   const InT* qbase = static_cast<const InT*>(p.q) + rowbase * DK;
@@ -878,7 +881,8 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) {
         const int t = ps * RPP + tid / TPR;
-        if constexpr (OPS) {
+        if (!want_out) {
+        } else if constexpr (OPS) {
           Pol::store_run(Qs + t * LDX, col, __builtin_bit_cast(frag_t, pq[ps]));
         } else {
           float qv[VW];
@@ -904,7 +908,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
 #pragma unroll
       for (int j = 0; j < NVT; ++j) {
         if (R::solve) reinterpret_cast<u32x4*>(Ts + rr * LDC + cc2)[j] = pt[j];
-        reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
+        if (want_out) reinterpret_cast<u32x4*>(Ms + rr * LDC + cc2)[j] = pm[j];
       }
       if (tid < CH) {
         s_fac[tid] = pf[0];
@@ -969,7 +973,8 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) {
         const int tau = tn + ps * RPP + tid / TPR;
-        if constexpr (OPS) {
+        if (!want_out) {
+        } else if constexpr (OPS) {
           pq[ps] = ld16(rec + RC::kPQ, (uint32_t)((ps * RPP + tid / TPR) * DK + col) * 2u);
         } else {
           pq[ps] = u32x4{0u, 0u, 0u, 0u};
@@ -992,7 +997,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
 #pragma unroll
       for (int j = 0; j < NVT; ++j) {
         if (R::solve) pt[j] = Tg[j];
-        pm[j] = Mg[j];
+        if (want_out) pm[j] = Mg[j];
       }
       if (tid < CH) {
         const float* fac = reinterpret_cast<const float*>(rec + RC::kFac);
@@ -1128,6 +1133,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
       }
 
       // O = diag(Gamma) Q S + M U
+      if (want_out) {
       f4 O[NMT];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
@@ -1171,6 +1177,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
             else obase32[o] = O[mt][ii];
           }
         }
+      }
 
       // S' = Gamma_C S + X^T (diag(Gamma_C/Gamma) U)
       float mut = 0.f;

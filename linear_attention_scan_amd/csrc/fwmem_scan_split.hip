@@ -763,9 +763,13 @@ __global__ __launch_bounds__(NTS) void prop_split_kernel(ScanParams p) {
     return;
   }
 
+  // A null output asks for the state alone (the segmented scan's state passes): the
+  // resource is then empty, based at the keys, so every output store falls outside it and
+  // is dropped.
   constexpr uint32_t oes = OBF ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t ro =
-      rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes);
+      p.out != nullptr ? rsrc(static_cast<const char*>(p.out) + rowbase * dv * oes, (uint32_t)(p.T * dv) * oes)
+                       : rsrc(kb, 0u);
   const uint32_t vo = (uint32_t)(8 * L.g * dv + col) * oes;
   for (int c = 0; c < p.nchunks; c += 2) {
     beta_step<DK, SOLVE, OBF>(p, B0, H, c, L, dv, vo, ro);

@@ -15,9 +15,10 @@ namespace {
 
 constexpr int NTH = 256;
 
-// Virtual initial states. Local pass: the caller's state for segment 0, zero for the
-// others. Transition pass: the identity. Both carry the same key: the caller's for
-// segment 0, the last (raw, or elu+1 of the raw) key of the previous segment for p >= 1.
+// Virtual initial states. Segment 0's start state: the caller's state, or zero (the
+// combine and the output pass read it; the other segments' start states come from the
+// combine). Transition pass: the identity. Every pass carries the same key: the caller's
+// for segment 0, the last (raw, or elu+1 of the raw) key of the previous segment for p >= 1.
 template <typename InT>
 __global__ __launch_bounds__(NTH) void seg_init_kernel(SegParams s) {
   const int vh = blockIdx.x, h = vh / s.P, p = vh % s.P;
@@ -26,9 +27,7 @@ __global__ __launch_bounds__(NTH) void seg_init_kernel(SegParams s) {
   float* B = s.B0_S + (size_t)vh * dk * dv;
   float* A = s.A0_S + (size_t)vh * dk * dk;
   const float* Sin = (p == 0 && s.S_in != nullptr) ? s.S_in + (size_t)h * dk * dv : nullptr;
-  // with the segment states formed first, the combine writes the start states of the
-  // later segments
-  if (p == 0 || !s.diag)
+  if (p == 0)
     for (int e = threadIdx.x; e < dk * dv; e += NTH) B[e] = Sin != nullptr ? Sin[e] : 0.f;
   if (!s.diag)
     for (int e = threadIdx.x; e < dk * dk; e += NTH) A[e] = (e / dk == e % dk) ? 1.f : 0.f;
@@ -97,70 +96,87 @@ __global__ __launch_bounds__(NTH) void seg_combine_diag_kernel(SegParams s) {
 }
 
 // General transitions: S_start(p+1) = A_p S_start(p) + B_p, a [d_k x d_k] x [d_k x 16]
-// product per segment on fp32 MFMA. Wave w owns row tiles w, w + 4 of the tile in C layout;
-// the current start state goes through LDS so that every wave reads all of it as B
-// fragments.
+// product per segment on fp32 MFMA. The local pass ran every segment from zero, so the
+// chain starts at S_start(0), the caller's state (its copy in B0 made at set-up); without
+// one, at S_start(1) = B_0. Wave w owns row tiles w, w + 4 of the tile in C layout; the
+// current start state goes through LDS so that every wave reads all of it as B fragments.
 template <int DK>
 __device__ void combine_general(const SegParams& s, int h, int j0) {
   constexpr int NRT = DK / 16, RPW = (NRT + 3) / 4;
-  __shared__ float cur[DK * 16];
+  __shared__ float cur[2][DK * 16];
   const int dv = s.dv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
+  const bool from_in = s.S_in != nullptr;
+  const int p0 = from_in ? 0 : 1;
   f4 v[RPW];
-  const float* B0 = s.B1_S + (size_t)(h * s.P) * DK * dv;
+  const float* V0 = (from_in ? s.B0_S : s.B1_S) + (size_t)(h * s.P) * DK * dv;
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int rt = wave + 4 * r;
     if (rt < NRT) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[r][i] = B0[(size_t)(16 * rt + 4 * g + i) * dv + j0 + n];
-        cur[(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
+        v[r][i] = V0[(size_t)(16 * rt + 4 * g + i) * dv + j0 + n];
+        cur[p0 & 1][(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
       }
     }
   }
-  __syncthreads();
-  for (int p = 1; p < s.P; ++p) {
+  // The lane's rows of A_p and its elements of B_p do not depend on the chain: they are
+  // loaded one step ahead, so a step waits only for its product and one barrier (the
+  // start state alternates between two LDS tiles).
+  f4 an[RPW][NRT], bn[RPW];
+  auto fetch = [&](int p) {
     const size_t vh = (size_t)h * s.P + p;
-    float* St = s.S_start + vh * DK * dv;
     const float* A = s.A1_S + vh * DK * DK;
     const float* Bm = s.B1_S + vh * DK * dv;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int rt = wave + 4 * r;
+      if (rt < NRT) {
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb)
+          an[r][kb] = *reinterpret_cast<const f4*>(A + (size_t)(16 * rt + n) * DK + 16 * kb + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bn[r][i] = Bm[(size_t)(16 * rt + 4 * g + i) * dv + j0 + n];
+      }
+    }
+  };
+  if (p0 < s.P) fetch(p0);
+  __syncthreads();
+  for (int p = p0; p < s.P; ++p) {
+    f4 a[RPW][NRT], b[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      b[r] = bn[r];
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) a[r][kb] = an[r][kb];
+    }
+    if (p + 1 < s.P) fetch(p + 1);
+    const float* cb = cur[p & 1];
+    float* cn = cur[(p + 1) & 1];
     f4 bfr[NRT];
 #pragma unroll
     for (int kb = 0; kb < NRT; ++kb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bfr[kb][q] = cur[(16 * kb + 4 * g + q) * 16 + n];
-    f4 nv[RPW];
+      for (int q = 0; q < 4; ++q) bfr[kb][q] = cb[(16 * kb + 4 * g + q) * 16 + n];
+    float* St = s.S_start + ((size_t)h * s.P + p) * DK * dv;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int rt = wave + 4 * r;
       if (rt < NRT) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NRT; ++kb) {
-          const f4 a = *reinterpret_cast<const f4*>(A + (size_t)(16 * rt + n) * DK + 16 * kb + 4 * g);
-          mma_f32_block(acc, a, bfr[kb]);
-        }
+        for (int kb = 0; kb < NRT; ++kb) mma_f32_block(acc, a[r][kb], bfr[kb]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const size_t e = (size_t)(16 * rt + 4 * g + i) * dv + j0 + n;
-          St[e] = v[r][i];
-          nv[r][i] = acc[i] + Bm[e];
+          if (p > 0) St[(size_t)(16 * rt + 4 * g + i) * dv + j0 + n] = v[r][i];
+          v[r][i] = acc[i] + b[r][i];
+          cn[(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
         }
       }
     }
-    __syncthreads();  // every wave has read cur
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int rt = wave + 4 * r;
-      if (rt < NRT) {
-        v[r] = nv[r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cur[(16 * rt + 4 * g + i) * 16 + n] = v[r][i];
-      }
-    }
-    __syncthreads();
+    __syncthreads();  // the next start state is in cn; every wave has read cb
   }
   if (s.S_out != nullptr) {
 #pragma unroll
@@ -175,95 +191,13 @@ __device__ void combine_general(const SegParams& s, int h, int j0) {
 }
 
 // S_start(p+1) = A_p S_start(p) + B_p, serial over the segments of one head, for one
-// 16-column tile per workgroup (columns evolve independently). S_start(1) is segment 0's
-// final local state, which began at the caller's state. Writes S_start(p) for p >= 1, and
-// the final state, carried key and flag to the caller's state.
+// 16-column tile per workgroup (columns evolve independently). Writes S_start(p) for
+// p >= 1, and the final state, carried key and flag to the caller's state.
 __global__ __launch_bounds__(NTH) void seg_combine_kernel(SegParams s) {
   const int ntile = s.dv / 16;
   const int h = blockIdx.x / ntile, j0 = (blockIdx.x % ntile) * 16;
   if (s.dk == 64) combine_general<64>(s, h, j0);
   else combine_general<128>(s, h, j0);
-}
-
-// out[vh, t, :] += S_start(vh)^T z_t for segments p >= 1, a [64 x dk] x [dk x dv] product
-// per tile of 64 tokens, on bf16 MFMA with hi/lo split operands (the products hi.hi,
-// hi.lo and lo.hi keep about 16 bits of each factor). One workgroup per (virtual head,
-// group of up to kFixTiles token tiles); wave w owns value columns 16 NTW w ..
-// 16 NTW (w + 1) - 1 and keeps their S_start fragments in registers across the tiles.
-constexpr int kFixTiles = 2;
-
-__device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
-  float a[4], b[4];
-  In<float>::load(p, a);
-  In<float>::load(p + 4, b);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = a[e];
-    x[4 + e] = b[e];
-  }
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void seg_fixup_kernel(SegParams s) {
-  constexpr int NKQ = DK / 32, NTW = DV / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, n = lane & 15;
-  const int ntb = s.L / 64, ngrp = (ntb + kFixTiles - 1) / kFixTiles;
-  int b = blockIdx.x;
-  const int tg = b % ngrp;
-  b /= ngrp;
-  const int nseg = s.P - 1;
-  const int h = b / nseg, p = 1 + b % nseg;
-  const size_t vh = (size_t)h * s.P + p;
-
-  // B fragments: lane (g, n) holds S_start[32 kq + 8 g + e][column 16 (NTW wave + j) + n]
-  bf8 bh[NTW][NKQ], bl[NTW][NKQ];
-  {
-    const float* St = s.S_start + vh * DK * DV;
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int col = 16 * (NTW * wave + j) + n;
-#pragma unroll
-      for (int kq = 0; kq < NKQ; ++kq) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = St[(size_t)(32 * kq + 8 * g + e) * DV + col];
-        split8(x, bh[j][kq], bl[j][kq]);
-      }
-    }
-  }
-  const int tt1 = min(ntb, (tg + 1) * kFixTiles);
-  for (int tt = tg * kFixTiles; tt < tt1; ++tt) {
-    const size_t row0 = vh * s.L + (size_t)tt * 64;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      // A fragments: lane (g, n) holds z[token 16 mt + n][32 kq + 8 g + e]
-      const size_t row = row0 + 16 * mt + n;
-      f4 acc[NTW];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kq = 0; kq < NKQ; ++kq) {
-        float x[8];
-        load_row8(s.z + row * DK + 32 * kq + 8 * g, x);
-        bf8 ah, al;
-        split8(x, ah, al);
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          mma_bf16(acc[j], ah, bh[j][kq]);
-          mma_bf16(acc[j], ah, bl[j][kq]);
-          mma_bf16(acc[j], al, bh[j][kq]);
-        }
-      }
-      // acc[j][i] is token 16 mt + 4 g + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* o = s.out + (row0 + 16 * mt + 4 * g + i) * DV + n;
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) o[16 * (NTW * wave + j)] += acc[j][i];
-      }
-    }
-  }
 }
 
 // Eight K slots of a bf16 MFMA operand from a row-major [token][column] tile by two LDS
@@ -521,14 +455,6 @@ hipError_t launch_state_in(const SegParams& s, unsigned grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fixup_dims(const SegParams& s, unsigned grid, hipStream_t st) {
-  if (s.dk == 64 && s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<64, 64>), dim3(grid), dim3(NTH), 0, st, s);
-  else if (s.dk == 64) hipLaunchKernelGGL((seg_fixup_kernel<64, 128>), dim3(grid), dim3(NTH), 0, st, s);
-  else if (s.dv == 64) hipLaunchKernelGGL((seg_fixup_kernel<128, 64>), dim3(grid), dim3(NTH), 0, st, s);
-  else hipLaunchKernelGGL((seg_fixup_kernel<128, 128>), dim3(grid), dim3(NTH), 0, st, s);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int scan_segments(size_t BH, size_t T, int dk, int dv, int bf16, int rule, uint32_t flags) {
@@ -578,13 +504,6 @@ hipError_t launch_seg_extras(const SegParams& s, hipStream_t st) {
   if (s.S_out == nullptr) return hipSuccess;
   hipLaunchKernelGGL(seg_extras_kernel, dim3((unsigned)s.BH), dim3(NTH), 0, st, s);
   return hipGetLastError();
-}
-
-hipError_t launch_seg_fixup(const SegParams& s, hipStream_t st) {
-  const size_t ngrp = ((size_t)s.L / 64 + kFixTiles - 1) / kFixTiles;
-  const size_t n = (size_t)s.BH * (s.P - 1) * ngrp;
-  if (n == 0) return hipSuccess;
-  return launch_fixup_dims(s, (unsigned)n, st);
 }
 
 }  // namespace fwmem
