@@ -45,12 +45,12 @@ MEASURED_TRAFFIC = {
     ("delta_bf16_h16", "prop_split_kernel"): {
         "sources": ('fwmem_scan_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
-            "fwmem_scan_split.hip": "888db0e0e31bca242ef147c8412775f748ed947fd0abc340b58805efbbd84eab",
+            "fwmem_scan_split.hip": "8dad3d6f246efa0358bc68fa1ca0969768f0cbb50970ea006490d38df3a1dcf9",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 150222.9, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 150222.5, "write_kib": 135202.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "prep_split_kernel"): {
         "sources": ('fwmem_prep_split.hip', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
@@ -58,18 +58,18 @@ MEASURED_TRAFFIC = {
             "fwmem_prep_split.hip": "3101a25cff5f80c14678715ef955e7813e5203414cf5f028e6a8e885c74a10f8",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 66681.5, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66681.6, "write_kib": 103566.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("decode", "step_kernel"): {
         "sources": ('fwmem_step.hip', 'fwmem_device.h', 'fwmem_internal.h'),
         "sha256": {
             "fwmem_step.hip": "abf27317cda12cc5a31bfd56f61be55aedc5758d577a0abf5f1d25a096ca1990",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 267738.3, "write_kib": 532861.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 267738.2, "write_kib": 532870.6, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_prep_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
@@ -78,9 +78,9 @@ MEASURED_TRAFFIC = {
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 66694.9, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 66695.4, "write_kib": 210048.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_state_bf_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
@@ -89,9 +89,9 @@ MEASURED_TRAFFIC = {
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 100195.2, "write_kib": 393218.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 100195.2, "write_kib": 393216.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_dstate_bf_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
@@ -100,9 +100,9 @@ MEASURED_TRAFFIC = {
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 199003.2, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 199003.4, "write_kib": 397314.0, "read_factor": 2.0, "write_factor": 1.0,
     },
     ("delta_bf16_h16", "bwd_grad_kernel"): {
         "sources": ('fwmem_backward_chunk.hip', 'fwmem_backward.h', 'fwmem_split.h', 'fwmem_device.h', 'fwmem_internal.h'),
@@ -111,9 +111,9 @@ MEASURED_TRAFFIC = {
             "fwmem_backward.h": "a5fd0f8c1f47a680f2609b5378a6eaef440ead7d30c31d73b985adaf1ed93a10",
             "fwmem_split.h": "4591e7fd7055f318ad39f2d4e4db57e3d0fc5b48fefc454192d92052048145be",
             "fwmem_device.h": "90ffc6ed9c432872bfbb7f5721e8afbed17fcc7efdc6a739875472e513370cd9",
-            "fwmem_internal.h": "7c624f93fcc78df43abc95a170b3055a73935e42f7c7a2386df18d1af3a09e60",
+            "fwmem_internal.h": "033dab365d38d3acdac54d3b0c36484685eff444330d782d2e2eff68dba2abf0",
         },
-        "fetch_kib": 629742.8, "write_kib": 395446.7, "read_factor": 2.0, "write_factor": 1.0,
+        "fetch_kib": 629742.6, "write_kib": 395396.3, "read_factor": 2.0, "write_factor": 1.0,
     },
 }
 
