@@ -382,7 +382,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         pr ^= (a < 0.f) ? 1u : 0u;
         ev[u] = gs;  // in-segment prefix for now
         pl |= pr << u;
-        if (t == TA) {
+        if (u == TA % SEGP && part == TA / SEGP) {  // t == TA
           x_anc[i] = gs;
           x_apr[i] = pr;
         }
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       const float qh = (float)Qs[t * LDX + ip];
       const float ep = u ? ev[u - 1] : eprev;
       mAL = fmaxf(mAL, fabsf(xh * ep));
-      mBX = fmaxf(mBX, fabsf(xh / ev[u]));
+      mBX = fmaxf(mBX, fabsf(xh * __builtin_amdgcn_rcpf(ev[u])));
       mAM = fmaxf(mAM, fabsf(qh * ev[u]));
     }
     {
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         const float scp = u ? (((esg >> (u - 1)) & 1u) ? -1.f : 1.f) : (sprev0 ? -1.f : 1.f);
         const float ep = u ? ev[u - 1] : eprev;
         if (R::solve) AL[t * LDX + ip] = Pol::cvt(xh * scp * ep * sAL);
-        BX[t * LDX + ip] = Pol::cvt(xh * sc / ev[u] * sBX);
+        BX[t * LDX + ip] = Pol::cvt(xh * sc * __builtin_amdgcn_rcpf(ev[u]) * sBX);
         AM[t * LDX + ip] = Pol::cvt(qh * sc * ev[u] * sAM);
       }
     }

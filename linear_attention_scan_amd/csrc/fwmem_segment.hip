@@ -1,4 +1,4 @@
-// Segment-parallel scan: the set-up, combine and fix-up kernels (see SegParams in
+// Segment-parallel scan: the set-up, segment-state and combine kernels (see SegParams in
 // fwmem_internal.h). The split of a long sequence into segments whose maps compose
 // is the scan's own linearity: the write S_t = (diag(a_t) - eta_t x_t x_t^T) S_{t-1}
 // + eta_t x_t v_t^T (delta rule; "Fast Weight Attention for Continual Learning"

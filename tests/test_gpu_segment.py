@@ -100,8 +100,9 @@ def test_segmented_propagate_is_repeatable_after_one_prep(rule):
 
 
 # ---- diagonal transitions: the additive rule with a scalar decay composes segments by a
-# scalar (the product of the retentions), so there is no transition pass; the fix-up
-# forms Gamma_t phi(q_t) itself.
+# scalar (the product of the retentions), so there is no transition pass; the segments'
+# own states come from one product each, and one pass from the chained start states
+# forms the outputs.
 
 def test_diagonal_segments_elu1_eight_heads():
     """Eight heads of 4096 tokens (8 segments each), C3's distributions."""
@@ -113,7 +114,7 @@ def test_diagonal_segments_elu1_eight_heads():
 def test_diagonal_segments_split_pair_qk_norm_and_gate_preactivations():
     """Split pair (bf16 identity); the retention and write scale arrive as
     pre-activations (the decay kernel activates them), q and k are L2-normalised by the
-    scan (the fix-up rescales the queries)."""
+    scan (the segment-state product rescales the keys)."""
     w = wl.make_scan(B=1, H=2, T=8192, dk=128, dv=128, rule=wl.RULE_ADDITIVE, normalise_qk=False,
                      qk_norm="l2", beta_kind="sigmoid", lam_kind="gamma", seed=12,
                      name="diagonal segments split qk-l2 gates-pre")
