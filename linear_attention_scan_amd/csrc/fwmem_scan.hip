@@ -88,13 +88,25 @@ __device__ __forceinline__ u32x4 ld16(const T* base, uint32_t byte_off) {
   return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
+// Workgroup barrier for LDS: waits for this wave's LDS operations only. Every barrier of
+// these kernels orders LDS traffic alone (no wave reads global memory that another wave
+// of the workgroup writes), and a plain __syncthreads would also wait until the wave's
+// outstanding global loads have returned and its stores (record rows, outputs) have
+// been acknowledged.
+static __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Block-wide max of a per-thread value (all threads must call it).
 __device__ __forceinline__ float block_max(float v, float* s_red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_max(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) s_red[wave] = v;
-  __syncthreads();
+  lds_barrier();
   float m = s_red[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) m = fmaxf(m, s_red[w]);
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       if (tid % TPRL == 0) s_lam[t] = p.lam != nullptr ? act_lam(m, p.flags, true) : 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Token scalars: eta_t, and for scalar decay the in-chunk prefix of log|a|.
   if (wave == 0) {
@@ -337,7 +349,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     s_g[t] = la;
     s_sg[t] = (ng & 1) ? -1.f : 1.f;
   }
-  __syncthreads();
+  lds_barrier();
 
   // Operand sources of the two Gram products.
   const op_t* A_L = Xs;  // rows x_t (scaled); scalar decay is applied by the mask
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       x_tot[tid] = gs;
       x_par[tid] = pr;
     }
-    __syncthreads();
+    lds_barrier();
     float off = 0.f, anc, gtot = 0.f;
     uint32_t poff = 0, apr, ptot = 0;
     {
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         AM[t * LDX + ip] = Pol::cvt(qh * sc * ev[u] * sAM);
       }
     }
-    __syncthreads();
+    lds_barrier();
     A_L = AL;
     A_M = AM;
     B_X = BX;
@@ -508,7 +520,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
           Pol::mma(acc[jj], Pol::lds_row(arow, kb, g), Pol::lds_row(brow, kb, g));
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
       const int job = wave + NW * jj;
@@ -542,7 +554,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // T = (I + L)^-1 by blocked forward substitution (16x16 blocks, fp32).
   if (R::solve) {
@@ -570,7 +582,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // Below the diagonal on fp32 MFMA: wave j forms column block j top-down,
     //   T_ij = -D_i sum_{k=j}^{i-1} L_ik T_kj,
     // keeping the column's blocks in registers (C layout, which is the B operand's layout),
@@ -579,7 +591,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
     if (wave == 0) t_column_block<0, LDF>(Lf, Tf, lane);
     else if (wave == 1) t_column_block<1, LDF>(Lf, Tf, lane);
     else if (wave == 2) t_column_block<2, LDF>(Lf, Tf, lane);
-    __syncthreads();
+    lds_barrier();
   }
 
   // Write T (delta rule) and M, scaled and in operand order, plus the token factors.
@@ -921,7 +933,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
         s_misc[1] = pinvT;
         s_misc[2] = pinvM;
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (c + 1 < p.nchunks) {
       // ---- global -> registers (chunk c+1)
@@ -1037,7 +1049,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
       if (c + 1 < p.nchunks) load_lam(t0 + CH);
       s_pg[tid] = gsum;
       s_pp[tid] = pr;
-      __syncthreads();
+      lds_barrier();
       float off = 0.f, gC = 0.f;
       uint32_t poff = 0, pC = 0;
 #pragma unroll
@@ -1067,7 +1079,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
         Qs[t * LDX + ip] = Pol::cvt((float)Qs[t * LDX + ip] * fcur);
         fprev = fcur;
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     if (wave_on) {
@@ -1211,7 +1223,7 @@ __global__ __launch_bounds__(NT, sizeof(InT) == 2 ? 2 : 1) void prop_kernel(Scan
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // final state
