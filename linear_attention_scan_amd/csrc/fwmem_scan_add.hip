@@ -78,6 +78,16 @@ __device__ __forceinline__ void lane_prefix(float& la, int& ng) {
   }
 }
 
+// Workgroup barrier for LDS: waits for this wave's LDS operations only. The kernel's
+// barriers order LDS traffic alone; a plain __syncthreads would also wait for the next
+// chunk's rows in flight and for the previous chunk's output stores to be acknowledged.
+static __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int DK, int DV, bool ELU, bool ZN>
 __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
   using L = AddLds<DK, DV, ELU>;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
       s_g[lane] = with_sign(__builtin_amdgcn_exp2f(la), ng & 1);
       s_w[lane] = gb * with_sign(__builtin_amdgcn_exp2f(lc - la), pc ^ (ng & 1));
     }
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < p.nchunks) prefetch(c + 1);
 
     // ---- P^T tiles (rows s, columns t) of the lower triangle, masked: fragment f of the
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(4 * DV) void add_kernel(ScanParams p) {
         s[rt] = s[rt] * gC + acc;
       }
     }
-    __syncthreads();  // the P fragments are complete
+    lds_barrier();  // the P fragments are complete
 
     // ---- O += (P o D) V, stored. The next chunk's staging only begins after every wave
     // has passed this chunk's second barrier, and nothing below reads LDS except the P
