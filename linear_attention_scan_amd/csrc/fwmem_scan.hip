@@ -441,8 +441,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         const int t = tb + u;
         const float g = off + ev[u];
         const uint32_t pcur = poff ^ ((pl >> u) & 1u);
-        const float fcur = (pcur ? -1.f : 1.f) * __expf(g);
-        const float fend = ((ptot ^ pcur) ? -1.f : 1.f) * __expf(gtot - g);
+        // signs set in the sign bit of the positive exponentials
+        const float fcur = __uint_as_float(__float_as_uint(__expf(g)) | (pcur << 31));
+        const float fend = __uint_as_float(__float_as_uint(__expf(gtot - g)) | ((ptot ^ pcur) << 31));
         const float xh = (float)Xs[t * LDX + ip];
         px[t * DK + i] = Pol::cvt(xh * fprev);
         pu[t * DK + i] = Pol::cvt(xh * fend);
@@ -451,16 +452,16 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
       }
       if (part == 0) reinterpret_cast<float*>(rec + RC::kPG)[i] = (ptot ? -1.f : 1.f) * __expf(gtot);
     }
-    // e_t and its sign (bit u of esg), then the block maxima (for the fp16 scales)
-    uint32_t esg = 0;
-    float eprev = __expf(off - anc);
-    const uint32_t sprev0 = poff ^ apr;
+    // e_t with its sign (set in the sign bit of the positive exponential, so that the
+    // operands below are plain products), then the block maxima (for the fp16 scales)
+    const float eprev =
+        __uint_as_float(__float_as_uint(__expf(off - anc)) | ((poff ^ apr) << 31));
     float mAL = 0.f, mBX = 0.f, mAM = 0.f;
 #pragma unroll
     for (int u = 0; u < SEGP; ++u) {
       const int t = tb + u;
-      ev[u] = __expf(off + ev[u] - anc);
-      esg |= (poff ^ ((pl >> u) & 1u) ^ apr) << u;
+      const uint32_t sgn = poff ^ ((pl >> u) & 1u) ^ apr;
+      ev[u] = __uint_as_float(__float_as_uint(__expf(off + ev[u] - anc)) | (sgn << 31));
       const float xh = (float)Xs[t * LDX + ip];
       const float qh = (float)Qs[t * LDX + ip];
       const float ep = u ? ev[u - 1] : eprev;
@@ -482,12 +483,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(ScanParams p) {
         const int t = tb + u;
         const float xh = (float)Xs[t * LDX + ip];
         const float qh = (float)Qs[t * LDX + ip];
-        const float sc = ((esg >> u) & 1u) ? -1.f : 1.f;
-        const float scp = u ? (((esg >> (u - 1)) & 1u) ? -1.f : 1.f) : (sprev0 ? -1.f : 1.f);
         const float ep = u ? ev[u - 1] : eprev;
-        if (R::solve) AL[t * LDX + ip] = Pol::cvt(xh * scp * ep * sAL);
-        BX[t * LDX + ip] = Pol::cvt(xh * sc * __builtin_amdgcn_rcpf(ev[u]) * sBX);
-        AM[t * LDX + ip] = Pol::cvt(qh * sc * ev[u] * sAM);
+        if (R::solve) AL[t * LDX + ip] = Pol::cvt(xh * ep * sAL);
+        BX[t * LDX + ip] = Pol::cvt(xh * __builtin_amdgcn_rcpf(ev[u]) * sBX);
+        AM[t * LDX + ip] = Pol::cvt(qh * ev[u] * sAM);
       }
     }
     lds_barrier();
