@@ -1,8 +1,10 @@
 """GPU parity of the segment-parallel scan. Few heads and long sequences leave most of
 the GPU idle in the ordinary scan, so the library runs P segments of each head as
-virtual heads (local and transition passes), chains the segment maps and fixes up the
-outputs. These shapes all take that form (P = 16); the full-size long per-channel
-workload in test_gpu_full.py does too."""
+virtual heads: each segment's own state change (a local and a transition pass that form
+states only, or for diagonal transitions one product), a chain of the segment maps from
+the caller's state, and one pass from the true start states that forms the outputs.
+These shapes all take that form (P = 8 or 16); the full-size long per-channel workload
+in test_gpu_full.py does too (P = 32)."""
 import numpy as np
 import pytest
 
@@ -67,6 +69,31 @@ def test_segmented_nonzero_state_in_place():
     assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
     np.testing.assert_array_equal(x, x_ref.astype(np.float32).astype(np.float64))
     assert np.all(h == 1)
+
+
+@pytest.mark.parametrize("case", ["per_channel_bf16", "f32"])
+def test_segmented_general_path_nonzero_state(case):
+    """The general pair from a nonzero initial state with a carried key: the local pass
+    runs every segment from zero, so the combine chains the caller's state through
+    segment 0's transition (S_start(1) = A_0 S_0 + B_0)."""
+    if case == "f32":
+        w, d = _delta(H=2, dtype="f32", d=64, seed=8), 64
+    else:
+        w, d = _delta(H=2, seed=9, beta_kind="sigmoid", lam_mu=-5.0, per_channel=True), 128
+    rng = np.random.default_rng(10)
+    S0 = (rng.standard_normal((1, 2, d, d)) * 0.05).astype(np.float32)
+    x0 = wl.round_to_bf16((rng.standard_normal((1, 2, d)) * 0.09).astype(np.float32))
+    h0 = np.array([[1, 1]], dtype=np.int32)
+    from tests.gpu_helpers import make_state
+    st = make_state(1, 2, d, d, S=S0, xprev=x0, has=h0)
+    say(f"[segmented] general pair {case}, nonzero S0, carried key")
+    o, st2 = gpu_scan(w, S_in=st)
+    o_ref, S_ref, _, _ = oracle_scan(w, S0=S0, xprev0=x0, has0=h0)
+    S, _, _ = state_np(st2)
+    eo, eS = orc.relerr(o, o_ref), orc.relerr(S, S_ref)
+    say(f"    err(o)={eo:.3e} err(S)={eS:.3e}")
+    tol = TOL["f32" if case == "f32" else "bf16"]
+    assert eo <= tol and eS <= tol
 
 
 @pytest.mark.parametrize("rule", [wl.RULE_DELTA, wl.RULE_ADDITIVE])
