@@ -27,10 +27,20 @@ __global__ __launch_bounds__(NTH) void seg_init_kernel(SegParams s) {
   float* B = s.B0_S + (size_t)vh * dk * dv;
   float* A = s.A0_S + (size_t)vh * dk * dk;
   const float* Sin = (p == 0 && s.S_in != nullptr) ? s.S_in + (size_t)h * dk * dv : nullptr;
-  if (p == 0)
+  // the caller's state (4-byte aligned only): eight loads in flight per thread
+  if (p == 0) {
+#pragma unroll 8
     for (int e = threadIdx.x; e < dk * dv; e += NTH) B[e] = Sin != nullptr ? Sin[e] : 0.f;
+  }
+  // the identity in 16-byte stores (A lies in the workspace, 256-byte aligned, and dk is a
+  // multiple of 4)
   if (!s.diag)
-    for (int e = threadIdx.x; e < dk * dk; e += NTH) A[e] = (e / dk == e % dk) ? 1.f : 0.f;
+    for (int e = 4 * threadIdx.x; e < dk * dk; e += 4 * NTH) {
+      f4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = ((e + j) / dk == (e + j) % dk) ? 1.f : 0.f;
+      *reinterpret_cast<f4*>(A + e) = a;
+    }
   const InT* kprev = static_cast<const InT*>(s.k) + ((size_t)vh * s.L - 1) * dk;  // p >= 1 only
   for (int i = threadIdx.x; i < dk; i += NTH) {
     float x = 0.f;
